@@ -1,0 +1,271 @@
+"""fp64 reference ("oracle") for one pipeline stage of patch-level DiT inference.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the package smoke check and the
+benchmark's CPU-baseline leg may import or run anything in this directory; the
+product path never does.  It shares no code with the HIP path: it is plain numpy
+float64, slow and written to be checked by eye against the method.
+
+What it computes (sources: the PipeFusion technical summaries on gist.science,
+Korean page 1 and French page 4, "Core mechanisms" / "Mecanismes principaux"):
+
+* Dual partitioning (mechanism 1): the stage owns L contiguous transformer
+  layers; the token sequence is split into M non-overlapping patches that are
+  pushed through those layers one patch at a time.
+* Temporal redundancy (mechanism 2): attention of the current step T uses
+  "stale" feature maps from step T+1 as context for the parts of the image not
+  yet recomputed; a device starts computing on stale activations rather than
+  waiting for fresh ones.
+* Memory (mechanism 4): each device keeps full-spatial K and V only for its own
+  layers, in one buffer per layer.
+* The DiT keeps full (non-local) attention (Key contributions, first bullet).
+
+Readings taken where the pages are silent (each listed in the design notes):
+the block is a pre-LN adaLN-modulated DiT block with gated residuals, tanh GELU
+MLP, LayerNorm eps 1e-6 without affine, biases present, attention scale
+1/sqrt(d), non-causal, no mask; the KV buffer is updated in place, so when
+patch m runs, rows of patches < m already hold step-T values, its own rows are
+fresh and rows of later patches still hold step-(T+1) values; step 0 is a
+warm-up that runs all rows as one patch; text-prefix rows (if any) run first as
+their own micro-step in every step.
+
+Two precision modes, both fp64 code:
+* ``exact``: no intermediate rounding (the plain definition).
+* ``bf16``: every tensor the bf16 path stores and feeds to a contraction is
+  rounded to bf16 (round to nearest even): the modulated LayerNorm outputs,
+  Q/K/V, the KV buffer after drift noise, the attention output and the GELU
+  output.  Softmax probabilities are not rounded.
+
+Parity status: every function below is pinned in the CPU test-suite by closed
+forms, invariants, library special cases or brute force.  The choice of block
+(LayerNorm / adaLN / GELU, which the pages do not define) is a reading, so the
+block composition is "parity unpinned" with respect to the pages themselves.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+F64 = np.float64
+
+
+# ---------------------------------------------------------------------------
+# Number format
+# ---------------------------------------------------------------------------
+
+def bf16_round(x) -> np.ndarray:
+    """Round float64 values to the nearest bfloat16 value, ties to even.
+
+    bfloat16 keeps 8 significant bits (1 implicit + 7 stored) and the fp32
+    exponent range.  For |x| in [2^(e-1), 2^e) the spacing is 2^(e-8); below
+    the smallest normal 2^-126 the spacing stays 2^-133 (subnormals).  Values
+    beyond the largest finite bf16 become inf.  np.rint rounds half to even.
+    """
+    x = np.asarray(x, dtype=F64)
+    out = np.array(x, dtype=F64, copy=True)
+    finite = np.isfinite(x) & (x != 0)
+    xf = x[finite]
+    _, e = np.frexp(xf)                       # xf = m * 2^e, 0.5 <= |m| < 1
+    q = np.ldexp(1.0, np.maximum(e, -125) - 8)
+    r = np.rint(xf / q) * q
+    max_bf16 = (2.0 - 2.0 ** -7) * 2.0 ** 127
+    r = np.where(np.abs(r) > max_bf16, np.copysign(np.inf, r), r)
+    out[finite] = r
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Elementwise and row operations of the block
+# ---------------------------------------------------------------------------
+
+def layer_norm(x, eps: float = 1e-6) -> np.ndarray:
+    """Row LayerNorm without affine: (x - mean) / sqrt(var + eps), biased variance."""
+    x = np.asarray(x, dtype=F64)
+    mean = x.mean(axis=-1, keepdims=True)
+    var = ((x - mean) ** 2).mean(axis=-1, keepdims=True)
+    return (x - mean) / np.sqrt(var + eps)
+
+
+def modulate(y, shift, scale) -> np.ndarray:
+    """adaLN modulation: y * (1 + scale) + shift (per column)."""
+    return np.asarray(y, F64) * (1.0 + np.asarray(scale, F64)) + np.asarray(shift, F64)
+
+
+def silu(x) -> np.ndarray:
+    x = np.asarray(x, F64)
+    return x / (1.0 + np.exp(-x))
+
+
+def gelu_tanh(x) -> np.ndarray:
+    """GELU, tanh approximation: 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3)))."""
+    x = np.asarray(x, F64)
+    return 0.5 * x * (1.0 + np.tanh(math.sqrt(2.0 / math.pi) * (x + 0.044715 * x ** 3)))
+
+
+def gelu_erf(x) -> np.ndarray:
+    """GELU, exact form: x * Phi(x) = 0.5 x (1 + erf(x / sqrt 2))."""
+    from scipy.special import erf
+    x = np.asarray(x, F64)
+    return 0.5 * x * (1.0 + erf(x / math.sqrt(2.0)))
+
+
+def linear(x, w, b=None) -> np.ndarray:
+    """nn.Linear convention: y = x @ w.T + b, w stored [out, in]."""
+    y = np.asarray(x, F64) @ np.asarray(w, F64).T
+    if b is not None:
+        y = y + np.asarray(b, F64)
+    return y
+
+
+def adaln(c, w_ada, b_ada) -> np.ndarray:
+    """Per-layer modulation vector: SiLU(c) @ W_ada.T + b_ada, returned as [6, h]
+    in the order shift1, scale1, gate1, shift2, scale2, gate2."""
+    m = linear(silu(c)[None, :], w_ada, b_ada)[0]
+    return m.reshape(6, -1)
+
+
+# ---------------------------------------------------------------------------
+# Attention over the full-spatial buffer
+# ---------------------------------------------------------------------------
+
+def softmax_rows(s) -> np.ndarray:
+    """Two-pass softmax along the last axis: subtract the row max, exponentiate, normalise."""
+    s = np.asarray(s, F64)
+    e = np.exp(s - s.max(axis=-1, keepdims=True))
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def attention(q, k, v, heads: int, head_dim: int, chunk: int = 256) -> np.ndarray:
+    """Full non-causal multi-head attention of the rows of q over every row of k/v.
+
+    Head j uses columns [j*d, (j+1)*d) of q, k and v.  O_j = softmax(Q_j K_j^T / sqrt(d)) V_j.
+    Query rows are processed in chunks only to bound memory; each row's arithmetic is unchanged.
+    """
+    q = np.asarray(q, F64)
+    k = np.asarray(k, F64)
+    v = np.asarray(v, F64)
+    n = q.shape[0]
+    out = np.empty((n, heads * head_dim), F64)
+    scale = 1.0 / math.sqrt(head_dim)
+    for j in range(heads):
+        cs = slice(j * head_dim, (j + 1) * head_dim)
+        kj = k[:, cs]
+        vj = v[:, cs]
+        for r0 in range(0, n, chunk):
+            r1 = min(n, r0 + chunk)
+            p = softmax_rows((q[r0:r1, cs] @ kj.T) * scale)
+            out[r0:r1, cs] = p @ vj
+    return out
+
+
+# ---------------------------------------------------------------------------
+# KV buffer splice
+# ---------------------------------------------------------------------------
+
+def splice(dst, src, offset: int):
+    """In-place splice of a row block: dst[offset + i, :] = src[i, :] for i < len(src).
+
+    Returns dst (same object).  Rows outside [offset, offset + len(src)) are untouched.
+    Works on any dtype (byte-exact for integer views of bf16 / fp32 data).
+    """
+    n = src.shape[0]
+    if offset < 0 or offset + n > dst.shape[0]:
+        raise ValueError("splice out of range")
+    dst[offset:offset + n, ...] = src
+    return dst
+
+
+# ---------------------------------------------------------------------------
+# One pipeline stage
+# ---------------------------------------------------------------------------
+
+class StageOracle:
+    """L contiguous layers of one stage with their per-layer full-spatial K/V buffers.
+
+    layers: list of dicts with w_qkv [3h,h], b_qkv [3h], w_o [h,h], b_o [h], w1 [rh,h],
+    b1 [rh], w2 [h,rh], b2 [h], w_ada [6h,h], b_ada [6h] (any float dtype).
+    """
+
+    def __init__(self, layers, *, heads: int, head_dim: int, seq_txt: int, seq_img: int,
+                 num_patches: int, mlp_ratio: int, ln_eps: float = 1e-6, gelu: str = "tanh",
+                 mode: str = "exact"):
+        if mode not in ("exact", "bf16"):
+            raise ValueError(mode)
+        if seq_img % num_patches:
+            raise ValueError("seq_img must be a multiple of num_patches")
+        self.W = [{k: np.asarray(a, F64) for k, a in lw.items()} for lw in layers]
+        self.heads, self.head_dim = heads, head_dim
+        self.hidden = heads * head_dim
+        self.seq_txt, self.seq_img, self.num_patches = seq_txt, seq_img, num_patches
+        self.seq_kv = seq_txt + seq_img
+        self.patch_rows = seq_img // num_patches
+        self.mlp_ratio = mlp_ratio
+        self.ln_eps = ln_eps
+        self.gelu = gelu_tanh if gelu == "tanh" else gelu_erf
+        self.mode = mode
+        self.K = [np.zeros((self.seq_kv, self.hidden), F64) for _ in self.W]
+        self.V = [np.zeros((self.seq_kv, self.hidden), F64) for _ in self.W]
+        self.mod = None
+        self.trace = None          # set to a list to record per-layer intermediates
+
+    def _r(self, a):
+        return bf16_round(a) if self.mode == "bf16" else a
+
+    def set_cond(self, c):
+        self.mod = [adaln(c, W["w_ada"], W["b_ada"]) for W in self.W]
+
+    def run_rows(self, offset: int, rows: int, x) -> np.ndarray:
+        """Push buffer rows [offset, offset+rows) through every layer of the stage.
+
+        In each layer the rows' fresh K/V are spliced into the layer's buffer before
+        the rows attend over all seq_kv buffer rows (their own rows are therefore fresh).
+        """
+        if self.mod is None:
+            raise RuntimeError("set_cond first")
+        h, H, d = self.hidden, self.heads, self.head_dim
+        x = np.array(x, F64).reshape(rows, h)
+        for l, W in enumerate(self.W):
+            shift1, scale1, gate1, shift2, scale2, gate2 = self.mod[l]
+            h1 = self._r(modulate(layer_norm(x, self.ln_eps), shift1, scale1))
+            qkv = self._r(linear(h1, W["w_qkv"], W["b_qkv"]))
+            q, k, v = qkv[:, :h], qkv[:, h:2 * h], qkv[:, 2 * h:]
+            splice(self.K[l], k, offset)
+            splice(self.V[l], v, offset)
+            o = self._r(attention(q, self.K[l], self.V[l], H, d))
+            x = x + gate1 * linear(o, W["w_o"], W["b_o"])
+            rec = {"layer": l, "offset": offset, "h1": h1, "qkv": qkv, "o": o, "x_attn": x.copy()}
+            if self.mlp_ratio > 0:
+                h2 = self._r(modulate(layer_norm(x, self.ln_eps), shift2, scale2))
+                u = self._r(self.gelu(linear(h2, W["w1"], W["b1"])))
+                x = x + gate2 * linear(u, W["w2"], W["b2"])
+                rec.update(h2=h2, u=u)
+            rec["x_out"] = x.copy()
+            if self.trace is not None:
+                self.trace.append(rec)
+        return x
+
+    def micro_steps(self, warmup: bool):
+        """(offset, rows) of each micro-step of a step, in execution order."""
+        if warmup:
+            return [(0, self.seq_kv)]
+        out = []
+        if self.seq_txt > 0:
+            out.append((0, self.seq_txt))
+        for m in range(self.num_patches):
+            out.append((self.seq_txt + m * self.patch_rows, self.patch_rows))
+        return out
+
+    def step(self, x_all, c, warmup: bool = False) -> np.ndarray:
+        """One diffusion step of this stage over all seq_kv rows; returns the stage output."""
+        self.set_cond(c)
+        x_all = np.asarray(x_all, F64)
+        out = np.empty((self.seq_kv, self.hidden), F64)
+        for off, n in self.micro_steps(warmup):
+            out[off:off + n] = self.run_rows(off, n, x_all[off:off + n])
+        return out
+
+    def add_noise(self, noise):
+        """Step boundary: every stale K/V value drifts by the given per-layer noise."""
+        for l, (nk, nv) in enumerate(noise):
+            self.K[l] = self._r(self.K[l] + np.asarray(nk, F64))
+            self.V[l] = self._r(self.V[l] + np.asarray(nv, F64))

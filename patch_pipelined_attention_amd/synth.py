@@ -1,0 +1,110 @@
+"""Seeded synthetic inputs shared by the tests, the benchmark and the oracle checks.
+
+This module only draws random numbers and converts storage formats; it holds no
+step of the method.  Recipe (one numpy PCG64 stream per workload, seed from the
+shape table):
+
+1. per layer, in order: W_qkv [3h,h], b_qkv [3h], W_o [h,h], b_o [h],
+   W1 [rh,h], b1 [rh], W2 [h,rh], b2 [h], W_ada [6h,h], b_ada [6h]
+   (all N(0, w_std^2); the MLP entries are skipped when r = 0);
+2. x_all [S_kv, h] ~ N(0, 1), the stage input (kept constant across steps);
+3. c [h] ~ N(0, 1), the conditioning vector;
+4. for each step s >= 1 and each layer: noise_k, noise_v [S_kv, h] ~ N(0, sigma_kv^2),
+   the per-step drift of the stale K/V context.
+
+For bf16 workloads weight matrices are rounded once to bf16 (round to nearest
+even, via torch's dtype conversion) and both the HIP path and the oracle read
+those exact values; biases, x, c and the noise stay fp32.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+
+from .configs import StageShape
+
+WEIGHT_NAMES = ("w_qkv", "b_qkv", "w_o", "b_o", "w1", "b1", "w2", "b2", "w_ada", "b_ada")
+MATRIX_NAMES = ("w_qkv", "w_o", "w1", "w2", "w_ada")
+
+
+def to_bf16_values(a: np.ndarray) -> np.ndarray:
+    """fp32 array -> fp32 array holding the nearest-even bf16 values (torch conversion)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    return t.to(torch.bfloat16).to(torch.float32).numpy()
+
+
+def layer_shapes(h: int, r: int):
+    shapes = {"w_qkv": (3 * h, h), "b_qkv": (3 * h,), "w_o": (h, h), "b_o": (h,),
+              "w1": (r * h, h), "b1": (r * h,), "w2": (h, r * h), "b2": (h,),
+              "w_ada": (6 * h, h), "b_ada": (6 * h,)}
+    return shapes
+
+
+@dataclasses.dataclass
+class StageInputs:
+    shape: StageShape
+    layers: list          # list of dict name -> fp32 ndarray
+    x: np.ndarray         # fp32 [S_kv, h]
+    c: np.ndarray         # fp32 [h]
+    _rng: np.random.Generator
+    _next_step: int = 1
+
+    def next_noise(self):
+        """Noise for the next step (s = 1, 2, ... in order): list of (nk, nv) per layer."""
+        s = self.shape
+        out = []
+        for _ in range(s.num_layers):
+            nk = self._rng.standard_normal((s.seq_kv, s.hidden), dtype=np.float32) * np.float32(s.sigma_kv)
+            nv = self._rng.standard_normal((s.seq_kv, s.hidden), dtype=np.float32) * np.float32(s.sigma_kv)
+            out.append((nk, nv))
+        self._next_step += 1
+        return out
+
+
+def stage_inputs(shape: StageShape, seed: int | None = None) -> StageInputs:
+    rng = np.random.Generator(np.random.PCG64(shape.seed if seed is None else seed))
+    h, r = shape.hidden, shape.mlp_ratio
+    shapes = layer_shapes(h, r)
+    std = np.float32(shape.w_std)
+    layers = []
+    for _ in range(shape.num_layers):
+        lw = {}
+        for name in WEIGHT_NAMES:
+            shp = shapes[name]
+            if r == 0 and name in ("w1", "b1", "w2", "b2"):
+                lw[name] = np.zeros(shp, np.float32)
+                continue
+            a = rng.standard_normal(shp, dtype=np.float32) * std
+            if shape.dtype == "bf16" and name in MATRIX_NAMES:
+                a = to_bf16_values(a)
+            lw[name] = a
+        layers.append(lw)
+    x = rng.standard_normal((shape.seq_kv, h), dtype=np.float32)
+    c = rng.standard_normal((h,), dtype=np.float32)
+    return StageInputs(shape, layers, x, c, rng)
+
+
+def randn(shape, seed: int, std: float = 1.0, bf16: bool = False) -> np.ndarray:
+    """Plain seeded N(0, std^2) array (fp32), optionally rounded to bf16 values."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    a = rng.standard_normal(shape, dtype=np.float32) * np.float32(std)
+    return to_bf16_values(a) if bf16 else a
+
+
+def rand_bits16(shape, seed: int) -> np.ndarray:
+    """Seeded arbitrary 16-bit patterns that are finite bf16 values (for byte-copy tests)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    a = rng.integers(0, 1 << 16, size=shape, dtype=np.uint32).astype(np.uint16)
+    exp_all_ones = (a & 0x7F80) == 0x7F80          # inf/nan patterns -> clear one exponent bit
+    a[exp_all_ones] &= np.uint16(0xBF7F)
+    return a
+
+
+def rand_bits32(shape, seed: int) -> np.ndarray:
+    rng = np.random.Generator(np.random.PCG64(seed))
+    a = rng.integers(0, 1 << 32, size=shape, dtype=np.uint64).astype(np.uint32)
+    bad = (a & 0x7F800000) == 0x7F800000
+    a[bad] &= np.uint32(0xBF7FFFFF)
+    return a

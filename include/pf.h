@@ -1,0 +1,214 @@
+/*
+ * pf.h - C ABI of one pipeline stage of patch-level (PipeFusion-style) DiT
+ * inference on an AMD Instinct MI355X (gfx950).
+ *
+ * The method (PipeFusion technical summaries, gist.science Korean page and French
+ * page, "Core mechanisms"):
+ *   - dual partitioning: a stage owns L contiguous transformer layers, and the token
+ *     sequence is split into M non-overlapping patches that flow through the stage's
+ *     layers one patch at a time (mechanism 1);
+ *   - temporal redundancy: attention in step T uses stale step-(T+1) activations as
+ *     context for the rows not yet recomputed, instead of waiting for fresh ones
+ *     (mechanism 2);
+ *   - memory: the stage keeps full-spatial K and V only for its own layers, one buffer
+ *     per layer (mechanism 4);
+ *   - the DiT keeps full attention over the whole image (Key contributions).
+ *
+ * Conventions shared by every call:
+ *   - All pointers named "device" are device memory of the current HIP device and must
+ *     be 16-byte aligned.  Row strides ("ld") are in elements and must keep every row
+ *     16-byte aligned.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Every call only
+ *     enqueues work on that stream and returns; no call synchronises the host.
+ *   - Every argument is validated before anything is enqueued: a call that returns an
+ *     error has enqueued nothing and written nothing.  pf_last_error() then describes
+ *     the failure.  Errors are status codes; nothing aborts or throws across the ABI.
+ *   - A device fault shows up on the caller's next synchronisation; after a failed HIP
+ *     call a stage returns PF_ERR_HIP from every later call.
+ *   - One stage object is used from one stream at a time; there is no internal locking.
+ *   - bf16 is bfloat16 (round to nearest even on every fp32 -> bf16 conversion).  bf16
+ *     contractions accumulate in fp32; softmax statistics are fp32; the residual stream
+ *     and the stage's input/output rows are fp32.
+ */
+#ifndef PF_H
+#define PF_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pf_status {
+  PF_OK = 0,
+  PF_ERR_INVALID_ARG = 1,   /* a pointer, size, stride or range is invalid            */
+  PF_ERR_UNSUPPORTED = 2,   /* valid but not implemented (e.g. head_dim 96, not gfx950) */
+  PF_ERR_OOM = 3,           /* device allocation failed                                */
+  PF_ERR_STATE = 4,         /* call order violated (weights or condition not set)      */
+  PF_ERR_HIP = 5            /* a HIP runtime call failed                               */
+} pf_status;
+
+typedef enum pf_dtype { PF_BF16 = 0, PF_FP32 = 1 } pf_dtype;
+typedef enum pf_gelu { PF_GELU_TANH = 0, PF_GELU_ERF = 1 } pf_gelu;
+
+/* Row layout of a K or V buffer.
+ *   PF_LAYOUT_ROWS: element (r, c) at r * ld + c.
+ *   PF_LAYOUT_K8:   rows are interleaved in groups of 8: element (r, c) at
+ *                   ((r / 8) * row_elems + c) * 8 + (r % 8).  A row range [8a, 8b) is one
+ *                   contiguous block; 8 consecutive rows of one column are 16 contiguous
+ *                   bytes (the operand order of the attention kernel's P.V product).
+ *                   `ld` is ignored and storage covers ceil(rows / 8) * 8 rows. */
+typedef enum pf_layout { PF_LAYOUT_ROWS = 0, PF_LAYOUT_K8 = 1 } pf_layout;
+
+/* Epilogues of pf_gemm (y = a . w^T + bias, a [m,k], w [n,k], y [m,n]). */
+typedef enum pf_epilogue {
+  PF_EPI_STORE = 0,          /* c[i,j] = y (stored in `dtype`)                          */
+  PF_EPI_GELU_TANH = 1,      /* c[i,j] = gelu_tanh(y)                                    */
+  PF_EPI_GELU_ERF = 2,       /* c[i,j] = gelu_erf(y)                                     */
+  PF_EPI_GATED_RESIDUAL = 3  /* c[i,j] += gate[j] * y, c is fp32 (the residual stream)  */
+} pf_epilogue;
+
+#define PF_STEP_WARMUP 1u    /* stage_run_step flag: run all buffer rows as one patch */
+
+typedef struct pf_stage_config {
+  int32_t num_layers;   /* L >= 1: contiguous layers owned by this stage                   */
+  int32_t hidden;       /* h = heads * head_dim                                             */
+  int32_t heads;        /* H >= 1                                                           */
+  int32_t head_dim;     /* d in {64, 72, 128}                                               */
+  int32_t mlp_ratio;    /* r >= 0; 0 = attention sublayer only                              */
+  int32_t num_patches;  /* M >= 1; seq_img % M == 0                                         */
+  int64_t seq_img;      /* image rows, >= 1                                                 */
+  int64_t seq_txt;      /* text-prefix rows (>= 0), kept at buffer rows [0, seq_txt)        */
+  int32_t dtype;        /* pf_dtype of weights, activations and KV buffers                  */
+  int32_t gelu;         /* pf_gelu of the MLP                                               */
+  float ln_eps;         /* LayerNorm epsilon (1e-6 is the DiT value)                        */
+  uint32_t flags;       /* reserved, must be 0                                              */
+} pf_stage_config;
+
+/* One layer's parameters, all device pointers, weights in the stage dtype, row-major
+ * [out, in] (nn.Linear layout), biases fp32.  W_qkv rows are Q (0..h), K (h..2h),
+ * V (2h..3h); head j owns columns [j*d, (j+1)*d) of each.  W_ada rows are the six
+ * modulation vectors shift1, scale1, gate1, shift2, scale2, gate2 (h rows each).
+ * w1/b1/w2/b2 may be NULL when mlp_ratio == 0. */
+typedef struct pf_layer_weights {
+  const void* w_qkv;  const float* b_qkv;   /* [3h, h], [3h]   */
+  const void* w_o;    const float* b_o;     /* [h, h],  [h]    */
+  const void* w1;     const float* b1;      /* [rh, h], [rh]   */
+  const void* w2;     const float* b2;      /* [h, rh], [h]    */
+  const void* w_ada;  const float* b_ada;   /* [6h, h], [6h]   */
+} pf_layer_weights;
+
+/* A pair of K and V row buffers (device memory). */
+typedef struct pf_kv_view {
+  void* k;
+  void* v;
+  int64_t rows;        /* logical rows                                          */
+  int64_t row_elems;   /* elements per row                                      */
+  int64_t k_ld;        /* K row stride in elements (K is always PF_LAYOUT_ROWS)  */
+  int64_t v_ld;        /* V row stride in elements when v_layout == ROWS        */
+  int32_t dtype;       /* pf_dtype                                              */
+  int32_t v_layout;    /* pf_layout of V                                        */
+} pf_kv_view;
+
+typedef struct pf_stage pf_stage;
+
+/* Create a stage on the current HIP device (must be gfx950).  Allocates, once, all
+ * device memory the stage uses: the L layers' weights, the L per-layer K/V buffers of
+ * seq_txt + seq_img rows (one copy, updated in place: the stage keeps full-spatial K/V
+ * for its own layers only, PipeFusion mechanism 4), and scratch for seq_txt + seq_img
+ * rows.  bf16 stages keep V in PF_LAYOUT_K8, fp32 stages in PF_LAYOUT_ROWS.  Buffers
+ * start zeroed.  Requires h = H * d, d in {64,72,128}, h % 64 == 0 for bf16,
+ * seq_img % num_patches == 0.  Errors: INVALID_ARG, UNSUPPORTED, OOM, HIP; nothing is
+ * allocated on failure.  *out receives the stage. */
+pf_status stage_create(const pf_stage_config* cfg, pf_stage** out);
+
+/* Free everything the stage owns.  The caller synchronises its stream first.  NULL is a
+ * no-op. */
+pf_status stage_destroy(pf_stage* st);
+
+/* Copy layer `layer`'s parameters (device pointers, see pf_layer_weights) into memory
+ * the stage owns (stream-ordered device-to-device copies).  The caller may release its
+ * copies once the stream has passed this call.  Every layer must be loaded before any
+ * run call (else PF_ERR_STATE). */
+pf_status stage_load_weights(pf_stage* st, int32_t layer, const pf_layer_weights* w, void* stream);
+
+/* Compute every layer's adaLN modulation from the conditioning vector `cond` (device,
+ * fp32 [h]): mod_l = SiLU(cond) . W_ada,l^T + b_ada,l, kept by the stage for later
+ * stage_run_patch calls of this diffusion step. */
+pf_status stage_set_cond(pf_stage* st, const float* cond, void* stream);
+
+/* One micro-step: push buffer rows [row_off, row_off + rows) through all L layers
+ * (PipeFusion mechanism 1: one patch through the stage's contiguous layers).  In each
+ * layer: LayerNorm + modulation, QKV projection, in-place splice of the rows' fresh K/V
+ * into the layer's buffer, full attention of the rows' queries over all seq_txt +
+ * seq_img buffer rows (rows not yet recomputed this step hold stale values from the
+ * previous step, mechanism 2), output projection with gated residual, and (r > 0) the
+ * modulated GELU MLP with gated residual.
+ * x_in / x_out: device fp32 [rows, h] (x_out may equal x_in; otherwise they must not
+ * overlap).  Requires 0 <= row_off, rows >= 1, row_off + rows <= seq_txt + seq_img,
+ * weights loaded and stage_set_cond called. */
+pf_status stage_run_patch(pf_stage* st, int64_t row_off, int64_t rows, const float* x_in,
+                          float* x_out, void* stream);
+
+/* One diffusion step over all seq_txt + seq_img rows: stage_set_cond(cond), then
+ *   with PF_STEP_WARMUP: stage_run_patch(0, seq_txt + seq_img)  (start-up: every buffer
+ *                        row is computed fresh, so the pipeline has no stale context yet);
+ *   otherwise:           stage_run_patch(0, seq_txt) if seq_txt > 0, then
+ *                        stage_run_patch(seq_txt + m*P, P) for m = 0 .. M-1, P = seq_img/M.
+ * x_in / x_out: device fp32 [seq_txt + seq_img, h], x_out may equal x_in. */
+pf_status stage_run_step(pf_stage* st, const float* x_in, float* x_out, const float* cond,
+                         uint32_t flags, void* stream);
+
+/* Bit copy of a row block into a K/V buffer pair:
+ *   for i < len, c < row_elems:  dst.K(offset + i, c) = src.K(i, c), same for V,
+ * each view addressed through its own layout.  No other byte of dst changes.  len == 0
+ * is a no-op.  Requires equal dtype and row_elems, 0 <= offset, offset + len <= dst.rows,
+ * len <= src.rows, and src/dst not overlapping.  Needs no stage.  This is the update that
+ * makes a layer's buffer hold fresh rows for the current patch and the previous step's
+ * values elsewhere (PipeFusion mechanism 2). */
+pf_status kvbuf_splice(const pf_kv_view* dst, const pf_kv_view* src, int64_t offset, int64_t len,
+                       void* stream);
+
+/* Describe layer `layer`'s K/V buffer (owned by the stage; valid until stage_destroy). */
+pf_status stage_get_kvbuf(pf_stage* st, int32_t layer, pf_kv_view* out);
+
+/* Thread-local text of the last non-OK status returned on this thread. */
+const char* pf_last_error(void);
+
+/* ---------------------------------------------------------------------------------
+ * Component entry points: each runs one of the stage's kernels on its own.  The stage
+ * calls the same kernels; these exist so each kernel can be checked and timed alone.
+ * --------------------------------------------------------------------------------- */
+
+/* y[i, :] = LayerNorm(x[i, :]) * (1 + scale) + shift for i < rows; LayerNorm without
+ * affine, biased variance, fp32 statistics.  x fp32 [rows, hidden] (row stride hidden),
+ * shift/scale fp32 [hidden], y [rows, hidden] in `dtype`. */
+pf_status pf_ln_modulate(const float* x, int64_t rows, int32_t hidden, const float* shift,
+                         const float* scale, float eps, void* y, int32_t dtype, void* stream);
+
+/* y = a . w^T + bias with a [m, k] (row stride lda), w [n, k] (row-major), bias fp32 [n],
+ * then the epilogue `epi` (pf_epilogue) into c (row stride ldc).  a/w/c in `dtype`, except
+ * c is fp32 for PF_EPI_GATED_RESIDUAL (gate fp32 [n]).  fp32 accumulation.  For bf16:
+ * n % 64 == 0 and k % 64 == 0. */
+pf_status pf_gemm(const void* a, int64_t lda, const void* w, const float* bias, int64_t m,
+                  int64_t n, int64_t k, int32_t epi, void* c, int64_t ldc, const float* gate,
+                  int32_t dtype, void* stream);
+
+/* Full non-causal attention of `rows` query rows over the first seq_kv rows of kv:
+ * for head j (columns [j*d, (j+1)*d)): O_j = softmax(Q_j K_j^T / sqrt(d)) V_j.
+ * q [rows, heads*head_dim] (row stride ldq), o [rows, heads*head_dim] (row stride ldo),
+ * both in kv->dtype.  bf16 requires kv->v_layout == PF_LAYOUT_K8, fp32 PF_LAYOUT_ROWS. */
+pf_status pf_attention(const void* q, int64_t ldq, const pf_kv_view* kv, int64_t seq_kv,
+                       int64_t rows, int32_t heads, int32_t head_dim, void* o, int64_t ldo,
+                       void* stream);
+
+/* mod = SiLU(cond) . w_ada^T + b_ada: cond fp32 [hidden], w_ada [6*hidden, hidden] in
+ * `dtype`, b_ada fp32 [6*hidden], mod fp32 [6*hidden]. */
+pf_status pf_adaln(const float* cond, const void* w_ada, const float* b_ada, int32_t hidden,
+                   float* mod, int32_t dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PF_H */

@@ -214,11 +214,13 @@ class StageOracle:
     def set_cond(self, c):
         self.mod = [adaln(c, W["w_ada"], W["b_ada"]) for W in self.W]
 
-    def run_rows(self, offset: int, rows: int, x) -> np.ndarray:
+    def run_rows(self, offset: int, rows: int, x, sample=None) -> np.ndarray:
         """Push buffer rows [offset, offset+rows) through every layer of the stage.
 
         In each layer the rows' fresh K/V are spliced into the layer's buffer before
         the rows attend over all seq_kv buffer rows (their own rows are therefore fresh).
+        `sample` (indices into the rows) limits the last layer's attention and MLP to
+        those rows and returns only their outputs; every buffer update is still complete.
         """
         if self.mod is None:
             raise RuntimeError("set_cond first")
@@ -231,6 +233,8 @@ class StageOracle:
             q, k, v = qkv[:, :h], qkv[:, h:2 * h], qkv[:, 2 * h:]
             splice(self.K[l], k, offset)
             splice(self.V[l], v, offset)
+            if sample is not None and l == len(self.W) - 1:
+                q, x, qkv, h1 = q[sample], x[sample], qkv[sample], h1[sample]
             o = self._r(attention(q, self.K[l], self.V[l], H, d))
             x = x + gate1 * linear(o, W["w_o"], W["b_o"])
             rec = {"layer": l, "offset": offset, "h1": h1, "qkv": qkv, "o": o, "x_attn": x.copy()}
@@ -262,6 +266,19 @@ class StageOracle:
         out = np.empty((self.seq_kv, self.hidden), F64)
         for off, n in self.micro_steps(warmup):
             out[off:off + n] = self.run_rows(off, n, x_all[off:off + n])
+        return out
+
+    def step_sampled(self, x_all, c, rows_global, warmup: bool = False) -> np.ndarray:
+        """Like step(), but returns only the outputs of the given buffer rows (sorted,
+        unique); the buffers end in the same state as after step()."""
+        self.set_cond(c)
+        x_all = np.asarray(x_all, F64)
+        rows_global = np.asarray(rows_global)
+        out = np.empty((len(rows_global), self.hidden), F64)
+        for off, n in self.micro_steps(warmup):
+            sel = np.nonzero((rows_global >= off) & (rows_global < off + n))[0]
+            res = self.run_rows(off, n, x_all[off:off + n], sample=rows_global[sel] - off)
+            out[sel] = res
         return out
 
     def add_noise(self, noise):

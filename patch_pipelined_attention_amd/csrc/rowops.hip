@@ -1,0 +1,138 @@
+// Row kernels of the DiT block: LayerNorm + adaLN modulation, and the adaLN GEMV.
+// Both are HBM-bound: one pass over the input rows / weight rows, 16-byte accesses,
+// fp32 statistics and accumulation.
+#include "pf_internal.h"
+
+namespace pf {
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// ---------------------------------------------------------------------------------
+// y = LayerNorm(x) * (1 + scale) + shift, one wavefront per row.  The row is held in
+// registers (float4 per lane and slot), so x is read once.  mean and variance are the
+// two-pass fp32 statistics of the row (biased variance), no affine.
+// ---------------------------------------------------------------------------------
+template <typename OutT>
+__global__ __launch_bounds__(256) void ln_modulate_kernel(const float* __restrict__ x, int64_t rows,
+                                                          int hidden, const float* __restrict__ shift,
+                                                          const float* __restrict__ scale, float eps,
+                                                          OutT* __restrict__ y) {
+  constexpr int kSlots = kMaxHidden / 256;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int n4 = hidden >> 2;
+  const float4* xr = reinterpret_cast<const float4*>(x + row * hidden);
+  float4 v[kSlots];
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < kSlots; ++i) {
+    const int idx = lane + i * 64;
+    if (idx < n4) {
+      v[i] = xr[idx];
+      sum += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+    }
+  }
+  const float inv_h = 1.0f / (float)hidden;
+  const float mean = wave_sum(sum) * inv_h;
+  float sq = 0.f;
+#pragma unroll
+  for (int i = 0; i < kSlots; ++i) {
+    const int idx = lane + i * 64;
+    if (idx < n4) {
+      const float a = v[i].x - mean, b = v[i].y - mean, c = v[i].z - mean, d = v[i].w - mean;
+      sq += (a * a + b * b) + (c * c + d * d);
+    }
+  }
+  const float var = wave_sum(sq) * inv_h;
+  const float rstd = 1.0f / sqrtf(var + eps);
+  const float4* sh4 = reinterpret_cast<const float4*>(shift);
+  const float4* sc4 = reinterpret_cast<const float4*>(scale);
+#pragma unroll
+  for (int i = 0; i < kSlots; ++i) {
+    const int idx = lane + i * 64;
+    if (idx < n4) {
+      const float4 sh = sh4[idx], sc = sc4[idx];
+      float o0 = (v[i].x - mean) * rstd * (1.0f + sc.x) + sh.x;
+      float o1 = (v[i].y - mean) * rstd * (1.0f + sc.y) + sh.y;
+      float o2 = (v[i].z - mean) * rstd * (1.0f + sc.z) + sh.z;
+      float o3 = (v[i].w - mean) * rstd * (1.0f + sc.w) + sh.w;
+      if constexpr (sizeof(OutT) == 2) {
+        bf16x4 o = {(bf16)o0, (bf16)o1, (bf16)o2, (bf16)o3};
+        *reinterpret_cast<bf16x4*>(y + row * hidden + idx * 4) = o;
+      } else {
+        *reinterpret_cast<float4*>(y + row * hidden + idx * 4) = make_float4(o0, o1, o2, o3);
+      }
+    }
+  }
+}
+
+hipError_t launch_ln_modulate(const float* x, int64_t rows, int hidden, const float* shift,
+                              const float* scale, float eps, void* y, int dtype, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  dim3 grid((unsigned)((rows + 3) / 4));
+  if (dtype == kDtypeBF16)
+    hipLaunchKernelGGL(ln_modulate_kernel<bf16>, grid, dim3(256), 0, s, x, rows, hidden, shift, scale,
+                       eps, static_cast<bf16*>(y));
+  else
+    hipLaunchKernelGGL(ln_modulate_kernel<float>, grid, dim3(256), 0, s, x, rows, hidden, shift, scale,
+                       eps, static_cast<float*>(y));
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------
+// mod[j] = sum_i SiLU(c[i]) * W[j, i] + b[j] for j < 6h.  SiLU(c) is staged in LDS
+// once per block; one wavefront per output row streams that row of W with 16-byte loads.
+// ---------------------------------------------------------------------------------
+template <typename WT>
+__global__ __launch_bounds__(256) void adaln_kernel(const float* __restrict__ cond,
+                                                    const WT* __restrict__ w,
+                                                    const float* __restrict__ b, int hidden,
+                                                    int n_out, float* __restrict__ mod) {
+  extern __shared__ float s_act[];
+  for (int i = threadIdx.x; i < hidden; i += 256) {
+    const float c = cond[i];
+    s_act[i] = c / (1.0f + expf(-c));
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  for (int row = blockIdx.x * 4 + (threadIdx.x >> 6); row < n_out; row += gridDim.x * 4) {
+    const WT* wr = w + (int64_t)row * hidden;
+    float acc = 0.f;
+    for (int k = lane * 8; k < hidden; k += 512) {
+      if constexpr (sizeof(WT) == 2) {
+        const bf16x8 wv = *reinterpret_cast<const bf16x8*>(wr + k);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc += (float)wv[e] * s_act[k + e];
+      } else {
+        const float4 w0 = *reinterpret_cast<const float4*>(wr + k);
+        const float4 w1 = *reinterpret_cast<const float4*>(wr + k + 4);
+        acc += w0.x * s_act[k] + w0.y * s_act[k + 1] + w0.z * s_act[k + 2] + w0.w * s_act[k + 3];
+        acc += w1.x * s_act[k + 4] + w1.y * s_act[k + 5] + w1.z * s_act[k + 6] + w1.w * s_act[k + 7];
+      }
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) mod[row] = acc + b[row];
+  }
+}
+
+hipError_t launch_adaln(const float* cond, const void* w, const float* b, int hidden, float* mod,
+                        int dtype, hipStream_t s) {
+  const int n_out = 6 * hidden;
+  int blocks = (n_out + 3) / 4;
+  if (blocks > 2048) blocks = 2048;
+  const size_t lds = sizeof(float) * (size_t)hidden;
+  if (dtype == kDtypeBF16)
+    hipLaunchKernelGGL(adaln_kernel<bf16>, dim3(blocks), dim3(256), lds, s, cond,
+                       static_cast<const bf16*>(w), b, hidden, n_out, mod);
+  else
+    hipLaunchKernelGGL(adaln_kernel<float>, dim3(blocks), dim3(256), lds, s, cond,
+                       static_cast<const float*>(w), b, hidden, n_out, mod);
+  return hipGetLastError();
+}
+
+}  // namespace pf

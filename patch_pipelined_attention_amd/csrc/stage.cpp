@@ -1,0 +1,567 @@
+// Stage runtime and C ABI of libpf (declarations and contracts in include/pf.h).
+//
+// One pf_stage is one GPU's share of a PipeFusion pipeline (technical summaries on
+// gist.science, "Core mechanisms" 1, 2 and 4): the weights of L contiguous layers, one
+// full-spatial K/V buffer per layer (a single copy, updated in place), and scratch for a
+// micro-step of up to seq_txt + seq_img rows.  Every call validates its arguments before
+// enqueuing anything, then enqueues kernels on the caller's stream and returns.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "pf.h"
+#include "pf_internal.h"
+
+using namespace pf;
+
+// ------------------------------------------------------------------------------------
+// errors
+// ------------------------------------------------------------------------------------
+static thread_local std::string g_last_error;
+
+static pf_status fail(pf_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+static pf_status hip_fail(hipError_t e, const char* what) {
+  return fail(PF_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+extern "C" const char* pf_last_error(void) { return g_last_error.c_str(); }
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+static size_t dtype_size(int dt) { return dt == PF_BF16 ? 2 : 4; }
+static bool dtype_ok(int dt) { return dt == PF_BF16 || dt == PF_FP32; }
+
+// The kernels are built for gfx950 only.
+static pf_status check_device() {
+  static thread_local int checked_dev = -1;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev == checked_dev) return PF_OK;
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(PF_ERR_UNSUPPORTED, "device %d is %s; libpf is built for gfx950 only", dev, prop.gcnArchName);
+  checked_dev = dev;
+  return PF_OK;
+}
+
+// ------------------------------------------------------------------------------------
+// component validation helpers (pure host checks: no HIP call)
+// ------------------------------------------------------------------------------------
+static pf_status validate_ln(const float* x, int64_t rows, int32_t hidden, const float* shift,
+                             const float* scale, void* y, int32_t dtype) {
+  if (!dtype_ok(dtype)) return fail(PF_ERR_INVALID_ARG, "ln_modulate: bad dtype %d", dtype);
+  if (rows < 0) return fail(PF_ERR_INVALID_ARG, "ln_modulate: rows < 0");
+  if (hidden <= 0 || hidden % 8 != 0 || hidden > kMaxHidden)
+    return fail(PF_ERR_UNSUPPORTED, "ln_modulate: hidden %d must be a positive multiple of 8 <= %d", hidden,
+                kMaxHidden);
+  if (!x || !shift || !scale || !y) return fail(PF_ERR_INVALID_ARG, "ln_modulate: null pointer");
+  if (!aligned16(x) || !aligned16(shift) || !aligned16(scale) || !aligned16(y))
+    return fail(PF_ERR_INVALID_ARG, "ln_modulate: pointers must be 16-byte aligned");
+  return PF_OK;
+}
+
+static pf_status validate_gemm(const void* a, int64_t lda, const void* w, const float* bias, int64_t m,
+                               int64_t n, int64_t k, int32_t epi, void* c, int64_t ldc, const float* gate,
+                               int32_t dtype) {
+  if (!dtype_ok(dtype)) return fail(PF_ERR_INVALID_ARG, "gemm: bad dtype %d", dtype);
+  if (epi < PF_EPI_STORE || epi > PF_EPI_GATED_RESIDUAL) return fail(PF_ERR_INVALID_ARG, "gemm: bad epilogue %d", epi);
+  if (m < 0 || n <= 0 || k <= 0) return fail(PF_ERR_INVALID_ARG, "gemm: bad sizes m=%lld n=%lld k=%lld",
+                                             (long long)m, (long long)n, (long long)k);
+  if (!a || !w || !bias || !c || (epi == PF_EPI_GATED_RESIDUAL && !gate))
+    return fail(PF_ERR_INVALID_ARG, "gemm: null pointer");
+  if (lda < k || ldc < n) return fail(PF_ERR_INVALID_ARG, "gemm: lda < k or ldc < n");
+  if (!aligned16(a) || !aligned16(w) || !aligned16(bias) || !aligned16(c) || (gate && !aligned16(gate)))
+    return fail(PF_ERR_INVALID_ARG, "gemm: pointers must be 16-byte aligned");
+  if (dtype == PF_BF16) {
+    if (n % 64 != 0 || k % 64 != 0)
+      return fail(PF_ERR_UNSUPPORTED, "gemm: bf16 needs n %% 64 == 0 and k %% 64 == 0 (n=%lld k=%lld)",
+                  (long long)n, (long long)k);
+    if (lda % 8 != 0 || ldc % 4 != 0) return fail(PF_ERR_INVALID_ARG, "gemm: bf16 needs lda %% 8 == 0, ldc %% 4 == 0");
+  }
+  return PF_OK;
+}
+
+static pf_status validate_kv_view(const pf_kv_view* v, const char* who) {
+  if (!v) return fail(PF_ERR_INVALID_ARG, "%s: null view", who);
+  if (!dtype_ok(v->dtype)) return fail(PF_ERR_INVALID_ARG, "%s: bad view dtype", who);
+  if (v->v_layout != PF_LAYOUT_ROWS && v->v_layout != PF_LAYOUT_K8)
+    return fail(PF_ERR_INVALID_ARG, "%s: bad v_layout", who);
+  if (v->rows < 0 || v->row_elems <= 0) return fail(PF_ERR_INVALID_ARG, "%s: bad view rows/row_elems", who);
+  if (!v->k || !v->v) return fail(PF_ERR_INVALID_ARG, "%s: null K or V pointer", who);
+  if (v->k_ld < v->row_elems) return fail(PF_ERR_INVALID_ARG, "%s: k_ld < row_elems", who);
+  if (v->v_layout == PF_LAYOUT_ROWS && v->v_ld < v->row_elems)
+    return fail(PF_ERR_INVALID_ARG, "%s: v_ld < row_elems", who);
+  return PF_OK;
+}
+
+// byte extent [lo, hi) of the K or V matrix of a view (rows covered by the view)
+static void view_extent(const pf_kv_view* v, bool is_v, int64_t r0, int64_t n, uintptr_t* lo, uintptr_t* hi) {
+  const size_t es = dtype_size(v->dtype);
+  if (n <= 0) { *lo = *hi = 0; return; }
+  if (is_v && v->v_layout == PF_LAYOUT_K8) {
+    const int64_t g0 = r0 / 8, g1 = (r0 + n - 1) / 8 + 1;
+    *lo = (uintptr_t)v->v + (uintptr_t)(g0 * v->row_elems * 8 * es);
+    *hi = (uintptr_t)v->v + (uintptr_t)(g1 * v->row_elems * 8 * es);
+  } else {
+    const int64_t ld = is_v ? v->v_ld : v->k_ld;
+    const char* base = (const char*)(is_v ? v->v : v->k);
+    *lo = (uintptr_t)base + (uintptr_t)(r0 * ld * es);
+    *hi = (uintptr_t)base + (uintptr_t)(((r0 + n - 1) * ld + v->row_elems) * es);
+  }
+}
+
+static pf_status validate_splice(const pf_kv_view* dst, const pf_kv_view* src, int64_t offset, int64_t len) {
+  pf_status st = validate_kv_view(dst, "kvbuf_splice(dst)");
+  if (st != PF_OK) return st;
+  st = validate_kv_view(src, "kvbuf_splice(src)");
+  if (st != PF_OK) return st;
+  if (dst->dtype != src->dtype) return fail(PF_ERR_INVALID_ARG, "kvbuf_splice: dtype mismatch");
+  if (dst->row_elems != src->row_elems) return fail(PF_ERR_INVALID_ARG, "kvbuf_splice: row_elems mismatch");
+  if (offset < 0 || len < 0) return fail(PF_ERR_INVALID_ARG, "kvbuf_splice: negative offset or len");
+  if (offset + len > dst->rows) return fail(PF_ERR_INVALID_ARG, "kvbuf_splice: offset + len > dst.rows");
+  if (len > src->rows) return fail(PF_ERR_INVALID_ARG, "kvbuf_splice: len > src.rows");
+  const size_t es = dtype_size(dst->dtype);
+  if (!aligned16(dst->k) || !aligned16(dst->v) || (es == 4 && (((uintptr_t)src->k | (uintptr_t)src->v) & 3)) ||
+      (es == 2 && (((uintptr_t)src->k | (uintptr_t)src->v) & 1)))
+    return fail(PF_ERR_INVALID_ARG, "kvbuf_splice: misaligned pointer");
+  if (len == 0) return PF_OK;
+  for (int a = 0; a < 2; ++a)
+    for (int b = 0; b < 2; ++b) {
+      uintptr_t dlo, dhi, slo, shi;
+      view_extent(dst, a == 1, offset, len, &dlo, &dhi);
+      view_extent(src, b == 1, 0, len, &slo, &shi);
+      if (dlo < shi && slo < dhi) return fail(PF_ERR_INVALID_ARG, "kvbuf_splice: src and dst overlap");
+    }
+  return PF_OK;
+}
+
+static pf_status validate_attention(const void* q, int64_t ldq, const pf_kv_view* kv, int64_t seq_kv,
+                                    int64_t rows, int32_t heads, int32_t head_dim, void* o, int64_t ldo) {
+  pf_status st = validate_kv_view(kv, "attention");
+  if (st != PF_OK) return st;
+  if (head_dim != 64 && head_dim != 72 && head_dim != 128)
+    return fail(PF_ERR_UNSUPPORTED, "attention: head_dim %d not in {64, 72, 128}", head_dim);
+  if (heads <= 0) return fail(PF_ERR_INVALID_ARG, "attention: heads <= 0");
+  const int64_t h = (int64_t)heads * head_dim;
+  if (kv->row_elems != h) return fail(PF_ERR_INVALID_ARG, "attention: kv row_elems != heads*head_dim");
+  if (seq_kv < 1 || seq_kv > kv->rows) return fail(PF_ERR_INVALID_ARG, "attention: seq_kv out of range");
+  if (rows < 0) return fail(PF_ERR_INVALID_ARG, "attention: rows < 0");
+  if (!q || !o) return fail(PF_ERR_INVALID_ARG, "attention: null pointer");
+  if (ldq < h || ldo < h) return fail(PF_ERR_INVALID_ARG, "attention: ldq/ldo < heads*head_dim");
+  if (!aligned16(q) || !aligned16(o) || !aligned16(kv->k) || !aligned16(kv->v))
+    return fail(PF_ERR_INVALID_ARG, "attention: pointers must be 16-byte aligned");
+  if (kv->dtype == PF_BF16) {
+    if (kv->v_layout != PF_LAYOUT_K8) return fail(PF_ERR_UNSUPPORTED, "attention: bf16 needs V in PF_LAYOUT_K8");
+    if (ldq % 8 || ldo % 4 || kv->k_ld % 8) return fail(PF_ERR_INVALID_ARG, "attention: bf16 strides must keep 16 B rows");
+    if (seq_kv * (int64_t)heads > (int64_t)1 << 40) return fail(PF_ERR_UNSUPPORTED, "attention: too large");
+  } else {
+    if (kv->v_layout != PF_LAYOUT_ROWS) return fail(PF_ERR_UNSUPPORTED, "attention: fp32 needs V in PF_LAYOUT_ROWS");
+  }
+  const int64_t tiles = (rows + 127) / 128 * heads;
+  if (tiles > 0x7fffffff) return fail(PF_ERR_UNSUPPORTED, "attention: grid too large");
+  return PF_OK;
+}
+
+// ------------------------------------------------------------------------------------
+// component entry points
+// ------------------------------------------------------------------------------------
+extern "C" pf_status pf_ln_modulate(const float* x, int64_t rows, int32_t hidden, const float* shift,
+                                    const float* scale, float eps, void* y, int32_t dtype, void* stream) {
+  pf_status st = validate_ln(x, rows, hidden, shift, scale, y, dtype);
+  if (st != PF_OK) return st;
+  if ((st = check_device()) != PF_OK) return st;
+  hipError_t e = launch_ln_modulate(x, rows, hidden, shift, scale, eps, y, dtype, (hipStream_t)stream);
+  return e == hipSuccess ? PF_OK : hip_fail(e, "ln_modulate launch");
+}
+
+extern "C" pf_status pf_gemm(const void* a, int64_t lda, const void* w, const float* bias, int64_t m, int64_t n,
+                             int64_t k, int32_t epi, void* c, int64_t ldc, const float* gate, int32_t dtype,
+                             void* stream) {
+  pf_status st = validate_gemm(a, lda, w, bias, m, n, k, epi, c, ldc, gate, dtype);
+  if (st != PF_OK) return st;
+  if ((st = check_device()) != PF_OK) return st;
+  hipError_t e = launch_gemm(a, lda, w, bias, m, n, k, epi, c, ldc, gate, dtype, (hipStream_t)stream);
+  return e == hipSuccess ? PF_OK : hip_fail(e, "gemm launch");
+}
+
+extern "C" pf_status pf_attention(const void* q, int64_t ldq, const pf_kv_view* kv, int64_t seq_kv, int64_t rows,
+                                  int32_t heads, int32_t head_dim, void* o, int64_t ldo, void* stream) {
+  pf_status st = validate_attention(q, ldq, kv, seq_kv, rows, heads, head_dim, o, ldo);
+  if (st != PF_OK) return st;
+  if ((st = check_device()) != PF_OK) return st;
+  hipError_t e = launch_attention(q, ldq, kv->k, kv->k_ld, kv->v, kv->v_ld, kv->v_layout, kv->row_elems, seq_kv,
+                                  rows, heads, head_dim, o, ldo, kv->dtype, (hipStream_t)stream);
+  return e == hipSuccess ? PF_OK : hip_fail(e, "attention launch");
+}
+
+extern "C" pf_status pf_adaln(const float* cond, const void* w_ada, const float* b_ada, int32_t hidden, float* mod,
+                              int32_t dtype, void* stream) {
+  if (!dtype_ok(dtype)) return fail(PF_ERR_INVALID_ARG, "adaln: bad dtype");
+  if (hidden <= 0 || hidden % 8 != 0 || hidden > 16384)
+    return fail(PF_ERR_UNSUPPORTED, "adaln: hidden must be a positive multiple of 8 <= 16384");
+  if (!cond || !w_ada || !b_ada || !mod) return fail(PF_ERR_INVALID_ARG, "adaln: null pointer");
+  if (!aligned16(w_ada)) return fail(PF_ERR_INVALID_ARG, "adaln: w_ada must be 16-byte aligned");
+  pf_status st = check_device();
+  if (st != PF_OK) return st;
+  hipError_t e = launch_adaln(cond, w_ada, b_ada, hidden, mod, dtype, (hipStream_t)stream);
+  return e == hipSuccess ? PF_OK : hip_fail(e, "adaln launch");
+}
+
+static hipError_t splice_views(const pf_kv_view* dst, const pf_kv_view* src, int64_t offset, int64_t len,
+                               hipStream_t s) {
+  KVDesc d[2] = {{dst->k, dst->k_ld, PF_LAYOUT_ROWS}, {dst->v, dst->v_ld, dst->v_layout}};
+  KVDesc sr[2] = {{src->k, src->k_ld, PF_LAYOUT_ROWS}, {src->v, src->v_ld, src->v_layout}};
+  return launch_splice(d, sr, dst->row_elems, offset, len, (int)dtype_size(dst->dtype), s);
+}
+
+extern "C" pf_status kvbuf_splice(const pf_kv_view* dst, const pf_kv_view* src, int64_t offset, int64_t len,
+                                  void* stream) {
+  pf_status st = validate_splice(dst, src, offset, len);
+  if (st != PF_OK) return st;
+  if (len == 0) return PF_OK;
+  if ((st = check_device()) != PF_OK) return st;
+  hipError_t e = splice_views(dst, src, offset, len, (hipStream_t)stream);
+  return e == hipSuccess ? PF_OK : hip_fail(e, "kvbuf_splice launch");
+}
+
+// ------------------------------------------------------------------------------------
+// the stage
+// ------------------------------------------------------------------------------------
+struct LayerMem {
+  void *w_qkv, *w_o, *w1, *w2, *w_ada;
+  float *b_qkv, *b_o, *b1, *b2, *b_ada;
+  void *k, *v;
+  float* mod;   // [6h]: shift1, scale1, gate1, shift2, scale2, gate2
+  bool loaded;
+};
+
+struct pf_stage {
+  pf_stage_config cfg;
+  int device;
+  int64_t h, rh, s_kv, s_alloc, patch_rows;
+  size_t es;
+  void* wmem = nullptr;
+  void* kvmem = nullptr;
+  void* scratch = nullptr;
+  float* modmem = nullptr;
+  void *h1, *qkv, *o, *u;
+  std::vector<LayerMem> layers;
+  bool cond_set = false;
+  bool broken = false;   // a HIP call failed: every later call returns PF_ERR_HIP
+};
+
+static size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+static pf_status validate_config(const pf_stage_config* c) {
+  if (!c) return fail(PF_ERR_INVALID_ARG, "stage_create: null config");
+  if (c->num_layers < 1) return fail(PF_ERR_INVALID_ARG, "stage_create: num_layers < 1");
+  if (c->heads < 1) return fail(PF_ERR_INVALID_ARG, "stage_create: heads < 1");
+  if (c->head_dim != 64 && c->head_dim != 72 && c->head_dim != 128)
+    return fail(PF_ERR_UNSUPPORTED, "stage_create: head_dim %d not in {64, 72, 128}", c->head_dim);
+  if ((int64_t)c->hidden != (int64_t)c->heads * c->head_dim)
+    return fail(PF_ERR_INVALID_ARG, "stage_create: hidden %d != heads * head_dim", c->hidden);
+  if (c->mlp_ratio < 0 || c->mlp_ratio > 16) return fail(PF_ERR_INVALID_ARG, "stage_create: mlp_ratio out of range");
+  if (c->num_patches < 1) return fail(PF_ERR_INVALID_ARG, "stage_create: num_patches < 1");
+  if (c->seq_img < 1 || c->seq_txt < 0) return fail(PF_ERR_INVALID_ARG, "stage_create: bad sequence lengths");
+  if (c->seq_img % c->num_patches != 0)
+    return fail(PF_ERR_INVALID_ARG, "stage_create: seq_img %% num_patches != 0");
+  if (!dtype_ok(c->dtype)) return fail(PF_ERR_INVALID_ARG, "stage_create: bad dtype");
+  if (c->gelu != PF_GELU_TANH && c->gelu != PF_GELU_ERF) return fail(PF_ERR_INVALID_ARG, "stage_create: bad gelu");
+  if (!(c->ln_eps > 0.f) || !std::isfinite(c->ln_eps)) return fail(PF_ERR_INVALID_ARG, "stage_create: bad ln_eps");
+  if (c->flags != 0) return fail(PF_ERR_INVALID_ARG, "stage_create: flags must be 0");
+  if (c->hidden > kMaxHidden) return fail(PF_ERR_UNSUPPORTED, "stage_create: hidden > %d", kMaxHidden);
+  if (c->dtype == PF_BF16 && c->hidden % 64 != 0)
+    return fail(PF_ERR_UNSUPPORTED, "stage_create: bf16 stages need hidden %% 64 == 0");
+  if (c->dtype == PF_FP32 && c->hidden % 8 != 0)
+    return fail(PF_ERR_UNSUPPORTED, "stage_create: hidden %% 8 != 0");
+  if (c->seq_txt + c->seq_img > ((int64_t)1 << 31))
+    return fail(PF_ERR_UNSUPPORTED, "stage_create: sequence too long");
+  return PF_OK;
+}
+
+static void free_stage_mem(pf_stage* st) {
+  if (st->wmem) (void)hipFree(st->wmem);
+  if (st->kvmem) (void)hipFree(st->kvmem);
+  if (st->scratch) (void)hipFree(st->scratch);
+  if (st->modmem) (void)hipFree(st->modmem);
+  st->wmem = st->kvmem = st->scratch = nullptr;
+  st->modmem = nullptr;
+}
+
+extern "C" pf_status stage_create(const pf_stage_config* cfg, pf_stage** out) {
+  if (!out) return fail(PF_ERR_INVALID_ARG, "stage_create: null out");
+  *out = nullptr;
+  pf_status vs = validate_config(cfg);
+  if (vs != PF_OK) return vs;
+  if ((vs = check_device()) != PF_OK) return vs;
+
+  pf_stage* st = new (std::nothrow) pf_stage();
+  if (!st) return fail(PF_ERR_OOM, "stage_create: host allocation failed");
+  st->cfg = *cfg;
+  (void)hipGetDevice(&st->device);
+  st->h = cfg->hidden;
+  st->rh = (int64_t)cfg->mlp_ratio * cfg->hidden;
+  st->s_kv = cfg->seq_txt + cfg->seq_img;
+  st->s_alloc = (int64_t)round_up((size_t)st->s_kv, 64);   // K8 groups and key tiles never leave the allocation
+  st->patch_rows = cfg->seq_img / cfg->num_patches;
+  st->es = dtype_size(cfg->dtype);
+  const int64_t h = st->h, rh = st->rh, L = cfg->num_layers;
+  const size_t es = st->es;
+
+  // weights: matrices then fp32 biases, each 256-byte aligned
+  const size_t mats[5] = {(size_t)(3 * h * h), (size_t)(h * h), (size_t)(rh * h), (size_t)(h * rh), (size_t)(6 * h * h)};
+  const size_t biases[5] = {(size_t)(3 * h), (size_t)h, (size_t)rh, (size_t)h, (size_t)(6 * h)};
+  size_t per_layer = 0;
+  for (int i = 0; i < 5; ++i) per_layer += round_up(mats[i] * es, 256) + round_up(biases[i] * 4, 256);
+  const size_t kv_mat = round_up((size_t)(st->s_alloc * h) * es, 256);
+  const size_t scr_h = round_up((size_t)(st->s_alloc * h) * es, 256);
+  const size_t scr_qkv = round_up((size_t)(st->s_alloc * 3 * h) * es, 256);
+  const size_t scr_u = round_up((size_t)(st->s_alloc * (rh > 0 ? rh : 1)) * es, 256);
+
+  hipError_t e;
+  if ((e = hipMalloc(&st->wmem, per_layer * L)) != hipSuccess ||
+      (e = hipMalloc(&st->kvmem, 2 * kv_mat * L)) != hipSuccess ||
+      (e = hipMalloc(&st->scratch, 2 * scr_h + scr_qkv + scr_u)) != hipSuccess ||
+      (e = hipMalloc((void**)&st->modmem, sizeof(float) * 6 * h * L)) != hipSuccess) {
+    free_stage_mem(st);
+    delete st;
+    (void)hipGetLastError();
+    return e == hipErrorOutOfMemory ? fail(PF_ERR_OOM, "stage_create: device allocation failed")
+                                    : hip_fail(e, "stage_create: hipMalloc");
+  }
+  // zero the KV buffers (including the padding rows past seq_kv) once, synchronously
+  if ((e = hipMemset(st->kvmem, 0, 2 * kv_mat * L)) != hipSuccess ||
+      (e = hipMemset(st->modmem, 0, sizeof(float) * 6 * h * L)) != hipSuccess ||
+      (e = hipDeviceSynchronize()) != hipSuccess) {
+    free_stage_mem(st);
+    delete st;
+    return hip_fail(e, "stage_create: hipMemset");
+  }
+  char* wp = (char*)st->wmem;
+  char* kp = (char*)st->kvmem;
+  st->layers.resize(L);
+  for (int64_t l = 0; l < L; ++l) {
+    LayerMem& lm = st->layers[l];
+    void** mp[5] = {&lm.w_qkv, &lm.w_o, &lm.w1, &lm.w2, &lm.w_ada};
+    float** bp[5] = {&lm.b_qkv, &lm.b_o, &lm.b1, &lm.b2, &lm.b_ada};
+    for (int i = 0; i < 5; ++i) {
+      *mp[i] = wp;
+      wp += round_up(mats[i] * es, 256);
+      *bp[i] = (float*)wp;
+      wp += round_up(biases[i] * 4, 256);
+    }
+    lm.k = kp;
+    kp += kv_mat;
+    lm.v = kp;
+    kp += kv_mat;
+    lm.mod = st->modmem + 6 * h * l;
+    lm.loaded = false;
+  }
+  char* sp = (char*)st->scratch;
+  st->h1 = sp;
+  sp += scr_h;
+  st->o = sp;
+  sp += scr_h;
+  st->qkv = sp;
+  sp += scr_qkv;
+  st->u = sp;
+  *out = st;
+  return PF_OK;
+}
+
+extern "C" pf_status stage_destroy(pf_stage* st) {
+  if (!st) return PF_OK;
+  free_stage_mem(st);
+  delete st;
+  return PF_OK;
+}
+
+static pf_status check_stage(pf_stage* st, const char* who) {
+  if (!st) return fail(PF_ERR_INVALID_ARG, "%s: null stage", who);
+  if (st->broken) return fail(PF_ERR_HIP, "%s: an earlier HIP call on this stage failed", who);
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev != st->device) return fail(PF_ERR_INVALID_ARG, "%s: current device %d is not the stage's device %d", who,
+                                     dev, st->device);
+  return PF_OK;
+}
+
+static pf_status stage_hip_fail(pf_stage* st, hipError_t e, const char* what) {
+  st->broken = true;
+  return hip_fail(e, what);
+}
+
+extern "C" pf_status stage_load_weights(pf_stage* st, int32_t layer, const pf_layer_weights* w, void* stream) {
+  pf_status s = check_stage(st, "stage_load_weights");
+  if (s != PF_OK) return s;
+  if (layer < 0 || layer >= st->cfg.num_layers) return fail(PF_ERR_INVALID_ARG, "stage_load_weights: bad layer %d", layer);
+  if (!w) return fail(PF_ERR_INVALID_ARG, "stage_load_weights: null weights");
+  const bool mlp = st->rh > 0;
+  if (!w->w_qkv || !w->b_qkv || !w->w_o || !w->b_o || !w->w_ada || !w->b_ada ||
+      (mlp && (!w->w1 || !w->b1 || !w->w2 || !w->b2)))
+    return fail(PF_ERR_INVALID_ARG, "stage_load_weights: null weight pointer");
+  const int64_t h = st->h, rh = st->rh;
+  const size_t es = st->es;
+  LayerMem& lm = st->layers[layer];
+  struct Cp { void* dst; const void* src; size_t bytes; } cps[10] = {
+      {lm.w_qkv, w->w_qkv, (size_t)(3 * h * h) * es}, {lm.b_qkv, w->b_qkv, (size_t)(3 * h) * 4},
+      {lm.w_o, w->w_o, (size_t)(h * h) * es},         {lm.b_o, w->b_o, (size_t)h * 4},
+      {lm.w1, w->w1, (size_t)(rh * h) * es},          {lm.b1, w->b1, (size_t)rh * 4},
+      {lm.w2, w->w2, (size_t)(h * rh) * es},          {lm.b2, w->b2, (size_t)h * 4},
+      {lm.w_ada, w->w_ada, (size_t)(6 * h * h) * es}, {lm.b_ada, w->b_ada, (size_t)(6 * h) * 4}};
+  for (auto& c : cps) {
+    if (c.bytes == 0) continue;
+    hipError_t e = hipMemcpyAsync(c.dst, c.src, c.bytes, hipMemcpyDeviceToDevice, (hipStream_t)stream);
+    if (e != hipSuccess) return stage_hip_fail(st, e, "stage_load_weights: hipMemcpyAsync");
+  }
+  lm.loaded = true;
+  return PF_OK;
+}
+
+static pf_status check_loaded(pf_stage* st, const char* who) {
+  for (int l = 0; l < st->cfg.num_layers; ++l)
+    if (!st->layers[l].loaded) return fail(PF_ERR_STATE, "%s: layer %d weights not loaded", who, l);
+  return PF_OK;
+}
+
+static pf_status set_cond_impl(pf_stage* st, const float* cond, hipStream_t s) {
+  for (auto& lm : st->layers) {
+    hipError_t e = launch_adaln(cond, lm.w_ada, lm.b_ada, (int)st->h, lm.mod, st->cfg.dtype, s);
+    if (e != hipSuccess) return stage_hip_fail(st, e, "stage_set_cond: adaln launch");
+  }
+  st->cond_set = true;
+  return PF_OK;
+}
+
+extern "C" pf_status stage_set_cond(pf_stage* st, const float* cond, void* stream) {
+  pf_status s = check_stage(st, "stage_set_cond");
+  if (s != PF_OK) return s;
+  if (!cond) return fail(PF_ERR_INVALID_ARG, "stage_set_cond: null cond");
+  if ((s = check_loaded(st, "stage_set_cond")) != PF_OK) return s;
+  return set_cond_impl(st, cond, (hipStream_t)stream);
+}
+
+// rows [off, off + n) through all layers; x (fp32 [n, h]) is updated in place
+static pf_status run_rows(pf_stage* st, int64_t off, int64_t n, float* x, hipStream_t s) {
+  const int64_t h = st->h, rh = st->rh;
+  const int dt = st->cfg.dtype;
+  const size_t es = st->es;
+  const float eps = st->cfg.ln_eps;
+  const int gelu_epi = st->cfg.gelu == PF_GELU_ERF ? kEpiGeluErf : kEpiGeluTanh;
+  char* qkv = (char*)st->qkv;
+  for (auto& lm : st->layers) {
+    const float* mod = lm.mod;
+    hipError_t e;
+    if ((e = launch_ln_modulate(x, n, (int)h, mod, mod + h, eps, st->h1, dt, s)) != hipSuccess)
+      return stage_hip_fail(st, e, "ln_modulate");
+    if ((e = launch_gemm(st->h1, h, lm.w_qkv, lm.b_qkv, n, 3 * h, h, kEpiStore, qkv, 3 * h, nullptr, dt, s)) !=
+        hipSuccess)
+      return stage_hip_fail(st, e, "qkv gemm");
+    KVDesc dst[2] = {{lm.k, h, kLayoutRows}, {lm.v, h, dt == PF_BF16 ? kLayoutK8 : kLayoutRows}};
+    KVDesc src[2] = {{qkv + h * es, 3 * h, kLayoutRows}, {qkv + 2 * h * es, 3 * h, kLayoutRows}};
+    if ((e = launch_splice(dst, src, h, off, n, (int)es, s)) != hipSuccess) return stage_hip_fail(st, e, "kv splice");
+    if ((e = launch_attention(qkv, 3 * h, lm.k, h, lm.v, h, dst[1].layout, h, st->s_kv, n, st->cfg.heads,
+                              st->cfg.head_dim, st->o, h, dt, s)) != hipSuccess)
+      return stage_hip_fail(st, e, "attention");
+    if ((e = launch_gemm(st->o, h, lm.w_o, lm.b_o, n, h, h, kEpiGatedResidual, x, h, mod + 2 * h, dt, s)) !=
+        hipSuccess)
+      return stage_hip_fail(st, e, "out-proj gemm");
+    if (rh > 0) {
+      if ((e = launch_ln_modulate(x, n, (int)h, mod + 3 * h, mod + 4 * h, eps, st->h1, dt, s)) != hipSuccess)
+        return stage_hip_fail(st, e, "ln_modulate (mlp)");
+      if ((e = launch_gemm(st->h1, h, lm.w1, lm.b1, n, rh, h, gelu_epi, st->u, rh, nullptr, dt, s)) != hipSuccess)
+        return stage_hip_fail(st, e, "mlp up gemm");
+      if ((e = launch_gemm(st->u, rh, lm.w2, lm.b2, n, h, rh, kEpiGatedResidual, x, h, mod + 5 * h, dt, s)) !=
+          hipSuccess)
+        return stage_hip_fail(st, e, "mlp down gemm");
+    }
+  }
+  return PF_OK;
+}
+
+static pf_status run_patch_impl(pf_stage* st, int64_t off, int64_t n, const float* x_in, float* x_out,
+                                hipStream_t s) {
+  if (x_out != x_in) {
+    hipError_t e = hipMemcpyAsync(x_out, x_in, (size_t)(n * st->h) * sizeof(float), hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess) return stage_hip_fail(st, e, "stage_run_patch: hipMemcpyAsync");
+  }
+  return run_rows(st, off, n, x_out, s);
+}
+
+static bool ranges_overlap(const void* a, size_t an, const void* b, size_t bn) {
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + bn && b0 < a0 + an;
+}
+
+extern "C" pf_status stage_run_patch(pf_stage* st, int64_t row_off, int64_t rows, const float* x_in, float* x_out,
+                                     void* stream) {
+  pf_status s = check_stage(st, "stage_run_patch");
+  if (s != PF_OK) return s;
+  if (row_off < 0 || rows < 1 || row_off + rows > st->s_kv)
+    return fail(PF_ERR_INVALID_ARG, "stage_run_patch: rows [%lld, %lld) outside [0, %lld)", (long long)row_off,
+                (long long)(row_off + rows), (long long)st->s_kv);
+  if (!x_in || !x_out) return fail(PF_ERR_INVALID_ARG, "stage_run_patch: null x");
+  if (!aligned16(x_in) || !aligned16(x_out)) return fail(PF_ERR_INVALID_ARG, "stage_run_patch: x must be 16-byte aligned");
+  const size_t bytes = (size_t)(rows * st->h) * sizeof(float);
+  if (x_in != x_out && ranges_overlap(x_in, bytes, x_out, bytes))
+    return fail(PF_ERR_INVALID_ARG, "stage_run_patch: x_in and x_out partially overlap");
+  if ((s = check_loaded(st, "stage_run_patch")) != PF_OK) return s;
+  if (!st->cond_set) return fail(PF_ERR_STATE, "stage_run_patch: stage_set_cond not called");
+  return run_patch_impl(st, row_off, rows, x_in, x_out, (hipStream_t)stream);
+}
+
+extern "C" pf_status stage_run_step(pf_stage* st, const float* x_in, float* x_out, const float* cond, uint32_t flags,
+                                    void* stream) {
+  pf_status s = check_stage(st, "stage_run_step");
+  if (s != PF_OK) return s;
+  if (!x_in || !x_out || !cond) return fail(PF_ERR_INVALID_ARG, "stage_run_step: null pointer");
+  if (!aligned16(x_in) || !aligned16(x_out)) return fail(PF_ERR_INVALID_ARG, "stage_run_step: x must be 16-byte aligned");
+  if (flags & ~PF_STEP_WARMUP) return fail(PF_ERR_INVALID_ARG, "stage_run_step: unknown flags");
+  const size_t bytes = (size_t)(st->s_kv * st->h) * sizeof(float);
+  if (x_in != x_out && ranges_overlap(x_in, bytes, x_out, bytes))
+    return fail(PF_ERR_INVALID_ARG, "stage_run_step: x_in and x_out partially overlap");
+  if ((s = check_loaded(st, "stage_run_step")) != PF_OK) return s;
+  hipStream_t hs = (hipStream_t)stream;
+  if ((s = set_cond_impl(st, cond, hs)) != PF_OK) return s;
+  const int64_t h = st->h;
+  if (flags & PF_STEP_WARMUP) return run_patch_impl(st, 0, st->s_kv, x_in, x_out, hs);
+  if (st->cfg.seq_txt > 0 && (s = run_patch_impl(st, 0, st->cfg.seq_txt, x_in, x_out, hs)) != PF_OK) return s;
+  for (int m = 0; m < st->cfg.num_patches; ++m) {
+    const int64_t off = st->cfg.seq_txt + (int64_t)m * st->patch_rows;
+    if ((s = run_patch_impl(st, off, st->patch_rows, x_in + off * h, x_out + off * h, hs)) != PF_OK) return s;
+  }
+  return PF_OK;
+}
+
+extern "C" pf_status stage_get_kvbuf(pf_stage* st, int32_t layer, pf_kv_view* out) {
+  if (!st) return fail(PF_ERR_INVALID_ARG, "stage_get_kvbuf: null stage");
+  if (!out) return fail(PF_ERR_INVALID_ARG, "stage_get_kvbuf: null out");
+  if (layer < 0 || layer >= st->cfg.num_layers) return fail(PF_ERR_INVALID_ARG, "stage_get_kvbuf: bad layer");
+  const LayerMem& lm = st->layers[layer];
+  out->k = lm.k;
+  out->v = lm.v;
+  out->rows = st->s_kv;
+  out->row_elems = st->h;
+  out->k_ld = st->h;
+  out->v_ld = st->h;
+  out->dtype = st->cfg.dtype;
+  out->v_layout = st->cfg.dtype == PF_BF16 ? PF_LAYOUT_K8 : PF_LAYOUT_ROWS;
+  return PF_OK;
+}

@@ -1,0 +1,48 @@
+"""Shared helpers for the GPU parity tests (comparison metrics and device setup)."""
+import numpy as np
+import pytest
+
+# Tolerances for bf16-in / fp32-accumulate outputs against the fp64 oracle.
+MAX_ABS = 2e-2
+REL_L2 = 5e-3
+
+
+def rel_l2(got, want) -> float:
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    den = np.linalg.norm(want)
+    return float(np.linalg.norm(got - want) / (den if den > 0 else 1.0))
+
+
+def max_abs(got, want) -> float:
+    return float(np.abs(np.asarray(got, np.float64) - np.asarray(want, np.float64)).max())
+
+
+def assert_close(got, want, what: str, max_abs_tol=MAX_ABS, rel_tol=REL_L2):
+    ma, rl = max_abs(got, want), rel_l2(got, want)
+    print(f"[parity] {what}: max_abs={ma:.3e} rel_l2={rl:.3e}", flush=True)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    if max_abs_tol is not None:
+        assert ma <= max_abs_tol, f"{what}: max_abs {ma:.3e} > {max_abs_tol}"
+    if rel_tol is not None:
+        assert rl <= rel_tol, f"{what}: rel_l2 {rl:.3e} > {rel_tol}"
+
+
+def torch_cuda():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from patch_pipelined_attention_amd import binding
+    binding.lib()        # raises if the HIP library is missing: no silent fallback
+    return torch
+
+
+def dev(torch, a, dtype=None):
+    dtype = dtype or torch.float32
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(device="cuda", dtype=dtype)
+
+
+def host(t):
+    import torch
+    torch.cuda.synchronize()
+    return t.float().cpu().numpy().astype(np.float64)

@@ -371,3 +371,21 @@ def test_pins_catch_planted_mistakes():
     o_late = ref.attention(qkv[:, :8], st.K[0], st.V[0], 2, 4)   # attends over the drifted buffer
     late = x + mod[2] * ref.linear(o_late, W["w_o"], W["b_o"])
     assert np.abs(late - full).max() > 1e-2
+
+
+def test_sampled_step_matches_full_step():
+    st, layers = _tiny_stage(M=2, S_txt=2, S_img=8, L=2)
+    st2, _ = _tiny_stage(M=2, S_txt=2, S_img=8, L=2)
+    rng = np.random.default_rng(18)
+    x = rng.standard_normal((10, 8))
+    c = rng.standard_normal(8)
+    noise = [(rng.standard_normal((10, 8)), rng.standard_normal((10, 8))) for _ in layers]
+    full = st.step(x, c, warmup=True)
+    rows = np.array([0, 3, 4, 9])
+    np.testing.assert_allclose(st2.step_sampled(x, c, rows, warmup=True), full[rows], rtol=1e-13, atol=1e-13)
+    st.add_noise(noise)
+    st2.add_noise(noise)
+    full = st.step(x, c)
+    np.testing.assert_allclose(st2.step_sampled(x, c, rows), full[rows], rtol=1e-13, atol=1e-13)
+    for l in range(2):
+        np.testing.assert_array_equal(st.K[l], st2.K[l])

@@ -1,0 +1,222 @@
+"""Stage-level parity of the HIP path against the fp64 oracle, plus the properties
+the PipeFusion summaries fix: (a) fresh == stale context reproduces unpartitioned
+full attention, (b) a micro-step changes only its own buffer rows, stale step-(T+1)
+rows elsewhere; determinism; call-order errors."""
+import dataclasses
+
+import numpy as np
+import pytest
+
+from oracle import ref
+from patch_pipelined_attention_amd import binding as B
+from patch_pipelined_attention_amd import synth
+from patch_pipelined_attention_amd.configs import C1, C2, C3, C4, C5
+from patch_pipelined_attention_amd.stage import Stage
+
+from _util import REL_L2, assert_close, dev, host, torch_cuda
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle(shape, inputs, mode):
+    return ref.StageOracle(inputs.layers, heads=shape.heads, head_dim=shape.head_dim, seq_txt=shape.seq_txt,
+                           seq_img=shape.seq_img, num_patches=shape.num_patches, mlp_ratio=shape.mlp_ratio,
+                           mode=mode)
+
+
+SMALL = {
+    "c2s": C2.small(seq_img=400, num_layers=2),                          # D=72, P=100: ragged tiles
+    "c3s": C3.small(seq_img=1024, num_layers=2),                         # D=64, M=8, P=128
+    "c4s": C4.small(seq_img=256, num_layers=2, seq_txt=40),              # D=128, ragged text prefix
+    "c5s": C5.small(seq_img=2048, num_layers=1, num_patches=16),         # D=72, M=16
+}
+
+
+def _run_chain(shape, steps, check_exact=True):
+    torch = torch_cuda()
+    inputs = synth.stage_inputs(shape)
+    bf16 = shape.dtype == "bf16"
+    orc_b = _oracle(shape, inputs, "bf16") if bf16 else None
+    orc_e = _oracle(shape, inputs, "exact")
+    with Stage(shape) as st:
+        st.load(inputs.layers)
+        x = dev(torch, inputs.x)
+        c = dev(torch, inputs.c)
+        out = torch.empty_like(x)
+        for s in range(steps):
+            warm = s == 0
+            if s > 0:
+                noise = inputs.next_noise()
+                st.add_noise(noise)
+                orc_e.add_noise(noise)
+                if orc_b:
+                    orc_b.add_noise(noise)
+            print(f"[stage] {shape.name} step {s} warmup={warm}", flush=True)
+            st.run_step(x, c, warmup=warm, out=out)
+            got = host(out)
+            want_e = orc_e.step(inputs.x, inputs.c, warmup=warm)
+            if bf16:
+                want_b = orc_b.step(inputs.x, inputs.c, warmup=warm)
+                assert_close(got, want_b, f"{shape.name} step {s} vs bf16-in oracle")
+                if check_exact:
+                    assert_close(got, want_e, f"{shape.name} step {s} vs exact oracle", max_abs_tol=None)
+                for l in range(shape.num_layers):
+                    k, v = st.kv_get(l)
+                    assert_close(k, orc_b.K[l], f"{shape.name} step {s} K[{l}]")
+                    assert_close(v, orc_b.V[l], f"{shape.name} step {s} V[{l}]")
+            else:
+                assert_close(got, want_e, f"{shape.name} step {s} vs exact oracle", max_abs_tol=1e-3, rel_tol=1e-5)
+                for l in range(shape.num_layers):
+                    k, v = st.kv_get(l)
+                    assert_close(k, orc_e.K[l], f"{shape.name} step {s} K[{l}]", max_abs_tol=1e-4, rel_tol=1e-5)
+                    assert_close(v, orc_e.V[l], f"{shape.name} step {s} V[{l}]", max_abs_tol=1e-4, rel_tol=1e-5)
+
+
+def test_c1_tiny_fp32_all_steps():
+    _run_chain(C1, C1.steps)
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_small_bf16_stage_chain(name):
+    _run_chain(SMALL[name], 3)
+
+
+def test_property_a_single_patch_overwrites_stale_context():
+    """M = 1: the patch splices every row before attending, so any stale content is irrelevant."""
+    torch = torch_cuda()
+    shape = dataclasses.replace(C3.small(seq_img=512, num_layers=2), num_patches=1)
+    inputs = synth.stage_inputs(shape)
+    with Stage(shape) as st:
+        st.load(inputs.layers)
+        x, c = dev(torch, inputs.x), dev(torch, inputs.c)
+        warm = host(st.run_step(x, c, warmup=True, out=torch.empty_like(x)))
+        rng = np.random.default_rng(3)
+        for l in range(shape.num_layers):
+            k, v = st.kv_get(l)
+            st.kv_set(l, k + 30 * rng.standard_normal(k.shape), v + 30 * rng.standard_normal(v.shape))
+        patched = host(st.run_step(x, c, warmup=False, out=torch.empty_like(x)))
+        np.testing.assert_array_equal(patched, warm)
+
+
+@pytest.mark.parametrize("shape", [C2, C3, C4], ids=lambda s: s.name)
+def test_property_a_no_drift_full_size_bitwise(shape):
+    """At full size and in the benchmark's launch configuration: with no drift between steps
+    (fresh == stale) every patched step reproduces the warm-up (unpartitioned) output bit for bit."""
+    torch = torch_cuda()
+    shape = dataclasses.replace(shape, num_layers=min(shape.num_layers, 2))
+    inputs = synth.stage_inputs(shape)
+    with Stage(shape) as st:
+        st.load(inputs.layers)
+        x, c = dev(torch, inputs.x), dev(torch, inputs.c)
+        print(f"[stage] {shape.name} full-size property (a)", flush=True)
+        warm = st.run_step(x, c, warmup=True, out=torch.empty_like(x)).clone()
+        k0, v0 = st.kv_raw(0)
+        out = torch.empty_like(x)
+        st.run_step(x, c, warmup=False, out=out)
+        torch.cuda.synchronize()
+        assert torch.equal(out, warm)
+        k1, v1 = st.kv_raw(0)
+        assert torch.equal(k0, k1) and torch.equal(v0, v1)
+        assert bool(torch.isfinite(out).all())
+
+
+@pytest.mark.parametrize("shape", [C2, C3, C4], ids=lambda s: s.name)
+def test_full_size_one_layer_sampled_parity(shape):
+    """Full sequence length and width, one layer: warm-up and one drifted patched step,
+    checked against the oracle on sampled rows of every patch."""
+    torch = torch_cuda()
+    shape = dataclasses.replace(shape, num_layers=1, name=shape.name + "-L1")
+    inputs = synth.stage_inputs(shape)
+    orc = _oracle(shape, inputs, "bf16")
+    rng = np.random.default_rng(11)
+    rows = np.unique(np.concatenate([rng.choice(shape.seq_kv, 96, replace=False),
+                                     [0, shape.seq_kv - 1] + list(shape.patch_offsets())]))
+    with Stage(shape) as st:
+        st.load(inputs.layers)
+        x, c = dev(torch, inputs.x), dev(torch, inputs.c)
+        out = torch.empty_like(x)
+        for s in range(2):
+            if s == 1:
+                noise = inputs.next_noise()
+                st.add_noise(noise)
+                orc.add_noise(noise)
+            print(f"[stage] {shape.name} sampled step {s}", flush=True)
+            st.run_step(x, c, warmup=(s == 0), out=out)
+            got = host(out)[rows]
+            want = orc.step_sampled(inputs.x, inputs.c, rows, warmup=(s == 0))
+            assert_close(got, want, f"{shape.name} step {s} sampled rows vs bf16-in oracle")
+            k, v = st.kv_get(0)
+            assert_close(k, orc.K[0], f"{shape.name} step {s} K buffer")
+            assert_close(v, orc.V[0], f"{shape.name} step {s} V buffer")
+
+
+def test_property_b_micro_steps_touch_only_their_rows():
+    torch = torch_cuda()
+    shape = SMALL["c4s"]
+    inputs = synth.stage_inputs(shape)
+    orc = _oracle(shape, inputs, "bf16")
+    with Stage(shape) as st:
+        st.load(inputs.layers)
+        x, c = dev(torch, inputs.x), dev(torch, inputs.c)
+        st.run_step(x, c, warmup=True, out=torch.empty_like(x))
+        orc.step(inputs.x, inputs.c, warmup=True)
+        noise = inputs.next_noise()
+        st.add_noise(noise)
+        orc.add_noise(noise)
+        st.set_cond(c)
+        orc.set_cond(inputs.c)
+        xo = x.clone()
+        h = shape.hidden
+        for off, n in orc.micro_steps(False):
+            before = [st.kv_get(l) for l in range(shape.num_layers)]
+            st.run_patch(off, n, x[off:off + n], xo[off:off + n])
+            orc.run_rows(off, n, inputs.x[off:off + n])
+            for l in range(shape.num_layers):
+                k, v = st.kv_get(l)
+                outside = np.ones(shape.seq_kv, bool)
+                outside[off:off + n] = False
+                np.testing.assert_array_equal(k[outside], before[l][0][outside])
+                np.testing.assert_array_equal(v[outside], before[l][1][outside])
+                assert_close(k[off:off + n], orc.K[l][off:off + n], f"fresh K rows [{off},{off + n}) layer {l}")
+                assert_close(v[off:off + n], orc.V[l][off:off + n], f"fresh V rows [{off},{off + n}) layer {l}")
+        assert h == shape.hidden
+
+
+def test_deterministic_bytes():
+    torch = torch_cuda()
+    shape = SMALL["c2s"]
+    inputs = synth.stage_inputs(shape)
+    outs = []
+    for _ in range(2):
+        with Stage(shape) as st:
+            st.load(inputs.layers)
+            x, c = dev(torch, inputs.x), dev(torch, inputs.c)
+            st.run_step(x, c, warmup=True, out=torch.empty_like(x))
+            outs.append(st.run_step(x, c, warmup=False, out=torch.empty_like(x)).clone())
+    assert torch.equal(outs[0], outs[1])
+
+
+def test_call_order_and_range_errors():
+    torch = torch_cuda()
+    shape = C1
+    inputs = synth.stage_inputs(shape)
+    with Stage(shape) as st:
+        x = dev(torch, inputs.x)
+        c = dev(torch, inputs.c)
+        with pytest.raises(B.PFError) as ei:
+            st.run_step(x, c, warmup=True)
+        assert ei.value.status == B.PF_ERR_STATE
+        st.load(inputs.layers)
+        with pytest.raises(B.PFError) as ei:
+            B.stage_run_patch(st.handle, 0, 64, x, x)          # condition not set yet
+        assert ei.value.status == B.PF_ERR_STATE
+        st.set_cond(c)
+        for off, n in [(-1, 4), (0, 0), (250, 7)]:
+            with pytest.raises(B.PFError) as ei:
+                B.stage_run_patch(st.handle, off, n, x, x)
+            assert ei.value.status == B.PF_ERR_INVALID_ARG
+        with pytest.raises(B.PFError):
+            B.stage_get_kvbuf(st.handle, 1)
+        view = st.kv_view(0)
+        assert view.rows == shape.seq_kv and view.row_elems == shape.hidden
+        assert view.v_layout == B.PF_LAYOUT_ROWS and view.dtype == B.PF_FP32

@@ -28,12 +28,17 @@ fresh and rows of later patches still hold step-(T+1) values; step 0 is a
 warm-up that runs all rows as one patch; text-prefix rows (if any) run first as
 their own micro-step in every step.
 
-Two precision modes, both fp64 code:
+Three precision modes, all fp64 code:
 * ``exact``: no intermediate rounding (the plain definition).
 * ``bf16``: every tensor the bf16 path stores and feeds to a contraction is
   rounded to bf16 (round to nearest even): the modulated LayerNorm outputs,
   Q/K/V, the KV buffer after drift noise, the attention output and the GELU
   output.  Softmax probabilities are not rounded.
+* ``bf16p``: ``bf16`` plus the unnormalised softmax weights exp(s - rowmax)
+  rounded to bf16 before the product with V.  It is the same computation with
+  one more rounding point; comparing it with ``bf16`` measures how far bf16
+  probabilities alone move a stage's output (the noise floor any bf16
+  flash-attention path shares).
 
 Parity status: every function below is pinned in the CPU test-suite by closed
 forms, invariants, library special cases or brute force.  The choice of block
@@ -135,11 +140,13 @@ def softmax_rows(s) -> np.ndarray:
     return e / e.sum(axis=-1, keepdims=True)
 
 
-def attention(q, k, v, heads: int, head_dim: int, chunk: int = 256) -> np.ndarray:
+def attention(q, k, v, heads: int, head_dim: int, chunk: int = 256, round_p: bool = False) -> np.ndarray:
     """Full non-causal multi-head attention of the rows of q over every row of k/v.
 
     Head j uses columns [j*d, (j+1)*d) of q, k and v.  O_j = softmax(Q_j K_j^T / sqrt(d)) V_j.
     Query rows are processed in chunks only to bound memory; each row's arithmetic is unchanged.
+    round_p: the unnormalised weights exp(s - rowmax) are rounded to bf16 before the product
+    with V and the row sum is taken unrounded (the plain definition of bf16 probabilities).
     """
     q = np.asarray(q, F64)
     k = np.asarray(k, F64)
@@ -153,8 +160,12 @@ def attention(q, k, v, heads: int, head_dim: int, chunk: int = 256) -> np.ndarra
         vj = v[:, cs]
         for r0 in range(0, n, chunk):
             r1 = min(n, r0 + chunk)
-            p = softmax_rows((q[r0:r1, cs] @ kj.T) * scale)
-            out[r0:r1, cs] = p @ vj
+            s = (q[r0:r1, cs] @ kj.T) * scale
+            if round_p:
+                e = np.exp(s - s.max(axis=-1, keepdims=True))
+                out[r0:r1, cs] = (bf16_round(e) @ vj) / e.sum(axis=-1, keepdims=True)
+            else:
+                out[r0:r1, cs] = softmax_rows(s) @ vj
     return out
 
 
@@ -189,7 +200,7 @@ class StageOracle:
     def __init__(self, layers, *, heads: int, head_dim: int, seq_txt: int, seq_img: int,
                  num_patches: int, mlp_ratio: int, ln_eps: float = 1e-6, gelu: str = "tanh",
                  mode: str = "exact"):
-        if mode not in ("exact", "bf16"):
+        if mode not in ("exact", "bf16", "bf16p"):
             raise ValueError(mode)
         if seq_img % num_patches:
             raise ValueError("seq_img must be a multiple of num_patches")
@@ -209,7 +220,7 @@ class StageOracle:
         self.trace = None          # set to a list to record per-layer intermediates
 
     def _r(self, a):
-        return bf16_round(a) if self.mode == "bf16" else a
+        return a if self.mode == "exact" else bf16_round(a)
 
     def set_cond(self, c):
         self.mod = [adaln(c, W["w_ada"], W["b_ada"]) for W in self.W]
@@ -235,7 +246,7 @@ class StageOracle:
             splice(self.V[l], v, offset)
             if sample is not None and l == len(self.W) - 1:
                 q, x, qkv, h1 = q[sample], x[sample], qkv[sample], h1[sample]
-            o = self._r(attention(q, self.K[l], self.V[l], H, d))
+            o = self._r(attention(q, self.K[l], self.V[l], H, d, round_p=self.mode == "bf16p"))
             x = x + gate1 * linear(o, W["w_o"], W["b_o"])
             rec = {"layer": l, "offset": offset, "h1": h1, "qkv": qkv, "o": o, "x_attn": x.copy()}
             if self.mlp_ratio > 0:

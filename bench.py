@@ -1,0 +1,244 @@
+"""Benchmark: one GPU's pipeline stage of patch-level (PipeFusion-style) DiT inference.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c2] [--breakdown] [--no-cpu-baseline]
+
+A step is one patched diffusion step of the stage: every layer for every patch
+(QKV projection, in-place KV splice, attention of the patch over the full
+buffer, output projection, modulated MLP) over synthetic inputs already resident
+in HBM.  Prints one JSON line.  `value` is stage tokens/s (buffer rows per step
+divided by the median step time).  `roofline` describes the dominant kernel (the
+patch attention), timed with HIP events at the stage's launch shape.
+`cpu_baseline` times the fp64 oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "stage tokens/s and patch-attention TFLOP/s (% bf16 MFMA peak), 1 MI355X"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA (published)
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E (published)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", default="c2")
+    ap.add_argument("--breakdown", action="store_true", help="also time every kernel of a patch-layer")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+def time_kernel(torch, fn, iters=20, warm=3):
+    """Average duration (s) of fn() over `iters` launches, HIP events on the current stream."""
+    for _ in range(warm):
+        fn()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(iters):
+        fn()
+    e.record()
+    e.synchronize()
+    return s.elapsed_time(e) / 1e3 / iters
+
+
+def kernel_probes(torch, B, st, shape, layer_w):
+    """Component launches at the exact shapes one patch-layer of the stage issues."""
+    h, P, S, r = shape.hidden, shape.patch_rows, shape.seq_kv, shape.mlp_ratio
+    bf = torch.bfloat16
+    dev = "cuda"
+    x = torch.randn((P, h), device=dev)
+    shift = torch.zeros(h, device=dev)
+    scale = torch.zeros(h, device=dev)
+    h1 = torch.empty((P, h), dtype=bf, device=dev)
+    qkv = torch.randn((P, 3 * h), device=dev).to(bf)
+    o = torch.empty((P, h), dtype=bf, device=dev)
+    u = torch.empty((P, r * h), dtype=bf, device=dev)
+    kv = st.kv_view(0)
+    gate = torch.zeros(h, device=dev)
+    qkv_src = B.KVView(k=qkv.data_ptr() + h * 2, v=qkv.data_ptr() + 2 * h * 2, rows=P, row_elems=h, k_ld=3 * h,
+                       v_ld=3 * h, dtype=B.PF_BF16, v_layout=B.PF_LAYOUT_ROWS)
+    off = shape.patch_offsets()[-1]
+    w = layer_w
+    probes = {
+        "ln_modulate": (lambda: B.pf_ln_modulate(x, shift, scale, 1e-6, h1), 12.0 * P * h, "hbm"),
+        "gemm_qkv": (lambda: B.pf_gemm(h1, w["w_qkv"], w["b_qkv"], B.PF_EPI_STORE, qkv), 6.0 * P * h * h, "mfma"),
+        "kv_splice": (lambda: B.kvbuf_splice(kv, qkv_src, off, P), 8.0 * P * h, "hbm"),
+        "attention": (lambda: B.pf_attention(qkv, kv, S, P, shape.heads, shape.head_dim, o), 4.0 * P * S * h, "mfma"),
+        "gemm_out": (lambda: B.pf_gemm(o, w["w_o"], w["b_o"], B.PF_EPI_GATED_RESIDUAL, x, gate=gate),
+                     2.0 * P * h * h, "mfma"),
+    }
+    if r > 0:
+        probes["gemm_up_gelu"] = (lambda: B.pf_gemm(h1, w["w1"], w["b1"], B.PF_EPI_GELU_TANH, u), 2.0 * r * P * h * h,
+                                  "mfma")
+        probes["gemm_down"] = (lambda: B.pf_gemm(u, w["w2"], w["b2"], B.PF_EPI_GATED_RESIDUAL, x, gate=gate),
+                               2.0 * r * P * h * h, "mfma")
+    return probes
+
+
+def cpu_baseline(shape, inputs, budget_s):
+    """Oracle (fp64 numpy) on a bounded sample: whole patches through all layers with a full
+    buffer, repeated until `budget_s` of CPU time; scaled to a step's rows."""
+    import numpy as np
+    from oracle import ref
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    orc = ref.StageOracle(inputs.layers, heads=shape.heads, head_dim=shape.head_dim, seq_txt=shape.seq_txt,
+                          seq_img=shape.seq_img, num_patches=shape.num_patches, mlp_ratio=shape.mlp_ratio,
+                          mode="exact")
+    rng = np.random.default_rng(0)
+    for l in range(shape.num_layers):           # a filled buffer (values do not change the work)
+        orc.K[l][:] = rng.standard_normal(orc.K[l].shape)
+        orc.V[l][:] = rng.standard_normal(orc.V[l].shape)
+    orc.set_cond(inputs.c)
+    P = shape.patch_rows
+    offs = shape.patch_offsets()
+    done_rows, t0 = 0, time.perf_counter()
+    i = 0
+    while True:
+        off = offs[i % len(offs)]
+        orc.run_rows(off, P, inputs.x[off:off + P])
+        done_rows += P
+        i += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or i >= 4 * len(offs):
+            break
+    rate = done_rows / el
+    return {"value": rate, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{i} patch(es) of {P} rows through all {shape.num_layers} layers over a full "
+                      f"{shape.seq_kv}-row buffer (fp64 numpy, exact mode), {el:.1f} s; tokens/s = rows / time",
+            "host_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0))}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU's pipeline stage; --gpus {args.gpus} is not supported "
+              "(this build runs on one GPU only).", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from patch_pipelined_attention_amd import binding as B
+    from patch_pipelined_attention_amd import synth
+    from patch_pipelined_attention_amd.configs import CONFIGS
+    from patch_pipelined_attention_amd.stage import Stage
+
+    B.lib()
+    shape = CONFIGS[args.config]
+    torch.cuda.set_device(0)
+    print(f"[bench] {shape.name}: generating inputs", file=sys.stderr, flush=True)
+    inputs = synth.stage_inputs(shape)
+    st = Stage(shape)
+    st.load(inputs.layers)
+    x = torch.from_numpy(inputs.x).cuda()
+    c = torch.from_numpy(inputs.c).cuda()
+    out = torch.empty_like(x)
+
+    # warm-up step (fills every buffer fresh), then untimed patched steps
+    st.run_step(x, c, warmup=True, out=out)
+    for _ in range(args.warmup):
+        st.run_step(x, c, warmup=False, out=out)
+    torch.cuda.synchronize()
+    print(f"[bench] timing {args.steps} patched steps", file=sys.stderr, flush=True)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s, e in evs:
+        s.record()
+        st.run_step(x, c, warmup=False, out=out)
+        e.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_s = [s.elapsed_time(e) / 1e3 for s, e in evs]
+    med = statistics.median(step_s)
+    assert bool(torch.isfinite(out).all()), "non-finite stage output"
+
+    # warm-up (M = 1) step time, same FLOPs: patching overhead on one GPU
+    ws, we = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ws.record()
+    st.run_step(x, c, warmup=True, out=out)
+    we.record()
+    we.synchronize()
+    warm_s = ws.elapsed_time(we) / 1e3
+
+    # dominant kernel: patch attention at the stage's launch shape
+    wdev = {k: torch.from_numpy(np.ascontiguousarray(a)).cuda().to(torch.bfloat16 if k.startswith("w") else torch.float32)
+            for k, a in inputs.layers[0].items()}
+    probes = kernel_probes(torch, B, st, shape, wdev)
+    attn_fn, attn_flop, _ = probes["attention"]
+    attn_s = time_kernel(torch, attn_fn, iters=max(10, args.steps))
+    attn_tflops = attn_flop / attn_s / 1e12
+    breakdown = None
+    if args.breakdown:
+        breakdown = {}
+        for name, (fn, work, bound) in probes.items():
+            t = time_kernel(torch, fn)
+            if bound == "mfma":
+                breakdown[name] = {"us": t * 1e6, "tflops": work / t / 1e12,
+                                   "frac_peak": work / t / 1e12 / PEAK_BF16_TFLOPS}
+            else:
+                breakdown[name] = {"us": t * 1e6, "gbs": work / t / 1e9, "frac_peak": work / t / 1e9 / PEAK_HBM_GBS}
+
+    tokens = shape.seq_kv
+    rec = {
+        "metric": METRIC,
+        "value": tokens / med,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": med * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": shape.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{shape.name}: one pipeline stage, {shape.num_layers} DiT blocks, hidden "
+                               f"{shape.hidden}, {shape.heads}x{shape.head_dim} heads, MLP {shape.mlp_ratio}x, "
+                               f"{shape.seq_kv} buffer rows, M={shape.num_patches} patches of {shape.patch_rows}",
+                   "num_layers": shape.num_layers, "hidden": shape.hidden, "heads": shape.heads,
+                   "head_dim": shape.head_dim, "seq_kv": shape.seq_kv, "num_patches": shape.num_patches,
+                   "patch_rows": shape.patch_rows, "parallelism": "single GPU stage"},
+        "stage_tflops": shape.flops_per_step() / med / 1e12,
+        "stage_frac_peak": shape.flops_per_step() / med / 1e12 / PEAK_BF16_TFLOPS,
+        "attention_tflops": attn_tflops,
+        "attention_frac_peak": attn_tflops / PEAK_BF16_TFLOPS,
+        "ms_min_step": min(step_s) * 1e3,
+        "ms_warmup_step": warm_s * 1e3,
+        "patching_overhead": med / warm_s,
+        "wall_s_timed": wall,
+        "roofline": {"kernel": "attn_bf16_kernel", "bound": "mfma", "achieved": attn_tflops,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": attn_tflops / PEAK_BF16_TFLOPS,
+                     "traffic": None, "avg_launch_us": attn_s * 1e6,
+                     "work": f"4*P*S_kv*h = {attn_flop:.4g} FLOP per launch (P={shape.patch_rows}, "
+                             f"S_kv={shape.seq_kv}, h={shape.hidden})"},
+    }
+    if breakdown:
+        rec["breakdown"] = breakdown
+    st.close()
+    del x, out
+    torch.cuda.synchronize()
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(shape, inputs, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -197,10 +197,18 @@ pf_status pf_gemm(const void* a, int64_t lda, const void* w, const float* bias, 
 /* Full non-causal attention of `rows` query rows over the first seq_kv rows of kv:
  * for head j (columns [j*d, (j+1)*d)): O_j = softmax(Q_j K_j^T / sqrt(d)) V_j.
  * q [rows, heads*head_dim] (row stride ldq), o [rows, heads*head_dim] (row stride ldo),
- * both in kv->dtype.  bf16 requires kv->v_layout == PF_LAYOUT_K8, fp32 PF_LAYOUT_ROWS. */
+ * both in kv->dtype.  bf16 requires kv->v_layout == PF_LAYOUT_K8, fp32 PF_LAYOUT_ROWS.
+ * `workspace` (device, may be NULL) lets a query grid too small to fill the GPU split the
+ * key range across workgroups; pf_attention_workspace_size gives the bytes that allow every
+ * split the kernel may choose.  A smaller (or NULL) workspace limits the split; the result
+ * is the same function of the inputs either way, up to fp32 summation order.  The caller
+ * owns the workspace and must not use it concurrently with this call. */
 pf_status pf_attention(const void* q, int64_t ldq, const pf_kv_view* kv, int64_t seq_kv,
                        int64_t rows, int32_t heads, int32_t head_dim, void* o, int64_t ldo,
-                       void* stream);
+                       void* workspace, uint64_t workspace_bytes, void* stream);
+
+/* Workspace bytes pf_attention can use for `rows` queries of `heads` x `head_dim`. */
+pf_status pf_attention_workspace_size(int64_t rows, int32_t heads, int32_t head_dim, uint64_t* bytes);
 
 /* mod = SiLU(cond) . w_ada^T + b_ada: cond fp32 [hidden], w_ada [6*hidden, hidden] in
  * `dtype`, b_ada fp32 [6*hidden], mod fp32 [6*hidden]. */

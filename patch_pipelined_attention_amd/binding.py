@@ -65,7 +65,8 @@ _SIGNATURES = {
     "stage_get_kvbuf": [_P, _I32, ctypes.POINTER(KVView)],
     "pf_ln_modulate": [_P, _I64, _I32, _P, _P, _F, _P, _I32, _P],
     "pf_gemm": [_P, _I64, _P, _P, _I64, _I64, _I64, _I32, _P, _I64, _P, _I32, _P],
-    "pf_attention": [_P, _I64, ctypes.POINTER(KVView), _I64, _I64, _I32, _I32, _P, _I64, _P],
+    "pf_attention": [_P, _I64, ctypes.POINTER(KVView), _I64, _I64, _I32, _I32, _P, _I64, _P, ctypes.c_uint64, _P],
+    "pf_attention_workspace_size": [_I64, _I32, _I32, ctypes.POINTER(ctypes.c_uint64)],
     "pf_adaln": [_P, _P, _P, _I32, _P, _I32, _P],
 }
 
@@ -183,11 +184,25 @@ def pf_gemm(a, w, bias, epi: int, c, gate=None, m=None, lda=None, ldc=None, stre
 
 
 def pf_attention(q, kv: KVView, seq_kv: int, rows: int, heads: int, head_dim: int, o, ldq=None, ldo=None,
-                 stream=None) -> None:
+                 workspace=None, stream=None) -> None:
     ldq = q.stride(0) if ldq is None else ldq
     ldo = o.stride(0) if ldo is None else ldo
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().pf_attention(_ptr(q), ldq, ctypes.byref(kv), seq_kv, rows, heads, head_dim, _ptr(o), ldo,
-                              _stream(stream)))
+                              _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def pf_attention_workspace_size(rows: int, heads: int, head_dim: int) -> int:
+    b = ctypes.c_uint64()
+    _check(lib().pf_attention_workspace_size(rows, heads, head_dim, ctypes.byref(b)))
+    return b.value
+
+
+def attention_workspace(rows: int, heads: int, head_dim: int):
+    """torch uint8 device buffer of pf_attention_workspace_size bytes (None when zero)."""
+    import torch
+    n = pf_attention_workspace_size(rows, heads, head_dim)
+    return torch.empty((n,), dtype=torch.uint8, device="cuda") if n else None
 
 
 def pf_adaln(cond, w_ada, b_ada, mod, stream=None) -> None:

@@ -10,6 +10,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <algorithm>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -203,13 +204,23 @@ extern "C" pf_status pf_gemm(const void* a, int64_t lda, const void* w, const fl
 }
 
 extern "C" pf_status pf_attention(const void* q, int64_t ldq, const pf_kv_view* kv, int64_t seq_kv, int64_t rows,
-                                  int32_t heads, int32_t head_dim, void* o, int64_t ldo, void* stream) {
+                                  int32_t heads, int32_t head_dim, void* o, int64_t ldo, void* workspace,
+                                  uint64_t workspace_bytes, void* stream) {
   pf_status st = validate_attention(q, ldq, kv, seq_kv, rows, heads, head_dim, o, ldo);
   if (st != PF_OK) return st;
+  if (workspace && !aligned16(workspace)) return fail(PF_ERR_INVALID_ARG, "attention: workspace must be 16-byte aligned");
   if ((st = check_device()) != PF_OK) return st;
   hipError_t e = launch_attention(q, ldq, kv->k, kv->k_ld, kv->v, kv->v_ld, kv->v_layout, kv->row_elems, seq_kv,
-                                  rows, heads, head_dim, o, ldo, kv->dtype, (hipStream_t)stream);
+                                  rows, heads, head_dim, o, ldo, kv->dtype, workspace,
+                                  workspace ? (size_t)workspace_bytes : 0, (hipStream_t)stream);
   return e == hipSuccess ? PF_OK : hip_fail(e, "attention launch");
+}
+
+extern "C" pf_status pf_attention_workspace_size(int64_t rows, int32_t heads, int32_t head_dim, uint64_t* bytes) {
+  if (!bytes) return fail(PF_ERR_INVALID_ARG, "attention_workspace_size: null out");
+  if (rows < 0 || heads <= 0 || head_dim <= 0) return fail(PF_ERR_INVALID_ARG, "attention_workspace_size: bad sizes");
+  *bytes = attention_workspace_bytes(rows, (int64_t)heads * head_dim, heads, kMaxAttnSplit);
+  return PF_OK;
 }
 
 extern "C" pf_status pf_adaln(const float* cond, const void* w_ada, const float* b_ada, int32_t hidden, float* mod,
@@ -263,6 +274,8 @@ struct pf_stage {
   void* scratch = nullptr;
   float* modmem = nullptr;
   void *h1, *qkv, *o, *u;
+  void* attn_ws = nullptr;   // key-range split partials of the patch attention
+  size_t attn_ws_bytes = 0;
   std::vector<LayerMem> layers;
   bool cond_set = false;
   bool broken = false;   // a HIP call failed: every later call returns PF_ERR_HIP
@@ -302,6 +315,8 @@ static void free_stage_mem(pf_stage* st) {
   if (st->kvmem) (void)hipFree(st->kvmem);
   if (st->scratch) (void)hipFree(st->scratch);
   if (st->modmem) (void)hipFree(st->modmem);
+  if (st->attn_ws) (void)hipFree(st->attn_ws);
+  st->attn_ws = nullptr;
   st->wmem = st->kvmem = st->scratch = nullptr;
   st->modmem = nullptr;
 }
@@ -336,8 +351,13 @@ extern "C" pf_status stage_create(const pf_stage_config* cfg, pf_stage** out) {
   const size_t scr_qkv = round_up((size_t)(st->s_alloc * 3 * h) * es, 256);
   const size_t scr_u = round_up((size_t)(st->s_alloc * (rh > 0 ? rh : 1)) * es, 256);
 
+  // split partials for a patch or the text prefix (the warm-up pass fills the GPU unsplit)
+  const int64_t split_rows = std::max<int64_t>(st->patch_rows, cfg->seq_txt);
+  st->attn_ws_bytes = cfg->dtype == PF_BF16 ? attention_workspace_bytes(split_rows, h, cfg->heads, kMaxAttnSplit) : 0;
+
   hipError_t e;
   if ((e = hipMalloc(&st->wmem, per_layer * L)) != hipSuccess ||
+      (st->attn_ws_bytes && (e = hipMalloc(&st->attn_ws, st->attn_ws_bytes)) != hipSuccess) ||
       (e = hipMalloc(&st->kvmem, 2 * kv_mat * L)) != hipSuccess ||
       (e = hipMalloc(&st->scratch, 2 * scr_h + scr_qkv + scr_u)) != hipSuccess ||
       (e = hipMalloc((void**)&st->modmem, sizeof(float) * 6 * h * L)) != hipSuccess) {
@@ -482,7 +502,7 @@ static pf_status run_rows(pf_stage* st, int64_t off, int64_t n, float* x, hipStr
     KVDesc src[2] = {{qkv + h * es, 3 * h, kLayoutRows}, {qkv + 2 * h * es, 3 * h, kLayoutRows}};
     if ((e = launch_splice(dst, src, h, off, n, (int)es, s)) != hipSuccess) return stage_hip_fail(st, e, "kv splice");
     if ((e = launch_attention(qkv, 3 * h, lm.k, h, lm.v, h, dst[1].layout, h, st->s_kv, n, st->cfg.heads,
-                              st->cfg.head_dim, st->o, h, dt, s)) != hipSuccess)
+                              st->cfg.head_dim, st->o, h, dt, st->attn_ws, st->attn_ws_bytes, s)) != hipSuccess)
       return stage_hip_fail(st, e, "attention");
     if ((e = launch_gemm(st->o, h, lm.w_o, lm.b_o, n, h, h, kEpiGatedResidual, x, h, mod + 2 * h, dt, s)) !=
         hipSuccess)

@@ -111,11 +111,14 @@ def _kv_bf16(torch, K, V):
 
 
 ATTN_CASES = [(64, 2, 64, 1), (64, 2, 100, 50), (64, 3, 1000, 129), (72, 2, 64, 128), (72, 2, 777, 300),
-              (72, 4, 2053, 77), (128, 2, 65, 128), (128, 2, 1500, 200), (128, 1, 8, 3)]
+              (72, 4, 2053, 77), (128, 2, 65, 128), (128, 2, 1500, 200), (128, 1, 8, 3), (64, 2, 4133, 257),
+              (72, 1, 3000, 600), (128, 3, 2500, 513)]
 
 
+@pytest.mark.parametrize("split", [False, True], ids=["whole", "split"])
 @pytest.mark.parametrize("D,H,S,rows", ATTN_CASES)
-def test_attention_bf16(D, H, S, rows):
+def test_attention_bf16(D, H, S, rows, split):
+    """`split` passes a workspace, letting small query grids split the key range (merge kernel)."""
     torch = torch_cuda()
     h = H * D
     seed = D * 1000 + S + rows
@@ -124,8 +127,9 @@ def test_attention_bf16(D, H, S, rows):
     V = synth.randn((S, h), seed + 2, std=1.0, bf16=True)
     kt, vt, kv = _kv_bf16(torch, K, V)
     o = torch.empty((rows, h), dtype=torch.bfloat16, device="cuda")
-    print(f"[attn] D={D} H={H} S={S} rows={rows}", flush=True)
-    B.pf_attention(dev(torch, q, torch.bfloat16), kv, S, rows, H, D, o)
+    ws = B.attention_workspace(rows, H, D) if split else None
+    print(f"[attn] D={D} H={H} S={S} rows={rows} split={split}", flush=True)
+    B.pf_attention(dev(torch, q, torch.bfloat16), kv, S, rows, H, D, o, workspace=ws)
     want = ref.attention(q[:, :h], K, V, H, D)
     assert_close(host(o), ref.bf16_round(want), f"attention bf16 D={D} S={S} rows={rows} vs bf16-in")
     assert_close(host(o), want, f"attention bf16 D={D} S={S} rows={rows} vs exact")

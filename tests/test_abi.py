@@ -107,10 +107,16 @@ def test_component_validation(lib):
     assert lib.pf_gemm(base, 128, base, base, 10, 128, 128, 3, base, 128, None, B.PF_BF16, None) == B.PF_ERR_INVALID_ARG
     # attention: head_dim 80 unsupported, bf16 needs K8 V
     kv = _view(base, base + (1 << 30), 1000, elems=160, layout=B.PF_LAYOUT_K8)
-    assert lib.pf_attention(base, 480, ctypes.byref(kv), 1000, 10, 2, 80, base, 160, None) == B.PF_ERR_UNSUPPORTED
+    assert lib.pf_attention(base, 480, ctypes.byref(kv), 1000, 10, 2, 80, base, 160, None, 0, None) == B.PF_ERR_UNSUPPORTED
     kv2 = _view(base, base + (1 << 30), 1000, elems=128, layout=B.PF_LAYOUT_ROWS)
-    assert lib.pf_attention(base, 384, ctypes.byref(kv2), 1000, 10, 2, 64, base, 128, None) == B.PF_ERR_UNSUPPORTED
-    assert lib.pf_attention(base, 384, ctypes.byref(kv), 1001, 10, 2, 64, base, 128, None) == B.PF_ERR_INVALID_ARG
+    assert lib.pf_attention(base, 384, ctypes.byref(kv2), 1000, 10, 2, 64, base, 128, None, 0, None) == B.PF_ERR_UNSUPPORTED
+    assert lib.pf_attention(base, 384, ctypes.byref(kv), 1001, 10, 2, 64, base, 128, None, 0, None) == B.PF_ERR_INVALID_ARG
+    # misaligned workspace
+    assert lib.pf_attention(base, 384, ctypes.byref(kv), 1000, 10, 2, 64, base, 128, base + 8, 1 << 20, None) == B.PF_ERR_INVALID_ARG
+    # workspace size query: 8 splits of fp32 partial rows plus (m, l) per split
+    n = ctypes.c_uint64()
+    assert lib.pf_attention_workspace_size(1024, 16, 72, ctypes.byref(n)) == B.PF_OK
+    assert n.value == 4 * (8 * 1024 * 1152 + 2 * 8 * 1024 * 16)
     # misaligned pointer
     assert lib.pf_ln_modulate(base + 4, 3, 64, base, base, 1e-6, base, 0, None) == B.PF_ERR_INVALID_ARG
 

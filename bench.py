@@ -71,12 +71,14 @@ def kernel_probes(torch, B, st, shape, layer_w):
     qkv_src = B.KVView(k=qkv.data_ptr() + h * 2, v=qkv.data_ptr() + 2 * h * 2, rows=P, row_elems=h, k_ld=3 * h,
                        v_ld=3 * h, dtype=B.PF_BF16, v_layout=B.PF_LAYOUT_ROWS)
     off = shape.patch_offsets()[-1]
+    ws = B.attention_workspace(P, shape.heads, shape.head_dim)   # same split choice as the stage
     w = layer_w
     probes = {
         "ln_modulate": (lambda: B.pf_ln_modulate(x, shift, scale, 1e-6, h1), 12.0 * P * h, "hbm"),
         "gemm_qkv": (lambda: B.pf_gemm(h1, w["w_qkv"], w["b_qkv"], B.PF_EPI_STORE, qkv), 6.0 * P * h * h, "mfma"),
         "kv_splice": (lambda: B.kvbuf_splice(kv, qkv_src, off, P), 8.0 * P * h, "hbm"),
-        "attention": (lambda: B.pf_attention(qkv, kv, S, P, shape.heads, shape.head_dim, o), 4.0 * P * S * h, "mfma"),
+        "attention": (lambda: B.pf_attention(qkv, kv, S, P, shape.heads, shape.head_dim, o, workspace=ws),
+                      4.0 * P * S * h, "mfma"),
         "gemm_out": (lambda: B.pf_gemm(o, w["w_o"], w["b_o"], B.PF_EPI_GATED_RESIDUAL, x, gate=gate),
                      2.0 * P * h * h, "mfma"),
     }

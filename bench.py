@@ -71,22 +71,25 @@ def kernel_probes(torch, B, st, shape, layer_w):
     qkv_src = B.KVView(k=qkv.data_ptr() + h * 2, v=qkv.data_ptr() + 2 * h * 2, rows=P, row_elems=h, k_ld=3 * h,
                        v_ld=3 * h, dtype=B.PF_BF16, v_layout=B.PF_LAYOUT_ROWS)
     off = shape.patch_offsets()[-1]
-    ws = B.attention_workspace(P, shape.heads, shape.head_dim)   # same split choice as the stage
+    ws = B.attention_workspace(P, shape.heads, shape.head_dim)   # same split choices as the stage
+    gws = {k: B.gemm_workspace(P, n, kk) for k, (n, kk) in
+           {"qkv": (3 * h, h), "out": (h, h), "up": (r * h, h), "down": (h, r * h)}.items() if n > 0}
     w = layer_w
     probes = {
         "ln_modulate": (lambda: B.pf_ln_modulate(x, shift, scale, 1e-6, h1), 12.0 * P * h, "hbm"),
-        "gemm_qkv": (lambda: B.pf_gemm(h1, w["w_qkv"], w["b_qkv"], B.PF_EPI_STORE, qkv), 6.0 * P * h * h, "mfma"),
+        "gemm_qkv": (lambda: B.pf_gemm(h1, w["w_qkv"], w["b_qkv"], B.PF_EPI_STORE, qkv, workspace=gws["qkv"]),
+                     6.0 * P * h * h, "mfma"),
         "kv_splice": (lambda: B.kvbuf_splice(kv, qkv_src, off, P), 8.0 * P * h, "hbm"),
         "attention": (lambda: B.pf_attention(qkv, kv, S, P, shape.heads, shape.head_dim, o, workspace=ws),
                       4.0 * P * S * h, "mfma"),
-        "gemm_out": (lambda: B.pf_gemm(o, w["w_o"], w["b_o"], B.PF_EPI_GATED_RESIDUAL, x, gate=gate),
-                     2.0 * P * h * h, "mfma"),
+        "gemm_out": (lambda: B.pf_gemm(o, w["w_o"], w["b_o"], B.PF_EPI_GATED_RESIDUAL, x, gate=gate,
+                                       workspace=gws["out"]), 2.0 * P * h * h, "mfma"),
     }
     if r > 0:
-        probes["gemm_up_gelu"] = (lambda: B.pf_gemm(h1, w["w1"], w["b1"], B.PF_EPI_GELU_TANH, u), 2.0 * r * P * h * h,
-                                  "mfma")
-        probes["gemm_down"] = (lambda: B.pf_gemm(u, w["w2"], w["b2"], B.PF_EPI_GATED_RESIDUAL, x, gate=gate),
-                               2.0 * r * P * h * h, "mfma")
+        probes["gemm_up_gelu"] = (lambda: B.pf_gemm(h1, w["w1"], w["b1"], B.PF_EPI_GELU_TANH, u,
+                                                    workspace=gws["up"]), 2.0 * r * P * h * h, "mfma")
+        probes["gemm_down"] = (lambda: B.pf_gemm(u, w["w2"], w["b2"], B.PF_EPI_GATED_RESIDUAL, x, gate=gate,
+                                                 workspace=gws["down"]), 2.0 * r * P * h * h, "mfma")
     return probes
 
 

@@ -189,10 +189,15 @@ pf_status pf_ln_modulate(const float* x, int64_t rows, int32_t hidden, const flo
 /* y = a . w^T + bias with a [m, k] (row stride lda), w [n, k] (row-major), bias fp32 [n],
  * then the epilogue `epi` (pf_epilogue) into c (row stride ldc).  a/w/c in `dtype`, except
  * c is fp32 for PF_EPI_GATED_RESIDUAL (gate fp32 [n]).  fp32 accumulation.  For bf16:
- * n % 64 == 0 and k % 64 == 0. */
+ * n % 64 == 0 and k % 64 == 0.  `workspace` (device, may be NULL) lets a grid too small to
+ * fill the GPU split k into slices summed by a second pass (in a fixed order: deterministic);
+ * pf_gemm_workspace_size gives the bytes that allow the split the library would choose. */
 pf_status pf_gemm(const void* a, int64_t lda, const void* w, const float* bias, int64_t m,
                   int64_t n, int64_t k, int32_t epi, void* c, int64_t ldc, const float* gate,
-                  int32_t dtype, void* stream);
+                  int32_t dtype, void* workspace, uint64_t workspace_bytes, void* stream);
+
+/* Workspace bytes pf_gemm can use for an [m, n, k] bf16 product (0: it never splits). */
+pf_status pf_gemm_workspace_size(int64_t m, int64_t n, int64_t k, uint64_t* bytes);
 
 /* Full non-causal attention of `rows` query rows over the first seq_kv rows of kv:
  * for head j (columns [j*d, (j+1)*d)): O_j = softmax(Q_j K_j^T / sqrt(d)) V_j.

@@ -64,7 +64,8 @@ _SIGNATURES = {
     "kvbuf_splice": [ctypes.POINTER(KVView), ctypes.POINTER(KVView), _I64, _I64, _P],
     "stage_get_kvbuf": [_P, _I32, ctypes.POINTER(KVView)],
     "pf_ln_modulate": [_P, _I64, _I32, _P, _P, _F, _P, _I32, _P],
-    "pf_gemm": [_P, _I64, _P, _P, _I64, _I64, _I64, _I32, _P, _I64, _P, _I32, _P],
+    "pf_gemm": [_P, _I64, _P, _P, _I64, _I64, _I64, _I32, _P, _I64, _P, _I32, _P, ctypes.c_uint64, _P],
+    "pf_gemm_workspace_size": [_I64, _I64, _I64, ctypes.POINTER(ctypes.c_uint64)],
     "pf_attention": [_P, _I64, ctypes.POINTER(KVView), _I64, _I64, _I32, _I32, _P, _I64, _P, ctypes.c_uint64, _P],
     "pf_attention_workspace_size": [_I64, _I32, _I32, ctypes.POINTER(ctypes.c_uint64)],
     "pf_adaln": [_P, _P, _P, _I32, _P, _I32, _P],
@@ -174,13 +175,27 @@ def pf_ln_modulate(x, shift, scale, eps: float, y, stream=None) -> None:
                                 _stream(stream)))
 
 
-def pf_gemm(a, w, bias, epi: int, c, gate=None, m=None, lda=None, ldc=None, stream=None) -> None:
+def pf_gemm(a, w, bias, epi: int, c, gate=None, m=None, lda=None, ldc=None, workspace=None, stream=None) -> None:
     n, k = w.shape
     m = a.shape[0] if m is None else m
     lda = a.stride(0) if lda is None else lda
     ldc = c.stride(0) if ldc is None else ldc
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().pf_gemm(_ptr(a), lda, _ptr(w), _ptr(bias), m, n, k, epi, _ptr(c), ldc, _ptr(gate),
-                         _dtype_code(w), _stream(stream)))
+                         _dtype_code(w), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def pf_gemm_workspace_size(m: int, n: int, k: int) -> int:
+    b = ctypes.c_uint64()
+    _check(lib().pf_gemm_workspace_size(m, n, k, ctypes.byref(b)))
+    return b.value
+
+
+def gemm_workspace(m: int, n: int, k: int):
+    """torch uint8 device buffer of pf_gemm_workspace_size bytes (None when zero)."""
+    import torch
+    nb = pf_gemm_workspace_size(m, n, k)
+    return torch.empty((nb,), dtype=torch.uint8, device="cuda") if nb else None
 
 
 def pf_attention(q, kv: KVView, seq_kv: int, rows: int, heads: int, head_dim: int, o, ldq=None, ldo=None,

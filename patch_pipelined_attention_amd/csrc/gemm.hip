@@ -7,11 +7,9 @@
 // per lane, one token and 4 consecutive output features per 8-row group, so every
 // epilogue stores 4 contiguous values per access (8 B bf16 / 16 B fp32).
 //
-// Tile: 128 tokens x 128 features x 64 k per iteration, 256 threads = 4 wavefronts in a
-// 2x2 grid, each owning 64 features x 64 tokens = 2x2 MFMA blocks.  Global tiles are
-// prefetched into registers while the current LDS tile is consumed.  LDS rows are padded
-// to 72 elements (144 B = 9 x 16 B) so the 16-byte fragment reads of 16 consecutive rows
-// fall in distinct bank groups.
+// Tiles: 256 x 256 (each wavefront 128 x 128 = 4 x 4 MFMA blocks, 0.5 KB of LDS operand
+// reads per MFMA) when the grid of big tiles fills the GPU, else 128 x 128, split along k
+// with a reduce pass when even those are too few.
 //
 // fp32 path (tiny fp32 stages only): a plain 64x64 LDS-tiled FMA kernel.
 #include "pf_internal.h"
@@ -33,123 +31,193 @@ __device__ __forceinline__ float epi_act(float v) {
   else return v;
 }
 
-namespace {
-constexpr int kBT = 128;   // tokens per tile
-constexpr int kBF = 128;   // features per tile
-constexpr int kBK = 64;    // k per iteration
-constexpr int kLdsLd = kBK + 8;
-}  // namespace
+__device__ __forceinline__ int gemm_xcd_remap(int bid, int nb) {
+  const int per = nb / 8, rem = nb % 8;
+  const int x = bid % 8;
+  return x * per + (x < rem ? x : rem) + bid / 8;
+}
 
-template <int EPI>
-__global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const bf16* __restrict__ A, int64_t lda,
-                                                           const bf16* __restrict__ W,
-                                                           const float* __restrict__ bias, int64_t M,
-                                                           int64_t N, int64_t K, void* __restrict__ C,
-                                                           int64_t ldc, const float* __restrict__ gate,
-                                                           int tiles_n) {
-  __shared__ __attribute__((aligned(16))) bf16 sW[kBF * kLdsLd];
-  __shared__ __attribute__((aligned(16))) bf16 sX[kBT * kLdsLd];
+// bf16 tile kernel: BF features x BT tokens per workgroup (4 wavefronts in a 2 x 2 grid, each
+// (BF/2) x (BT/2) = FB x TB blocks of 32 x 32), k staged 64 at a time (4 MFMA k-steps per
+// barrier).  The W rows and X rows of a k tile are copied global -> LDS with direct 16-byte
+// loads into a 2-stage ring (one tile ahead; the other resident workgroup covers the rest of
+// the latency); LDS units are swizzled so every 8-lane operand read phase hits distinct bank
+// groups, and the operands of k-step s+1 are read while the MFMAs of step s run.  With
+// SPLIT, the workgroup covers one slice of the k range and writes an fp32 partial tile;
+// gemm_reduce_kernel then sums the slices and applies the epilogue.
+template <int BF, int BT, int EPI, bool SPLIT>
+__global__ __launch_bounds__(256, (BF * BT >= 256 * 256) ? 1 : 2) void gemm_bf16_kernel(
+    const bf16* __restrict__ A, int64_t lda, const bf16* __restrict__ W, const float* __restrict__ bias, int64_t M,
+    int64_t N, int64_t K, void* __restrict__ C, int64_t ldc, const float* __restrict__ gate, int tiles_n,
+    int n_split, int ktiles_per_split, float* __restrict__ part) {
+  constexpr int BK = 64;                 // k per stage: four MFMA k-steps
+  constexpr int KSTEPS = BK / 16;
+  constexpr int ROWS = BF + BT;          // stage rows: W rows, then X rows
+  constexpr int UNITS = ROWS * 8;        // 16-byte units per stage (8 per row)
+  constexpr int NINST = UNITS / 64;      // 64-lane direct loads per stage
+  constexpr int NPW = NINST / 4;         // per wavefront
+  constexpr int NSTAGE = 2;
+  constexpr int FB = BF / 64, TB = BT / 64;
+  static_assert(NINST % 4 == 0, "stage must split evenly over 4 wavefronts");
+  __shared__ __attribute__((aligned(16))) uint4 lds[NSTAGE][UNITS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
   const int wf = wave & 1, wt = wave >> 1;
 
-  const int tile_n = blockIdx.x % tiles_n;
-  const int64_t tile_m = blockIdx.x / tiles_n;
-  const int64_t n0 = (int64_t)tile_n * kBF;
-  const int64_t m0 = tile_m * kBT;
+  const int lid = gemm_xcd_remap(blockIdx.x, gridDim.x);
+  const int split = lid % n_split;
+  const int rest = lid / n_split;
+  const int tile_n = rest % tiles_n;
+  const int64_t tile_m = rest / tiles_n;
+  const int64_t n0 = (int64_t)tile_n * BF;
+  const int64_t m0 = tile_m * BT;
+  const int64_t nkt = K / BK;
+  const int64_t kt0 = (int64_t)split * ktiles_per_split;
+  const int64_t kt1 = kt0 + ktiles_per_split < nkt ? kt0 + ktiles_per_split : nkt;
 
-  // global -> register staging: 4 chunks of 16 B of W and of X per thread per k tile
-  uint4 rw[4], rx[4];
-  auto load_tile = [&](int64_t k0) {
+  // unit of (row, chunk c in 0..7): rows r..r+7 at one chunk land in 8 distinct bank groups
+  auto unit = [](int r, int c) { return r * 8 + (c ^ (r & 7)); };
+
+  // per-lane source of each of this wavefront's loads (rows past M or N read a clamped row;
+  // their results are never stored)
+  const char* src[NPW];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i;
-      const int row = c >> 3, kc = c & 7;
-      const int64_t n = n0 + row, m = m0 + row;
-      rw[i] = n < N ? *reinterpret_cast<const uint4*>(W + n * K + k0 + kc * 8) : make_uint4(0, 0, 0, 0);
-      rx[i] = m < M ? *reinterpret_cast<const uint4*>(A + m * lda + k0 + kc * 8) : make_uint4(0, 0, 0, 0);
+  for (int j = 0; j < NPW; ++j) {
+    const int u = (wave + 4 * j) * 64 + lane;
+    const int r = u >> 3;
+    const int c = (u & 7) ^ (r & 7);
+    if (r < BF) {
+      int64_t n = n0 + r;
+      n = n < N ? n : N - 1;
+      src[j] = reinterpret_cast<const char*>(W + n * K + c * 8);
+    } else {
+      int64_t m = m0 + (r - BF);
+      m = m < M ? m : M - 1;
+      src[j] = reinterpret_cast<const char*>(A + m * lda + c * 8);
     }
-  };
-  auto store_tile = [&]() {
+  }
+  auto issue = [&](int64_t kt, int st) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i;
-      const int row = c >> 3, kc = c & 7;
-      *reinterpret_cast<uint4*>(&sW[row * kLdsLd + kc * 8]) = rw[i];
-      *reinterpret_cast<uint4*>(&sX[row * kLdsLd + kc * 8]) = rx[i];
-    }
+    for (int j = 0; j < NPW; ++j)
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src[j] + kt * BK * 2),
+                                       (__attribute__((address_space(3))) void*)&lds[st][(wave + 4 * j) * 64], 16, 0,
+                                       0);
   };
 
-  f32x16 acc[2][2];
+  f32x16 acc[FB][TB];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < FB; ++i)
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < TB; ++t)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][t][e] = 0.f;
 
-  const int64_t nk = K / kBK;
-  load_tile(0);
-  store_tile();
-  __syncthreads();
-  for (int64_t kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) load_tile((kt + 1) * kBK);
+  auto read_frags = [&](const uint4* L, int ks, bf16x8 (&a)[FB], bf16x8 (&b)[TB]) {
 #pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
-      bf16x8 a[2], b[2];
+    for (int i = 0; i < FB; ++i)
+      a[i] = *reinterpret_cast<const bf16x8*>(&L[unit(wf * (BF / 2) + i * 32 + l32, 2 * ks + hi)]);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        a[i] = *reinterpret_cast<const bf16x8*>(&sW[(wf * 64 + i * 32 + l32) * kLdsLd + kk * 16 + hi * 8]);
+    for (int t = 0; t < TB; ++t)
+      b[t] = *reinterpret_cast<const bf16x8*>(&L[unit(BF + wt * (BT / 2) + t * 32 + l32, 2 * ks + hi)]);
+  };
+
+  issue(kt0, 0);
+  int st = 0;
+  for (int64_t kt = kt0; kt < kt1; ++kt) {
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));   // this wavefront's loads of tile kt are done
+    __syncthreads();   // ... for every wavefront; all are done reading the other stage
+    if (kt + 1 < kt1) issue(kt + 1, st ^ 1);
+    const uint4* L = lds[st];
+    bf16x8 a[2][FB], b[2][TB];
+    read_frags(L, 0, a[0], b[0]);
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
-        b[t] = *reinterpret_cast<const bf16x8*>(&sX[(wt * 64 + t * 32 + l32) * kLdsLd + kk * 16 + hi * 8]);
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      if (ks + 1 < KSTEPS) read_frags(L, ks + 1, a[(ks + 1) & 1], b[(ks + 1) & 1]);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < FB; ++i)
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
-          acc[i][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[t], acc[i][t], 0, 0, 0);
+        for (int t = 0; t < TB; ++t)
+          acc[i][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks & 1][i], b[ks & 1][t], acc[i][t], 0, 0, 0);
     }
-    __syncthreads();
-    if (kt + 1 < nk) {
-      store_tile();
-      __syncthreads();
-    }
+    st ^= 1;
   }
 
-  // Epilogue.  acc[i][t][4g+j] = y[token = m0 + wt*64 + t*32 + l32][feature = n0 + wf*64 + i*32 + 8g + 4hi + j]
+  // acc[i][t][4g+j] = y[token = m0 + wt*BT/2 + t*32 + l32][feature = n0 + wf*BF/2 + i*32 + 8g + 4hi + j]
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int64_t m = m0 + wt * 64 + t * 32 + l32;
+  for (int t = 0; t < TB; ++t) {
+    const int64_t m = m0 + wt * (BT / 2) + t * 32 + l32;
     if (m >= M) continue;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < FB; ++i) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int64_t f = n0 + wf * 64 + i * 32 + 8 * g + 4 * hi;
+        const int64_t f = n0 + wf * (BF / 2) + i * 32 + 8 * g + 4 * hi;
         if (f >= N) continue;
-        const float4 bv = *reinterpret_cast<const float4*>(bias + f);
-        float v0 = acc[i][t][4 * g + 0] + bv.x;
-        float v1 = acc[i][t][4 * g + 1] + bv.y;
-        float v2 = acc[i][t][4 * g + 2] + bv.z;
-        float v3 = acc[i][t][4 * g + 3] + bv.w;
-        if constexpr (EPI == kEpiGatedResidual) {
-          float* cp = static_cast<float*>(C) + m * ldc + f;
-          const float4 gv = *reinterpret_cast<const float4*>(gate + f);
-          float4 cv = *reinterpret_cast<float4*>(cp);
-          cv.x += gv.x * v0;
-          cv.y += gv.y * v1;
-          cv.z += gv.z * v2;
-          cv.w += gv.w * v3;
-          *reinterpret_cast<float4*>(cp) = cv;
+        if constexpr (SPLIT) {
+          *reinterpret_cast<float4*>(part + ((int64_t)split * M + m) * N + f) =
+              make_float4(acc[i][t][4 * g + 0], acc[i][t][4 * g + 1], acc[i][t][4 * g + 2], acc[i][t][4 * g + 3]);
         } else {
-          bf16x4 o = {(bf16)epi_act<EPI>(v0), (bf16)epi_act<EPI>(v1), (bf16)epi_act<EPI>(v2),
-                      (bf16)epi_act<EPI>(v3)};
-          *reinterpret_cast<bf16x4*>(static_cast<bf16*>(C) + m * ldc + f) = o;
+          const float4 bv = *reinterpret_cast<const float4*>(bias + f);
+          const float v0 = acc[i][t][4 * g + 0] + bv.x;
+          const float v1 = acc[i][t][4 * g + 1] + bv.y;
+          const float v2 = acc[i][t][4 * g + 2] + bv.z;
+          const float v3 = acc[i][t][4 * g + 3] + bv.w;
+          if constexpr (EPI == kEpiGatedResidual) {
+            float* cp = static_cast<float*>(C) + m * ldc + f;
+            const float4 gv = *reinterpret_cast<const float4*>(gate + f);
+            float4 cv = *reinterpret_cast<float4*>(cp);
+            cv.x += gv.x * v0;
+            cv.y += gv.y * v1;
+            cv.z += gv.z * v2;
+            cv.w += gv.w * v3;
+            *reinterpret_cast<float4*>(cp) = cv;
+          } else {
+            bf16x4 o = {(bf16)epi_act<EPI>(v0), (bf16)epi_act<EPI>(v1), (bf16)epi_act<EPI>(v2),
+                        (bf16)epi_act<EPI>(v3)};
+            *reinterpret_cast<bf16x4*>(static_cast<bf16*>(C) + m * ldc + f) = o;
+          }
         }
       }
     }
+  }
+}
+
+// Sum of the k slices of a split GEMM, then bias and the epilogue.  One thread per 4
+// consecutive outputs of a row; slices are summed in order, so the result is deterministic.
+template <int EPI>
+__global__ __launch_bounds__(256) void gemm_reduce_kernel(const float* __restrict__ part, int n_split, int64_t M,
+                                                          int64_t N, const float* __restrict__ bias,
+                                                          void* __restrict__ C, int64_t ldc,
+                                                          const float* __restrict__ gate) {
+  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t nq = N / 4;
+  if (id >= M * nq) return;
+  const int64_t m = id / nq;
+  const int64_t f = (id - m * nq) * 4;
+  float4 s = *reinterpret_cast<const float4*>(part + m * N + f);
+  for (int sp = 1; sp < n_split; ++sp) {
+    const float4 v = *reinterpret_cast<const float4*>(part + ((int64_t)sp * M + m) * N + f);
+    s.x += v.x;
+    s.y += v.y;
+    s.z += v.z;
+    s.w += v.w;
+  }
+  const float4 bv = *reinterpret_cast<const float4*>(bias + f);
+  const float v0 = s.x + bv.x, v1 = s.y + bv.y, v2 = s.z + bv.z, v3 = s.w + bv.w;
+  if constexpr (EPI == kEpiGatedResidual) {
+    float* cp = static_cast<float*>(C) + m * ldc + f;
+    const float4 gv = *reinterpret_cast<const float4*>(gate + f);
+    float4 cv = *reinterpret_cast<float4*>(cp);
+    cv.x += gv.x * v0;
+    cv.y += gv.y * v1;
+    cv.z += gv.z * v2;
+    cv.w += gv.w * v3;
+    *reinterpret_cast<float4*>(cp) = cv;
+  } else {
+    bf16x4 o = {(bf16)epi_act<EPI>(v0), (bf16)epi_act<EPI>(v1), (bf16)epi_act<EPI>(v2), (bf16)epi_act<EPI>(v3)};
+    *reinterpret_cast<bf16x4*>(static_cast<bf16*>(C) + m * ldc + f) = o;
   }
 }
 
@@ -209,33 +277,110 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
   }
 }
 
+#ifndef PF_GEMM_BIG_TILES
+#define PF_GEMM_BIG_TILES 0
+#endif
+constexpr bool kGemmBigTiles = PF_GEMM_BIG_TILES;
+
+// Launch plan of a bf16 GEMM: tile size and k-split count.
+struct GemmPlan {
+  int big;      // 1: 256 x 256 tiles (1 workgroup per CU), 0: 128 x 128 tiles (2 per CU)
+  int split;    // k slices (1 = no split)
+};
+
+static int gemm_cus() {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) ==
+                                                hipSuccess && v > 0)
+      cus = v;
+    else
+      cus = 256;
+    (void)hipGetLastError();
+  }
+  return cus;
+}
+
+// Big tiles when they alone give every CU work; otherwise 128 x 128 tiles, split along k
+// (each slice >= 4 k tiles of 64) when that lowers the estimated time: rounds of resident
+// workgroups x the slice's compute, plus writing and re-reading the fp32 partials.
+static GemmPlan gemm_plan(int64_t m, int64_t n, int64_t k, size_t ws_bytes) {
+  const int cus = gemm_cus();
+  const int64_t big_tiles = ((m + 255) / 256) * ((n + 255) / 256);
+  if (kGemmBigTiles && big_tiles >= cus) return {1, 1};
+  const int64_t tiles = ((m + 127) / 128) * ((n + 127) / 128);
+  const int64_t slots = 2 * (int64_t)cus;
+  const double tile_s = 2.0 * 128 * 128 * (double)k / 2.0e12;   // one resident tile at ~2 TFLOP/s
+  const double bytes_s = 1.0 / 5.0e12;                           // partial traffic at ~5 TB/s
+  int split = 1;
+  double best = (double)((tiles + slots - 1) / slots) * tile_s;
+  for (int sp = 2; sp <= kMaxGemmSplit; ++sp) {
+    if (k / 64 < 4LL * sp) break;
+    if ((size_t)sp * m * n * sizeof(float) > ws_bytes) break;
+    const double t = (double)((tiles * sp + slots - 1) / slots) * tile_s / sp +
+                     2.0 * sp * (double)m * (double)n * sizeof(float) * bytes_s;
+    if (t < best) {
+      best = t;
+      split = sp;
+    }
+  }
+  return {0, split};
+}
+
+size_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k) {
+  const GemmPlan p = gemm_plan(m, n, k, (size_t)-1);
+  return p.split > 1 ? (size_t)p.split * m * n * sizeof(float) : 0;
+}
+
 template <int EPI>
-static void launch_gemm_epi(const void* a, int64_t lda, const void* w, const float* bias, int64_t m,
-                            int64_t n, int64_t k, void* c, int64_t ldc, const float* gate, int dtype,
-                            hipStream_t s) {
+static void launch_gemm_epi(const void* a, int64_t lda, const void* w, const float* bias, int64_t m, int64_t n,
+                            int64_t k, void* c, int64_t ldc, const float* gate, int dtype, void* ws,
+                            size_t ws_bytes, hipStream_t s) {
   if (dtype == kDtypeBF16) {
-    const int tiles_n = (int)((n + kBF - 1) / kBF);
-    const int64_t tiles = (int64_t)tiles_n * ((m + kBT - 1) / kBT);
-    hipLaunchKernelGGL(gemm_bf16_kernel<EPI>, dim3((unsigned)tiles), dim3(256), 0, s,
-                       static_cast<const bf16*>(a), lda, static_cast<const bf16*>(w), bias, m, n, k, c, ldc,
-                       gate, tiles_n);
+    const bf16* A = static_cast<const bf16*>(a);
+    const bf16* Wt = static_cast<const bf16*>(w);
+    const GemmPlan p = gemm_plan(m, n, k, ws ? ws_bytes : 0);
+    const int nkt = (int)(k / 64);
+    if (p.big) {
+      const int tiles_n = (int)((n + 255) / 256);
+      const int64_t tiles = (int64_t)tiles_n * ((m + 255) / 256);
+      hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, EPI, false>), dim3((unsigned)tiles), dim3(256), 0, s, A, lda, Wt,
+                         bias, m, n, k, c, ldc, gate, tiles_n, 1, nkt, nullptr);
+    } else {
+      const int tiles_n = (int)((n + 127) / 128);
+      const int64_t tiles = (int64_t)tiles_n * ((m + 127) / 128);
+      if (p.split == 1) {
+        hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, EPI, false>), dim3((unsigned)tiles), dim3(256), 0, s, A, lda,
+                           Wt, bias, m, n, k, c, ldc, gate, tiles_n, 1, nkt, nullptr);
+      } else {
+        const int kps = (nkt + p.split - 1) / p.split;
+        const int used = (nkt + kps - 1) / kps;
+        float* part = static_cast<float*>(ws);
+        hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, EPI, true>), dim3((unsigned)(tiles * used)), dim3(256), 0, s, A,
+                           lda, Wt, bias, m, n, k, c, ldc, gate, tiles_n, used, kps, part);
+        const int64_t units = m * (n / 4);
+        hipLaunchKernelGGL(gemm_reduce_kernel<EPI>, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, s, part, used,
+                           m, n, bias, c, ldc, gate);
+      }
+    }
   } else {
     const int tiles_n = (int)((n + 63) / 64);
     const int64_t tiles = (int64_t)tiles_n * ((m + 63) / 64);
-    hipLaunchKernelGGL(gemm_f32_kernel<EPI>, dim3((unsigned)tiles), dim3(256), 0, s,
-                       static_cast<const float*>(a), lda, static_cast<const float*>(w), bias, m, n, k,
-                       static_cast<float*>(c), ldc, gate, tiles_n);
+    hipLaunchKernelGGL(gemm_f32_kernel<EPI>, dim3((unsigned)tiles), dim3(256), 0, s, static_cast<const float*>(a), lda,
+                       static_cast<const float*>(w), bias, m, n, k, static_cast<float*>(c), ldc, gate, tiles_n);
   }
 }
 
-hipError_t launch_gemm(const void* a, int64_t lda, const void* w, const float* bias, int64_t m, int64_t n,
-                       int64_t k, int epi, void* c, int64_t ldc, const float* gate, int dtype, hipStream_t s) {
+hipError_t launch_gemm(const void* a, int64_t lda, const void* w, const float* bias, int64_t m, int64_t n, int64_t k,
+                       int epi, void* c, int64_t ldc, const float* gate, int dtype, void* ws, size_t ws_bytes,
+                       hipStream_t s) {
   if (m <= 0) return hipSuccess;
   switch (epi) {
-    case kEpiStore: launch_gemm_epi<kEpiStore>(a, lda, w, bias, m, n, k, c, ldc, gate, dtype, s); break;
-    case kEpiGeluTanh: launch_gemm_epi<kEpiGeluTanh>(a, lda, w, bias, m, n, k, c, ldc, gate, dtype, s); break;
-    case kEpiGeluErf: launch_gemm_epi<kEpiGeluErf>(a, lda, w, bias, m, n, k, c, ldc, gate, dtype, s); break;
-    default: launch_gemm_epi<kEpiGatedResidual>(a, lda, w, bias, m, n, k, c, ldc, gate, dtype, s); break;
+    case kEpiStore: launch_gemm_epi<kEpiStore>(a, lda, w, bias, m, n, k, c, ldc, gate, dtype, ws, ws_bytes, s); break;
+    case kEpiGeluTanh: launch_gemm_epi<kEpiGeluTanh>(a, lda, w, bias, m, n, k, c, ldc, gate, dtype, ws, ws_bytes, s); break;
+    case kEpiGeluErf: launch_gemm_epi<kEpiGeluErf>(a, lda, w, bias, m, n, k, c, ldc, gate, dtype, ws, ws_bytes, s); break;
+    default: launch_gemm_epi<kEpiGatedResidual>(a, lda, w, bias, m, n, k, c, ldc, gate, dtype, ws, ws_bytes, s); break;
   }
   return hipGetLastError();
 }

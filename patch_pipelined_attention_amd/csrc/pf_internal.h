@@ -45,9 +45,15 @@ hipError_t launch_ln_modulate(const float* x, int64_t rows, int hidden, const fl
 hipError_t launch_adaln(const float* cond, const void* w, const float* b, int hidden, float* mod,
                         int dtype, hipStream_t s);
 
+// `ws` (may be NULL) is scratch for the k-split of grids too small to fill the GPU.
 hipError_t launch_gemm(const void* a, int64_t lda, const void* w, const float* bias, int64_t m,
                        int64_t n, int64_t k, int epi, void* c, int64_t ldc, const float* gate,
-                       int dtype, hipStream_t s);
+                       int dtype, void* ws, size_t ws_bytes, hipStream_t s);
+
+// Scratch bytes the bf16 GEMM would use for its k-split at this shape (0: no split).
+size_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k);
+
+constexpr int kMaxGemmSplit = 8;
 
 // `ws` (may be NULL) is scratch for the key-range split of small query grids; the split
 // count is chosen so its partial results fit in ws_bytes (NULL: no split).

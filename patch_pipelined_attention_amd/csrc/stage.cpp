@@ -195,12 +195,23 @@ extern "C" pf_status pf_ln_modulate(const float* x, int64_t rows, int32_t hidden
 
 extern "C" pf_status pf_gemm(const void* a, int64_t lda, const void* w, const float* bias, int64_t m, int64_t n,
                              int64_t k, int32_t epi, void* c, int64_t ldc, const float* gate, int32_t dtype,
-                             void* stream) {
+                             void* workspace, uint64_t workspace_bytes, void* stream) {
   pf_status st = validate_gemm(a, lda, w, bias, m, n, k, epi, c, ldc, gate, dtype);
   if (st != PF_OK) return st;
+  if (workspace && !aligned16(workspace)) return fail(PF_ERR_INVALID_ARG, "gemm: workspace must be 16-byte aligned");
   if ((st = check_device()) != PF_OK) return st;
-  hipError_t e = launch_gemm(a, lda, w, bias, m, n, k, epi, c, ldc, gate, dtype, (hipStream_t)stream);
+  hipError_t e = launch_gemm(a, lda, w, bias, m, n, k, epi, c, ldc, gate, dtype, workspace,
+                             workspace ? (size_t)workspace_bytes : 0, (hipStream_t)stream);
   return e == hipSuccess ? PF_OK : hip_fail(e, "gemm launch");
+}
+
+extern "C" pf_status pf_gemm_workspace_size(int64_t m, int64_t n, int64_t k, uint64_t* bytes) {
+  if (!bytes) return fail(PF_ERR_INVALID_ARG, "gemm_workspace_size: null out");
+  if (m < 0 || n <= 0 || k <= 0) return fail(PF_ERR_INVALID_ARG, "gemm_workspace_size: bad sizes");
+  pf_status st = check_device();   // the plan depends on the device's CU count
+  if (st != PF_OK) return st;
+  *bytes = gemm_workspace_bytes(m, n, k);
+  return PF_OK;
 }
 
 extern "C" pf_status pf_attention(const void* q, int64_t ldq, const pf_kv_view* kv, int64_t seq_kv, int64_t rows,
@@ -276,6 +287,8 @@ struct pf_stage {
   void *h1, *qkv, *o, *u;
   void* attn_ws = nullptr;   // key-range split partials of the patch attention
   size_t attn_ws_bytes = 0;
+  void* gemm_ws = nullptr;   // k-split partials of the projections
+  size_t gemm_ws_bytes = 0;
   std::vector<LayerMem> layers;
   bool cond_set = false;
   bool broken = false;   // a HIP call failed: every later call returns PF_ERR_HIP
@@ -316,7 +329,8 @@ static void free_stage_mem(pf_stage* st) {
   if (st->scratch) (void)hipFree(st->scratch);
   if (st->modmem) (void)hipFree(st->modmem);
   if (st->attn_ws) (void)hipFree(st->attn_ws);
-  st->attn_ws = nullptr;
+  if (st->gemm_ws) (void)hipFree(st->gemm_ws);
+  st->attn_ws = st->gemm_ws = nullptr;
   st->wmem = st->kvmem = st->scratch = nullptr;
   st->modmem = nullptr;
 }
@@ -354,10 +368,21 @@ extern "C" pf_status stage_create(const pf_stage_config* cfg, pf_stage** out) {
   // split partials for a patch or the text prefix (the warm-up pass fills the GPU unsplit)
   const int64_t split_rows = std::max<int64_t>(st->patch_rows, cfg->seq_txt);
   st->attn_ws_bytes = cfg->dtype == PF_BF16 ? attention_workspace_bytes(split_rows, h, cfg->heads, kMaxAttnSplit) : 0;
+  // k-split partials for the projections of a patch or the text prefix
+  st->gemm_ws_bytes = 0;
+  if (cfg->dtype == PF_BF16) {
+    const int64_t shapes[4][2] = {{3 * h, h}, {h, h}, {rh, h}, {h, rh}};
+    for (const int64_t rows : {(int64_t)st->patch_rows, (int64_t)cfg->seq_txt}) {
+      if (rows <= 0) continue;
+      for (const auto& nk : shapes)
+        if (nk[0] > 0 && nk[1] > 0) st->gemm_ws_bytes = std::max(st->gemm_ws_bytes, gemm_workspace_bytes(rows, nk[0], nk[1]));
+    }
+  }
 
   hipError_t e;
   if ((e = hipMalloc(&st->wmem, per_layer * L)) != hipSuccess ||
       (st->attn_ws_bytes && (e = hipMalloc(&st->attn_ws, st->attn_ws_bytes)) != hipSuccess) ||
+      (st->gemm_ws_bytes && (e = hipMalloc(&st->gemm_ws, st->gemm_ws_bytes)) != hipSuccess) ||
       (e = hipMalloc(&st->kvmem, 2 * kv_mat * L)) != hipSuccess ||
       (e = hipMalloc(&st->scratch, 2 * scr_h + scr_qkv + scr_u)) != hipSuccess ||
       (e = hipMalloc((void**)&st->modmem, sizeof(float) * 6 * h * L)) != hipSuccess) {
@@ -495,7 +520,8 @@ static pf_status run_rows(pf_stage* st, int64_t off, int64_t n, float* x, hipStr
     hipError_t e;
     if ((e = launch_ln_modulate(x, n, (int)h, mod, mod + h, eps, st->h1, dt, s)) != hipSuccess)
       return stage_hip_fail(st, e, "ln_modulate");
-    if ((e = launch_gemm(st->h1, h, lm.w_qkv, lm.b_qkv, n, 3 * h, h, kEpiStore, qkv, 3 * h, nullptr, dt, s)) !=
+    if ((e = launch_gemm(st->h1, h, lm.w_qkv, lm.b_qkv, n, 3 * h, h, kEpiStore, qkv, 3 * h, nullptr, dt, st->gemm_ws,
+                           st->gemm_ws_bytes, s)) !=
         hipSuccess)
       return stage_hip_fail(st, e, "qkv gemm");
     KVDesc dst[2] = {{lm.k, h, kLayoutRows}, {lm.v, h, dt == PF_BF16 ? kLayoutK8 : kLayoutRows}};
@@ -504,15 +530,18 @@ static pf_status run_rows(pf_stage* st, int64_t off, int64_t n, float* x, hipStr
     if ((e = launch_attention(qkv, 3 * h, lm.k, h, lm.v, h, dst[1].layout, h, st->s_kv, n, st->cfg.heads,
                               st->cfg.head_dim, st->o, h, dt, st->attn_ws, st->attn_ws_bytes, s)) != hipSuccess)
       return stage_hip_fail(st, e, "attention");
-    if ((e = launch_gemm(st->o, h, lm.w_o, lm.b_o, n, h, h, kEpiGatedResidual, x, h, mod + 2 * h, dt, s)) !=
+    if ((e = launch_gemm(st->o, h, lm.w_o, lm.b_o, n, h, h, kEpiGatedResidual, x, h, mod + 2 * h, dt,
+                           st->gemm_ws, st->gemm_ws_bytes, s)) !=
         hipSuccess)
       return stage_hip_fail(st, e, "out-proj gemm");
     if (rh > 0) {
       if ((e = launch_ln_modulate(x, n, (int)h, mod + 3 * h, mod + 4 * h, eps, st->h1, dt, s)) != hipSuccess)
         return stage_hip_fail(st, e, "ln_modulate (mlp)");
-      if ((e = launch_gemm(st->h1, h, lm.w1, lm.b1, n, rh, h, gelu_epi, st->u, rh, nullptr, dt, s)) != hipSuccess)
+      if ((e = launch_gemm(st->h1, h, lm.w1, lm.b1, n, rh, h, gelu_epi, st->u, rh, nullptr, dt, st->gemm_ws,
+                             st->gemm_ws_bytes, s)) != hipSuccess)
         return stage_hip_fail(st, e, "mlp up gemm");
-      if ((e = launch_gemm(st->u, rh, lm.w2, lm.b2, n, h, rh, kEpiGatedResidual, x, h, mod + 5 * h, dt, s)) !=
+      if ((e = launch_gemm(st->u, rh, lm.w2, lm.b2, n, h, rh, kEpiGatedResidual, x, h, mod + 5 * h, dt,
+                             st->gemm_ws, st->gemm_ws_bytes, s)) !=
           hipSuccess)
         return stage_hip_fail(st, e, "mlp down gemm");
     }

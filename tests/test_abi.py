@@ -101,10 +101,10 @@ def test_kvbuf_splice_zero_length_is_noop_without_device(lib):
 def test_component_validation(lib):
     base = 1 << 40
     # gemm: bf16 n must be a multiple of 64
-    assert lib.pf_gemm(base, 128, base, base, 10, 100, 128, 0, base, 100, None, B.PF_BF16, None) == B.PF_ERR_UNSUPPORTED
-    assert lib.pf_gemm(base, 128, base, base, 10, 128, 128, 9, base, 128, None, B.PF_BF16, None) == B.PF_ERR_INVALID_ARG
+    assert lib.pf_gemm(base, 128, base, base, 10, 100, 128, 0, base, 100, None, B.PF_BF16, None, 0, None) == B.PF_ERR_UNSUPPORTED
+    assert lib.pf_gemm(base, 128, base, base, 10, 128, 128, 9, base, 128, None, B.PF_BF16, None, 0, None) == B.PF_ERR_INVALID_ARG
     # gated residual needs a gate
-    assert lib.pf_gemm(base, 128, base, base, 10, 128, 128, 3, base, 128, None, B.PF_BF16, None) == B.PF_ERR_INVALID_ARG
+    assert lib.pf_gemm(base, 128, base, base, 10, 128, 128, 3, base, 128, None, B.PF_BF16, None, 0, None) == B.PF_ERR_INVALID_ARG
     # attention: head_dim 80 unsupported, bf16 needs K8 V
     kv = _view(base, base + (1 << 30), 1000, elems=160, layout=B.PF_LAYOUT_K8)
     assert lib.pf_attention(base, 480, ctypes.byref(kv), 1000, 10, 2, 80, base, 160, None, 0, None) == B.PF_ERR_UNSUPPORTED

@@ -39,13 +39,16 @@ def test_ln_modulate(rows, hidden, dtype):
 # ------------------------------------------------------------------ GEMM
 
 GEMM_SHAPES = [(1, 64, 64), (77, 192, 128), (128, 128, 1152), (300, 1152, 1152), (1000, 3456, 1152),
-               (130, 576, 4608)]
+               (130, 576, 4608), (1024, 1152, 4608), (4100, 4608, 1152)]
 
 
+@pytest.mark.parametrize("split", [False, True], ids=["whole", "ksplit"])
 @pytest.mark.parametrize("m,n,k", GEMM_SHAPES)
 @pytest.mark.parametrize("epi", [B.PF_EPI_STORE, B.PF_EPI_GELU_TANH, B.PF_EPI_GELU_ERF, B.PF_EPI_GATED_RESIDUAL])
-def test_gemm_bf16(m, n, k, epi):
+def test_gemm_bf16(m, n, k, epi, split):
+    """Small grids split k when given a workspace; (4100, 4608, 1152) takes the 256 x 256 tiles."""
     torch = torch_cuda()
+    ws = B.gemm_workspace(m, n, k) if split else None
     seed = m * 7 + n * 11 + k * 13 + epi
     a = synth.randn((m, k), seed, std=1.0, bf16=True)
     w = synth.randn((n, k), seed + 1, std=1.0 / math.sqrt(k), bf16=True)
@@ -56,11 +59,12 @@ def test_gemm_bf16(m, n, k, epi):
         gate = synth.randn((n,), seed + 4)
         c = dev(torch, x0)
         B.pf_gemm(dev(torch, a, torch.bfloat16), dev(torch, w, torch.bfloat16), dev(torch, bias), epi, c,
-                  gate=dev(torch, gate))
+                  gate=dev(torch, gate), workspace=ws)
         want = x0 + gate * y
     else:
         c = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
-        B.pf_gemm(dev(torch, a, torch.bfloat16), dev(torch, w, torch.bfloat16), dev(torch, bias), epi, c)
+        B.pf_gemm(dev(torch, a, torch.bfloat16), dev(torch, w, torch.bfloat16), dev(torch, bias), epi, c,
+                  workspace=ws)
         act = {B.PF_EPI_STORE: lambda v: v, B.PF_EPI_GELU_TANH: ref.gelu_tanh, B.PF_EPI_GELU_ERF: ref.gelu_erf}[epi]
         want = ref.bf16_round(act(y))
     assert_close(host(c), want, f"gemm bf16 {m}x{n}x{k} epi={epi}")

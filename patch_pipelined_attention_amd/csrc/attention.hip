@@ -3,11 +3,18 @@
 // stale rows).  Flash-style single pass with online softmax; no score matrix is stored.
 //
 // bf16 kernel (head_dim D in {64, 72, 128}), gfx950 MFMA v_mfma_f32_32x32x16_bf16:
-//   * workgroup = 4 wavefronts; each wavefront owns QB blocks of 32 queries of one head,
-//     so every K/V operand read from LDS feeds QB MFMAs.  Key tiles of 32 rows are copied
-//     global -> LDS by the gfx950 direct 16-byte loads (no register staging) into a
-//     5-stage ring; one barrier per tile.  K keeps its rows in a permuted, swizzled unit
-//     order (conflict-free operand reads), V the K8 layout of the buffer (see pf.h).
+//   * workgroup = 8 wavefronts in two groups of four; wavefronts w and w + 4 share a SIMD.
+//     Each wavefront owns QB blocks of 32 queries of one head, so every K/V operand read
+//     from LDS feeds QB MFMAs.  The groups run one phase apart between workgroup barriers
+//     ("ping-pong"): while one wavefront of a SIMD issues its MFMAs (P.V of the previous
+//     key tile and the scores of the current one) the other runs its softmax on the VALU,
+//     so the matrix cores and the vector ALUs of every SIMD work at the same time.
+//   * key tiles of 32 rows are copied global -> LDS by the gfx950 direct 16-byte loads (no
+//     register staging) into a 5-stage ring, three tiles ahead; the loads are counted with
+//     explicit vmcnt waits, so they stay in flight across barriers.  K keeps its rows in a
+//     permuted, swizzled unit order (conflict-free operand reads), V the K8 layout of the
+//     buffer (see pf.h).  The V operands of a tile are read into registers at the end of
+//     its softmax phase, so the next MFMA phase starts without waiting on LDS.
 //   * scores are computed transposed, S^T = K . Q^T, so each lane owns one query and 16
 //     keys per block: the row max is a lane-local max chain plus one exchange with the
 //     lane 32 away, and the row sum stays lane-local until the end.
@@ -17,8 +24,9 @@
 //     cross-lane shuffle, and the matching V^T operand is one 16-byte K8 read per lane.
 //   * softmax in base 2: p = exp2(s * log2(e)/sqrt(D) - m), fp32 statistics, P rounded to
 //     bf16 for the P.V product and the row sum taken over the same rounded values (for
-//     D = 72 by the P.V MFMA itself, through a ones row in the padding of O^T).  The reference max m is raised (and O, l rescaled) only
-//     when a tile's max exceeds it by more than 8, so p <= 2^8 and the rescale is rare.
+//     D = 72 by the P.V MFMA itself, through a ones row in the padding of O^T).  The
+//     reference max m is raised (and O, l rescaled) only when a tile's max exceeds it by
+//     more than 8, so p <= 2^8 and the rescale is rare.
 //   * D = 72 pads the score contraction to 80 and the output rows to 96 with zero
 //     operands; nothing outside the real 72 columns is read or written.
 //   * when there are too few (query tile, head) pairs to fill the GPU, the key range is
@@ -44,60 +52,42 @@ __device__ __forceinline__ int xcd_remap(int bid, int nb) {
   return x * per + (x < rem ? x : rem) + bid / 8;
 }
 
-// Per head_dim tuning: query blocks of 32 per wavefront (QB) and the wavefronts per SIMD the
-// register budget is sized for (MINW; 2 caps a wavefront at 256 registers).
-#ifndef PF_ATTN_QB64
-#define PF_ATTN_QB64 2
-#endif
-#ifndef PF_ATTN_QB72
-#define PF_ATTN_QB72 2
-#endif
-#ifndef PF_ATTN_QB128
-#define PF_ATTN_QB128 1
-#endif
-#ifndef PF_ATTN_MINW64
-#define PF_ATTN_MINW64 2
-#endif
-#ifndef PF_ATTN_MINW72
-#define PF_ATTN_MINW72 2
-#endif
-#ifndef PF_ATTN_MINW128
-#define PF_ATTN_MINW128 2
-#endif
+// Query blocks of 32 per wavefront (QB) per head_dim; two wavefronts per SIMD cap each at
+// 256 registers (head_dim 128 with QB = 2 would spill).
 template <int D> struct AttnCfg;
-template <> struct AttnCfg<64> { static constexpr int QB = PF_ATTN_QB64, MINW = PF_ATTN_MINW64; };
-template <> struct AttnCfg<72> { static constexpr int QB = PF_ATTN_QB72, MINW = PF_ATTN_MINW72; };
-template <> struct AttnCfg<128> { static constexpr int QB = PF_ATTN_QB128, MINW = PF_ATTN_MINW128; };
+template <> struct AttnCfg<64> { static constexpr int QB = 2; };
+template <> struct AttnCfg<72> { static constexpr int QB = 2; };
+template <> struct AttnCfg<128> { static constexpr int QB = 1; };
+constexpr int kAttnWaves = 8;
+constexpr int kAttnStages = 5;
 
 template <int D, int QB>
-__global__ __launch_bounds__(256, AttnCfg<D>::MINW) void attn_bf16_kernel(const bf16* __restrict__ Q, int64_t ldq,
-                                                           const bf16* __restrict__ Kb, int64_t ldk,
-                                                           const bf16* __restrict__ Vb, int64_t hidden,
-                                                           int64_t S, int64_t rows, int n_qtiles, int n_split,
-                                                           int tiles_per_split, bf16* __restrict__ O,
-                                                           int64_t ldo, float* __restrict__ part_o,
-                                                           float* __restrict__ part_ml, float scale_log2) {
-  constexpr int BQ = 4 * 32 * QB;                     // queries per workgroup
-  constexpr int KS = (D + 15) / 16;                   // k-steps of the score MFMA
-  constexpr int DB = (D + 31) / 32;                   // 32-row blocks of O^T
+__global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const bf16* __restrict__ Q, int64_t ldq,
+                                                         const bf16* __restrict__ Kb, int64_t ldk,
+                                                         const bf16* __restrict__ Vb, int64_t hidden,
+                                                         int64_t S, int64_t rows, int n_qtiles, int n_split,
+                                                         int tiles_per_split, bf16* __restrict__ O,
+                                                         int64_t ldo, float* __restrict__ part_o,
+                                                         float* __restrict__ part_ml, float scale_log2) {
+  constexpr int BQ = kAttnWaves * 32 * QB;
+  constexpr int KS = (D + 15) / 16;
+  constexpr int DB = (D + 31) / 32;
   constexpr int TK = kTileKeys;
-  constexpr int W = D / 8;                            // 16-byte units per K row
-  constexpr int KU = TK * W;                          // units of the K part of a tile (= V part)
-  constexpr int KUP = (KU + 63) / 64 * 64;            // ... rounded to whole 64-lane loads
-  constexpr int NI = KUP / 64;                        // 64-lane direct loads per part
-  constexpr int NINST = 2 * NI;                       // per tile (K loads, then V loads)
-  constexpr int NJ = (NINST + 3) / 4;                 // most loads one wavefront issues per tile
-  constexpr int NMIN = NINST / 4;                     // fewest
-  constexpr int NSTAGE = 5;                           // tile t being read, t+1 .. t+3 loading
-
-  // Tile stage in LDS, in 16-byte units.  K part: position p (0..31) holds key row
-  // swap_bits23(p), W units per position, unit order swizzled so the 8 lanes of one LDS
-  // read phase (positions p..p+7, same chunk) hit distinct bank groups.  V part (from unit
-  // KUP): the K8 order of the buffer, [TK/8 groups][D][8 keys].
+  constexpr int W = D / 8;
+  constexpr int KU = TK * W;
+  constexpr int KUP = (KU + 63) / 64 * 64;
+  constexpr int NI = KUP / 64;
+  constexpr int NINST = 2 * NI;
+  constexpr int NJ = (NINST + 3) / 4;
+  constexpr int NMIN = NINST / 4;
+  constexpr int NSTAGE = kAttnStages;
+  static_assert(NSTAGE >= 3 && NSTAGE <= 8, "stage ring");
   __shared__ __attribute__((aligned(16))) uint4 lds[NSTAGE][2 * KUP];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wavefront-uniform (scalar)
+  const int grp = wave >> 2, wl = wave & 3;
   const int l32 = lane & 31, hi = lane >> 5;
 
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
@@ -114,7 +104,6 @@ __global__ __launch_bounds__(256, AttnCfg<D>::MINW) void attn_bf16_kernel(const 
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) q_row[qb] = (int64_t)qt * BQ + (wave * QB + qb) * 32 + l32;
 
-  // Q^T fragments (the "B" operand of the score MFMA): 8 consecutive d of this lane's query.
   bf16x8 qf[QB][KS];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb)
@@ -128,39 +117,40 @@ __global__ __launch_bounds__(256, AttnCfg<D>::MINW) void attn_bf16_kernel(const 
         for (int e = 0; e < 8; ++e) qf[qb][ks][e] = (bf16)0.f;
       }
     }
+  // Q has landed before the first direct load is issued: from here on every outstanding
+  // global load is a tile load, counted by the explicit waits below.
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
 
   f32x16 o[QB][DB];
   float m_ref[QB], l_run[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     l_run[qb] = 0.f;
+    m_ref[qb] = -INFINITY;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int e = 0; e < 16; ++e) o[qb][db][e] = 0.f;
   }
 
-  const int64_t ngroups = (S + 7) >> 3;   // K8 groups present in the V buffer
+  const int64_t ngroups = (S + 7) >> 3;
   auto k_unit = [](int p, int c) -> int {
     if constexpr (W % 2 == 1) return p * W + c;
     else if constexpr (W == 8) return p * 8 + (c ^ (p & 7));
     else return p * 16 + (c ^ (p & 15));
   };
 
-  // Direct global -> LDS loads of key tile t into stage st: wavefront w issues the 64-lane
-  // loads i = w, w+4, ...; lane l of load i fills unit 64i + l of its part.  Each lane's
-  // byte offset from the tile's (uniform) base is fixed, so a full tile costs one address
-  // add per load.  In a tile that runs past the end of the buffer, rows and groups read a
-  // clamped (valid) address; their scores are masked and their V entries zeroed before use.
+  // Lane l of load i (i = wl + 4j, this wavefront's j-th) fills unit 64(i mod NI) + l of the
+  // K part (i < NI) or the V part.  Lanes past the part's KU real units fill padding units
+  // that nothing reads, from the part's unit 0 (a valid address), so no lane is masked off.
   uint32_t ld_off[NJ];
   int ld_row[NJ];
-  bool ld_on[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
-    const int i = wave + 4 * j;
+    const int i = wl + 4 * j;
     const bool kpart = i < NI;
-    const int u = (kpart ? i : i - NI) * 64 + lane;
-    ld_on[j] = i < NINST && u < KU;
+    int u = (kpart ? i : i - NI) * 64 + lane;
+    if (u >= KU) u = 0;
     if (kpart) {
       int p, c;
       if constexpr (W % 2 == 1) {
@@ -182,66 +172,81 @@ __global__ __launch_bounds__(256, AttnCfg<D>::MINW) void attn_bf16_kernel(const 
       ld_off[j] = (uint32_t)((g * hidden + d) * 16);
     }
   }
+  // Tile t into stage st (group 0 only).  Only the buffer's last tile can run past S: its rows
+  // (K8 groups) past the end read the last valid row (group) instead; their scores are masked
+  // and their V entries zeroed before use.
   auto issue_tile = [&](int64_t t, int st) {
     const char* kbase = reinterpret_cast<const char*>(Kb + (t * TK) * ldk + col0);
     const char* vbase = reinterpret_cast<const char*>(Vb + (t * (TK / 8) * hidden + col0) * 8);
-    const bool full = (t + 1) * TK <= S;
+    if ((t + 1) * TK <= S) {
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int i = wave + 4 * j;
-      if (i >= NINST) continue;                   // wavefront-uniform
-      if (!ld_on[j]) continue;                    // tail lanes of a part's last load
-      const bool kpart = i < NI;
-      const char* src = (kpart ? kbase : vbase) + ld_off[j];
-      if (!full) {
+      for (int j = 0; j < NJ; ++j) {
+        const int i = wl + 4 * j;
+        if (i >= NINST) continue;                   // wavefront-uniform
+        const bool kpart = i < NI;
+        dma_load16(kpart ? kbase : vbase, ld_off[j], &lds[st][(kpart ? i : KUP / 64 + i - NI) * 64]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int i = wl + 4 * j;
+        if (i >= NINST) continue;
+        const bool kpart = i < NI;
+        uint32_t off = ld_off[j];
         if (kpart) {
           const int64_t over = t * TK + ld_row[j] - (S - 1);
-          if (over > 0) src -= over * ldk * 2;
+          if (over > 0) off -= (uint32_t)(over * ldk * 2);
         } else {
           const int64_t over = t * (TK / 8) + ld_row[j] - (ngroups - 1);
-          if (over > 0) src -= over * hidden * 16;
+          if (over > 0) off -= (uint32_t)(over * hidden * 16);
         }
+        dma_load16(kpart ? kbase : vbase, off, &lds[st][(kpart ? i : KUP / 64 + i - NI) * 64]);
       }
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                       (__attribute__((address_space(3))) void*)&lds[st][(kpart ? i : KUP / 64 + i - NI) * 64],
-                                       16, 0, 0);
     }
   };
-  // Stage ring: tile t lives in stage (t - t_begin + 1) mod NSTAGE.
-  auto next_stage = [](int st) { return st + 1 == NSTAGE ? 0 : st + 1; };
-  auto wait_loads = [&](int newer_tiles) {   // at most `newer_tiles` tiles of loads still in flight
-    if (newer_tiles >= 2) __builtin_amdgcn_s_waitcnt(((2 * NMIN) & 15) | (((2 * NMIN) >> 4) << 14) | (7 << 4) | (15 << 8));
+  auto wait_loads = [&](int newer_tiles) {
+    if (newer_tiles >= 3) __builtin_amdgcn_s_waitcnt(((3 * NMIN) & 15) | (((3 * NMIN) >> 4) << 14) | (7 << 4) | (15 << 8));
+    else if (newer_tiles == 2) __builtin_amdgcn_s_waitcnt(((2 * NMIN) & 15) | (((2 * NMIN) >> 4) << 14) | (7 << 4) | (15 << 8));
     else if (newer_tiles == 1) __builtin_amdgcn_s_waitcnt((NMIN & 15) | ((NMIN >> 4) << 14) | (7 << 4) | (15 << 8));
     else __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
   };
+  auto barrier = [] {
+    __builtin_amdgcn_sched_barrier(0);
+    lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
 
-  for (int64_t t = t_begin; t < t_end && t < t_begin + 3; ++t) issue_tile(t, (int)(t - t_begin + 1));
-
-  // score tile t: S^T = K_t . Q^T (lane: query l32 of each block, 16 keys)
-  auto scores = [&](int st, f32x16 (&sc)[QB]) {
+  // K_t operands of S^T = K_t . Q^T (lane: key row l32, 8 consecutive d).  Rows of the
+  // padded k-step past D read a valid LDS unit and are zeroed by a select (no branch).
+  auto read_k = [&](int st, bf16x8 (&kf)[KS]) {
     const uint4* base = lds[st];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int d0 = ks * 16 + hi * 8;
+      if constexpr (KS * 16 > D) {
+        if (ks == KS - 1) {
+          const int c = d0 < D ? 2 * ks + hi : 2 * ks;
+          const u32x4 w = *reinterpret_cast<const u32x4*>(&base[k_unit(l32, c)]);
+          const u32x4 z = {0u, 0u, 0u, 0u};
+          kf[ks] = __builtin_bit_cast(bf16x8, d0 < D ? w : z);
+          continue;
+        }
+      }
+      kf[ks] = *reinterpret_cast<const bf16x8*>(&base[k_unit(l32, 2 * ks + hi)]);
+    }
+  };
+  auto scores = [&](const bf16x8 (&kf)[KS], f32x16 (&sc)[QB]) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) sc[qb][e] = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int d0 = ks * 16 + hi * 8;
-      bf16x8 a;
-      if (d0 < D) {
-        a = *reinterpret_cast<const bf16x8*>(&base[k_unit(l32, 2 * ks + hi)]);
-      } else {
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) a[e] = (bf16)0.f;
-      }
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) sc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][ks], sc[qb], 0, 0, 0);
-    }
+      for (int qb = 0; qb < QB; ++qb) sc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[qb][ks], sc[qb], 0, 0, 0);
   };
-  // keys of a lane's acc index 4g+j: t*32 + swap_bits23(8g + 4hi + j) = t*32 + 16(g>>1) + 8hi + 4(g&1) + j;
-  // only the buffer's last tile has keys past S
   auto mask_scores = [&](int64_t t, f32x16 (&sc)[QB]) {
-    const int lim = (int)(S - t * TK);      // valid keys in this tile (< 32 here)
+    const int lim = (int)(S - t * TK);
 #pragma unroll
     for (int g = 0; g < 4; ++g)
 #pragma unroll
@@ -252,57 +257,81 @@ __global__ __launch_bounds__(256, AttnCfg<D>::MINW) void attn_bf16_kernel(const 
         }
       }
   };
-  auto tile_max = [&](const f32x16 (&sc)[QB], float (&mt)[QB]) {
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float m0 = fmaxf(sc[qb][0], fmaxf(sc[qb][1], sc[qb][2]));
-      float m1 = fmaxf(sc[qb][3], fmaxf(sc[qb][4], sc[qb][5]));
-      float m2 = fmaxf(sc[qb][6], fmaxf(sc[qb][7], sc[qb][8]));
-      float m3 = fmaxf(sc[qb][9], fmaxf(sc[qb][10], sc[qb][11]));
-      float m4 = fmaxf(sc[qb][12], fmaxf(sc[qb][13], sc[qb][14]));
-      float mx = fmaxf(fmaxf(m0, fmaxf(m1, m2)), fmaxf(m3, fmaxf(m4, sc[qb][15])));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      mt[qb] = mx * scale_log2;
-    }
-  };
-  // D = 72: the padded O^T row 72 (lane l32 == 8 of the last block) multiplies ones, so the
-  // P.V MFMA itself accumulates the row sum of the same bf16 weights; other head_dims keep
-  // the row sum with v_dot2 in the softmax.
   constexpr bool kSumRow = D % 32 != 0;
-  constexpr int kSumIdx = 4 * ((D % 32) / 8) + 0;          // acc index of row D in the last block (hi = 0)
-  // O^T += V_t^T . P^T for two halves of 16 keys; `zero_tail` zeroes V rows past S
-  auto pv = [&](int64_t t, int st, const bf16x8 (&pb)[QB][2], bool zero_tail) {
+  constexpr int kSumIdx = 4 * ((D % 32) / 8) + 0;
+  // V_t^T operands of O^T += V_t^T . P^T (lane: row d = db*32 + l32, 8 keys of group 2*h2 + hi);
+  // rows past D are zero, or ones in row D for the MFMA row sum; `zero_tail` zeroes keys past S
+  auto read_v = [&](int64_t t, int st, bf16x8 (&vf)[2][DB], bool zero_tail) {
     const uint4* base = lds[st] + KUP;
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
-      const int grp = 2 * h2 + hi;
+      const int grp8 = 2 * h2 + hi;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const int d = db * 32 + l32;
-        bf16x8 a;
-        if (d < D) {
-          a = *reinterpret_cast<const bf16x8*>(&base[grp * D + d]);
-          if (zero_tail) {
-            const int lim = (int)(S - t * TK) - grp * 8;
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-              if (e >= lim) a[e] = (bf16)0.f;
-          }
+        if (db * 32 + 32 <= D) {
+          vf[h2][db] = *reinterpret_cast<const bf16x8*>(&base[grp8 * D + d]);
         } else {
-          const bf16 fill = (kSumRow && d == D) ? (bf16)1.0f : (bf16)0.f;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) a[e] = fill;
+          // rows past D: zero, or ones in row D (MFMA row sum); selected without a branch
+          const u32x4 w = *reinterpret_cast<const u32x4*>(&base[grp8 * D + (d < D ? d : D - 1)]);
+          const uint32_t f = (kSumRow && d == D) ? 0x3f803f80u : 0u;   // bf16 pair (1, 1) or (0, 0)
+          const u32x4 fv = {f, f, f, f};
+          vf[h2][db] = __builtin_bit_cast(bf16x8, d < D ? w : fv);
         }
+        if (zero_tail) {
+          const int lim = (int)(S - t * TK) - grp8 * 8;
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[qb][h2], o[qb][db], 0, 0, 0);
+          for (int e = 0; e < 8; ++e)
+            if (e >= lim && db * 32 + l32 < D) vf[h2][db][e] = (bf16)0.f;
+        }
       }
     }
   };
+  auto pv = [&](const bf16x8 (&vf)[2][DB], const bf16x8 (&pb)[QB][2]) {
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[h2][db], pb[qb][h2], o[qb][db], 0, 0, 0);
+  };
   const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
-  // p = 2^(s*c - m) rounded to bf16 in pairs (the P.V operand); without the MFMA sum row the
-  // row sum accumulates the same rounded values with v_dot2 against (1, 1)
-  auto softmax = [&](const f32x16 (&sc)[QB], bf16x8 (&pc)[QB][2]) {
+  // tile max (3-input maximum tree; the two 32-lane halves hold the same queries' other keys),
+  // lazy rescale, p = 2^(s*c - m) packed to bf16
+  auto softmax = [&](f32x16 (&sc)[QB], bf16x8 (&pc)[QB][2]) {
+    float mt[QB];
+    bool raise = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      auto mx3 = [](float a, float b, float c) {
+        return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+      };
+      const float m0 = mx3(sc[qb][0], sc[qb][1], sc[qb][2]);
+      const float m1 = mx3(sc[qb][3], sc[qb][4], sc[qb][5]);
+      const float m2 = mx3(sc[qb][6], sc[qb][7], sc[qb][8]);
+      const float m3 = mx3(sc[qb][9], sc[qb][10], sc[qb][11]);
+      const float m4 = mx3(sc[qb][12], sc[qb][13], sc[qb][14]);
+      const float m5 = mx3(m0, m1, sc[qb][15]);
+      const float mh = mx3(m2, m3, mx3(m4, m5, m5));
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mh), __float_as_uint(mh), false, false);
+      const float mx = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      mt[qb] = mx * scale_log2;
+      raise |= mt[qb] > m_ref[qb] + 8.0f;
+    }
+    if (__any(raise)) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const float m_new = fmaxf(m_ref[qb], mt[qb]);
+        const float alpha = __builtin_amdgcn_exp2f(m_ref[qb] - m_new);
+        m_ref[qb] = m_new;
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) o[qb][db][e] *= alpha;
+      }
+    }
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       uint32_t pk[8];
@@ -322,59 +351,69 @@ __global__ __launch_bounds__(256, AttnCfg<D>::MINW) void attn_bf16_kernel(const 
     }
   };
 
-  // ---- main loop: tile t is in LDS; tiles up to t+4 are loading ----
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) m_ref[qb] = -INFINITY;
-  int st = 1, st_issue = 4;   // stages of tiles t and t+3
-  // `partial` is a literal at both call sites: only the buffer's last tile can run past S,
-  // so the main loop carries no masking code.
-  auto tile = [&](int64_t t, bool partial) {
-    const int64_t ahead = t_end - 1 - t;              // tiles issued after t (at most 2)
-    wait_loads((int)(ahead < 2 ? ahead : 2));
-    __syncthreads();   // tile t landed for every wavefront; all are done with tile t-1
-    if (t + 3 < t_end) issue_tile(t + 3, st_issue);
+  // Slots between barriers: group 0 runs the MFMA phase of tile t in slot 2(t - t_begin) and
+  // its softmax in the next slot; group 1 runs the same one slot later.  MFMA phase of t:
+  // P.V of tile t-1 (V operands already in registers) and the scores of tile t.  Softmax
+  // phase of t: P_t, then the V_t operands are read for the next MFMA phase.  Tile t sits in
+  // stage (t - t_begin) mod NSTAGE and is last read by group 1 in slot 2(t - t_begin) + 2,
+  // so group 0 issues tile t + NSTAGE - 2 at the start of its slot 2(t - t_begin), into
+  // the stage tile t - 2 used.
+  const int64_t nt = t_end - t_begin;
+  if (grp == 0) {
+    for (int64_t u = 0; u < nt && u < NSTAGE - 2; ++u) issue_tile(t_begin + u, (int)u);
+    const int64_t newer = (nt < NSTAGE - 2 ? nt : NSTAGE - 2) - 1;
+    wait_loads((int)newer);
+  }
+  barrier();
+  if (grp == 1) barrier();
 
+  // P.V of "tile t_begin - 1" multiplies zero weights, so every MFMA phase has the same shape
+  bf16x8 pb[QB][2];
+  bf16x8 vf[2][DB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pb[qb][0][e] = pb[qb][1][e] = (bf16)0.f;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) vf[0][db][e] = vf[1][db][e] = (bf16)0.f;
+  int st = 0;                         // stage of tile t
+  int st_issue = NSTAGE - 2;          // stage of tile t + NSTAGE - 2
+  auto iter = [&](int64_t t, bool partial) {
+    bf16x8 kf[KS];
+    read_k(st, kf);
     f32x16 sc[QB];
-    scores(st, sc);
+    pv(vf, pb);
+    if (grp == 0 && t + NSTAGE - 2 < t_end) issue_tile(t + NSTAGE - 2, st_issue);
+    scores(kf, sc);
+    barrier();
     if (partial) mask_scores(t, sc);
-    float mt[QB];
-    tile_max(sc, mt);
-    bool raise = false;
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) raise |= mt[qb] > m_ref[qb] + 8.0f;
-    if (__any(raise)) {
-      // a tile max exceeds the reference by more than 2^8: move the reference, rescale O, l
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const float m_new = fmaxf(m_ref[qb], mt[qb]);
-        const float alpha = __builtin_amdgcn_exp2f(m_ref[qb] - m_new);
-        m_ref[qb] = m_new;
-        l_run[qb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) o[qb][db][e] *= alpha;
-      }
-    }
-    bf16x8 pb[QB][2];
     softmax(sc, pb);
-    pv(t, st, pb, partial);
-    st = next_stage(st);
-    st_issue = next_stage(st_issue);
+    read_v(t, st, vf, partial);
+    if (grp == 0) {
+      const int64_t last_issued = t + NSTAGE - 2 < t_end - 1 ? t + NSTAGE - 2 : t_end - 1;
+      const int64_t newer = last_issued - (t + 1);
+      wait_loads((int)(newer < 0 ? 0 : newer));
+    }
+    barrier();
+    st = st + 1 == NSTAGE ? 0 : st + 1;
+    st_issue = st_issue + 1 == NSTAGE ? 0 : st_issue + 1;
   };
-  const int64_t t_full = t_end * TK > S ? t_end - 1 : t_end;   // tiles before t_full are full
-  for (int64_t t = t_begin; t < t_full; ++t) tile(t, false);
-  if (t_full < t_end) tile(t_full, true);
+  const int64_t t_full = t_end * TK > S ? t_end - 1 : t_end;
+  for (int64_t t = t_begin; t < t_full; ++t) iter(t, false);
+  if (t_full < t_end) iter(t_full, true);
+  if (nt > 0) pv(vf, pb);
+  if (grp == 0) barrier();
 
   if constexpr (kSumRow) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      const float sum_row = o[qb][DB - 1][kSumIdx];   // valid in lanes hi == 0
+      const float sum_row = o[qb][DB - 1][kSumIdx];
       l_run[qb] = hi == 0 ? sum_row : 0.f;
     }
   }
 
-  // ---- finish: lane holds O[query][d = db*32 + 8g + 4hi + j] ----
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float l_tot = l_run[qb] + __shfl_xor(l_run[qb], 32, 64);
@@ -523,8 +562,8 @@ static int attn_slots() {
   if (cached[dev] == 0) {
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_bf16_kernel<D, AttnCfg<D>::QB>, 256, 0) !=
-            hipSuccess || per_cu <= 0)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_bf16_kernel<D, AttnCfg<D>::QB>, 64 * kAttnWaves,
+                                                     0) != hipSuccess || per_cu <= 0)
       per_cu = 1;
     (void)hipGetLastError();
     cached[dev] = cus * per_cu;
@@ -557,7 +596,7 @@ static hipError_t launch_attn_d(const void* q, int64_t ldq, const void* k, int64
                                 int dtype, void* ws, size_t ws_bytes, hipStream_t s) {
   if (dtype == kDtypeBF16) {
     constexpr int QB = AttnCfg<D>::QB;
-    constexpr int BQ = 4 * 32 * QB;
+    constexpr int BQ = kAttnWaves * 32 * QB;
     const int n_qtiles = (int)((rows + BQ - 1) / BQ);
     const int64_t ntiles = (seq_kv + kTileKeys - 1) / kTileKeys;
     const int64_t wg = (int64_t)n_qtiles * heads;
@@ -567,7 +606,7 @@ static hipError_t launch_attn_d(const void* q, int64_t ldq, const void* k, int64
     const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
     float* part_o = static_cast<float*>(ws);
     float* part_ml = part_o ? part_o + (size_t)n_used * rows * hidden : nullptr;
-    hipLaunchKernelGGL((attn_bf16_kernel<D, QB>), dim3((unsigned)(wg * n_used)), dim3(256), 0, s,
+    hipLaunchKernelGGL((attn_bf16_kernel<D, QB>), dim3((unsigned)(wg * n_used)), dim3(64 * kAttnWaves), 0, s,
                        static_cast<const bf16*>(q), ldq, static_cast<const bf16*>(k), ldk,
                        static_cast<const bf16*>(v), hidden, seq_kv, rows, n_qtiles, n_used, tps,
                        static_cast<bf16*>(o), ldo, part_o, part_ml, scale_log2);

@@ -28,6 +28,46 @@ constexpr int kEpiGeluTanh = 1;
 constexpr int kEpiGeluErf = 2;
 constexpr int kEpiGatedResidual = 3;
 
+// Workgroup barrier for kernels that keep direct global -> LDS loads in flight across
+// barriers.  __syncthreads() (and any release fence covering LDS) makes each wavefront
+// drain every outstanding global load, those LDS-bound ones included, before the
+// barrier.  Here the caller waits for exactly the loads that must have landed with an
+// explicit vmcnt count, and every LDS read issued before the barrier has been consumed
+// (and so completed) by then; the empty asm statements keep the compiler from moving
+// memory accesses across the barrier, the scheduling barriers keep any instruction from
+// crossing it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// 16-byte direct global -> LDS load (gfx950 global_load_lds_dwordx4, scalar-base form):
+// lane l reads sbase + voff[l] and writes lds_base + 16 l.  sbase and lds_base must be
+// wavefront-uniform (the first lane's values are used).  Written as asm so that the compiler does not see an LDS store it
+// cannot tell apart from every LDS read: it would otherwise make each later LDS read
+// wait for all loads in flight (vmcnt 0), which serialises a prefetch ring.  The caller
+// owns the wait: s_waitcnt vmcnt for this wavefront's loads, then a workgroup barrier,
+// before any wavefront reads the stage.  The instruction has no destination register.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma_load16(const void* sbase, uint32_t voff, const void* lds_base) {
+  // readfirstlane returns int: both halves go through uint32_t so the low word is
+  // zero-extended when the pointer is put back together
+  const uint32_t m0 = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
+  const uint64_t b = (uint64_t)(uintptr_t)sbase;
+  const uint32_t b_hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  const uint32_t b_lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint64_t bs = ((uint64_t)b_hi << 32) | (uint64_t)b_lo;
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(bs), "s"(m0)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 // Largest hidden size the row kernels (LayerNorm) keep in registers.
 constexpr int kMaxHidden = 6144;
 

@@ -37,7 +37,61 @@ def parse():
     ap.add_argument("--breakdown", action="store_true", help="also time every kernel of a patch-layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--probe", choices=["attention", "copy"],
+                    help="only launch the dominant kernel at the bench launch shape (or a plain 1 GiB copy) "
+                         "--probe-iters times; a target for rocprofv3 counter runs")
+    ap.add_argument("--probe-iters", type=int, default=3)
+    ap.add_argument("--pmc-summary", metavar="DIR",
+                    help="print per-kernel average counters of the rocprofv3 counter CSVs under DIR, then exit")
     return ap.parse_args()
+
+
+# Calibrated HBM traffic of the dominant kernel, recorded by a counter run (see the file for
+# its commands).  It describes the kernel sources whose hash it names; once they change, the
+# recorded traffic no longer applies and bench.py reports null.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_c2_traffic.md")
+ATTENTION_SOURCES = ("patch_pipelined_attention_amd/csrc/attention.hip", "patch_pipelined_attention_amd/csrc/pf_internal.h")
+
+
+def attention_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in ATTENTION_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(config: str):
+    """Bytes per attention call from TRAFFIC_FILE if it matches this config and the current
+    kernel sources, else None."""
+    try:
+        fields = {}
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                if line.startswith("- ") and ": " in line:
+                    k, v = line[2:].split(": ", 1)
+                    fields[k.strip()] = v.strip().strip("`")
+        if fields.get("config") != config or fields.get("source_sha256") != attention_source_hash():
+            return None
+        return float(fields["traffic_bytes_per_call"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def pmc_summary(d: str) -> None:
+    """Average of every counter per kernel over the dispatches in rocprofv3 CSVs under d."""
+    import csv
+    import glob
+    import collections
+    per = collections.defaultdict(lambda: collections.defaultdict(float))
+    for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                per[(r["Kernel_Name"], r["Counter_Name"])][r["Dispatch_Id"]] += float(r["Counter_Value"])
+    for (kern, ctr), disp in sorted(per.items()):
+        vals = list(disp.values())
+        print(f"{ctr:16s} {sum(vals) / len(vals):14.1f} avg over {len(vals)} dispatches  {kern[:90]}")
 
 
 def time_kernel(torch, fn, iters=20, warm=3):
@@ -130,12 +184,49 @@ def cpu_baseline(shape, inputs, budget_s):
             "host_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0))}
 
 
+def probe(args):
+    """Launch only the dominant kernel at the bench's launch shape (or a 1 GiB device copy)
+    args.probe_iters times, then exit: the program rocprofv3 counter runs profile."""
+    import torch
+    from patch_pipelined_attention_amd import binding as B
+    from patch_pipelined_attention_amd.configs import CONFIGS
+    torch.cuda.set_device(0)
+    if args.probe == "copy":
+        n = 1 << 30
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(args.probe_iters):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[probe] copied {n} bytes x {args.probe_iters}", file=sys.stderr, flush=True)
+        return
+    B.lib()
+    shape = CONFIGS[args.config]
+    h, P, S = shape.hidden, shape.patch_rows, shape.seq_kv
+    qkv = torch.randn((P, 3 * h), device="cuda").to(torch.bfloat16)
+    k = torch.randn((S, h), device="cuda").to(torch.bfloat16)
+    v = torch.randn(((S + 7) // 8 * 8 * h,), device="cuda").to(torch.bfloat16)
+    kv = B.kv_view(k, v, S, h, B.PF_LAYOUT_K8)
+    o = torch.empty((P, h), dtype=torch.bfloat16, device="cuda")
+    ws = B.attention_workspace(P, shape.heads, shape.head_dim)   # same split choice as the stage
+    for _ in range(args.probe_iters):
+        B.pf_attention(qkv, kv, S, P, shape.heads, shape.head_dim, o, workspace=ws)
+    torch.cuda.synchronize()
+    print(f"[probe] attention {shape.name} P={P} S_kv={S} x {args.probe_iters}", file=sys.stderr, flush=True)
+
+
 def main():
     args = parse()
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU's pipeline stage; --gpus {args.gpus} is not supported "
               "(this build runs on one GPU only).", file=sys.stderr)
         sys.exit(2)
+    if args.probe:
+        probe(args)
+        return
     import numpy as np
     import torch
 
@@ -230,7 +321,9 @@ def main():
         "wall_s_timed": wall,
         "roofline": {"kernel": "attn_bf16_kernel", "bound": "mfma", "achieved": attn_tflops,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": attn_tflops / PEAK_BF16_TFLOPS,
-                     "traffic": None, "avg_launch_us": attn_s * 1e6,
+                     "traffic": recorded_traffic(args.config), "avg_launch_us": attn_s * 1e6,
+                     "launch": "one pf_attention call: attn_bf16_kernel plus, when the key range is split, "
+                               "attn_combine_kernel; the duration covers both",
                      "work": f"4*P*S_kv*h = {attn_flop:.4g} FLOP per launch (P={shape.patch_rows}, "
                              f"S_kv={shape.seq_kv}, h={shape.hidden})"},
     }

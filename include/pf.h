@@ -191,7 +191,10 @@ pf_status pf_ln_modulate(const float* x, int64_t rows, int32_t hidden, const flo
  * c is fp32 for PF_EPI_GATED_RESIDUAL (gate fp32 [n]).  fp32 accumulation.  For bf16:
  * n % 64 == 0 and k % 64 == 0.  `workspace` (device, may be NULL) lets a grid too small to
  * fill the GPU split k into slices summed by a second pass (in a fixed order: deterministic);
- * pf_gemm_workspace_size gives the bytes that allow the split the library would choose. */
+ * pf_gemm_workspace_size gives the bytes that allow the split the library would choose.
+ * The tile size (128 x 128, or 256 x 256 for long reductions) is chosen per shape; the
+ * environment variable PF_GEMM_TILE=128 or 256 forces it (read on every call, so set it
+ * before pf_gemm_workspace_size as well). */
 pf_status pf_gemm(const void* a, int64_t lda, const void* w, const float* bias, int64_t m,
                   int64_t n, int64_t k, int32_t epi, void* c, int64_t ldc, const float* gate,
                   int32_t dtype, void* workspace, uint64_t workspace_bytes, void* stream);

@@ -7,19 +7,27 @@
 // per lane, one token and 4 consecutive output features per 8-row group, so every
 // epilogue stores 4 contiguous values per access (8 B bf16 / 16 B fp32).
 //
-// Tiles: 256 x 256 (each wavefront 128 x 128 = 4 x 4 MFMA blocks, 0.5 KB of LDS operand
-// reads per MFMA) when the grid of big tiles fills the GPU, else 128 x 128, split along k
-// with a reduce pass when even those are too few.
+// Tiles: 128 x 128 (two workgroups per CU) by default; 256 x 256 (one per CU, each wavefront
+// 128 x 128 = 4 x 4 MFMA blocks, 0.5 KB of LDS operand reads per MFMA) for long reductions
+// (k >= 8192), where its higher per-k rate outweighs its fixed cost per tile.  Grids too
+// small to fill the GPU split k and sum the slices in a reduce pass.
 //
 // fp32 path (tiny fp32 stages only): a plain 64x64 LDS-tiled FMA kernel.
 #include "pf_internal.h"
 
+#include <cstdlib>
+#include <cstring>
+
 namespace pf {
 
 __device__ __forceinline__ float gelu_tanh_f(float x) {
-  // 0.5 x (1 + tanh(u)) = x * sigmoid(2u), u = sqrt(2/pi) (x + 0.044715 x^3)
-  const float u = 0.7978845608028654f * (x + 0.044715f * x * x * x);
-  return x / (1.0f + expf(-2.0f * u));
+  // 0.5 x (1 + tanh(u)) = x * sigmoid(2u) = x / (1 + 2^(-2u log2 e)), u = sqrt(2/pi) (x + 0.044715 x^3).
+  // Hardware exp2 and reciprocal (about 1 ulp each); for large |x| the power saturates to
+  // 0 or inf and the result to x or 0.
+  const float x2 = x * x;
+  const float t = x * fmaf(x2, -2.0f * 1.4426950408889634f * 0.7978845608028654f * 0.044715f,
+                           -2.0f * 1.4426950408889634f * 0.7978845608028654f);   // -2u log2 e
+  return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(t));
 }
 
 __device__ __forceinline__ float gelu_erf_f(float x) { return 0.5f * x * (1.0f + erff(x * 0.7071067811865476f)); }
@@ -39,14 +47,14 @@ __device__ __forceinline__ int gemm_xcd_remap(int bid, int nb) {
 
 // bf16 tile kernel: BF features x BT tokens per workgroup (4 wavefronts in a 2 x 2 grid, each
 // (BF/2) x (BT/2) = FB x TB blocks of 32 x 32), k staged 64 at a time (4 MFMA k-steps per
-// barrier).  The W rows and X rows of a k tile are copied global -> LDS with direct 16-byte
-// loads into a 2-stage ring (one tile ahead; the other resident workgroup covers the rest of
-// the latency); LDS units are swizzled so every 8-lane operand read phase hits distinct bank
-// groups, and the operands of k-step s+1 are read while the MFMAs of step s run.  With
-// SPLIT, the workgroup covers one slice of the k range and writes an fp32 partial tile;
-// gemm_reduce_kernel then sums the slices and applies the epilogue.
+// barrier), two workgroups per CU.  The W rows and X rows of a k tile are copied global ->
+// LDS with direct 16-byte loads into a 2-stage ring (one tile ahead; the other resident
+// workgroup covers the rest of the latency); LDS units are swizzled so every 8-lane operand
+// read phase hits distinct bank groups, and the operands of k-step s+1 are read while the
+// MFMAs of step s run.  With SPLIT, the workgroup covers one slice of the k range and writes
+// an fp32 partial tile; gemm_reduce_kernel then sums the slices and applies the epilogue.
 template <int BF, int BT, int EPI, bool SPLIT>
-__global__ __launch_bounds__(256, (BF * BT >= 256 * 256) ? 1 : 2) void gemm_bf16_kernel(
+__global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
     const bf16* __restrict__ A, int64_t lda, const bf16* __restrict__ W, const float* __restrict__ bias, int64_t M,
     int64_t N, int64_t K, void* __restrict__ C, int64_t ldc, const float* __restrict__ gate, int tiles_n,
     int n_split, int ktiles_per_split, float* __restrict__ part) {
@@ -59,10 +67,12 @@ __global__ __launch_bounds__(256, (BF * BT >= 256 * 256) ? 1 : 2) void gemm_bf16
   constexpr int NSTAGE = 2;
   constexpr int FB = BF / 64, TB = BT / 64;
   static_assert(NINST % 4 == 0, "stage must split evenly over 4 wavefronts");
+  static_assert(BF * 8 % 256 == 0, "each load fills only W rows or only X rows");
   __shared__ __attribute__((aligned(16))) uint4 lds[NSTAGE][UNITS];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
   const int wf = wave & 1, wt = wave >> 1;
 
@@ -80,30 +90,31 @@ __global__ __launch_bounds__(256, (BF * BT >= 256 * 256) ? 1 : 2) void gemm_bf16
   // unit of (row, chunk c in 0..7): rows r..r+7 at one chunk land in 8 distinct bank groups
   auto unit = [](int r, int c) { return r * 8 + (c ^ (r & 7)); };
 
-  // per-lane source of each of this wavefront's loads (rows past M or N read a clamped row;
-  // their results are never stored)
-  const char* src[NPW];
+  // per-lane byte offset of each of this wavefront's loads from the tile's row-0 base (rows
+  // past M or N read the last valid row; their results are never stored)
+  const bf16* Wt = W + n0 * K;
+  const bf16* Xt = A + m0 * lda;
+  uint32_t off[NPW];
+  bool wrow[NPW];
 #pragma unroll
   for (int j = 0; j < NPW; ++j) {
     const int u = (wave + 4 * j) * 64 + lane;
     const int r = u >> 3;
     const int c = (u & 7) ^ (r & 7);
+    wrow[j] = (wave + 4 * j) * 64 < BF * 8;     // wavefront-uniform
     if (r < BF) {
-      int64_t n = n0 + r;
-      n = n < N ? n : N - 1;
-      src[j] = reinterpret_cast<const char*>(W + n * K + c * 8);
+      const int64_t rr = n0 + r < N ? r : N - 1 - n0;
+      off[j] = (uint32_t)((rr * K + c * 8) * 2);
     } else {
-      int64_t m = m0 + (r - BF);
-      m = m < M ? m : M - 1;
-      src[j] = reinterpret_cast<const char*>(A + m * lda + c * 8);
+      const int64_t rr = m0 + (r - BF) < M ? r - BF : M - 1 - m0;
+      off[j] = (uint32_t)((rr * lda + c * 8) * 2);
     }
   }
   auto issue = [&](int64_t kt, int st) {
+    const char* wb = reinterpret_cast<const char*>(Wt + kt * BK);
+    const char* xb = reinterpret_cast<const char*>(Xt + kt * BK);
 #pragma unroll
-    for (int j = 0; j < NPW; ++j)
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src[j] + kt * BK * 2),
-                                       (__attribute__((address_space(3))) void*)&lds[st][(wave + 4 * j) * 64], 16, 0,
-                                       0);
+    for (int j = 0; j < NPW; ++j) dma_load16(wrow[j] ? wb : xb, off[j], &lds[st][(wave + 4 * j) * 64]);
   };
 
   f32x16 acc[FB][TB];
@@ -125,13 +136,15 @@ __global__ __launch_bounds__(256, (BF * BT >= 256 * 256) ? 1 : 2) void gemm_bf16
 
   issue(kt0, 0);
   int st = 0;
-  for (int64_t kt = kt0; kt < kt1; ++kt) {
+  // One k tile; `more`: tile kt+1 exists (the steady-state body then has no branch, so the
+  // compiler waits for exactly the operand reads each MFMA needs).
+  auto ktile = [&](int64_t kt, bool more) {
     __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));   // this wavefront's loads of tile kt are done
-    __syncthreads();   // ... for every wavefront; all are done reading the other stage
-    if (kt + 1 < kt1) issue(kt + 1, st ^ 1);
+    lds_barrier();   // ... for every wavefront; all are done reading the other stage
     const uint4* L = lds[st];
     bf16x8 a[2][FB], b[2][TB];
-    read_frags(L, 0, a[0], b[0]);
+    read_frags(L, 0, a[0], b[0]);                      // before the loads: nothing crosses their asm
+    if (more) issue(kt + 1, st ^ 1);
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
       if (ks + 1 < KSTEPS) read_frags(L, ks + 1, a[(ks + 1) & 1], b[(ks + 1) & 1]);
@@ -141,8 +154,211 @@ __global__ __launch_bounds__(256, (BF * BT >= 256 * 256) ? 1 : 2) void gemm_bf16
         for (int t = 0; t < TB; ++t)
           acc[i][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks & 1][i], b[ks & 1][t], acc[i][t], 0, 0, 0);
     }
+    // schedule: operand reads of k-steps 0 and 1, then each k-step's MFMAs followed by the
+    // reads of the k-step after the next, so every read has one k-step of MFMAs to land
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * (FB + TB), 0);
+#pragma unroll
+    for (int ks = 0; ks + 2 < KSTEPS; ++ks) {
+      __builtin_amdgcn_sched_group_barrier(0x008, FB * TB, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, FB + TB, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * FB * TB, 0);
     st ^= 1;
+  };
+  int64_t kt = kt0;
+  for (; kt + 1 < kt1; ++kt) ktile(kt, true);
+  if (kt < kt1) ktile(kt, false);
+
+  // acc[i][t][4g+j] = y[token = m0 + wt*BT/2 + t*32 + l32][feature = n0 + wf*BF/2 + i*32 + 8g + 4hi + j]
+#pragma unroll
+  for (int t = 0; t < TB; ++t) {
+    const int64_t m = m0 + wt * (BT / 2) + t * 32 + l32;
+    if (m >= M) continue;
+#pragma unroll
+    for (int i = 0; i < FB; ++i) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int64_t f = n0 + wf * (BF / 2) + i * 32 + 8 * g + 4 * hi;
+        if (f >= N) continue;
+        if constexpr (SPLIT) {
+          *reinterpret_cast<float4*>(part + ((int64_t)split * M + m) * N + f) =
+              make_float4(acc[i][t][4 * g + 0], acc[i][t][4 * g + 1], acc[i][t][4 * g + 2], acc[i][t][4 * g + 3]);
+        } else {
+          const float4 bv = *reinterpret_cast<const float4*>(bias + f);
+          const float v0 = acc[i][t][4 * g + 0] + bv.x;
+          const float v1 = acc[i][t][4 * g + 1] + bv.y;
+          const float v2 = acc[i][t][4 * g + 2] + bv.z;
+          const float v3 = acc[i][t][4 * g + 3] + bv.w;
+          if constexpr (EPI == kEpiGatedResidual) {
+            float* cp = static_cast<float*>(C) + m * ldc + f;
+            const float4 gv = *reinterpret_cast<const float4*>(gate + f);
+            float4 cv = *reinterpret_cast<float4*>(cp);
+            cv.x += gv.x * v0;
+            cv.y += gv.y * v1;
+            cv.z += gv.z * v2;
+            cv.w += gv.w * v3;
+            *reinterpret_cast<float4*>(cp) = cv;
+          } else {
+            bf16x4 o = {(bf16)epi_act<EPI>(v0), (bf16)epi_act<EPI>(v1), (bf16)epi_act<EPI>(v2),
+                        (bf16)epi_act<EPI>(v3)};
+            *reinterpret_cast<bf16x4*>(static_cast<bf16*>(C) + m * ldc + f) = o;
+          }
+        }
+      }
+    }
   }
+}
+
+// bf16 big-tile kernel: 256 features x 256 tokens per workgroup, 4 wavefronts in a 2 x 2
+// grid, each 128 x 128 = 4 x 4 blocks of 32 x 32 (256 fp32 accumulators per lane, which
+// the compiler keeps in the accumulation registers).  Per MFMA a wavefront reads 0.5 KB of
+// operands from LDS, half the 128 x 128 tile's share.  k is staged 32 at a time (two MFMA
+// k-steps) in a 4-stage ring filled three tiles ahead by direct global -> LDS loads; the
+// loads are counted with explicit vmcnt waits so they stay in flight across barriers.  The
+// first operands of tile kt+1 are read right after the barrier that publishes it, while the
+// MFMAs of tile kt's last k-step are still running.  One workgroup per CU.
+template <int EPI, bool SPLIT>
+__global__ __launch_bounds__(256, 1) void gemm_big_kernel(const bf16* __restrict__ A, int64_t lda,
+                                                          const bf16* __restrict__ W, const float* __restrict__ bias,
+                                                          int64_t M, int64_t N, int64_t K, void* __restrict__ C,
+                                                          int64_t ldc, const float* __restrict__ gate, int tiles_n,
+                                                          int n_split, int ktiles_per_split,
+                                                          float* __restrict__ part) {
+  constexpr int BF = 256, BT = 256;
+  constexpr int BK = 32;                 // k per stage: two MFMA k-steps
+  constexpr int KSTEPS = BK / 16;
+  constexpr int ROWS = BF + BT;          // stage rows: W rows, then X rows
+  constexpr int UPR = BK / 8;            // 16-byte units per row (4)
+  constexpr int UNITS = ROWS * UPR;      // 2048 units = 32 KB per stage
+  constexpr int NINST = UNITS / 64;      // 64-lane direct loads per stage (32)
+  constexpr int NPW = NINST / 4;         // per wavefront (8)
+  constexpr int NSTAGE = 4;
+  constexpr int FB = 4, TB = 4;
+  static_assert(NPW % 2 == 0, "W and X loads split evenly");
+  __shared__ __attribute__((aligned(16))) uint4 lds[NSTAGE][UNITS];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int wf = wave & 1, wt = wave >> 1;
+
+  const int lid = gemm_xcd_remap(blockIdx.x, gridDim.x);
+  const int split = lid % n_split;
+  const int rest = lid / n_split;
+  const int tile_n = rest % tiles_n;
+  const int64_t tile_m = rest / tiles_n;
+  const int64_t n0 = (int64_t)tile_n * BF;
+  const int64_t m0 = tile_m * BT;
+  const int64_t nkt = K / BK;
+  const int64_t kt0 = (int64_t)split * ktiles_per_split;
+  const int64_t kt1 = kt0 + ktiles_per_split < nkt ? kt0 + ktiles_per_split : nkt;
+
+  // unit of (row r, chunk c in 0..3): the 8 rows of one 8-lane read phase land on distinct
+  // 16-byte bank groups (rows r, r+1 differ by 64 B; pairs of rows take the 4 chunk XORs)
+  auto unit = [](int r, int c) { return r * UPR + (c ^ ((r >> 1) & 3)); };
+
+  // Loads: wavefront w issues loads i = w + 4j; loads 0..15 fill the W rows, 16..31 the X
+  // rows (j < NPW/2: W, else X, for every wavefront).  Per-lane byte offsets from the tile's
+  // row-0 base; rows past N or M read the last valid row (their results are never stored).
+  const bf16* Wt = W + n0 * K;
+  const bf16* Xt = A + m0 * lda;
+  uint32_t off[NPW];
+#pragma unroll
+  for (int j = 0; j < NPW; ++j) {
+    const int u = (wave + 4 * j) * 64 + lane;
+    const int r = u / UPR;
+    const int c = (u % UPR) ^ ((r >> 1) & 3);
+    if (r < BF) {
+      const int64_t rr = n0 + r < N ? r : N - 1 - n0;
+      off[j] = (uint32_t)((rr * K + c * 8) * 2);
+    } else {
+      const int64_t rr = m0 + (r - BF) < M ? r - BF : M - 1 - m0;
+      off[j] = (uint32_t)((rr * lda + c * 8) * 2);
+    }
+  }
+  auto issue = [&](int64_t kt, int st) {
+    const char* wb = reinterpret_cast<const char*>(Wt + kt * BK);
+    const char* xb = reinterpret_cast<const char*>(Xt + kt * BK);
+#pragma unroll
+    for (int j = 0; j < NPW; ++j)
+      dma_load16(j < NPW / 2 ? wb : xb, off[j], &lds[st][(wave + 4 * j) * 64]);
+  };
+  // this wavefront's loads of the tile before the `newer` most recently issued tiles are done
+  auto wait_tiles = [&](int newer) {
+    if (newer >= 3) __builtin_amdgcn_s_waitcnt(((3 * NPW) & 15) | (((3 * NPW) >> 4) << 14) | (7 << 4) | (15 << 8));
+    else if (newer == 2) __builtin_amdgcn_s_waitcnt(((2 * NPW) & 15) | (((2 * NPW) >> 4) << 14) | (7 << 4) | (15 << 8));
+    else if (newer == 1) __builtin_amdgcn_s_waitcnt((NPW & 15) | ((NPW >> 4) << 14) | (7 << 4) | (15 << 8));
+    else __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+  };
+
+  f32x16 acc[FB][TB];
+#pragma unroll
+  for (int i = 0; i < FB; ++i)
+#pragma unroll
+    for (int t = 0; t < TB; ++t)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][t][e] = 0.f;
+
+  auto read_frags = [&](const uint4* L, int ks, bf16x8 (&a)[FB], bf16x8 (&b)[TB]) {
+#pragma unroll
+    for (int i = 0; i < FB; ++i)
+      a[i] = *reinterpret_cast<const bf16x8*>(&L[unit(wf * (BF / 2) + i * 32 + l32, 2 * ks + hi)]);
+#pragma unroll
+    for (int t = 0; t < TB; ++t)
+      b[t] = *reinterpret_cast<const bf16x8*>(&L[unit(BF + wt * (BT / 2) + t * 32 + l32, 2 * ks + hi)]);
+  };
+
+  const int64_t nt = kt1 - kt0;
+  bf16x8 a[2][FB], b[2][TB];
+  // prologue: tiles kt0 .. kt0+NSTAGE-2 in flight, wait for kt0
+  for (int64_t u = 0; u < nt && u < NSTAGE - 1; ++u) issue(kt0 + u, (int)u);
+  {
+    const int64_t newer = (nt < NSTAGE - 1 ? nt : NSTAGE - 1) - 1;
+    wait_tiles((int)(newer < 0 ? 0 : newer));
+  }
+  lds_barrier();
+  if (nt > 0) read_frags(lds[0], 0, a[0], b[0]);
+  int st = 0;
+  // One k tile.  `steady`: tile kt + NSTAGE - 1 exists (so the loop body has no branch and
+  // the compiler can wait for exactly the operand reads each MFMA needs).
+  auto ktile = [&](int64_t kt, bool steady) {
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      const int cur = ks & 1, nxt = cur ^ 1;   // KSTEPS is even: k-step 0 of every tile uses buffer 0
+      if (ks + 1 < KSTEPS) {
+        read_frags(lds[st], ks + 1, a[nxt], b[nxt]);
+      } else if (steady || kt + 1 < kt1) {
+        // tile kt+1 landed for every wavefront; all are done with tile kt-1's stage
+        if (steady) {
+          wait_tiles(NSTAGE - 3);   // issued so far: tiles up to kt + NSTAGE - 2
+        } else {
+          const int64_t issued_after = (kt + NSTAGE - 2 < kt1 - 1 ? kt + NSTAGE - 2 : kt1 - 1) - (kt + 1);
+          wait_tiles((int)issued_after);
+        }
+        lds_barrier();
+        // operand reads first: the loads below are asm with a memory clobber, which nothing
+        // crosses, so reads placed after them could only start once all loads are issued
+        const int st1 = st + 1 == NSTAGE ? 0 : st + 1;
+        read_frags(lds[st1], 0, a[nxt], b[nxt]);
+        if (steady || kt + NSTAGE - 1 < kt1) issue(kt + NSTAGE - 1, st == 0 ? NSTAGE - 1 : st - 1);
+      }
+#pragma unroll
+      for (int i = 0; i < FB; ++i)
+#pragma unroll
+        for (int t = 0; t < TB; ++t)
+          acc[i][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cur][i], b[cur][t], acc[i][t], 0, 0, 0);
+      if (ks + 1 == KSTEPS && steady) {
+        // schedule: the next tile's operand reads, then this k-step's MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, FB + TB, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, FB * TB, 0);
+      }
+    }
+    st = st + 1 == NSTAGE ? 0 : st + 1;
+  };
+  int64_t kt = kt0;
+  for (; kt + NSTAGE - 1 < kt1; ++kt) ktile(kt, true);
+  for (; kt < kt1; ++kt) ktile(kt, false);
 
   // acc[i][t][4g+j] = y[token = m0 + wt*BT/2 + t*32 + l32][feature = n0 + wf*BF/2 + i*32 + 8g + 4hi + j]
 #pragma unroll
@@ -277,11 +493,6 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
   }
 }
 
-#ifndef PF_GEMM_BIG_TILES
-#define PF_GEMM_BIG_TILES 0
-#endif
-constexpr bool kGemmBigTiles = PF_GEMM_BIG_TILES;
-
 // Launch plan of a bf16 GEMM: tile size and k-split count.
 struct GemmPlan {
   int big;      // 1: 256 x 256 tiles (1 workgroup per CU), 0: 128 x 128 tiles (2 per CU)
@@ -302,30 +513,49 @@ static int gemm_cus() {
   return cus;
 }
 
-// Big tiles when they alone give every CU work; otherwise 128 x 128 tiles, split along k
-// (each slice >= 4 k tiles of 64) when that lowers the estimated time: rounds of resident
-// workgroups x the slice's compute, plus writing and re-reading the fp32 partials.
+// Big tiles pay off only for long reductions: their per-k rate is about twice a 128 x 128
+// slot's, but each tile carries a large fixed cost (measured on MI355X at the DiT projection
+// shapes: faster for k = 12288, slower for every k <= 4608).
+constexpr int64_t kBigTileMinK = 8192;
+
+// Smallest estimated time over tile size x k-split: rounds of resident workgroups x one
+// slice's time (a fixed cost plus its FLOPs at the tile's measured rate), plus writing and
+// re-reading the fp32 partials of a split.
+// The environment variable PF_GEMM_TILE=128 or 256 forces the tile size (the k-split is still
+// chosen by the estimate); any other value, or none, leaves both to the estimate.
+static int gemm_tile_override() {
+  const char* v = std::getenv("PF_GEMM_TILE");
+  if (!v) return 0;
+  if (std::strcmp(v, "128") == 0) return 128;
+  if (std::strcmp(v, "256") == 0) return 256;
+  return 0;
+}
+
 static GemmPlan gemm_plan(int64_t m, int64_t n, int64_t k, size_t ws_bytes) {
   const int cus = gemm_cus();
-  const int64_t big_tiles = ((m + 255) / 256) * ((n + 255) / 256);
-  if (kGemmBigTiles && big_tiles >= cus) return {1, 1};
-  const int64_t tiles = ((m + 127) / 128) * ((n + 127) / 128);
-  const int64_t slots = 2 * (int64_t)cus;
-  const double tile_s = 2.0 * 128 * 128 * (double)k / 2.0e12;   // one resident tile at ~2 TFLOP/s
-  const double bytes_s = 1.0 / 5.0e12;                           // partial traffic at ~5 TB/s
-  int split = 1;
-  double best = (double)((tiles + slots - 1) / slots) * tile_s;
-  for (int sp = 2; sp <= kMaxGemmSplit; ++sp) {
-    if (k / 64 < 4LL * sp) break;
-    if ((size_t)sp * m * n * sizeof(float) > ws_bytes) break;
-    const double t = (double)((tiles * sp + slots - 1) / slots) * tile_s / sp +
-                     2.0 * sp * (double)m * (double)n * sizeof(float) * bytes_s;
-    if (t < best) {
-      best = t;
-      split = sp;
+  const int force = gemm_tile_override();
+  GemmPlan best_plan{force == 256 ? 1 : 0, 1};
+  double best = 1e30;
+  for (int big = 0; big <= 1; ++big) {
+    if (force ? (big != (force == 256)) : (big && k < kBigTileMinK)) continue;
+    const int64_t bt = big ? 256 : 128;
+    const int64_t bk = big ? 32 : 64;
+    const int64_t tiles = ((m + bt - 1) / bt) * ((n + bt - 1) / bt);
+    const int64_t slots = big ? (int64_t)cus : 2 * (int64_t)cus;
+    const double fixed_s = big ? 30e-6 : 3e-6;
+    const double rate = big ? 6.7e12 : 1.65e12;      // FLOP/s of one resident workgroup
+    for (int sp = 1; sp <= kMaxGemmSplit; ++sp) {
+      if (sp > 1 && k / bk < 4LL * sp) break;
+      if (sp > 1 && (size_t)sp * m * n * sizeof(float) > ws_bytes) break;
+      const double t = (double)((tiles * sp + slots - 1) / slots) * (fixed_s + 2.0 * bt * bt * (double)k / sp / rate) +
+                       (sp > 1 ? 2.0 * sp * (double)m * (double)n * sizeof(float) / 5.0e12 : 0.0);
+      if (t < best * 0.98) {
+        best = t;
+        best_plan = {big, sp};
+      }
     }
   }
-  return {0, split};
+  return best_plan;
 }
 
 size_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k) {
@@ -341,28 +571,33 @@ static void launch_gemm_epi(const void* a, int64_t lda, const void* w, const flo
     const bf16* A = static_cast<const bf16*>(a);
     const bf16* Wt = static_cast<const bf16*>(w);
     const GemmPlan p = gemm_plan(m, n, k, ws ? ws_bytes : 0);
-    const int nkt = (int)(k / 64);
+    const int bt = p.big ? 256 : 128;
+    const int nkt = (int)(k / (p.big ? 32 : 64));
+    const int tiles_n = (int)((n + bt - 1) / bt);
+    const int64_t tiles = (int64_t)tiles_n * ((m + bt - 1) / bt);
+    const int kps = (nkt + p.split - 1) / p.split;
+    const int used = (nkt + kps - 1) / kps;          // every slice gets at least one k tile
+    float* part = static_cast<float*>(ws);
+    const dim3 grid((unsigned)(tiles * used));
     if (p.big) {
-      const int tiles_n = (int)((n + 255) / 256);
-      const int64_t tiles = (int64_t)tiles_n * ((m + 255) / 256);
-      hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, EPI, false>), dim3((unsigned)tiles), dim3(256), 0, s, A, lda, Wt,
-                         bias, m, n, k, c, ldc, gate, tiles_n, 1, nkt, nullptr);
+      if (used == 1)
+        hipLaunchKernelGGL((gemm_big_kernel<EPI, false>), grid, dim3(256), 0, s, A, lda, Wt, bias, m, n, k, c, ldc,
+                           gate, tiles_n, 1, nkt, nullptr);
+      else
+        hipLaunchKernelGGL((gemm_big_kernel<EPI, true>), grid, dim3(256), 0, s, A, lda, Wt, bias, m, n, k, c, ldc,
+                           gate, tiles_n, used, kps, part);
     } else {
-      const int tiles_n = (int)((n + 127) / 128);
-      const int64_t tiles = (int64_t)tiles_n * ((m + 127) / 128);
-      if (p.split == 1) {
-        hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, EPI, false>), dim3((unsigned)tiles), dim3(256), 0, s, A, lda,
-                           Wt, bias, m, n, k, c, ldc, gate, tiles_n, 1, nkt, nullptr);
-      } else {
-        const int kps = (nkt + p.split - 1) / p.split;
-        const int used = (nkt + kps - 1) / kps;
-        float* part = static_cast<float*>(ws);
-        hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, EPI, true>), dim3((unsigned)(tiles * used)), dim3(256), 0, s, A,
-                           lda, Wt, bias, m, n, k, c, ldc, gate, tiles_n, used, kps, part);
-        const int64_t units = m * (n / 4);
-        hipLaunchKernelGGL(gemm_reduce_kernel<EPI>, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, s, part, used,
-                           m, n, bias, c, ldc, gate);
-      }
+      if (used == 1)
+        hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, EPI, false>), grid, dim3(256), 0, s, A, lda, Wt, bias, m, n, k,
+                           c, ldc, gate, tiles_n, 1, nkt, nullptr);
+      else
+        hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, EPI, true>), grid, dim3(256), 0, s, A, lda, Wt, bias, m, n, k,
+                           c, ldc, gate, tiles_n, used, kps, part);
+    }
+    if (used > 1) {
+      const int64_t units = m * (n / 4);
+      hipLaunchKernelGGL(gemm_reduce_kernel<EPI>, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, s, part, used,
+                         m, n, bias, c, ldc, gate);
     }
   } else {
     const int tiles_n = (int)((n + 63) / 64);

@@ -46,7 +46,7 @@ GEMM_SHAPES = [(1, 64, 64), (77, 192, 128), (128, 128, 1152), (300, 1152, 1152),
 @pytest.mark.parametrize("m,n,k", GEMM_SHAPES)
 @pytest.mark.parametrize("epi", [B.PF_EPI_STORE, B.PF_EPI_GELU_TANH, B.PF_EPI_GELU_ERF, B.PF_EPI_GATED_RESIDUAL])
 def test_gemm_bf16(m, n, k, epi, split):
-    """Small grids split k when given a workspace; (4100, 4608, 1152) takes the 256 x 256 tiles."""
+    """Small grids split k when given a workspace (default tile choice: 128 x 128 here)."""
     torch = torch_cuda()
     ws = B.gemm_workspace(m, n, k) if split else None
     seed = m * 7 + n * 11 + k * 13 + epi
@@ -68,6 +68,57 @@ def test_gemm_bf16(m, n, k, epi, split):
         act = {B.PF_EPI_STORE: lambda v: v, B.PF_EPI_GELU_TANH: ref.gelu_tanh, B.PF_EPI_GELU_ERF: ref.gelu_erf}[epi]
         want = ref.bf16_round(act(y))
     assert_close(host(c), want, f"gemm bf16 {m}x{n}x{k} epi={epi}")
+
+
+@pytest.mark.parametrize("split", [False, True], ids=["whole", "ksplit"])
+@pytest.mark.parametrize("m,n,k", [(77, 192, 128), (300, 1344, 1152), (257, 640, 4608)])
+@pytest.mark.parametrize("epi", [B.PF_EPI_STORE, B.PF_EPI_GELU_TANH, B.PF_EPI_GATED_RESIDUAL])
+def test_gemm_bf16_big_tiles(m, n, k, epi, split, monkeypatch):
+    """256 x 256 tiles forced through PF_GEMM_TILE: ragged m and n (partial tiles in both),
+    k from a single 32-deep stage group to a long ring, with and without the k split."""
+    torch = torch_cuda()
+    monkeypatch.setenv("PF_GEMM_TILE", "256")
+    ws = B.gemm_workspace(m, n, k) if split else None
+    seed = m * 5 + n * 3 + k + epi
+    a = synth.randn((m, k), seed, std=1.0, bf16=True)
+    w = synth.randn((n, k), seed + 1, std=1.0 / math.sqrt(k), bf16=True)
+    bias = synth.randn((n,), seed + 2, std=0.5)
+    y = ref.linear(a, w, bias)
+    if epi == B.PF_EPI_GATED_RESIDUAL:
+        x0 = synth.randn((m, n), seed + 3)
+        gate = synth.randn((n,), seed + 4)
+        c = dev(torch, x0)
+        B.pf_gemm(dev(torch, a, torch.bfloat16), dev(torch, w, torch.bfloat16), dev(torch, bias), epi, c,
+                  gate=dev(torch, gate), workspace=ws)
+        want = x0 + gate * y
+    else:
+        c = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+        B.pf_gemm(dev(torch, a, torch.bfloat16), dev(torch, w, torch.bfloat16), dev(torch, bias), epi, c,
+                  workspace=ws)
+        act = {B.PF_EPI_STORE: lambda v: v, B.PF_EPI_GELU_TANH: ref.gelu_tanh}[epi]
+        want = ref.bf16_round(act(y))
+    assert_close(host(c), want, f"gemm bf16 big tiles {m}x{n}x{k} epi={epi}")
+
+
+def test_gemm_bf16_long_k_default_plan():
+    """The Flux-shaped MLP down projection (2048 x 3072 x 12288, gated residual) with the
+    workspace the stage gives it: the default plan takes the 256 x 256 tiles and splits k.
+    Checked on 64 sampled rows (the full fp64 product is too slow for the oracle)."""
+    torch = torch_cuda()
+    m, n, k = 2048, 3072, 12288
+    ws = B.gemm_workspace(m, n, k)
+    seed = 4242
+    a = synth.randn((m, k), seed, std=1.0, bf16=True)
+    w = synth.randn((n, k), seed + 1, std=1.0 / math.sqrt(k), bf16=True)
+    bias = synth.randn((n,), seed + 2, std=0.5)
+    x0 = synth.randn((m, n), seed + 3)
+    gate = synth.randn((n,), seed + 4)
+    c = dev(torch, x0)
+    B.pf_gemm(dev(torch, a, torch.bfloat16), dev(torch, w, torch.bfloat16), dev(torch, bias),
+              B.PF_EPI_GATED_RESIDUAL, c, gate=dev(torch, gate), workspace=ws)
+    rows = np.random.default_rng(seed).choice(m, 64, replace=False)
+    want = x0[rows] + gate * ref.linear(a[rows], w, bias)
+    assert_close(host(c)[rows], want, "gemm bf16 2048x3072x12288 gated residual, sampled rows")
 
 
 def test_gemm_bf16_strided_operands():

@@ -190,6 +190,35 @@ def test_attention_bf16(D, H, S, rows, split):
     assert_close(host(o), want, f"attention bf16 D={D} S={S} rows={rows} vs exact")
 
 
+@pytest.mark.parametrize("cfg", ["c3", "c4", "c5"])
+def test_attention_full_size_sampled(cfg):
+    """One patch's attention at a stage's full size and launch configuration (the patch rows
+    against the whole S_kv-row buffer, with the stage's split workspace): SD3 (d = 64), Flux
+    (d = 128, text prefix included in S_kv) and long-sequence PixArt (d = 72, 262144 keys).
+    Checked on 48 sampled query rows (first, last, tile edges, random) against the oracle over
+    the full key range."""
+    from patch_pipelined_attention_amd.configs import CONFIGS
+    torch = torch_cuda()
+    shape = CONFIGS[cfg]
+    P, S, H, D = shape.patch_rows, shape.seq_kv, shape.heads, shape.head_dim
+    h = H * D
+    seed = 7000 + S + D
+    q = synth.randn((P, 3 * h), seed, std=1.0, bf16=True)
+    K = synth.randn((S, h), seed + 1, std=1.0, bf16=True)
+    V = synth.randn((S, h), seed + 2, std=1.0, bf16=True)
+    kt, vt, kv = _kv_bf16(torch, K, V)
+    o = torch.empty((P, h), dtype=torch.bfloat16, device="cuda")
+    ws = B.attention_workspace(P, H, D)
+    print(f"[attn] full size {cfg}: P={P} S={S} H={H} D={D}", flush=True)
+    B.pf_attention(dev(torch, q, torch.bfloat16), kv, S, P, H, D, o, workspace=ws)
+    rng = np.random.default_rng(seed)
+    rows = np.unique(np.concatenate([[0, 1, 255, 256, 511, 512, P - 1], rng.choice(P, 41, replace=False)]))
+    got = host(o)[rows]
+    want = ref.attention(q[rows, :h], K, V, H, D)
+    assert_close(got, ref.bf16_round(want), f"attention {cfg} full size, sampled rows vs bf16-in")
+    assert_close(got, want, f"attention {cfg} full size, sampled rows vs exact")
+
+
 @pytest.mark.parametrize("D", [64, 72, 128])
 def test_attention_bf16_closed_forms(D):
     torch = torch_cuda()

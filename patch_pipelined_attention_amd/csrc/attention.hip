@@ -30,8 +30,8 @@
 //   * D = 72 pads the score contraction to 80 and the output rows to 96 with zero
 //     operands; nothing outside the real 72 columns is read or written.
 //   * when there are too few (query tile, head) pairs to fill the GPU, the key range is
-//     split across workgroups; each writes its unnormalised partial O with (m, l) and a
-//     combine kernel merges them.
+//     split across workgroups; each writes its slice's normalised result in bf16 with the
+//     slice's (m, l), and a combine kernel merges them (a convex combination).
 //   * the block index is remapped so each XCD (blocks are dealt round-robin to the 8
 //     XCDs) works on a contiguous run of query tiles that share K/V in its L2.
 //
@@ -67,7 +67,7 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const bf16* __restric
                                                          const bf16* __restrict__ Vb, int64_t hidden,
                                                          int64_t S, int64_t rows, int n_qtiles, int n_split,
                                                          int tiles_per_split, bf16* __restrict__ O,
-                                                         int64_t ldo, float* __restrict__ part_o,
+                                                         int64_t ldo, bf16* __restrict__ part_o,
                                                          float* __restrict__ part_ml, float scale_log2) {
   constexpr int BQ = kAttnWaves * 32 * QB;
   constexpr int KS = (D + 15) / 16;
@@ -415,33 +415,25 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const bf16* __restric
   }
 
 #pragma unroll
+  // Whole key range: O = acc / l in bf16.  One slice of a split range: the slice's own
+  // normalised result acc_s / l_s, also in bf16, plus (m_s, l_s) for the merge.
   for (int qb = 0; qb < QB; ++qb) {
     const float l_tot = l_run[qb] + __shfl_xor(l_run[qb], 32, 64);
     if (q_row[qb] >= rows) continue;
-    if (n_split == 1) {
-      const float inv = 1.0f / l_tot;
+    const float inv = 1.0f / l_tot;
+    bf16* dst = n_split == 1 ? O + q_row[qb] * ldo + col0 : part_o + ((int64_t)split * rows + q_row[qb]) * hidden + col0;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int d = db * 32 + 8 * g + 4 * hi;
-          if (d < D) {
-            bf16x4 ov = {(bf16)(o[qb][db][4 * g + 0] * inv), (bf16)(o[qb][db][4 * g + 1] * inv),
-                         (bf16)(o[qb][db][4 * g + 2] * inv), (bf16)(o[qb][db][4 * g + 3] * inv)};
-            *reinterpret_cast<bf16x4*>(O + q_row[qb] * ldo + col0 + d) = ov;
-          }
+      for (int g = 0; g < 4; ++g) {
+        const int d = db * 32 + 8 * g + 4 * hi;
+        if (d < D) {
+          bf16x4 ov = {(bf16)(o[qb][db][4 * g + 0] * inv), (bf16)(o[qb][db][4 * g + 1] * inv),
+                       (bf16)(o[qb][db][4 * g + 2] * inv), (bf16)(o[qb][db][4 * g + 3] * inv)};
+          *reinterpret_cast<bf16x4*>(dst + d) = ov;
         }
-    } else {
-      float* po = part_o + ((int64_t)split * rows + q_row[qb]) * hidden + col0;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int d = db * 32 + 8 * g + 4 * hi;
-          if (d < D)
-            *reinterpret_cast<float4*>(po + d) =
-                make_float4(o[qb][db][4 * g + 0], o[qb][db][4 * g + 1], o[qb][db][4 * g + 2], o[qb][db][4 * g + 3]);
-        }
+      }
+    if (n_split > 1) {
       if (hi == 0) {
         const int64_t H = hidden / D;
         part_ml[(((int64_t)split * 2 + 0) * H + head) * rows + q_row[qb]] = m_ref[qb];
@@ -451,10 +443,12 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const bf16* __restric
   }
 }
 
-// Merge the per-split partial results: O = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s.
+// Merge the per-split partial results.  Slice s holds x_s = acc_s / l_s (bf16) with its
+// reference max m_s and weight sum l_s, so O = sum_s w_s x_s / sum_s w_s with
+// w_s = 2^(m_s - M) l_s (M = max_s m_s): a convex combination of the slices' results.
 // One thread per (row, head, 8 columns).
 template <int D>
-__global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ part_o,
+__global__ __launch_bounds__(256) void attn_combine_kernel(const bf16* __restrict__ part_o,
                                                            const float* __restrict__ part_ml, int n_split,
                                                            int64_t rows, int H, bf16* __restrict__ O,
                                                            int64_t ldo) {
@@ -473,13 +467,12 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
   for (int sp = 0; sp < n_split; ++sp) {
     const float m = part_ml[(((int64_t)sp * 2) * H + head) * rows + row];
     const float l = part_ml[(((int64_t)sp * 2 + 1) * H + head) * rows + row];
-    const float w = __builtin_amdgcn_exp2f(m - M);
-    wsum += w * l;
-    const float* po = part_o + ((int64_t)sp * rows + row) * hidden + (int64_t)head * D + chunk * 8;
-    const float4 a = *reinterpret_cast<const float4*>(po);
-    const float4 b = *reinterpret_cast<const float4*>(po + 4);
-    acc[0] += w * a.x; acc[1] += w * a.y; acc[2] += w * a.z; acc[3] += w * a.w;
-    acc[4] += w * b.x; acc[5] += w * b.y; acc[6] += w * b.z; acc[7] += w * b.w;
+    const float w = __builtin_amdgcn_exp2f(m - M) * l;
+    wsum += w;
+    const bf16x8 x = *reinterpret_cast<const bf16x8*>(part_o + ((int64_t)sp * rows + row) * hidden +
+                                                      (int64_t)head * D + chunk * 8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, (float)x[e], acc[e]);
   }
   const float inv = 1.0f / wsum;
   bf16x8 out;
@@ -604,8 +597,9 @@ static hipError_t launch_attn_d(const void* q, int64_t ldq, const void* k, int64
     const int tps = (int)((ntiles + n_split - 1) / n_split);
     const int n_used = (int)((ntiles + tps - 1) / tps);      // every split gets at least one tile
     const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
-    float* part_o = static_cast<float*>(ws);
-    float* part_ml = part_o ? part_o + (size_t)n_used * rows * hidden : nullptr;
+    // workspace: bf16 slice results [n_used][rows][hidden], then fp32 (m, l) [n_used][2][heads][rows]
+    bf16* part_o = static_cast<bf16*>(ws);
+    float* part_ml = part_o ? reinterpret_cast<float*>(part_o + (size_t)n_used * rows * hidden) : nullptr;
     hipLaunchKernelGGL((attn_bf16_kernel<D, QB>), dim3((unsigned)(wg * n_used)), dim3(64 * kAttnWaves), 0, s,
                        static_cast<const bf16*>(q), ldq, static_cast<const bf16*>(k), ldk,
                        static_cast<const bf16*>(v), hidden, seq_kv, rows, n_qtiles, n_used, tps,
@@ -627,7 +621,7 @@ static hipError_t launch_attn_d(const void* q, int64_t ldq, const void* k, int64
 
 size_t attention_workspace_bytes(int64_t rows, int64_t hidden, int heads, int n_split) {
   if (n_split <= 1) return 0;
-  return sizeof(float) * ((size_t)n_split * rows * hidden + 2 * (size_t)n_split * rows * heads);
+  return sizeof(bf16) * (size_t)n_split * rows * hidden + sizeof(float) * 2 * (size_t)n_split * rows * heads;
 }
 
 hipError_t launch_attention(const void* q, int64_t ldq, const void* k, int64_t ldk, const void* v, int64_t ldv,

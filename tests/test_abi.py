@@ -113,10 +113,10 @@ def test_component_validation(lib):
     assert lib.pf_attention(base, 384, ctypes.byref(kv), 1001, 10, 2, 64, base, 128, None, 0, None) == B.PF_ERR_INVALID_ARG
     # misaligned workspace
     assert lib.pf_attention(base, 384, ctypes.byref(kv), 1000, 10, 2, 64, base, 128, base + 8, 1 << 20, None) == B.PF_ERR_INVALID_ARG
-    # workspace size query: 8 splits of fp32 partial rows plus (m, l) per split
+    # workspace size query: 8 splits of bf16 slice results plus fp32 (m, l) per split
     n = ctypes.c_uint64()
     assert lib.pf_attention_workspace_size(1024, 16, 72, ctypes.byref(n)) == B.PF_OK
-    assert n.value == 4 * (8 * 1024 * 1152 + 2 * 8 * 1024 * 16)
+    assert n.value == 2 * 8 * 1024 * 1152 + 4 * 2 * 8 * 1024 * 16
     # misaligned pointer
     assert lib.pf_ln_modulate(base + 4, 3, 64, base, base, 1e-6, base, 0, None) == B.PF_ERR_INVALID_ARG
 

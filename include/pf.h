@@ -191,6 +191,7 @@ pf_status pf_ln_modulate(const float* x, int64_t rows, int32_t hidden, const flo
  * c is fp32 for PF_EPI_GATED_RESIDUAL (gate fp32 [n]).  fp32 accumulation.  For bf16:
  * n % 64 == 0 and k % 64 == 0.  `workspace` (device, may be NULL) lets a grid too small to
  * fill the GPU split k into slices summed by a second pass (in a fixed order: deterministic);
+ * calls sharing a workspace must not overlap in time (one stream, or ordered streams).
  * pf_gemm_workspace_size gives the bytes that allow the split the library would choose.
  * The tile size (128 x 128, or 256 x 256 for long reductions) is chosen per shape; the
  * environment variable PF_GEMM_TILE=128 or 256 forces it (read on every call, so set it
@@ -198,6 +199,20 @@ pf_status pf_ln_modulate(const float* x, int64_t rows, int32_t hidden, const flo
 pf_status pf_gemm(const void* a, int64_t lda, const void* w, const float* bias, int64_t m,
                   int64_t n, int64_t k, int32_t epi, void* c, int64_t ldc, const float* gate,
                   int32_t dtype, void* workspace, uint64_t workspace_bytes, void* stream);
+
+/* The stage's QKV projection with the KV splice in its epilogue (bf16 only): the product
+ * y = a . w^T + bias with a [m, hidden] (row stride lda), w [3 hidden, hidden], bias fp32
+ * [3 hidden], split by output feature: y[:, 0:h] (Q) to q (row stride ldq), y[:, h:2h] to
+ * rows [row_offset, row_offset + m) of kv's K matrix and y[:, 2h:3h] to the same rows of its
+ * V matrix.  kv must have row_elems == k_ld == hidden and V in the K8 layout; no other byte
+ * of the buffer changes.  Each value is the bf16 rounding of its fp32 sum, identical to
+ * pf_gemm(PF_EPI_STORE) followed by kvbuf_splice of the K and V columns.  This is the
+ * in-place update of a layer's full-spatial buffer with the current patch's fresh K/V
+ * (PipeFusion mechanism 2), done where the values are produced.  q, a and the buffer must not
+ * overlap.  The workspace is as for pf_gemm with n = 3 hidden, k = hidden. */
+pf_status pf_gemm_qkv_splice(const void* a, int64_t lda, const void* w, const float* bias, int64_t m,
+                             int64_t hidden, void* q, int64_t ldq, const pf_kv_view* kv, int64_t row_offset,
+                             void* workspace, uint64_t workspace_bytes, void* stream);
 
 /* Workspace bytes pf_gemm can use for an [m, n, k] bf16 product (0: it never splits). */
 pf_status pf_gemm_workspace_size(int64_t m, int64_t n, int64_t k, uint64_t* bytes);

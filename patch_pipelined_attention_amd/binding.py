@@ -65,6 +65,8 @@ _SIGNATURES = {
     "stage_get_kvbuf": [_P, _I32, ctypes.POINTER(KVView)],
     "pf_ln_modulate": [_P, _I64, _I32, _P, _P, _F, _P, _I32, _P],
     "pf_gemm": [_P, _I64, _P, _P, _I64, _I64, _I64, _I32, _P, _I64, _P, _I32, _P, ctypes.c_uint64, _P],
+    "pf_gemm_qkv_splice": [_P, _I64, _P, _P, _I64, _I64, _P, _I64, ctypes.POINTER(KVView), _I64, _P, ctypes.c_uint64,
+                           _P],
     "pf_gemm_workspace_size": [_I64, _I64, _I64, ctypes.POINTER(ctypes.c_uint64)],
     "pf_attention": [_P, _I64, ctypes.POINTER(KVView), _I64, _I64, _I32, _I32, _P, _I64, _P, ctypes.c_uint64, _P],
     "pf_attention_workspace_size": [_I64, _I32, _I32, ctypes.POINTER(ctypes.c_uint64)],
@@ -183,6 +185,17 @@ def pf_gemm(a, w, bias, epi: int, c, gate=None, m=None, lda=None, ldc=None, work
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().pf_gemm(_ptr(a), lda, _ptr(w), _ptr(bias), m, n, k, epi, _ptr(c), ldc, _ptr(gate),
                          _dtype_code(w), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def pf_gemm_qkv_splice(a, w, bias, q, kv: KVView, row_offset: int, m=None, lda=None, ldq=None, workspace=None,
+                       stream=None) -> None:
+    m = a.shape[0] if m is None else m
+    hidden = w.shape[1]
+    lda = a.stride(0) if lda is None else lda
+    ldq = q.stride(0) if ldq is None else ldq
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().pf_gemm_qkv_splice(_ptr(a), lda, _ptr(w), _ptr(bias), m, hidden, _ptr(q), ldq, ctypes.byref(kv),
+                                    row_offset, _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def pf_gemm_workspace_size(m: int, n: int, k: int) -> int:

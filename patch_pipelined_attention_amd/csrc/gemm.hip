@@ -10,7 +10,15 @@
 // Tiles: 128 x 128 (two workgroups per CU) by default; 256 x 256 (one per CU, each wavefront
 // 128 x 128 = 4 x 4 MFMA blocks, 0.5 KB of LDS operand reads per MFMA) for long reductions
 // (k >= 8192), where its higher per-k rate outweighs its fixed cost per tile.  Grids too
-// small to fill the GPU split k and sum the slices in a reduce pass.
+// small to fill the GPU split k: every slice writes its fp32 partial tile and a reduce pass
+// sums the slices in order (deterministic) and applies the epilogue.  (A last-arriving-slice
+// merge inside the GEMM measured slower on MI355X: the partials cross XCDs, whose L2s are
+// not coherent, so they must be written through and read back from the device-coherent
+// level, a longer latency chain than one more launch.)
+//
+// Workgroup ids map to tiles XCD by XCD (consecutive ids on one XCD), and within that in
+// groups of kGroupRows tile rows walked column by column, so the workgroups an XCD runs at
+// once share a few weight and activation row blocks in its L2.
 //
 // fp32 path (tiny fp32 stages only): a plain 64x64 LDS-tiled FMA kernel.
 #include "pf_internal.h"
@@ -45,6 +53,115 @@ __device__ __forceinline__ int gemm_xcd_remap(int bid, int nb) {
   return x * per + (x < rem ? x : rem) + bid / 8;
 }
 
+constexpr int kGroupRows = 4;
+
+// Tile (row tm, column tn) of tile id `rest` in [0, tiles_m * tiles_n): groups of kGroupRows
+// tile rows (fewer in the last group), each walked column by column.
+__device__ __forceinline__ void gemm_tile_of(int rest, int tiles_m, int tiles_n, int64_t& tm, int& tn) {
+  const int grp = rest / (kGroupRows * tiles_n);
+  const int within = rest - grp * kGroupRows * tiles_n;
+  const int left = tiles_m - grp * kGroupRows;
+  const int gm = left < kGroupRows ? left : kGroupRows;
+  tm = (int64_t)grp * kGroupRows + within % gm;
+  tn = within / gm;
+}
+
+// Bias, activation and store of 4 consecutive outputs y[m][f..f+3] (f % 4 == 0).
+template <int EPI>
+__device__ __forceinline__ void gemm_store4(float v0, float v1, float v2, float v3, int64_t m, int64_t f,
+                                            const float* __restrict__ bias, void* __restrict__ C, int64_t ldc,
+                                            const float* __restrict__ gate, const QkvSplice& sp) {
+  const float4 bv = *reinterpret_cast<const float4*>(bias + f);
+  v0 += bv.x;
+  v1 += bv.y;
+  v2 += bv.z;
+  v3 += bv.w;
+  if constexpr (EPI == kEpiGatedResidual) {
+    float* cp = static_cast<float*>(C) + m * ldc + f;
+    const float4 gv = *reinterpret_cast<const float4*>(gate + f);
+    float4 cv = *reinterpret_cast<float4*>(cp);
+    cv.x += gv.x * v0;
+    cv.y += gv.y * v1;
+    cv.z += gv.z * v2;
+    cv.w += gv.w * v3;
+    *reinterpret_cast<float4*>(cp) = cv;
+  } else if constexpr (EPI == kEpiQkvSplice) {
+    const bf16x4 o = {(bf16)v0, (bf16)v1, (bf16)v2, (bf16)v3};
+    if (f < sp.h) {
+      *reinterpret_cast<bf16x4*>(static_cast<bf16*>(C) + m * ldc + f) = o;
+    } else if (f < 2 * sp.h) {
+      *reinterpret_cast<bf16x4*>(static_cast<bf16*>(sp.k) + (sp.row0 + m) * sp.h + (f - sp.h)) = o;
+    } else {
+      // K8: element (r, c) at ((r / 8) * h + c) * 8 + r % 8, so columns c .. c+3 are 8 apart
+      const int64_t r = sp.row0 + m, c = f - 2 * sp.h;
+      bf16* vp = static_cast<bf16*>(sp.v) + ((r >> 3) * sp.h + c) * 8 + (r & 7);
+      vp[0] = o[0];
+      vp[8] = o[1];
+      vp[16] = o[2];
+      vp[24] = o[3];
+    }
+  } else {
+    const bf16x4 o = {(bf16)epi_act<EPI>(v0), (bf16)epi_act<EPI>(v1), (bf16)epi_act<EPI>(v2),
+                      (bf16)epi_act<EPI>(v3)};
+    *reinterpret_cast<bf16x4*>(static_cast<bf16*>(C) + m * ldc + f) = o;
+  }
+}
+
+// Epilogue of a BF x BT tile held by 4 wavefronts in a 2 x 2 grid:
+//   acc[i][t][4g+j] = y[token m0 + wt*BT/2 + t*32 + l32][feature n0 + wf*BF/2 + i*32 + 8g + 4hi + j].
+// With SPLIT the slice stores its fp32 partial tile (part[split][m][f]) for the reduce pass.
+template <int BF, int BT, int FB, int TB, int EPI, bool SPLIT>
+__device__ __forceinline__ void gemm_epilogue(f32x16 (&acc)[FB][TB], int64_t m0, int64_t n0, int64_t M, int64_t N,
+                                              const float* __restrict__ bias, void* __restrict__ C, int64_t ldc,
+                                              const float* __restrict__ gate, const QkvSplice& sp, int split,
+                                              float* __restrict__ part) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int wf = wave & 1, wt = wave >> 1;
+#pragma unroll
+  for (int t = 0; t < TB; ++t) {
+    const int64_t m = m0 + wt * (BT / 2) + t * 32 + l32;
+    if (m >= M) continue;
+#pragma unroll
+    for (int i = 0; i < FB; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int64_t f = n0 + wf * (BF / 2) + i * 32 + 8 * g + 4 * hi;
+        if (f >= N) continue;
+        if constexpr (SPLIT)
+          *reinterpret_cast<float4*>(part + ((int64_t)split * M + m) * N + f) =
+              make_float4(acc[i][t][4 * g + 0], acc[i][t][4 * g + 1], acc[i][t][4 * g + 2], acc[i][t][4 * g + 3]);
+        else
+          gemm_store4<EPI>(acc[i][t][4 * g + 0], acc[i][t][4 * g + 1], acc[i][t][4 * g + 2], acc[i][t][4 * g + 3], m,
+                           f, bias, C, ldc, gate, sp);
+      }
+  }
+}
+
+// Sum of the k slices of a split GEMM, then bias and the epilogue.  One thread per 4
+// consecutive outputs of a row; slices are summed in order, so the result is deterministic.
+template <int EPI>
+__global__ __launch_bounds__(256) void gemm_reduce_kernel(const float* __restrict__ part, int n_split, int64_t M,
+                                                          int64_t N, const float* __restrict__ bias,
+                                                          void* __restrict__ C, int64_t ldc,
+                                                          const float* __restrict__ gate, QkvSplice sp) {
+  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t nq = N / 4;
+  if (id >= M * nq) return;
+  const int64_t m = id / nq;
+  const int64_t f = (id - m * nq) * 4;
+  float4 s = *reinterpret_cast<const float4*>(part + m * N + f);
+  for (int s2 = 1; s2 < n_split; ++s2) {
+    const float4 v = *reinterpret_cast<const float4*>(part + ((int64_t)s2 * M + m) * N + f);
+    s.x += v.x;
+    s.y += v.y;
+    s.z += v.z;
+    s.w += v.w;
+  }
+  gemm_store4<EPI>(s.x, s.y, s.z, s.w, m, f, bias, C, ldc, gate, sp);
+}
+
 // bf16 tile kernel: BF features x BT tokens per workgroup (4 wavefronts in a 2 x 2 grid, each
 // (BF/2) x (BT/2) = FB x TB blocks of 32 x 32), k staged 64 at a time (4 MFMA k-steps per
 // barrier), two workgroups per CU.  The W rows and X rows of a k tile are copied global ->
@@ -57,7 +174,7 @@ template <int BF, int BT, int EPI, bool SPLIT>
 __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
     const bf16* __restrict__ A, int64_t lda, const bf16* __restrict__ W, const float* __restrict__ bias, int64_t M,
     int64_t N, int64_t K, void* __restrict__ C, int64_t ldc, const float* __restrict__ gate, int tiles_n,
-    int n_split, int ktiles_per_split, float* __restrict__ part) {
+    int n_split, int ktiles_per_split, float* __restrict__ part, QkvSplice sp) {
   constexpr int BK = 64;                 // k per stage: four MFMA k-steps
   constexpr int KSTEPS = BK / 16;
   constexpr int ROWS = BF + BT;          // stage rows: W rows, then X rows
@@ -79,8 +196,9 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
   const int lid = gemm_xcd_remap(blockIdx.x, gridDim.x);
   const int split = lid % n_split;
   const int rest = lid / n_split;
-  const int tile_n = rest % tiles_n;
-  const int64_t tile_m = rest / tiles_n;
+  int64_t tile_m;
+  int tile_n;
+  gemm_tile_of(rest, (int)((M + BT - 1) / BT), tiles_n, tile_m, tile_n);
   const int64_t n0 = (int64_t)tile_n * BF;
   const int64_t m0 = tile_m * BT;
   const int64_t nkt = K / BK;
@@ -169,44 +287,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
   for (; kt + 1 < kt1; ++kt) ktile(kt, true);
   if (kt < kt1) ktile(kt, false);
 
-  // acc[i][t][4g+j] = y[token = m0 + wt*BT/2 + t*32 + l32][feature = n0 + wf*BF/2 + i*32 + 8g + 4hi + j]
-#pragma unroll
-  for (int t = 0; t < TB; ++t) {
-    const int64_t m = m0 + wt * (BT / 2) + t * 32 + l32;
-    if (m >= M) continue;
-#pragma unroll
-    for (int i = 0; i < FB; ++i) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int64_t f = n0 + wf * (BF / 2) + i * 32 + 8 * g + 4 * hi;
-        if (f >= N) continue;
-        if constexpr (SPLIT) {
-          *reinterpret_cast<float4*>(part + ((int64_t)split * M + m) * N + f) =
-              make_float4(acc[i][t][4 * g + 0], acc[i][t][4 * g + 1], acc[i][t][4 * g + 2], acc[i][t][4 * g + 3]);
-        } else {
-          const float4 bv = *reinterpret_cast<const float4*>(bias + f);
-          const float v0 = acc[i][t][4 * g + 0] + bv.x;
-          const float v1 = acc[i][t][4 * g + 1] + bv.y;
-          const float v2 = acc[i][t][4 * g + 2] + bv.z;
-          const float v3 = acc[i][t][4 * g + 3] + bv.w;
-          if constexpr (EPI == kEpiGatedResidual) {
-            float* cp = static_cast<float*>(C) + m * ldc + f;
-            const float4 gv = *reinterpret_cast<const float4*>(gate + f);
-            float4 cv = *reinterpret_cast<float4*>(cp);
-            cv.x += gv.x * v0;
-            cv.y += gv.y * v1;
-            cv.z += gv.z * v2;
-            cv.w += gv.w * v3;
-            *reinterpret_cast<float4*>(cp) = cv;
-          } else {
-            bf16x4 o = {(bf16)epi_act<EPI>(v0), (bf16)epi_act<EPI>(v1), (bf16)epi_act<EPI>(v2),
-                        (bf16)epi_act<EPI>(v3)};
-            *reinterpret_cast<bf16x4*>(static_cast<bf16*>(C) + m * ldc + f) = o;
-          }
-        }
-      }
-    }
-  }
+  gemm_epilogue<BF, BT, FB, TB, EPI, SPLIT>(acc, m0, n0, M, N, bias, C, ldc, gate, sp, split, part);
 }
 
 // bf16 big-tile kernel: 256 features x 256 tokens per workgroup, 4 wavefronts in a 2 x 2
@@ -223,7 +304,7 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(const bf16* __restrict
                                                           int64_t M, int64_t N, int64_t K, void* __restrict__ C,
                                                           int64_t ldc, const float* __restrict__ gate, int tiles_n,
                                                           int n_split, int ktiles_per_split,
-                                                          float* __restrict__ part) {
+                                                          float* __restrict__ part, QkvSplice sp) {
   constexpr int BF = 256, BT = 256;
   constexpr int BK = 32;                 // k per stage: two MFMA k-steps
   constexpr int KSTEPS = BK / 16;
@@ -246,8 +327,9 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(const bf16* __restrict
   const int lid = gemm_xcd_remap(blockIdx.x, gridDim.x);
   const int split = lid % n_split;
   const int rest = lid / n_split;
-  const int tile_n = rest % tiles_n;
-  const int64_t tile_m = rest / tiles_n;
+  int64_t tile_m;
+  int tile_n;
+  gemm_tile_of(rest, (int)((M + BT - 1) / BT), tiles_n, tile_m, tile_n);
   const int64_t n0 = (int64_t)tile_n * BF;
   const int64_t m0 = tile_m * BT;
   const int64_t nkt = K / BK;
@@ -360,81 +442,7 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(const bf16* __restrict
   for (; kt + NSTAGE - 1 < kt1; ++kt) ktile(kt, true);
   for (; kt < kt1; ++kt) ktile(kt, false);
 
-  // acc[i][t][4g+j] = y[token = m0 + wt*BT/2 + t*32 + l32][feature = n0 + wf*BF/2 + i*32 + 8g + 4hi + j]
-#pragma unroll
-  for (int t = 0; t < TB; ++t) {
-    const int64_t m = m0 + wt * (BT / 2) + t * 32 + l32;
-    if (m >= M) continue;
-#pragma unroll
-    for (int i = 0; i < FB; ++i) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int64_t f = n0 + wf * (BF / 2) + i * 32 + 8 * g + 4 * hi;
-        if (f >= N) continue;
-        if constexpr (SPLIT) {
-          *reinterpret_cast<float4*>(part + ((int64_t)split * M + m) * N + f) =
-              make_float4(acc[i][t][4 * g + 0], acc[i][t][4 * g + 1], acc[i][t][4 * g + 2], acc[i][t][4 * g + 3]);
-        } else {
-          const float4 bv = *reinterpret_cast<const float4*>(bias + f);
-          const float v0 = acc[i][t][4 * g + 0] + bv.x;
-          const float v1 = acc[i][t][4 * g + 1] + bv.y;
-          const float v2 = acc[i][t][4 * g + 2] + bv.z;
-          const float v3 = acc[i][t][4 * g + 3] + bv.w;
-          if constexpr (EPI == kEpiGatedResidual) {
-            float* cp = static_cast<float*>(C) + m * ldc + f;
-            const float4 gv = *reinterpret_cast<const float4*>(gate + f);
-            float4 cv = *reinterpret_cast<float4*>(cp);
-            cv.x += gv.x * v0;
-            cv.y += gv.y * v1;
-            cv.z += gv.z * v2;
-            cv.w += gv.w * v3;
-            *reinterpret_cast<float4*>(cp) = cv;
-          } else {
-            bf16x4 o = {(bf16)epi_act<EPI>(v0), (bf16)epi_act<EPI>(v1), (bf16)epi_act<EPI>(v2),
-                        (bf16)epi_act<EPI>(v3)};
-            *reinterpret_cast<bf16x4*>(static_cast<bf16*>(C) + m * ldc + f) = o;
-          }
-        }
-      }
-    }
-  }
-}
-
-// Sum of the k slices of a split GEMM, then bias and the epilogue.  One thread per 4
-// consecutive outputs of a row; slices are summed in order, so the result is deterministic.
-template <int EPI>
-__global__ __launch_bounds__(256) void gemm_reduce_kernel(const float* __restrict__ part, int n_split, int64_t M,
-                                                          int64_t N, const float* __restrict__ bias,
-                                                          void* __restrict__ C, int64_t ldc,
-                                                          const float* __restrict__ gate) {
-  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t nq = N / 4;
-  if (id >= M * nq) return;
-  const int64_t m = id / nq;
-  const int64_t f = (id - m * nq) * 4;
-  float4 s = *reinterpret_cast<const float4*>(part + m * N + f);
-  for (int sp = 1; sp < n_split; ++sp) {
-    const float4 v = *reinterpret_cast<const float4*>(part + ((int64_t)sp * M + m) * N + f);
-    s.x += v.x;
-    s.y += v.y;
-    s.z += v.z;
-    s.w += v.w;
-  }
-  const float4 bv = *reinterpret_cast<const float4*>(bias + f);
-  const float v0 = s.x + bv.x, v1 = s.y + bv.y, v2 = s.z + bv.z, v3 = s.w + bv.w;
-  if constexpr (EPI == kEpiGatedResidual) {
-    float* cp = static_cast<float*>(C) + m * ldc + f;
-    const float4 gv = *reinterpret_cast<const float4*>(gate + f);
-    float4 cv = *reinterpret_cast<float4*>(cp);
-    cv.x += gv.x * v0;
-    cv.y += gv.y * v1;
-    cv.z += gv.z * v2;
-    cv.w += gv.w * v3;
-    *reinterpret_cast<float4*>(cp) = cv;
-  } else {
-    bf16x4 o = {(bf16)epi_act<EPI>(v0), (bf16)epi_act<EPI>(v1), (bf16)epi_act<EPI>(v2), (bf16)epi_act<EPI>(v3)};
-    *reinterpret_cast<bf16x4*>(static_cast<bf16*>(C) + m * ldc + f) = o;
-  }
+  gemm_epilogue<BF, BT, FB, TB, EPI, SPLIT>(acc, m0, n0, M, N, bias, C, ldc, gate, sp, split, part);
 }
 
 // ---------------------------------------------------------------------------------
@@ -566,7 +574,7 @@ size_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k) {
 template <int EPI>
 static void launch_gemm_epi(const void* a, int64_t lda, const void* w, const float* bias, int64_t m, int64_t n,
                             int64_t k, void* c, int64_t ldc, const float* gate, int dtype, void* ws,
-                            size_t ws_bytes, hipStream_t s) {
+                            size_t ws_bytes, hipStream_t s, const QkvSplice& sp) {
   if (dtype == kDtypeBF16) {
     const bf16* A = static_cast<const bf16*>(a);
     const bf16* Wt = static_cast<const bf16*>(w);
@@ -582,22 +590,22 @@ static void launch_gemm_epi(const void* a, int64_t lda, const void* w, const flo
     if (p.big) {
       if (used == 1)
         hipLaunchKernelGGL((gemm_big_kernel<EPI, false>), grid, dim3(256), 0, s, A, lda, Wt, bias, m, n, k, c, ldc,
-                           gate, tiles_n, 1, nkt, nullptr);
+                           gate, tiles_n, 1, nkt, nullptr, sp);
       else
         hipLaunchKernelGGL((gemm_big_kernel<EPI, true>), grid, dim3(256), 0, s, A, lda, Wt, bias, m, n, k, c, ldc,
-                           gate, tiles_n, used, kps, part);
+                           gate, tiles_n, used, kps, part, sp);
     } else {
       if (used == 1)
         hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, EPI, false>), grid, dim3(256), 0, s, A, lda, Wt, bias, m, n, k,
-                           c, ldc, gate, tiles_n, 1, nkt, nullptr);
+                           c, ldc, gate, tiles_n, 1, nkt, nullptr, sp);
       else
         hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, EPI, true>), grid, dim3(256), 0, s, A, lda, Wt, bias, m, n, k,
-                           c, ldc, gate, tiles_n, used, kps, part);
+                           c, ldc, gate, tiles_n, used, kps, part, sp);
     }
     if (used > 1) {
       const int64_t units = m * (n / 4);
       hipLaunchKernelGGL(gemm_reduce_kernel<EPI>, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, s, part, used,
-                         m, n, bias, c, ldc, gate);
+                         m, n, bias, c, ldc, gate, sp);
     }
   } else {
     const int tiles_n = (int)((n + 63) / 64);
@@ -609,13 +617,18 @@ static void launch_gemm_epi(const void* a, int64_t lda, const void* w, const flo
 
 hipError_t launch_gemm(const void* a, int64_t lda, const void* w, const float* bias, int64_t m, int64_t n, int64_t k,
                        int epi, void* c, int64_t ldc, const float* gate, int dtype, void* ws, size_t ws_bytes,
-                       hipStream_t s) {
+                       hipStream_t s, const QkvSplice* splice) {
   if (m <= 0) return hipSuccess;
+  const QkvSplice sp = splice ? *splice : QkvSplice{nullptr, nullptr, 0, 0};
   switch (epi) {
-    case kEpiStore: launch_gemm_epi<kEpiStore>(a, lda, w, bias, m, n, k, c, ldc, gate, dtype, ws, ws_bytes, s); break;
-    case kEpiGeluTanh: launch_gemm_epi<kEpiGeluTanh>(a, lda, w, bias, m, n, k, c, ldc, gate, dtype, ws, ws_bytes, s); break;
-    case kEpiGeluErf: launch_gemm_epi<kEpiGeluErf>(a, lda, w, bias, m, n, k, c, ldc, gate, dtype, ws, ws_bytes, s); break;
-    default: launch_gemm_epi<kEpiGatedResidual>(a, lda, w, bias, m, n, k, c, ldc, gate, dtype, ws, ws_bytes, s); break;
+    case kEpiStore: launch_gemm_epi<kEpiStore>(a, lda, w, bias, m, n, k, c, ldc, gate, dtype, ws, ws_bytes, s, sp); break;
+    case kEpiGeluTanh: launch_gemm_epi<kEpiGeluTanh>(a, lda, w, bias, m, n, k, c, ldc, gate, dtype, ws, ws_bytes, s, sp); break;
+    case kEpiGeluErf: launch_gemm_epi<kEpiGeluErf>(a, lda, w, bias, m, n, k, c, ldc, gate, dtype, ws, ws_bytes, s, sp); break;
+    case kEpiQkvSplice:
+      if (dtype != kDtypeBF16 || !splice) return hipErrorInvalidValue;
+      launch_gemm_epi<kEpiQkvSplice>(a, lda, w, bias, m, n, k, c, ldc, gate, dtype, ws, ws_bytes, s, sp);
+      break;
+    default: launch_gemm_epi<kEpiGatedResidual>(a, lda, w, bias, m, n, k, c, ldc, gate, dtype, ws, ws_bytes, s, sp); break;
   }
   return hipGetLastError();
 }

@@ -27,6 +27,7 @@ constexpr int kEpiStore = 0;
 constexpr int kEpiGeluTanh = 1;
 constexpr int kEpiGeluErf = 2;
 constexpr int kEpiGatedResidual = 3;
+constexpr int kEpiQkvSplice = 4;   // stage only: Q to C, K and V into the layer's KV buffer
 
 // Workgroup barrier for kernels that keep direct global -> LDS loads in flight across
 // barriers.  __syncthreads() (and any release fence covering LDS) makes each wavefront
@@ -85,10 +86,21 @@ hipError_t launch_ln_modulate(const float* x, int64_t rows, int hidden, const fl
 hipError_t launch_adaln(const float* cond, const void* w, const float* b, int hidden, float* mod,
                         int dtype, hipStream_t s);
 
+// Destination of the fused QKV epilogue (kEpiQkvSplice, bf16 only): output features [0, h)
+// (Q) go to c; features [h, 2h) are row `row0 + i` of the K buffer (ROWS layout, row stride
+// h) and [2h, 3h) the same row of the V buffer (K8 layout, h columns).
+struct QkvSplice {
+  void* k;
+  void* v;
+  int64_t row0;
+  int64_t h;
+};
+
 // `ws` (may be NULL) is scratch for the k-split of grids too small to fill the GPU.
 hipError_t launch_gemm(const void* a, int64_t lda, const void* w, const float* bias, int64_t m,
                        int64_t n, int64_t k, int epi, void* c, int64_t ldc, const float* gate,
-                       int dtype, void* ws, size_t ws_bytes, hipStream_t s);
+                       int dtype, void* ws, size_t ws_bytes, hipStream_t s,
+                       const QkvSplice* splice = nullptr);
 
 // Scratch bytes the bf16 GEMM would use for its k-split at this shape (0: no split).
 size_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k);

@@ -13,54 +13,67 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 // ---------------------------------------------------------------------------------
 // y = LayerNorm(x) * (1 + scale) + shift, one wavefront per row.  The row is held in
-// registers (float4 per lane and slot), so x is read once.  mean and variance are the
-// two-pass fp32 statistics of the row (biased variance), no affine.
+// registers (NS float4 per lane), so x is read once; all NS loads of a lane (and, for
+// hidden <= 3072, those of shift and scale) are issued before the first use: indices past
+// the row are clamped to its last chunk and masked out of the sums.  mean and variance are the two-pass fp32
+// statistics of the row (biased variance), no affine.
 // ---------------------------------------------------------------------------------
-template <typename OutT>
+template <typename OutT, int NS>
 __global__ __launch_bounds__(256) void ln_modulate_kernel(const float* __restrict__ x, int64_t rows,
                                                           int hidden, const float* __restrict__ shift,
                                                           const float* __restrict__ scale, float eps,
                                                           OutT* __restrict__ y) {
-  constexpr int kSlots = kMaxHidden / 256;
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
   const int n4 = hidden >> 2;
   const float4* xr = reinterpret_cast<const float4*>(x + row * hidden);
-  float4 v[kSlots];
-  float sum = 0.f;
+  const float4* sh4 = reinterpret_cast<const float4*>(shift);
+  const float4* sc4 = reinterpret_cast<const float4*>(scale);
+  // shift and scale are loaded up front too while they fit in registers (hidden <= 3072)
+  constexpr bool kPreload = NS <= 12;
+  float4 v[NS], sh[NS], sc[NS];
 #pragma unroll
-  for (int i = 0; i < kSlots; ++i) {
-    const int idx = lane + i * 64;
-    if (idx < n4) {
-      v[i] = xr[idx];
-      sum += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+  for (int i = 0; i < NS; ++i) {
+    const int idx = lane + i * 64 < n4 ? lane + i * 64 : n4 - 1;
+    v[i] = xr[idx];
+  }
+  if constexpr (kPreload) {
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const int idx = lane + i * 64 < n4 ? lane + i * 64 : n4 - 1;
+      sh[i] = sh4[idx];
+      sc[i] = sc4[idx];
     }
   }
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < NS; ++i)
+    if (lane + i * 64 < n4) sum += (v[i].x + v[i].y) + (v[i].z + v[i].w);
   const float inv_h = 1.0f / (float)hidden;
   const float mean = wave_sum(sum) * inv_h;
   float sq = 0.f;
 #pragma unroll
-  for (int i = 0; i < kSlots; ++i) {
-    const int idx = lane + i * 64;
-    if (idx < n4) {
+  for (int i = 0; i < NS; ++i) {
+    if (lane + i * 64 < n4) {
       const float a = v[i].x - mean, b = v[i].y - mean, c = v[i].z - mean, d = v[i].w - mean;
       sq += (a * a + b * b) + (c * c + d * d);
     }
   }
   const float var = wave_sum(sq) * inv_h;
   const float rstd = 1.0f / sqrtf(var + eps);
-  const float4* sh4 = reinterpret_cast<const float4*>(shift);
-  const float4* sc4 = reinterpret_cast<const float4*>(scale);
 #pragma unroll
-  for (int i = 0; i < kSlots; ++i) {
+  for (int i = 0; i < NS; ++i) {
     const int idx = lane + i * 64;
     if (idx < n4) {
-      const float4 sh = sh4[idx], sc = sc4[idx];
-      float o0 = (v[i].x - mean) * rstd * (1.0f + sc.x) + sh.x;
-      float o1 = (v[i].y - mean) * rstd * (1.0f + sc.y) + sh.y;
-      float o2 = (v[i].z - mean) * rstd * (1.0f + sc.z) + sh.z;
-      float o3 = (v[i].w - mean) * rstd * (1.0f + sc.w) + sh.w;
+      if constexpr (!kPreload) {
+        sh[i] = sh4[idx];
+        sc[i] = sc4[idx];
+      }
+      const float o0 = (v[i].x - mean) * rstd * (1.0f + sc[i].x) + sh[i].x;
+      const float o1 = (v[i].y - mean) * rstd * (1.0f + sc[i].y) + sh[i].y;
+      const float o2 = (v[i].z - mean) * rstd * (1.0f + sc[i].z) + sh[i].z;
+      const float o3 = (v[i].w - mean) * rstd * (1.0f + sc[i].w) + sh[i].w;
       if constexpr (sizeof(OutT) == 2) {
         bf16x4 o = {(bf16)o0, (bf16)o1, (bf16)o2, (bf16)o3};
         *reinterpret_cast<bf16x4*>(y + row * hidden + idx * 4) = o;
@@ -71,16 +84,26 @@ __global__ __launch_bounds__(256) void ln_modulate_kernel(const float* __restric
   }
 }
 
+template <typename OutT, int NS>
+static void launch_ln_ns(int ns, dim3 grid, const float* x, int64_t rows, int hidden, const float* shift,
+                         const float* scale, float eps, OutT* y, hipStream_t s) {
+  if constexpr (NS > 1) {
+    if (ns < NS) return launch_ln_ns<OutT, NS - 1>(ns, grid, x, rows, hidden, shift, scale, eps, y, s);
+  }
+  hipLaunchKernelGGL((ln_modulate_kernel<OutT, NS>), grid, dim3(256), 0, s, x, rows, hidden, shift, scale, eps, y);
+}
+
 hipError_t launch_ln_modulate(const float* x, int64_t rows, int hidden, const float* shift,
                               const float* scale, float eps, void* y, int dtype, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
+  constexpr int kSlots = kMaxHidden / 256;
+  const int ns = (hidden / 4 + 63) / 64;             // float4 chunks per lane
+  if (ns < 1 || ns > kSlots) return hipErrorInvalidValue;
   dim3 grid((unsigned)((rows + 3) / 4));
   if (dtype == kDtypeBF16)
-    hipLaunchKernelGGL(ln_modulate_kernel<bf16>, grid, dim3(256), 0, s, x, rows, hidden, shift, scale,
-                       eps, static_cast<bf16*>(y));
+    launch_ln_ns<bf16, kSlots>(ns, grid, x, rows, hidden, shift, scale, eps, static_cast<bf16*>(y), s);
   else
-    hipLaunchKernelGGL(ln_modulate_kernel<float>, grid, dim3(256), 0, s, x, rows, hidden, shift, scale,
-                       eps, static_cast<float*>(y));
+    launch_ln_ns<float, kSlots>(ns, grid, x, rows, hidden, shift, scale, eps, static_cast<float*>(y), s);
   return hipGetLastError();
 }
 

@@ -205,6 +205,33 @@ extern "C" pf_status pf_gemm(const void* a, int64_t lda, const void* w, const fl
   return e == hipSuccess ? PF_OK : hip_fail(e, "gemm launch");
 }
 
+extern "C" pf_status pf_gemm_qkv_splice(const void* a, int64_t lda, const void* w, const float* bias, int64_t m,
+                                        int64_t hidden, void* q, int64_t ldq, const pf_kv_view* kv,
+                                        int64_t row_offset, void* workspace, uint64_t workspace_bytes, void* stream) {
+  pf_status st = validate_kv_view(kv, "gemm_qkv_splice");
+  if (st != PF_OK) return st;
+  if (kv->dtype != PF_BF16) return fail(PF_ERR_UNSUPPORTED, "gemm_qkv_splice: bf16 only");
+  if (kv->v_layout != PF_LAYOUT_K8) return fail(PF_ERR_UNSUPPORTED, "gemm_qkv_splice: V must use the K8 layout");
+  if (hidden <= 0 || hidden % 64 != 0) return fail(PF_ERR_UNSUPPORTED, "gemm_qkv_splice: hidden %% 64 != 0");
+  if (kv->row_elems != hidden || kv->k_ld != hidden)
+    return fail(PF_ERR_INVALID_ARG, "gemm_qkv_splice: buffer row_elems and k_ld must equal hidden");
+  if (m < 0 || row_offset < 0 || row_offset + m > kv->rows)
+    return fail(PF_ERR_INVALID_ARG, "gemm_qkv_splice: rows [%lld, %lld) outside the buffer", (long long)row_offset,
+                (long long)(row_offset + m));
+  if (!a || !w || !bias || !q) return fail(PF_ERR_INVALID_ARG, "gemm_qkv_splice: null pointer");
+  if (lda < hidden || lda % 8 != 0 || ldq < hidden || ldq % 4 != 0)
+    return fail(PF_ERR_INVALID_ARG, "gemm_qkv_splice: bad lda or ldq");
+  if (!aligned16(a) || !aligned16(w) || !aligned16(bias) || !aligned16(q) || !aligned16(kv->k) || !aligned16(kv->v))
+    return fail(PF_ERR_INVALID_ARG, "gemm_qkv_splice: pointers must be 16-byte aligned");
+  if (workspace && !aligned16(workspace))
+    return fail(PF_ERR_INVALID_ARG, "gemm_qkv_splice: workspace must be 16-byte aligned");
+  if ((st = check_device()) != PF_OK) return st;
+  const QkvSplice sp{kv->k, kv->v, row_offset, hidden};
+  hipError_t e = launch_gemm(a, lda, w, bias, m, 3 * hidden, hidden, kEpiQkvSplice, q, ldq, nullptr, PF_BF16,
+                             workspace, workspace ? (size_t)workspace_bytes : 0, (hipStream_t)stream, &sp);
+  return e == hipSuccess ? PF_OK : hip_fail(e, "gemm_qkv_splice launch");
+}
+
 extern "C" pf_status pf_gemm_workspace_size(int64_t m, int64_t n, int64_t k, uint64_t* bytes) {
   if (!bytes) return fail(PF_ERR_INVALID_ARG, "gemm_workspace_size: null out");
   if (m < 0 || n <= 0 || k <= 0) return fail(PF_ERR_INVALID_ARG, "gemm_workspace_size: bad sizes");
@@ -520,14 +547,23 @@ static pf_status run_rows(pf_stage* st, int64_t off, int64_t n, float* x, hipStr
     hipError_t e;
     if ((e = launch_ln_modulate(x, n, (int)h, mod, mod + h, eps, st->h1, dt, s)) != hipSuccess)
       return stage_hip_fail(st, e, "ln_modulate");
-    if ((e = launch_gemm(st->h1, h, lm.w_qkv, lm.b_qkv, n, 3 * h, h, kEpiStore, qkv, 3 * h, nullptr, dt, st->gemm_ws,
-                           st->gemm_ws_bytes, s)) !=
-        hipSuccess)
-      return stage_hip_fail(st, e, "qkv gemm");
-    KVDesc dst[2] = {{lm.k, h, kLayoutRows}, {lm.v, h, dt == PF_BF16 ? kLayoutK8 : kLayoutRows}};
-    KVDesc src[2] = {{qkv + h * es, 3 * h, kLayoutRows}, {qkv + 2 * h * es, 3 * h, kLayoutRows}};
-    if ((e = launch_splice(dst, src, h, off, n, (int)es, s)) != hipSuccess) return stage_hip_fail(st, e, "kv splice");
-    if ((e = launch_attention(qkv, 3 * h, lm.k, h, lm.v, h, dst[1].layout, h, st->s_kv, n, st->cfg.heads,
+    const int v_layout = dt == PF_BF16 ? kLayoutK8 : kLayoutRows;
+    if (dt == PF_BF16) {
+      // QKV projection with the splice in its epilogue: Q to the scratch, the patch's fresh K and
+      // V straight into rows [off, off + n) of the layer's buffer (no other row changes)
+      const QkvSplice sp{lm.k, lm.v, off, h};
+      if ((e = launch_gemm(st->h1, h, lm.w_qkv, lm.b_qkv, n, 3 * h, h, kEpiQkvSplice, qkv, 3 * h, nullptr, dt,
+                           st->gemm_ws, st->gemm_ws_bytes, s, &sp)) != hipSuccess)
+        return stage_hip_fail(st, e, "qkv gemm + kv splice");
+    } else {
+      if ((e = launch_gemm(st->h1, h, lm.w_qkv, lm.b_qkv, n, 3 * h, h, kEpiStore, qkv, 3 * h, nullptr, dt,
+                           st->gemm_ws, st->gemm_ws_bytes, s)) != hipSuccess)
+        return stage_hip_fail(st, e, "qkv gemm");
+      KVDesc dst[2] = {{lm.k, h, kLayoutRows}, {lm.v, h, kLayoutRows}};
+      KVDesc src[2] = {{qkv + h * es, 3 * h, kLayoutRows}, {qkv + 2 * h * es, 3 * h, kLayoutRows}};
+      if ((e = launch_splice(dst, src, h, off, n, (int)es, s)) != hipSuccess) return stage_hip_fail(st, e, "kv splice");
+    }
+    if ((e = launch_attention(qkv, 3 * h, lm.k, h, lm.v, h, v_layout, h, st->s_kv, n, st->cfg.heads,
                               st->cfg.head_dim, st->o, h, dt, st->attn_ws, st->attn_ws_bytes, s)) != hipSuccess)
       return stage_hip_fail(st, e, "attention");
     if ((e = launch_gemm(st->o, h, lm.w_o, lm.b_o, n, h, h, kEpiGatedResidual, x, h, mod + 2 * h, dt,

@@ -18,7 +18,7 @@ pytestmark = pytest.mark.gpu
 
 # ------------------------------------------------------------------ LayerNorm + modulation
 
-@pytest.mark.parametrize("rows,hidden", [(1, 128), (77, 1152), (300, 1536), (5, 3072), (64, 4096)])
+@pytest.mark.parametrize("rows,hidden", [(1, 128), (77, 1152), (300, 1536), (5, 3072), (64, 4096), (3, 6144)])
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_ln_modulate(rows, hidden, dtype):
     torch = torch_cuda()
@@ -119,6 +119,38 @@ def test_gemm_bf16_long_k_default_plan():
     rows = np.random.default_rng(seed).choice(m, 64, replace=False)
     want = x0[rows] + gate * ref.linear(a[rows], w, bias)
     assert_close(host(c)[rows], want, "gemm bf16 2048x3072x12288 gated residual, sampled rows")
+
+
+def test_gemm_bf16_split_workspace_reuse():
+    """One workspace serves k-split GEMMs of different shapes in turn (the stage's pattern:
+    QKV, out-projection, QKV again): results match the oracle, and a repeated call reproduces
+    its output bit for bit (slices are summed in a fixed order)."""
+    torch = torch_cuda()
+    shapes = [(1024, 3456, 1152, B.PF_EPI_STORE), (1024, 1152, 1152, B.PF_EPI_GATED_RESIDUAL)]
+    sizes = [B.pf_gemm_workspace_size(m, n, k) for m, n, k, _ in shapes]
+    ws = torch.empty((max(sizes),), dtype=torch.uint8, device="cuda") if max(sizes) else None
+    outs = []
+    for rep, (m, n, k, epi) in enumerate(shapes + shapes[:1]):
+        seed = 900 + m + n + k
+        a = synth.randn((m, k), seed, std=1.0, bf16=True)
+        w = synth.randn((n, k), seed + 1, std=1.0 / math.sqrt(k), bf16=True)
+        bias = synth.randn((n,), seed + 2, std=0.5)
+        if epi == B.PF_EPI_GATED_RESIDUAL:
+            x0 = synth.randn((m, n), seed + 3)
+            gate = synth.randn((n,), seed + 4)
+            c = dev(torch, x0)
+            B.pf_gemm(dev(torch, a, torch.bfloat16), dev(torch, w, torch.bfloat16), dev(torch, bias), epi, c,
+                      gate=dev(torch, gate), workspace=ws)
+            want = x0 + gate * ref.linear(a, w, bias)
+        else:
+            c = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+            B.pf_gemm(dev(torch, a, torch.bfloat16), dev(torch, w, torch.bfloat16), dev(torch, bias), epi, c,
+                      workspace=ws)
+            want = ref.bf16_round(ref.linear(a, w, bias))
+        got = host(c)
+        assert_close(got, want, f"gemm split reuse {m}x{n}x{k} call {rep}")
+        outs.append(got)
+    assert np.array_equal(outs[0], outs[2]), "repeated split GEMM is not bit-identical"
 
 
 def test_gemm_bf16_strided_operands():

@@ -143,3 +143,46 @@ def test_invalid_splice_writes_nothing():
     with pytest.raises(B.PFError):
         B.kvbuf_splice(dst, src, 30, 20)         # past the end
     np.testing.assert_array_equal(_to_host(torch, t, np.uint16), buf)
+
+
+@pytest.mark.parametrize("m,off,split", [(1024, 1024, False), (77, 1003, False), (300, 8, True), (1, 4095, True)],
+                         ids=["patch", "ragged", "ksplit", "one-row-ksplit"])
+def test_fused_qkv_splice_matches_gemm_then_splice(m, off, split):
+    """The stage's QKV projection writes K and V straight into the buffer (pf_gemm_qkv_splice).
+    Its Q and every byte of the buffer must equal the unfused path, pf_gemm(PF_EPI_STORE) then
+    kvbuf_splice of the K and V columns (itself bit-exact against the oracle's slice
+    assignment above): same rows replaced, including partial 8-row groups of the K8 layout,
+    and nothing else touched."""
+    import math
+    from _util import dev
+    torch = torch_cuda()
+    E, R = 1152, 4096
+    seed = 7000 + m + off
+    a = synth.randn((m, E), seed, bf16=True)
+    w = synth.randn((3 * E, E), seed + 1, std=1.0 / math.sqrt(E), bf16=True)
+    bias = synth.randn((3 * E,), seed + 2, std=0.5)
+    k0 = synth.rand_bits16((R, E), seed + 3)
+    v0 = synth.rand_bits16((R * E,), seed + 4)
+    bufs = [(_to_dev(torch, k0, torch.bfloat16), _to_dev(torch, v0, torch.bfloat16)) for _ in range(2)]
+    views = [B.KVView(k=k.data_ptr(), v=v.data_ptr(), rows=R, row_elems=E, k_ld=E, v_ld=E, dtype=B.PF_BF16,
+                      v_layout=B.PF_LAYOUT_K8) for k, v in bufs]
+    ws = B.gemm_workspace(m, 3 * E, E) if split else None
+    if split:
+        assert ws is not None, "shape expected to split k"
+    a_d, w_d, b_d = dev(torch, a, torch.bfloat16), dev(torch, w, torch.bfloat16), dev(torch, bias)
+    print(f"[fused qkv splice] m={m} off={off} split={split}", flush=True)
+    q = torch.empty((m, E), dtype=torch.bfloat16, device="cuda")
+    B.pf_gemm_qkv_splice(a_d, w_d, b_d, q, views[0], off, workspace=ws)
+    qkv = torch.empty((m, 3 * E), dtype=torch.bfloat16, device="cuda")
+    B.pf_gemm(a_d, w_d, b_d, B.PF_EPI_STORE, qkv, workspace=ws)
+    src = B.KVView(k=qkv.data_ptr() + E * 2, v=qkv.data_ptr() + 2 * E * 2, rows=m, row_elems=E, k_ld=3 * E,
+                   v_ld=3 * E, dtype=B.PF_BF16, v_layout=B.PF_LAYOUT_ROWS)
+    B.kvbuf_splice(views[1], src, off, m)
+    torch.cuda.synchronize()
+    assert torch.equal(q.view(torch.int16), qkv[:, :E].contiguous().view(torch.int16)), "Q differs"
+    for i, name in ((0, "K"), (1, "V")):
+        got, want = bufs[0][i].view(torch.int16), bufs[1][i].view(torch.int16)
+        assert torch.equal(got, want), f"{name} buffer differs from gemm + kvbuf_splice"
+    # rows outside the patch keep their old bits (the unfused path is checked against the oracle above)
+    k_after = _to_host(torch, bufs[0][0], np.uint16)
+    assert np.array_equal(k_after[:off], k0[:off]) and np.array_equal(k_after[off + m:], k0[off + m:])

@@ -118,10 +118,13 @@ def test_property_a_single_patch_overwrites_stale_context():
 def test_property_a_no_drift_full_size(shape):
     """At full size and in the benchmark's launch configuration: with no drift between steps
     (fresh == stale) a patched step reproduces the warm-up (unpartitioned) step.  The first
-    layer's K/V buffers are identical bit for bit (same inputs, same per-row arithmetic).  The
-    outputs agree up to fp32 summation order: a patch's attention splits the key range across
-    workgroups and merges the partials while the warm-up pass does not, and later bf16
-    rounding points turn those last-bit differences into occasional one-ulp flips."""
+    layer's K/V buffers see the same inputs; they agree to within one bf16 ulp per element
+    (plus a tiny absolute floor for sums that cancel), since a patch-sized QKV projection may
+    split its k range across workgroups (fp32 partial sums added in another order) while the
+    warm-up pass does not.  The outputs agree up to
+    fp32 summation order too: a patch's attention also splits the key range and merges the
+    partials, and later bf16 rounding points turn last-bit differences into occasional
+    one-ulp flips."""
     torch = torch_cuda()
     shape = dataclasses.replace(shape, num_layers=min(shape.num_layers, 2))
     inputs = synth.stage_inputs(shape)
@@ -135,7 +138,17 @@ def test_property_a_no_drift_full_size(shape):
         st.run_step(x, c, warmup=False, out=out)
         torch.cuda.synchronize()
         k1, v1 = st.kv_raw(0)
-        assert torch.equal(k0, k1) and torch.equal(v0, v1)
+        for name, a, b in (("K", k0, k1), ("V", v0, v1)):
+            a, b = a.float(), b.float()
+            # one bf16 ulp of either value, plus an absolute floor for results that cancel to
+            # near zero, where a reordered fp32 sum (|error| ~ 1e-7 of the summed magnitudes)
+            # exceeds the ulp of the result itself
+            tol = torch.maximum(a.abs(), b.abs()) * 2.0 ** -7 + 2.0 ** -19
+            d = (a - b).abs()
+            bad = d > tol
+            assert not bool(bad.any()), (f"layer-0 {name}: {int(bad.sum())} elements beyond one bf16 ulp, "
+                                         f"max |diff| {float(d.max()):.3g} at |value| "
+                                         f"{float(a.flatten()[int(d.argmax())].abs()):.3g}")
         assert bool(torch.isfinite(out).all())
         # rel-L2 is the contract tolerance; max-abs only bounds gross errors here, because at
         # h = 3072 the large adaLN gates turn one-ulp bf16 flips into ~0.1 single-element moves

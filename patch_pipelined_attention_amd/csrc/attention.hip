@@ -446,7 +446,9 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const bf16* __restric
 // Merge the per-split partial results.  Slice s holds x_s = acc_s / l_s (bf16) with its
 // reference max m_s and weight sum l_s, so O = sum_s w_s x_s / sum_s w_s with
 // w_s = 2^(m_s - M) l_s (M = max_s m_s): a convex combination of the slices' results.
-// One thread per (row, head, 8 columns).
+// One thread per (row, head, 8 columns).  The loop over slices is unrolled to the largest
+// split count (indices past n_split clamped, their terms skipped), so every load of a thread
+// is issued before the first is used.
 template <int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const bf16* __restrict__ part_o,
                                                            const float* __restrict__ part_ml, int n_split,
@@ -460,19 +462,29 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const bf16* __restric
   const int head = (int)(rest % H);
   const int64_t row = rest / H;
   const int64_t hidden = (int64_t)H * D;
-  float M = -INFINITY;
-  for (int sp = 0; sp < n_split; ++sp) M = fmaxf(M, part_ml[(((int64_t)sp * 2) * H + head) * rows + row]);
+  float m[kMaxAttnSplit], l[kMaxAttnSplit];
+  bf16x8 x[kMaxAttnSplit];
+#pragma unroll
+  for (int sp = 0; sp < kMaxAttnSplit; ++sp) {
+    const int64_t sc = sp < n_split ? sp : n_split - 1;   // slices past n_split re-read the last (unused)
+    m[sp] = part_ml[((sc * 2) * H + head) * rows + row];
+    l[sp] = part_ml[((sc * 2 + 1) * H + head) * rows + row];
+    x[sp] = *reinterpret_cast<const bf16x8*>(part_o + (sc * rows + row) * hidden + (int64_t)head * D + chunk * 8);
+  }
+  float M = m[0];
+#pragma unroll
+  for (int sp = 1; sp < kMaxAttnSplit; ++sp)
+    if (sp < n_split) M = fmaxf(M, m[sp]);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
-  for (int sp = 0; sp < n_split; ++sp) {
-    const float m = part_ml[(((int64_t)sp * 2) * H + head) * rows + row];
-    const float l = part_ml[(((int64_t)sp * 2 + 1) * H + head) * rows + row];
-    const float w = __builtin_amdgcn_exp2f(m - M) * l;
-    wsum += w;
-    const bf16x8 x = *reinterpret_cast<const bf16x8*>(part_o + ((int64_t)sp * rows + row) * hidden +
-                                                      (int64_t)head * D + chunk * 8);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, (float)x[e], acc[e]);
+  for (int sp = 0; sp < kMaxAttnSplit; ++sp) {
+    if (sp < n_split) {
+      const float w = __builtin_amdgcn_exp2f(m[sp] - M) * l[sp];
+      wsum += w;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, (float)x[sp][e], acc[e]);
+    }
   }
   const float inv = 1.0f / wsum;
   bf16x8 out;

@@ -7,9 +7,8 @@
 // per lane, one token and 4 consecutive output features per 8-row group, so every
 // epilogue stores 4 contiguous values per access (8 B bf16 / 16 B fp32).
 //
-// Tiles: 128 x 128 (two workgroups per CU) by default; 256 x 256 (one per CU, each wavefront
-// 128 x 128 = 4 x 4 MFMA blocks, 0.5 KB of LDS operand reads per MFMA) for long reductions
-// (k >= 8192), where its higher per-k rate outweighs its fixed cost per tile.  Grids too
+// Tiles: 128 x 128 with a 2-stage ring, two workgroups per CU.  Two deep-ring variants (256 x
+// 256 and 128 x 128, one workgroup per CU) can be forced for comparison.  Grids too
 // small to fill the GPU split k: every slice writes its fp32 partial tile and a reduce pass
 // sums the slices in order (deterministic) and applies the epilogue.  (A last-arriving-slice
 // merge inside the GEMM measured slower on MI355X: the partials cross XCDs, whose L2s are
@@ -290,32 +289,41 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
   gemm_epilogue<BF, BT, FB, TB, EPI, SPLIT>(acc, m0, n0, M, N, bias, C, ldc, gate, sp, split, part);
 }
 
-// bf16 big-tile kernel: 256 features x 256 tokens per workgroup, 4 wavefronts in a 2 x 2
-// grid, each 128 x 128 = 4 x 4 blocks of 32 x 32 (256 fp32 accumulators per lane, which
-// the compiler keeps in the accumulation registers).  Per MFMA a wavefront reads 0.5 KB of
-// operands from LDS, half the 128 x 128 tile's share.  k is staged 32 at a time (two MFMA
-// k-steps) in a 4-stage ring filled three tiles ahead by direct global -> LDS loads; the
-// loads are counted with explicit vmcnt waits so they stay in flight across barriers.  The
-// first operands of tile kt+1 are read right after the barrier that publishes it, while the
-// MFMAs of tile kt's last k-step are still running.  One workgroup per CU.
-template <int EPI, bool SPLIT>
-__global__ __launch_bounds__(256, 1) void gemm_big_kernel(const bf16* __restrict__ A, int64_t lda,
-                                                          const bf16* __restrict__ W, const float* __restrict__ bias,
-                                                          int64_t M, int64_t N, int64_t K, void* __restrict__ C,
-                                                          int64_t ldc, const float* __restrict__ gate, int tiles_n,
-                                                          int n_split, int ktiles_per_split,
-                                                          float* __restrict__ part, QkvSplice sp) {
-  constexpr int BF = 256, BT = 256;
+// vmcnt-only wait: at most N vector memory operations of this wavefront still outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// bf16 deep-ring kernel: BF features x BT tokens per workgroup, 4 wavefronts in a 2 x 2 grid,
+// each (BF/2) x (BT/2) = FB x TB blocks of 32 x 32.  k is staged 32 at a time (two MFMA
+// k-steps) in an NSTAGE ring filled NSTAGE - 1 tiles ahead by direct global -> LDS loads;
+// the loads are counted with explicit vmcnt waits so they stay in flight across barriers.
+// The first operands of tile kt+1 are read right after the barrier that publishes it, while
+// the MFMAs of tile kt's last k-step are still running.  One workgroup per CU.
+//   256 x 256, 4 stages: each wavefront 128 x 128 = 4 x 4 blocks (256 fp32 accumulators per
+//     lane, kept in the accumulation registers), 0.5 KB of LDS operand reads per MFMA: the
+//     highest per-k rate, for long reductions.
+//   128 x 128, 8 stages: seven tiles (224 k values) in flight hide the load latency that
+//     bounds a lone 2-stage workgroup, for grids with about one tile per CU.
+template <int BF, int BT, int NSTAGE, int EPI, bool SPLIT>
+__global__ __launch_bounds__(256, 1) void gemm_deep_kernel(const bf16* __restrict__ A, int64_t lda,
+                                                           const bf16* __restrict__ W, const float* __restrict__ bias,
+                                                           int64_t M, int64_t N, int64_t K, void* __restrict__ C,
+                                                           int64_t ldc, const float* __restrict__ gate, int tiles_n,
+                                                           int n_split, int ktiles_per_split,
+                                                           float* __restrict__ part, QkvSplice sp) {
   constexpr int BK = 32;                 // k per stage: two MFMA k-steps
   constexpr int KSTEPS = BK / 16;
   constexpr int ROWS = BF + BT;          // stage rows: W rows, then X rows
   constexpr int UPR = BK / 8;            // 16-byte units per row (4)
-  constexpr int UNITS = ROWS * UPR;      // 2048 units = 32 KB per stage
-  constexpr int NINST = UNITS / 64;      // 64-lane direct loads per stage (32)
-  constexpr int NPW = NINST / 4;         // per wavefront (8)
-  constexpr int NSTAGE = 4;
-  constexpr int FB = 4, TB = 4;
-  static_assert(NPW % 2 == 0, "W and X loads split evenly");
+  constexpr int UNITS = ROWS * UPR;      // 16-byte units per stage
+  constexpr int NINST = UNITS / 64;      // 64-lane direct loads per stage
+  constexpr int NPW = NINST / 4;         // per wavefront
+  constexpr int FB = BF / 64, TB = BT / 64;
+  static_assert(BF == BT && NPW % 2 == 0, "W and X loads split evenly");
+  static_assert(NSTAGE >= 3 && NSTAGE <= 9 && (NSTAGE - 2) * NPW < 64, "stage ring");
   __shared__ __attribute__((aligned(16))) uint4 lds[NSTAGE][UNITS];
 
   const int tid = threadIdx.x;
@@ -367,11 +375,16 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(const bf16* __restrict
       dma_load16(j < NPW / 2 ? wb : xb, off[j], &lds[st][(wave + 4 * j) * 64]);
   };
   // this wavefront's loads of the tile before the `newer` most recently issued tiles are done
+  // (newer <= NSTAGE - 2: at most that many later tiles are ever in flight)
   auto wait_tiles = [&](int newer) {
-    if (newer >= 3) __builtin_amdgcn_s_waitcnt(((3 * NPW) & 15) | (((3 * NPW) >> 4) << 14) | (7 << 4) | (15 << 8));
-    else if (newer == 2) __builtin_amdgcn_s_waitcnt(((2 * NPW) & 15) | (((2 * NPW) >> 4) << 14) | (7 << 4) | (15 << 8));
-    else if (newer == 1) __builtin_amdgcn_s_waitcnt((NPW & 15) | ((NPW >> 4) << 14) | (7 << 4) | (15 << 8));
-    else __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+    if constexpr (NSTAGE - 2 >= 7) { if (newer >= 7) { wait_vmcnt<(NSTAGE - 2 >= 7 ? 7 : 0) * NPW>(); return; } }
+    if constexpr (NSTAGE - 2 >= 6) { if (newer == 6) { wait_vmcnt<(NSTAGE - 2 >= 6 ? 6 : 0) * NPW>(); return; } }
+    if constexpr (NSTAGE - 2 >= 5) { if (newer == 5) { wait_vmcnt<(NSTAGE - 2 >= 5 ? 5 : 0) * NPW>(); return; } }
+    if constexpr (NSTAGE - 2 >= 4) { if (newer == 4) { wait_vmcnt<(NSTAGE - 2 >= 4 ? 4 : 0) * NPW>(); return; } }
+    if constexpr (NSTAGE - 2 >= 3) { if (newer == 3) { wait_vmcnt<(NSTAGE - 2 >= 3 ? 3 : 0) * NPW>(); return; } }
+    if (newer == 2) { wait_vmcnt<2 * NPW>(); return; }
+    if (newer == 1) { wait_vmcnt<NPW>(); return; }
+    wait_vmcnt<0>();
   };
 
   f32x16 acc[FB][TB];
@@ -501,9 +514,10 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
   }
 }
 
-// Launch plan of a bf16 GEMM: tile size and k-split count.
+// Launch plan of a bf16 GEMM: kernel and k-split count.
+enum GemmKind { kGemm128 = 0, kGemmDeep256 = 1, kGemmDeep128 = 2 };
 struct GemmPlan {
-  int big;      // 1: 256 x 256 tiles (1 workgroup per CU), 0: 128 x 128 tiles (2 per CU)
+  int kind;     // GemmKind: 128 x 128 2-stage (2 per CU), 256 x 256 4-stage, 128 x 128 8-stage (1 per CU)
   int split;    // k slices (1 = no split)
 };
 
@@ -521,37 +535,38 @@ static int gemm_cus() {
   return cus;
 }
 
-// Big tiles pay off only for long reductions: their per-k rate is about twice a 128 x 128
-// slot's, but each tile carries a large fixed cost (measured on MI355X at the DiT projection
-// shapes: faster for k = 12288, slower for every k <= 4608).
-constexpr int64_t kBigTileMinK = 8192;
-
+// The estimate only considers the 2-stage 128 x 128 kernel: with the grouped tile order it
+// measured faster than both deep-ring kernels at every DiT projection shape on MI355X (k from
+// 1152 to 12288, m from 1024 to 16384); the deep-ring kernels stay selectable for
+// experiments and tests through PF_GEMM_TILE.
 // Smallest estimated time over tile size x k-split: rounds of resident workgroups x one
 // slice's time (a fixed cost plus its FLOPs at the tile's measured rate), plus writing and
 // re-reading the fp32 partials of a split.
-// The environment variable PF_GEMM_TILE=128 or 256 forces the tile size (the k-split is still
-// chosen by the estimate); any other value, or none, leaves both to the estimate.
-static int gemm_tile_override() {
+// The environment variable PF_GEMM_TILE=128, 256 or 128d (the 8-stage 128 x 128 kernel) forces
+// the kernel (the k-split is still chosen by the estimate); any other value, or none, leaves
+// both to the estimate.
+static int gemm_kind_override() {
   const char* v = std::getenv("PF_GEMM_TILE");
-  if (!v) return 0;
-  if (std::strcmp(v, "128") == 0) return 128;
-  if (std::strcmp(v, "256") == 0) return 256;
-  return 0;
+  if (!v) return -1;
+  if (std::strcmp(v, "128") == 0) return kGemm128;
+  if (std::strcmp(v, "256") == 0) return kGemmDeep256;
+  if (std::strcmp(v, "128d") == 0) return kGemmDeep128;
+  return -1;
 }
 
 static GemmPlan gemm_plan(int64_t m, int64_t n, int64_t k, size_t ws_bytes) {
   const int cus = gemm_cus();
-  const int force = gemm_tile_override();
-  GemmPlan best_plan{force == 256 ? 1 : 0, 1};
+  const int force = gemm_kind_override();
+  GemmPlan best_plan{force >= 0 ? force : kGemm128, 1};
   double best = 1e30;
-  for (int big = 0; big <= 1; ++big) {
-    if (force ? (big != (force == 256)) : (big && k < kBigTileMinK)) continue;
-    const int64_t bt = big ? 256 : 128;
-    const int64_t bk = big ? 32 : 64;
+  for (int kind = 0; kind <= 2; ++kind) {
+    if (force >= 0 ? kind != force : kind != kGemm128) continue;
+    const int64_t bt = kind == kGemmDeep256 ? 256 : 128;
+    const int64_t bk = kind == kGemm128 ? 64 : 32;
     const int64_t tiles = ((m + bt - 1) / bt) * ((n + bt - 1) / bt);
-    const int64_t slots = big ? (int64_t)cus : 2 * (int64_t)cus;
-    const double fixed_s = big ? 30e-6 : 3e-6;
-    const double rate = big ? 6.7e12 : 1.65e12;      // FLOP/s of one resident workgroup
+    const int64_t slots = kind == kGemm128 ? 2 * (int64_t)cus : (int64_t)cus;
+    const double fixed_s = kind == kGemmDeep256 ? 30e-6 : 3e-6;
+    const double rate = kind == kGemmDeep256 ? 6.7e12 : 1.65e12;      // FLOP/s of one resident workgroup
     for (int sp = 1; sp <= kMaxGemmSplit; ++sp) {
       if (sp > 1 && k / bk < 4LL * sp) break;
       if (sp > 1 && (size_t)sp * m * n * sizeof(float) > ws_bytes) break;
@@ -559,7 +574,7 @@ static GemmPlan gemm_plan(int64_t m, int64_t n, int64_t k, size_t ws_bytes) {
                        (sp > 1 ? 2.0 * sp * (double)m * (double)n * sizeof(float) / 5.0e12 : 0.0);
       if (t < best * 0.98) {
         best = t;
-        best_plan = {big, sp};
+        best_plan = {kind, sp};
       }
     }
   }
@@ -571,6 +586,13 @@ size_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k) {
   return p.split > 1 ? (size_t)p.split * m * n * sizeof(float) : 0;
 }
 
+template <int EPI, bool SPLIT>
+static constexpr auto gemm_small128 = gemm_bf16_kernel<128, 128, EPI, SPLIT>;
+template <int EPI, bool SPLIT>
+static constexpr auto gemm_deep256 = gemm_deep_kernel<256, 256, 4, EPI, SPLIT>;
+template <int EPI, bool SPLIT>
+static constexpr auto gemm_deep128 = gemm_deep_kernel<128, 128, 8, EPI, SPLIT>;
+
 template <int EPI>
 static void launch_gemm_epi(const void* a, int64_t lda, const void* w, const float* bias, int64_t m, int64_t n,
                             int64_t k, void* c, int64_t ldc, const float* gate, int dtype, void* ws,
@@ -579,29 +601,27 @@ static void launch_gemm_epi(const void* a, int64_t lda, const void* w, const flo
     const bf16* A = static_cast<const bf16*>(a);
     const bf16* Wt = static_cast<const bf16*>(w);
     const GemmPlan p = gemm_plan(m, n, k, ws ? ws_bytes : 0);
-    const int bt = p.big ? 256 : 128;
-    const int nkt = (int)(k / (p.big ? 32 : 64));
+    const int bt = p.kind == kGemmDeep256 ? 256 : 128;
+    const int nkt = (int)(k / (p.kind == kGemm128 ? 64 : 32));
     const int tiles_n = (int)((n + bt - 1) / bt);
     const int64_t tiles = (int64_t)tiles_n * ((m + bt - 1) / bt);
     const int kps = (nkt + p.split - 1) / p.split;
     const int used = (nkt + kps - 1) / kps;          // every slice gets at least one k tile
     float* part = static_cast<float*>(ws);
     const dim3 grid((unsigned)(tiles * used));
-    if (p.big) {
-      if (used == 1)
-        hipLaunchKernelGGL((gemm_big_kernel<EPI, false>), grid, dim3(256), 0, s, A, lda, Wt, bias, m, n, k, c, ldc,
-                           gate, tiles_n, 1, nkt, nullptr, sp);
-      else
-        hipLaunchKernelGGL((gemm_big_kernel<EPI, true>), grid, dim3(256), 0, s, A, lda, Wt, bias, m, n, k, c, ldc,
-                           gate, tiles_n, used, kps, part, sp);
-    } else {
-      if (used == 1)
-        hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, EPI, false>), grid, dim3(256), 0, s, A, lda, Wt, bias, m, n, k,
-                           c, ldc, gate, tiles_n, 1, nkt, nullptr, sp);
-      else
-        hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, EPI, true>), grid, dim3(256), 0, s, A, lda, Wt, bias, m, n, k,
-                           c, ldc, gate, tiles_n, used, kps, part, sp);
-    }
+#define PF_GEMM_LAUNCH(KERNEL)                                                                                       \
+  do {                                                                                                               \
+    if (used == 1)                                                                                                   \
+      hipLaunchKernelGGL((KERNEL<EPI, false>), grid, dim3(256), 0, s, A, lda, Wt, bias, m, n, k, c, ldc, gate, tiles_n, \
+                         1, nkt, nullptr, sp);                                                                       \
+    else                                                                                                             \
+      hipLaunchKernelGGL((KERNEL<EPI, true>), grid, dim3(256), 0, s, A, lda, Wt, bias, m, n, k, c, ldc, gate, tiles_n, \
+                         used, kps, part, sp);                                                                       \
+  } while (0)
+    if (p.kind == kGemmDeep256) PF_GEMM_LAUNCH(gemm_deep256);
+    else if (p.kind == kGemmDeep128) PF_GEMM_LAUNCH(gemm_deep128);
+    else PF_GEMM_LAUNCH(gemm_small128);
+#undef PF_GEMM_LAUNCH
     if (used > 1) {
       const int64_t units = m * (n / 4);
       hipLaunchKernelGGL(gemm_reduce_kernel<EPI>, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, s, part, used,

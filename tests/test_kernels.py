@@ -70,14 +70,16 @@ def test_gemm_bf16(m, n, k, epi, split):
     assert_close(host(c), want, f"gemm bf16 {m}x{n}x{k} epi={epi}")
 
 
+@pytest.mark.parametrize("kernel", ["256", "128d"], ids=["deep256", "deep128"])
 @pytest.mark.parametrize("split", [False, True], ids=["whole", "ksplit"])
 @pytest.mark.parametrize("m,n,k", [(77, 192, 128), (300, 1344, 1152), (257, 640, 4608)])
 @pytest.mark.parametrize("epi", [B.PF_EPI_STORE, B.PF_EPI_GELU_TANH, B.PF_EPI_GATED_RESIDUAL])
-def test_gemm_bf16_big_tiles(m, n, k, epi, split, monkeypatch):
-    """256 x 256 tiles forced through PF_GEMM_TILE: ragged m and n (partial tiles in both),
-    k from a single 32-deep stage group to a long ring, with and without the k split."""
+def test_gemm_bf16_deep_ring(m, n, k, epi, split, kernel, monkeypatch):
+    """The deep-ring kernels forced through PF_GEMM_TILE (256 x 256 with 4 stages, 128 x 128
+    with 8): ragged m and n (partial tiles in both), k from fewer tiles than the ring holds to
+    a long ring, with and without the k split."""
     torch = torch_cuda()
-    monkeypatch.setenv("PF_GEMM_TILE", "256")
+    monkeypatch.setenv("PF_GEMM_TILE", kernel)
     ws = B.gemm_workspace(m, n, k) if split else None
     seed = m * 5 + n * 3 + k + epi
     a = synth.randn((m, k), seed, std=1.0, bf16=True)
@@ -97,12 +99,12 @@ def test_gemm_bf16_big_tiles(m, n, k, epi, split, monkeypatch):
                   workspace=ws)
         act = {B.PF_EPI_STORE: lambda v: v, B.PF_EPI_GELU_TANH: ref.gelu_tanh}[epi]
         want = ref.bf16_round(act(y))
-    assert_close(host(c), want, f"gemm bf16 big tiles {m}x{n}x{k} epi={epi}")
+    assert_close(host(c), want, f"gemm bf16 deep ring {kernel} {m}x{n}x{k} epi={epi}")
 
 
 def test_gemm_bf16_long_k_default_plan():
     """The Flux-shaped MLP down projection (2048 x 3072 x 12288, gated residual) with the
-    workspace the stage gives it: the default plan takes the 256 x 256 tiles and splits k.
+    workspace the stage gives it (the default plan: 128 x 128 tiles, a 192-step k loop).
     Checked on 64 sampled rows (the full fp64 product is too slow for the oracle)."""
     torch = torch_cuda()
     m, n, k = 2048, 3072, 12288

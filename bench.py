@@ -34,6 +34,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", default="c2")
+    ap.add_argument("--batch", type=int, default=1,
+                    help="samples per stage sharing the weights (2 = a classifier-free guidance pair)")
     ap.add_argument("--breakdown", action="store_true", help="also time every kernel of a patch-layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
@@ -135,44 +137,49 @@ def time_kernel_graph(torch, fn, iters=20, reps=5):
     return s.elapsed_time(e) / 1e3 / (reps * iters)
 
 
-def kernel_probes(torch, B, st, shape, layer_w):
-    """Component launches at the exact shapes one patch-layer of the stage issues."""
+def kernel_probes(torch, B, st, shape, layer_w, nb=1):
+    """Component launches at the exact shapes one patch-layer of the stage issues: the row
+    kernels and projections over the nb * P rows of all samples, the attention per sample
+    (P query rows over that sample's buffer; the stage launches it nb times)."""
     h, P, S, r = shape.hidden, shape.patch_rows, shape.seq_kv, shape.mlp_ratio
+    R = nb * P
     bf = torch.bfloat16
     dev = "cuda"
-    x = torch.randn((P, h), device=dev)
+    x = torch.randn((R, h), device=dev)
     shift = torch.zeros(h, device=dev)
     scale = torch.zeros(h, device=dev)
-    h1 = torch.empty((P, h), dtype=bf, device=dev)
-    qkv = torch.randn((P, 3 * h), device=dev).to(bf)
-    o = torch.empty((P, h), dtype=bf, device=dev)
-    u = torch.empty((P, r * h), dtype=bf, device=dev)
+    h1 = torch.empty((R, h), dtype=bf, device=dev)
+    qkv = torch.randn((R, 3 * h), device=dev).to(bf)
+    o = torch.empty((R, h), dtype=bf, device=dev)
+    u = torch.empty((R, r * h), dtype=bf, device=dev)
     kv = st.kv_view(0)
     gate = torch.zeros(h, device=dev)
     qkv_src = B.KVView(k=qkv.data_ptr() + h * 2, v=qkv.data_ptr() + 2 * h * 2, rows=P, row_elems=h, k_ld=3 * h,
                        v_ld=3 * h, dtype=B.PF_BF16, v_layout=B.PF_LAYOUT_ROWS)
     off = shape.patch_offsets()[-1]
+    off_all = min(off, S - R)      # the QKV probe writes all R rows into one buffer
     ws = B.attention_workspace(P, shape.heads, shape.head_dim)   # same split choices as the stage
-    gws = {k: B.gemm_workspace(P, n, kk) for k, (n, kk) in
+    gws = {k: B.gemm_workspace(R, n, kk) for k, (n, kk) in
            {"qkv": (3 * h, h), "out": (h, h), "up": (r * h, h), "down": (h, r * h)}.items() if n > 0}
     w = layer_w
     probes = {
-        "ln_modulate": (lambda: B.pf_ln_modulate(x, shift, scale, 1e-6, h1), 12.0 * P * h, "hbm"),
+        "ln_modulate": (lambda: B.pf_ln_modulate(x, shift, scale, 1e-6, h1), 12.0 * R * h, "hbm"),
         # the stage's QKV projection: Q to the scratch, K and V into the layer's buffer rows
-        "gemm_qkv_splice": (lambda: B.pf_gemm_qkv_splice(h1, w["w_qkv"], w["b_qkv"], qkv, kv, off, ldq=3 * h,
-                                                         workspace=gws["qkv"]), 6.0 * P * h * h, "mfma"),
+        "gemm_qkv_splice": (lambda: B.pf_gemm_qkv_splice(h1, w["w_qkv"], w["b_qkv"], qkv, kv, off_all, ldq=3 * h,
+                                                         workspace=gws["qkv"]), 6.0 * R * h * h, "mfma"),
         # the standalone splice entry point (the harness's buffer updates; the stage fuses it above)
         "kv_splice_entry": (lambda: B.kvbuf_splice(kv, qkv_src, off, P), 8.0 * P * h, "hbm"),
-        "attention": (lambda: B.pf_attention(qkv, kv, S, P, shape.heads, shape.head_dim, o, workspace=ws),
+        "attention": (lambda: B.pf_attention(qkv, kv, S, P, shape.heads, shape.head_dim, o, ldq=3 * h,
+                                             workspace=ws),
                       4.0 * P * S * h, "mfma"),
         "gemm_out": (lambda: B.pf_gemm(o, w["w_o"], w["b_o"], B.PF_EPI_GATED_RESIDUAL, x, gate=gate,
-                                       workspace=gws["out"]), 2.0 * P * h * h, "mfma"),
+                                       workspace=gws["out"]), 2.0 * R * h * h, "mfma"),
     }
     if r > 0:
         probes["gemm_up_gelu"] = (lambda: B.pf_gemm(h1, w["w1"], w["b1"], B.PF_EPI_GELU_TANH, u,
-                                                    workspace=gws["up"]), 2.0 * r * P * h * h, "mfma")
+                                                    workspace=gws["up"]), 2.0 * r * R * h * h, "mfma")
         probes["gemm_down"] = (lambda: B.pf_gemm(u, w["w2"], w["b2"], B.PF_EPI_GATED_RESIDUAL, x, gate=gate,
-                                                 workspace=gws["down"]), 2.0 * r * P * h * h, "mfma")
+                                                 workspace=gws["down"]), 2.0 * r * R * h * h, "mfma")
     return probes
 
 
@@ -269,10 +276,15 @@ def main():
     torch.cuda.set_device(0)
     print(f"[bench] {shape.name}: generating inputs", file=sys.stderr, flush=True)
     inputs = synth.stage_inputs(shape)
-    st = Stage(shape)
+    nb = args.batch
+    st = Stage(shape, batch=nb)
     st.load(inputs.layers)
-    x = torch.from_numpy(inputs.x).cuda()
-    c = torch.from_numpy(inputs.c).cuda()
+    if nb == 1:
+        x = torch.from_numpy(inputs.x).cuda()
+        c = torch.from_numpy(inputs.c).cuda()
+    else:   # every sample shares the latent rows; each has its own condition
+        x = torch.from_numpy(np.stack([inputs.x] * nb)).cuda()
+        c = torch.from_numpy(synth.batch_conds(shape, inputs.c, nb)).cuda()
     out = torch.empty_like(x)
 
     # warm-up step (fills every buffer fresh), then untimed patched steps
@@ -305,7 +317,7 @@ def main():
     # dominant kernel: patch attention at the stage's launch shape
     wdev = {k: torch.from_numpy(np.ascontiguousarray(a)).cuda().to(torch.bfloat16 if k.startswith("w") else torch.float32)
             for k, a in inputs.layers[0].items()}
-    probes = kernel_probes(torch, B, st, shape, wdev)
+    probes = kernel_probes(torch, B, st, shape, wdev, nb)
     attn_fn, attn_flop, _ = probes["attention"]
     attn_s = time_kernel(torch, attn_fn, iters=max(10, args.steps))
     attn_tflops = attn_flop / attn_s / 1e12
@@ -326,7 +338,12 @@ def main():
                 breakdown[name] = {"us": t * 1e6, "gbs": work / t / 1e9, "frac_peak": work / t / 1e9 / PEAK_HBM_GBS,
                                    "timing": how, "note": "cache-resident inputs across launches"}
 
-    tokens = shape.seq_kv
+    tokens = nb * shape.seq_kv
+    workload = (f"{shape.name}: one pipeline stage, {shape.num_layers} DiT blocks, hidden {shape.hidden}, "
+                f"{shape.heads}x{shape.head_dim} heads, MLP {shape.mlp_ratio}x, {shape.seq_kv} buffer rows, "
+                f"M={shape.num_patches} patches of {shape.patch_rows}")
+    if nb > 1:
+        workload += f", batch of {nb} samples (classifier-free guidance pair: shared weights, own buffers)"
     rec = {
         "metric": METRIC,
         "value": tokens / med,
@@ -340,14 +357,12 @@ def main():
         "vs_baseline": None,
         "dtype": shape.dtype,
         "data": "synthetic",
-        "config": {"workload": f"{shape.name}: one pipeline stage, {shape.num_layers} DiT blocks, hidden "
-                               f"{shape.hidden}, {shape.heads}x{shape.head_dim} heads, MLP {shape.mlp_ratio}x, "
-                               f"{shape.seq_kv} buffer rows, M={shape.num_patches} patches of {shape.patch_rows}",
+        "config": {"workload": workload, "batch": nb,
                    "num_layers": shape.num_layers, "hidden": shape.hidden, "heads": shape.heads,
                    "head_dim": shape.head_dim, "seq_kv": shape.seq_kv, "num_patches": shape.num_patches,
                    "patch_rows": shape.patch_rows, "parallelism": "single GPU stage"},
-        "stage_tflops": shape.flops_per_step() / med / 1e12,
-        "stage_frac_peak": shape.flops_per_step() / med / 1e12 / PEAK_BF16_TFLOPS,
+        "stage_tflops": nb * shape.flops_per_step() / med / 1e12,
+        "stage_frac_peak": nb * shape.flops_per_step() / med / 1e12 / PEAK_BF16_TFLOPS,
         "attention_tflops": attn_tflops,
         "attention_frac_peak": attn_tflops / PEAK_BF16_TFLOPS,
         "ms_min_step": min(step_s) * 1e3,

@@ -69,6 +69,7 @@ typedef enum pf_epilogue {
 } pf_epilogue;
 
 #define PF_STEP_WARMUP 1u    /* stage_run_step flag: run all buffer rows as one patch */
+#define PF_MAX_STAGE_BATCH 8 /* largest pf_stage_config.batch                          */
 
 typedef struct pf_stage_config {
   int32_t num_layers;   /* L >= 1: contiguous layers owned by this stage                   */
@@ -83,6 +84,9 @@ typedef struct pf_stage_config {
   int32_t gelu;         /* pf_gelu of the MLP                                               */
   float ln_eps;         /* LayerNorm epsilon (1e-6 is the DiT value)                        */
   uint32_t flags;       /* reserved, must be 0                                              */
+  int32_t batch;        /* samples sharing the weights, 0 or 1 = one; 2 = a classifier-free  */
+                        /* guidance pair.  Each sample has its own condition, rows and K/V  */
+                        /* buffers; the projections run once over all samples' rows.       */
 } pf_stage_config;
 
 /* One layer's parameters, all device pointers, weights in the stage dtype, row-major
@@ -114,9 +118,9 @@ typedef struct pf_stage pf_stage;
 
 /* Create a stage on the current HIP device (must be gfx950).  Allocates, once, all
  * device memory the stage uses: the L layers' weights, the L per-layer K/V buffers of
- * seq_txt + seq_img rows (one copy, updated in place: the stage keeps full-spatial K/V
- * for its own layers only, PipeFusion mechanism 4), and scratch for seq_txt + seq_img
- * rows.  bf16 stages keep V in PF_LAYOUT_K8, fp32 stages in PF_LAYOUT_ROWS.  Buffers
+ * seq_txt + seq_img rows per sample (one copy, updated in place: the stage keeps
+ * full-spatial K/V for its own layers only, PipeFusion mechanism 4), and scratch for
+ * seq_txt + seq_img rows of every sample.  bf16 stages keep V in PF_LAYOUT_K8, fp32 stages in PF_LAYOUT_ROWS.  Buffers
  * start zeroed.  Requires h = H * d, d in {64,72,128}, h % 64 == 0 for bf16,
  * seq_img % num_patches == 0.  Errors: INVALID_ARG, UNSUPPORTED, OOM, HIP; nothing is
  * allocated on failure.  *out receives the stage. */
@@ -132,9 +136,9 @@ pf_status stage_destroy(pf_stage* st);
  * run call (else PF_ERR_STATE). */
 pf_status stage_load_weights(pf_stage* st, int32_t layer, const pf_layer_weights* w, void* stream);
 
-/* Compute every layer's adaLN modulation from the conditioning vector `cond` (device,
- * fp32 [h]): mod_l = SiLU(cond) . W_ada,l^T + b_ada,l, kept by the stage for later
- * stage_run_patch calls of this diffusion step. */
+/* Compute every layer's adaLN modulation from the conditioning vectors `cond` (device,
+ * fp32 [batch, h], one per sample): mod_l,b = SiLU(cond_b) . W_ada,l^T + b_ada,l, kept by the
+ * stage for later stage_run_patch calls of this diffusion step. */
 pf_status stage_set_cond(pf_stage* st, const float* cond, void* stream);
 
 /* One micro-step: push buffer rows [row_off, row_off + rows) through all L layers
@@ -144,9 +148,12 @@ pf_status stage_set_cond(pf_stage* st, const float* cond, void* stream);
  * seq_img buffer rows (rows not yet recomputed this step hold stale values from the
  * previous step, mechanism 2), output projection with gated residual, and (r > 0) the
  * modulated GELU MLP with gated residual.
- * x_in / x_out: device fp32 [rows, h] (x_out may equal x_in; otherwise they must not
- * overlap).  Requires 0 <= row_off, rows >= 1, row_off + rows <= seq_txt + seq_img,
- * weights loaded and stage_set_cond called. */
+ * x_in / x_out: device fp32 [batch, rows, h] (x_out may equal x_in; otherwise they must not
+ * overlap).  With batch > 1, every sample's rows go through together: one projection over
+ * batch * rows rows, each sample's own modulation and gates, its fresh K/V spliced into its
+ * own buffers and its queries attending over its own buffer.  Requires 0 <= row_off,
+ * rows >= 1, row_off + rows <= seq_txt + seq_img, weights loaded and stage_set_cond
+ * called. */
 pf_status stage_run_patch(pf_stage* st, int64_t row_off, int64_t rows, const float* x_in,
                           float* x_out, void* stream);
 
@@ -155,7 +162,8 @@ pf_status stage_run_patch(pf_stage* st, int64_t row_off, int64_t rows, const flo
  *                        row is computed fresh, so the pipeline has no stale context yet);
  *   otherwise:           stage_run_patch(0, seq_txt) if seq_txt > 0, then
  *                        stage_run_patch(seq_txt + m*P, P) for m = 0 .. M-1, P = seq_img/M.
- * x_in / x_out: device fp32 [seq_txt + seq_img, h], x_out may equal x_in. */
+ * x_in / x_out: device fp32 [batch, seq_txt + seq_img, h], x_out may equal x_in; cond: fp32
+ * [batch, h]. */
 pf_status stage_run_step(pf_stage* st, const float* x_in, float* x_out, const float* cond,
                          uint32_t flags, void* stream);
 
@@ -169,8 +177,12 @@ pf_status stage_run_step(pf_stage* st, const float* x_in, float* x_out, const fl
 pf_status kvbuf_splice(const pf_kv_view* dst, const pf_kv_view* src, int64_t offset, int64_t len,
                        void* stream);
 
-/* Describe layer `layer`'s K/V buffer (owned by the stage; valid until stage_destroy). */
+/* Describe layer `layer`'s K/V buffer of sample 0 (owned by the stage; valid until
+ * stage_destroy). */
 pf_status stage_get_kvbuf(pf_stage* st, int32_t layer, pf_kv_view* out);
+
+/* The same for sample `sample` (0 <= sample < batch) of a batched stage. */
+pf_status stage_get_kvbuf_sample(pf_stage* st, int32_t layer, int32_t sample, pf_kv_view* out);
 
 /* Thread-local text of the last non-OK status returned on this thread. */
 const char* pf_last_error(void);

@@ -36,7 +36,8 @@ class StageConfig(ctypes.Structure):
     _fields_ = [("num_layers", ctypes.c_int32), ("hidden", ctypes.c_int32), ("heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("mlp_ratio", ctypes.c_int32), ("num_patches", ctypes.c_int32),
                 ("seq_img", ctypes.c_int64), ("seq_txt", ctypes.c_int64), ("dtype", ctypes.c_int32),
-                ("gelu", ctypes.c_int32), ("ln_eps", ctypes.c_float), ("flags", ctypes.c_uint32)]
+                ("gelu", ctypes.c_int32), ("ln_eps", ctypes.c_float), ("flags", ctypes.c_uint32),
+                ("batch", ctypes.c_int32)]
 
 
 class LayerWeights(ctypes.Structure):
@@ -63,6 +64,7 @@ _SIGNATURES = {
     "stage_run_step": [_P, _P, _P, _P, _U32, _P],
     "kvbuf_splice": [ctypes.POINTER(KVView), ctypes.POINTER(KVView), _I64, _I64, _P],
     "stage_get_kvbuf": [_P, _I32, ctypes.POINTER(KVView)],
+    "stage_get_kvbuf_sample": [_P, _I32, _I32, ctypes.POINTER(KVView)],
     "pf_ln_modulate": [_P, _I64, _I32, _P, _P, _F, _P, _I32, _P],
     "pf_gemm": [_P, _I64, _P, _P, _I64, _I64, _I64, _I32, _P, _I64, _P, _I32, _P, ctypes.c_uint64, _P],
     "pf_gemm_qkv_splice": [_P, _I64, _P, _P, _I64, _I64, _P, _I64, ctypes.POINTER(KVView), _I64, _P, ctypes.c_uint64,
@@ -163,9 +165,12 @@ def kvbuf_splice(dst: KVView, src: KVView, offset: int, length: int, stream=None
     _check(lib().kvbuf_splice(ctypes.byref(dst), ctypes.byref(src), offset, length, _stream(stream)))
 
 
-def stage_get_kvbuf(handle, layer: int) -> KVView:
+def stage_get_kvbuf(handle, layer: int, sample: int = 0) -> KVView:
     v = KVView()
-    _check(lib().stage_get_kvbuf(handle, layer, ctypes.byref(v)))
+    if sample == 0:
+        _check(lib().stage_get_kvbuf(handle, layer, ctypes.byref(v)))
+    else:
+        _check(lib().stage_get_kvbuf_sample(handle, layer, sample, ctypes.byref(v)))
     return v
 
 

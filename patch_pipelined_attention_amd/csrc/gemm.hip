@@ -66,18 +66,23 @@ __device__ __forceinline__ void gemm_tile_of(int rest, int tiles_m, int tiles_n,
 }
 
 // Bias, activation and store of 4 consecutive outputs y[m][f..f+3] (f % 4 == 0).
+// Gated residual: row m of sample g = m / rg.rows is row m - g * rg.rows of that sample's
+// block of C, with that sample's gate.  QKV splice: the same row split over sp.grp_rows picks
+// the sample's K / V buffers.
 template <int EPI>
 __device__ __forceinline__ void gemm_store4(float v0, float v1, float v2, float v3, int64_t m, int64_t f,
                                             const float* __restrict__ bias, void* __restrict__ C, int64_t ldc,
-                                            const float* __restrict__ gate, const QkvSplice& sp) {
+                                            const float* __restrict__ gate, const QkvSplice& sp,
+                                            const RowGroups& rg) {
   const float4 bv = *reinterpret_cast<const float4*>(bias + f);
   v0 += bv.x;
   v1 += bv.y;
   v2 += bv.z;
   v3 += bv.w;
   if constexpr (EPI == kEpiGatedResidual) {
-    float* cp = static_cast<float*>(C) + m * ldc + f;
-    const float4 gv = *reinterpret_cast<const float4*>(gate + f);
+    const int64_t g = m / rg.rows;
+    float* cp = static_cast<float*>(C) + g * rg.x_stride + (m - g * rg.rows) * ldc + f;
+    const float4 gv = *reinterpret_cast<const float4*>(gate + g * rg.p_stride + f);
     float4 cv = *reinterpret_cast<float4*>(cp);
     cv.x += gv.x * v0;
     cv.y += gv.y * v1;
@@ -86,14 +91,16 @@ __device__ __forceinline__ void gemm_store4(float v0, float v1, float v2, float 
     *reinterpret_cast<float4*>(cp) = cv;
   } else if constexpr (EPI == kEpiQkvSplice) {
     const bf16x4 o = {(bf16)v0, (bf16)v1, (bf16)v2, (bf16)v3};
+    const int64_t g = m / sp.grp_rows;
+    const int64_t r = sp.row0 + (m - g * sp.grp_rows);      // buffer row of this sample
     if (f < sp.h) {
       *reinterpret_cast<bf16x4*>(static_cast<bf16*>(C) + m * ldc + f) = o;
     } else if (f < 2 * sp.h) {
-      *reinterpret_cast<bf16x4*>(static_cast<bf16*>(sp.k) + (sp.row0 + m) * sp.h + (f - sp.h)) = o;
+      *reinterpret_cast<bf16x4*>(static_cast<bf16*>(sp.k) + g * sp.k_stride + r * sp.h + (f - sp.h)) = o;
     } else {
       // K8: element (r, c) at ((r / 8) * h + c) * 8 + r % 8, so columns c .. c+3 are 8 apart
-      const int64_t r = sp.row0 + m, c = f - 2 * sp.h;
-      bf16* vp = static_cast<bf16*>(sp.v) + ((r >> 3) * sp.h + c) * 8 + (r & 7);
+      const int64_t c = f - 2 * sp.h;
+      bf16* vp = static_cast<bf16*>(sp.v) + g * sp.v_stride + ((r >> 3) * sp.h + c) * 8 + (r & 7);
       vp[0] = o[0];
       vp[8] = o[1];
       vp[16] = o[2];
@@ -112,8 +119,8 @@ __device__ __forceinline__ void gemm_store4(float v0, float v1, float v2, float 
 template <int BF, int BT, int FB, int TB, int EPI, bool SPLIT>
 __device__ __forceinline__ void gemm_epilogue(f32x16 (&acc)[FB][TB], int64_t m0, int64_t n0, int64_t M, int64_t N,
                                               const float* __restrict__ bias, void* __restrict__ C, int64_t ldc,
-                                              const float* __restrict__ gate, const QkvSplice& sp, int split,
-                                              float* __restrict__ part) {
+                                              const float* __restrict__ gate, const QkvSplice& sp,
+                                              const RowGroups& rg, int split, float* __restrict__ part) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
@@ -133,7 +140,7 @@ __device__ __forceinline__ void gemm_epilogue(f32x16 (&acc)[FB][TB], int64_t m0,
               make_float4(acc[i][t][4 * g + 0], acc[i][t][4 * g + 1], acc[i][t][4 * g + 2], acc[i][t][4 * g + 3]);
         else
           gemm_store4<EPI>(acc[i][t][4 * g + 0], acc[i][t][4 * g + 1], acc[i][t][4 * g + 2], acc[i][t][4 * g + 3], m,
-                           f, bias, C, ldc, gate, sp);
+                           f, bias, C, ldc, gate, sp, rg);
       }
   }
 }
@@ -144,7 +151,8 @@ template <int EPI>
 __global__ __launch_bounds__(256) void gemm_reduce_kernel(const float* __restrict__ part, int n_split, int64_t M,
                                                           int64_t N, const float* __restrict__ bias,
                                                           void* __restrict__ C, int64_t ldc,
-                                                          const float* __restrict__ gate, QkvSplice sp) {
+                                                          const float* __restrict__ gate, QkvSplice sp,
+                                                          RowGroups rg) {
   const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t nq = N / 4;
   if (id >= M * nq) return;
@@ -158,7 +166,7 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(const float* __restric
     s.z += v.z;
     s.w += v.w;
   }
-  gemm_store4<EPI>(s.x, s.y, s.z, s.w, m, f, bias, C, ldc, gate, sp);
+  gemm_store4<EPI>(s.x, s.y, s.z, s.w, m, f, bias, C, ldc, gate, sp, rg);
 }
 
 // bf16 tile kernel: BF features x BT tokens per workgroup (4 wavefronts in a 2 x 2 grid, each
@@ -173,7 +181,7 @@ template <int BF, int BT, int EPI, bool SPLIT>
 __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
     const bf16* __restrict__ A, int64_t lda, const bf16* __restrict__ W, const float* __restrict__ bias, int64_t M,
     int64_t N, int64_t K, void* __restrict__ C, int64_t ldc, const float* __restrict__ gate, int tiles_n,
-    int n_split, int ktiles_per_split, float* __restrict__ part, QkvSplice sp) {
+    int n_split, int ktiles_per_split, float* __restrict__ part, QkvSplice sp, RowGroups rg) {
   constexpr int BK = 64;                 // k per stage: four MFMA k-steps
   constexpr int KSTEPS = BK / 16;
   constexpr int ROWS = BF + BT;          // stage rows: W rows, then X rows
@@ -286,7 +294,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
   for (; kt + 1 < kt1; ++kt) ktile(kt, true);
   if (kt < kt1) ktile(kt, false);
 
-  gemm_epilogue<BF, BT, FB, TB, EPI, SPLIT>(acc, m0, n0, M, N, bias, C, ldc, gate, sp, split, part);
+  gemm_epilogue<BF, BT, FB, TB, EPI, SPLIT>(acc, m0, n0, M, N, bias, C, ldc, gate, sp, rg, split, part);
 }
 
 // vmcnt-only wait: at most N vector memory operations of this wavefront still outstanding.
@@ -313,7 +321,7 @@ __global__ __launch_bounds__(256, 1) void gemm_deep_kernel(const bf16* __restric
                                                            int64_t M, int64_t N, int64_t K, void* __restrict__ C,
                                                            int64_t ldc, const float* __restrict__ gate, int tiles_n,
                                                            int n_split, int ktiles_per_split,
-                                                           float* __restrict__ part, QkvSplice sp) {
+                                                           float* __restrict__ part, QkvSplice sp, RowGroups rg) {
   constexpr int BK = 32;                 // k per stage: two MFMA k-steps
   constexpr int KSTEPS = BK / 16;
   constexpr int ROWS = BF + BT;          // stage rows: W rows, then X rows
@@ -455,7 +463,7 @@ __global__ __launch_bounds__(256, 1) void gemm_deep_kernel(const bf16* __restric
   for (; kt + NSTAGE - 1 < kt1; ++kt) ktile(kt, true);
   for (; kt < kt1; ++kt) ktile(kt, false);
 
-  gemm_epilogue<BF, BT, FB, TB, EPI, SPLIT>(acc, m0, n0, M, N, bias, C, ldc, gate, sp, split, part);
+  gemm_epilogue<BF, BT, FB, TB, EPI, SPLIT>(acc, m0, n0, M, N, bias, C, ldc, gate, sp, rg, split, part);
 }
 
 // ---------------------------------------------------------------------------------
@@ -468,7 +476,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
                                                        const float* __restrict__ bias, int64_t M,
                                                        int64_t N, int64_t K, float* __restrict__ C,
                                                        int64_t ldc, const float* __restrict__ gate,
-                                                       int tiles_n) {
+                                                       int tiles_n, RowGroups rg) {
   __shared__ float sA[16][64 + 4];
   __shared__ float sW[16][64 + 4];
   const int tid = threadIdx.x;
@@ -508,8 +516,12 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
       const int64_t n = n0 + tx * 4 + j;
       if (n >= N) continue;
       const float v = acc[i][j] + bias[n];
-      if constexpr (EPI == kEpiGatedResidual) C[m * ldc + n] += gate[n] * v;
-      else C[m * ldc + n] = epi_act<EPI>(v);
+      if constexpr (EPI == kEpiGatedResidual) {
+        const int64_t g = m / rg.rows;
+        C[g * rg.x_stride + (m - g * rg.rows) * ldc + n] += gate[g * rg.p_stride + n] * v;
+      } else {
+        C[m * ldc + n] = epi_act<EPI>(v);
+      }
     }
   }
 }
@@ -596,7 +608,7 @@ static constexpr auto gemm_deep128 = gemm_deep_kernel<128, 128, 8, EPI, SPLIT>;
 template <int EPI>
 static void launch_gemm_epi(const void* a, int64_t lda, const void* w, const float* bias, int64_t m, int64_t n,
                             int64_t k, void* c, int64_t ldc, const float* gate, int dtype, void* ws,
-                            size_t ws_bytes, hipStream_t s, const QkvSplice& sp) {
+                            size_t ws_bytes, hipStream_t s, const QkvSplice& sp, const RowGroups& rg) {
   if (dtype == kDtypeBF16) {
     const bf16* A = static_cast<const bf16*>(a);
     const bf16* Wt = static_cast<const bf16*>(w);
@@ -613,10 +625,10 @@ static void launch_gemm_epi(const void* a, int64_t lda, const void* w, const flo
   do {                                                                                                               \
     if (used == 1)                                                                                                   \
       hipLaunchKernelGGL((KERNEL<EPI, false>), grid, dim3(256), 0, s, A, lda, Wt, bias, m, n, k, c, ldc, gate, tiles_n, \
-                         1, nkt, nullptr, sp);                                                                       \
+                         1, nkt, nullptr, sp, rg);                                                                   \
     else                                                                                                             \
       hipLaunchKernelGGL((KERNEL<EPI, true>), grid, dim3(256), 0, s, A, lda, Wt, bias, m, n, k, c, ldc, gate, tiles_n, \
-                         used, kps, part, sp);                                                                       \
+                         used, kps, part, sp, rg);                                                                   \
   } while (0)
     if (p.kind == kGemmDeep256) PF_GEMM_LAUNCH(gemm_deep256);
     else if (p.kind == kGemmDeep128) PF_GEMM_LAUNCH(gemm_deep128);
@@ -625,30 +637,32 @@ static void launch_gemm_epi(const void* a, int64_t lda, const void* w, const flo
     if (used > 1) {
       const int64_t units = m * (n / 4);
       hipLaunchKernelGGL(gemm_reduce_kernel<EPI>, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, s, part, used,
-                         m, n, bias, c, ldc, gate, sp);
+                         m, n, bias, c, ldc, gate, sp, rg);
     }
   } else {
     const int tiles_n = (int)((n + 63) / 64);
     const int64_t tiles = (int64_t)tiles_n * ((m + 63) / 64);
     hipLaunchKernelGGL(gemm_f32_kernel<EPI>, dim3((unsigned)tiles), dim3(256), 0, s, static_cast<const float*>(a), lda,
-                       static_cast<const float*>(w), bias, m, n, k, static_cast<float*>(c), ldc, gate, tiles_n);
+                       static_cast<const float*>(w), bias, m, n, k, static_cast<float*>(c), ldc, gate, tiles_n, rg);
   }
 }
 
 hipError_t launch_gemm(const void* a, int64_t lda, const void* w, const float* bias, int64_t m, int64_t n, int64_t k,
                        int epi, void* c, int64_t ldc, const float* gate, int dtype, void* ws, size_t ws_bytes,
-                       hipStream_t s, const QkvSplice* splice) {
+                       hipStream_t s, const QkvSplice* splice, const RowGroups* groups) {
   if (m <= 0) return hipSuccess;
-  const QkvSplice sp = splice ? *splice : QkvSplice{nullptr, nullptr, 0, 0};
+  const QkvSplice sp = splice ? *splice : QkvSplice{nullptr, nullptr, 0, 0, m, 0, 0};
+  const RowGroups rg = groups ? *groups : RowGroups{m, 0, 0};
+  if (sp.grp_rows <= 0 || rg.rows <= 0) return hipErrorInvalidValue;
   switch (epi) {
-    case kEpiStore: launch_gemm_epi<kEpiStore>(a, lda, w, bias, m, n, k, c, ldc, gate, dtype, ws, ws_bytes, s, sp); break;
-    case kEpiGeluTanh: launch_gemm_epi<kEpiGeluTanh>(a, lda, w, bias, m, n, k, c, ldc, gate, dtype, ws, ws_bytes, s, sp); break;
-    case kEpiGeluErf: launch_gemm_epi<kEpiGeluErf>(a, lda, w, bias, m, n, k, c, ldc, gate, dtype, ws, ws_bytes, s, sp); break;
+    case kEpiStore: launch_gemm_epi<kEpiStore>(a, lda, w, bias, m, n, k, c, ldc, gate, dtype, ws, ws_bytes, s, sp, rg); break;
+    case kEpiGeluTanh: launch_gemm_epi<kEpiGeluTanh>(a, lda, w, bias, m, n, k, c, ldc, gate, dtype, ws, ws_bytes, s, sp, rg); break;
+    case kEpiGeluErf: launch_gemm_epi<kEpiGeluErf>(a, lda, w, bias, m, n, k, c, ldc, gate, dtype, ws, ws_bytes, s, sp, rg); break;
     case kEpiQkvSplice:
       if (dtype != kDtypeBF16 || !splice) return hipErrorInvalidValue;
-      launch_gemm_epi<kEpiQkvSplice>(a, lda, w, bias, m, n, k, c, ldc, gate, dtype, ws, ws_bytes, s, sp);
+      launch_gemm_epi<kEpiQkvSplice>(a, lda, w, bias, m, n, k, c, ldc, gate, dtype, ws, ws_bytes, s, sp, rg);
       break;
-    default: launch_gemm_epi<kEpiGatedResidual>(a, lda, w, bias, m, n, k, c, ldc, gate, dtype, ws, ws_bytes, s, sp); break;
+    default: launch_gemm_epi<kEpiGatedResidual>(a, lda, w, bias, m, n, k, c, ldc, gate, dtype, ws, ws_bytes, s, sp, rg); break;
   }
   return hipGetLastError();
 }

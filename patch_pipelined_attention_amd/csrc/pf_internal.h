@@ -78,29 +78,50 @@ struct KVDesc {            // one K or V matrix
   int layout;              // kLayoutRows / kLayoutK8
 };
 
-// ---- launchers (each enqueues one kernel on `s` and returns hipGetLastError()) ----
-
-hipError_t launch_ln_modulate(const float* x, int64_t rows, int hidden, const float* shift,
-                              const float* scale, float eps, void* y, int dtype, hipStream_t s);
-
-hipError_t launch_adaln(const float* cond, const void* w, const float* b, int hidden, float* mod,
-                        int dtype, hipStream_t s);
+// Rows of a batched launch (samples that share the weights): row j belongs to sample
+// g = j / rows, local row i = j - g * rows.  Sample g's rows of a strided operand (x, or C of
+// the gated residual) start `x_stride` elements after sample g-1's, and its per-feature
+// parameter vectors (shift, scale, gate) `p_stride` elements after sample g-1's.  One sample
+// is {total rows, 0, 0}.
+struct RowGroups {
+  int64_t rows;
+  int64_t x_stride;
+  int64_t p_stride;
+};
 
 // Destination of the fused QKV epilogue (kEpiQkvSplice, bf16 only): output features [0, h)
-// (Q) go to c; features [h, 2h) are row `row0 + i` of the K buffer (ROWS layout, row stride
-// h) and [2h, 3h) the same row of the V buffer (K8 layout, h columns).
+// (Q) go to c; features [h, 2h) of row j (sample g, local row i, see RowGroups with
+// grp_rows) are row `row0 + i` of sample g's K buffer (ROWS layout, row stride h) and
+// [2h, 3h) the same row of its V buffer (K8 layout, h columns).  Sample g's buffers start
+// k_stride / v_stride elements after sample g-1's.
 struct QkvSplice {
   void* k;
   void* v;
   int64_t row0;
   int64_t h;
+  int64_t grp_rows;
+  int64_t k_stride;
+  int64_t v_stride;
 };
 
+// ---- launchers (each enqueues one kernel on `s` and returns hipGetLastError()) ----
+
+// y (contiguous [rows, hidden]) from x; `groups` (NULL: one sample) gives each sample's x rows
+// and shift / scale vectors.
+hipError_t launch_ln_modulate(const float* x, int64_t rows, int hidden, const float* shift,
+                              const float* scale, float eps, void* y, int dtype, hipStream_t s,
+                              const RowGroups* groups = nullptr);
+
+hipError_t launch_adaln(const float* cond, const void* w, const float* b, int hidden, float* mod,
+                        int dtype, hipStream_t s);
+
 // `ws` (may be NULL) is scratch for the k-split of grids too small to fill the GPU.
+// `groups` (NULL: one sample) applies to the gated residual: each sample's rows of c and its
+// gate vector.
 hipError_t launch_gemm(const void* a, int64_t lda, const void* w, const float* bias, int64_t m,
                        int64_t n, int64_t k, int epi, void* c, int64_t ldc, const float* gate,
                        int dtype, void* ws, size_t ws_bytes, hipStream_t s,
-                       const QkvSplice* splice = nullptr);
+                       const QkvSplice* splice = nullptr, const RowGroups* groups = nullptr);
 
 // Scratch bytes the bf16 GEMM would use for its k-split at this shape (0: no split).
 size_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k);

@@ -22,14 +22,16 @@ template <typename OutT, int NS>
 __global__ __launch_bounds__(256) void ln_modulate_kernel(const float* __restrict__ x, int64_t rows,
                                                           int hidden, const float* __restrict__ shift,
                                                           const float* __restrict__ scale, float eps,
-                                                          OutT* __restrict__ y) {
+                                                          OutT* __restrict__ y, RowGroups grp) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
   const int n4 = hidden >> 2;
-  const float4* xr = reinterpret_cast<const float4*>(x + row * hidden);
-  const float4* sh4 = reinterpret_cast<const float4*>(shift);
-  const float4* sc4 = reinterpret_cast<const float4*>(scale);
+  // sample g's rows of x and its shift / scale (row is wavefront-uniform)
+  const int64_t g = row / grp.rows;
+  const float4* xr = reinterpret_cast<const float4*>(x + g * grp.x_stride + (row - g * grp.rows) * hidden);
+  const float4* sh4 = reinterpret_cast<const float4*>(shift + g * grp.p_stride);
+  const float4* sc4 = reinterpret_cast<const float4*>(scale + g * grp.p_stride);
   // shift and scale are loaded up front too while they fit in registers (hidden <= 3072)
   constexpr bool kPreload = NS <= 12;
   float4 v[NS], sh[NS], sc[NS];
@@ -86,24 +88,28 @@ __global__ __launch_bounds__(256) void ln_modulate_kernel(const float* __restric
 
 template <typename OutT, int NS>
 static void launch_ln_ns(int ns, dim3 grid, const float* x, int64_t rows, int hidden, const float* shift,
-                         const float* scale, float eps, OutT* y, hipStream_t s) {
+                         const float* scale, float eps, OutT* y, const RowGroups& g, hipStream_t s) {
   if constexpr (NS > 1) {
-    if (ns < NS) return launch_ln_ns<OutT, NS - 1>(ns, grid, x, rows, hidden, shift, scale, eps, y, s);
+    if (ns < NS) return launch_ln_ns<OutT, NS - 1>(ns, grid, x, rows, hidden, shift, scale, eps, y, g, s);
   }
-  hipLaunchKernelGGL((ln_modulate_kernel<OutT, NS>), grid, dim3(256), 0, s, x, rows, hidden, shift, scale, eps, y);
+  hipLaunchKernelGGL((ln_modulate_kernel<OutT, NS>), grid, dim3(256), 0, s, x, rows, hidden, shift, scale, eps, y,
+                     g);
 }
 
 hipError_t launch_ln_modulate(const float* x, int64_t rows, int hidden, const float* shift,
-                              const float* scale, float eps, void* y, int dtype, hipStream_t s) {
+                              const float* scale, float eps, void* y, int dtype, hipStream_t s,
+                              const RowGroups* groups) {
   if (rows <= 0) return hipSuccess;
   constexpr int kSlots = kMaxHidden / 256;
   const int ns = (hidden / 4 + 63) / 64;             // float4 chunks per lane
   if (ns < 1 || ns > kSlots) return hipErrorInvalidValue;
+  const RowGroups g = groups ? *groups : RowGroups{rows, 0, 0};
+  if (g.rows <= 0) return hipErrorInvalidValue;
   dim3 grid((unsigned)((rows + 3) / 4));
   if (dtype == kDtypeBF16)
-    launch_ln_ns<bf16, kSlots>(ns, grid, x, rows, hidden, shift, scale, eps, static_cast<bf16*>(y), s);
+    launch_ln_ns<bf16, kSlots>(ns, grid, x, rows, hidden, shift, scale, eps, static_cast<bf16*>(y), g, s);
   else
-    launch_ln_ns<float, kSlots>(ns, grid, x, rows, hidden, shift, scale, eps, static_cast<float*>(y), s);
+    launch_ln_ns<float, kSlots>(ns, grid, x, rows, hidden, shift, scale, eps, static_cast<float*>(y), g, s);
   return hipGetLastError();
 }
 

@@ -226,7 +226,7 @@ extern "C" pf_status pf_gemm_qkv_splice(const void* a, int64_t lda, const void* 
   if (workspace && !aligned16(workspace))
     return fail(PF_ERR_INVALID_ARG, "gemm_qkv_splice: workspace must be 16-byte aligned");
   if ((st = check_device()) != PF_OK) return st;
-  const QkvSplice sp{kv->k, kv->v, row_offset, hidden};
+  const QkvSplice sp{kv->k, kv->v, row_offset, hidden, m > 0 ? m : 1, 0, 0};
   hipError_t e = launch_gemm(a, lda, w, bias, m, 3 * hidden, hidden, kEpiQkvSplice, q, ldq, nullptr, PF_BF16,
                              workspace, workspace ? (size_t)workspace_bytes : 0, (hipStream_t)stream, &sp);
   return e == hipSuccess ? PF_OK : hip_fail(e, "gemm_qkv_splice launch");
@@ -297,8 +297,8 @@ extern "C" pf_status kvbuf_splice(const pf_kv_view* dst, const pf_kv_view* src, 
 struct LayerMem {
   void *w_qkv, *w_o, *w1, *w2, *w_ada;
   float *b_qkv, *b_o, *b1, *b2, *b_ada;
-  void *k, *v;
-  float* mod;   // [6h]: shift1, scale1, gate1, shift2, scale2, gate2
+  void *k, *v;  // sample 0's K and V buffers; sample b's are b * kv_sample_bytes further on
+  float* mod;   // [batch][6h]: shift1, scale1, gate1, shift2, scale2, gate2 per sample
   bool loaded;
 };
 
@@ -306,6 +306,8 @@ struct pf_stage {
   pf_stage_config cfg;
   int device;
   int64_t h, rh, s_kv, s_alloc, patch_rows;
+  int64_t batch;            // samples sharing the weights (each with its cond, rows and buffers)
+  size_t kv_sample_bytes;   // distance between two samples' K (or V) buffers of one layer
   size_t es;
   void* wmem = nullptr;
   void* kvmem = nullptr;
@@ -340,6 +342,8 @@ static pf_status validate_config(const pf_stage_config* c) {
   if (c->gelu != PF_GELU_TANH && c->gelu != PF_GELU_ERF) return fail(PF_ERR_INVALID_ARG, "stage_create: bad gelu");
   if (!(c->ln_eps > 0.f) || !std::isfinite(c->ln_eps)) return fail(PF_ERR_INVALID_ARG, "stage_create: bad ln_eps");
   if (c->flags != 0) return fail(PF_ERR_INVALID_ARG, "stage_create: flags must be 0");
+  if (c->batch < 0 || c->batch > PF_MAX_STAGE_BATCH)
+    return fail(PF_ERR_INVALID_ARG, "stage_create: batch %d outside [0, %d]", c->batch, PF_MAX_STAGE_BATCH);
   if (c->hidden > kMaxHidden) return fail(PF_ERR_UNSUPPORTED, "stage_create: hidden > %d", kMaxHidden);
   if (c->dtype == PF_BF16 && c->hidden % 64 != 0)
     return fail(PF_ERR_UNSUPPORTED, "stage_create: bf16 stages need hidden %% 64 == 0");
@@ -378,8 +382,9 @@ extern "C" pf_status stage_create(const pf_stage_config* cfg, pf_stage** out) {
   st->s_kv = cfg->seq_txt + cfg->seq_img;
   st->s_alloc = (int64_t)round_up((size_t)st->s_kv, 64);   // K8 groups and key tiles never leave the allocation
   st->patch_rows = cfg->seq_img / cfg->num_patches;
+  st->batch = cfg->batch > 0 ? cfg->batch : 1;
   st->es = dtype_size(cfg->dtype);
-  const int64_t h = st->h, rh = st->rh, L = cfg->num_layers;
+  const int64_t h = st->h, rh = st->rh, L = cfg->num_layers, nb = st->batch;
   const size_t es = st->es;
 
   // weights: matrices then fp32 biases, each 256-byte aligned
@@ -388,18 +393,21 @@ extern "C" pf_status stage_create(const pf_stage_config* cfg, pf_stage** out) {
   size_t per_layer = 0;
   for (int i = 0; i < 5; ++i) per_layer += round_up(mats[i] * es, 256) + round_up(biases[i] * 4, 256);
   const size_t kv_mat = round_up((size_t)(st->s_alloc * h) * es, 256);
-  const size_t scr_h = round_up((size_t)(st->s_alloc * h) * es, 256);
-  const size_t scr_qkv = round_up((size_t)(st->s_alloc * 3 * h) * es, 256);
-  const size_t scr_u = round_up((size_t)(st->s_alloc * (rh > 0 ? rh : 1)) * es, 256);
+  st->kv_sample_bytes = 2 * kv_mat;   // per layer: K0, V0, K1, V1, ...
+  // scratch for a micro-step of up to s_kv rows of every sample
+  const size_t scr_h = round_up((size_t)(nb * st->s_alloc * h) * es, 256);
+  const size_t scr_qkv = round_up((size_t)(nb * st->s_alloc * 3 * h) * es, 256);
+  const size_t scr_u = round_up((size_t)(nb * st->s_alloc * (rh > 0 ? rh : 1)) * es, 256);
 
-  // split partials for a patch or the text prefix (the warm-up pass fills the GPU unsplit)
+  // split partials for a patch or the text prefix of one sample (attention runs per sample;
+  // the warm-up pass fills the GPU unsplit)
   const int64_t split_rows = std::max<int64_t>(st->patch_rows, cfg->seq_txt);
   st->attn_ws_bytes = cfg->dtype == PF_BF16 ? attention_workspace_bytes(split_rows, h, cfg->heads, kMaxAttnSplit) : 0;
-  // k-split partials for the projections of a patch or the text prefix
+  // k-split partials for the projections of a patch or the text prefix of all samples
   st->gemm_ws_bytes = 0;
   if (cfg->dtype == PF_BF16) {
     const int64_t shapes[4][2] = {{3 * h, h}, {h, h}, {rh, h}, {h, rh}};
-    for (const int64_t rows : {(int64_t)st->patch_rows, (int64_t)cfg->seq_txt}) {
+    for (const int64_t rows : {nb * st->patch_rows, nb * cfg->seq_txt}) {
       if (rows <= 0) continue;
       for (const auto& nk : shapes)
         if (nk[0] > 0 && nk[1] > 0) st->gemm_ws_bytes = std::max(st->gemm_ws_bytes, gemm_workspace_bytes(rows, nk[0], nk[1]));
@@ -410,9 +418,9 @@ extern "C" pf_status stage_create(const pf_stage_config* cfg, pf_stage** out) {
   if ((e = hipMalloc(&st->wmem, per_layer * L)) != hipSuccess ||
       (st->attn_ws_bytes && (e = hipMalloc(&st->attn_ws, st->attn_ws_bytes)) != hipSuccess) ||
       (st->gemm_ws_bytes && (e = hipMalloc(&st->gemm_ws, st->gemm_ws_bytes)) != hipSuccess) ||
-      (e = hipMalloc(&st->kvmem, 2 * kv_mat * L)) != hipSuccess ||
+      (e = hipMalloc(&st->kvmem, 2 * kv_mat * L * nb)) != hipSuccess ||
       (e = hipMalloc(&st->scratch, 2 * scr_h + scr_qkv + scr_u)) != hipSuccess ||
-      (e = hipMalloc((void**)&st->modmem, sizeof(float) * 6 * h * L)) != hipSuccess) {
+      (e = hipMalloc((void**)&st->modmem, sizeof(float) * 6 * h * L * nb)) != hipSuccess) {
     free_stage_mem(st);
     delete st;
     (void)hipGetLastError();
@@ -420,8 +428,8 @@ extern "C" pf_status stage_create(const pf_stage_config* cfg, pf_stage** out) {
                                     : hip_fail(e, "stage_create: hipMalloc");
   }
   // zero the KV buffers (including the padding rows past seq_kv) once, synchronously
-  if ((e = hipMemset(st->kvmem, 0, 2 * kv_mat * L)) != hipSuccess ||
-      (e = hipMemset(st->modmem, 0, sizeof(float) * 6 * h * L)) != hipSuccess ||
+  if ((e = hipMemset(st->kvmem, 0, 2 * kv_mat * L * nb)) != hipSuccess ||
+      (e = hipMemset(st->modmem, 0, sizeof(float) * 6 * h * L * nb)) != hipSuccess ||
       (e = hipDeviceSynchronize()) != hipSuccess) {
     free_stage_mem(st);
     delete st;
@@ -441,10 +449,9 @@ extern "C" pf_status stage_create(const pf_stage_config* cfg, pf_stage** out) {
       wp += round_up(biases[i] * 4, 256);
     }
     lm.k = kp;
-    kp += kv_mat;
-    lm.v = kp;
-    kp += kv_mat;
-    lm.mod = st->modmem + 6 * h * l;
+    lm.v = kp + kv_mat;
+    kp += 2 * kv_mat * nb;
+    lm.mod = st->modmem + 6 * h * nb * l;
     lm.loaded = false;
   }
   char* sp = (char*)st->scratch;
@@ -518,10 +525,12 @@ static pf_status check_loaded(pf_stage* st, const char* who) {
 }
 
 static pf_status set_cond_impl(pf_stage* st, const float* cond, hipStream_t s) {
-  for (auto& lm : st->layers) {
-    hipError_t e = launch_adaln(cond, lm.w_ada, lm.b_ada, (int)st->h, lm.mod, st->cfg.dtype, s);
-    if (e != hipSuccess) return stage_hip_fail(st, e, "stage_set_cond: adaln launch");
-  }
+  for (auto& lm : st->layers)
+    for (int64_t b = 0; b < st->batch; ++b) {
+      hipError_t e = launch_adaln(cond + b * st->h, lm.w_ada, lm.b_ada, (int)st->h, lm.mod + b * 6 * st->h,
+                                  st->cfg.dtype, s);
+      if (e != hipSuccess) return stage_hip_fail(st, e, "stage_set_cond: adaln launch");
+    }
   st->cond_set = true;
   return PF_OK;
 }
@@ -534,64 +543,81 @@ extern "C" pf_status stage_set_cond(pf_stage* st, const float* cond, void* strea
   return set_cond_impl(st, cond, (hipStream_t)stream);
 }
 
-// rows [off, off + n) through all layers; x (fp32 [n, h]) is updated in place
-static pf_status run_rows(pf_stage* st, int64_t off, int64_t n, float* x, hipStream_t s) {
-  const int64_t h = st->h, rh = st->rh;
+// Buffer rows [off, off + n) of every sample through all layers.  Sample b's rows of x (fp32,
+// updated in place) are [x + b * x_stride, + n * h); inside the micro-step the samples' rows
+// are stacked (rows b*n .. b*n + n - 1 of the scratch), so every projection runs once over
+// batch * n rows with shared weights, while each sample keeps its own modulation, gates, K/V
+// buffers and attention.
+static pf_status run_rows(pf_stage* st, int64_t off, int64_t n, float* x, int64_t x_stride, hipStream_t s) {
+  const int64_t h = st->h, rh = st->rh, nb = st->batch, rows = nb * n;
   const int dt = st->cfg.dtype;
   const size_t es = st->es;
   const float eps = st->cfg.ln_eps;
   const int gelu_epi = st->cfg.gelu == PF_GELU_ERF ? kEpiGeluErf : kEpiGeluTanh;
+  const int64_t kv_stride = (int64_t)(st->kv_sample_bytes / es);   // elements between samples' buffers
+  const RowGroups xg{n, x_stride, 6 * h};   // x rows and modulation vectors per sample
   char* qkv = (char*)st->qkv;
   for (auto& lm : st->layers) {
     const float* mod = lm.mod;
     hipError_t e;
-    if ((e = launch_ln_modulate(x, n, (int)h, mod, mod + h, eps, st->h1, dt, s)) != hipSuccess)
+    if ((e = launch_ln_modulate(x, rows, (int)h, mod, mod + h, eps, st->h1, dt, s, &xg)) != hipSuccess)
       return stage_hip_fail(st, e, "ln_modulate");
     const int v_layout = dt == PF_BF16 ? kLayoutK8 : kLayoutRows;
     if (dt == PF_BF16) {
-      // QKV projection with the splice in its epilogue: Q to the scratch, the patch's fresh K and
-      // V straight into rows [off, off + n) of the layer's buffer (no other row changes)
-      const QkvSplice sp{lm.k, lm.v, off, h};
-      if ((e = launch_gemm(st->h1, h, lm.w_qkv, lm.b_qkv, n, 3 * h, h, kEpiQkvSplice, qkv, 3 * h, nullptr, dt,
+      // QKV projection with the splice in its epilogue: Q to the scratch, each sample's fresh K
+      // and V straight into rows [off, off + n) of its own buffer (no other row changes)
+      const QkvSplice sp{lm.k, lm.v, off, h, n, kv_stride, kv_stride};
+      if ((e = launch_gemm(st->h1, h, lm.w_qkv, lm.b_qkv, rows, 3 * h, h, kEpiQkvSplice, qkv, 3 * h, nullptr, dt,
                            st->gemm_ws, st->gemm_ws_bytes, s, &sp)) != hipSuccess)
         return stage_hip_fail(st, e, "qkv gemm + kv splice");
     } else {
-      if ((e = launch_gemm(st->h1, h, lm.w_qkv, lm.b_qkv, n, 3 * h, h, kEpiStore, qkv, 3 * h, nullptr, dt,
+      if ((e = launch_gemm(st->h1, h, lm.w_qkv, lm.b_qkv, rows, 3 * h, h, kEpiStore, qkv, 3 * h, nullptr, dt,
                            st->gemm_ws, st->gemm_ws_bytes, s)) != hipSuccess)
         return stage_hip_fail(st, e, "qkv gemm");
-      KVDesc dst[2] = {{lm.k, h, kLayoutRows}, {lm.v, h, kLayoutRows}};
-      KVDesc src[2] = {{qkv + h * es, 3 * h, kLayoutRows}, {qkv + 2 * h * es, 3 * h, kLayoutRows}};
-      if ((e = launch_splice(dst, src, h, off, n, (int)es, s)) != hipSuccess) return stage_hip_fail(st, e, "kv splice");
+      for (int64_t b = 0; b < nb; ++b) {
+        const char* src_row = qkv + (size_t)(b * n * 3 * h) * es;
+        KVDesc dst[2] = {{(char*)lm.k + b * st->kv_sample_bytes, h, kLayoutRows},
+                         {(char*)lm.v + b * st->kv_sample_bytes, h, kLayoutRows}};
+        KVDesc src[2] = {{src_row + h * es, 3 * h, kLayoutRows}, {src_row + 2 * h * es, 3 * h, kLayoutRows}};
+        if ((e = launch_splice(dst, src, h, off, n, (int)es, s)) != hipSuccess)
+          return stage_hip_fail(st, e, "kv splice");
+      }
     }
-    if ((e = launch_attention(qkv, 3 * h, lm.k, h, lm.v, h, v_layout, h, st->s_kv, n, st->cfg.heads,
-                              st->cfg.head_dim, st->o, h, dt, st->attn_ws, st->attn_ws_bytes, s)) != hipSuccess)
-      return stage_hip_fail(st, e, "attention");
-    if ((e = launch_gemm(st->o, h, lm.w_o, lm.b_o, n, h, h, kEpiGatedResidual, x, h, mod + 2 * h, dt,
-                           st->gemm_ws, st->gemm_ws_bytes, s)) !=
-        hipSuccess)
+    for (int64_t b = 0; b < nb; ++b) {   // each sample attends over its own buffer
+      const char* q = qkv + (size_t)(b * n * 3 * h) * es;
+      char* o = (char*)st->o + (size_t)(b * n * h) * es;
+      if ((e = launch_attention(q, 3 * h, (char*)lm.k + b * st->kv_sample_bytes, h,
+                                (char*)lm.v + b * st->kv_sample_bytes, h, v_layout, h, st->s_kv, n, st->cfg.heads,
+                                st->cfg.head_dim, o, h, dt, st->attn_ws, st->attn_ws_bytes, s)) != hipSuccess)
+        return stage_hip_fail(st, e, "attention");
+    }
+    if ((e = launch_gemm(st->o, h, lm.w_o, lm.b_o, rows, h, h, kEpiGatedResidual, x, h, mod + 2 * h, dt,
+                         st->gemm_ws, st->gemm_ws_bytes, s, nullptr, &xg)) != hipSuccess)
       return stage_hip_fail(st, e, "out-proj gemm");
     if (rh > 0) {
-      if ((e = launch_ln_modulate(x, n, (int)h, mod + 3 * h, mod + 4 * h, eps, st->h1, dt, s)) != hipSuccess)
+      if ((e = launch_ln_modulate(x, rows, (int)h, mod + 3 * h, mod + 4 * h, eps, st->h1, dt, s, &xg)) != hipSuccess)
         return stage_hip_fail(st, e, "ln_modulate (mlp)");
-      if ((e = launch_gemm(st->h1, h, lm.w1, lm.b1, n, rh, h, gelu_epi, st->u, rh, nullptr, dt, st->gemm_ws,
-                             st->gemm_ws_bytes, s)) != hipSuccess)
+      if ((e = launch_gemm(st->h1, h, lm.w1, lm.b1, rows, rh, h, gelu_epi, st->u, rh, nullptr, dt, st->gemm_ws,
+                           st->gemm_ws_bytes, s)) != hipSuccess)
         return stage_hip_fail(st, e, "mlp up gemm");
-      if ((e = launch_gemm(st->u, rh, lm.w2, lm.b2, n, h, rh, kEpiGatedResidual, x, h, mod + 5 * h, dt,
-                             st->gemm_ws, st->gemm_ws_bytes, s)) !=
-          hipSuccess)
+      if ((e = launch_gemm(st->u, rh, lm.w2, lm.b2, rows, h, rh, kEpiGatedResidual, x, h, mod + 5 * h, dt,
+                           st->gemm_ws, st->gemm_ws_bytes, s, nullptr, &xg)) != hipSuccess)
         return stage_hip_fail(st, e, "mlp down gemm");
     }
   }
   return PF_OK;
 }
 
+// x_in / x_out: sample b's n rows at + b * x_stride elements.
 static pf_status run_patch_impl(pf_stage* st, int64_t off, int64_t n, const float* x_in, float* x_out,
-                                hipStream_t s) {
+                                int64_t x_stride, hipStream_t s) {
   if (x_out != x_in) {
-    hipError_t e = hipMemcpyAsync(x_out, x_in, (size_t)(n * st->h) * sizeof(float), hipMemcpyDeviceToDevice, s);
-    if (e != hipSuccess) return stage_hip_fail(st, e, "stage_run_patch: hipMemcpyAsync");
+    const size_t row_bytes = (size_t)(n * st->h) * sizeof(float);
+    hipError_t e = hipMemcpy2DAsync(x_out, (size_t)x_stride * sizeof(float), x_in, (size_t)x_stride * sizeof(float),
+                                    row_bytes, (size_t)st->batch, hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess) return stage_hip_fail(st, e, "stage_run_patch: hipMemcpy2DAsync");
   }
-  return run_rows(st, off, n, x_out, s);
+  return run_rows(st, off, n, x_out, x_stride, s);
 }
 
 static bool ranges_overlap(const void* a, size_t an, const void* b, size_t bn) {
@@ -608,12 +634,12 @@ extern "C" pf_status stage_run_patch(pf_stage* st, int64_t row_off, int64_t rows
                 (long long)(row_off + rows), (long long)st->s_kv);
   if (!x_in || !x_out) return fail(PF_ERR_INVALID_ARG, "stage_run_patch: null x");
   if (!aligned16(x_in) || !aligned16(x_out)) return fail(PF_ERR_INVALID_ARG, "stage_run_patch: x must be 16-byte aligned");
-  const size_t bytes = (size_t)(rows * st->h) * sizeof(float);
+  const size_t bytes = (size_t)(st->batch * rows * st->h) * sizeof(float);
   if (x_in != x_out && ranges_overlap(x_in, bytes, x_out, bytes))
     return fail(PF_ERR_INVALID_ARG, "stage_run_patch: x_in and x_out partially overlap");
   if ((s = check_loaded(st, "stage_run_patch")) != PF_OK) return s;
   if (!st->cond_set) return fail(PF_ERR_STATE, "stage_run_patch: stage_set_cond not called");
-  return run_patch_impl(st, row_off, rows, x_in, x_out, (hipStream_t)stream);
+  return run_patch_impl(st, row_off, rows, x_in, x_out, rows * st->h, (hipStream_t)stream);
 }
 
 extern "C" pf_status stage_run_step(pf_stage* st, const float* x_in, float* x_out, const float* cond, uint32_t flags,
@@ -623,29 +649,30 @@ extern "C" pf_status stage_run_step(pf_stage* st, const float* x_in, float* x_ou
   if (!x_in || !x_out || !cond) return fail(PF_ERR_INVALID_ARG, "stage_run_step: null pointer");
   if (!aligned16(x_in) || !aligned16(x_out)) return fail(PF_ERR_INVALID_ARG, "stage_run_step: x must be 16-byte aligned");
   if (flags & ~PF_STEP_WARMUP) return fail(PF_ERR_INVALID_ARG, "stage_run_step: unknown flags");
-  const size_t bytes = (size_t)(st->s_kv * st->h) * sizeof(float);
+  const size_t bytes = (size_t)(st->batch * st->s_kv * st->h) * sizeof(float);
   if (x_in != x_out && ranges_overlap(x_in, bytes, x_out, bytes))
     return fail(PF_ERR_INVALID_ARG, "stage_run_step: x_in and x_out partially overlap");
   if ((s = check_loaded(st, "stage_run_step")) != PF_OK) return s;
   hipStream_t hs = (hipStream_t)stream;
   if ((s = set_cond_impl(st, cond, hs)) != PF_OK) return s;
-  const int64_t h = st->h;
-  if (flags & PF_STEP_WARMUP) return run_patch_impl(st, 0, st->s_kv, x_in, x_out, hs);
-  if (st->cfg.seq_txt > 0 && (s = run_patch_impl(st, 0, st->cfg.seq_txt, x_in, x_out, hs)) != PF_OK) return s;
+  const int64_t h = st->h, xs = st->s_kv * h;   // sample b's rows start b * s_kv rows on
+  if (flags & PF_STEP_WARMUP) return run_patch_impl(st, 0, st->s_kv, x_in, x_out, xs, hs);
+  if (st->cfg.seq_txt > 0 && (s = run_patch_impl(st, 0, st->cfg.seq_txt, x_in, x_out, xs, hs)) != PF_OK) return s;
   for (int m = 0; m < st->cfg.num_patches; ++m) {
     const int64_t off = st->cfg.seq_txt + (int64_t)m * st->patch_rows;
-    if ((s = run_patch_impl(st, off, st->patch_rows, x_in + off * h, x_out + off * h, hs)) != PF_OK) return s;
+    if ((s = run_patch_impl(st, off, st->patch_rows, x_in + off * h, x_out + off * h, xs, hs)) != PF_OK) return s;
   }
   return PF_OK;
 }
 
-extern "C" pf_status stage_get_kvbuf(pf_stage* st, int32_t layer, pf_kv_view* out) {
+extern "C" pf_status stage_get_kvbuf_sample(pf_stage* st, int32_t layer, int32_t sample, pf_kv_view* out) {
   if (!st) return fail(PF_ERR_INVALID_ARG, "stage_get_kvbuf: null stage");
   if (!out) return fail(PF_ERR_INVALID_ARG, "stage_get_kvbuf: null out");
   if (layer < 0 || layer >= st->cfg.num_layers) return fail(PF_ERR_INVALID_ARG, "stage_get_kvbuf: bad layer");
+  if (sample < 0 || sample >= st->batch) return fail(PF_ERR_INVALID_ARG, "stage_get_kvbuf: bad sample");
   const LayerMem& lm = st->layers[layer];
-  out->k = lm.k;
-  out->v = lm.v;
+  out->k = (char*)lm.k + sample * st->kv_sample_bytes;
+  out->v = (char*)lm.v + sample * st->kv_sample_bytes;
   out->rows = st->s_kv;
   out->row_elems = st->h;
   out->k_ld = st->h;
@@ -653,4 +680,8 @@ extern "C" pf_status stage_get_kvbuf(pf_stage* st, int32_t layer, pf_kv_view* ou
   out->dtype = st->cfg.dtype;
   out->v_layout = st->cfg.dtype == PF_BF16 ? PF_LAYOUT_K8 : PF_LAYOUT_ROWS;
   return PF_OK;
+}
+
+extern "C" pf_status stage_get_kvbuf(pf_stage* st, int32_t layer, pf_kv_view* out) {
+  return stage_get_kvbuf_sample(st, layer, 0, out);
 }

@@ -35,15 +35,20 @@ def rows_to_k8(a: np.ndarray) -> np.ndarray:
 
 
 class Stage:
-    def __init__(self, shape: StageShape, gelu: str = "tanh", ln_eps: float = 1e-6):
+    """`batch` > 1: samples sharing the weights (a classifier-free guidance pair is 2); x is
+    then [batch, rows, h] and cond [batch, h], and each sample has its own K/V buffers."""
+
+    def __init__(self, shape: StageShape, gelu: str = "tanh", ln_eps: float = 1e-6, batch: int = 1):
         torch = _torch()
         self.shape = shape
+        self.batch = batch
         self.dtype = torch.bfloat16 if shape.dtype == "bf16" else torch.float32
         self.pf_dtype = B.PF_BF16 if shape.dtype == "bf16" else B.PF_FP32
         cfg = B.StageConfig(num_layers=shape.num_layers, hidden=shape.hidden, heads=shape.heads,
                             head_dim=shape.head_dim, mlp_ratio=shape.mlp_ratio, num_patches=shape.num_patches,
                             seq_img=shape.seq_img, seq_txt=shape.seq_txt, dtype=self.pf_dtype,
-                            gelu=B.PF_GELU_TANH if gelu == "tanh" else B.PF_GELU_ERF, ln_eps=ln_eps, flags=0)
+                            gelu=B.PF_GELU_TANH if gelu == "tanh" else B.PF_GELU_ERF, ln_eps=ln_eps, flags=0,
+                            batch=batch)
         self.handle = B.stage_create(cfg)
         self.v_layout = B.PF_LAYOUT_K8 if self.pf_dtype == B.PF_BF16 else B.PF_LAYOUT_ROWS
 
@@ -100,8 +105,8 @@ class Stage:
         return x_out
 
     # ------------------------------------------------------------------ KV buffers
-    def kv_view(self, layer: int) -> B.KVView:
-        return B.stage_get_kvbuf(self.handle, layer)
+    def kv_view(self, layer: int, sample: int = 0) -> B.KVView:
+        return B.stage_get_kvbuf(self.handle, layer, sample)
 
     def _scratch_pair(self):
         torch = _torch()
@@ -112,16 +117,16 @@ class Stage:
         view = B.kv_view(k, v, s, h, self.v_layout)
         return k, v, view
 
-    def kv_raw(self, layer: int):
+    def kv_raw(self, layer: int, sample: int = 0):
         """Device copies (torch) of layer's K ([S,h]) and V (storage layout) buffers."""
         k, v, view = self._scratch_pair()
-        B.kvbuf_splice(view, self.kv_view(layer), 0, self.shape.seq_kv)
+        B.kvbuf_splice(view, self.kv_view(layer, sample), 0, self.shape.seq_kv)
         return k, v
 
-    def kv_get(self, layer: int):
+    def kv_get(self, layer: int, sample: int = 0):
         """Host fp32 arrays [S, h] of layer's K and V (logical rows)."""
         torch = _torch()
-        k, v = self.kv_raw(layer)
+        k, v = self.kv_raw(layer, sample)
         torch.cuda.synchronize()
         kh = k.float().cpu().numpy()
         vh = v.float().cpu().numpy()
@@ -129,18 +134,18 @@ class Stage:
             vh = k8_to_rows(vh, self.shape.seq_kv, self.shape.hidden)
         return kh, vh
 
-    def kv_set(self, layer: int, k_rows: np.ndarray, v_rows: np.ndarray):
+    def kv_set(self, layer: int, k_rows: np.ndarray, v_rows: np.ndarray, sample: int = 0):
         """Overwrite layer's whole K/V buffer from host arrays (rounded to the stage dtype by torch)."""
         torch = _torch()
         kt = torch.from_numpy(np.ascontiguousarray(k_rows, np.float32)).to(device="cuda", dtype=self.dtype)
         vv = rows_to_k8(np.asarray(v_rows, np.float32)) if self.v_layout == B.PF_LAYOUT_K8 else v_rows
         vt = torch.from_numpy(np.ascontiguousarray(vv, np.float32)).to(device="cuda", dtype=self.dtype)
         view = B.kv_view(kt, vt, self.shape.seq_kv, self.shape.hidden, self.v_layout)
-        B.kvbuf_splice(self.kv_view(layer), view, 0, self.shape.seq_kv)
+        B.kvbuf_splice(self.kv_view(layer, sample), view, 0, self.shape.seq_kv)
         torch.cuda.synchronize()
 
-    def add_noise(self, noise):
+    def add_noise(self, noise, sample: int = 0):
         """Step boundary drift: K += nk, V += nv for every layer (fp32 add, then stage dtype)."""
         for l, (nk, nv) in enumerate(noise):
-            k, v = self.kv_get(l)
-            self.kv_set(l, k + nk, v + nv)
+            k, v = self.kv_get(l, sample)
+            self.kv_set(l, k + nk, v + nv, sample)

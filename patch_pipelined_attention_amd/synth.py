@@ -86,6 +86,14 @@ def stage_inputs(shape: StageShape, seed: int | None = None) -> StageInputs:
     return StageInputs(shape, layers, x, c, rng)
 
 
+def batch_conds(shape: StageShape, c: np.ndarray, batch: int) -> np.ndarray:
+    """Conditions of a batch of samples sharing the latent: sample 0 takes `c`; sample b >= 1
+    (e.g. the unconditional half of a classifier-free guidance pair) an N(0, 1) vector of its own
+    generator, PCG64(shape.seed + 7776 + b).  fp32 [batch, h]."""
+    rows = [np.asarray(c, np.float32)] + [randn((shape.hidden,), shape.seed + 7776 + b) for b in range(1, batch)]
+    return np.stack(rows)
+
+
 def randn(shape, seed: int, std: float = 1.0, bf16: bool = False) -> np.ndarray:
     """Plain seeded N(0, std^2) array (fp32), optionally rounded to bf16 values."""
     rng = np.random.Generator(np.random.PCG64(seed))

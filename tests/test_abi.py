@@ -42,6 +42,8 @@ def _cfg(**kw):
     (dict(flags=1), B.PF_ERR_INVALID_ARG),
     (dict(heads=1, hidden=72), B.PF_ERR_UNSUPPORTED),        # bf16 needs hidden % 64 == 0
     (dict(mlp_ratio=-1), B.PF_ERR_INVALID_ARG),
+    (dict(batch=-1), B.PF_ERR_INVALID_ARG),
+    (dict(batch=9), B.PF_ERR_INVALID_ARG),             # PF_MAX_STAGE_BATCH is 8
 ])
 def test_stage_create_rejects_bad_configs(lib, kw, status):
     cfg = _cfg(**kw)

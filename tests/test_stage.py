@@ -97,6 +97,102 @@ def test_small_bf16_stage_chain(name):
     _run_chain(SMALL[name], 3)
 
 
+def _run_pair_chain(shape, steps):
+    """A classifier-free guidance pair through one batched stage: both samples share the
+    latent rows and the weights, each has its own condition (the second stands in for the
+    unconditional embedding), its own drift between steps and its own K/V buffers.  Each
+    sample must match its own oracle stage, which never sees the other sample."""
+    torch = torch_cuda()
+    inputs = synth.stage_inputs(shape)
+    conds = list(synth.batch_conds(shape, inputs.c, 2))
+    bf16 = shape.dtype == "bf16"
+    orc_b = [_oracle(shape, inputs, "bf16" if bf16 else "exact") for _ in range(2)]
+    orc_p = [_oracle(shape, inputs, "bf16p") for _ in range(2)] if bf16 else None
+    S, h, L = shape.seq_kv, shape.hidden, shape.num_layers
+    with Stage(shape, batch=2) as st:
+        st.load(inputs.layers)
+        x = dev(torch, np.stack([inputs.x, inputs.x]))
+        c = dev(torch, np.stack(conds))
+        out = torch.empty_like(x)
+        for s in range(steps):
+            warm = s == 0
+            if s > 0:
+                for b in range(2):
+                    seed = shape.seed + 100 * s + 10 * b
+                    noise = [(synth.randn((S, h), seed + 2 * l, std=shape.sigma_kv),
+                              synth.randn((S, h), seed + 2 * l + 1, std=shape.sigma_kv)) for l in range(L)]
+                    st.add_noise(noise, sample=b)
+                    orc_b[b].add_noise(noise)
+                    if bf16:
+                        orc_p[b].add_noise(noise)
+            print(f"[stage pair] {shape.name} step {s} warmup={warm}", flush=True)
+            st.run_step(x, c, warmup=warm, out=out)
+            got = host(out)
+            for b in range(2):
+                want = orc_b[b].step(inputs.x, conds[b], warmup=warm)
+                if bf16:
+                    want_p = orc_p[b].step(inputs.x, conds[b], warmup=warm)
+                    tol = stage_output_max_abs_tol(want, want_p)
+                    assert_close(got[b], want, f"{shape.name} pair step {s} sample {b} vs bf16-in oracle",
+                                 max_abs_tol=tol)
+                    for l in range(L):
+                        k, v = st.kv_get(l, sample=b)
+                        assert_bf16_close(k, orc_b[b].K[l], f"pair step {s} sample {b} K[{l}]",
+                                          floor=2.0 * max_abs(orc_p[b].K[l], orc_b[b].K[l]))
+                        assert_bf16_close(v, orc_b[b].V[l], f"pair step {s} sample {b} V[{l}]",
+                                          floor=2.0 * max_abs(orc_p[b].V[l], orc_b[b].V[l]))
+                else:
+                    assert_close(got[b], want, f"{shape.name} pair step {s} sample {b} vs exact oracle",
+                                 max_abs_tol=1e-3, rel_tol=1e-5)
+                    for l in range(L):
+                        k, v = st.kv_get(l, sample=b)
+                        assert_close(k, orc_b[b].K[l], f"pair step {s} sample {b} K[{l}]", max_abs_tol=1e-4,
+                                     rel_tol=1e-5)
+                        assert_close(v, orc_b[b].V[l], f"pair step {s} sample {b} V[{l}]", max_abs_tol=1e-4,
+                                     rel_tol=1e-5)
+            # the two samples really differ (different conditions reach every row)
+            assert max_abs(got[0], got[1]) > 1e-3
+
+
+@pytest.mark.parametrize("name", ["c1", "c2s", "c4s"])
+def test_cfg_pair_stage_chain(name):
+    shape = C1 if name == "c1" else SMALL[name]
+    _run_pair_chain(shape, 3)
+
+
+def test_cfg_pair_patch_matches_single_stages():
+    """stage_run_patch on a pair equals the same micro-step on two single-sample stages, each
+    with that sample's condition and buffer contents (up to the fp32 summation order of
+    projections that see twice the rows)."""
+    torch = torch_cuda()
+    shape = SMALL["c2s"]
+    inputs = synth.stage_inputs(shape)
+    conds = list(synth.batch_conds(shape, inputs.c, 2))
+    P, off = shape.patch_rows, shape.patch_offsets()[1]
+    x_patch = inputs.x[off:off + P]
+    with Stage(shape, batch=2) as pair, Stage(shape) as s0, Stage(shape) as s1:
+        singles = [s0, s1]
+        for st in (pair, s0, s1):
+            st.load(inputs.layers)
+        # fill every buffer with a warm-up step of its own condition
+        x_all = dev(torch, inputs.x)
+        pair.run_step(dev(torch, np.stack([inputs.x, inputs.x])), dev(torch, np.stack(conds)), warmup=True,
+                      out=torch.empty((2, shape.seq_kv, shape.hidden), device="cuda"))
+        for b, st in enumerate(singles):
+            st.run_step(x_all, dev(torch, conds[b]), warmup=True, out=torch.empty_like(x_all))
+        pair.set_cond(dev(torch, np.stack(conds)))
+        got = host(pair.run_patch(off, P, dev(torch, np.stack([x_patch, x_patch]))))
+        for b, st in enumerate(singles):
+            st.set_cond(dev(torch, conds[b]))
+            want = host(st.run_patch(off, P, dev(torch, x_patch)))
+            assert_close(got[b], want, f"pair patch sample {b} vs single stage")
+            for l in range(shape.num_layers):
+                kp, vp = pair.kv_get(l, sample=b)
+                ks, vs = st.kv_get(l)
+                assert_bf16_close(kp, ks, f"pair patch sample {b} K[{l}] vs single stage")
+                assert_bf16_close(vp, vs, f"pair patch sample {b} V[{l}] vs single stage")
+
+
 def test_property_a_single_patch_overwrites_stale_context():
     """M = 1: the patch splices every row before attending, so any stale content is irrelevant."""
     torch = torch_cuda()

@@ -68,7 +68,8 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const bf16* __restric
                                                          int64_t S, int64_t rows, int n_qtiles, int n_split,
                                                          int tiles_per_split, bf16* __restrict__ O,
                                                          int64_t ldo, bf16* __restrict__ part_o,
-                                                         float* __restrict__ part_ml, float scale_log2) {
+                                                         float* __restrict__ part_ml, float scale_log2,
+                                                         int64_t grp_rows, int qtiles_per_grp, int64_t kv_stride) {
   constexpr int BQ = kAttnWaves * 32 * QB;
   constexpr int KS = (D + 15) / 16;
   constexpr int DB = (D + 31) / 32;
@@ -90,19 +91,32 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const bf16* __restric
   const int grp = wave >> 2, wl = wave & 3;
   const int l32 = lane & 31, hi = lane >> 5;
 
+  // Samples of a batch: query rows [g * grp_rows, (g+1) * grp_rows) of Q / O and the partials
+  // belong to sample g, whose K / V buffers start g * kv_stride elements on; each sample has
+  // qtiles_per_grp query tiles (n_qtiles in all).
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
-  const int qt = lid % n_qtiles;
+  const int qt_all = lid % n_qtiles;
   const int rest = lid / n_qtiles;
   const int split = rest % n_split;
   const int head = rest / n_split;
+  const int grp_id = qt_all / qtiles_per_grp;
+  const int qt = qt_all - grp_id * qtiles_per_grp;
+  Kb += grp_id * kv_stride;
+  Vb += grp_id * kv_stride;
+  const int64_t row_base = (int64_t)grp_id * grp_rows;
   const int64_t col0 = (int64_t)head * D;
   const int64_t ntiles = (S + TK - 1) / TK;
   const int64_t t_begin = (int64_t)split * tiles_per_split;
   const int64_t t_end = t_begin + tiles_per_split < ntiles ? t_begin + tiles_per_split : ntiles;
 
-  int64_t q_row[QB];
+  int64_t q_row[QB];   // row of Q / O / the partials
+  bool q_ok[QB];       // inside this sample's rows
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) q_row[qb] = (int64_t)qt * BQ + (wave * QB + qb) * 32 + l32;
+  for (int qb = 0; qb < QB; ++qb) {
+    const int64_t local = (int64_t)qt * BQ + (wave * QB + qb) * 32 + l32;
+    q_ok[qb] = local < grp_rows;
+    q_row[qb] = row_base + local;
+  }
 
   bf16x8 qf[QB][KS];
 #pragma unroll
@@ -110,7 +124,7 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const bf16* __restric
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int d0 = ks * 16 + hi * 8;
-      if (q_row[qb] < rows && d0 < D) {
+      if (q_ok[qb] && d0 < D) {
         qf[qb][ks] = *reinterpret_cast<const bf16x8*>(Q + q_row[qb] * ldq + col0 + d0);
       } else {
 #pragma unroll
@@ -419,7 +433,7 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const bf16* __restric
   // normalised result acc_s / l_s, also in bf16, plus (m_s, l_s) for the merge.
   for (int qb = 0; qb < QB; ++qb) {
     const float l_tot = l_run[qb] + __shfl_xor(l_run[qb], 32, 64);
-    if (q_row[qb] >= rows) continue;
+    if (!q_ok[qb]) continue;
     const float inv = 1.0f / l_tot;
     bf16* dst = n_split == 1 ? O + q_row[qb] * ldo + col0 : part_o + ((int64_t)split * rows + q_row[qb]) * hidden + col0;
 #pragma unroll
@@ -595,38 +609,44 @@ static int choose_split(int64_t wg, int slots, int64_t ntiles, int64_t rows, int
   return best;
 }
 
+// `rows` query rows per sample, `batch` samples: sample b's query rows are rows b*rows ..
+// of Q and O, its K / V buffers start b * kv_stride elements after sample 0's.
 template <int D>
 static hipError_t launch_attn_d(const void* q, int64_t ldq, const void* k, int64_t ldk, const void* v, int64_t ldv,
                                 int64_t hidden, int64_t seq_kv, int64_t rows, int heads, void* o, int64_t ldo,
-                                int dtype, void* ws, size_t ws_bytes, hipStream_t s) {
+                                int dtype, void* ws, size_t ws_bytes, hipStream_t s, int64_t batch,
+                                int64_t kv_stride) {
   if (dtype == kDtypeBF16) {
     constexpr int QB = AttnCfg<D>::QB;
     constexpr int BQ = kAttnWaves * 32 * QB;
-    const int n_qtiles = (int)((rows + BQ - 1) / BQ);
+    const int64_t all_rows = batch * rows;
+    const int per_grp = (int)((rows + BQ - 1) / BQ);
+    const int n_qtiles = (int)(batch * per_grp);
     const int64_t ntiles = (seq_kv + kTileKeys - 1) / kTileKeys;
     const int64_t wg = (int64_t)n_qtiles * heads;
-    const int n_split = ws ? choose_split(wg, attn_slots<D>(), ntiles, rows, hidden, heads, ws_bytes) : 1;
+    const int n_split = ws ? choose_split(wg, attn_slots<D>(), ntiles, all_rows, hidden, heads, ws_bytes) : 1;
     const int tps = (int)((ntiles + n_split - 1) / n_split);
     const int n_used = (int)((ntiles + tps - 1) / tps);      // every split gets at least one tile
     const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
-    // workspace: bf16 slice results [n_used][rows][hidden], then fp32 (m, l) [n_used][2][heads][rows]
+    // workspace: bf16 slice results [n_used][all_rows][hidden], then fp32 (m, l) [n_used][2][heads][all_rows]
     bf16* part_o = static_cast<bf16*>(ws);
-    float* part_ml = part_o ? reinterpret_cast<float*>(part_o + (size_t)n_used * rows * hidden) : nullptr;
+    float* part_ml = part_o ? reinterpret_cast<float*>(part_o + (size_t)n_used * all_rows * hidden) : nullptr;
     hipLaunchKernelGGL((attn_bf16_kernel<D, QB>), dim3((unsigned)(wg * n_used)), dim3(64 * kAttnWaves), 0, s,
                        static_cast<const bf16*>(q), ldq, static_cast<const bf16*>(k), ldk,
-                       static_cast<const bf16*>(v), hidden, seq_kv, rows, n_qtiles, n_used, tps,
-                       static_cast<bf16*>(o), ldo, part_o, part_ml, scale_log2);
+                       static_cast<const bf16*>(v), hidden, seq_kv, all_rows, n_qtiles, n_used, tps,
+                       static_cast<bf16*>(o), ldo, part_o, part_ml, scale_log2, rows, per_grp, kv_stride);
     if (n_used > 1) {
-      const int64_t units = rows * heads * (D / 8);
+      const int64_t units = all_rows * heads * (D / 8);
       hipLaunchKernelGGL(attn_combine_kernel<D>, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, s, part_o,
-                         part_ml, n_used, rows, heads, static_cast<bf16*>(o), ldo);
+                         part_ml, n_used, all_rows, heads, static_cast<bf16*>(o), ldo);
     }
   } else {
     const int n_qtiles = (int)((rows + 63) / 64);
-    hipLaunchKernelGGL(attn_f32_kernel<D>, dim3((unsigned)(n_qtiles * heads)), dim3(64), 0, s,
-                       static_cast<const float*>(q), ldq, static_cast<const float*>(k), ldk,
-                       static_cast<const float*>(v), ldv, seq_kv, rows, n_qtiles, static_cast<float*>(o), ldo,
-                       1.0f / sqrtf((float)D));
+    for (int64_t b = 0; b < batch; ++b)
+      hipLaunchKernelGGL(attn_f32_kernel<D>, dim3((unsigned)(n_qtiles * heads)), dim3(64), 0, s,
+                         static_cast<const float*>(q) + b * rows * ldq, ldq, static_cast<const float*>(k) + b * kv_stride,
+                         ldk, static_cast<const float*>(v) + b * kv_stride, ldv, seq_kv, rows, n_qtiles,
+                         static_cast<float*>(o) + b * rows * ldo, ldo, 1.0f / sqrtf((float)D));
   }
   return hipGetLastError();
 }
@@ -638,13 +658,20 @@ size_t attention_workspace_bytes(int64_t rows, int64_t hidden, int heads, int n_
 
 hipError_t launch_attention(const void* q, int64_t ldq, const void* k, int64_t ldk, const void* v, int64_t ldv,
                             int v_layout, int64_t hidden, int64_t seq_kv, int64_t rows, int heads, int head_dim,
-                            void* o, int64_t ldo, int dtype, void* ws, size_t ws_bytes, hipStream_t s) {
+                            void* o, int64_t ldo, int dtype, void* ws, size_t ws_bytes, hipStream_t s,
+                            int64_t batch, int64_t kv_stride) {
   (void)v_layout;
-  if (rows <= 0) return hipSuccess;
+  if (rows <= 0 || batch <= 0) return hipSuccess;
   switch (head_dim) {
-    case 64: return launch_attn_d<64>(q, ldq, k, ldk, v, ldv, hidden, seq_kv, rows, heads, o, ldo, dtype, ws, ws_bytes, s);
-    case 72: return launch_attn_d<72>(q, ldq, k, ldk, v, ldv, hidden, seq_kv, rows, heads, o, ldo, dtype, ws, ws_bytes, s);
-    default: return launch_attn_d<128>(q, ldq, k, ldk, v, ldv, hidden, seq_kv, rows, heads, o, ldo, dtype, ws, ws_bytes, s);
+    case 64:
+      return launch_attn_d<64>(q, ldq, k, ldk, v, ldv, hidden, seq_kv, rows, heads, o, ldo, dtype, ws, ws_bytes, s,
+                               batch, kv_stride);
+    case 72:
+      return launch_attn_d<72>(q, ldq, k, ldk, v, ldv, hidden, seq_kv, rows, heads, o, ldo, dtype, ws, ws_bytes, s,
+                               batch, kv_stride);
+    default:
+      return launch_attn_d<128>(q, ldq, k, ldk, v, ldv, hidden, seq_kv, rows, heads, o, ldo, dtype, ws, ws_bytes, s,
+                                batch, kv_stride);
   }
 }
 

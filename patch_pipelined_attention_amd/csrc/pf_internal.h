@@ -129,13 +129,16 @@ size_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k);
 constexpr int kMaxGemmSplit = 8;
 
 // `ws` (may be NULL) is scratch for the key-range split of small query grids; the split
-// count is chosen so its partial results fit in ws_bytes (NULL: no split).
+// count is chosen so its partial results fit in ws_bytes (NULL: no split).  `batch` samples of
+// `rows` query rows each in one launch: sample b's rows are rows b*rows .. of q and o, its K / V
+// buffers start b * kv_stride elements after k / v.
 hipError_t launch_attention(const void* q, int64_t ldq, const void* k, int64_t ldk, const void* v,
                             int64_t ldv, int v_layout, int64_t hidden, int64_t seq_kv, int64_t rows,
                             int heads, int head_dim, void* o, int64_t ldo, int dtype, void* ws,
-                            size_t ws_bytes, hipStream_t s);
+                            size_t ws_bytes, hipStream_t s, int64_t batch = 1, int64_t kv_stride = 0);
 
-// Scratch bytes the attention needs for `n_split` key-range splits of `rows` queries.
+// Scratch bytes the attention needs for `n_split` key-range splits of `rows` queries (all
+// samples' rows of a batched launch).
 size_t attention_workspace_bytes(int64_t rows, int64_t hidden, int heads, int n_split);
 
 // Upper bound of the split count launch_attention uses.

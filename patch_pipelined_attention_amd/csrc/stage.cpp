@@ -399,9 +399,9 @@ extern "C" pf_status stage_create(const pf_stage_config* cfg, pf_stage** out) {
   const size_t scr_qkv = round_up((size_t)(nb * st->s_alloc * 3 * h) * es, 256);
   const size_t scr_u = round_up((size_t)(nb * st->s_alloc * (rh > 0 ? rh : 1)) * es, 256);
 
-  // split partials for a patch or the text prefix of one sample (attention runs per sample;
-  // the warm-up pass fills the GPU unsplit)
-  const int64_t split_rows = std::max<int64_t>(st->patch_rows, cfg->seq_txt);
+  // split partials for a patch or the text prefix of every sample (the warm-up pass fills the
+  // GPU unsplit)
+  const int64_t split_rows = nb * std::max<int64_t>(st->patch_rows, cfg->seq_txt);
   st->attn_ws_bytes = cfg->dtype == PF_BF16 ? attention_workspace_bytes(split_rows, h, cfg->heads, kMaxAttnSplit) : 0;
   // k-split partials for the projections of a patch or the text prefix of all samples
   st->gemm_ws_bytes = 0;
@@ -583,14 +583,11 @@ static pf_status run_rows(pf_stage* st, int64_t off, int64_t n, float* x, int64_
           return stage_hip_fail(st, e, "kv splice");
       }
     }
-    for (int64_t b = 0; b < nb; ++b) {   // each sample attends over its own buffer
-      const char* q = qkv + (size_t)(b * n * 3 * h) * es;
-      char* o = (char*)st->o + (size_t)(b * n * h) * es;
-      if ((e = launch_attention(q, 3 * h, (char*)lm.k + b * st->kv_sample_bytes, h,
-                                (char*)lm.v + b * st->kv_sample_bytes, h, v_layout, h, st->s_kv, n, st->cfg.heads,
-                                st->cfg.head_dim, o, h, dt, st->attn_ws, st->attn_ws_bytes, s)) != hipSuccess)
-        return stage_hip_fail(st, e, "attention");
-    }
+    // one launch for every sample; each sample's queries attend over its own buffer
+    if ((e = launch_attention(qkv, 3 * h, lm.k, h, lm.v, h, v_layout, h, st->s_kv, n, st->cfg.heads,
+                              st->cfg.head_dim, st->o, h, dt, st->attn_ws, st->attn_ws_bytes, s, nb, kv_stride)) !=
+        hipSuccess)
+      return stage_hip_fail(st, e, "attention");
     if ((e = launch_gemm(st->o, h, lm.w_o, lm.b_o, rows, h, h, kEpiGatedResidual, x, h, mod + 2 * h, dt,
                          st->gemm_ws, st->gemm_ws_bytes, s, nullptr, &xg)) != hipSuccess)
       return stage_hip_fail(st, e, "out-proj gemm");

@@ -160,12 +160,15 @@ def test_cfg_pair_stage_chain(name):
     _run_pair_chain(shape, 3)
 
 
-def test_cfg_pair_patch_matches_single_stages():
+@pytest.mark.parametrize("name", ["c2s", "c2-full-L1", "c4-full-L1"])
+def test_cfg_pair_patch_matches_single_stages(name):
     """stage_run_patch on a pair equals the same micro-step on two single-sample stages, each
     with that sample's condition and buffer contents (up to the fp32 summation order of
-    projections that see twice the rows)."""
+    projections that see twice the rows, and of the key-range split: at full size the pair's
+    batched attention splits the keys in fewer slices than a single sample's)."""
     torch = torch_cuda()
-    shape = SMALL["c2s"]
+    shape = {"c2s": SMALL["c2s"], "c2-full-L1": dataclasses.replace(C2, num_layers=1),
+             "c4-full-L1": dataclasses.replace(C4, num_layers=1)}[name]
     inputs = synth.stage_inputs(shape)
     conds = list(synth.batch_conds(shape, inputs.c, 2))
     P, off = shape.patch_rows, shape.patch_offsets()[1]
@@ -185,7 +188,9 @@ def test_cfg_pair_patch_matches_single_stages():
         for b, st in enumerate(singles):
             st.set_cond(dev(torch, conds[b]))
             want = host(st.run_patch(off, P, dev(torch, x_patch)))
-            assert_close(got[b], want, f"pair patch sample {b} vs single stage")
+            # rel-L2 is the contract tolerance; max-abs only bounds gross errors, because at
+            # h = 3072 the large adaLN gates turn one-ulp bf16 flips into ~0.1 single-element moves
+            assert_close(got[b], want, f"pair patch sample {b} vs single stage", max_abs_tol=0.25)
             for l in range(shape.num_layers):
                 kp, vp = pair.kv_get(l, sample=b)
                 ks, vs = st.kv_get(l)

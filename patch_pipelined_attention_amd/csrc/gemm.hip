@@ -7,8 +7,9 @@
 // per lane, one token and 4 consecutive output features per 8-row group, so every
 // epilogue stores 4 contiguous values per access (8 B bf16 / 16 B fp32).
 //
-// Tiles: 128 x 128 with a 2-stage ring, two workgroups per CU.  Two deep-ring variants (256 x
-// 256 and 128 x 128, one workgroup per CU) can be forced for comparison.  Grids too
+// Tiles: 128 x 128 with a 2-stage ring, two workgroups per CU.  A 128 x 64 variant and two
+// deep-ring variants (256 x 256 and 128 x 128, one workgroup per CU) can be forced for
+// comparison.  Grids too
 // small to fill the GPU split k: every slice writes its fp32 partial tile and a reduce pass
 // sums the slices in order (deterministic) and applies the epilogue.  (A last-arriving-slice
 // merge inside the GEMM measured slower on MI355X: the partials cross XCDs, whose L2s are
@@ -527,7 +528,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 }
 
 // Launch plan of a bf16 GEMM: kernel and k-split count.
-enum GemmKind { kGemm128 = 0, kGemmDeep256 = 1, kGemmDeep128 = 2 };
+enum GemmKind { kGemm128 = 0, kGemmDeep256 = 1, kGemmDeep128 = 2, kGemm128x64 = 3 };
 struct GemmPlan {
   int kind;     // GemmKind: 128 x 128 2-stage (2 per CU), 256 x 256 4-stage, 128 x 128 8-stage (1 per CU)
   int split;    // k slices (1 = no split)
@@ -549,40 +550,54 @@ static int gemm_cus() {
 
 // The estimate only considers the 2-stage 128 x 128 kernel: with the grouped tile order it
 // measured faster than both deep-ring kernels at every DiT projection shape on MI355X (k from
-// 1152 to 12288, m from 1024 to 16384); the deep-ring kernels stay selectable for
-// experiments and tests through PF_GEMM_TILE.
+// 1152 to 12288, m from 1024 to 16384).  128 x 64 tiles beat it on narrow, short products
+// timed alone (the out-projections: PixArt patch 17.6 -> 12.1 us) but lost inside the stage,
+// where the weight tiles are no longer cache-resident and each is read by twice the
+// workgroups (C2 step 2.354 -> 2.377 ms).  The others stay selectable through PF_GEMM_TILE.
 // Smallest estimated time over tile size x k-split: rounds of resident workgroups x one
 // slice's time (a fixed cost plus its FLOPs at the tile's measured rate), plus writing and
 // re-reading the fp32 partials of a split.
-// The environment variable PF_GEMM_TILE=128, 256 or 128d (the 8-stage 128 x 128 kernel) forces
-// the kernel (the k-split is still chosen by the estimate); any other value, or none, leaves
-// both to the estimate.
+// The environment variable PF_GEMM_TILE=128, 128x64, 256 or 128d (the 8-stage 128 x 128 kernel)
+// forces the kernel (the k-split is still chosen by the estimate); any other value, or none,
+// leaves both to the plan.
 static int gemm_kind_override() {
   const char* v = std::getenv("PF_GEMM_TILE");
   if (!v) return -1;
   if (std::strcmp(v, "128") == 0) return kGemm128;
   if (std::strcmp(v, "256") == 0) return kGemmDeep256;
   if (std::strcmp(v, "128d") == 0) return kGemmDeep128;
+  if (std::strcmp(v, "128x64") == 0) return kGemm128x64;
   return -1;
+}
+
+// PF_GEMM_SPLIT=s forces s k slices where the workspace and k allow them (for measurements).
+static int gemm_split_override() {
+  const char* v = std::getenv("PF_GEMM_SPLIT");
+  if (!v) return 0;
+  const int sp = std::atoi(v);
+  return sp >= 1 && sp <= kMaxGemmSplit ? sp : 0;
 }
 
 static GemmPlan gemm_plan(int64_t m, int64_t n, int64_t k, size_t ws_bytes) {
   const int cus = gemm_cus();
   const int force = gemm_kind_override();
+  const int force_sp = gemm_split_override();
   GemmPlan best_plan{force >= 0 ? force : kGemm128, 1};
   double best = 1e30;
-  for (int kind = 0; kind <= 2; ++kind) {
+  for (int kind = 0; kind <= 3; ++kind) {
     if (force >= 0 ? kind != force : kind != kGemm128) continue;
-    const int64_t bt = kind == kGemmDeep256 ? 256 : 128;
-    const int64_t bk = kind == kGemm128 ? 64 : 32;
-    const int64_t tiles = ((m + bt - 1) / bt) * ((n + bt - 1) / bt);
-    const int64_t slots = kind == kGemm128 ? 2 * (int64_t)cus : (int64_t)cus;
+    const int64_t bt = kind == kGemmDeep256 ? 256 : 128;                // features per tile
+    const int64_t bm = kind == kGemm128x64 ? 64 : bt;                  // tokens per tile
+    const int64_t bk = kind == kGemm128 || kind == kGemm128x64 ? 64 : 32;
+    const int64_t tiles = ((m + bm - 1) / bm) * ((n + bt - 1) / bt);
+    const int64_t slots = kind == kGemm128 || kind == kGemm128x64 ? 2 * (int64_t)cus : (int64_t)cus;
     const double fixed_s = kind == kGemmDeep256 ? 30e-6 : 3e-6;
     const double rate = kind == kGemmDeep256 ? 6.7e12 : 1.65e12;      // FLOP/s of one resident workgroup
     for (int sp = 1; sp <= kMaxGemmSplit; ++sp) {
       if (sp > 1 && k / bk < 4LL * sp) break;
       if (sp > 1 && (size_t)sp * m * n * sizeof(float) > ws_bytes) break;
-      const double t = (double)((tiles * sp + slots - 1) / slots) * (fixed_s + 2.0 * bt * bt * (double)k / sp / rate) +
+      if (force_sp && sp != force_sp) continue;
+      const double t = (double)((tiles * sp + slots - 1) / slots) * (fixed_s + 2.0 * bt * bm * (double)k / sp / rate) +
                        (sp > 1 ? 2.0 * sp * (double)m * (double)n * sizeof(float) / 5.0e12 : 0.0);
       if (t < best * 0.98) {
         best = t;
@@ -601,6 +616,8 @@ size_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k) {
 template <int EPI, bool SPLIT>
 static constexpr auto gemm_small128 = gemm_bf16_kernel<128, 128, EPI, SPLIT>;
 template <int EPI, bool SPLIT>
+static constexpr auto gemm_small128x64 = gemm_bf16_kernel<128, 64, EPI, SPLIT>;
+template <int EPI, bool SPLIT>
 static constexpr auto gemm_deep256 = gemm_deep_kernel<256, 256, 4, EPI, SPLIT>;
 template <int EPI, bool SPLIT>
 static constexpr auto gemm_deep128 = gemm_deep_kernel<128, 128, 8, EPI, SPLIT>;
@@ -614,9 +631,10 @@ static void launch_gemm_epi(const void* a, int64_t lda, const void* w, const flo
     const bf16* Wt = static_cast<const bf16*>(w);
     const GemmPlan p = gemm_plan(m, n, k, ws ? ws_bytes : 0);
     const int bt = p.kind == kGemmDeep256 ? 256 : 128;
-    const int nkt = (int)(k / (p.kind == kGemm128 ? 64 : 32));
+    const int bm = p.kind == kGemm128x64 ? 64 : bt;
+    const int nkt = (int)(k / (p.kind == kGemm128 || p.kind == kGemm128x64 ? 64 : 32));
     const int tiles_n = (int)((n + bt - 1) / bt);
-    const int64_t tiles = (int64_t)tiles_n * ((m + bt - 1) / bt);
+    const int64_t tiles = (int64_t)tiles_n * ((m + bm - 1) / bm);
     const int kps = (nkt + p.split - 1) / p.split;
     const int used = (nkt + kps - 1) / kps;          // every slice gets at least one k tile
     float* part = static_cast<float*>(ws);
@@ -632,6 +650,7 @@ static void launch_gemm_epi(const void* a, int64_t lda, const void* w, const flo
   } while (0)
     if (p.kind == kGemmDeep256) PF_GEMM_LAUNCH(gemm_deep256);
     else if (p.kind == kGemmDeep128) PF_GEMM_LAUNCH(gemm_deep128);
+    else if (p.kind == kGemm128x64) PF_GEMM_LAUNCH(gemm_small128x64);
     else PF_GEMM_LAUNCH(gemm_small128);
 #undef PF_GEMM_LAUNCH
     if (used > 1) {

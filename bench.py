@@ -36,6 +36,8 @@ def parse():
     ap.add_argument("--config", default="c2")
     ap.add_argument("--batch", type=int, default=1,
                     help="samples per stage sharing the weights (2 = a classifier-free guidance pair)")
+    ap.add_argument("--denoiser", type=int, default=0, metavar="STEPS",
+                    help="also time a denoising loop of STEPS steps (1 warm-up) around the stage")
     ap.add_argument("--breakdown", action="store_true", help="also time every kernel of a patch-layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
@@ -181,6 +183,36 @@ def kernel_probes(torch, B, st, shape, layer_w, nb=1):
         probes["gemm_down"] = (lambda: B.pf_gemm(u, w["w2"], w["b2"], B.PF_EPI_GATED_RESIDUAL, x, gate=gate,
                                                  workspace=gws["down"]), 2.0 * r * R * h * h, "mfma")
     return probes
+
+
+def time_denoiser(torch, B, synth, st, shape, nb, steps):
+    """The loop around the stage (timestep MLP, patch embedding, final layer, guided DDIM) over
+    `steps` evenly spaced timesteps, the first a warm-up step; random weights, 4-channel latent,
+    2x2 patches on a square grid."""
+    import numpy as np
+    din = synth.denoiser_inputs(shape, batch=nb)
+    cfg = B.DenoiserConfig(in_channels=4, patch=2, grid_h=din.grid_h, grid_w=din.grid_w, freq_dim=256,
+                           train_steps=1000, beta_start=1e-4, beta_end=0.02)
+    d = B.denoiser_create(st.handle, cfg)
+    try:
+        B.denoiser_load_weights(d, {k: torch.from_numpy(v).cuda() for k, v in din.weights.items()})
+        z, y = torch.from_numpy(din.z).cuda(), torch.from_numpy(din.y).cuda()
+        ts = [int(t) for t in np.linspace(999, 0, steps).round()]
+        B.denoiser_run(d, z, y, ts, warmup_steps=1, guidance=4.5)      # untimed pass
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        B.denoiser_run(d, z, y, ts, warmup_steps=1, guidance=4.5)
+        e.record()
+        e.synchronize()
+        total = s.elapsed_time(e) / 1e3
+        assert bool(torch.isfinite(z).all()), "non-finite latent"
+    finally:
+        torch.cuda.synchronize()
+        B.denoiser_destroy(d)
+    return {"steps": steps, "warmup_steps": 1, "s_total": total, "ms_per_step": total / steps * 1e3,
+            "images_per_s": nb / total if nb == 1 else 1.0 / total,
+            "note": "whole denoising loop: condition, patch embedding, stage step, final layer, DDIM update"}
 
 
 def cpu_baseline(shape, inputs, budget_s):
@@ -379,6 +411,8 @@ def main():
     }
     if breakdown:
         rec["breakdown"] = breakdown
+    if args.denoiser:
+        rec["denoiser"] = time_denoiser(torch, B, synth, st, shape, nb, args.denoiser)
     st.close()
     del x, out
     torch.cuda.synchronize()

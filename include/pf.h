@@ -184,6 +184,69 @@ pf_status stage_get_kvbuf(pf_stage* st, int32_t layer, pf_kv_view* out);
 /* The same for sample `sample` (0 <= sample < batch) of a batched stage. */
 pf_status stage_get_kvbuf_sample(pf_stage* st, int32_t layer, int32_t sample, pf_kv_view* out);
 
+/* The stage's configuration as created (batch 0 reads back as 1). */
+pf_status stage_get_config(const pf_stage* st, pf_stage_config* out);
+
+/* ---------------------------------------------------------------------------------
+ * The denoising loop around one stage (one GPU holding every layer).  The pages put the
+ * stage inside a diffusion loop (PipeFusion "Core mechanisms" 2: consecutive steps see
+ * similar inputs, so each step reuses the previous step's K/V as stale context; only the
+ * start-up has none) without defining the loop; this is the plainest DiT reading.  Per step:
+ *   c_b  = W_t2 . SiLU(W_t1 . freq(t) + b_t1) + b_t2 + y_b,  freq(t) = [cos(t f_j), sin(t f_j)],
+ *          f_j = 10000^(-j / (freq_dim/2));
+ *   x_b  = [text rows x_txt_b (zeros if NULL); patches of z_b . W_patch^T + b_patch + pos],
+ *          patches p x p, row-major over the grid, values (c p + dy) p + dx; pos a fixed
+ *          2-D sine-cosine table (width quarters sin/cos of the patch row and column times
+ *          10000^(-k / (h/4)));
+ *   one stage_run_step(x, c) (PF_STEP_WARMUP for warm-up steps);
+ *   eps_b = unpatchify(LN(x_b image rows) (1 + scale_b) + shift_b) . W_out^T + b_out), with
+ *          (shift_b, scale_b) = SiLU(c_b) . W_fada^T + b_fada;
+ *   a pair (batch 2: sample 0 conditional, sample 1 unconditional, sharing the latent) uses
+ *          eps = eps_1 + guidance (eps_0 - eps_1) for both samples;
+ *   z_b <- sqrt(abar_next) (z_b - sqrt(1 - abar_t) eps) / sqrt(abar_t) + sqrt(1 - abar_next) eps
+ *          (DDIM, eta = 0), abar from a linear beta schedule, abar of "no next step" = 1.
+ * Everything around the stage runs in fp32.
+ * --------------------------------------------------------------------------------- */
+typedef struct pf_denoiser pf_denoiser;
+
+typedef struct pf_denoiser_config {
+  int32_t in_channels;   /* C: latent channels                                       */
+  int32_t patch;         /* p: patch edge                                            */
+  int32_t grid_h;        /* patch rows; grid_h * grid_w must equal the stage's seq_img */
+  int32_t grid_w;        /* patch columns                                            */
+  int32_t freq_dim;      /* even width of the timestep frequency features            */
+  int32_t train_steps;   /* T of the noise schedule; timesteps are in [0, T)         */
+  float beta_start;      /* linear betas from beta_start to beta_end                 */
+  float beta_end;
+} pf_denoiser_config;
+
+/* Device fp32 parameters (copied by denoiser_load_weights), [out, in] row-major. */
+typedef struct pf_denoiser_weights {
+  const float* w_patch; const float* b_patch;   /* [h, C p p], [h]         */
+  const float* w_t1;    const float* b_t1;      /* [h, freq_dim], [h]      */
+  const float* w_t2;    const float* b_t2;      /* [h, h], [h]             */
+  const float* w_fada;  const float* b_fada;    /* [2h, h], [2h]: shift, scale */
+  const float* w_out;   const float* b_out;     /* [C p p, h], [C p p]     */
+} pf_denoiser_weights;
+
+/* A loop around `st` (which it uses but does not own; destroy the denoiser first).  Allocates
+ * its weights, the position table and per-step buffers on the current device. */
+pf_status denoiser_create(pf_stage* st, const pf_denoiser_config* cfg, pf_denoiser** out);
+pf_status denoiser_destroy(pf_denoiser* d);
+pf_status denoiser_load_weights(pf_denoiser* d, const pf_denoiser_weights* w, void* stream);
+
+/* One step from timestep t to t_next (-1: the last step).  z: device fp32
+ * [batch, C, grid_h p, grid_w p], updated in place; y: device fp32 [batch, h]; x_txt: device
+ * fp32 [batch, seq_txt, h] or NULL.  The stage's weights must be loaded. */
+pf_status denoiser_step(pf_denoiser* d, float* z, const float* y, const float* x_txt, int32_t t,
+                        int32_t t_next, uint32_t flags, float guidance, void* stream);
+
+/* n_steps steps over the host array `timesteps` (strictly decreasing); the first
+ * warmup_steps (>= 1) run as warm-up steps. */
+pf_status denoiser_run(pf_denoiser* d, float* z, const float* y, const float* x_txt,
+                       const int32_t* timesteps, int32_t n_steps, int32_t warmup_steps, float guidance,
+                       void* stream);
+
 /* Thread-local text of the last non-OK status returned on this thread. */
 const char* pf_last_error(void);
 

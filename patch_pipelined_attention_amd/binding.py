@@ -51,6 +51,19 @@ class KVView(ctypes.Structure):
                 ("dtype", ctypes.c_int32), ("v_layout", ctypes.c_int32)]
 
 
+class DenoiserConfig(ctypes.Structure):
+    _fields_ = [("in_channels", ctypes.c_int32), ("patch", ctypes.c_int32), ("grid_h", ctypes.c_int32),
+                ("grid_w", ctypes.c_int32), ("freq_dim", ctypes.c_int32), ("train_steps", ctypes.c_int32),
+                ("beta_start", ctypes.c_float), ("beta_end", ctypes.c_float)]
+
+
+DENOISER_WEIGHT_NAMES = ("w_patch", "b_patch", "w_t1", "b_t1", "w_t2", "b_t2", "w_fada", "b_fada", "w_out", "b_out")
+
+
+class DenoiserWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in DENOISER_WEIGHT_NAMES]
+
+
 _lib = None
 
 _P = ctypes.c_void_p
@@ -65,6 +78,12 @@ _SIGNATURES = {
     "kvbuf_splice": [ctypes.POINTER(KVView), ctypes.POINTER(KVView), _I64, _I64, _P],
     "stage_get_kvbuf": [_P, _I32, ctypes.POINTER(KVView)],
     "stage_get_kvbuf_sample": [_P, _I32, _I32, ctypes.POINTER(KVView)],
+    "stage_get_config": [_P, ctypes.POINTER(StageConfig)],
+    "denoiser_create": [_P, ctypes.POINTER(DenoiserConfig), ctypes.POINTER(_P)],
+    "denoiser_destroy": [_P],
+    "denoiser_load_weights": [_P, ctypes.POINTER(DenoiserWeights), _P],
+    "denoiser_step": [_P, _P, _P, _P, _I32, _I32, _U32, _F, _P],
+    "denoiser_run": [_P, _P, _P, _P, ctypes.POINTER(ctypes.c_int32), _I32, _I32, _F, _P],
     "pf_ln_modulate": [_P, _I64, _I32, _P, _P, _F, _P, _I32, _P],
     "pf_gemm": [_P, _I64, _P, _P, _I64, _I64, _I64, _I32, _P, _I64, _P, _I32, _P, ctypes.c_uint64, _P],
     "pf_gemm_qkv_splice": [_P, _I64, _P, _P, _I64, _I64, _P, _I64, ctypes.POINTER(KVView), _I64, _P, ctypes.c_uint64,
@@ -249,3 +268,36 @@ def kv_view(k, v, rows: int, row_elems: int, v_layout: int, k_ld=None, v_ld=None
     return KVView(k=_ptr(k), v=_ptr(v), rows=rows, row_elems=row_elems,
                   k_ld=row_elems if k_ld is None else k_ld, v_ld=row_elems if v_ld is None else v_ld,
                   dtype=_dtype_code(k), v_layout=v_layout)
+
+
+def stage_get_config(handle) -> StageConfig:
+    c = StageConfig()
+    _check(lib().stage_get_config(handle, ctypes.byref(c)))
+    return c
+
+
+def denoiser_create(stage_handle, cfg: DenoiserConfig):
+    h = ctypes.c_void_p()
+    _check(lib().denoiser_create(stage_handle, ctypes.byref(cfg), ctypes.byref(h)))
+    return h
+
+
+def denoiser_destroy(handle) -> None:
+    _check(lib().denoiser_destroy(handle))
+
+
+def denoiser_load_weights(handle, w: dict, stream=None) -> None:
+    lw = DenoiserWeights(**{n: _ptr(w[n]) for n in DENOISER_WEIGHT_NAMES})
+    _check(lib().denoiser_load_weights(handle, ctypes.byref(lw), _stream(stream)))
+
+
+def denoiser_step(handle, z, y, t: int, t_next: int, warmup: bool = False, guidance: float = 1.0, x_txt=None,
+                  stream=None) -> None:
+    _check(lib().denoiser_step(handle, _ptr(z), _ptr(y), _ptr(x_txt), t, t_next, PF_STEP_WARMUP if warmup else 0,
+                               guidance, _stream(stream)))
+
+
+def denoiser_run(handle, z, y, timesteps, warmup_steps: int, guidance: float = 1.0, x_txt=None, stream=None) -> None:
+    ts = (ctypes.c_int32 * len(timesteps))(*[int(t) for t in timesteps])
+    _check(lib().denoiser_run(handle, _ptr(z), _ptr(y), _ptr(x_txt), ts, len(timesteps), warmup_steps, guidance,
+                              _stream(stream)))

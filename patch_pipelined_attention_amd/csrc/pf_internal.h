@@ -17,6 +17,9 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// Message returned by pf_last_error() on this thread (set by every failing call).
+void pf_set_last_error(const char* msg);
+
 constexpr int kDtypeBF16 = 0;
 constexpr int kDtypeFP32 = 1;
 constexpr int kLayoutRows = 0;
@@ -143,6 +146,20 @@ size_t attention_workspace_bytes(int64_t rows, int64_t hidden, int heads, int n_
 
 // Upper bound of the split count launch_attention uses.
 constexpr int kMaxAttnSplit = 8;
+
+// ---- the denoising loop around a stage (fp32) ----
+// out[b][j] = act(sum_i in[i] W[j, i] + bias[j]) + add[b][j]; in == NULL uses the frequency
+// features of timestep t; add == NULL needs batch == 1.
+hipError_t launch_gemv_f32(const float* in, double t, bool silu_in, const float* W, const float* bias, int k,
+                           int n_out, bool silu_out, const float* add, int batch, float* out, hipStream_t s);
+// x[b][row0 + s] = patch_{b,s} . Wp^T + bp + pos[s] for every patch s of every sample b.
+hipError_t launch_patch_embed(const float* z, int C, int p, int grid_w, int64_t n_patches, int hidden, const float* Wp,
+                              const float* bp, const float* pos, float* x, int64_t x_batch_stride, int64_t row0,
+                              int batch, hipStream_t s);
+// z = a z + e eps per latent element, eps unpatchified from v [batch][n_patches][C p p]
+// (guided: a pair's eps_1 + g (eps_0 - eps_1) for both samples).
+hipError_t launch_guided_ddim(float* z, const float* v, int C, int p, int grid_w, int64_t n_patches, int batch,
+                              bool guided, float g, float a, float e, hipStream_t s);
 
 // Bit copy of `len` rows x `row_elems` elements of K and of V (two matrices per call).
 hipError_t launch_splice(const KVDesc dst[2], const KVDesc src[2], int64_t row_elems, int64_t offset,

@@ -41,6 +41,8 @@ static pf_status hip_fail(hipError_t e, const char* what) {
 
 extern "C" const char* pf_last_error(void) { return g_last_error.c_str(); }
 
+void pf::pf_set_last_error(const char* msg) { g_last_error = msg; }
+
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 static size_t dtype_size(int dt) { return dt == PF_BF16 ? 2 : 4; }
 static bool dtype_ok(int dt) { return dt == PF_BF16 || dt == PF_FP32; }
@@ -676,6 +678,13 @@ extern "C" pf_status stage_get_kvbuf_sample(pf_stage* st, int32_t layer, int32_t
   out->v_ld = st->h;
   out->dtype = st->cfg.dtype;
   out->v_layout = st->cfg.dtype == PF_BF16 ? PF_LAYOUT_K8 : PF_LAYOUT_ROWS;
+  return PF_OK;
+}
+
+extern "C" pf_status stage_get_config(const pf_stage* st, pf_stage_config* out) {
+  if (!st || !out) return fail(PF_ERR_INVALID_ARG, "stage_get_config: null argument");
+  *out = st->cfg;
+  out->batch = (int32_t)st->batch;
   return PF_OK;
 }
 

@@ -94,6 +94,37 @@ def batch_conds(shape: StageShape, c: np.ndarray, batch: int) -> np.ndarray:
     return np.stack(rows)
 
 
+@dataclasses.dataclass
+class DenoiserInputs:
+    weights: dict          # name -> fp32 ndarray (pf_denoiser_weights order)
+    z: np.ndarray          # fp32 [batch, C, grid_h p, grid_w p]; a batch shares one latent
+    y: np.ndarray          # fp32 [batch, h]: one condition embedding per sample
+    grid_h: int
+    grid_w: int
+
+
+def denoiser_inputs(shape: StageShape, batch: int = 1, in_channels: int = 4, patch: int = 2, freq_dim: int = 256,
+                    seed: int | None = None) -> DenoiserInputs:
+    """Random weights of the loop around a stage (generator PCG64(shape.seed + 5000)), drawn in
+    the order w_patch, b_patch, w_t1, b_t1, w_t2, b_t2, w_fada, b_fada, w_out, b_out, then z and y.
+    Matrices ~ N(0, 1/fan_in) (w_fada ~ N(0, 0.02^2), as the blocks' adaLN), biases ~ N(0, 0.02^2),
+    z and y ~ N(0, 1).  The patch grid is square: grid_h = grid_w = sqrt(seq_img)."""
+    g = int(round(shape.seq_img ** 0.5))
+    if g * g != shape.seq_img:
+        raise ValueError("denoiser_inputs needs a square patch grid")
+    rng = np.random.Generator(np.random.PCG64(shape.seed + 5000 if seed is None else seed))
+    h, k = shape.hidden, in_channels * patch * patch
+    dims = {"w_patch": (h, k), "b_patch": (h,), "w_t1": (h, freq_dim), "b_t1": (h,), "w_t2": (h, h), "b_t2": (h,),
+            "w_fada": (2 * h, h), "b_fada": (2 * h,), "w_out": (k, h), "b_out": (k,)}
+    w = {}
+    for name, dim in dims.items():
+        std = 0.02 if (name.startswith("b") or name == "w_fada") else 1.0 / np.sqrt(dim[1])
+        w[name] = rng.standard_normal(dim, dtype=np.float32) * np.float32(std)
+    z1 = rng.standard_normal((in_channels, g * patch, g * patch), dtype=np.float32)
+    y = rng.standard_normal((batch, h), dtype=np.float32)
+    return DenoiserInputs(w, np.stack([z1] * batch), y, g, g)
+
+
 def randn(shape, seed: int, std: float = 1.0, bf16: bool = False) -> np.ndarray:
     """Plain seeded N(0, std^2) array (fp32), optionally rounded to bf16 values."""
     rng = np.random.Generator(np.random.PCG64(seed))

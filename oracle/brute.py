@@ -56,16 +56,43 @@ def silu(a):
     return a / (1.0 + math.exp(-a))
 
 
+def rms_heads_row(row, heads, d, gamma, eps=1e-6):
+    out = []
+    for j in range(heads):
+        seg = row[j * d:(j + 1) * d]
+        r = math.sqrt(math.fsum(a * a for a in seg) / d + eps)
+        out.extend(seg[i] / r * gamma[i] for i in range(d))
+    return out
+
+
+def rope_row(row, heads, d, angles):
+    out = list(row)
+    for j in range(heads):
+        for k in range(d // 2):
+            a0, a1 = row[j * d + 2 * k], row[j * d + 2 * k + 1]
+            cs, sn = math.cos(angles[k]), math.sin(angles[k])
+            out[j * d + 2 * k] = a0 * cs - a1 * sn
+            out[j * d + 2 * k + 1] = a0 * sn + a1 * cs
+    return out
+
+
 def stage_step(layers, kbuf, vbuf, x_all, c, *, heads, d, seq_txt, num_patches, mlp_ratio,
-               warmup, eps=1e-6):
-    """One step over all rows; kbuf/vbuf (lists of per-layer row lists) are updated in place."""
+               warmup, eps=1e-6, txt_layers=None, qk_norm=False, rope_angles=None):
+    """One step over all rows; kbuf/vbuf (lists of per-layer row lists) are updated in place.
+    txt_layers: weights of the text-prefix rows (dual stream); qk_norm: per-head RMSNorm of Q
+    and K with the row's weights' q_norm / k_norm; rope_angles: per buffer row, d/2 angles."""
     h = heads * d
     S = len(x_all)
-    mods = []
-    for W in layers:
-        sc = [silu(a) for a in c]
-        m = matvec_rows([sc], W["w_ada"], W["b_ada"])[0]
-        mods.append([m[i * h:(i + 1) * h] for i in range(6)])
+
+    def mods_of(ws):
+        out = []
+        for W in ws:
+            sc = [silu(a) for a in c]
+            m = matvec_rows([sc], W["w_ada"], W["b_ada"])[0]
+            out.append([m[i * h:(i + 1) * h] for i in range(6)])
+        return out
+    mods = mods_of(layers)
+    mods_t = mods_of(txt_layers) if txt_layers is not None else None
     if warmup:
         micro = [(0, S)]
     else:
@@ -74,21 +101,36 @@ def stage_step(layers, kbuf, vbuf, x_all, c, *, heads, d, seq_txt, num_patches, 
     out = [None] * S
     for off, n in micro:
         x = [list(r) for r in x_all[off:off + n]]
-        for l, W in enumerate(layers):
-            sh1, sc1, g1, sh2, sc2, g2 = mods[l]
-            h1 = [[a * (1.0 + sc1[i]) + sh1[i] for i, a in enumerate(layer_norm_row(r, eps))] for r in x]
-            qkv = matvec_rows(h1, W["w_qkv"], W["b_qkv"])
+        for l in range(len(layers)):
+            # every row on its own, with the weights and modulation of its stream
+            def wm(i):
+                if txt_layers is not None and off + i < seq_txt:
+                    return txt_layers[l], mods_t[l]
+                return layers[l], mods[l]
+            qs = []
             for i in range(n):
-                kbuf[l][off + i] = qkv[i][h:2 * h]
-                vbuf[l][off + i] = qkv[i][2 * h:3 * h]
-            o = attention([r[:h] for r in qkv], kbuf[l], vbuf[l], heads, d)
-            y = matvec_rows(o, W["w_o"], W["b_o"])
-            x = [[x[i][t] + g1[t] * y[i][t] for t in range(h)] for i in range(n)]
-            if mlp_ratio > 0:
-                h2 = [[a * (1.0 + sc2[i]) + sh2[i] for i, a in enumerate(layer_norm_row(r, eps))] for r in x]
-                u = [[gelu_tanh(a) for a in r] for r in matvec_rows(h2, W["w1"], W["b1"])]
-                y2 = matvec_rows(u, W["w2"], W["b2"])
-                x = [[x[i][t] + g2[t] * y2[i][t] for t in range(h)] for i in range(n)]
+                W, (sh1, sc1, g1, sh2, sc2, g2) = wm(i)
+                h1 = [a * (1.0 + sc1[t]) + sh1[t] for t, a in enumerate(layer_norm_row(x[i], eps))]
+                qkv = matvec_rows([h1], W["w_qkv"], W["b_qkv"])[0]
+                q, k = qkv[:h], qkv[h:2 * h]
+                if qk_norm:
+                    q, k = rms_heads_row(q, heads, d, W["q_norm"], eps), rms_heads_row(k, heads, d, W["k_norm"], eps)
+                if rope_angles is not None:
+                    q, k = rope_row(q, heads, d, rope_angles[off + i]), rope_row(k, heads, d, rope_angles[off + i])
+                kbuf[l][off + i] = k
+                vbuf[l][off + i] = qkv[2 * h:3 * h]
+                qs.append(q)
+            o = attention(qs, kbuf[l], vbuf[l], heads, d)
+            for i in range(n):
+                W, (sh1, sc1, g1, sh2, sc2, g2) = wm(i)
+                y = matvec_rows([o[i]], W["w_o"], W["b_o"])[0]
+                xi = [x[i][t] + g1[t] * y[t] for t in range(h)]
+                if mlp_ratio > 0:
+                    h2 = [a * (1.0 + sc2[t]) + sh2[t] for t, a in enumerate(layer_norm_row(xi, eps))]
+                    u = [gelu_tanh(a) for a in matvec_rows([h2], W["w1"], W["b1"])[0]]
+                    y2 = matvec_rows([u], W["w2"], W["b2"])[0]
+                    xi = [xi[t] + g2[t] * y2[t] for t in range(h)]
+                x[i] = xi
         for i in range(n):
             out[off + i] = x[i]
     return out

@@ -173,6 +173,26 @@ def attention(q, k, v, heads: int, head_dim: int, chunk: int = 256, round_p: boo
 # KV buffer splice
 # ---------------------------------------------------------------------------
 
+def rms_norm_heads(x, heads: int, head_dim: int, gamma, eps: float = 1e-6) -> np.ndarray:
+    """Per-head RMSNorm of rows of x ([n, heads*d]): each head's d values divided by
+    sqrt(mean of their squares + eps), times gamma [d] (shared by the heads)."""
+    x = np.asarray(x, F64).reshape(-1, heads, head_dim)
+    r = np.sqrt((x * x).mean(axis=-1, keepdims=True) + eps)
+    return (x / r * np.asarray(gamma, F64)).reshape(-1, heads * head_dim)
+
+
+def rope(x, heads: int, head_dim: int, angles) -> np.ndarray:
+    """Rotary embedding of rows of x ([n, heads*d]) with per-row angles [n, d/2]: in every head,
+    the pair (x[2k], x[2k+1]) is rotated by angles[row, k]."""
+    x = np.asarray(x, F64).reshape(-1, heads, head_dim // 2, 2)
+    a = np.asarray(angles, F64)[:, None, :]
+    c, s = np.cos(a), np.sin(a)
+    out = np.empty_like(x)
+    out[..., 0] = x[..., 0] * c - x[..., 1] * s
+    out[..., 1] = x[..., 0] * s + x[..., 1] * c
+    return out.reshape(-1, heads * head_dim)
+
+
 def splice(dst, src, offset: int):
     """In-place splice of a row block: dst[offset + i, :] = src[i, :] for i < len(src).
 
@@ -194,17 +214,32 @@ class StageOracle:
     """L contiguous layers of one stage with their per-layer full-spatial K/V buffers.
 
     layers: list of dicts with w_qkv [3h,h], b_qkv [3h], w_o [h,h], b_o [h], w1 [rh,h],
-    b1 [rh], w2 [h,rh], b2 [h], w_ada [6h,h], b_ada [6h] (any float dtype).
+    b1 [rh], w2 [h,rh], b2 [h], w_ada [6h,h], b_ada [6h] (any float dtype), plus q_norm and
+    k_norm [d] when qk_norm is set.
+
+    Options of the MM-DiT block variants (SD3 / Flux; readings, the pages name the models only):
+    * txt_layers: a second weight set of the same form for the text-prefix rows (dual stream);
+      the text rows and the image rows then use their own projections, modulation and gates,
+      and attention stays joint over every buffer row;
+    * qk_norm: per-head RMSNorm of Q and K (after the projection, before RoPE) with the layer's
+      (stream's) q_norm / k_norm scales;
+    * rope_angles [seq_kv, d/2]: rotary embedding of Q and K, buffer row r's pairs turned by
+      rope_angles[r].
+    In bf16 mode Q and K are rounded after the projection and again after norm / rotation (the
+    GPU stores them between the two).
     """
 
     def __init__(self, layers, *, heads: int, head_dim: int, seq_txt: int, seq_img: int,
                  num_patches: int, mlp_ratio: int, ln_eps: float = 1e-6, gelu: str = "tanh",
-                 mode: str = "exact"):
+                 mode: str = "exact", txt_layers=None, qk_norm: bool = False, rope_angles=None):
         if mode not in ("exact", "bf16", "bf16p"):
             raise ValueError(mode)
         if seq_img % num_patches:
             raise ValueError("seq_img must be a multiple of num_patches")
         self.W = [{k: np.asarray(a, F64) for k, a in lw.items()} for lw in layers]
+        self.Wt = None if txt_layers is None else [{k: np.asarray(a, F64) for k, a in lw.items()} for lw in txt_layers]
+        self.qk_norm = qk_norm
+        self.rope_angles = None if rope_angles is None else np.asarray(rope_angles, F64)
         self.heads, self.head_dim = heads, head_dim
         self.hidden = heads * head_dim
         self.seq_txt, self.seq_img, self.num_patches = seq_txt, seq_img, num_patches
@@ -217,6 +252,7 @@ class StageOracle:
         self.K = [np.zeros((self.seq_kv, self.hidden), F64) for _ in self.W]
         self.V = [np.zeros((self.seq_kv, self.hidden), F64) for _ in self.W]
         self.mod = None
+        self.mod_txt = None
         self.trace = None          # set to a list to record per-layer intermediates
 
     def _r(self, a):
@@ -224,6 +260,16 @@ class StageOracle:
 
     def set_cond(self, c):
         self.mod = [adaln(c, W["w_ada"], W["b_ada"]) for W in self.W]
+        if self.Wt is not None:
+            self.mod_txt = [adaln(c, W["w_ada"], W["b_ada"]) for W in self.Wt]
+
+    def _streams(self, rows_global):
+        """Index arrays (into rows_global) of the text-stream rows and the image-stream rows."""
+        rows_global = np.asarray(rows_global)
+        if self.Wt is None:
+            return [(np.arange(len(rows_global)), False)]
+        txt = rows_global < self.seq_txt
+        return [(np.nonzero(txt)[0], True), (np.nonzero(~txt)[0], False)]
 
     def run_rows(self, offset: int, rows: int, x, sample=None) -> np.ndarray:
         """Push buffer rows [offset, offset+rows) through every layer of the stage.
@@ -237,23 +283,58 @@ class StageOracle:
             raise RuntimeError("set_cond first")
         h, H, d = self.hidden, self.heads, self.head_dim
         x = np.array(x, F64).reshape(rows, h)
-        for l, W in enumerate(self.W):
-            shift1, scale1, gate1, shift2, scale2, gate2 = self.mod[l]
-            h1 = self._r(modulate(layer_norm(x, self.ln_eps), shift1, scale1))
-            qkv = self._r(linear(h1, W["w_qkv"], W["b_qkv"]))
-            q, k, v = qkv[:, :h], qkv[:, h:2 * h], qkv[:, 2 * h:]
-            splice(self.K[l], k, offset)
-            splice(self.V[l], v, offset)
+        rows_g = offset + np.arange(rows)
+        for l in range(len(self.W)):
+            def weights(txt):
+                return (self.Wt[l], self.mod_txt[l]) if txt else (self.W[l], self.mod[l])
+            q_all = np.empty((rows, h), F64)
+            rec = {"layer": l, "offset": offset, "h1": np.empty((rows, h)), "qkv": np.empty((rows, 3 * h))}
+            for idx, txt in self._streams(rows_g):
+                if len(idx) == 0:
+                    continue
+                W, mod = weights(txt)
+                shift1, scale1 = mod[0], mod[1]
+                h1 = self._r(modulate(layer_norm(x[idx], self.ln_eps), shift1, scale1))
+                qkv = self._r(linear(h1, W["w_qkv"], W["b_qkv"]))
+                q, k, v = qkv[:, :h], qkv[:, h:2 * h], qkv[:, 2 * h:]
+                if self.qk_norm:
+                    q = rms_norm_heads(q, H, d, W["q_norm"])
+                    k = rms_norm_heads(k, H, d, W["k_norm"])
+                if self.rope_angles is not None:
+                    q = rope(q, H, d, self.rope_angles[rows_g[idx]])
+                    k = rope(k, H, d, self.rope_angles[rows_g[idx]])
+                if self.qk_norm or self.rope_angles is not None:
+                    q, k = self._r(q), self._r(k)
+                self.K[l][rows_g[idx]] = k
+                self.V[l][rows_g[idx]] = v
+                q_all[idx] = q
+                rec["h1"][idx], rec["qkv"][idx] = h1, qkv
+            sel = np.arange(rows)
             if sample is not None and l == len(self.W) - 1:
-                q, x, qkv, h1 = q[sample], x[sample], qkv[sample], h1[sample]
-            o = self._r(attention(q, self.K[l], self.V[l], H, d, round_p=self.mode == "bf16p"))
-            x = x + gate1 * linear(o, W["w_o"], W["b_o"])
-            rec = {"layer": l, "offset": offset, "h1": h1, "qkv": qkv, "o": o, "x_attn": x.copy()}
+                sel = np.asarray(sample)
+                x = x[sel]
+            o = self._r(attention(q_all[sel], self.K[l], self.V[l], H, d, round_p=self.mode == "bf16p"))
+            x_attn = np.empty_like(x)
+            for idx, txt in self._streams(rows_g[sel]):
+                if len(idx) == 0:
+                    continue
+                W, mod = weights(txt)
+                x_attn[idx] = x[idx] + mod[2] * linear(o[idx], W["w_o"], W["b_o"])
+            x = x_attn
+            rec.update(o=o, x_attn=x.copy())
             if self.mlp_ratio > 0:
-                h2 = self._r(modulate(layer_norm(x, self.ln_eps), shift2, scale2))
-                u = self._r(self.gelu(linear(h2, W["w1"], W["b1"])))
-                x = x + gate2 * linear(u, W["w2"], W["b2"])
-                rec.update(h2=h2, u=u)
+                x_mlp = np.empty_like(x)
+                rec["h2"] = np.empty_like(x)
+                rec["u"] = np.empty((x.shape[0], self.mlp_ratio * h))
+                for idx, txt in self._streams(rows_g[sel]):
+                    if len(idx) == 0:
+                        continue
+                    W, mod = weights(txt)
+                    h2 = self._r(modulate(layer_norm(x[idx], self.ln_eps), mod[3], mod[4]))
+                    u = self._r(self.gelu(linear(h2, W["w1"], W["b1"])))
+                    x_mlp[idx] = x[idx] + mod[5] * linear(u, W["w2"], W["b2"])
+                    rec["h2"][idx], rec["u"][idx] = h2, u
+                x = x_mlp
             rec["x_out"] = x.copy()
             if self.trace is not None:
                 self.trace.append(rec)

@@ -407,3 +407,91 @@ def test_round_p_closed_forms():
     o = ref.attention(q, k, np.ones((40, 8)), 2, 4, round_p=True)
     assert np.abs(o - 1).max() <= 2.0 ** -8
     assert np.abs(o - 1).max() > 0              # the rounding is really applied
+
+
+# ---------------------------------------------------------------- MM-DiT block variants
+
+def test_rms_norm_heads_closed_forms():
+    H, d = 2, 4
+    x = np.array([[3.0, 3.0, 3.0, 3.0, 1.0, -1.0, 1.0, -1.0]])
+    g = np.array([1.0, 2.0, 0.5, -1.0])
+    y = ref.rms_norm_heads(x, H, d, g, eps=0.0)
+    np.testing.assert_allclose(y, [[1.0, 2.0, 0.5, -1.0, 1.0, -2.0, 0.5, 1.0]], rtol=1e-15)
+    z = np.random.default_rng(0).standard_normal((5, H * d))
+    np.testing.assert_allclose(ref.rms_norm_heads(7.5 * z, H, d, np.ones(d), eps=0.0),
+                               ref.rms_norm_heads(z, H, d, np.ones(d), eps=0.0), rtol=1e-13)   # scale invariant
+    assert np.allclose((ref.rms_norm_heads(z, H, d, np.ones(d), eps=0.0).reshape(5, H, d) ** 2).mean(-1), 1.0)
+
+
+def test_rope_closed_forms_and_relative_positions():
+    H, d = 2, 4
+    rng = np.random.default_rng(1)
+    q = rng.standard_normal((1, H * d))
+    np.testing.assert_array_equal(ref.rope(q, H, d, np.zeros((1, d // 2))), q)                 # angle 0
+    e = np.zeros((1, H * d)); e[0, 0] = 1.0
+    np.testing.assert_allclose(ref.rope(e, H, d, [[math.pi / 2, 0.0]])[0, :2], [0.0, 1.0], atol=1e-15)
+    r = ref.rope(q, H, d, rng.uniform(-5, 5, (1, d // 2)))
+    np.testing.assert_allclose(np.linalg.norm(r.reshape(H, d // 2, 2), axis=-1),
+                               np.linalg.norm(q.reshape(H, d // 2, 2), axis=-1), rtol=1e-13)   # rotation
+    # 1-axis positions theta_i = i * w_k: <rope(q, i), rope(k, j)> depends on i - j only
+    w = np.array([1.0, 0.1])
+    k = rng.standard_normal((1, H * d))
+    def dot(i, j):
+        return float((ref.rope(q, H, d, [i * w]) * ref.rope(k, H, d, [j * w])).sum())
+    assert dot(5, 2) == pytest.approx(dot(13, 10), rel=1e-12)
+    assert dot(5, 2) != pytest.approx(dot(5, 3), rel=1e-6)
+
+
+def _mmdit_layers(L, h, r, d, seed):
+    layers = _tiny_layers(L, h, r, seed)
+    rng = np.random.default_rng(seed + 50)
+    for W in layers:
+        W["q_norm"] = 1.0 + 0.3 * rng.standard_normal(d)
+        W["k_norm"] = 1.0 + 0.3 * rng.standard_normal(d)
+    return layers
+
+
+def test_mmdit_options_vs_brute_force_two_steps():
+    """Dual-stream weights, QK-RMSNorm and RoPE together: the numpy oracle against the loop
+    restatement on a tiny stage with a text prefix, warm-up then a drifted patched step."""
+    H, d, r, L, S_txt, S_img, M = 2, 4, 2, 2, 2, 8, 2
+    h, S = H * d, S_txt + S_img
+    img, txt = _mmdit_layers(L, h, r, d, 30), _mmdit_layers(L, h, r, d, 31)
+    rng = np.random.default_rng(12)
+    ang = rng.uniform(-3, 3, (S, d // 2))
+    st = ref.StageOracle(img, heads=H, head_dim=d, seq_txt=S_txt, seq_img=S_img, num_patches=M, mlp_ratio=r,
+                         txt_layers=txt, qk_norm=True, rope_angles=ang)
+    x = rng.standard_normal((S, h))
+    c = rng.standard_normal(h)
+    noise = [(rng.standard_normal((S, h)) * 0.1, rng.standard_normal((S, h)) * 0.1) for _ in range(L)]
+    kb = [[[0.0] * h for _ in range(S)] for _ in range(L)]
+    vb = [[[0.0] * h for _ in range(S)] for _ in range(L)]
+    lw = [{k: a.tolist() for k, a in W.items()} for W in img]
+    tw = [{k: a.tolist() for k, a in W.items()} for W in txt]
+    kw = dict(heads=H, d=d, seq_txt=S_txt, num_patches=M, mlp_ratio=r, txt_layers=tw, qk_norm=True,
+              rope_angles=ang.tolist())
+    np.testing.assert_allclose(st.step(x, c, warmup=True),
+                               brute.stage_step(lw, kb, vb, x.tolist(), c.tolist(), warmup=True, **kw),
+                               rtol=1e-11, atol=1e-11)
+    st.add_noise(noise)
+    for l, (nk, nv) in enumerate(noise):
+        kb[l] = (np.array(kb[l]) + nk).tolist()
+        vb[l] = (np.array(vb[l]) + nv).tolist()
+    np.testing.assert_allclose(st.step(x, c, warmup=False),
+                               brute.stage_step(lw, kb, vb, x.tolist(), c.tolist(), warmup=False, **kw),
+                               rtol=1e-11, atol=1e-11)
+    for l in range(L):
+        np.testing.assert_allclose(st.K[l], kb[l], rtol=1e-12, atol=1e-12)
+
+
+def test_dual_stream_with_equal_weights_is_the_single_stream_block():
+    H, d, r, L, S_txt, S_img, M = 2, 4, 2, 2, 3, 8, 2
+    h, S = H * d, S_txt + S_img
+    img = _mmdit_layers(L, h, r, d, 40)
+    rng = np.random.default_rng(13)
+    x, c = rng.standard_normal((S, h)), rng.standard_normal(h)
+    kw = dict(heads=H, head_dim=d, seq_txt=S_txt, seq_img=S_img, num_patches=M, mlp_ratio=r, qk_norm=True)
+    one = ref.StageOracle(img, **kw)
+    two = ref.StageOracle(img, txt_layers=[dict(W) for W in img], **kw)
+    for warm in (True, False):
+        np.testing.assert_array_equal(one.step(x, c, warmup=warm), two.step(x, c, warmup=warm))

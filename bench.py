@@ -38,6 +38,9 @@ def parse():
                     help="samples per stage sharing the weights (2 = a classifier-free guidance pair)")
     ap.add_argument("--denoiser", type=int, default=0, metavar="STEPS",
                     help="also time a denoising loop of STEPS steps (1 warm-up) around the stage")
+    ap.add_argument("--mmdit", action="store_true",
+                    help="Flux.1-style MM-DiT block: dual-stream text weights, QK-RMSNorm and RoPE "
+                         "(needs a config with a text prefix, e.g. c4)")
     ap.add_argument("--breakdown", action="store_true", help="also time every kernel of a patch-layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
@@ -139,10 +142,11 @@ def time_kernel_graph(torch, fn, iters=20, reps=5):
     return s.elapsed_time(e) / 1e3 / (reps * iters)
 
 
-def kernel_probes(torch, B, st, shape, layer_w, nb=1):
+def kernel_probes(torch, B, st, shape, layer_w, nb=1, mm=None):
     """Component launches at the exact shapes one patch-layer of the stage issues: the row
     kernels and projections over the nb * P rows of all samples, the attention per sample
-    (P query rows over that sample's buffer; the stage launches it nb times)."""
+    (P query rows over that sample's buffer; the stage launches it nb times).  `mm` (MM-DiT
+    inputs) adds the QK-norm / rotation step of one sample's patch."""
     h, P, S, r = shape.hidden, shape.patch_rows, shape.seq_kv, shape.mlp_ratio
     R = nb * P
     bf = torch.bfloat16
@@ -177,6 +181,15 @@ def kernel_probes(torch, B, st, shape, layer_w, nb=1):
         "gemm_out": (lambda: B.pf_gemm(o, w["w_o"], w["b_o"], B.PF_EPI_GATED_RESIDUAL, x, gate=gate,
                                        workspace=gws["out"]), 2.0 * R * h * h, "mfma"),
     }
+    if mm is not None:
+        d = shape.head_dim
+        gq = torch.from_numpy(mm.layers[0]["q_norm"]).cuda()
+        gk = torch.from_numpy(mm.layers[0]["k_norm"]).cuda()
+        ang = torch.from_numpy(mm.angles).cuda()
+        # Q and K of P rows read and written once (bf16), plus the rows' angles (fp32)
+        probes["qk_norm_rope"] = (lambda: B.pf_qk_norm_rope(qkv, kv, off, P, shape.heads, d, q_gamma=gq, k_gamma=gk,
+                                                            angles=ang, ldq=3 * h),
+                                  8.0 * P * h + 2.0 * P * d, "hbm")
     if r > 0:
         probes["gemm_up_gelu"] = (lambda: B.pf_gemm(h1, w["w1"], w["b1"], B.PF_EPI_GELU_TANH, u,
                                                     workspace=gws["up"]), 2.0 * r * R * h * h, "mfma")
@@ -215,7 +228,7 @@ def time_denoiser(torch, B, synth, st, shape, nb, steps):
             "note": "whole denoising loop: condition, patch embedding, stage step, final layer, DDIM update"}
 
 
-def cpu_baseline(shape, inputs, budget_s):
+def cpu_baseline(shape, inputs, budget_s, mm=None):
     """Oracle (fp64 numpy) on a bounded sample: whole patches through all layers with a full
     buffer, repeated until `budget_s` of CPU time; scaled to a step's rows."""
     import numpy as np
@@ -225,9 +238,10 @@ def cpu_baseline(shape, inputs, budget_s):
         threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     except Exception:
         threads = os.cpu_count() or 1
-    orc = ref.StageOracle(inputs.layers, heads=shape.heads, head_dim=shape.head_dim, seq_txt=shape.seq_txt,
-                          seq_img=shape.seq_img, num_patches=shape.num_patches, mlp_ratio=shape.mlp_ratio,
-                          mode="exact")
+    opts = {} if mm is None else dict(txt_layers=mm.txt_layers, qk_norm=True, rope_angles=mm.angles)
+    orc = ref.StageOracle(inputs.layers if mm is None else mm.layers, heads=shape.heads, head_dim=shape.head_dim,
+                          seq_txt=shape.seq_txt, seq_img=shape.seq_img, num_patches=shape.num_patches,
+                          mlp_ratio=shape.mlp_ratio, mode="exact", **opts)
     rng = np.random.default_rng(0)
     for l in range(shape.num_layers):           # a filled buffer (values do not change the work)
         orc.K[l][:] = rng.standard_normal(orc.K[l].shape)
@@ -309,8 +323,16 @@ def main():
     print(f"[bench] {shape.name}: generating inputs", file=sys.stderr, flush=True)
     inputs = synth.stage_inputs(shape)
     nb = args.batch
-    st = Stage(shape, batch=nb)
-    st.load(inputs.layers)
+    mm = None
+    if args.mmdit:
+        if shape.seq_txt < 1:
+            print(f"--mmdit needs a text prefix; {shape.name} has none", file=sys.stderr)
+            sys.exit(2)
+        mm = synth.mmdit_inputs(shape, inputs)
+    st = Stage(shape, batch=nb, qk_norm=mm is not None, dual_stream=mm is not None, rope=mm is not None)
+    st.load(inputs.layers if mm is None else mm.layers, None if mm is None else mm.txt_layers)
+    if mm is not None:
+        st.set_rope(mm.angles)
     if nb == 1:
         x = torch.from_numpy(inputs.x).cuda()
         c = torch.from_numpy(inputs.c).cuda()
@@ -349,7 +371,7 @@ def main():
     # dominant kernel: patch attention at the stage's launch shape
     wdev = {k: torch.from_numpy(np.ascontiguousarray(a)).cuda().to(torch.bfloat16 if k.startswith("w") else torch.float32)
             for k, a in inputs.layers[0].items()}
-    probes = kernel_probes(torch, B, st, shape, wdev, nb)
+    probes = kernel_probes(torch, B, st, shape, wdev, nb, mm)
     attn_fn, attn_flop, _ = probes["attention"]
     attn_s = time_kernel(torch, attn_fn, iters=max(10, args.steps))
     attn_tflops = attn_flop / attn_s / 1e12
@@ -374,6 +396,9 @@ def main():
     workload = (f"{shape.name}: one pipeline stage, {shape.num_layers} DiT blocks, hidden {shape.hidden}, "
                 f"{shape.heads}x{shape.head_dim} heads, MLP {shape.mlp_ratio}x, {shape.seq_kv} buffer rows, "
                 f"M={shape.num_patches} patches of {shape.patch_rows}")
+    if mm is not None:
+        workload += (", Flux.1-style MM-DiT blocks (dual-stream text weights, QK-RMSNorm, RoPE on a 3-axis "
+                     "position table)")
     if nb > 1:
         workload += f", batch of {nb} samples (classifier-free guidance pair: shared weights, own buffers)"
     rec = {
@@ -389,7 +414,7 @@ def main():
         "vs_baseline": None,
         "dtype": shape.dtype,
         "data": "synthetic",
-        "config": {"workload": workload, "batch": nb,
+        "config": {"workload": workload, "batch": nb, "block": "mmdit" if mm is not None else "dit",
                    "num_layers": shape.num_layers, "hidden": shape.hidden, "heads": shape.heads,
                    "head_dim": shape.head_dim, "seq_kv": shape.seq_kv, "num_patches": shape.num_patches,
                    "patch_rows": shape.patch_rows, "parallelism": "single GPU stage"},
@@ -418,7 +443,7 @@ def main():
     torch.cuda.synchronize()
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
-        rec["cpu_baseline"] = cpu_baseline(shape, inputs, args.cpu_seconds)
+        rec["cpu_baseline"] = cpu_baseline(shape, inputs, args.cpu_seconds, mm)
     print(json.dumps(rec), flush=True)
 
 

@@ -71,6 +71,20 @@ typedef enum pf_epilogue {
 #define PF_STEP_WARMUP 1u    /* stage_run_step flag: run all buffer rows as one patch */
 #define PF_MAX_STAGE_BATCH 8 /* largest pf_stage_config.batch                          */
 
+/* Block options (pf_stage_config.flags) of the MM-DiT variants the pages evaluate (SD3,
+ * Flux.1; Experiments section).  The pages name the models, not their blocks; these follow
+ * the published designs.  bf16 stages only.
+ *   PF_STAGE_QK_NORM:     per-head RMSNorm of Q and K after the projection (eps 1e-6), scaled
+ *                         by the layer's q_norm / k_norm vectors [d];
+ *   PF_STAGE_DUAL_STREAM: the text-prefix rows use a second weight set (stage_load_text_weights):
+ *                         their own projections, modulation and gates; attention stays joint
+ *                         over every buffer row;
+ *   PF_STAGE_ROPE:        rotary embedding of Q and K (after the norm): in every head, the pair
+ *                         (2k, 2k+1) of buffer row r turns by angles[r][k] (stage_set_rope). */
+#define PF_STAGE_QK_NORM 1u
+#define PF_STAGE_DUAL_STREAM 2u
+#define PF_STAGE_ROPE 4u
+
 typedef struct pf_stage_config {
   int32_t num_layers;   /* L >= 1: contiguous layers owned by this stage                   */
   int32_t hidden;       /* h = heads * head_dim                                             */
@@ -83,7 +97,7 @@ typedef struct pf_stage_config {
   int32_t dtype;        /* pf_dtype of weights, activations and KV buffers                  */
   int32_t gelu;         /* pf_gelu of the MLP                                               */
   float ln_eps;         /* LayerNorm epsilon (1e-6 is the DiT value)                        */
-  uint32_t flags;       /* reserved, must be 0                                              */
+  uint32_t flags;       /* PF_STAGE_* block options (0: the plain DiT block)                 */
   int32_t batch;        /* samples sharing the weights, 0 or 1 = one; 2 = a classifier-free  */
                         /* guidance pair.  Each sample has its own condition, rows and K/V  */
                         /* buffers; the projections run once over all samples' rows.       */
@@ -100,6 +114,7 @@ typedef struct pf_layer_weights {
   const void* w1;     const float* b1;      /* [rh, h], [rh]   */
   const void* w2;     const float* b2;      /* [h, rh], [h]    */
   const void* w_ada;  const float* b_ada;   /* [6h, h], [6h]   */
+  const float* q_norm; const float* k_norm; /* [d], [d] fp32 (PF_STAGE_QK_NORM only; else ignored) */
 } pf_layer_weights;
 
 /* A pair of K and V row buffers (device memory). */
@@ -135,6 +150,14 @@ pf_status stage_destroy(pf_stage* st);
  * copies once the stream has passed this call.  Every layer must be loaded before any
  * run call (else PF_ERR_STATE). */
 pf_status stage_load_weights(pf_stage* st, int32_t layer, const pf_layer_weights* w, void* stream);
+
+/* PF_STAGE_DUAL_STREAM: layer `layer`'s text-stream parameters (same form and rules as
+ * stage_load_weights); every layer's must be loaded before any run call. */
+pf_status stage_load_text_weights(pf_stage* st, int32_t layer, const pf_layer_weights* w, void* stream);
+
+/* PF_STAGE_ROPE: copy the rotation angles, device fp32 [seq_txt + seq_img, head_dim / 2]
+ * (row r: the angles of buffer row r).  Must be called before any run call. */
+pf_status stage_set_rope(pf_stage* st, const float* angles, void* stream);
 
 /* Compute every layer's adaLN modulation from the conditioning vectors `cond` (device,
  * fp32 [batch, h], one per sample): mod_l,b = SiLU(cond_b) . W_ada,l^T + b_ada,l, kept by the
@@ -314,6 +337,19 @@ pf_status pf_attention_workspace_size(int64_t rows, int32_t heads, int32_t head_
  * `dtype`, b_ada fp32 [6*hidden], mod fp32 [6*hidden]. */
 pf_status pf_adaln(const float* cond, const void* w_ada, const float* b_ada, int32_t hidden,
                    float* mod, int32_t dtype, void* stream);
+
+/* The MM-DiT options' step between the QKV projection and attention (bf16, in place): for
+ * every query row i < rows (q + i * ldq) and the K row of buffer row row_offset + i of kv, in
+ * every head (columns [j*d, (j+1)*d)): with PF_STAGE_QK_NORM, x / sqrt(mean(x^2) + 1e-6) times
+ * q_gamma (Q) or k_gamma (K), fp32 [head_dim]; then with PF_STAGE_ROPE, the pair (2k, 2k+1)
+ * turned by angles[row_offset + i][k] (fp32 [kv->rows, head_dim / 2], radians).  fp32
+ * arithmetic, one bf16 rounding per value.  `flags` holds only those two bits (0: nothing
+ * happens).  V and every other buffer row stay as they are.  q must not overlap the buffer.
+ * Requirements: kv->dtype bf16, row_elems == heads * head_dim <= 6144, ldq and k_ld multiples
+ * of 8; q, K, the gammas and the angles 16-byte aligned. */
+pf_status pf_qk_norm_rope(void* q, int64_t ldq, const pf_kv_view* kv, int64_t row_offset, int64_t rows,
+                          int32_t heads, int32_t head_dim, const float* q_gamma, const float* k_gamma,
+                          const float* angles, uint32_t flags, void* stream);
 
 #ifdef __cplusplus
 }

@@ -21,6 +21,7 @@ PF_GELU_TANH, PF_GELU_ERF = 0, 1
 PF_LAYOUT_ROWS, PF_LAYOUT_K8 = 0, 1
 PF_EPI_STORE, PF_EPI_GELU_TANH, PF_EPI_GELU_ERF, PF_EPI_GATED_RESIDUAL = range(4)
 PF_STEP_WARMUP = 1
+PF_STAGE_QK_NORM, PF_STAGE_DUAL_STREAM, PF_STAGE_ROPE = 1, 2, 4
 
 STATUS_NAMES = {0: "PF_OK", 1: "PF_ERR_INVALID_ARG", 2: "PF_ERR_UNSUPPORTED", 3: "PF_ERR_OOM",
                 4: "PF_ERR_STATE", 5: "PF_ERR_HIP"}
@@ -42,7 +43,7 @@ class StageConfig(ctypes.Structure):
 
 class LayerWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
-                ("w_qkv", "b_qkv", "w_o", "b_o", "w1", "b1", "w2", "b2", "w_ada", "b_ada")]
+                ("w_qkv", "b_qkv", "w_o", "b_o", "w1", "b1", "w2", "b2", "w_ada", "b_ada", "q_norm", "k_norm")]
 
 
 class KVView(ctypes.Structure):
@@ -72,6 +73,8 @@ _SIGNATURES = {
     "stage_create": [ctypes.POINTER(StageConfig), ctypes.POINTER(_P)],
     "stage_destroy": [_P],
     "stage_load_weights": [_P, _I32, ctypes.POINTER(LayerWeights), _P],
+    "stage_load_text_weights": [_P, _I32, ctypes.POINTER(LayerWeights), _P],
+    "stage_set_rope": [_P, _P, _P],
     "stage_set_cond": [_P, _P, _P],
     "stage_run_patch": [_P, _I64, _I64, _P, _P, _P],
     "stage_run_step": [_P, _P, _P, _P, _U32, _P],
@@ -90,6 +93,7 @@ _SIGNATURES = {
                            _P],
     "pf_gemm_workspace_size": [_I64, _I64, _I64, ctypes.POINTER(ctypes.c_uint64)],
     "pf_attention": [_P, _I64, ctypes.POINTER(KVView), _I64, _I64, _I32, _I32, _P, _I64, _P, ctypes.c_uint64, _P],
+    "pf_qk_norm_rope": [_P, _I64, ctypes.POINTER(KVView), _I64, _I64, _I32, _I32, _P, _P, _P, _U32, _P],
     "pf_attention_workspace_size": [_I64, _I32, _I32, ctypes.POINTER(ctypes.c_uint64)],
     "pf_adaln": [_P, _P, _P, _I32, _P, _I32, _P],
 }
@@ -167,6 +171,15 @@ def stage_load_weights(handle, layer: int, w: dict, stream=None) -> None:
     _check(lib().stage_load_weights(handle, layer, ctypes.byref(lw), _stream(stream)))
 
 
+def stage_load_text_weights(handle, layer: int, w: dict, stream=None) -> None:
+    lw = LayerWeights(**{k: _ptr(w.get(k)) for k, _ in LayerWeights._fields_})
+    _check(lib().stage_load_text_weights(handle, layer, ctypes.byref(lw), _stream(stream)))
+
+
+def stage_set_rope(handle, angles, stream=None) -> None:
+    _check(lib().stage_set_rope(handle, _ptr(angles), _stream(stream)))
+
+
 def stage_set_cond(handle, cond, stream=None) -> None:
     _check(lib().stage_set_cond(handle, _ptr(cond), _stream(stream)))
 
@@ -242,6 +255,16 @@ def pf_attention(q, kv: KVView, seq_kv: int, rows: int, heads: int, head_dim: in
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().pf_attention(_ptr(q), ldq, ctypes.byref(kv), seq_kv, rows, heads, head_dim, _ptr(o), ldo,
                               _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def pf_qk_norm_rope(q, kv: KVView, row_offset: int, rows: int, heads: int, head_dim: int, q_gamma=None,
+                    k_gamma=None, angles=None, ldq=None, stream=None) -> None:
+    """QK-RMSNorm (when both gammas are given) and rotary embedding (when angles are given) of
+    q's rows and K rows [row_offset, row_offset + rows) of kv, in place."""
+    ldq = q.stride(0) if ldq is None else ldq
+    flags = (PF_STAGE_QK_NORM if q_gamma is not None else 0) | (PF_STAGE_ROPE if angles is not None else 0)
+    _check(lib().pf_qk_norm_rope(_ptr(q), ldq, ctypes.byref(kv), row_offset, rows, heads, head_dim, _ptr(q_gamma),
+                                 _ptr(k_gamma), _ptr(angles), flags, _stream(stream)))
 
 
 def pf_attention_workspace_size(rows: int, heads: int, head_dim: int) -> int:

@@ -147,6 +147,13 @@ size_t attention_workspace_bytes(int64_t rows, int64_t hidden, int heads, int n_
 // Upper bound of the split count launch_attention uses.
 constexpr int kMaxAttnSplit = 8;
 
+// Q rows (q, row stride ldq) and K buffer rows [off, off + n) (row stride ldk; sample g's
+// buffer kv_stride elements after sample 0's) of nb samples, bf16 in place: per-head RMSNorm
+// times gq / gk (norm), then rotary pairs by angles[buffer row] (rope).
+hipError_t launch_qk_norm_rope(void* q, int64_t ldq, void* k, int64_t ldk, int64_t kv_stride, int64_t off, int64_t n,
+                               int64_t nb, int heads, int head_dim, const float* gq, const float* gk,
+                               const float* angles, bool norm, bool rope, hipStream_t s);
+
 // ---- the denoising loop around a stage (fp32) ----
 // out[b][j] = act(sum_i in[i] W[j, i] + bias[j]) + add[b][j]; in == NULL uses the frequency
 // features of timestep t; add == NULL needs batch == 1.

@@ -114,6 +114,151 @@ hipError_t launch_ln_modulate(const float* x, int64_t rows, int hidden, const fl
 }
 
 // ---------------------------------------------------------------------------------
+// Q and K of one part of a micro-step, in place (bf16): per (row, head), an optional RMSNorm
+// (eps 1e-6) times gamma [D], then an optional rotary embedding of the pairs (2k, 2k+1) by
+// angles[buffer row][k].  Rows r < nb * n: sample g = r / n, local row i = r - g n, buffer
+// row off + i; Q row r is at q + r * ldq, its K row at k + g * kv_stride + (off + i) * ldk
+// (the buffer, ROWS layout).
+//
+// One workgroup per row.  Thread t owns the 16-byte chunks c = t, t + 256, ... (8 values; D is
+// a multiple of 8, so a chunk never straddles two heads) of both the Q row and the K row, and
+// issues all its loads before any arithmetic: the kernel is bound by HBM, and a row's Q and K
+// (up to 24 KB) are in flight at once.  The per-head sums of squares go through LDS as one
+// partial per chunk, summed by each reader in chunk order (deterministic).
+// ---------------------------------------------------------------------------------
+constexpr int kQkChunks = kMaxHidden / 8 / 256;   // chunks per thread and matrix
+
+__device__ __forceinline__ float sumsq8(const bf16x8& v) {
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float f = (float)v[e];
+    s = fmaf(f, f, s);
+  }
+  return s;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void qk_norm_rope_kernel(bf16* __restrict__ q, int64_t ldq, bf16* __restrict__ k,
+                                                           int64_t ldk, int64_t kv_stride, int64_t off, int64_t n,
+                                                           int hidden, const float* __restrict__ gq,
+                                                           const float* __restrict__ gk,
+                                                           const float* __restrict__ angles, int do_norm,
+                                                           int do_rope) {
+  constexpr int kCph = D / 8;   // chunks per head
+  __shared__ float part[2][kMaxHidden / 8];
+  const int64_t r = blockIdx.x;
+  const int64_t g = r / n, i = r - g * n;
+  bf16* qr = q + r * ldq;
+  bf16* kr = k + g * kv_stride + (off + i) * ldk;
+  const float* ar = angles + (off + i) * (D / 2);
+  const int nch = hidden / 8;
+  bf16x8 vq[kQkChunks], vk[kQkChunks];
+  float4 an[kQkChunks];
+#pragma unroll
+  for (int j = 0; j < kQkChunks; ++j) {
+    const int c = threadIdx.x + j * 256;
+    if (c < nch) {
+      vq[j] = *reinterpret_cast<const bf16x8*>(qr + 8 * c);
+      vk[j] = *reinterpret_cast<const bf16x8*>(kr + 8 * c);
+      if (do_rope) an[j] = *reinterpret_cast<const float4*>(ar + (8 * c) % D / 2);
+    }
+  }
+  float rq[kQkChunks], rk[kQkChunks];
+  if (do_norm) {
+#pragma unroll
+    for (int j = 0; j < kQkChunks; ++j) {
+      const int c = threadIdx.x + j * 256;
+      if (c < nch) {
+        part[0][c] = sumsq8(vq[j]);
+        part[1][c] = sumsq8(vk[j]);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kQkChunks; ++j) {
+      const int c = threadIdx.x + j * 256;
+      const int h0 = c < nch ? c / kCph * kCph : 0;
+      float sq = 0.f, sk = 0.f;
+#pragma unroll
+      for (int m = 0; m < kCph; ++m) {
+        sq += part[0][h0 + m];
+        sk += part[1][h0 + m];
+      }
+      rq[j] = 1.0f / sqrtf(sq / (float)D + 1e-6f);
+      rk[j] = 1.0f / sqrtf(sk / (float)D + 1e-6f);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kQkChunks; ++j) {
+    const int c = threadIdx.x + j * 256;
+    if (c >= nch) continue;
+    float fq[8], fk[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      fq[e] = (float)vq[j][e];
+      fk[e] = (float)vk[j][e];
+    }
+    if (do_norm) {
+      const float4* g4q = reinterpret_cast<const float4*>(gq + (8 * c) % D);
+      const float4* g4k = reinterpret_cast<const float4*>(gk + (8 * c) % D);
+      const float4 q0 = g4q[0], q1 = g4q[1], k0 = g4k[0], k1 = g4k[1];
+      const float wq[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+      const float wk[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        fq[e] = fq[e] * rq[j] * wq[e];
+        fk[e] = fk[e] * rk[j] * wk[e];
+      }
+    }
+    if (do_rope) {
+      const float a[4] = {an[j].x, an[j].y, an[j].z, an[j].w};
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        float sn, cs;
+        sincosf(a[p], &sn, &cs);
+        const float q0 = fq[2 * p], q1 = fq[2 * p + 1], k0 = fk[2 * p], k1 = fk[2 * p + 1];
+        fq[2 * p] = q0 * cs - q1 * sn;
+        fq[2 * p + 1] = q0 * sn + q1 * cs;
+        fk[2 * p] = k0 * cs - k1 * sn;
+        fk[2 * p + 1] = k0 * sn + k1 * cs;
+      }
+    }
+    bf16x8 oq, ok;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      oq[e] = (bf16)fq[e];
+      ok[e] = (bf16)fk[e];
+    }
+    *reinterpret_cast<bf16x8*>(qr + 8 * c) = oq;
+    *reinterpret_cast<bf16x8*>(kr + 8 * c) = ok;
+  }
+}
+
+hipError_t launch_qk_norm_rope(void* q, int64_t ldq, void* k, int64_t ldk, int64_t kv_stride, int64_t off, int64_t n,
+                               int64_t nb, int heads, int head_dim, const float* gq, const float* gk,
+                               const float* angles, bool norm, bool rope, hipStream_t s) {
+  const int64_t rows = nb * n;
+  if (rows <= 0 || (!norm && !rope)) return hipSuccess;
+  const int hidden = heads * head_dim;
+  if (hidden > kMaxHidden || hidden % 8 != 0 || rows > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)rows);
+  bf16* qp = static_cast<bf16*>(q);
+  bf16* kp = static_cast<bf16*>(k);
+#define PF_QK_LAUNCH(D)                                                                                        \
+  hipLaunchKernelGGL(qk_norm_rope_kernel<D>, grid, dim3(256), 0, s, qp, ldq, kp, ldk, kv_stride, off, n, hidden, \
+                     gq, gk, angles, norm ? 1 : 0, rope ? 1 : 0)
+  switch (head_dim) {
+    case 64: PF_QK_LAUNCH(64); break;
+    case 72: PF_QK_LAUNCH(72); break;
+    case 128: PF_QK_LAUNCH(128); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef PF_QK_LAUNCH
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------
 // mod[j] = sum_i SiLU(c[i]) * W[j, i] + b[j] for j < 6h.  SiLU(c) is staged in LDS
 // once per block; one wavefront per output row streams that row of W with 16-byte loads.
 // ---------------------------------------------------------------------------------

@@ -234,6 +234,41 @@ extern "C" pf_status pf_gemm_qkv_splice(const void* a, int64_t lda, const void* 
   return e == hipSuccess ? PF_OK : hip_fail(e, "gemm_qkv_splice launch");
 }
 
+extern "C" pf_status pf_qk_norm_rope(void* q, int64_t ldq, const pf_kv_view* kv, int64_t row_offset, int64_t rows,
+                                     int32_t heads, int32_t head_dim, const float* q_gamma, const float* k_gamma,
+                                     const float* angles, uint32_t flags, void* stream) {
+  pf_status st = validate_kv_view(kv, "qk_norm_rope");
+  if (st != PF_OK) return st;
+  if (kv->dtype != PF_BF16) return fail(PF_ERR_UNSUPPORTED, "qk_norm_rope: bf16 only");
+  if (flags & ~(PF_STAGE_QK_NORM | PF_STAGE_ROPE)) return fail(PF_ERR_INVALID_ARG, "qk_norm_rope: bad flags");
+  if (head_dim != 64 && head_dim != 72 && head_dim != 128)
+    return fail(PF_ERR_UNSUPPORTED, "qk_norm_rope: head_dim %d not in {64, 72, 128}", head_dim);
+  if (heads <= 0 || kv->row_elems != (int64_t)heads * head_dim)
+    return fail(PF_ERR_INVALID_ARG, "qk_norm_rope: kv row_elems != heads * head_dim");
+  if (rows < 0 || row_offset < 0 || row_offset + rows > kv->rows)
+    return fail(PF_ERR_INVALID_ARG, "qk_norm_rope: rows [%lld, %lld) outside the buffer", (long long)row_offset,
+                (long long)(row_offset + rows));
+  if (kv->row_elems > kMaxHidden) return fail(PF_ERR_UNSUPPORTED, "qk_norm_rope: heads * head_dim > %d", kMaxHidden);
+  if (!q) return fail(PF_ERR_INVALID_ARG, "qk_norm_rope: null q");
+  if (ldq < kv->row_elems || (ldq & 7) || (kv->k_ld & 7) || !aligned16(q) || !aligned16(kv->k))
+    return fail(PF_ERR_INVALID_ARG,
+                "qk_norm_rope: ldq / k_ld must be multiples of 8 (ldq >= row_elems), q and K 16-byte aligned");
+  const bool norm = (flags & PF_STAGE_QK_NORM) != 0, rope = (flags & PF_STAGE_ROPE) != 0;
+  if ((norm && (!q_gamma || !k_gamma)) || (rope && !angles))
+    return fail(PF_ERR_INVALID_ARG, "qk_norm_rope: null gamma or angles for the requested flags");
+  if ((norm && (!aligned16(q_gamma) || !aligned16(k_gamma))) || (rope && !aligned16(angles)))
+    return fail(PF_ERR_INVALID_ARG, "qk_norm_rope: gammas and angles must be 16-byte aligned");
+  if (rows == 0 || flags == 0) return PF_OK;
+  uintptr_t klo, khi;
+  view_extent(kv, false, row_offset, rows, &klo, &khi);
+  const uintptr_t q0 = (uintptr_t)q, q1 = q0 + (uintptr_t)(((rows - 1) * ldq + kv->row_elems) * 2);
+  if (q0 < khi && klo < q1) return fail(PF_ERR_INVALID_ARG, "qk_norm_rope: q overlaps the K rows");
+  if ((st = check_device()) != PF_OK) return st;
+  hipError_t e = launch_qk_norm_rope(q, ldq, kv->k, kv->k_ld, 0, row_offset, rows, 1, heads, head_dim, q_gamma,
+                                     k_gamma, angles, norm, rope, (hipStream_t)stream);
+  return e == hipSuccess ? PF_OK : hip_fail(e, "qk_norm_rope launch");
+}
+
 extern "C" pf_status pf_gemm_workspace_size(int64_t m, int64_t n, int64_t k, uint64_t* bytes) {
   if (!bytes) return fail(PF_ERR_INVALID_ARG, "gemm_workspace_size: null out");
   if (m < 0 || n <= 0 || k <= 0) return fail(PF_ERR_INVALID_ARG, "gemm_workspace_size: bad sizes");
@@ -296,12 +331,19 @@ extern "C" pf_status kvbuf_splice(const pf_kv_view* dst, const pf_kv_view* src, 
 // ------------------------------------------------------------------------------------
 // the stage
 // ------------------------------------------------------------------------------------
-struct LayerMem {
+// One stream's parameters of a layer (the image stream; with PF_STAGE_DUAL_STREAM also the
+// text stream) and the modulation computed from them for the current condition.
+struct WeightSet {
   void *w_qkv, *w_o, *w1, *w2, *w_ada;
   float *b_qkv, *b_o, *b1, *b2, *b_ada;
-  void *k, *v;  // sample 0's K and V buffers; sample b's are b * kv_sample_bytes further on
-  float* mod;   // [batch][6h]: shift1, scale1, gate1, shift2, scale2, gate2 per sample
+  float *q_norm, *k_norm;   // [d] each (PF_STAGE_QK_NORM)
+  float* mod;               // [batch][6h]: shift1, scale1, gate1, shift2, scale2, gate2 per sample
   bool loaded;
+};
+
+struct LayerMem {
+  WeightSet img, txt;   // txt is used only with PF_STAGE_DUAL_STREAM
+  void *k, *v;  // sample 0's K and V buffers; sample b's are b * kv_sample_bytes further on
 };
 
 struct pf_stage {
@@ -315,6 +357,8 @@ struct pf_stage {
   void* kvmem = nullptr;
   void* scratch = nullptr;
   float* modmem = nullptr;
+  float* rope = nullptr;     // [s_kv, d/2] rotation angles (PF_STAGE_ROPE)
+  bool rope_set = false;
   void *h1, *qkv, *o, *u;
   void* attn_ws = nullptr;   // key-range split partials of the patch attention
   size_t attn_ws_bytes = 0;
@@ -343,7 +387,12 @@ static pf_status validate_config(const pf_stage_config* c) {
   if (!dtype_ok(c->dtype)) return fail(PF_ERR_INVALID_ARG, "stage_create: bad dtype");
   if (c->gelu != PF_GELU_TANH && c->gelu != PF_GELU_ERF) return fail(PF_ERR_INVALID_ARG, "stage_create: bad gelu");
   if (!(c->ln_eps > 0.f) || !std::isfinite(c->ln_eps)) return fail(PF_ERR_INVALID_ARG, "stage_create: bad ln_eps");
-  if (c->flags != 0) return fail(PF_ERR_INVALID_ARG, "stage_create: flags must be 0");
+  if (c->flags & ~(PF_STAGE_QK_NORM | PF_STAGE_DUAL_STREAM | PF_STAGE_ROPE))
+    return fail(PF_ERR_INVALID_ARG, "stage_create: unknown flags 0x%x", c->flags);
+  if (c->flags != 0 && c->dtype != PF_BF16)
+    return fail(PF_ERR_UNSUPPORTED, "stage_create: block options need a bf16 stage");
+  if ((c->flags & PF_STAGE_DUAL_STREAM) && c->seq_txt < 1)
+    return fail(PF_ERR_INVALID_ARG, "stage_create: PF_STAGE_DUAL_STREAM needs a text prefix (seq_txt >= 1)");
   if (c->batch < 0 || c->batch > PF_MAX_STAGE_BATCH)
     return fail(PF_ERR_INVALID_ARG, "stage_create: batch %d outside [0, %d]", c->batch, PF_MAX_STAGE_BATCH);
   if (c->hidden > kMaxHidden) return fail(PF_ERR_UNSUPPORTED, "stage_create: hidden > %d", kMaxHidden);
@@ -361,6 +410,8 @@ static void free_stage_mem(pf_stage* st) {
   if (st->kvmem) (void)hipFree(st->kvmem);
   if (st->scratch) (void)hipFree(st->scratch);
   if (st->modmem) (void)hipFree(st->modmem);
+  if (st->rope) (void)hipFree(st->rope);
+  st->rope = nullptr;
   if (st->attn_ws) (void)hipFree(st->attn_ws);
   if (st->gemm_ws) (void)hipFree(st->gemm_ws);
   st->attn_ws = st->gemm_ws = nullptr;
@@ -388,12 +439,18 @@ extern "C" pf_status stage_create(const pf_stage_config* cfg, pf_stage** out) {
   st->es = dtype_size(cfg->dtype);
   const int64_t h = st->h, rh = st->rh, L = cfg->num_layers, nb = st->batch;
   const size_t es = st->es;
+  const int64_t n_sets = (cfg->flags & PF_STAGE_DUAL_STREAM) ? 2 : 1;   // weight sets (streams) per layer
+  const int64_t d = cfg->head_dim;
 
-  // weights: matrices then fp32 biases, each 256-byte aligned
+  // weights: matrices then fp32 biases, each 256-byte aligned, then the two norm scales
   const size_t mats[5] = {(size_t)(3 * h * h), (size_t)(h * h), (size_t)(rh * h), (size_t)(h * rh), (size_t)(6 * h * h)};
   const size_t biases[5] = {(size_t)(3 * h), (size_t)h, (size_t)rh, (size_t)h, (size_t)(6 * h)};
-  size_t per_layer = 0;
-  for (int i = 0; i < 5; ++i) per_layer += round_up(mats[i] * es, 256) + round_up(biases[i] * 4, 256);
+  size_t per_set = 0;
+  for (int i = 0; i < 5; ++i) per_set += round_up(mats[i] * es, 256) + round_up(biases[i] * 4, 256);
+  const size_t norm_bytes = round_up((size_t)d * 4, 256);
+  per_set += 2 * norm_bytes;
+  const size_t per_layer = per_set * (size_t)n_sets;
+  const size_t rope_bytes = (cfg->flags & PF_STAGE_ROPE) ? (size_t)(st->s_kv * (d / 2)) * 4 : 0;
   const size_t kv_mat = round_up((size_t)(st->s_alloc * h) * es, 256);
   st->kv_sample_bytes = 2 * kv_mat;   // per layer: K0, V0, K1, V1, ...
   // scratch for a micro-step of up to s_kv rows of every sample
@@ -422,7 +479,8 @@ extern "C" pf_status stage_create(const pf_stage_config* cfg, pf_stage** out) {
       (st->gemm_ws_bytes && (e = hipMalloc(&st->gemm_ws, st->gemm_ws_bytes)) != hipSuccess) ||
       (e = hipMalloc(&st->kvmem, 2 * kv_mat * L * nb)) != hipSuccess ||
       (e = hipMalloc(&st->scratch, 2 * scr_h + scr_qkv + scr_u)) != hipSuccess ||
-      (e = hipMalloc((void**)&st->modmem, sizeof(float) * 6 * h * L * nb)) != hipSuccess) {
+      (e = hipMalloc((void**)&st->modmem, sizeof(float) * 6 * h * L * nb * n_sets)) != hipSuccess ||
+      (rope_bytes && (e = hipMalloc((void**)&st->rope, rope_bytes)) != hipSuccess)) {
     free_stage_mem(st);
     delete st;
     (void)hipGetLastError();
@@ -431,7 +489,7 @@ extern "C" pf_status stage_create(const pf_stage_config* cfg, pf_stage** out) {
   }
   // zero the KV buffers (including the padding rows past seq_kv) once, synchronously
   if ((e = hipMemset(st->kvmem, 0, 2 * kv_mat * L * nb)) != hipSuccess ||
-      (e = hipMemset(st->modmem, 0, sizeof(float) * 6 * h * L * nb)) != hipSuccess ||
+      (e = hipMemset(st->modmem, 0, sizeof(float) * 6 * h * L * nb * n_sets)) != hipSuccess ||
       (e = hipDeviceSynchronize()) != hipSuccess) {
     free_stage_mem(st);
     delete st;
@@ -442,19 +500,27 @@ extern "C" pf_status stage_create(const pf_stage_config* cfg, pf_stage** out) {
   st->layers.resize(L);
   for (int64_t l = 0; l < L; ++l) {
     LayerMem& lm = st->layers[l];
-    void** mp[5] = {&lm.w_qkv, &lm.w_o, &lm.w1, &lm.w2, &lm.w_ada};
-    float** bp[5] = {&lm.b_qkv, &lm.b_o, &lm.b1, &lm.b2, &lm.b_ada};
-    for (int i = 0; i < 5; ++i) {
-      *mp[i] = wp;
-      wp += round_up(mats[i] * es, 256);
-      *bp[i] = (float*)wp;
-      wp += round_up(biases[i] * 4, 256);
+    for (int64_t set = 0; set < 2; ++set) {
+      WeightSet& ws = set == 0 ? lm.img : lm.txt;
+      ws = WeightSet{};
+      if (set >= n_sets) continue;
+      void** mp[5] = {&ws.w_qkv, &ws.w_o, &ws.w1, &ws.w2, &ws.w_ada};
+      float** bp[5] = {&ws.b_qkv, &ws.b_o, &ws.b1, &ws.b2, &ws.b_ada};
+      for (int i = 0; i < 5; ++i) {
+        *mp[i] = wp;
+        wp += round_up(mats[i] * es, 256);
+        *bp[i] = (float*)wp;
+        wp += round_up(biases[i] * 4, 256);
+      }
+      ws.q_norm = (float*)wp;
+      wp += norm_bytes;
+      ws.k_norm = (float*)wp;
+      wp += norm_bytes;
+      ws.mod = st->modmem + 6 * h * nb * (l * n_sets + set);
     }
     lm.k = kp;
     lm.v = kp + kv_mat;
     kp += 2 * kv_mat * nb;
-    lm.mod = st->modmem + 6 * h * nb * l;
-    lm.loaded = false;
   }
   char* sp = (char*)st->scratch;
   st->h1 = sp;
@@ -492,27 +558,30 @@ static pf_status stage_hip_fail(pf_stage* st, hipError_t e, const char* what) {
   return hip_fail(e, what);
 }
 
-extern "C" pf_status stage_load_weights(pf_stage* st, int32_t layer, const pf_layer_weights* w, void* stream) {
-  pf_status s = check_stage(st, "stage_load_weights");
+static pf_status load_set(pf_stage* st, int32_t layer, const pf_layer_weights* w, bool txt, void* stream,
+                          const char* who) {
+  pf_status s = check_stage(st, who);
   if (s != PF_OK) return s;
-  if (layer < 0 || layer >= st->cfg.num_layers) return fail(PF_ERR_INVALID_ARG, "stage_load_weights: bad layer %d", layer);
-  if (!w) return fail(PF_ERR_INVALID_ARG, "stage_load_weights: null weights");
+  if (layer < 0 || layer >= st->cfg.num_layers) return fail(PF_ERR_INVALID_ARG, "%s: bad layer %d", who, layer);
+  if (!w) return fail(PF_ERR_INVALID_ARG, "%s: null weights", who);
   const bool mlp = st->rh > 0;
+  const bool qkn = (st->cfg.flags & PF_STAGE_QK_NORM) != 0;
   if (!w->w_qkv || !w->b_qkv || !w->w_o || !w->b_o || !w->w_ada || !w->b_ada ||
-      (mlp && (!w->w1 || !w->b1 || !w->w2 || !w->b2)))
-    return fail(PF_ERR_INVALID_ARG, "stage_load_weights: null weight pointer");
-  const int64_t h = st->h, rh = st->rh;
+      (mlp && (!w->w1 || !w->b1 || !w->w2 || !w->b2)) || (qkn && (!w->q_norm || !w->k_norm)))
+    return fail(PF_ERR_INVALID_ARG, "%s: null weight pointer", who);
+  const int64_t h = st->h, rh = st->rh, d = st->cfg.head_dim;
   const size_t es = st->es;
-  LayerMem& lm = st->layers[layer];
-  struct Cp { void* dst; const void* src; size_t bytes; } cps[10] = {
+  WeightSet& lm = txt ? st->layers[layer].txt : st->layers[layer].img;
+  struct Cp { void* dst; const void* src; size_t bytes; } cps[12] = {
       {lm.w_qkv, w->w_qkv, (size_t)(3 * h * h) * es}, {lm.b_qkv, w->b_qkv, (size_t)(3 * h) * 4},
       {lm.w_o, w->w_o, (size_t)(h * h) * es},         {lm.b_o, w->b_o, (size_t)h * 4},
       {lm.w1, w->w1, (size_t)(rh * h) * es},          {lm.b1, w->b1, (size_t)rh * 4},
       {lm.w2, w->w2, (size_t)(h * rh) * es},          {lm.b2, w->b2, (size_t)h * 4},
-      {lm.w_ada, w->w_ada, (size_t)(6 * h * h) * es}, {lm.b_ada, w->b_ada, (size_t)(6 * h) * 4}};
-  for (int i = 0; i < 10; ++i) {
+      {lm.w_ada, w->w_ada, (size_t)(6 * h * h) * es}, {lm.b_ada, w->b_ada, (size_t)(6 * h) * 4},
+      {lm.q_norm, w->q_norm, (size_t)d * 4},          {lm.k_norm, w->k_norm, (size_t)d * 4}};
+  for (int i = 0; i < 12; ++i) {
     const Cp& c = cps[i];
-    if (c.bytes == 0 || (!mlp && i >= 4 && i < 8)) continue;   // no MLP parameters when r == 0
+    if (c.bytes == 0 || (!mlp && i >= 4 && i < 8) || (!qkn && i >= 10)) continue;   // unused parameters
     hipError_t e = hipMemcpyAsync(c.dst, c.src, c.bytes, hipMemcpyDeviceToDevice, (hipStream_t)stream);
     if (e != hipSuccess) return stage_hip_fail(st, e, "stage_load_weights: hipMemcpyAsync");
   }
@@ -520,18 +589,54 @@ extern "C" pf_status stage_load_weights(pf_stage* st, int32_t layer, const pf_la
   return PF_OK;
 }
 
+extern "C" pf_status stage_load_weights(pf_stage* st, int32_t layer, const pf_layer_weights* w, void* stream) {
+  return load_set(st, layer, w, false, stream, "stage_load_weights");
+}
+
+extern "C" pf_status stage_load_text_weights(pf_stage* st, int32_t layer, const pf_layer_weights* w, void* stream) {
+  if (st && !(st->cfg.flags & PF_STAGE_DUAL_STREAM))
+    return fail(PF_ERR_INVALID_ARG, "stage_load_text_weights: the stage was created without PF_STAGE_DUAL_STREAM");
+  return load_set(st, layer, w, true, stream, "stage_load_text_weights");
+}
+
+extern "C" pf_status stage_set_rope(pf_stage* st, const float* angles, void* stream) {
+  pf_status s = check_stage(st, "stage_set_rope");
+  if (s != PF_OK) return s;
+  if (!(st->cfg.flags & PF_STAGE_ROPE))
+    return fail(PF_ERR_INVALID_ARG, "stage_set_rope: the stage was created without PF_STAGE_ROPE");
+  if (!angles) return fail(PF_ERR_INVALID_ARG, "stage_set_rope: null angles");
+  if ((uintptr_t)angles & 3u) return fail(PF_ERR_INVALID_ARG, "stage_set_rope: angles must be 4-byte aligned");
+  if ((uintptr_t)angles < (uintptr_t)st->rope + (st->s_kv * (st->cfg.head_dim / 2)) * sizeof(float) &&
+      (uintptr_t)st->rope < (uintptr_t)angles + (st->s_kv * (st->cfg.head_dim / 2)) * sizeof(float))
+    return fail(PF_ERR_INVALID_ARG, "stage_set_rope: angles overlap the stage's table");
+  const size_t bytes = (size_t)(st->s_kv * (st->cfg.head_dim / 2)) * sizeof(float);
+  hipError_t e = hipMemcpyAsync(st->rope, angles, bytes, hipMemcpyDeviceToDevice, (hipStream_t)stream);
+  if (e != hipSuccess) return stage_hip_fail(st, e, "stage_set_rope: hipMemcpyAsync");
+  st->rope_set = true;
+  return PF_OK;
+}
+
+static bool dual(const pf_stage* st) { return (st->cfg.flags & PF_STAGE_DUAL_STREAM) != 0; }
+
 static pf_status check_loaded(pf_stage* st, const char* who) {
-  for (int l = 0; l < st->cfg.num_layers; ++l)
-    if (!st->layers[l].loaded) return fail(PF_ERR_STATE, "%s: layer %d weights not loaded", who, l);
+  for (int l = 0; l < st->cfg.num_layers; ++l) {
+    if (!st->layers[l].img.loaded) return fail(PF_ERR_STATE, "%s: layer %d weights not loaded", who, l);
+    if (dual(st) && !st->layers[l].txt.loaded)
+      return fail(PF_ERR_STATE, "%s: layer %d text-stream weights not loaded", who, l);
+  }
+  if ((st->cfg.flags & PF_STAGE_ROPE) && !st->rope_set) return fail(PF_ERR_STATE, "%s: stage_set_rope not called", who);
   return PF_OK;
 }
 
 static pf_status set_cond_impl(pf_stage* st, const float* cond, hipStream_t s) {
   for (auto& lm : st->layers)
-    for (int64_t b = 0; b < st->batch; ++b) {
-      hipError_t e = launch_adaln(cond + b * st->h, lm.w_ada, lm.b_ada, (int)st->h, lm.mod + b * 6 * st->h,
-                                  st->cfg.dtype, s);
-      if (e != hipSuccess) return stage_hip_fail(st, e, "stage_set_cond: adaln launch");
+    for (int set = 0; set < (dual(st) ? 2 : 1); ++set) {
+      const WeightSet& ws = set == 0 ? lm.img : lm.txt;
+      for (int64_t b = 0; b < st->batch; ++b) {
+        hipError_t e = launch_adaln(cond + b * st->h, ws.w_ada, ws.b_ada, (int)st->h, ws.mod + b * 6 * st->h,
+                                    st->cfg.dtype, s);
+        if (e != hipSuccess) return stage_hip_fail(st, e, "stage_set_cond: adaln launch");
+      }
     }
   st->cond_set = true;
   return PF_OK;
@@ -546,62 +651,107 @@ extern "C" pf_status stage_set_cond(pf_stage* st, const float* cond, void* strea
 }
 
 // Buffer rows [off, off + n) of every sample through all layers.  Sample b's rows of x (fp32,
-// updated in place) are [x + b * x_stride, + n * h); inside the micro-step the samples' rows
-// are stacked (rows b*n .. b*n + n - 1 of the scratch), so every projection runs once over
-// batch * n rows with shared weights, while each sample keeps its own modulation, gates, K/V
-// buffers and attention.
+// updated in place) are [x + b * x_stride, + n * h).  With PF_STAGE_DUAL_STREAM the rows split
+// at seq_txt into a text part and an image part, each with its own weight set; otherwise there
+// is one part.  Inside a part the samples' rows are stacked (scratch row srow + b * n_part + i),
+// so every projection runs once over batch * n_part rows with shared weights, while each sample
+// keeps its own modulation, gates, K/V buffers and attention.  Attention is joint: every part's
+// K/V rows are in the buffers before any row attends.
+namespace {
+struct Part {
+  int64_t off, n;        // buffer rows [off, off + n)
+  int64_t srow;          // first scratch row (batch-stacked)
+  float* x;              // sample 0's first row of x
+  const WeightSet* (*pick)(const LayerMem&);
+};
+const WeightSet* pick_img(const LayerMem& lm) { return &lm.img; }
+const WeightSet* pick_txt(const LayerMem& lm) { return &lm.txt; }
+}  // namespace
+
 static pf_status run_rows(pf_stage* st, int64_t off, int64_t n, float* x, int64_t x_stride, hipStream_t s) {
-  const int64_t h = st->h, rh = st->rh, nb = st->batch, rows = nb * n;
+  const int64_t h = st->h, rh = st->rh, nb = st->batch;
   const int dt = st->cfg.dtype;
   const size_t es = st->es;
   const float eps = st->cfg.ln_eps;
   const int gelu_epi = st->cfg.gelu == PF_GELU_ERF ? kEpiGeluErf : kEpiGeluTanh;
   const int64_t kv_stride = (int64_t)(st->kv_sample_bytes / es);   // elements between samples' buffers
-  const RowGroups xg{n, x_stride, 6 * h};   // x rows and modulation vectors per sample
-  char* qkv = (char*)st->qkv;
+  const bool qk_norm = (st->cfg.flags & PF_STAGE_QK_NORM) != 0, rope = (st->cfg.flags & PF_STAGE_ROPE) != 0;
+  Part parts[2];
+  int n_parts = 0;
+  const int64_t split = dual(st) ? std::min(std::max(st->cfg.seq_txt - off, (int64_t)0), n) : 0;
+  if (split > 0) parts[n_parts++] = Part{off, split, 0, x, pick_txt};
+  if (split < n) parts[n_parts++] = Part{off + split, n - split, nb * split, x + split * h, pick_img};
+  char* const qkv = (char*)st->qkv;
+  char* const h1 = (char*)st->h1;
+  char* const o = (char*)st->o;
   for (auto& lm : st->layers) {
-    const float* mod = lm.mod;
     hipError_t e;
-    if ((e = launch_ln_modulate(x, rows, (int)h, mod, mod + h, eps, st->h1, dt, s, &xg)) != hipSuccess)
-      return stage_hip_fail(st, e, "ln_modulate");
     const int v_layout = dt == PF_BF16 ? kLayoutK8 : kLayoutRows;
-    if (dt == PF_BF16) {
-      // QKV projection with the splice in its epilogue: Q to the scratch, each sample's fresh K
-      // and V straight into rows [off, off + n) of its own buffer (no other row changes)
-      const QkvSplice sp{lm.k, lm.v, off, h, n, kv_stride, kv_stride};
-      if ((e = launch_gemm(st->h1, h, lm.w_qkv, lm.b_qkv, rows, 3 * h, h, kEpiQkvSplice, qkv, 3 * h, nullptr, dt,
-                           st->gemm_ws, st->gemm_ws_bytes, s, &sp)) != hipSuccess)
-        return stage_hip_fail(st, e, "qkv gemm + kv splice");
-    } else {
-      if ((e = launch_gemm(st->h1, h, lm.w_qkv, lm.b_qkv, rows, 3 * h, h, kEpiStore, qkv, 3 * h, nullptr, dt,
-                           st->gemm_ws, st->gemm_ws_bytes, s)) != hipSuccess)
-        return stage_hip_fail(st, e, "qkv gemm");
-      for (int64_t b = 0; b < nb; ++b) {
-        const char* src_row = qkv + (size_t)(b * n * 3 * h) * es;
-        KVDesc dst[2] = {{(char*)lm.k + b * st->kv_sample_bytes, h, kLayoutRows},
-                         {(char*)lm.v + b * st->kv_sample_bytes, h, kLayoutRows}};
-        KVDesc src[2] = {{src_row + h * es, 3 * h, kLayoutRows}, {src_row + 2 * h * es, 3 * h, kLayoutRows}};
-        if ((e = launch_splice(dst, src, h, off, n, (int)es, s)) != hipSuccess)
-          return stage_hip_fail(st, e, "kv splice");
+    for (int pi = 0; pi < n_parts; ++pi) {
+      const Part& p = parts[pi];
+      const WeightSet& ws = *p.pick(lm);
+      const RowGroups xg{p.n, x_stride, 6 * h};   // x rows and modulation vectors per sample
+      const int64_t rows = nb * p.n;
+      char* h1p = h1 + (size_t)(p.srow * h) * es;
+      char* qkvp = qkv + (size_t)(p.srow * 3 * h) * es;
+      if ((e = launch_ln_modulate(p.x, rows, (int)h, ws.mod, ws.mod + h, eps, h1p, dt, s, &xg)) != hipSuccess)
+        return stage_hip_fail(st, e, "ln_modulate");
+      if (dt == PF_BF16) {
+        // QKV projection with the splice in its epilogue: Q to the scratch, each sample's fresh K
+        // and V straight into rows [p.off, p.off + p.n) of its own buffer (no other row changes)
+        const QkvSplice sp{lm.k, lm.v, p.off, h, p.n, kv_stride, kv_stride};
+        if ((e = launch_gemm(h1p, h, ws.w_qkv, ws.b_qkv, rows, 3 * h, h, kEpiQkvSplice, qkvp, 3 * h, nullptr, dt,
+                             st->gemm_ws, st->gemm_ws_bytes, s, &sp)) != hipSuccess)
+          return stage_hip_fail(st, e, "qkv gemm + kv splice");
+        // QK-RMSNorm and rotary embedding in place: Q rows in the scratch, K rows in the buffers
+        if ((qk_norm || rope) &&
+            (e = launch_qk_norm_rope(qkvp, 3 * h, lm.k, h, kv_stride, p.off, p.n, nb, st->cfg.heads,
+                                     st->cfg.head_dim, ws.q_norm, ws.k_norm, st->rope, qk_norm, rope, s)) != hipSuccess)
+          return stage_hip_fail(st, e, "qk norm / rope");
+      } else {
+        if ((e = launch_gemm(h1p, h, ws.w_qkv, ws.b_qkv, rows, 3 * h, h, kEpiStore, qkvp, 3 * h, nullptr, dt,
+                             st->gemm_ws, st->gemm_ws_bytes, s)) != hipSuccess)
+          return stage_hip_fail(st, e, "qkv gemm");
+        for (int64_t b = 0; b < nb; ++b) {
+          const char* src_row = qkvp + (size_t)(b * p.n * 3 * h) * es;
+          KVDesc dst[2] = {{(char*)lm.k + b * st->kv_sample_bytes, h, kLayoutRows},
+                           {(char*)lm.v + b * st->kv_sample_bytes, h, kLayoutRows}};
+          KVDesc src[2] = {{src_row + h * es, 3 * h, kLayoutRows}, {src_row + 2 * h * es, 3 * h, kLayoutRows}};
+          if ((e = launch_splice(dst, src, h, p.off, p.n, (int)es, s)) != hipSuccess)
+            return stage_hip_fail(st, e, "kv splice");
+        }
       }
     }
-    // one launch for every sample; each sample's queries attend over its own buffer
-    if ((e = launch_attention(qkv, 3 * h, lm.k, h, lm.v, h, v_layout, h, st->s_kv, n, st->cfg.heads,
-                              st->cfg.head_dim, st->o, h, dt, st->attn_ws, st->attn_ws_bytes, s, nb, kv_stride)) !=
-        hipSuccess)
-      return stage_hip_fail(st, e, "attention");
-    if ((e = launch_gemm(st->o, h, lm.w_o, lm.b_o, rows, h, h, kEpiGatedResidual, x, h, mod + 2 * h, dt,
-                         st->gemm_ws, st->gemm_ws_bytes, s, nullptr, &xg)) != hipSuccess)
-      return stage_hip_fail(st, e, "out-proj gemm");
-    if (rh > 0) {
-      if ((e = launch_ln_modulate(x, rows, (int)h, mod + 3 * h, mod + 4 * h, eps, st->h1, dt, s, &xg)) != hipSuccess)
-        return stage_hip_fail(st, e, "ln_modulate (mlp)");
-      if ((e = launch_gemm(st->h1, h, lm.w1, lm.b1, rows, rh, h, gelu_epi, st->u, rh, nullptr, dt, st->gemm_ws,
-                           st->gemm_ws_bytes, s)) != hipSuccess)
-        return stage_hip_fail(st, e, "mlp up gemm");
-      if ((e = launch_gemm(st->u, rh, lm.w2, lm.b2, rows, h, rh, kEpiGatedResidual, x, h, mod + 5 * h, dt,
+    // one launch per part for every sample; each sample's queries attend over its own buffer
+    for (int pi = 0; pi < n_parts; ++pi) {
+      const Part& p = parts[pi];
+      if ((e = launch_attention(qkv + (size_t)(p.srow * 3 * h) * es, 3 * h, lm.k, h, lm.v, h, v_layout, h, st->s_kv,
+                                p.n, st->cfg.heads, st->cfg.head_dim, o + (size_t)(p.srow * h) * es, h, dt,
+                                st->attn_ws, st->attn_ws_bytes, s, nb, kv_stride)) != hipSuccess)
+        return stage_hip_fail(st, e, "attention");
+    }
+    for (int pi = 0; pi < n_parts; ++pi) {
+      const Part& p = parts[pi];
+      const WeightSet& ws = *p.pick(lm);
+      const RowGroups xg{p.n, x_stride, 6 * h};
+      const int64_t rows = nb * p.n;
+      char* h1p = h1 + (size_t)(p.srow * h) * es;
+      char* op = o + (size_t)(p.srow * h) * es;
+      char* up = (char*)st->u + (size_t)(p.srow * rh) * es;
+      if ((e = launch_gemm(op, h, ws.w_o, ws.b_o, rows, h, h, kEpiGatedResidual, p.x, h, ws.mod + 2 * h, dt,
                            st->gemm_ws, st->gemm_ws_bytes, s, nullptr, &xg)) != hipSuccess)
-        return stage_hip_fail(st, e, "mlp down gemm");
+        return stage_hip_fail(st, e, "out-proj gemm");
+      if (rh > 0) {
+        if ((e = launch_ln_modulate(p.x, rows, (int)h, ws.mod + 3 * h, ws.mod + 4 * h, eps, h1p, dt, s, &xg)) !=
+            hipSuccess)
+          return stage_hip_fail(st, e, "ln_modulate (mlp)");
+        if ((e = launch_gemm(h1p, h, ws.w1, ws.b1, rows, rh, h, gelu_epi, up, rh, nullptr, dt, st->gemm_ws,
+                             st->gemm_ws_bytes, s)) != hipSuccess)
+          return stage_hip_fail(st, e, "mlp up gemm");
+        if ((e = launch_gemm(up, rh, ws.w2, ws.b2, rows, h, rh, kEpiGatedResidual, p.x, h, ws.mod + 5 * h, dt,
+                             st->gemm_ws, st->gemm_ws_bytes, s, nullptr, &xg)) != hipSuccess)
+          return stage_hip_fail(st, e, "mlp down gemm");
+      }
     }
   }
   return PF_OK;

@@ -36,9 +36,14 @@ def rows_to_k8(a: np.ndarray) -> np.ndarray:
 
 class Stage:
     """`batch` > 1: samples sharing the weights (a classifier-free guidance pair is 2); x is
-    then [batch, rows, h] and cond [batch, h], and each sample has its own K/V buffers."""
+    then [batch, rows, h] and cond [batch, h], and each sample has its own K/V buffers.
 
-    def __init__(self, shape: StageShape, gelu: str = "tanh", ln_eps: float = 1e-6, batch: int = 1):
+    MM-DiT block options (bf16 stages): qk_norm (per-head RMSNorm of Q and K; each layer dict
+    then holds q_norm and k_norm [d]), dual_stream (the text rows use the layer dicts given as
+    `txt_layers` to load()) and rope (rotation angles given to set_rope())."""
+
+    def __init__(self, shape: StageShape, gelu: str = "tanh", ln_eps: float = 1e-6, batch: int = 1,
+                 qk_norm: bool = False, dual_stream: bool = False, rope: bool = False):
         torch = _torch()
         self.shape = shape
         self.batch = batch
@@ -47,8 +52,9 @@ class Stage:
         cfg = B.StageConfig(num_layers=shape.num_layers, hidden=shape.hidden, heads=shape.heads,
                             head_dim=shape.head_dim, mlp_ratio=shape.mlp_ratio, num_patches=shape.num_patches,
                             seq_img=shape.seq_img, seq_txt=shape.seq_txt, dtype=self.pf_dtype,
-                            gelu=B.PF_GELU_TANH if gelu == "tanh" else B.PF_GELU_ERF, ln_eps=ln_eps, flags=0,
-                            batch=batch)
+                            gelu=B.PF_GELU_TANH if gelu == "tanh" else B.PF_GELU_ERF, ln_eps=ln_eps,
+                            flags=(B.PF_STAGE_QK_NORM if qk_norm else 0) | (B.PF_STAGE_DUAL_STREAM if dual_stream else 0)
+                            | (B.PF_STAGE_ROPE if rope else 0), batch=batch)
         self.handle = B.stage_create(cfg)
         self.v_layout = B.PF_LAYOUT_K8 if self.pf_dtype == B.PF_BF16 else B.PF_LAYOUT_ROWS
 
@@ -72,23 +78,32 @@ class Stage:
             pass
 
     # ------------------------------------------------------------------ weights
-    def load(self, layers):
-        """layers: list of dicts of host fp32 arrays (synth.StageInputs.layers)."""
+    def load(self, layers, txt_layers=None):
+        """layers (and, for a dual-stream stage, txt_layers): lists of dicts of host fp32 arrays
+        (synth.StageInputs.layers); matrices go to the stage dtype, vectors stay fp32."""
         torch = _torch()
         keep = []
-        for l, lw in enumerate(layers):
-            dev = {}
-            for name, a in lw.items():
-                t = torch.from_numpy(np.ascontiguousarray(a, np.float32))
-                dt = self.dtype if name.startswith("w") else torch.float32
-                dev[name] = t.to(device="cuda", dtype=dt)
-            if self.shape.mlp_ratio == 0:
-                for n in ("w1", "b1", "w2", "b2"):
-                    dev[n] = None
-            B.stage_load_weights(self.handle, l, dev)
-            keep.append(dev)
+        for sets, loader in ((layers, B.stage_load_weights), (txt_layers or [], B.stage_load_text_weights)):
+            for l, lw in enumerate(sets):
+                dev = {}
+                for name, a in lw.items():
+                    t = torch.from_numpy(np.ascontiguousarray(a, np.float32))
+                    dt = self.dtype if name.startswith("w") else torch.float32
+                    dev[name] = t.to(device="cuda", dtype=dt)
+                if self.shape.mlp_ratio == 0:
+                    for n in ("w1", "b1", "w2", "b2"):
+                        dev[n] = None
+                loader(self.handle, l, dev)
+                keep.append(dev)
         torch.cuda.synchronize()
         del keep
+
+    def set_rope(self, angles):
+        """angles: host array [seq_kv, head_dim / 2] (radians; row r turns buffer row r)."""
+        torch = _torch()
+        t = torch.from_numpy(np.ascontiguousarray(angles, np.float32)).to("cuda")
+        B.stage_set_rope(self.handle, t)
+        torch.cuda.synchronize()
 
     # ------------------------------------------------------------------ runs
     def run_step(self, x, cond, warmup: bool = False, out=None):

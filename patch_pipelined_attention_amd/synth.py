@@ -86,6 +86,60 @@ def stage_inputs(shape: StageShape, seed: int | None = None) -> StageInputs:
     return StageInputs(shape, layers, x, c, rng)
 
 
+@dataclasses.dataclass
+class MMDiTInputs:
+    layers: list           # image-stream layer dicts: the StageInputs layers plus q_norm, k_norm [d]
+    txt_layers: list       # text-stream layer dicts of the same form
+    angles: np.ndarray     # fp32 [S_kv, d/2] rotation angles of the buffer rows
+
+
+def mmdit_inputs(shape: StageShape, inputs: StageInputs, seed: int | None = None) -> MMDiTInputs:
+    """Extra inputs of the MM-DiT block options, from generator PCG64(shape.seed + 3000): a
+    text-stream layer set drawn like step 1 of the recipe, then per layer q_norm and k_norm of
+    the image stream and of the text stream, each [d] ~ 1 + N(0, 0.3^2).
+
+    The rotation angles follow the published Flux.1 position layout (no random draw): a buffer
+    row has a 3-axis position, (0, 0, 0) for every text row and (0, gy, gx) for image row
+    gy * gw + gx (gw: the largest divisor of seq_img not above its square root); the d/2 pairs
+    of a head split into axes of a0 = d // 16 pairs and two of (d/2 - a0) / 2, and pair j of
+    an axis with n pairs turns by position * 10000^(-j / n).  fp32."""
+    rng = np.random.Generator(np.random.PCG64(shape.seed + 3000 if seed is None else seed))
+    h, r, d = shape.hidden, shape.mlp_ratio, shape.head_dim
+    shapes = layer_shapes(h, r)
+    std = np.float32(shape.w_std)
+    txt = []
+    for _ in range(shape.num_layers):
+        lw = {}
+        for name in WEIGHT_NAMES:
+            if r == 0 and name in ("w1", "b1", "w2", "b2"):
+                lw[name] = np.zeros(shapes[name], np.float32)
+                continue
+            a = rng.standard_normal(shapes[name], dtype=np.float32) * std
+            if shape.dtype == "bf16" and name in MATRIX_NAMES:
+                a = to_bf16_values(a)
+            lw[name] = a
+        txt.append(lw)
+    img = [dict(lw) for lw in inputs.layers]
+    for sets in (img, txt):
+        for lw in sets:
+            lw["q_norm"] = (1.0 + 0.3 * rng.standard_normal(d)).astype(np.float32)
+            lw["k_norm"] = (1.0 + 0.3 * rng.standard_normal(d)).astype(np.float32)
+    gw = max(g for g in range(1, int(shape.seq_img ** 0.5) + 1) if shape.seq_img % g == 0)
+    a0 = d // 16
+    a1 = (d // 2 - a0) // 2
+    axes = (a0, a1, d // 2 - a0 - a1)
+    pos = np.zeros((shape.seq_kv, 3), np.float64)
+    s_img = np.arange(shape.seq_img)
+    pos[shape.seq_txt:, 1] = s_img // gw
+    pos[shape.seq_txt:, 2] = s_img % gw
+    cols = []
+    for axis, n in enumerate(axes):
+        freq = 10000.0 ** (-np.arange(n, dtype=np.float64) / n)
+        cols.append(pos[:, axis:axis + 1] * freq[None, :])
+    angles = np.concatenate(cols, axis=1).astype(np.float32)
+    return MMDiTInputs(img, txt, angles)
+
+
 def batch_conds(shape: StageShape, c: np.ndarray, batch: int) -> np.ndarray:
     """Conditions of a batch of samples sharing the latent: sample 0 takes `c`; sample b >= 1
     (e.g. the unconditional half of a classifier-free guidance pair) an N(0, 1) vector of its own

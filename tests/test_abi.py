@@ -39,7 +39,9 @@ def _cfg(**kw):
     (dict(dtype=7), B.PF_ERR_INVALID_ARG),
     (dict(gelu=5), B.PF_ERR_INVALID_ARG),
     (dict(ln_eps=0.0), B.PF_ERR_INVALID_ARG),
-    (dict(flags=1), B.PF_ERR_INVALID_ARG),
+    (dict(flags=8), B.PF_ERR_INVALID_ARG),              # unknown block option
+    (dict(flags=B.PF_STAGE_QK_NORM, dtype=B.PF_FP32), B.PF_ERR_UNSUPPORTED),   # options are bf16-only
+    (dict(flags=B.PF_STAGE_DUAL_STREAM, seq_txt=0), B.PF_ERR_INVALID_ARG),     # dual stream needs text rows
     (dict(heads=1, hidden=72), B.PF_ERR_UNSUPPORTED),        # bf16 needs hidden % 64 == 0
     (dict(mlp_ratio=-1), B.PF_ERR_INVALID_ARG),
     (dict(batch=-1), B.PF_ERR_INVALID_ARG),
@@ -59,6 +61,8 @@ def test_null_arguments(lib):
     assert lib.stage_destroy(None) == B.PF_OK
     assert lib.stage_run_patch(None, 0, 1, None, None, None) == B.PF_ERR_INVALID_ARG
     assert lib.stage_get_kvbuf(None, 0, None) == B.PF_ERR_INVALID_ARG
+    assert lib.stage_load_text_weights(None, 0, None, None) == B.PF_ERR_INVALID_ARG
+    assert lib.stage_set_rope(None, None, None) == B.PF_ERR_INVALID_ARG
 
 
 def _view(k, v, rows, elems=64, dtype=B.PF_BF16, layout=B.PF_LAYOUT_ROWS, k_ld=None, v_ld=None):

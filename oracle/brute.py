@@ -77,10 +77,11 @@ def rope_row(row, heads, d, angles):
 
 
 def stage_step(layers, kbuf, vbuf, x_all, c, *, heads, d, seq_txt, num_patches, mlp_ratio,
-               warmup, eps=1e-6, txt_layers=None, qk_norm=False, rope_angles=None):
+               warmup, eps=1e-6, txt_layers=None, qk_norm=False, rope_angles=None, parallel=False):
     """One step over all rows; kbuf/vbuf (lists of per-layer row lists) are updated in place.
     txt_layers: weights of the text-prefix rows (dual stream); qk_norm: per-head RMSNorm of Q
-    and K with the row's weights' q_norm / k_norm; rope_angles: per buffer row, d/2 angles."""
+    and K with the row's weights' q_norm / k_norm; rope_angles: per buffer row, d/2 angles;
+    parallel: attention and MLP on the same modulated row, x += gate * W2 [o, u] + b2."""
     h = heads * d
     S = len(x_all)
 
@@ -89,7 +90,7 @@ def stage_step(layers, kbuf, vbuf, x_all, c, *, heads, d, seq_txt, num_patches, 
         for W in ws:
             sc = [silu(a) for a in c]
             m = matvec_rows([sc], W["w_ada"], W["b_ada"])[0]
-            out.append([m[i * h:(i + 1) * h] for i in range(6)])
+            out.append([m[i * h:(i + 1) * h] for i in range(len(m) // h)])
         return out
     mods = mods_of(layers)
     mods_t = mods_of(txt_layers) if txt_layers is not None else None
@@ -107,10 +108,13 @@ def stage_step(layers, kbuf, vbuf, x_all, c, *, heads, d, seq_txt, num_patches, 
                 if txt_layers is not None and off + i < seq_txt:
                     return txt_layers[l], mods_t[l]
                 return layers[l], mods[l]
-            qs = []
+            qs, us = [], []
             for i in range(n):
-                W, (sh1, sc1, g1, sh2, sc2, g2) = wm(i)
+                W, md = wm(i)
+                sh1, sc1 = md[0], md[1]
                 h1 = [a * (1.0 + sc1[t]) + sh1[t] for t, a in enumerate(layer_norm_row(x[i], eps))]
+                if parallel:
+                    us.append([gelu_tanh(a) for a in matvec_rows([h1], W["w1"], W["b1"])[0]] if mlp_ratio else [])
                 qkv = matvec_rows([h1], W["w_qkv"], W["b_qkv"])[0]
                 q, k = qkv[:h], qkv[h:2 * h]
                 if qk_norm:
@@ -122,7 +126,12 @@ def stage_step(layers, kbuf, vbuf, x_all, c, *, heads, d, seq_txt, num_patches, 
                 qs.append(q)
             o = attention(qs, kbuf[l], vbuf[l], heads, d)
             for i in range(n):
-                W, (sh1, sc1, g1, sh2, sc2, g2) = wm(i)
+                W, md = wm(i)
+                if parallel:
+                    y = matvec_rows([list(o[i]) + us[i]], W["w2"], W["b2"])[0]
+                    x[i] = [x[i][t] + md[2][t] * y[t] for t in range(h)]
+                    continue
+                g1, sh2, sc2, g2 = md[2], md[3], md[4], md[5]
                 y = matvec_rows([o[i]], W["w_o"], W["b_o"])[0]
                 xi = [x[i][t] + g1[t] * y[t] for t in range(h)]
                 if mlp_ratio > 0:

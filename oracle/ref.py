@@ -123,10 +123,11 @@ def linear(x, w, b=None) -> np.ndarray:
 
 
 def adaln(c, w_ada, b_ada) -> np.ndarray:
-    """Per-layer modulation vector: SiLU(c) @ W_ada.T + b_ada, returned as [6, h]
-    in the order shift1, scale1, gate1, shift2, scale2, gate2."""
+    """Per-layer modulation vector: SiLU(c) @ W_ada.T + b_ada, returned as [k, h]: k = 6 for
+    the DiT block (shift1, scale1, gate1, shift2, scale2, gate2), k = 3 for the parallel block
+    (shift, scale, gate)."""
     m = linear(silu(c)[None, :], w_ada, b_ada)[0]
-    return m.reshape(6, -1)
+    return m.reshape(-1, np.asarray(w_ada).shape[1])
 
 
 # ---------------------------------------------------------------------------
@@ -224,14 +225,20 @@ class StageOracle:
     * qk_norm: per-head RMSNorm of Q and K (after the projection, before RoPE) with the layer's
       (stream's) q_norm / k_norm scales;
     * rope_angles [seq_kv, d/2]: rotary embedding of Q and K, buffer row r's pairs turned by
-      rope_angles[r].
+      rope_angles[r];
+    * parallel: the Flux.1 single-stream block, attention and MLP side by side on one modulated
+      LayerNorm: h1 = LN(x) (1 + scale) + shift; Q, K, V = h1 W_qkv^T + b_qkv (then norm / rope,
+      splice, attention -> o); u = GELU(h1 W1^T + b1); x += gate * ([o, u] W2^T + b2) with
+      W2 [h, h + rh] (columns [0, h) act on o); w_ada is [3h, h] (shift, scale, gate) and
+      w_o / b_o are not used.
     In bf16 mode Q and K are rounded after the projection and again after norm / rotation (the
     GPU stores them between the two).
     """
 
     def __init__(self, layers, *, heads: int, head_dim: int, seq_txt: int, seq_img: int,
                  num_patches: int, mlp_ratio: int, ln_eps: float = 1e-6, gelu: str = "tanh",
-                 mode: str = "exact", txt_layers=None, qk_norm: bool = False, rope_angles=None):
+                 mode: str = "exact", txt_layers=None, qk_norm: bool = False, rope_angles=None,
+                 parallel: bool = False):
         if mode not in ("exact", "bf16", "bf16p"):
             raise ValueError(mode)
         if seq_img % num_patches:
@@ -239,6 +246,7 @@ class StageOracle:
         self.W = [{k: np.asarray(a, F64) for k, a in lw.items()} for lw in layers]
         self.Wt = None if txt_layers is None else [{k: np.asarray(a, F64) for k, a in lw.items()} for lw in txt_layers]
         self.qk_norm = qk_norm
+        self.parallel = parallel
         self.rope_angles = None if rope_angles is None else np.asarray(rope_angles, F64)
         self.heads, self.head_dim = heads, head_dim
         self.hidden = heads * head_dim
@@ -288,6 +296,7 @@ class StageOracle:
             def weights(txt):
                 return (self.Wt[l], self.mod_txt[l]) if txt else (self.W[l], self.mod[l])
             q_all = np.empty((rows, h), F64)
+            u_all = np.empty((rows, self.mlp_ratio * h), F64) if self.parallel else None
             rec = {"layer": l, "offset": offset, "h1": np.empty((rows, h)), "qkv": np.empty((rows, 3 * h))}
             for idx, txt in self._streams(rows_g):
                 if len(idx) == 0:
@@ -309,11 +318,26 @@ class StageOracle:
                 self.V[l][rows_g[idx]] = v
                 q_all[idx] = q
                 rec["h1"][idx], rec["qkv"][idx] = h1, qkv
+                if self.parallel and self.mlp_ratio > 0:
+                    u_all[idx] = self._r(self.gelu(linear(h1, W["w1"], W["b1"])))
             sel = np.arange(rows)
             if sample is not None and l == len(self.W) - 1:
                 sel = np.asarray(sample)
                 x = x[sel]
             o = self._r(attention(q_all[sel], self.K[l], self.V[l], H, d, round_p=self.mode == "bf16p"))
+            if self.parallel:
+                ou = o if self.mlp_ratio == 0 else np.concatenate([o, u_all[sel]], axis=1)
+                x_par = np.empty_like(x)
+                for idx, txt in self._streams(rows_g[sel]):
+                    if len(idx) == 0:
+                        continue
+                    W, mod = weights(txt)
+                    x_par[idx] = x[idx] + mod[2] * linear(ou[idx], W["w2"], W["b2"])
+                x = x_par
+                rec.update(o=o, u=None if u_all is None else u_all[sel], x_out=x.copy())
+                if self.trace is not None:
+                    self.trace.append(rec)
+                continue
             x_attn = np.empty_like(x)
             for idx, txt in self._streams(rows_g[sel]):
                 if len(idx) == 0:

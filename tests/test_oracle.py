@@ -495,3 +495,92 @@ def test_dual_stream_with_equal_weights_is_the_single_stream_block():
     two = ref.StageOracle(img, txt_layers=[dict(W) for W in img], **kw)
     for warm in (True, False):
         np.testing.assert_array_equal(one.step(x, c, warmup=warm), two.step(x, c, warmup=warm))
+
+
+def _parallel_layers(L, h, r, d, seed, std=0.3):
+    """Weights of the parallel (Flux.1 single-stream) block: w_qkv [3h,h], w1 [rh,h],
+    w2 [h, h + rh], w_ada [3h,h], plus q_norm / k_norm [d]."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(L):
+        out.append({"w_qkv": rng.standard_normal((3 * h, h)) * std, "b_qkv": rng.standard_normal(3 * h) * std,
+                    "w1": rng.standard_normal((r * h, h)) * std, "b1": rng.standard_normal(r * h) * std,
+                    "w2": rng.standard_normal((h, h + r * h)) * std, "b2": rng.standard_normal(h) * std,
+                    "w_ada": rng.standard_normal((3 * h, h)) * std, "b_ada": rng.standard_normal(3 * h) * std,
+                    "q_norm": 1.0 + 0.3 * rng.standard_normal(d), "k_norm": 1.0 + 0.3 * rng.standard_normal(d)})
+    return out
+
+
+def test_parallel_block_vs_brute_force_two_steps():
+    """The parallel block with QK-RMSNorm and RoPE: numpy oracle against the loop restatement,
+    warm-up then a drifted patched step, with a text prefix."""
+    H, d, r, L, S_txt, S_img, M = 2, 4, 2, 2, 2, 8, 2
+    h, S = H * d, S_txt + S_img
+    lw = _parallel_layers(L, h, r, d, 60)
+    rng = np.random.default_rng(14)
+    ang = rng.uniform(-3, 3, (S, d // 2))
+    st = ref.StageOracle(lw, heads=H, head_dim=d, seq_txt=S_txt, seq_img=S_img, num_patches=M, mlp_ratio=r,
+                         qk_norm=True, rope_angles=ang, parallel=True)
+    x, c = rng.standard_normal((S, h)), rng.standard_normal(h)
+    noise = [(rng.standard_normal((S, h)) * 0.1, rng.standard_normal((S, h)) * 0.1) for _ in range(L)]
+    kb = [[[0.0] * h for _ in range(S)] for _ in range(L)]
+    vb = [[[0.0] * h for _ in range(S)] for _ in range(L)]
+    bw = [{k: a.tolist() for k, a in W.items()} for W in lw]
+    kw = dict(heads=H, d=d, seq_txt=S_txt, num_patches=M, mlp_ratio=r, qk_norm=True, rope_angles=ang.tolist(),
+              parallel=True)
+    np.testing.assert_allclose(st.step(x, c, warmup=True),
+                               brute.stage_step(bw, kb, vb, x.tolist(), c.tolist(), warmup=True, **kw),
+                               rtol=1e-11, atol=1e-11)
+    st.add_noise(noise)
+    for l, (nk, nv) in enumerate(noise):
+        kb[l] = (np.array(kb[l]) + nk).tolist()
+        vb[l] = (np.array(vb[l]) + nv).tolist()
+    np.testing.assert_allclose(st.step(x, c, warmup=False),
+                               brute.stage_step(bw, kb, vb, x.tolist(), c.tolist(), warmup=False, **kw),
+                               rtol=1e-11, atol=1e-11)
+    for l in range(L):
+        np.testing.assert_allclose(st.K[l], kb[l], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(st.V[l], vb[l], rtol=1e-12, atol=1e-12)
+
+
+def _standard_from_parallel(pw, h, *, attn_only):
+    """DiT-block weights that compute what a parallel block computes in one of two special
+    cases: attn_only (its W2 has zero MLP columns) -> the attention-only block (r = 0) with
+    W_o = W2[:, :h]; otherwise (its V projection is zero, so o = 0) -> a block whose attention
+    sublayer adds nothing (W_o = 0, b_o = 0) and whose MLP sublayer uses the same shift, scale
+    and gate, W1, b1, W2[:, h:], b2."""
+    sw = {"w_qkv": pw["w_qkv"], "b_qkv": pw["b_qkv"], "q_norm": pw["q_norm"], "k_norm": pw["k_norm"]}
+    if attn_only:
+        sw.update(w_o=pw["w2"][:, :h], b_o=pw["b2"], w1=np.zeros((0, h)), b1=np.zeros(0), w2=np.zeros((h, 0)),
+                  b2=np.zeros(h), w_ada=np.concatenate([pw["w_ada"], np.zeros((3 * h, h))]),
+                  b_ada=np.concatenate([pw["b_ada"], np.zeros(3 * h)]))
+    else:
+        sw.update(w_o=np.zeros((h, h)), b_o=np.zeros(h), w1=pw["w1"], b1=pw["b1"], w2=pw["w2"][:, h:], b2=pw["b2"],
+                  w_ada=np.concatenate([pw["w_ada"], pw["w_ada"]]), b_ada=np.concatenate([pw["b_ada"], pw["b_ada"]]))
+    return sw
+
+
+@pytest.mark.parametrize("attn_only", [True, False], ids=["zero-mlp-columns", "zero-values"])
+def test_parallel_block_special_cases_reduce_to_the_dit_block(attn_only):
+    """Two special cases of the parallel block equal the (separately pinned) DiT block: with
+    W2's MLP columns zero it is the attention-only block with W_o = W2[:, :h]; with a zero V
+    projection it is the MLP sublayer alone (same modulation) with W2's MLP columns.  A swapped
+    [u, o] order, a wrong modulation chunk or a second LayerNorm fails one of them."""
+    H, d, r, L, S_txt, S_img, M = 2, 4, 2, 2, 2, 8, 2
+    h, S = H * d, S_txt + S_img
+    lw = _parallel_layers(L, h, r, d, 70)
+    for W in lw:
+        if attn_only:
+            W["w2"][:, h:] = 0.0
+        else:
+            W["w_qkv"][2 * h:] = 0.0
+            W["b_qkv"][2 * h:] = 0.0
+    rng = np.random.default_rng(15)
+    ang = rng.uniform(-3, 3, (S, d // 2))
+    x, c = rng.standard_normal((S, h)), rng.standard_normal(h)
+    kw = dict(heads=H, head_dim=d, seq_txt=S_txt, seq_img=S_img, num_patches=M, qk_norm=True, rope_angles=ang)
+    par = ref.StageOracle(lw, mlp_ratio=r, parallel=True, **kw)
+    std = ref.StageOracle([_standard_from_parallel(W, h, attn_only=attn_only) for W in lw],
+                          mlp_ratio=0 if attn_only else r, **kw)
+    for warm in (True, False):
+        np.testing.assert_allclose(par.step(x, c, warmup=warm), std.step(x, c, warmup=warm), rtol=1e-12, atol=1e-12)

@@ -38,9 +38,10 @@ def parse():
                     help="samples per stage sharing the weights (2 = a classifier-free guidance pair)")
     ap.add_argument("--denoiser", type=int, default=0, metavar="STEPS",
                     help="also time a denoising loop of STEPS steps (1 warm-up) around the stage")
-    ap.add_argument("--mmdit", action="store_true",
-                    help="Flux.1-style MM-DiT block: dual-stream text weights, QK-RMSNorm and RoPE "
-                         "(needs a config with a text prefix, e.g. c4)")
+    ap.add_argument("--block", choices=["dit", "mmdit", "flux-single"], default="dit",
+                    help="dit: adaLN DiT block; mmdit: Flux.1 double-stream block (dual-stream text weights, "
+                         "QK-RMSNorm, RoPE; needs a text prefix, e.g. c4); flux-single: Flux.1 single-stream "
+                         "block (parallel attention + MLP, QK-RMSNorm, RoPE)")
     ap.add_argument("--breakdown", action="store_true", help="also time every kernel of a patch-layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
@@ -142,11 +143,12 @@ def time_kernel_graph(torch, fn, iters=20, reps=5):
     return s.elapsed_time(e) / 1e3 / (reps * iters)
 
 
-def kernel_probes(torch, B, st, shape, layer_w, nb=1, mm=None):
+def kernel_probes(torch, B, st, shape, layer_w, nb=1, mm=None, parallel=False):
     """Component launches at the exact shapes one patch-layer of the stage issues: the row
     kernels and projections over the nb * P rows of all samples, the attention per sample
     (P query rows over that sample's buffer; the stage launches it nb times).  `mm` (MM-DiT
-    inputs) adds the QK-norm / rotation step of one sample's patch."""
+    inputs) adds the QK-norm / rotation step of one sample's patch; `parallel` swaps the
+    out-projection and the MLP down-projection for the parallel block's single [o, u] product."""
     h, P, S, r = shape.hidden, shape.patch_rows, shape.seq_kv, shape.mlp_ratio
     R = nb * P
     bf = torch.bfloat16
@@ -156,8 +158,9 @@ def kernel_probes(torch, B, st, shape, layer_w, nb=1, mm=None):
     scale = torch.zeros(h, device=dev)
     h1 = torch.empty((R, h), dtype=bf, device=dev)
     qkv = torch.randn((R, 3 * h), device=dev).to(bf)
-    o = torch.empty((R, h), dtype=bf, device=dev)
-    u = torch.empty((R, r * h), dtype=bf, device=dev)
+    ou = torch.empty((R, h + r * h), dtype=bf, device=dev)      # the parallel block's [o, u] rows
+    o = ou[:, :h] if parallel else torch.empty((R, h), dtype=bf, device=dev)
+    u = ou[:, h:] if parallel else torch.empty((R, r * h), dtype=bf, device=dev)
     kv = st.kv_view(0)
     gate = torch.zeros(h, device=dev)
     qkv_src = B.KVView(k=qkv.data_ptr() + h * 2, v=qkv.data_ptr() + 2 * h * 2, rows=P, row_elems=h, k_ld=3 * h,
@@ -166,7 +169,8 @@ def kernel_probes(torch, B, st, shape, layer_w, nb=1, mm=None):
     off_all = min(off, S - R)      # the QKV probe writes all R rows into one buffer
     ws = B.attention_workspace(P, shape.heads, shape.head_dim)   # same split choices as the stage
     gws = {k: B.gemm_workspace(R, n, kk) for k, (n, kk) in
-           {"qkv": (3 * h, h), "out": (h, h), "up": (r * h, h), "down": (h, r * h)}.items() if n > 0}
+           {"qkv": (3 * h, h), "out": (h, h), "up": (r * h, h), "down": (h, r * h),
+            "linear2": (h, h + r * h)}.items() if n > 0}
     w = layer_w
     probes = {
         "ln_modulate": (lambda: B.pf_ln_modulate(x, shift, scale, 1e-6, h1), 12.0 * R * h, "hbm"),
@@ -176,11 +180,12 @@ def kernel_probes(torch, B, st, shape, layer_w, nb=1, mm=None):
         # the standalone splice entry point (the harness's buffer updates; the stage fuses it above)
         "kv_splice_entry": (lambda: B.kvbuf_splice(kv, qkv_src, off, P), 8.0 * P * h, "hbm"),
         "attention": (lambda: B.pf_attention(qkv, kv, S, P, shape.heads, shape.head_dim, o, ldq=3 * h,
-                                             workspace=ws),
+                                             ldo=o.stride(0), workspace=ws),
                       4.0 * P * S * h, "mfma"),
-        "gemm_out": (lambda: B.pf_gemm(o, w["w_o"], w["b_o"], B.PF_EPI_GATED_RESIDUAL, x, gate=gate,
-                                       workspace=gws["out"]), 2.0 * R * h * h, "mfma"),
     }
+    if not parallel:
+        probes["gemm_out"] = (lambda: B.pf_gemm(o, w["w_o"], w["b_o"], B.PF_EPI_GATED_RESIDUAL, x, gate=gate,
+                                                workspace=gws["out"]), 2.0 * R * h * h, "mfma")
     if mm is not None:
         d = shape.head_dim
         gq = torch.from_numpy(mm.layers[0]["q_norm"]).cuda()
@@ -191,8 +196,12 @@ def kernel_probes(torch, B, st, shape, layer_w, nb=1, mm=None):
                                                             angles=ang, ldq=3 * h),
                                   8.0 * P * h + 2.0 * P * d, "hbm")
     if r > 0:
-        probes["gemm_up_gelu"] = (lambda: B.pf_gemm(h1, w["w1"], w["b1"], B.PF_EPI_GELU_TANH, u,
+        probes["gemm_up_gelu"] = (lambda: B.pf_gemm(h1, w["w1"], w["b1"], B.PF_EPI_GELU_TANH, u, ldc=u.stride(0),
                                                     workspace=gws["up"]), 2.0 * r * R * h * h, "mfma")
+    if parallel:
+        probes["gemm_linear2"] = (lambda: B.pf_gemm(ou, w["w2"], w["b2"], B.PF_EPI_GATED_RESIDUAL, x, gate=gate,
+                                                    workspace=gws["linear2"]), 2.0 * (1 + r) * R * h * h, "mfma")
+    elif r > 0:
         probes["gemm_down"] = (lambda: B.pf_gemm(u, w["w2"], w["b2"], B.PF_EPI_GATED_RESIDUAL, x, gate=gate,
                                                  workspace=gws["down"]), 2.0 * r * R * h * h, "mfma")
     return probes
@@ -238,7 +247,8 @@ def cpu_baseline(shape, inputs, budget_s, mm=None):
         threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     except Exception:
         threads = os.cpu_count() or 1
-    opts = {} if mm is None else dict(txt_layers=mm.txt_layers, qk_norm=True, rope_angles=mm.angles)
+    opts = {} if mm is None else dict(txt_layers=mm.txt_layers or None, qk_norm=True, rope_angles=mm.angles,
+                                      parallel=not mm.txt_layers)
     orc = ref.StageOracle(inputs.layers if mm is None else mm.layers, heads=shape.heads, head_dim=shape.head_dim,
                           seq_txt=shape.seq_txt, seq_img=shape.seq_img, num_patches=shape.num_patches,
                           mlp_ratio=shape.mlp_ratio, mode="exact", **opts)
@@ -324,13 +334,17 @@ def main():
     inputs = synth.stage_inputs(shape)
     nb = args.batch
     mm = None
-    if args.mmdit:
+    parallel = args.block == "flux-single"
+    if args.block == "mmdit":
         if shape.seq_txt < 1:
-            print(f"--mmdit needs a text prefix; {shape.name} has none", file=sys.stderr)
+            print(f"--block mmdit needs a text prefix; {shape.name} has none", file=sys.stderr)
             sys.exit(2)
         mm = synth.mmdit_inputs(shape, inputs)
-    st = Stage(shape, batch=nb, qk_norm=mm is not None, dual_stream=mm is not None, rope=mm is not None)
-    st.load(inputs.layers if mm is None else mm.layers, None if mm is None else mm.txt_layers)
+    elif parallel:
+        mm = synth.parallel_inputs(shape)
+    st = Stage(shape, batch=nb, qk_norm=mm is not None, dual_stream=args.block == "mmdit", rope=mm is not None,
+               parallel=parallel)
+    st.load(inputs.layers if mm is None else mm.layers, mm.txt_layers if args.block == "mmdit" else None)
     if mm is not None:
         st.set_rope(mm.angles)
     if nb == 1:
@@ -370,8 +384,8 @@ def main():
 
     # dominant kernel: patch attention at the stage's launch shape
     wdev = {k: torch.from_numpy(np.ascontiguousarray(a)).cuda().to(torch.bfloat16 if k.startswith("w") else torch.float32)
-            for k, a in inputs.layers[0].items()}
-    probes = kernel_probes(torch, B, st, shape, wdev, nb, mm)
+            for k, a in (inputs.layers if mm is None else mm.layers)[0].items()}
+    probes = kernel_probes(torch, B, st, shape, wdev, nb, mm, parallel)
     attn_fn, attn_flop, _ = probes["attention"]
     attn_s = time_kernel(torch, attn_fn, iters=max(10, args.steps))
     attn_tflops = attn_flop / attn_s / 1e12
@@ -396,9 +410,12 @@ def main():
     workload = (f"{shape.name}: one pipeline stage, {shape.num_layers} DiT blocks, hidden {shape.hidden}, "
                 f"{shape.heads}x{shape.head_dim} heads, MLP {shape.mlp_ratio}x, {shape.seq_kv} buffer rows, "
                 f"M={shape.num_patches} patches of {shape.patch_rows}")
-    if mm is not None:
-        workload += (", Flux.1-style MM-DiT blocks (dual-stream text weights, QK-RMSNorm, RoPE on a 3-axis "
+    if args.block == "mmdit":
+        workload += (", Flux.1 double-stream MM-DiT blocks (dual-stream text weights, QK-RMSNorm, RoPE on a 3-axis "
                      "position table)")
+    elif parallel:
+        workload += (", Flux.1 single-stream blocks (attention and MLP in parallel on one modulated LayerNorm, "
+                     "QK-RMSNorm, RoPE on a 3-axis position table)")
     if nb > 1:
         workload += f", batch of {nb} samples (classifier-free guidance pair: shared weights, own buffers)"
     rec = {
@@ -414,7 +431,7 @@ def main():
         "vs_baseline": None,
         "dtype": shape.dtype,
         "data": "synthetic",
-        "config": {"workload": workload, "batch": nb, "block": "mmdit" if mm is not None else "dit",
+        "config": {"workload": workload, "batch": nb, "block": args.block,
                    "num_layers": shape.num_layers, "hidden": shape.hidden, "heads": shape.heads,
                    "head_dim": shape.head_dim, "seq_kv": shape.seq_kv, "num_patches": shape.num_patches,
                    "patch_rows": shape.patch_rows, "parallelism": "single GPU stage"},

@@ -80,10 +80,17 @@ typedef enum pf_epilogue {
  *                         their own projections, modulation and gates; attention stays joint
  *                         over every buffer row;
  *   PF_STAGE_ROPE:        rotary embedding of Q and K (after the norm): in every head, the pair
- *                         (2k, 2k+1) of buffer row r turns by angles[r][k] (stage_set_rope). */
+ *                         (2k, 2k+1) of buffer row r turns by angles[r][k] (stage_set_rope);
+ *   PF_STAGE_PARALLEL:    the Flux.1 single-stream block: attention and MLP side by side on one
+ *                         modulated LayerNorm, h1 = LN(x) (1 + scale) + shift, Q/K/V from h1,
+ *                         u = GELU(h1 W1^T + b1), x += gate * ([O, u] W2^T + b2).  Weights:
+ *                         w_qkv [3h, h], w1 [rh, h], w2 [h, h + rh] (columns [0, h) act on the
+ *                         attention output), w_ada [3h, h] and b_ada [3h] (shift, scale, gate);
+ *                         w_o / b_o are not used.  Not combined with PF_STAGE_DUAL_STREAM. */
 #define PF_STAGE_QK_NORM 1u
 #define PF_STAGE_DUAL_STREAM 2u
 #define PF_STAGE_ROPE 4u
+#define PF_STAGE_PARALLEL 8u
 
 typedef struct pf_stage_config {
   int32_t num_layers;   /* L >= 1: contiguous layers owned by this stage                   */
@@ -107,7 +114,9 @@ typedef struct pf_stage_config {
  * [out, in] (nn.Linear layout), biases fp32.  W_qkv rows are Q (0..h), K (h..2h),
  * V (2h..3h); head j owns columns [j*d, (j+1)*d) of each.  W_ada rows are the six
  * modulation vectors shift1, scale1, gate1, shift2, scale2, gate2 (h rows each).
- * w1/b1/w2/b2 may be NULL when mlp_ratio == 0. */
+ * w1/b1/w2/b2 may be NULL when mlp_ratio == 0.  PF_STAGE_PARALLEL changes the shapes of w2
+ * ([h, h + rh]) and w_ada / b_ada ([3h, h], [3h]); w_o / b_o may then be NULL, and w2 / b2
+ * are required even when mlp_ratio == 0. */
 typedef struct pf_layer_weights {
   const void* w_qkv;  const float* b_qkv;   /* [3h, h], [3h]   */
   const void* w_o;    const float* b_o;     /* [h, h],  [h]    */

@@ -21,7 +21,7 @@ PF_GELU_TANH, PF_GELU_ERF = 0, 1
 PF_LAYOUT_ROWS, PF_LAYOUT_K8 = 0, 1
 PF_EPI_STORE, PF_EPI_GELU_TANH, PF_EPI_GELU_ERF, PF_EPI_GATED_RESIDUAL = range(4)
 PF_STEP_WARMUP = 1
-PF_STAGE_QK_NORM, PF_STAGE_DUAL_STREAM, PF_STAGE_ROPE = 1, 2, 4
+PF_STAGE_QK_NORM, PF_STAGE_DUAL_STREAM, PF_STAGE_ROPE, PF_STAGE_PARALLEL = 1, 2, 4, 8
 
 STATUS_NAMES = {0: "PF_OK", 1: "PF_ERR_INVALID_ARG", 2: "PF_ERR_UNSUPPORTED", 3: "PF_ERR_OOM",
                 4: "PF_ERR_STATE", 5: "PF_ERR_HIP"}

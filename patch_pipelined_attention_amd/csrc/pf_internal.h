@@ -115,8 +115,9 @@ hipError_t launch_ln_modulate(const float* x, int64_t rows, int hidden, const fl
                               const float* scale, float eps, void* y, int dtype, hipStream_t s,
                               const RowGroups* groups = nullptr);
 
+// mod [chunks * hidden] = SiLU(cond) . w^T + b (chunks: 6 for the DiT block, 3 for the parallel one)
 hipError_t launch_adaln(const float* cond, const void* w, const float* b, int hidden, float* mod,
-                        int dtype, hipStream_t s);
+                        int dtype, hipStream_t s, int chunks = 6);
 
 // `ws` (may be NULL) is scratch for the k-split of grids too small to fill the GPU.
 // `groups` (NULL: one sample) applies to the gated residual: each sample's rows of c and its

@@ -259,7 +259,7 @@ hipError_t launch_qk_norm_rope(void* q, int64_t ldq, void* k, int64_t ldk, int64
 }
 
 // ---------------------------------------------------------------------------------
-// mod[j] = sum_i SiLU(c[i]) * W[j, i] + b[j] for j < 6h.  SiLU(c) is staged in LDS
+// mod[j] = sum_i SiLU(c[i]) * W[j, i] + b[j] for j < chunks * h (6 or 3 vectors of h).  SiLU(c) is staged in LDS
 // once per block; one wavefront per output row streams that row of W with 16-byte loads.
 // ---------------------------------------------------------------------------------
 template <typename WT>
@@ -295,8 +295,8 @@ __global__ __launch_bounds__(256) void adaln_kernel(const float* __restrict__ co
 }
 
 hipError_t launch_adaln(const float* cond, const void* w, const float* b, int hidden, float* mod,
-                        int dtype, hipStream_t s) {
-  const int n_out = 6 * hidden;
+                        int dtype, hipStream_t s, int chunks) {
+  const int n_out = chunks * hidden;
   int blocks = (n_out + 3) / 4;
   if (blocks > 2048) blocks = 2048;
   const size_t lds = sizeof(float) * (size_t)hidden;

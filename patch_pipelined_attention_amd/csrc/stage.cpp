@@ -360,6 +360,8 @@ struct pf_stage {
   float* rope = nullptr;     // [s_kv, d/2] rotation angles (PF_STAGE_ROPE)
   bool rope_set = false;
   void *h1, *qkv, *o, *u;
+  int64_t ld_o, ld_u;        // row strides of o and u (the parallel block keeps [o, u] side by side)
+  int n_mod;                 // modulation vectors per sample: 6 (DiT block) or 3 (parallel block)
   void* attn_ws = nullptr;   // key-range split partials of the patch attention
   size_t attn_ws_bytes = 0;
   void* gemm_ws = nullptr;   // k-split partials of the projections
@@ -387,8 +389,10 @@ static pf_status validate_config(const pf_stage_config* c) {
   if (!dtype_ok(c->dtype)) return fail(PF_ERR_INVALID_ARG, "stage_create: bad dtype");
   if (c->gelu != PF_GELU_TANH && c->gelu != PF_GELU_ERF) return fail(PF_ERR_INVALID_ARG, "stage_create: bad gelu");
   if (!(c->ln_eps > 0.f) || !std::isfinite(c->ln_eps)) return fail(PF_ERR_INVALID_ARG, "stage_create: bad ln_eps");
-  if (c->flags & ~(PF_STAGE_QK_NORM | PF_STAGE_DUAL_STREAM | PF_STAGE_ROPE))
+  if (c->flags & ~(PF_STAGE_QK_NORM | PF_STAGE_DUAL_STREAM | PF_STAGE_ROPE | PF_STAGE_PARALLEL))
     return fail(PF_ERR_INVALID_ARG, "stage_create: unknown flags 0x%x", c->flags);
+  if ((c->flags & PF_STAGE_PARALLEL) && (c->flags & PF_STAGE_DUAL_STREAM))
+    return fail(PF_ERR_UNSUPPORTED, "stage_create: the parallel block is single-stream (no PF_STAGE_DUAL_STREAM)");
   if (c->flags != 0 && c->dtype != PF_BF16)
     return fail(PF_ERR_UNSUPPORTED, "stage_create: block options need a bf16 stage");
   if ((c->flags & PF_STAGE_DUAL_STREAM) && c->seq_txt < 1)
@@ -443,8 +447,13 @@ extern "C" pf_status stage_create(const pf_stage_config* cfg, pf_stage** out) {
   const int64_t d = cfg->head_dim;
 
   // weights: matrices then fp32 biases, each 256-byte aligned, then the two norm scales
-  const size_t mats[5] = {(size_t)(3 * h * h), (size_t)(h * h), (size_t)(rh * h), (size_t)(h * rh), (size_t)(6 * h * h)};
-  const size_t biases[5] = {(size_t)(3 * h), (size_t)h, (size_t)rh, (size_t)h, (size_t)(6 * h)};
+  // (w_qkv, w_o, w1, w2, w_ada; the parallel block has no w_o, a wider w2 and 3 modulation vectors)
+  const bool par = (cfg->flags & PF_STAGE_PARALLEL) != 0;
+  st->n_mod = par ? 3 : 6;
+  const int64_t k2 = par ? h + rh : rh;   // input width of the second MLP matrix
+  const size_t mats[5] = {(size_t)(3 * h * h), par ? 0 : (size_t)(h * h), (size_t)(rh * h), (size_t)(h * k2),
+                          (size_t)(st->n_mod * h * h)};
+  const size_t biases[5] = {(size_t)(3 * h), par ? 0 : (size_t)h, (size_t)rh, (size_t)h, (size_t)(st->n_mod * h)};
   size_t per_set = 0;
   for (int i = 0; i < 5; ++i) per_set += round_up(mats[i] * es, 256) + round_up(biases[i] * 4, 256);
   const size_t norm_bytes = round_up((size_t)d * 4, 256);
@@ -454,9 +463,12 @@ extern "C" pf_status stage_create(const pf_stage_config* cfg, pf_stage** out) {
   const size_t kv_mat = round_up((size_t)(st->s_alloc * h) * es, 256);
   st->kv_sample_bytes = 2 * kv_mat;   // per layer: K0, V0, K1, V1, ...
   // scratch for a micro-step of up to s_kv rows of every sample
+  st->ld_o = par ? h + rh : h;
+  st->ld_u = par ? h + rh : rh;
   const size_t scr_h = round_up((size_t)(nb * st->s_alloc * h) * es, 256);
+  const size_t scr_o = round_up((size_t)(nb * st->s_alloc * st->ld_o) * es, 256);
   const size_t scr_qkv = round_up((size_t)(nb * st->s_alloc * 3 * h) * es, 256);
-  const size_t scr_u = round_up((size_t)(nb * st->s_alloc * (rh > 0 ? rh : 1)) * es, 256);
+  const size_t scr_u = par ? 0 : round_up((size_t)(nb * st->s_alloc * (rh > 0 ? rh : 1)) * es, 256);
 
   // split partials for a patch or the text prefix of every sample (the warm-up pass fills the
   // GPU unsplit)
@@ -465,7 +477,7 @@ extern "C" pf_status stage_create(const pf_stage_config* cfg, pf_stage** out) {
   // k-split partials for the projections of a patch or the text prefix of all samples
   st->gemm_ws_bytes = 0;
   if (cfg->dtype == PF_BF16) {
-    const int64_t shapes[4][2] = {{3 * h, h}, {h, h}, {rh, h}, {h, rh}};
+    const int64_t shapes[4][2] = {{3 * h, h}, {par ? 0 : h, h}, {rh, h}, {h, k2}};
     for (const int64_t rows : {nb * st->patch_rows, nb * cfg->seq_txt}) {
       if (rows <= 0) continue;
       for (const auto& nk : shapes)
@@ -478,7 +490,7 @@ extern "C" pf_status stage_create(const pf_stage_config* cfg, pf_stage** out) {
       (st->attn_ws_bytes && (e = hipMalloc(&st->attn_ws, st->attn_ws_bytes)) != hipSuccess) ||
       (st->gemm_ws_bytes && (e = hipMalloc(&st->gemm_ws, st->gemm_ws_bytes)) != hipSuccess) ||
       (e = hipMalloc(&st->kvmem, 2 * kv_mat * L * nb)) != hipSuccess ||
-      (e = hipMalloc(&st->scratch, 2 * scr_h + scr_qkv + scr_u)) != hipSuccess ||
+      (e = hipMalloc(&st->scratch, scr_h + scr_o + scr_qkv + scr_u)) != hipSuccess ||
       (e = hipMalloc((void**)&st->modmem, sizeof(float) * 6 * h * L * nb * n_sets)) != hipSuccess ||
       (rope_bytes && (e = hipMalloc((void**)&st->rope, rope_bytes)) != hipSuccess)) {
     free_stage_mem(st);
@@ -526,10 +538,10 @@ extern "C" pf_status stage_create(const pf_stage_config* cfg, pf_stage** out) {
   st->h1 = sp;
   sp += scr_h;
   st->o = sp;
-  sp += scr_h;
+  sp += scr_o;
   st->qkv = sp;
   sp += scr_qkv;
-  st->u = sp;
+  st->u = par ? (char*)st->o + h * es : sp;
   *out = st;
   return PF_OK;
 }
@@ -566,22 +578,23 @@ static pf_status load_set(pf_stage* st, int32_t layer, const pf_layer_weights* w
   if (!w) return fail(PF_ERR_INVALID_ARG, "%s: null weights", who);
   const bool mlp = st->rh > 0;
   const bool qkn = (st->cfg.flags & PF_STAGE_QK_NORM) != 0;
-  if (!w->w_qkv || !w->b_qkv || !w->w_o || !w->b_o || !w->w_ada || !w->b_ada ||
-      (mlp && (!w->w1 || !w->b1 || !w->w2 || !w->b2)) || (qkn && (!w->q_norm || !w->k_norm)))
+  const bool par = (st->cfg.flags & PF_STAGE_PARALLEL) != 0;
+  if (!w->w_qkv || !w->b_qkv || (!par && (!w->w_o || !w->b_o)) || !w->w_ada || !w->b_ada ||
+      (mlp && (!w->w1 || !w->b1)) || ((mlp || par) && (!w->w2 || !w->b2)) || (qkn && (!w->q_norm || !w->k_norm)))
     return fail(PF_ERR_INVALID_ARG, "%s: null weight pointer", who);
-  const int64_t h = st->h, rh = st->rh, d = st->cfg.head_dim;
+  const int64_t h = st->h, rh = st->rh, d = st->cfg.head_dim, k2 = par ? h + rh : rh, nm = st->n_mod;
   const size_t es = st->es;
   WeightSet& lm = txt ? st->layers[layer].txt : st->layers[layer].img;
   struct Cp { void* dst; const void* src; size_t bytes; } cps[12] = {
       {lm.w_qkv, w->w_qkv, (size_t)(3 * h * h) * es}, {lm.b_qkv, w->b_qkv, (size_t)(3 * h) * 4},
-      {lm.w_o, w->w_o, (size_t)(h * h) * es},         {lm.b_o, w->b_o, (size_t)h * 4},
+      {lm.w_o, w->w_o, par ? 0 : (size_t)(h * h) * es}, {lm.b_o, w->b_o, par ? 0 : (size_t)h * 4},
       {lm.w1, w->w1, (size_t)(rh * h) * es},          {lm.b1, w->b1, (size_t)rh * 4},
-      {lm.w2, w->w2, (size_t)(h * rh) * es},          {lm.b2, w->b2, (size_t)h * 4},
-      {lm.w_ada, w->w_ada, (size_t)(6 * h * h) * es}, {lm.b_ada, w->b_ada, (size_t)(6 * h) * 4},
+      {lm.w2, w->w2, (size_t)(h * k2) * es},          {lm.b2, w->b2, (size_t)h * 4},
+      {lm.w_ada, w->w_ada, (size_t)(nm * h * h) * es}, {lm.b_ada, w->b_ada, (size_t)(nm * h) * 4},
       {lm.q_norm, w->q_norm, (size_t)d * 4},          {lm.k_norm, w->k_norm, (size_t)d * 4}};
   for (int i = 0; i < 12; ++i) {
     const Cp& c = cps[i];
-    if (c.bytes == 0 || (!mlp && i >= 4 && i < 8) || (!qkn && i >= 10)) continue;   // unused parameters
+    if (c.bytes == 0 || (!mlp && i >= 4 && i < (par ? 6 : 8)) || (!qkn && i >= 10)) continue;   // unused parameters
     hipError_t e = hipMemcpyAsync(c.dst, c.src, c.bytes, hipMemcpyDeviceToDevice, (hipStream_t)stream);
     if (e != hipSuccess) return stage_hip_fail(st, e, "stage_load_weights: hipMemcpyAsync");
   }
@@ -634,7 +647,7 @@ static pf_status set_cond_impl(pf_stage* st, const float* cond, hipStream_t s) {
       const WeightSet& ws = set == 0 ? lm.img : lm.txt;
       for (int64_t b = 0; b < st->batch; ++b) {
         hipError_t e = launch_adaln(cond + b * st->h, ws.w_ada, ws.b_ada, (int)st->h, ws.mod + b * 6 * st->h,
-                                    st->cfg.dtype, s);
+                                    st->cfg.dtype, s, st->n_mod);
         if (e != hipSuccess) return stage_hip_fail(st, e, "stage_set_cond: adaln launch");
       }
     }
@@ -676,6 +689,8 @@ static pf_status run_rows(pf_stage* st, int64_t off, int64_t n, float* x, int64_
   const int gelu_epi = st->cfg.gelu == PF_GELU_ERF ? kEpiGeluErf : kEpiGeluTanh;
   const int64_t kv_stride = (int64_t)(st->kv_sample_bytes / es);   // elements between samples' buffers
   const bool qk_norm = (st->cfg.flags & PF_STAGE_QK_NORM) != 0, rope = (st->cfg.flags & PF_STAGE_ROPE) != 0;
+  const bool par = (st->cfg.flags & PF_STAGE_PARALLEL) != 0;
+  const int64_t ld_o = st->ld_o, ld_u = st->ld_u;
   Part parts[2];
   int n_parts = 0;
   const int64_t split = dual(st) ? std::min(std::max(st->cfg.seq_txt - off, (int64_t)0), n) : 0;
@@ -708,6 +723,12 @@ static pf_status run_rows(pf_stage* st, int64_t off, int64_t n, float* x, int64_
             (e = launch_qk_norm_rope(qkvp, 3 * h, lm.k, h, kv_stride, p.off, p.n, nb, st->cfg.heads,
                                      st->cfg.head_dim, ws.q_norm, ws.k_norm, st->rope, qk_norm, rope, s)) != hipSuccess)
           return stage_hip_fail(st, e, "qk norm / rope");
+        // parallel block: the MLP's first projection reads the same modulated rows; its GELU
+        // output lands beside the attention output ([o, u] rows of width h + rh)
+        if (par && rh > 0 &&
+            (e = launch_gemm(h1p, h, ws.w1, ws.b1, rows, rh, h, gelu_epi, (char*)st->u + (size_t)(p.srow * ld_u) * es,
+                             ld_u, nullptr, dt, st->gemm_ws, st->gemm_ws_bytes, s)) != hipSuccess)
+          return stage_hip_fail(st, e, "mlp up gemm (parallel)");
       } else {
         if ((e = launch_gemm(h1p, h, ws.w_qkv, ws.b_qkv, rows, 3 * h, h, kEpiStore, qkvp, 3 * h, nullptr, dt,
                              st->gemm_ws, st->gemm_ws_bytes, s)) != hipSuccess)
@@ -726,7 +747,7 @@ static pf_status run_rows(pf_stage* st, int64_t off, int64_t n, float* x, int64_
     for (int pi = 0; pi < n_parts; ++pi) {
       const Part& p = parts[pi];
       if ((e = launch_attention(qkv + (size_t)(p.srow * 3 * h) * es, 3 * h, lm.k, h, lm.v, h, v_layout, h, st->s_kv,
-                                p.n, st->cfg.heads, st->cfg.head_dim, o + (size_t)(p.srow * h) * es, h, dt,
+                                p.n, st->cfg.heads, st->cfg.head_dim, o + (size_t)(p.srow * ld_o) * es, ld_o, dt,
                                 st->attn_ws, st->attn_ws_bytes, s, nb, kv_stride)) != hipSuccess)
         return stage_hip_fail(st, e, "attention");
     }
@@ -736,8 +757,15 @@ static pf_status run_rows(pf_stage* st, int64_t off, int64_t n, float* x, int64_
       const RowGroups xg{p.n, x_stride, 6 * h};
       const int64_t rows = nb * p.n;
       char* h1p = h1 + (size_t)(p.srow * h) * es;
-      char* op = o + (size_t)(p.srow * h) * es;
-      char* up = (char*)st->u + (size_t)(p.srow * rh) * es;
+      char* op = o + (size_t)(p.srow * ld_o) * es;
+      char* up = (char*)st->u + (size_t)(p.srow * ld_u) * es;
+      if (par) {
+        // x += gate * ([o, u] W2^T + b2): one product over the side-by-side rows
+        if ((e = launch_gemm(op, ld_o, ws.w2, ws.b2, rows, h, h + rh, kEpiGatedResidual, p.x, h, ws.mod + 2 * h, dt,
+                             st->gemm_ws, st->gemm_ws_bytes, s, nullptr, &xg)) != hipSuccess)
+          return stage_hip_fail(st, e, "linear2 gemm (parallel)");
+        continue;
+      }
       if ((e = launch_gemm(op, h, ws.w_o, ws.b_o, rows, h, h, kEpiGatedResidual, p.x, h, ws.mod + 2 * h, dt,
                            st->gemm_ws, st->gemm_ws_bytes, s, nullptr, &xg)) != hipSuccess)
         return stage_hip_fail(st, e, "out-proj gemm");
@@ -745,10 +773,10 @@ static pf_status run_rows(pf_stage* st, int64_t off, int64_t n, float* x, int64_
         if ((e = launch_ln_modulate(p.x, rows, (int)h, ws.mod + 3 * h, ws.mod + 4 * h, eps, h1p, dt, s, &xg)) !=
             hipSuccess)
           return stage_hip_fail(st, e, "ln_modulate (mlp)");
-        if ((e = launch_gemm(h1p, h, ws.w1, ws.b1, rows, rh, h, gelu_epi, up, rh, nullptr, dt, st->gemm_ws,
+        if ((e = launch_gemm(h1p, h, ws.w1, ws.b1, rows, rh, h, gelu_epi, up, ld_u, nullptr, dt, st->gemm_ws,
                              st->gemm_ws_bytes, s)) != hipSuccess)
           return stage_hip_fail(st, e, "mlp up gemm");
-        if ((e = launch_gemm(up, rh, ws.w2, ws.b2, rows, h, rh, kEpiGatedResidual, p.x, h, ws.mod + 5 * h, dt,
+        if ((e = launch_gemm(up, ld_u, ws.w2, ws.b2, rows, h, rh, kEpiGatedResidual, p.x, h, ws.mod + 5 * h, dt,
                              st->gemm_ws, st->gemm_ws_bytes, s, nullptr, &xg)) != hipSuccess)
           return stage_hip_fail(st, e, "mlp down gemm");
       }

@@ -34,16 +34,22 @@ def rows_to_k8(a: np.ndarray) -> np.ndarray:
     return np.ascontiguousarray(pad.reshape(g, 8, e).transpose(0, 2, 1)).reshape(-1)
 
 
+def parallel_block(lw) -> bool:
+    """Layer dict of the parallel block (no out-projection of its own)."""
+    return "w_o" not in lw
+
+
 class Stage:
     """`batch` > 1: samples sharing the weights (a classifier-free guidance pair is 2); x is
     then [batch, rows, h] and cond [batch, h], and each sample has its own K/V buffers.
 
     MM-DiT block options (bf16 stages): qk_norm (per-head RMSNorm of Q and K; each layer dict
     then holds q_norm and k_norm [d]), dual_stream (the text rows use the layer dicts given as
-    `txt_layers` to load()) and rope (rotation angles given to set_rope())."""
+    `txt_layers` to load()), rope (rotation angles given to set_rope()) and parallel (the Flux.1
+    single-stream block; layer dicts as synth.parallel_inputs draws them)."""
 
     def __init__(self, shape: StageShape, gelu: str = "tanh", ln_eps: float = 1e-6, batch: int = 1,
-                 qk_norm: bool = False, dual_stream: bool = False, rope: bool = False):
+                 qk_norm: bool = False, dual_stream: bool = False, rope: bool = False, parallel: bool = False):
         torch = _torch()
         self.shape = shape
         self.batch = batch
@@ -54,7 +60,8 @@ class Stage:
                             seq_img=shape.seq_img, seq_txt=shape.seq_txt, dtype=self.pf_dtype,
                             gelu=B.PF_GELU_TANH if gelu == "tanh" else B.PF_GELU_ERF, ln_eps=ln_eps,
                             flags=(B.PF_STAGE_QK_NORM if qk_norm else 0) | (B.PF_STAGE_DUAL_STREAM if dual_stream else 0)
-                            | (B.PF_STAGE_ROPE if rope else 0), batch=batch)
+                            | (B.PF_STAGE_ROPE if rope else 0) | (B.PF_STAGE_PARALLEL if parallel else 0),
+                            batch=batch)
         self.handle = B.stage_create(cfg)
         self.v_layout = B.PF_LAYOUT_K8 if self.pf_dtype == B.PF_BF16 else B.PF_LAYOUT_ROWS
 
@@ -91,7 +98,7 @@ class Stage:
                     dt = self.dtype if name.startswith("w") else torch.float32
                     dev[name] = t.to(device="cuda", dtype=dt)
                 if self.shape.mlp_ratio == 0:
-                    for n in ("w1", "b1", "w2", "b2"):
+                    for n in ("w1", "b1") if parallel_block(lw) else ("w1", "b1", "w2", "b2"):
                         dev[n] = None
                 loader(self.handle, l, dev)
                 keep.append(dev)

@@ -98,11 +98,7 @@ def mmdit_inputs(shape: StageShape, inputs: StageInputs, seed: int | None = None
     text-stream layer set drawn like step 1 of the recipe, then per layer q_norm and k_norm of
     the image stream and of the text stream, each [d] ~ 1 + N(0, 0.3^2).
 
-    The rotation angles follow the published Flux.1 position layout (no random draw): a buffer
-    row has a 3-axis position, (0, 0, 0) for every text row and (0, gy, gx) for image row
-    gy * gw + gx (gw: the largest divisor of seq_img not above its square root); the d/2 pairs
-    of a head split into axes of a0 = d // 16 pairs and two of (d/2 - a0) / 2, and pair j of
-    an axis with n pairs turns by position * 10000^(-j / n).  fp32."""
+    The rotation angles are rope_angles(shape)."""
     rng = np.random.Generator(np.random.PCG64(shape.seed + 3000 if seed is None else seed))
     h, r, d = shape.hidden, shape.mlp_ratio, shape.head_dim
     shapes = layer_shapes(h, r)
@@ -124,6 +120,16 @@ def mmdit_inputs(shape: StageShape, inputs: StageInputs, seed: int | None = None
         for lw in sets:
             lw["q_norm"] = (1.0 + 0.3 * rng.standard_normal(d)).astype(np.float32)
             lw["k_norm"] = (1.0 + 0.3 * rng.standard_normal(d)).astype(np.float32)
+    return MMDiTInputs(img, txt, rope_angles(shape))
+
+
+def rope_angles(shape: StageShape) -> np.ndarray:
+    """fp32 [S_kv, d/2] rotation angles in the published Flux.1 position layout (no random draw):
+    a buffer row has a 3-axis position, (0, 0, 0) for every text row and (0, gy, gx) for image
+    row gy * gw + gx (gw: the largest divisor of seq_img not above its square root); the d/2
+    pairs of a head split into axes of a0 = d // 16 pairs and two of (d/2 - a0) / 2, and pair j
+    of an axis with n pairs turns by position * 10000^(-j / n)."""
+    d = shape.head_dim
     gw = max(g for g in range(1, int(shape.seq_img ** 0.5) + 1) if shape.seq_img % g == 0)
     a0 = d // 16
     a1 = (d // 2 - a0) // 2
@@ -136,8 +142,32 @@ def mmdit_inputs(shape: StageShape, inputs: StageInputs, seed: int | None = None
     for axis, n in enumerate(axes):
         freq = 10000.0 ** (-np.arange(n, dtype=np.float64) / n)
         cols.append(pos[:, axis:axis + 1] * freq[None, :])
-    angles = np.concatenate(cols, axis=1).astype(np.float32)
-    return MMDiTInputs(img, txt, angles)
+    return np.concatenate(cols, axis=1).astype(np.float32)
+
+
+def parallel_inputs(shape: StageShape, seed: int | None = None) -> MMDiTInputs:
+    """Layer weights of the parallel (Flux.1 single-stream) block, generator PCG64(shape.seed +
+    4000), per layer in order: W_qkv [3h,h], b_qkv, W1 [rh,h], b1, W2 [h, h + rh], b2,
+    W_ada [3h,h], b_ada [3h] (all N(0, w_std^2), matrices rounded to bf16 for bf16 shapes), then
+    q_norm, k_norm [d] ~ 1 + N(0, 0.3^2).  No text-stream set; angles are rope_angles(shape).
+    The stage input, condition and drift come from stage_inputs(shape) as for the DiT block."""
+    rng = np.random.Generator(np.random.PCG64(shape.seed + 4000 if seed is None else seed))
+    h, r, d = shape.hidden, shape.mlp_ratio, shape.head_dim
+    shapes = {"w_qkv": (3 * h, h), "b_qkv": (3 * h,), "w1": (r * h, h), "b1": (r * h,), "w2": (h, h + r * h),
+              "b2": (h,), "w_ada": (3 * h, h), "b_ada": (3 * h,)}
+    std = np.float32(shape.w_std)
+    layers = []
+    for _ in range(shape.num_layers):
+        lw = {}
+        for name, shp in shapes.items():
+            a = rng.standard_normal(shp, dtype=np.float32) * std
+            if shape.dtype == "bf16" and name.startswith("w"):
+                a = to_bf16_values(a)
+            lw[name] = a
+        lw["q_norm"] = (1.0 + 0.3 * rng.standard_normal(d)).astype(np.float32)
+        lw["k_norm"] = (1.0 + 0.3 * rng.standard_normal(d)).astype(np.float32)
+        layers.append(lw)
+    return MMDiTInputs(layers, [], rope_angles(shape))
 
 
 def batch_conds(shape: StageShape, c: np.ndarray, batch: int) -> np.ndarray:

@@ -39,9 +39,10 @@ def _cfg(**kw):
     (dict(dtype=7), B.PF_ERR_INVALID_ARG),
     (dict(gelu=5), B.PF_ERR_INVALID_ARG),
     (dict(ln_eps=0.0), B.PF_ERR_INVALID_ARG),
-    (dict(flags=8), B.PF_ERR_INVALID_ARG),              # unknown block option
     (dict(flags=B.PF_STAGE_QK_NORM, dtype=B.PF_FP32), B.PF_ERR_UNSUPPORTED),   # options are bf16-only
     (dict(flags=B.PF_STAGE_DUAL_STREAM, seq_txt=0), B.PF_ERR_INVALID_ARG),     # dual stream needs text rows
+    (dict(flags=B.PF_STAGE_DUAL_STREAM | B.PF_STAGE_PARALLEL, seq_txt=8), B.PF_ERR_UNSUPPORTED),
+    (dict(flags=16), B.PF_ERR_INVALID_ARG),             # unknown block option
     (dict(heads=1, hidden=72), B.PF_ERR_UNSUPPORTED),        # bf16 needs hidden % 64 == 0
     (dict(mlp_ratio=-1), B.PF_ERR_INVALID_ARG),
     (dict(batch=-1), B.PF_ERR_INVALID_ARG),

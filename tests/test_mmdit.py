@@ -1,7 +1,8 @@
 """MM-DiT block options of the stage (the SD3 / Flux.1 models of the PipeFusion experiments):
-dual-stream text weights, per-head QK-RMSNorm and rotary Q/K, each alone and together, against
-the fp64 oracle stage with the same options (bf16-in mode), over a warm-up step and patched
-steps with drifted stale context; a guidance pair with every option; call-order errors."""
+dual-stream text weights, per-head QK-RMSNorm and rotary Q/K, each alone and together, and the
+parallel (Flux.1 single-stream) block, against the fp64 oracle stage with the same options
+(bf16-in mode), over a warm-up step and patched steps with drifted stale context; guidance
+pairs; the QK step as a component; call-order errors."""
 import dataclasses
 
 import numpy as np
@@ -172,6 +173,75 @@ def test_mmdit_patch_across_the_text_boundary():
             k, _ = st.kv_get(l)
             assert_bf16_close(k, orc.K[l], f"straddling micro-step K[{l}]",
                               floor=2.0 * max_abs(orc_p.K[l], orc.K[l]), ulps=2)
+
+
+# parallel (Flux.1 single-stream) block: (shape, qk_norm, rope, mlp_ratio)
+PARALLEL = {
+    "c4s-par": ("c4s", True, True, 4),
+    "c3s-par-qknorm": ("c3s", True, False, 4),
+    "c2s-par-rope": ("c2s", False, True, 4),
+    "c2s-par-attn-only": ("c2s", True, True, 0),
+}
+
+
+def _parallel_chain(shape, par, qk_norm, rope, batch):
+    torch = torch_cuda()
+    inputs = synth.stage_inputs(shape)
+    conds = synth.batch_conds(shape, inputs.c, batch)
+    kw = dict(heads=shape.heads, head_dim=shape.head_dim, seq_txt=shape.seq_txt, seq_img=shape.seq_img,
+              num_patches=shape.num_patches, mlp_ratio=shape.mlp_ratio, qk_norm=qk_norm,
+              rope_angles=par.angles if rope else None, parallel=True)
+    orc_b = [ref.StageOracle(par.layers, mode="bf16", **kw) for _ in range(batch)]
+    orc_p = [ref.StageOracle(par.layers, mode="bf16p", **kw) for _ in range(batch)]
+    S, h, L = shape.seq_kv, shape.hidden, shape.num_layers
+    with Stage(shape, batch=batch, qk_norm=qk_norm, rope=rope, parallel=True) as st:
+        st.load(par.layers)
+        if rope:
+            st.set_rope(par.angles)
+        x = dev(torch, np.stack([inputs.x] * batch) if batch > 1 else inputs.x)
+        c = dev(torch, conds if batch > 1 else inputs.c)
+        out = torch.empty_like(x)
+        for s in range(3 if batch == 1 else 2):
+            warm = s == 0
+            if s > 0:
+                for b in range(batch):
+                    seed = shape.seed + 100 * s + 10 * b
+                    noise = [(synth.randn((S, h), seed + 2 * l, std=shape.sigma_kv),
+                              synth.randn((S, h), seed + 2 * l + 1, std=shape.sigma_kv)) for l in range(L)]
+                    st.add_noise(noise, sample=b)
+                    orc_b[b].add_noise(noise)
+                    orc_p[b].add_noise(noise)
+            print(f"[parallel] {shape.name} r={shape.mlp_ratio} batch {batch} step {s} warmup={warm}", flush=True)
+            st.run_step(x, c, warmup=warm, out=out)
+            got = host(out).reshape(batch, S, h)
+            for b in range(batch):
+                want = orc_b[b].step(inputs.x, conds[b], warmup=warm)
+                want_p = orc_p[b].step(inputs.x, conds[b], warmup=warm)
+                assert_close(got[b], want, f"parallel step {s} sample {b} vs bf16-in oracle",
+                             max_abs_tol=stage_output_max_abs_tol(want, want_p))
+                for l in range(L):
+                    k, v = st.kv_get(l, sample=b)
+                    assert_bf16_close(k, orc_b[b].K[l], f"parallel step {s} sample {b} K[{l}]",
+                                      floor=2.0 * max_abs(orc_p[b].K[l], orc_b[b].K[l]),
+                                      ulps=2 if qk_norm or rope else 1)
+                    assert_bf16_close(v, orc_b[b].V[l], f"parallel step {s} sample {b} V[{l}]",
+                                      floor=2.0 * max_abs(orc_p[b].V[l], orc_b[b].V[l]))
+        if batch > 1:
+            assert max_abs(got[0], got[1]) > 1e-3
+
+
+@pytest.mark.parametrize("case", sorted(PARALLEL))
+def test_parallel_block_stage_chain(case):
+    """The parallel block (attention and MLP side by side, one fused output projection) against
+    the oracle's, over a warm-up step and two drifted patched steps."""
+    name, qk_norm, rope, r = PARALLEL[case]
+    shape = dataclasses.replace(SHAPES[name], mlp_ratio=r)
+    _parallel_chain(shape, synth.parallel_inputs(shape), qk_norm, rope, 1)
+
+
+def test_parallel_block_guidance_pair():
+    shape = SHAPES["c4s"]
+    _parallel_chain(shape, synth.parallel_inputs(shape), True, True, 2)
 
 
 @pytest.mark.parametrize("d,heads,rows,off,norm,rope", [

@@ -435,6 +435,7 @@ def main():
                    "num_layers": shape.num_layers, "hidden": shape.hidden, "heads": shape.heads,
                    "head_dim": shape.head_dim, "seq_kv": shape.seq_kv, "num_patches": shape.num_patches,
                    "patch_rows": shape.patch_rows, "parallelism": "single GPU stage"},
+        "image_tokens_per_s": nb * shape.seq_img / med,
         "stage_tflops": nb * shape.flops_per_step() / med / 1e12,
         "stage_frac_peak": nb * shape.flops_per_step() / med / 1e12 / PEAK_BF16_TFLOPS,
         "attention_tflops": attn_tflops,

@@ -304,7 +304,10 @@ pf_status pf_ln_modulate(const float* x, int64_t rows, int32_t hidden, const flo
  * PF_GEMM_TILE=128x64, 256 or 128d forces another kernel (128 features x 64 tokens with the
  * same ring; or a deep ring: 256 x 256 with 4 stages, 128 x 128 with 8 stages, one workgroup
  * per CU), and PF_GEMM_SPLIT=s forces s k slices where the workspace allows; both are read on
- * every call, so set them before pf_gemm_workspace_size as well. */
+ * every call, so set them before pf_gemm_workspace_size as well.  Inside a stage, when a
+ * gated-residual projection is k-split, its reduce pass also computes the LayerNorm +
+ * modulation that reads the updated rows (same bits as the separate kernel);
+ * PF_FUSE_LN=0 turns that off. */
 pf_status pf_gemm(const void* a, int64_t lda, const void* w, const float* bias, int64_t m,
                   int64_t n, int64_t k, int32_t epi, void* c, int64_t ldc, const float* gate,
                   int32_t dtype, void* workspace, uint64_t workspace_bytes, void* stream);

@@ -571,6 +571,12 @@ static int gemm_kind_override() {
 }
 
 // PF_GEMM_SPLIT=s forces s k slices where the workspace and k allow them (for measurements).
+// PF_FUSE_LN=0 turns the fused reduce + LayerNorm off (read on every call).
+static bool ln_fusion_enabled() {
+  const char* e = getenv("PF_FUSE_LN");
+  return !(e && e[0] == '0');
+}
+
 static int gemm_split_override() {
   const char* v = std::getenv("PF_GEMM_SPLIT");
   if (!v) return 0;
@@ -625,7 +631,8 @@ static constexpr auto gemm_deep128 = gemm_deep_kernel<128, 128, 8, EPI, SPLIT>;
 template <int EPI>
 static void launch_gemm_epi(const void* a, int64_t lda, const void* w, const float* bias, int64_t m, int64_t n,
                             int64_t k, void* c, int64_t ldc, const float* gate, int dtype, void* ws,
-                            size_t ws_bytes, hipStream_t s, const QkvSplice& sp, const RowGroups& rg) {
+                            size_t ws_bytes, hipStream_t s, const QkvSplice& sp, const RowGroups& rg,
+                            const LnAfter* ln, bool* ln_done) {
   if (dtype == kDtypeBF16) {
     const bf16* A = static_cast<const bf16*>(a);
     const bf16* Wt = static_cast<const bf16*>(w);
@@ -654,9 +661,15 @@ static void launch_gemm_epi(const void* a, int64_t lda, const void* w, const flo
     else PF_GEMM_LAUNCH(gemm_small128);
 #undef PF_GEMM_LAUNCH
     if (used > 1) {
-      const int64_t units = m * (n / 4);
-      hipLaunchKernelGGL(gemm_reduce_kernel<EPI>, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, s, part, used,
-                         m, n, bias, c, ldc, gate, sp, rg);
+      if (EPI == kEpiGatedResidual && ln && ln_fusion_enabled() && n <= kMaxHidden) {
+        // the reduce pass already holds whole updated rows: it applies the next LayerNorm too
+        (void)launch_reduce_residual_ln(part, used, m, (int)n, bias, static_cast<float*>(c), ldc, gate, rg, *ln, s);
+        if (ln_done) *ln_done = true;
+      } else {
+        const int64_t units = m * (n / 4);
+        hipLaunchKernelGGL(gemm_reduce_kernel<EPI>, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, s, part,
+                           used, m, n, bias, c, ldc, gate, sp, rg);
+      }
     }
   } else {
     const int tiles_n = (int)((n + 63) / 64);
@@ -668,20 +681,26 @@ static void launch_gemm_epi(const void* a, int64_t lda, const void* w, const flo
 
 hipError_t launch_gemm(const void* a, int64_t lda, const void* w, const float* bias, int64_t m, int64_t n, int64_t k,
                        int epi, void* c, int64_t ldc, const float* gate, int dtype, void* ws, size_t ws_bytes,
-                       hipStream_t s, const QkvSplice* splice, const RowGroups* groups) {
+                       hipStream_t s, const QkvSplice* splice, const RowGroups* groups, const LnAfter* ln,
+                       bool* ln_done) {
+  if (ln_done) *ln_done = false;
   if (m <= 0) return hipSuccess;
   const QkvSplice sp = splice ? *splice : QkvSplice{nullptr, nullptr, 0, 0, m, 0, 0};
   const RowGroups rg = groups ? *groups : RowGroups{m, 0, 0};
   if (sp.grp_rows <= 0 || rg.rows <= 0) return hipErrorInvalidValue;
   switch (epi) {
-    case kEpiStore: launch_gemm_epi<kEpiStore>(a, lda, w, bias, m, n, k, c, ldc, gate, dtype, ws, ws_bytes, s, sp, rg); break;
-    case kEpiGeluTanh: launch_gemm_epi<kEpiGeluTanh>(a, lda, w, bias, m, n, k, c, ldc, gate, dtype, ws, ws_bytes, s, sp, rg); break;
-    case kEpiGeluErf: launch_gemm_epi<kEpiGeluErf>(a, lda, w, bias, m, n, k, c, ldc, gate, dtype, ws, ws_bytes, s, sp, rg); break;
+    case kEpiStore: launch_gemm_epi<kEpiStore>(a, lda, w, bias, m, n, k, c, ldc, gate, dtype, ws, ws_bytes, s, sp, rg, nullptr, nullptr); break;
+    case kEpiGeluTanh: launch_gemm_epi<kEpiGeluTanh>(a, lda, w, bias, m, n, k, c, ldc, gate, dtype, ws, ws_bytes, s, sp, rg, nullptr, nullptr); break;
+    case kEpiGeluErf: launch_gemm_epi<kEpiGeluErf>(a, lda, w, bias, m, n, k, c, ldc, gate, dtype, ws, ws_bytes, s, sp, rg, nullptr, nullptr); break;
     case kEpiQkvSplice:
       if (dtype != kDtypeBF16 || !splice) return hipErrorInvalidValue;
-      launch_gemm_epi<kEpiQkvSplice>(a, lda, w, bias, m, n, k, c, ldc, gate, dtype, ws, ws_bytes, s, sp, rg);
+      launch_gemm_epi<kEpiQkvSplice>(a, lda, w, bias, m, n, k, c, ldc, gate, dtype, ws, ws_bytes, s, sp, rg, nullptr,
+                                     nullptr);
       break;
-    default: launch_gemm_epi<kEpiGatedResidual>(a, lda, w, bias, m, n, k, c, ldc, gate, dtype, ws, ws_bytes, s, sp, rg); break;
+    default:
+      launch_gemm_epi<kEpiGatedResidual>(a, lda, w, bias, m, n, k, c, ldc, gate, dtype, ws, ws_bytes, s, sp, rg, ln,
+                                         ln_done);
+      break;
   }
   return hipGetLastError();
 }

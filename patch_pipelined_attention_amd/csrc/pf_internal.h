@@ -119,13 +119,34 @@ hipError_t launch_ln_modulate(const float* x, int64_t rows, int hidden, const fl
 hipError_t launch_adaln(const float* cond, const void* w, const float* b, int hidden, float* mod,
                         int dtype, hipStream_t s, int chunks = 6);
 
+// The LayerNorm + modulation that follows a gated-residual projection (the next sublayer's):
+// y [m, n] bf16 (row stride n) = LN(x)(1 + scale) + shift of the updated residual rows, with
+// each sample's shift / scale at + g * groups->p_stride.
+struct LnAfter {
+  const float* shift;
+  const float* scale;
+  float eps;
+  void* y;
+};
+
 // `ws` (may be NULL) is scratch for the k-split of grids too small to fill the GPU.
 // `groups` (NULL: one sample) applies to the gated residual: each sample's rows of c and its
-// gate vector.
+// gate vector.  `ln` (gated residual, bf16 only): when the product is k-split, its reduce pass
+// also computes the LayerNorm + modulation of the updated rows and sets *ln_done (otherwise
+// *ln_done is false and the caller runs launch_ln_modulate itself).
 hipError_t launch_gemm(const void* a, int64_t lda, const void* w, const float* bias, int64_t m,
                        int64_t n, int64_t k, int epi, void* c, int64_t ldc, const float* gate,
                        int dtype, void* ws, size_t ws_bytes, hipStream_t s,
-                       const QkvSplice* splice = nullptr, const RowGroups* groups = nullptr);
+                       const QkvSplice* splice = nullptr, const RowGroups* groups = nullptr,
+                       const LnAfter* ln = nullptr, bool* ln_done = nullptr);
+
+// Reduce of a k-split gated-residual product fused with the following LayerNorm + modulation:
+// per row m, y = sum_s part[s][m][:] + bias, x_m += gate_g * y (stored), then ln.y[m] =
+// LN(x_m)(1 + scale_g) + shift_g in bf16.  Same arithmetic, in the same order, as the plain
+// reduce followed by launch_ln_modulate, so the results are bit-identical.
+hipError_t launch_reduce_residual_ln(const float* part, int n_split, int64_t m, int n, const float* bias, float* x,
+                                     int64_t ldx, const float* gate, const RowGroups& rg, const LnAfter& ln,
+                                     hipStream_t s);
 
 // Scratch bytes the bf16 GEMM would use for its k-split at this shape (0: no split).
 size_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k);

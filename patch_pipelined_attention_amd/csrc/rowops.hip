@@ -114,6 +114,132 @@ hipError_t launch_ln_modulate(const float* x, int64_t rows, int hidden, const fl
 }
 
 // ---------------------------------------------------------------------------------
+// Reduce of a k-split gated-residual projection fused with the next LayerNorm + modulation,
+// one wavefront per row.  Per 4 columns: the slices summed in order, + bias, x += gate * y (the
+// reduce kernel's arithmetic); the updated row stays in registers for the LayerNorm (the LN
+// kernel's arithmetic and reduction order), so both results match the unfused pair bit for bit
+// while x is read once and one launch disappears.
+// ---------------------------------------------------------------------------------
+template <int NS>
+__global__ __launch_bounds__(256) void reduce_residual_ln_kernel(const float* __restrict__ part, int n_split,
+                                                                 int64_t rows, int hidden,
+                                                                 const float* __restrict__ bias,
+                                                                 float* __restrict__ x, int64_t ldx,
+                                                                 const float* __restrict__ gate, RowGroups grp,
+                                                                 const float* __restrict__ shift,
+                                                                 const float* __restrict__ scale, float eps,
+                                                                 bf16* __restrict__ y) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int n4 = hidden >> 2;
+  const int64_t g = row / grp.rows;
+  float* xr = x + g * grp.x_stride + (row - g * grp.rows) * ldx;
+  const float* gr = gate + g * grp.p_stride;
+  // chunks in batches of kBatch, every slice unrolled to kMaxGemmSplit (indices past n_split
+  // and past the row clamped, their terms skipped), so a batch's loads are all in flight
+  constexpr int kBatch = 4;
+  float4 v[NS];
+#pragma unroll
+  for (int i0 = 0; i0 < NS; i0 += kBatch) {
+    float4 pv[kBatch][kMaxGemmSplit], bv[kBatch], gv[kBatch], xv[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      if (i0 + j >= NS) break;
+      const int idx = lane + (i0 + j) * 64 < n4 ? lane + (i0 + j) * 64 : n4 - 1;
+      const int64_t f = (int64_t)idx * 4;
+#pragma unroll
+      for (int s2 = 0; s2 < kMaxGemmSplit; ++s2) {
+        const int64_t sc = s2 < n_split ? s2 : n_split - 1;
+        pv[j][s2] = *reinterpret_cast<const float4*>(part + (sc * rows + row) * hidden + f);
+      }
+      bv[j] = *reinterpret_cast<const float4*>(bias + f);
+      gv[j] = *reinterpret_cast<const float4*>(gr + f);
+      xv[j] = *reinterpret_cast<const float4*>(xr + f);
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int i = i0 + j;
+      if (i >= NS) break;
+      float4 acc = pv[j][0];
+#pragma unroll
+      for (int s2 = 1; s2 < kMaxGemmSplit; ++s2) {
+        if (s2 < n_split) {
+          acc.x += pv[j][s2].x;
+          acc.y += pv[j][s2].y;
+          acc.z += pv[j][s2].z;
+          acc.w += pv[j][s2].w;
+        }
+      }
+      acc.x += bv[j].x;
+      acc.y += bv[j].y;
+      acc.z += bv[j].z;
+      acc.w += bv[j].w;
+      float4 cv = xv[j];
+      cv.x += gv[j].x * acc.x;
+      cv.y += gv[j].y * acc.y;
+      cv.z += gv[j].z * acc.z;
+      cv.w += gv[j].w * acc.w;
+      v[i] = cv;
+      if (lane + i * 64 < n4) *reinterpret_cast<float4*>(xr + (int64_t)(lane + i * 64) * 4) = cv;
+    }
+  }
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < NS; ++i)
+    if (lane + i * 64 < n4) sum += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+  const float inv_h = 1.0f / (float)hidden;
+  const float mean = wave_sum(sum) * inv_h;
+  float sq = 0.f;
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    if (lane + i * 64 < n4) {
+      const float a = v[i].x - mean, b = v[i].y - mean, c = v[i].z - mean, d = v[i].w - mean;
+      sq += (a * a + b * b) + (c * c + d * d);
+    }
+  }
+  const float var = wave_sum(sq) * inv_h;
+  const float rstd = 1.0f / sqrtf(var + eps);
+  const float4* sh4 = reinterpret_cast<const float4*>(shift + g * grp.p_stride);
+  const float4* sc4 = reinterpret_cast<const float4*>(scale + g * grp.p_stride);
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    const int idx = lane + i * 64;
+    if (idx < n4) {
+      const float4 sh = sh4[idx], sc = sc4[idx];
+      const float o0 = (v[i].x - mean) * rstd * (1.0f + sc.x) + sh.x;
+      const float o1 = (v[i].y - mean) * rstd * (1.0f + sc.y) + sh.y;
+      const float o2 = (v[i].z - mean) * rstd * (1.0f + sc.z) + sh.z;
+      const float o3 = (v[i].w - mean) * rstd * (1.0f + sc.w) + sh.w;
+      bf16x4 o = {(bf16)o0, (bf16)o1, (bf16)o2, (bf16)o3};
+      *reinterpret_cast<bf16x4*>(y + row * hidden + idx * 4) = o;
+    }
+  }
+}
+
+template <int NS>
+static void launch_rrl_ns(int ns, dim3 grid, const float* part, int n_split, int64_t rows, int hidden,
+                          const float* bias, float* x, int64_t ldx, const float* gate, const RowGroups& g,
+                          const LnAfter& ln, hipStream_t s) {
+  if constexpr (NS > 1) {
+    if (ns < NS) return launch_rrl_ns<NS - 1>(ns, grid, part, n_split, rows, hidden, bias, x, ldx, gate, g, ln, s);
+  }
+  hipLaunchKernelGGL((reduce_residual_ln_kernel<NS>), grid, dim3(256), 0, s, part, n_split, rows, hidden, bias, x, ldx,
+                     gate, g, ln.shift, ln.scale, ln.eps, static_cast<bf16*>(ln.y));
+}
+
+hipError_t launch_reduce_residual_ln(const float* part, int n_split, int64_t m, int n, const float* bias, float* x,
+                                     int64_t ldx, const float* gate, const RowGroups& rg, const LnAfter& ln,
+                                     hipStream_t s) {
+  if (m <= 0) return hipSuccess;
+  constexpr int kSlots = kMaxHidden / 256;
+  const int ns = (n / 4 + 63) / 64;
+  if (ns < 1 || ns > kSlots || n % 4 != 0 || rg.rows <= 0) return hipErrorInvalidValue;
+  launch_rrl_ns<kSlots>(ns, dim3((unsigned)((m + 3) / 4)), part, n_split, m, n, bias, x, ldx, gate, rg, ln, s);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------
 // Q and K of one part of a micro-step, in place (bf16): per (row, head), an optional RMSNorm
 // (eps 1e-6) times gamma [D], then an optional rotary embedding of the pairs (2k, 2k+1) by
 // angles[buffer row][k].  Rows r < nb * n: sample g = r / n, local row i = r - g n, buffer

@@ -699,7 +699,13 @@ static pf_status run_rows(pf_stage* st, int64_t off, int64_t n, float* x, int64_
   char* const qkv = (char*)st->qkv;
   char* const h1 = (char*)st->h1;
   char* const o = (char*)st->o;
-  for (auto& lm : st->layers) {
+  // a k-split residual product whose reduce pass also ran the next LayerNorm leaves that
+  // part's h1 ready for the next layer
+  bool ln1_ready[2] = {false, false};
+  const int n_layers = (int)st->layers.size();
+  for (int li = 0; li < n_layers; ++li) {
+    LayerMem& lm = st->layers[li];
+    const LayerMem* next = li + 1 < n_layers ? &st->layers[li + 1] : nullptr;
     hipError_t e;
     const int v_layout = dt == PF_BF16 ? kLayoutK8 : kLayoutRows;
     for (int pi = 0; pi < n_parts; ++pi) {
@@ -709,8 +715,10 @@ static pf_status run_rows(pf_stage* st, int64_t off, int64_t n, float* x, int64_
       const int64_t rows = nb * p.n;
       char* h1p = h1 + (size_t)(p.srow * h) * es;
       char* qkvp = qkv + (size_t)(p.srow * 3 * h) * es;
-      if ((e = launch_ln_modulate(p.x, rows, (int)h, ws.mod, ws.mod + h, eps, h1p, dt, s, &xg)) != hipSuccess)
+      if (!ln1_ready[pi] &&
+          (e = launch_ln_modulate(p.x, rows, (int)h, ws.mod, ws.mod + h, eps, h1p, dt, s, &xg)) != hipSuccess)
         return stage_hip_fail(st, e, "ln_modulate");
+      ln1_ready[pi] = false;
       if (dt == PF_BF16) {
         // QKV projection with the splice in its epilogue: Q to the scratch, each sample's fresh K
         // and V straight into rows [p.off, p.off + p.n) of its own buffer (no other row changes)
@@ -759,25 +767,35 @@ static pf_status run_rows(pf_stage* st, int64_t off, int64_t n, float* x, int64_
       char* h1p = h1 + (size_t)(p.srow * h) * es;
       char* op = o + (size_t)(p.srow * ld_o) * es;
       char* up = (char*)st->u + (size_t)(p.srow * ld_u) * es;
+      // the LayerNorm that follows a layer's last residual product: the next layer's first
+      const WeightSet* nws = next ? p.pick(*next) : nullptr;
+      const LnAfter ln_next{nws ? nws->mod : nullptr, nws ? nws->mod + h : nullptr, eps, h1p};
       if (par) {
         // x += gate * ([o, u] W2^T + b2): one product over the side-by-side rows
         if ((e = launch_gemm(op, ld_o, ws.w2, ws.b2, rows, h, h + rh, kEpiGatedResidual, p.x, h, ws.mod + 2 * h, dt,
-                             st->gemm_ws, st->gemm_ws_bytes, s, nullptr, &xg)) != hipSuccess)
+                             st->gemm_ws, st->gemm_ws_bytes, s, nullptr, &xg, nws ? &ln_next : nullptr,
+                             &ln1_ready[pi])) != hipSuccess)
           return stage_hip_fail(st, e, "linear2 gemm (parallel)");
         continue;
       }
+      const LnAfter ln_mlp{ws.mod + 3 * h, ws.mod + 4 * h, eps, h1p};
+      const LnAfter* ln_out = rh > 0 ? &ln_mlp : (nws ? &ln_next : nullptr);
+      bool ln_done = false;
       if ((e = launch_gemm(op, h, ws.w_o, ws.b_o, rows, h, h, kEpiGatedResidual, p.x, h, ws.mod + 2 * h, dt,
-                           st->gemm_ws, st->gemm_ws_bytes, s, nullptr, &xg)) != hipSuccess)
+                           st->gemm_ws, st->gemm_ws_bytes, s, nullptr, &xg, ln_out, &ln_done)) != hipSuccess)
         return stage_hip_fail(st, e, "out-proj gemm");
+      if (rh == 0) ln1_ready[pi] = ln_done;
       if (rh > 0) {
-        if ((e = launch_ln_modulate(p.x, rows, (int)h, ws.mod + 3 * h, ws.mod + 4 * h, eps, h1p, dt, s, &xg)) !=
-            hipSuccess)
+        if (!ln_done &&
+            (e = launch_ln_modulate(p.x, rows, (int)h, ws.mod + 3 * h, ws.mod + 4 * h, eps, h1p, dt, s, &xg)) !=
+                hipSuccess)
           return stage_hip_fail(st, e, "ln_modulate (mlp)");
         if ((e = launch_gemm(h1p, h, ws.w1, ws.b1, rows, rh, h, gelu_epi, up, ld_u, nullptr, dt, st->gemm_ws,
                              st->gemm_ws_bytes, s)) != hipSuccess)
           return stage_hip_fail(st, e, "mlp up gemm");
         if ((e = launch_gemm(up, ld_u, ws.w2, ws.b2, rows, h, rh, kEpiGatedResidual, p.x, h, ws.mod + 5 * h, dt,
-                             st->gemm_ws, st->gemm_ws_bytes, s, nullptr, &xg)) != hipSuccess)
+                             st->gemm_ws, st->gemm_ws_bytes, s, nullptr, &xg, nws ? &ln_next : nullptr,
+                             &ln1_ready[pi])) != hipSuccess)
           return stage_hip_fail(st, e, "mlp down gemm");
       }
     }

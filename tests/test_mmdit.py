@@ -323,3 +323,49 @@ def test_mmdit_call_order_errors():
         with pytest.raises(B.PFError) as e:
             st.set_rope(mm.angles)
         assert e.value.status == B.PF_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("case", ["c2s-dit", "c2-full-L2", "c4s-mmdit", "c4s-parallel", "c2s-pair", "c4s-attn-only"])
+def test_fused_reduce_layernorm_is_bit_identical(case, monkeypatch):
+    """A k-split residual product whose reduce pass also computes the next LayerNorm + modulation
+    gives the same bits as the plain reduce followed by the LayerNorm kernel (PF_FUSE_LN=0):
+    outputs and every K/V buffer, over a warm-up step and a patched step."""
+    torch = torch_cuda()
+    name = case.split("-")[0]
+    shape = {"c2": dataclasses.replace(C2, num_layers=2)}.get(name, SHAPES.get(name))
+    if case == "c4s-attn-only":
+        shape = dataclasses.replace(shape, mlp_ratio=0)
+    inputs = synth.stage_inputs(shape)
+    batch = 2 if case.endswith("pair") else 1
+    opts, layers, txt, angles = {}, inputs.layers, None, None
+    if case.endswith("mmdit"):
+        mm = synth.mmdit_inputs(shape, inputs)
+        opts, layers, txt, angles = dict(qk_norm=True, dual_stream=True, rope=True), mm.layers, mm.txt_layers, mm.angles
+    elif case.endswith("parallel"):
+        par = synth.parallel_inputs(shape)
+        opts, layers, angles = dict(qk_norm=True, rope=True, parallel=True), par.layers, par.angles
+    x = dev(torch, np.stack([inputs.x] * batch) if batch > 1 else inputs.x)
+    c = dev(torch, synth.batch_conds(shape, inputs.c, batch) if batch > 1 else inputs.c)
+    results = []
+    for fuse in ("1", "0"):
+        monkeypatch.setenv("PF_FUSE_LN", fuse)
+        with Stage(shape, batch=batch, **opts) as st:
+            st.load(layers, txt)
+            if angles is not None:
+                st.set_rope(angles)
+            outs = []
+            for warm in (True, False):
+                print(f"[fused-ln] {case} fuse={fuse} warmup={warm}", flush=True)
+                out = torch.empty_like(x)
+                st.run_step(x, c, warmup=warm, out=out)
+                torch.cuda.synchronize()
+                outs.append(out.cpu().numpy())
+            kv = [[t.view(torch.int16).cpu().numpy() for t in st.kv_raw(l, b)]
+                  for l in range(shape.num_layers) for b in range(batch)]
+            results.append((outs, kv))
+    (o1, kv1), (o0, kv0) = results
+    for a, b in zip(o1, o0):
+        np.testing.assert_array_equal(a, b)
+    for (k1, v1), (k0, v0) in zip(kv1, kv0):
+        np.testing.assert_array_equal(k1, k0)
+        np.testing.assert_array_equal(v1, v0)

@@ -45,9 +45,9 @@ def parse():
     ap.add_argument("--breakdown", action="store_true", help="also time every kernel of a patch-layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
-    ap.add_argument("--probe", choices=["attention", "copy"],
-                    help="only launch the dominant kernel at the bench launch shape (or a plain 1 GiB copy) "
-                         "--probe-iters times; a target for rocprofv3 counter runs")
+    ap.add_argument("--probe", choices=PROBES,
+                    help="only launch one kernel of a patch-layer at the stage's launch shape (or a plain 1 GiB "
+                         "copy) --probe-iters times; a target for rocprofv3 counter runs")
     ap.add_argument("--probe-iters", type=int, default=3)
     ap.add_argument("--pmc-summary", metavar="DIR",
                     help="print per-kernel average counters of the rocprofv3 counter CSVs under DIR, then exit")
@@ -276,9 +276,15 @@ def cpu_baseline(shape, inputs, budget_s, mm=None):
             "host_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0))}
 
 
+PROBES = ["attention", "copy", "ln_modulate", "gemm_qkv_splice", "kv_splice_entry", "gemm_out", "gemm_up_gelu",
+          "gemm_down"]
+
+
 def probe(args):
-    """Launch only the dominant kernel at the bench's launch shape (or a 1 GiB device copy)
-    args.probe_iters times, then exit: the program rocprofv3 counter runs profile."""
+    """Launch only one kernel at the bench's launch shape (or a 1 GiB device copy)
+    args.probe_iters times, then exit: the program rocprofv3 counter runs profile.  The
+    attention probe runs over its own random buffer; the others are the --breakdown probes
+    (the last patch's launch shapes over a one-layer stage of the config)."""
     import torch
     from patch_pipelined_attention_amd import binding as B
     from patch_pipelined_attention_amd.configs import CONFIGS
@@ -294,6 +300,24 @@ def probe(args):
         return
     B.lib()
     shape = CONFIGS[args.config]
+    if args.probe != "attention":
+        import dataclasses
+        import numpy as np
+        from patch_pipelined_attention_amd import synth
+        from patch_pipelined_attention_amd.stage import Stage
+        one = dataclasses.replace(shape, num_layers=1)
+        inputs = synth.stage_inputs(one)
+        with Stage(one) as st:
+            st.load(inputs.layers)
+            wdev = {k: torch.from_numpy(np.ascontiguousarray(a)).cuda().to(torch.bfloat16 if k.startswith("w")
+                                                                             else torch.float32)
+                    for k, a in inputs.layers[0].items()}
+            fn = kernel_probes(torch, B, st, one, wdev)[args.probe][0]
+            for _ in range(args.probe_iters):
+                fn()
+            torch.cuda.synchronize()
+        print(f"[probe] {args.probe} {shape.name} x {args.probe_iters}", file=sys.stderr, flush=True)
+        return
     h, P, S = shape.hidden, shape.patch_rows, shape.seq_kv
     qkv = torch.randn((P, 3 * h), device="cuda").to(torch.bfloat16)
     k = torch.randn((S, h), device="cuda").to(torch.bfloat16)

@@ -102,9 +102,20 @@ def pmc_summary(d: str) -> None:
         print(f"{ctr:16s} {sum(vals) / len(vals):14.1f} avg over {len(vals)} dispatches  {kern[:90]}")
 
 
-def time_kernel(torch, fn, iters=20, warm=3):
-    """Average duration (s) of fn() over `iters` launches, HIP events on the current stream."""
+def time_kernel(torch, fn, iters=20, warm=3, warm_s=0.05):
+    """Average duration (s) of fn() over `iters` launches, HIP events on the current stream.
+    Warm-up: `warm` launches, then more until about `warm_s` seconds of launches have run (a
+    few launches right after other work run slower, up to 20% for the long attention calls)."""
     for _ in range(warm):
+        fn()
+    s0 = torch.cuda.Event(enable_timing=True)
+    e0 = torch.cuda.Event(enable_timing=True)
+    s0.record()
+    fn()
+    e0.record()
+    e0.synchronize()
+    one = max(s0.elapsed_time(e0) / 1e3, 1e-6)
+    for _ in range(min(1000, int(warm_s / one))):
         fn()
     s = torch.cuda.Event(enable_timing=True)
     e = torch.cuda.Event(enable_timing=True)

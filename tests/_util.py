@@ -34,22 +34,35 @@ def bf16_ulp(v):
     return np.ldexp(1.0, np.maximum(e, -125) - 8)
 
 
-def assert_bf16_close(got, want, what: str, floor: float = 0.0, ulps: int = 1):
-    """Stored bf16 tensors: each element within max(2e-2, `ulps` bf16 ulps of the oracle value,
-    floor) (a rounding flip at |v| >= 4 is 2^-5 > 2e-2), and rel-L2 within the contract tolerance.
-    `floor` is the bf16-probability noise floor of a chained comparison (0 when teacher-forced).
-    `ulps` = 2 for values rounded twice (a bf16 projection output, then a function of it rounded
-    again): a flip at the first rounding carries into the second result as up to one ulp."""
+def assert_bf16_close(got, want, what: str, floor: float = 0.0, ulps: int = 1, scale=None):
+    """Stored bf16 tensors: each element within max(2e-2, `ulps` bf16 ulps of `scale` (default:
+    the oracle value), floor) (a rounding flip at |v| >= 4 is 2^-5 > 2e-2), and rel-L2 within the
+    contract tolerance.  `floor` is the bf16-probability noise floor of a chained comparison (0
+    when teacher-forced).
+
+    Values rounded twice (a bf16 projection output, then a function of it rounded again, as Q/K
+    after QK-norm or RoPE) take ulps = 3: a one-ulp flip of the first rounding is a relative error
+    of at most 2^-7, i.e. under 2 ulps of the result, plus one ulp between the two final roundings.
+    A rotation keeps the error vector's length but not the components' sizes, so for rotated
+    pairs `scale` is the pair's norm (pair_norms)."""
     got = np.asarray(got, np.float64)
     want = np.asarray(want, np.float64)
     err = np.abs(got - want)
-    lim = np.maximum(max(MAX_ABS, floor), ulps * bf16_ulp(want))
+    lim = np.maximum(max(MAX_ABS, floor), ulps * bf16_ulp(want if scale is None else scale))
     rl = rel_l2(got, want)
     worst = float((err / lim).max())
     print(f"[parity] {what}: max_abs={err.max():.3e} worst/limit={worst:.2f} rel_l2={rl:.3e}", flush=True)
     assert np.all(np.isfinite(got)), f"{what}: non-finite"
     assert worst <= 1.0, f"{what}: an element is off by more than max(2e-2, {ulps} bf16 ulp)"
     assert rl <= REL_L2, f"{what}: rel_l2 {rl:.3e} > {REL_L2}"
+
+
+def pair_norms(a):
+    """|(a[.., 2k], a[.., 2k+1])| broadcast back to both elements of each pair (last axis even)."""
+    a = np.asarray(a, np.float64)
+    p = a.reshape(a.shape[:-1] + (a.shape[-1] // 2, 2))
+    n = np.sqrt((p * p).sum(axis=-1, keepdims=True))
+    return np.broadcast_to(n, p.shape).reshape(a.shape)
 
 
 def torch_cuda():

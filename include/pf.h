@@ -301,9 +301,10 @@ pf_status pf_ln_modulate(const float* x, int64_t rows, int32_t hidden, const flo
  * calls sharing a workspace must not overlap in time (one stream, or ordered streams).
  * pf_gemm_workspace_size gives the bytes that allow the split the library would choose.
  * Tiles are 128 x 128 (a 2-stage ring, two workgroups per CU); the environment variable
- * PF_GEMM_TILE=128x64, 256 or 128d forces another kernel (128 features x 64 tokens with the
- * same ring; or a deep ring: 256 x 256 with 4 stages, 128 x 128 with 8 stages, one workgroup
- * per CU), and PF_GEMM_SPLIT=s forces s k slices where the workspace allows; both are read on
+ * PF_GEMM_TILE=128x64, 256, 128d or 256x128 forces another kernel (128 features x 64 tokens
+ * with the same ring; or a deep ring: 256 x 256 with 4 stages, 128 x 128 with 8 stages, one
+ * workgroup per CU; 256 features x 128 tokens with 3 stages, two per CU), and
+ * PF_GEMM_SPLIT=s forces s k slices where the workspace allows; both are read on
  * every call, so set them before pf_gemm_workspace_size as well.  Inside a stage, when a
  * gated-residual projection is k-split, its reduce pass also computes the LayerNorm +
  * modulation that reads the updated rows (same bits as the separate kernel);

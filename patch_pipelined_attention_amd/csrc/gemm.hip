@@ -7,10 +7,9 @@
 // per lane, one token and 4 consecutive output features per 8-row group, so every
 // epilogue stores 4 contiguous values per access (8 B bf16 / 16 B fp32).
 //
-// Tiles: 128 x 128 with a 2-stage ring, two workgroups per CU.  A 128 x 64 variant and two
-// deep-ring variants (256 x 256 and 128 x 128, one workgroup per CU) can be forced for
-// comparison.  Grids too
-// small to fill the GPU split k: every slice writes its fp32 partial tile and a reduce pass
+// Tiles: 128 x 128 with a 2-stage ring, two workgroups per CU.  A 128 x 64 variant and three
+// deep-ring variants (256 x 256 and 128 x 128 with one workgroup per CU, 256 x 128 with two)
+// can be forced for comparison.  Grids too small to fill the GPU split k: every slice writes its fp32 partial tile and a reduce pass
 // sums the slices in order (deterministic) and applies the epilogue.  (A last-arriving-slice
 // merge inside the GEMM measured slower on MI355X: the partials cross XCDs, whose L2s are
 // not coherent, so they must be written through and read back from the device-coherent
@@ -316,8 +315,8 @@ __device__ __forceinline__ void wait_vmcnt() {
 //     highest per-k rate, for long reductions.
 //   128 x 128, 8 stages: seven tiles (224 k values) in flight hide the load latency that
 //     bounds a lone 2-stage workgroup, for grids with about one tile per CU.
-template <int BF, int BT, int NSTAGE, int EPI, bool SPLIT>
-__global__ __launch_bounds__(256, 1) void gemm_deep_kernel(const bf16* __restrict__ A, int64_t lda,
+template <int BF, int BT, int NSTAGE, int OCC, int EPI, bool SPLIT>
+__global__ __launch_bounds__(256, OCC) void gemm_deep_kernel(const bf16* __restrict__ A, int64_t lda,
                                                            const bf16* __restrict__ W, const float* __restrict__ bias,
                                                            int64_t M, int64_t N, int64_t K, void* __restrict__ C,
                                                            int64_t ldc, const float* __restrict__ gate, int tiles_n,
@@ -331,7 +330,8 @@ __global__ __launch_bounds__(256, 1) void gemm_deep_kernel(const bf16* __restric
   constexpr int NINST = UNITS / 64;      // 64-lane direct loads per stage
   constexpr int NPW = NINST / 4;         // per wavefront
   constexpr int FB = BF / 64, TB = BT / 64;
-  static_assert(BF == BT && NPW % 2 == 0, "W and X loads split evenly");
+  constexpr int WJ = BF * UPR / 256;     // loads j < WJ of every wavefront fill W rows, the rest X rows
+  static_assert(BF * UPR % 256 == 0 && BT * UPR % 256 == 0, "W and X loads split evenly over the wavefronts");
   static_assert(NSTAGE >= 3 && NSTAGE <= 9 && (NSTAGE - 2) * NPW < 64, "stage ring");
   __shared__ __attribute__((aligned(16))) uint4 lds[NSTAGE][UNITS];
 
@@ -357,8 +357,8 @@ __global__ __launch_bounds__(256, 1) void gemm_deep_kernel(const bf16* __restric
   // 16-byte bank groups (rows r, r+1 differ by 64 B; pairs of rows take the 4 chunk XORs)
   auto unit = [](int r, int c) { return r * UPR + (c ^ ((r >> 1) & 3)); };
 
-  // Loads: wavefront w issues loads i = w + 4j; loads 0..15 fill the W rows, 16..31 the X
-  // rows (j < NPW/2: W, else X, for every wavefront).  Per-lane byte offsets from the tile's
+  // Loads: wavefront w issues loads i = w + 4j; the first BF * UPR / 64 fill the W rows, the
+  // rest the X rows (j < WJ: W, else X, for every wavefront).  Per-lane byte offsets from the tile's
   // row-0 base; rows past N or M read the last valid row (their results are never stored).
   const bf16* Wt = W + n0 * K;
   const bf16* Xt = A + m0 * lda;
@@ -381,7 +381,7 @@ __global__ __launch_bounds__(256, 1) void gemm_deep_kernel(const bf16* __restric
     const char* xb = reinterpret_cast<const char*>(Xt + kt * BK);
 #pragma unroll
     for (int j = 0; j < NPW; ++j)
-      dma_load16(j < NPW / 2 ? wb : xb, off[j], &lds[st][(wave + 4 * j) * 64]);
+      dma_load16(j < WJ ? wb : xb, off[j], &lds[st][(wave + 4 * j) * 64]);
   };
   // this wavefront's loads of the tile before the `newer` most recently issued tiles are done
   // (newer <= NSTAGE - 2: at most that many later tiles are ever in flight)
@@ -528,9 +528,10 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 }
 
 // Launch plan of a bf16 GEMM: kernel and k-split count.
-enum GemmKind { kGemm128 = 0, kGemmDeep256 = 1, kGemmDeep128 = 2, kGemm128x64 = 3 };
+enum GemmKind { kGemm128 = 0, kGemmDeep256 = 1, kGemmDeep128 = 2, kGemm128x64 = 3, kGemm256x128 = 4 };
 struct GemmPlan {
-  int kind;     // GemmKind: 128 x 128 2-stage (2 per CU), 256 x 256 4-stage, 128 x 128 8-stage (1 per CU)
+  int kind;     // GemmKind: 128 x 128 2-stage (2 per CU), 256 x 256 4-stage, 128 x 128 8-stage (1 per CU),
+                // 128 x 64 2-stage (2 per CU), 256 x 128 3-stage with k 32 deep (2 per CU)
   int split;    // k slices (1 = no split)
 };
 
@@ -567,6 +568,7 @@ static int gemm_kind_override() {
   if (std::strcmp(v, "256") == 0) return kGemmDeep256;
   if (std::strcmp(v, "128d") == 0) return kGemmDeep128;
   if (std::strcmp(v, "128x64") == 0) return kGemm128x64;
+  if (std::strcmp(v, "256x128") == 0) return kGemm256x128;
   return -1;
 }
 
@@ -590,13 +592,14 @@ static GemmPlan gemm_plan(int64_t m, int64_t n, int64_t k, size_t ws_bytes) {
   const int force_sp = gemm_split_override();
   GemmPlan best_plan{force >= 0 ? force : kGemm128, 1};
   double best = 1e30;
-  for (int kind = 0; kind <= 3; ++kind) {
+  for (int kind = 0; kind <= 4; ++kind) {
     if (force >= 0 ? kind != force : kind != kGemm128) continue;
-    const int64_t bt = kind == kGemmDeep256 ? 256 : 128;                // features per tile
-    const int64_t bm = kind == kGemm128x64 ? 64 : bt;                  // tokens per tile
+    const int64_t bt = kind == kGemmDeep256 || kind == kGemm256x128 ? 256 : 128;   // features per tile
+    const int64_t bm = kind == kGemm128x64 ? 64 : kind == kGemm256x128 ? 128 : bt;  // tokens per tile
     const int64_t bk = kind == kGemm128 || kind == kGemm128x64 ? 64 : 32;
     const int64_t tiles = ((m + bm - 1) / bm) * ((n + bt - 1) / bt);
-    const int64_t slots = kind == kGemm128 || kind == kGemm128x64 ? 2 * (int64_t)cus : (int64_t)cus;
+    const int64_t slots = kind == kGemm128 || kind == kGemm128x64 || kind == kGemm256x128 ? 2 * (int64_t)cus
+                                                                                          : (int64_t)cus;
     const double fixed_s = kind == kGemmDeep256 ? 30e-6 : 3e-6;
     const double rate = kind == kGemmDeep256 ? 6.7e12 : 1.65e12;      // FLOP/s of one resident workgroup
     for (int sp = 1; sp <= kMaxGemmSplit; ++sp) {
@@ -624,9 +627,11 @@ static constexpr auto gemm_small128 = gemm_bf16_kernel<128, 128, EPI, SPLIT>;
 template <int EPI, bool SPLIT>
 static constexpr auto gemm_small128x64 = gemm_bf16_kernel<128, 64, EPI, SPLIT>;
 template <int EPI, bool SPLIT>
-static constexpr auto gemm_deep256 = gemm_deep_kernel<256, 256, 4, EPI, SPLIT>;
+static constexpr auto gemm_deep256 = gemm_deep_kernel<256, 256, 4, 1, EPI, SPLIT>;
 template <int EPI, bool SPLIT>
-static constexpr auto gemm_deep128 = gemm_deep_kernel<128, 128, 8, EPI, SPLIT>;
+static constexpr auto gemm_deep128 = gemm_deep_kernel<128, 128, 8, 1, EPI, SPLIT>;
+template <int EPI, bool SPLIT>
+static constexpr auto gemm_wide = gemm_deep_kernel<256, 128, 3, 2, EPI, SPLIT>;
 
 template <int EPI>
 static void launch_gemm_epi(const void* a, int64_t lda, const void* w, const float* bias, int64_t m, int64_t n,
@@ -637,8 +642,8 @@ static void launch_gemm_epi(const void* a, int64_t lda, const void* w, const flo
     const bf16* A = static_cast<const bf16*>(a);
     const bf16* Wt = static_cast<const bf16*>(w);
     const GemmPlan p = gemm_plan(m, n, k, ws ? ws_bytes : 0);
-    const int bt = p.kind == kGemmDeep256 ? 256 : 128;
-    const int bm = p.kind == kGemm128x64 ? 64 : bt;
+    const int bt = p.kind == kGemmDeep256 || p.kind == kGemm256x128 ? 256 : 128;
+    const int bm = p.kind == kGemm128x64 ? 64 : p.kind == kGemm256x128 ? 128 : bt;
     const int nkt = (int)(k / (p.kind == kGemm128 || p.kind == kGemm128x64 ? 64 : 32));
     const int tiles_n = (int)((n + bt - 1) / bt);
     const int64_t tiles = (int64_t)tiles_n * ((m + bm - 1) / bm);
@@ -658,6 +663,7 @@ static void launch_gemm_epi(const void* a, int64_t lda, const void* w, const flo
     if (p.kind == kGemmDeep256) PF_GEMM_LAUNCH(gemm_deep256);
     else if (p.kind == kGemmDeep128) PF_GEMM_LAUNCH(gemm_deep128);
     else if (p.kind == kGemm128x64) PF_GEMM_LAUNCH(gemm_small128x64);
+    else if (p.kind == kGemm256x128) PF_GEMM_LAUNCH(gemm_wide);
     else PF_GEMM_LAUNCH(gemm_small128);
 #undef PF_GEMM_LAUNCH
     if (used > 1) {

@@ -70,13 +70,14 @@ def test_gemm_bf16(m, n, k, epi, split):
     assert_close(host(c), want, f"gemm bf16 {m}x{n}x{k} epi={epi}")
 
 
-@pytest.mark.parametrize("kernel", ["256", "128d", "128x64"], ids=["deep256", "deep128", "t128x64"])
+@pytest.mark.parametrize("kernel", ["256", "128d", "128x64", "256x128"], ids=["deep256", "deep128", "t128x64", "t256x128"])
 @pytest.mark.parametrize("split", [False, True], ids=["whole", "ksplit"])
 @pytest.mark.parametrize("m,n,k", [(77, 192, 128), (300, 1344, 1152), (257, 640, 4608)])
 @pytest.mark.parametrize("epi", [B.PF_EPI_STORE, B.PF_EPI_GELU_TANH, B.PF_EPI_GATED_RESIDUAL])
 def test_gemm_bf16_deep_ring(m, n, k, epi, split, kernel, monkeypatch):
     """The kernels other than the default, forced through PF_GEMM_TILE (deep rings: 256 x 256
-    with 4 stages, 128 x 128 with 8; and 128 features x 64 tokens with the 2-stage ring): ragged
+    with 4 stages, 128 x 128 with 8, 256 features x 128 tokens with 3 and two workgroups per CU;
+    and 128 features x 64 tokens with the 2-stage ring): ragged
     m and n (partial tiles in both), k from fewer tiles than the ring holds to a long ring, with
     and without the k split."""
     torch = torch_cuda()

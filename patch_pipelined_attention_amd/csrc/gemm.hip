@@ -9,8 +9,9 @@
 //
 // Tiles: 128 x 128 with a 2-stage ring, two workgroups per CU.  A 128 x 64 variant and three
 // deep-ring variants (256 x 256 and 128 x 128 with one workgroup per CU, 256 x 128 with two)
-// can be forced for comparison.  Grids too small to fill the GPU split k: every slice writes its fp32 partial tile and a reduce pass
-// sums the slices in order (deterministic) and applies the epilogue.  (A last-arriving-slice
+// can be forced for comparison.  Grids too small to fill the GPU split k: every slice writes its
+// fp32 partial tile and a reduce pass sums the slices in order (deterministic) and applies the
+// epilogue.  (A last-arriving-slice
 // merge inside the GEMM measured slower on MI355X: the partials cross XCDs, whose L2s are
 // not coherent, so they must be written through and read back from the device-coherent
 // level, a longer latency chain than one more launch.)
@@ -695,9 +696,18 @@ hipError_t launch_gemm(const void* a, int64_t lda, const void* w, const float* b
   const RowGroups rg = groups ? *groups : RowGroups{m, 0, 0};
   if (sp.grp_rows <= 0 || rg.rows <= 0) return hipErrorInvalidValue;
   switch (epi) {
-    case kEpiStore: launch_gemm_epi<kEpiStore>(a, lda, w, bias, m, n, k, c, ldc, gate, dtype, ws, ws_bytes, s, sp, rg, nullptr, nullptr); break;
-    case kEpiGeluTanh: launch_gemm_epi<kEpiGeluTanh>(a, lda, w, bias, m, n, k, c, ldc, gate, dtype, ws, ws_bytes, s, sp, rg, nullptr, nullptr); break;
-    case kEpiGeluErf: launch_gemm_epi<kEpiGeluErf>(a, lda, w, bias, m, n, k, c, ldc, gate, dtype, ws, ws_bytes, s, sp, rg, nullptr, nullptr); break;
+    case kEpiStore:
+      launch_gemm_epi<kEpiStore>(a, lda, w, bias, m, n, k, c, ldc, gate, dtype, ws, ws_bytes, s, sp, rg, nullptr,
+                                 nullptr);
+      break;
+    case kEpiGeluTanh:
+      launch_gemm_epi<kEpiGeluTanh>(a, lda, w, bias, m, n, k, c, ldc, gate, dtype, ws, ws_bytes, s, sp, rg, nullptr,
+                                    nullptr);
+      break;
+    case kEpiGeluErf:
+      launch_gemm_epi<kEpiGeluErf>(a, lda, w, bias, m, n, k, c, ldc, gate, dtype, ws, ws_bytes, s, sp, rg, nullptr,
+                                   nullptr);
+      break;
     case kEpiQkvSplice:
       if (dtype != kDtypeBF16 || !splice) return hipErrorInvalidValue;
       launch_gemm_epi<kEpiQkvSplice>(a, lda, w, bias, m, n, k, c, ldc, gate, dtype, ws, ws_bytes, s, sp, rg, nullptr,

@@ -25,31 +25,57 @@ def _cfg(grid):
                             train_steps=T_TRAIN, beta_start=1e-4, beta_end=0.02)
 
 
-def _loop_oracle(shape, inputs, din, batch):
-    stages = [ref.StageOracle(inputs.layers, heads=shape.heads, head_dim=shape.head_dim, seq_txt=shape.seq_txt,
-                              seq_img=shape.seq_img, num_patches=shape.num_patches, mlp_ratio=shape.mlp_ratio,
-                              mode="bf16") for _ in range(batch)]
+def _block(shape, inputs, block):
+    """(layers, text layers, angles, Stage options, oracle options) of a block variant."""
+    if block == "mmdit":
+        mm = synth.mmdit_inputs(shape, inputs)
+        return (mm.layers, mm.txt_layers, mm.angles, dict(qk_norm=True, dual_stream=True, rope=True),
+                dict(txt_layers=mm.txt_layers, qk_norm=True, rope_angles=mm.angles))
+    if block == "flux-single":
+        par = synth.parallel_inputs(shape)
+        return (par.layers, None, par.angles, dict(qk_norm=True, rope=True, parallel=True),
+                dict(qk_norm=True, rope_angles=par.angles, parallel=True))
+    return inputs.layers, None, None, {}, {}
+
+
+def _loop_oracle(shape, inputs, din, batch, layers=None, opts=None, mode="bf16"):
+    stages = [ref.StageOracle(inputs.layers if layers is None else layers, heads=shape.heads,
+                              head_dim=shape.head_dim, seq_txt=shape.seq_txt, seq_img=shape.seq_img,
+                              num_patches=shape.num_patches, mlp_ratio=shape.mlp_ratio, mode=mode, **(opts or {}))
+              for _ in range(batch)]
     return sampler.DenoiserOracle(stages, din.weights, C_IN, PATCH, din.grid_h, din.grid_w, FREQ,
                                   sampler.alphas_cumprod(T_TRAIN, 1e-4, 0.02), seq_txt=shape.seq_txt)
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("name,batch,guidance", [("c2s", 1, 1.0), ("c2s", 2, 4.0), ("c4s", 1, 1.0)])
-def test_denoiser_steps_match_loop_oracle(name, batch, guidance):
+@pytest.mark.parametrize("name,batch,guidance,block", [("c2s", 1, 1.0, "dit"), ("c2s", 2, 4.0, "dit"),
+                                                      ("c4s", 1, 1.0, "dit"), ("c4s", 2, 3.5, "mmdit"),
+                                                      ("c4s", 1, 1.0, "flux-single")])
+def test_denoiser_steps_match_loop_oracle(name, batch, guidance, block):
     """Each step starts both sides from the GPU's latent (teacher forcing; each side keeps its own
     stale K/V buffers) and compares the noise prediction the step applied, recovered from the
     DDIM update as eps = (z' - a z) / e, against the oracle's.  The first two steps are
-    warm-up steps, the rest reuse stale buffers."""
+    warm-up steps, the rest reuse stale buffers.  The Flux-shaped cases also run the Flux.1
+    blocks (a guided pair over the double-stream block, one sample over the single-stream one).
+
+    Max-abs gate: the contract's 2e-2 or twice the deviation that rounding the softmax weights
+    to bf16 alone causes in the loop oracle (bf16p vs bf16 stages), whichever is larger, as for
+    the stage outputs.  Guidance eps_1 + g (eps_0 - eps_1) multiplies per-sample deviations by
+    up to |g| + |1 - g| (6 at g = 3.5), and the floor measures that on the oracle itself."""
     torch = torch_cuda()
     shape = {"c2s": C2.small(seq_img=256, num_layers=2, num_patches=4),
              "c4s": C4.small(seq_img=256, num_layers=1, num_patches=4, seq_txt=32)}[name]
     inputs = synth.stage_inputs(shape)
     din = synth.denoiser_inputs(shape, batch=batch)
     x_txt = synth.randn((batch, shape.seq_txt, shape.hidden), shape.seed + 6000) if shape.seq_txt else None
-    orc = _loop_oracle(shape, inputs, din, batch)
+    layers, txt_layers, angles, st_opts, orc_opts = _block(shape, inputs, block)
+    orc = _loop_oracle(shape, inputs, din, batch, layers, orc_opts)
+    orc_p = _loop_oracle(shape, inputs, din, batch, layers, orc_opts, mode="bf16p")
     abar = sampler.alphas_cumprod(T_TRAIN, 1e-4, 0.02)
-    with Stage(shape, batch=batch) as st:
-        st.load(inputs.layers)
+    with Stage(shape, batch=batch, **st_opts) as st:
+        st.load(layers, txt_layers)
+        if angles is not None:
+            st.set_rope(angles)
         d = B.denoiser_create(st.handle, _cfg(din.grid_h))
         try:
             B.denoiser_load_weights(d, {k: dev(torch, v) for k, v in din.weights.items()})
@@ -60,15 +86,18 @@ def test_denoiser_steps_match_loop_oracle(name, batch, guidance):
                 tn = TIMESTEPS[i + 1] if i + 1 < len(TIMESTEPS) else -1
                 warm = i < 2
                 z_before = host(z)
-                print(f"[denoiser] {name} batch={batch} step {i} t={t} warmup={warm}", flush=True)
+                print(f"[denoiser] {name} {block} batch={batch} step {i} t={t} warmup={warm}", flush=True)
                 B.denoiser_step(d, z, y, t, tn, warmup=warm, guidance=guidance, x_txt=xt)
                 z_after = host(z)
                 _, eps_want = orc.step(z_before, din.y, t, tn, warm, guidance, x_txt=x_txt)
+                _, eps_p = orc_p.step(z_before, din.y, t, tn, warm, guidance, x_txt=x_txt)
+                tol = max(MAX_ABS, 2.0 * float(np.abs(eps_p - eps_want).max()))
                 ab_n = abar[tn] if tn >= 0 else 1.0
                 a = math.sqrt(ab_n / abar[t])
                 e = math.sqrt(1.0 - ab_n) - a * math.sqrt(1.0 - abar[t])
                 eps_got = (z_after - a * z_before) / e
-                assert_close(eps_got, eps_want, f"{name} batch {batch} step {i}: eps vs loop oracle")
+                assert_close(eps_got, eps_want, f"{name} {block} batch {batch} step {i}: eps vs loop oracle",
+                             max_abs_tol=tol)
                 if batch == 2:
                     assert np.array_equal(z_after[0], z_after[1]), "a guided pair must keep one shared latent"
         finally:

@@ -450,8 +450,8 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const bf16* __restric
     if (n_split > 1) {
       if (hi == 0) {
         const int64_t H = hidden / D;
-        part_ml[(((int64_t)split * 2 + 0) * H + head) * rows + q_row[qb]] = m_ref[qb];
-        part_ml[(((int64_t)split * 2 + 1) * H + head) * rows + q_row[qb]] = l_tot;
+        reinterpret_cast<float2*>(part_ml)[((int64_t)split * H + head) * rows + q_row[qb]] =
+            make_float2(m_ref[qb], l_tot);
       }
     }
   }
@@ -481,8 +481,9 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const bf16* __restric
 #pragma unroll
   for (int sp = 0; sp < kMaxAttnSplit; ++sp) {
     const int64_t sc = sp < n_split ? sp : n_split - 1;   // slices past n_split re-read the last (unused)
-    m[sp] = part_ml[((sc * 2) * H + head) * rows + row];
-    l[sp] = part_ml[((sc * 2 + 1) * H + head) * rows + row];
+    const float2 ml = reinterpret_cast<const float2*>(part_ml)[(sc * H + head) * rows + row];
+    m[sp] = ml.x;
+    l[sp] = ml.y;
     x[sp] = *reinterpret_cast<const bf16x8*>(part_o + (sc * rows + row) * hidden + (int64_t)head * D + chunk * 8);
   }
   float M = m[0];
@@ -628,7 +629,7 @@ static hipError_t launch_attn_d(const void* q, int64_t ldq, const void* k, int64
     const int tps = (int)((ntiles + n_split - 1) / n_split);
     const int n_used = (int)((ntiles + tps - 1) / tps);      // every split gets at least one tile
     const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
-    // workspace: bf16 slice results [n_used][all_rows][hidden], then fp32 (m, l) [n_used][2][heads][all_rows]
+    // workspace: bf16 slice results [n_used][all_rows][hidden], then fp32 (m, l) pairs [n_used][heads][all_rows]
     bf16* part_o = static_cast<bf16*>(ws);
     float* part_ml = part_o ? reinterpret_cast<float*>(part_o + (size_t)n_used * all_rows * hidden) : nullptr;
     hipLaunchKernelGGL((attn_bf16_kernel<D, QB>), dim3((unsigned)(wg * n_used)), dim3(64 * kAttnWaves), 0, s,

@@ -119,6 +119,14 @@ hipError_t launch_ln_modulate(const float* x, int64_t rows, int hidden, const fl
 hipError_t launch_adaln(const float* cond, const void* w, const float* b, int hidden, float* mod,
                         int dtype, hipStream_t s, int chunks = 6);
 
+// The same for n_sets weight sets x n_samples conditions in one launch: set m's matrix at
+// w + m * w_stride elements, its bias at b + m * b_stride, its output for sample g at
+// mod + m * mod_stride + g * mod_sample_stride; sample g's cond at cond + g * cond_stride.
+hipError_t launch_adaln_batch(const float* cond, int64_t cond_stride, int n_samples, const void* w,
+                              int64_t w_stride, const float* b, int64_t b_stride, int n_sets, int hidden,
+                              float* mod, int64_t mod_stride, int64_t mod_sample_stride, int dtype, hipStream_t s,
+                              int chunks = 6);
+
 // The LayerNorm + modulation that follows a gated-residual projection (the next sublayer's):
 // y [m, n] bf16 (row stride n) = LN(x)(1 + scale) + shift of the updated residual rows, with
 // each sample's shift / scale at + g * groups->p_stride.

@@ -385,24 +385,35 @@ hipError_t launch_qk_norm_rope(void* q, int64_t ldq, void* k, int64_t ldk, int64
 }
 
 // ---------------------------------------------------------------------------------
-// mod[j] = sum_i SiLU(c[i]) * W[j, i] + b[j] for j < chunks * h (6 or 3 vectors of h).  SiLU(c) is staged in LDS
-// once per block; one wavefront per output row streams that row of W with 16-byte loads.
+// mod[j] = sum_i SiLU(c[i]) * W[j, i] + b[j] for j < chunks * h (6 or 3 vectors of h), for a
+// batch of weight sets (blockIdx.y: set m at w + m * w_stride, b + m * b_stride, output at
+// mod + m * mod_stride) and conditions (blockIdx.z: sample g's cond at + g * cond_stride, its
+// output at + g * mod_sample_stride), so one launch covers every layer, stream and sample.
+// SiLU(c) is staged in LDS once per block; one wavefront per output row streams that row of W
+// with 16-byte loads, four in flight per lane.
 // ---------------------------------------------------------------------------------
 template <typename WT>
-__global__ __launch_bounds__(256) void adaln_kernel(const float* __restrict__ cond,
-                                                    const WT* __restrict__ w,
-                                                    const float* __restrict__ b, int hidden,
-                                                    int n_out, float* __restrict__ mod) {
+__global__ __launch_bounds__(256) void adaln_kernel(const float* __restrict__ cond, int64_t cond_stride,
+                                                    const WT* __restrict__ w, int64_t w_stride,
+                                                    const float* __restrict__ b, int64_t b_stride, int hidden,
+                                                    int n_out, float* __restrict__ mod, int64_t mod_stride,
+                                                    int64_t mod_sample_stride) {
   extern __shared__ float s_act[];
+  const int m = blockIdx.y, g = blockIdx.z;
+  const float* cg = cond + g * cond_stride;
   for (int i = threadIdx.x; i < hidden; i += 256) {
-    const float c = cond[i];
+    const float c = cg[i];
     s_act[i] = c / (1.0f + expf(-c));
   }
   __syncthreads();
+  const WT* wm = w + m * w_stride;
+  const float* bm = b + m * b_stride;
+  float* om = mod + m * mod_stride + g * mod_sample_stride;
   const int lane = threadIdx.x & 63;
   for (int row = blockIdx.x * 4 + (threadIdx.x >> 6); row < n_out; row += gridDim.x * 4) {
-    const WT* wr = w + (int64_t)row * hidden;
+    const WT* wr = wm + (int64_t)row * hidden;
     float acc = 0.f;
+#pragma unroll 4
     for (int k = lane * 8; k < hidden; k += 512) {
       if constexpr (sizeof(WT) == 2) {
         const bf16x8 wv = *reinterpret_cast<const bf16x8*>(wr + k);
@@ -416,23 +427,34 @@ __global__ __launch_bounds__(256) void adaln_kernel(const float* __restrict__ co
       }
     }
     acc = wave_sum(acc);
-    if (lane == 0) mod[row] = acc + b[row];
+    if (lane == 0) om[row] = acc + bm[row];
   }
+}
+
+hipError_t launch_adaln_batch(const float* cond, int64_t cond_stride, int n_samples, const void* w,
+                              int64_t w_stride, const float* b, int64_t b_stride, int n_sets, int hidden,
+                              float* mod, int64_t mod_stride, int64_t mod_sample_stride, int dtype, hipStream_t s,
+                              int chunks) {
+  if (n_sets <= 0 || n_samples <= 0) return hipSuccess;
+  const int n_out = chunks * hidden;
+  int blocks = (n_out + 3) / 4;
+  const int cap = 8192 / (n_sets * n_samples);
+  if (blocks > cap) blocks = cap > 1 ? cap : 1;
+  const dim3 grid((unsigned)blocks, (unsigned)n_sets, (unsigned)n_samples);
+  const size_t lds = sizeof(float) * (size_t)hidden;
+  if (dtype == kDtypeBF16)
+    hipLaunchKernelGGL(adaln_kernel<bf16>, grid, dim3(256), lds, s, cond, cond_stride, static_cast<const bf16*>(w),
+                       w_stride, b, b_stride, hidden, n_out, mod, mod_stride, mod_sample_stride);
+  else
+    hipLaunchKernelGGL(adaln_kernel<float>, grid, dim3(256), lds, s, cond, cond_stride,
+                       static_cast<const float*>(w), w_stride, b, b_stride, hidden, n_out, mod, mod_stride,
+                       mod_sample_stride);
+  return hipGetLastError();
 }
 
 hipError_t launch_adaln(const float* cond, const void* w, const float* b, int hidden, float* mod,
                         int dtype, hipStream_t s, int chunks) {
-  const int n_out = chunks * hidden;
-  int blocks = (n_out + 3) / 4;
-  if (blocks > 2048) blocks = 2048;
-  const size_t lds = sizeof(float) * (size_t)hidden;
-  if (dtype == kDtypeBF16)
-    hipLaunchKernelGGL(adaln_kernel<bf16>, dim3(blocks), dim3(256), lds, s, cond,
-                       static_cast<const bf16*>(w), b, hidden, n_out, mod);
-  else
-    hipLaunchKernelGGL(adaln_kernel<float>, dim3(blocks), dim3(256), lds, s, cond,
-                       static_cast<const float*>(w), b, hidden, n_out, mod);
-  return hipGetLastError();
+  return launch_adaln_batch(cond, 0, 1, w, 0, b, 0, 1, hidden, mod, 0, 0, dtype, s, chunks);
 }
 
 }  // namespace pf

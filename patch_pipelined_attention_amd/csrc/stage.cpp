@@ -362,6 +362,7 @@ struct pf_stage {
   void *h1, *qkv, *o, *u;
   int64_t ld_o, ld_u;        // row strides of o and u (the parallel block keeps [o, u] side by side)
   int n_mod;                 // modulation vectors per sample: 6 (DiT block) or 3 (parallel block)
+  size_t set_bytes = 0;      // distance between two consecutive weight sets (layer by layer, stream by stream)
   void* attn_ws = nullptr;   // key-range split partials of the patch attention
   size_t attn_ws_bytes = 0;
   void* gemm_ws = nullptr;   // k-split partials of the projections
@@ -459,6 +460,7 @@ extern "C" pf_status stage_create(const pf_stage_config* cfg, pf_stage** out) {
   const size_t norm_bytes = round_up((size_t)d * 4, 256);
   per_set += 2 * norm_bytes;
   const size_t per_layer = per_set * (size_t)n_sets;
+  st->set_bytes = per_set;
   const size_t rope_bytes = (cfg->flags & PF_STAGE_ROPE) ? (size_t)(st->s_kv * (d / 2)) * 4 : 0;
   const size_t kv_mat = round_up((size_t)(st->s_alloc * h) * es, 256);
   st->kv_sample_bytes = 2 * kv_mat;   // per layer: K0, V0, K1, V1, ...
@@ -641,16 +643,16 @@ static pf_status check_loaded(pf_stage* st, const char* who) {
   return PF_OK;
 }
 
+// Every layer's (and stream's) modulation for every sample in one launch: the weight sets lie
+// set_bytes apart in the weight allocation, their modulation vectors 6h * batch floats apart.
 static pf_status set_cond_impl(pf_stage* st, const float* cond, hipStream_t s) {
-  for (auto& lm : st->layers)
-    for (int set = 0; set < (dual(st) ? 2 : 1); ++set) {
-      const WeightSet& ws = set == 0 ? lm.img : lm.txt;
-      for (int64_t b = 0; b < st->batch; ++b) {
-        hipError_t e = launch_adaln(cond + b * st->h, ws.w_ada, ws.b_ada, (int)st->h, ws.mod + b * 6 * st->h,
-                                    st->cfg.dtype, s, st->n_mod);
-        if (e != hipSuccess) return stage_hip_fail(st, e, "stage_set_cond: adaln launch");
-      }
-    }
+  const int n_sets = (int)st->layers.size() * (dual(st) ? 2 : 1);
+  const WeightSet& first = st->layers[0].img;
+  const int64_t h = st->h;
+  hipError_t e = launch_adaln_batch(cond, h, (int)st->batch, first.w_ada, (int64_t)(st->set_bytes / st->es),
+                                    first.b_ada, (int64_t)(st->set_bytes / sizeof(float)), n_sets, (int)h, first.mod,
+                                    6 * h * st->batch, 6 * h, st->cfg.dtype, s, st->n_mod);
+  if (e != hipSuccess) return stage_hip_fail(st, e, "stage_set_cond: adaln launch");
   st->cond_set = true;
   return PF_OK;
 }

@@ -852,12 +852,17 @@ extern "C" pf_status stage_run_step(pf_stage* st, const float* x_in, float* x_ou
   if ((s = check_loaded(st, "stage_run_step")) != PF_OK) return s;
   hipStream_t hs = (hipStream_t)stream;
   if ((s = set_cond_impl(st, cond, hs)) != PF_OK) return s;
+  // out of place: every row is copied once, then the micro-steps (disjoint rows) run in place
+  if (x_out != x_in) {
+    hipError_t e = hipMemcpyAsync(x_out, x_in, bytes, hipMemcpyDeviceToDevice, hs);
+    if (e != hipSuccess) return stage_hip_fail(st, e, "stage_run_step: hipMemcpyAsync");
+  }
   const int64_t h = st->h, xs = st->s_kv * h;   // sample b's rows start b * s_kv rows on
-  if (flags & PF_STEP_WARMUP) return run_patch_impl(st, 0, st->s_kv, x_in, x_out, xs, hs);
-  if (st->cfg.seq_txt > 0 && (s = run_patch_impl(st, 0, st->cfg.seq_txt, x_in, x_out, xs, hs)) != PF_OK) return s;
+  if (flags & PF_STEP_WARMUP) return run_rows(st, 0, st->s_kv, x_out, xs, hs);
+  if (st->cfg.seq_txt > 0 && (s = run_rows(st, 0, st->cfg.seq_txt, x_out, xs, hs)) != PF_OK) return s;
   for (int m = 0; m < st->cfg.num_patches; ++m) {
     const int64_t off = st->cfg.seq_txt + (int64_t)m * st->patch_rows;
-    if ((s = run_patch_impl(st, off, st->patch_rows, x_in + off * h, x_out + off * h, xs, hs)) != PF_OK) return s;
+    if ((s = run_rows(st, off, st->patch_rows, x_out + off * h, xs, hs)) != PF_OK) return s;
   }
   return PF_OK;
 }

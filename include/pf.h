@@ -161,11 +161,16 @@ pf_status stage_destroy(pf_stage* st);
 pf_status stage_load_weights(pf_stage* st, int32_t layer, const pf_layer_weights* w, void* stream);
 
 /* PF_STAGE_DUAL_STREAM: layer `layer`'s text-stream parameters (same form and rules as
- * stage_load_weights); every layer's must be loaded before any run call. */
+ * stage_load_weights); every layer's must be loaded before any run call (else PF_ERR_STATE).
+ * PF_ERR_INVALID_ARG on a stage created without PF_STAGE_DUAL_STREAM, a bad layer index or a
+ * NULL pointer the options need (q_norm / k_norm with PF_STAGE_QK_NORM). */
 pf_status stage_load_text_weights(pf_stage* st, int32_t layer, const pf_layer_weights* w, void* stream);
 
 /* PF_STAGE_ROPE: copy the rotation angles, device fp32 [seq_txt + seq_img, head_dim / 2]
- * (row r: the angles of buffer row r).  Must be called before any run call. */
+ * (row r: the angles of buffer row r, radians) into memory the stage owns (stream-ordered).
+ * Must be called before any run call (else PF_ERR_STATE); calling it again replaces the table
+ * for later runs.  PF_ERR_INVALID_ARG on a stage created without PF_STAGE_ROPE, a NULL or
+ * misaligned (4-byte) pointer, or angles overlapping the stage's own table. */
 pf_status stage_set_rope(pf_stage* st, const float* angles, void* stream);
 
 /* Compute every layer's adaLN modulation from the conditioning vectors `cond` (device,

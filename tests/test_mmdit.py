@@ -425,3 +425,93 @@ def test_full_size_flux_blocks_sampled_parity(block):
             k, v = st.kv_get(0)
             assert_bf16_close(k, orc.K[0], f"{block} full size step {s} K buffer", **k_bound(orc.K[0], True, True))
             assert_bf16_close(v, orc.V[0], f"{block} full size step {s} V buffer")
+
+
+@pytest.mark.parametrize("block", ["mmdit", "flux-single"])
+def test_flux_blocks_property_b_micro_steps_touch_only_their_rows(block):
+    """Property (b) for the Flux.1 blocks: each micro-step of a patched step (the text prefix,
+    then every patch) leaves every K and V buffer row outside its own range bit-identical (the
+    QK step rewrites K in place), and its own rows hold the fresh values the oracle computes."""
+    torch = torch_cuda()
+    shape = SHAPES["c4s"]
+    inputs = synth.stage_inputs(shape)
+    if block == "mmdit":
+        mm = synth.mmdit_inputs(shape, inputs)
+        opts, okw, txt = dict(qk_norm=True, dual_stream=True, rope=True), dict(txt_layers=mm.txt_layers), mm.txt_layers
+    else:
+        mm = synth.parallel_inputs(shape)
+        opts, okw, txt = dict(qk_norm=True, rope=True, parallel=True), dict(parallel=True), None
+    kw = dict(heads=shape.heads, head_dim=shape.head_dim, seq_txt=shape.seq_txt, seq_img=shape.seq_img,
+              num_patches=shape.num_patches, mlp_ratio=shape.mlp_ratio, qk_norm=True, rope_angles=mm.angles, **okw)
+    orc = ref.StageOracle(mm.layers, mode="bf16", **kw)
+    orc_p = ref.StageOracle(mm.layers, mode="bf16p", **kw)
+    with Stage(shape, **opts) as st:
+        st.load(mm.layers, txt)
+        st.set_rope(mm.angles)
+        x, c = dev(torch, inputs.x), dev(torch, inputs.c)
+        st.run_step(x, c, warmup=True, out=torch.empty_like(x))
+        orc.step(inputs.x, inputs.c, warmup=True)
+        orc_p.step(inputs.x, inputs.c, warmup=True)
+        noise = inputs.next_noise()
+        st.add_noise(noise)
+        orc.add_noise(noise)
+        orc_p.add_noise(noise)
+        st.set_cond(c)
+        orc.set_cond(inputs.c)
+        orc_p.set_cond(inputs.c)
+        xo = x.clone()
+        for off, n in orc.micro_steps(False):
+            print(f"[mmdit] {block} property b rows [{off}, {off + n})", flush=True)
+            before = [st.kv_get(l) for l in range(shape.num_layers)]
+            st.run_patch(off, n, x[off:off + n], xo[off:off + n])
+            orc.run_rows(off, n, inputs.x[off:off + n])
+            orc_p.run_rows(off, n, inputs.x[off:off + n])
+            rs = slice(off, off + n)
+            outside = np.ones(shape.seq_kv, bool)
+            outside[rs] = False
+            for l in range(shape.num_layers):
+                k, v = st.kv_get(l)
+                np.testing.assert_array_equal(k[outside], before[l][0][outside])
+                np.testing.assert_array_equal(v[outside], before[l][1][outside])
+                assert_bf16_close(k[rs], orc.K[l][rs], f"{block} fresh K rows [{off},{off + n}) layer {l}",
+                                  floor=2.0 * max_abs(orc_p.K[l][rs], orc.K[l][rs]), **k_bound(orc.K[l][rs], True, True))
+                assert_bf16_close(v[rs], orc.V[l][rs], f"{block} fresh V rows [{off},{off + n}) layer {l}",
+                                  floor=2.0 * max_abs(orc_p.V[l][rs], orc.V[l][rs]))
+
+
+@pytest.mark.parametrize("block", ["mmdit", "flux-single"])
+def test_flux_blocks_property_a_fresh_equals_stale(block):
+    """Property (a) for the Flux.1 blocks: with no drift between steps the stale context equals
+    the fresh one, so a patched step reproduces the unpartitioned (warm-up) step.  Layer-0 V
+    agrees within one bf16 ulp and K within three ulps of its pair norm (a patch-sized QKV
+    projection may split its k range, so its fp32 sums round differently, and K is normalised
+    and rotated after that rounding); outputs agree up to fp32 summation order."""
+    torch = torch_cuda()
+    shape = SHAPES["c4s"]
+    inputs = synth.stage_inputs(shape)
+    if block == "mmdit":
+        mm = synth.mmdit_inputs(shape, inputs)
+        opts, txt = dict(qk_norm=True, dual_stream=True, rope=True), mm.txt_layers
+    else:
+        mm = synth.parallel_inputs(shape)
+        opts, txt = dict(qk_norm=True, rope=True, parallel=True), None
+    with Stage(shape, **opts) as st:
+        st.load(mm.layers, txt)
+        st.set_rope(mm.angles)
+        x, c = dev(torch, inputs.x), dev(torch, inputs.c)
+        warm = torch.empty_like(x)
+        st.run_step(x, c, warmup=True, out=warm)
+        k0, v0 = (t.clone() for t in st.kv_raw(0))
+        patched = torch.empty_like(x)
+        st.run_step(x, c, warmup=False, out=patched)
+        k1, v1 = st.kv_raw(0)
+        ka, kb = host(k0), host(k1)
+        va, vb = host(v0), host(v1)
+        k_tol = 3.0 * bf16_ulp(pair_norms(np.maximum(np.abs(ka), np.abs(kb)))) + 2.0 ** -19
+        v_tol = bf16_ulp(np.maximum(np.abs(va), np.abs(vb))) + 2.0 ** -19
+        print(f"[mmdit] {block} property a: K max diff / bound {(np.abs(ka - kb) / k_tol).max():.2f}, "
+              f"V {(np.abs(va - vb) / v_tol).max():.2f}", flush=True)
+        assert (np.abs(ka - kb) <= k_tol).all(), "layer-0 K beyond three ulps of the pair norm"
+        assert (np.abs(va - vb) <= v_tol).all(), "layer-0 V beyond one ulp"
+        assert_close(host(patched), host(warm), f"{block} patched step vs warm-up step (fresh == stale)",
+                     max_abs_tol=0.25)

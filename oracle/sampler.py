@@ -29,7 +29,12 @@ not define the loop itself; the plainest DiT reading is taken and listed in the 
 Pins (tests/test_sampler_oracle.py): closed forms of the sinusoids at position 0, the DDIM
 step on an exactly predicted noise, patchify against torch's conv2d, the unpatchify
 round trip by brute force, the guidance limits g = 0 and g = 1, and the schedule's first
-value and monotonicity.
+value and monotonicity.  The loop as a whole (condition, eps, step) is pinned against the
+independent loop restatement oracle/brute_sampler.py over three steps (one sample; a guided
+pair with a text prefix), by two special cases of the final layer (W_fada = 0 with a zero
+and with a constant [shift; scale] bias) and by the guidance roles (g = 1 gives both samples
+the conditional prediction, g = 0 the unconditional one); a planted shift/scale swap and a
+planted swap of the guidance roles fail those pins.
 """
 from __future__ import annotations
 

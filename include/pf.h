@@ -151,31 +151,39 @@ typedef struct pf_stage pf_stage;
 pf_status stage_create(const pf_stage_config* cfg, pf_stage** out);
 
 /* Free everything the stage owns.  The caller synchronises its stream first.  NULL is a
- * no-op. */
+ * no-op.  Source: none on the pages (a resource call every user of a stage object needs). */
 pf_status stage_destroy(pf_stage* st);
 
 /* Copy layer `layer`'s parameters (device pointers, see pf_layer_weights) into memory
  * the stage owns (stream-ordered device-to-device copies).  The caller may release its
  * copies once the stream has passed this call.  Every layer must be loaded before any
- * run call (else PF_ERR_STATE). */
+ * run call (else PF_ERR_STATE).  Source: "Core mechanisms" 4 (memory efficiency) of the
+ * PipeFusion summaries: a device holds only the parameters of its own contiguous layers,
+ * 1/N of the model; and mechanism 1 (layer partitioning).  Errors: INVALID_ARG for a bad
+ * layer index or a NULL pointer the configuration needs, HIP if a copy cannot be enqueued. */
 pf_status stage_load_weights(pf_stage* st, int32_t layer, const pf_layer_weights* w, void* stream);
 
 /* PF_STAGE_DUAL_STREAM: layer `layer`'s text-stream parameters (same form and rules as
  * stage_load_weights); every layer's must be loaded before any run call (else PF_ERR_STATE).
  * PF_ERR_INVALID_ARG on a stage created without PF_STAGE_DUAL_STREAM, a bad layer index or a
- * NULL pointer the options need (q_norm / k_norm with PF_STAGE_QK_NORM). */
+ * NULL pointer the options need (q_norm / k_norm with PF_STAGE_QK_NORM).  Source: the
+ * Experiments section names SD3 and Flux.1 (MM-DiT models); their dual-stream block is a
+ * reading of the published designs. */
 pf_status stage_load_text_weights(pf_stage* st, int32_t layer, const pf_layer_weights* w, void* stream);
 
 /* PF_STAGE_ROPE: copy the rotation angles, device fp32 [seq_txt + seq_img, head_dim / 2]
  * (row r: the angles of buffer row r, radians) into memory the stage owns (stream-ordered).
  * Must be called before any run call (else PF_ERR_STATE); calling it again replaces the table
  * for later runs.  PF_ERR_INVALID_ARG on a stage created without PF_STAGE_ROPE, a NULL or
- * misaligned (4-byte) pointer, or angles overlapping the stage's own table. */
+ * misaligned (4-byte) pointer, or angles overlapping the stage's own table.  Source: as for
+ * stage_load_text_weights (the rotary embedding of the MM-DiT models, a reading). */
 pf_status stage_set_rope(pf_stage* st, const float* angles, void* stream);
 
 /* Compute every layer's adaLN modulation from the conditioning vectors `cond` (device,
  * fp32 [batch, h], one per sample): mod_l,b = SiLU(cond_b) . W_ada,l^T + b_ada,l, kept by the
- * stage for later stage_run_patch calls of this diffusion step. */
+ * stage for later stage_run_patch calls of this diffusion step.  Source: none on the pages
+ * (they name DiT models without their blocks); the per-step condition of a DiT block, a
+ * reading.  Errors: INVALID_ARG (NULL cond), STATE (weights not loaded), HIP. */
 pf_status stage_set_cond(pf_stage* st, const float* cond, void* stream);
 
 /* One micro-step: push buffer rows [row_off, row_off + rows) through all L layers
@@ -200,7 +208,11 @@ pf_status stage_run_patch(pf_stage* st, int64_t row_off, int64_t rows, const flo
  *   otherwise:           stage_run_patch(0, seq_txt) if seq_txt > 0, then
  *                        stage_run_patch(seq_txt + m*P, P) for m = 0 .. M-1, P = seq_img/M.
  * x_in / x_out: device fp32 [batch, seq_txt + seq_img, h], x_out may equal x_in; cond: fp32
- * [batch, h]. */
+ * [batch, h].  Source: "Core mechanisms" 1 (M non-overlapping patches through the stage's
+ * layers, one after another) and 2 (stale step-(T+1) context instead of waiting, so only the
+ * start-up has no stale context: the warm-up step) of the PipeFusion summaries.  Errors:
+ * INVALID_ARG (NULL or misaligned pointers, partially overlapping x_in / x_out, unknown
+ * flags), STATE (weights or rotation table missing), HIP. */
 pf_status stage_run_step(pf_stage* st, const float* x_in, float* x_out, const float* cond,
                          uint32_t flags, void* stream);
 
@@ -215,13 +227,20 @@ pf_status kvbuf_splice(const pf_kv_view* dst, const pf_kv_view* src, int64_t off
                        void* stream);
 
 /* Describe layer `layer`'s K/V buffer of sample 0 (owned by the stage; valid until
- * stage_destroy). */
+ * stage_destroy): rows = seq_txt + seq_img, row_elems = k_ld = hidden, V in PF_LAYOUT_K8
+ * (bf16) or PF_LAYOUT_ROWS (fp32).  Source: "Core mechanisms" 4 of the PipeFusion summaries:
+ * the stage's one full-spatial K/V buffer per own layer (1/N of all layers' buffers), exposed
+ * so a caller can inspect, checkpoint or perturb it (kvbuf_splice).  No HIP call; errors:
+ * INVALID_ARG (NULL stage or out, bad layer). */
 pf_status stage_get_kvbuf(pf_stage* st, int32_t layer, pf_kv_view* out);
 
-/* The same for sample `sample` (0 <= sample < batch) of a batched stage. */
+/* The same for sample `sample` (0 <= sample < batch) of a batched stage.  Source: as
+ * stage_get_kvbuf; a batch is the classifier-free guidance pair of the hybrid-parallelism
+ * page (two conditioned passes sharing the weights).  Errors: INVALID_ARG. */
 pf_status stage_get_kvbuf_sample(pf_stage* st, int32_t layer, int32_t sample, pf_kv_view* out);
 
-/* The stage's configuration as created (batch 0 reads back as 1). */
+/* The stage's configuration as created (batch 0 reads back as 1).  Source: none on the pages
+ * (a query a user of a stage object needs).  Errors: INVALID_ARG (NULL argument). */
 pf_status stage_get_config(const pf_stage* st, pf_stage_config* out);
 
 /* ---------------------------------------------------------------------------------
@@ -267,24 +286,36 @@ typedef struct pf_denoiser_weights {
 } pf_denoiser_weights;
 
 /* A loop around `st` (which it uses but does not own; destroy the denoiser first).  Allocates
- * its weights, the position table and per-step buffers on the current device. */
+ * its weights, the position table and per-step buffers on the current device.  Source: the diffusion
+ * loop of "Core mechanisms" 2 (see above).  Errors: INVALID_ARG (grid does not match the
+ * stage's image rows, bad sizes), OOM, HIP. */
 pf_status denoiser_create(pf_stage* st, const pf_denoiser_config* cfg, pf_denoiser** out);
+
+/* Free the loop's memory (not the stage's).  NULL is a no-op.  Source: none on the pages (a
+ * resource call). */
 pf_status denoiser_destroy(pf_denoiser* d);
+
+/* Copy the loop's parameters (stream-ordered device-to-device copies).  Source: the diffusion
+ * loop of "Core mechanisms" 2 (a reading).  Errors: INVALID_ARG (NULL pointer), HIP. */
 pf_status denoiser_load_weights(pf_denoiser* d, const pf_denoiser_weights* w, void* stream);
 
 /* One step from timestep t to t_next (-1: the last step).  z: device fp32
  * [batch, C, grid_h p, grid_w p], updated in place; y: device fp32 [batch, h]; x_txt: device
- * fp32 [batch, seq_txt, h] or NULL.  The stage's weights must be loaded. */
+ * fp32 [batch, seq_txt, h] or NULL.  The stage's weights must be loaded.  Source: the
+ * diffusion loop of "Core mechanisms" 2 (see above).  Errors: INVALID_ARG, STATE, HIP. */
 pf_status denoiser_step(pf_denoiser* d, float* z, const float* y, const float* x_txt, int32_t t,
                         int32_t t_next, uint32_t flags, float guidance, void* stream);
 
 /* n_steps steps over the host array `timesteps` (strictly decreasing); the first
- * warmup_steps (>= 1) run as warm-up steps. */
+ * warmup_steps (>= 1) run as warm-up steps.  Source: as
+ * denoiser_step. */
 pf_status denoiser_run(pf_denoiser* d, float* z, const float* y, const float* x_txt,
                        const int32_t* timesteps, int32_t n_steps, int32_t warmup_steps, float guidance,
                        void* stream);
 
-/* Thread-local text of the last non-OK status returned on this thread. */
+/* Thread-local text of the last non-OK status returned on this thread (an empty string if
+ * none; owned by the library, valid until the next failing call on this thread).  Source:
+ * none on the pages (the error channel of this status-code ABI). */
 const char* pf_last_error(void);
 
 /* ---------------------------------------------------------------------------------
@@ -294,7 +325,9 @@ const char* pf_last_error(void);
 
 /* y[i, :] = LayerNorm(x[i, :]) * (1 + scale) + shift for i < rows; LayerNorm without
  * affine, biased variance, fp32 statistics.  x fp32 [rows, hidden] (row stride hidden),
- * shift/scale fp32 [hidden], y [rows, hidden] in `dtype`. */
+ * shift/scale fp32 [hidden], y [rows, hidden] in `dtype`.  Source: none on the pages beyond
+ * "transformer layers" (mechanism 1); the DiT block's modulated LayerNorm is a reading.
+ * Errors: INVALID_ARG, UNSUPPORTED (hidden not a multiple of 8 or above 6144), HIP. */
 pf_status pf_ln_modulate(const float* x, int64_t rows, int32_t hidden, const float* shift,
                          const float* scale, float eps, void* y, int32_t dtype, void* stream);
 
@@ -305,15 +338,10 @@ pf_status pf_ln_modulate(const float* x, int64_t rows, int32_t hidden, const flo
  * fill the GPU split k into slices summed by a second pass (in a fixed order: deterministic);
  * calls sharing a workspace must not overlap in time (one stream, or ordered streams).
  * pf_gemm_workspace_size gives the bytes that allow the split the library would choose.
- * Tiles are 128 x 128 (a 2-stage ring, two workgroups per CU); the environment variable
- * PF_GEMM_TILE=128x64, 256, 128d or 256x128 forces another kernel (128 features x 64 tokens
- * with the same ring; or a deep ring: 256 x 256 with 4 stages, 128 x 128 with 8 stages, one
- * workgroup per CU; 256 features x 128 tokens with 3 stages, two per CU), and
- * PF_GEMM_SPLIT=s forces s k slices where the workspace allows; both are read on
- * every call, so set them before pf_gemm_workspace_size as well.  Inside a stage, when a
- * gated-residual projection is k-split, its reduce pass also computes the LayerNorm +
- * modulation that reads the updated rows (same bits as the separate kernel);
- * PF_FUSE_LN=0 turns that off. */
+ * Tiles are 128 x 128 (a 2-stage ring, two workgroups per CU).  Source: the projections of the
+ * transformer layers (mechanism 1; the block is a reading).  Errors: INVALID_ARG for a bad
+ * pointer, size, stride or epilogue; UNSUPPORTED for bf16 shapes with n or k not a multiple
+ * of 64; HIP if the launch fails. */
 pf_status pf_gemm(const void* a, int64_t lda, const void* w, const float* bias, int64_t m,
                   int64_t n, int64_t k, int32_t epi, void* c, int64_t ldc, const float* gate,
                   int32_t dtype, void* workspace, uint64_t workspace_bytes, void* stream);
@@ -332,7 +360,23 @@ pf_status pf_gemm_qkv_splice(const void* a, int64_t lda, const void* w, const fl
                              int64_t hidden, void* q, int64_t ldq, const pf_kv_view* kv, int64_t row_offset,
                              void* workspace, uint64_t workspace_bytes, void* stream);
 
-/* Workspace bytes pf_gemm can use for an [m, n, k] bf16 product (0: it never splits). */
+/* The gated-residual projection and the modulated LayerNorm that reads its result, as a stage
+ * runs them after the attention and MLP sublayers (bf16 only): x += gate * (a . w^T + bias),
+ * then y = LayerNorm(x) * (1 + scale) + shift.  a [m, k] bf16 (row stride lda), w [n, k] bf16,
+ * bias / gate / shift / scale fp32 [n], x fp32 [m, n] (contiguous, updated in place), y bf16
+ * [m, n] (contiguous, must not overlap x).  When the workspace lets the product split k, the
+ * pass that sums the slices also computes y (one launch fewer, x read once); otherwise the
+ * LayerNorm runs as its own kernel.  Either way x and y hold the same bits as pf_gemm
+ * (PF_EPI_GATED_RESIDUAL, same workspace) followed by pf_ln_modulate.  Requirements as for
+ * both calls (n % 64 == 0, k % 64 == 0, n <= 6144).  Errors: INVALID_ARG, UNSUPPORTED, HIP.  Source: as pf_gemm and pf_ln_modulate. */
+pf_status pf_gemm_residual_ln(const void* a, int64_t lda, const void* w, const float* bias, int64_t m,
+                              int64_t n, int64_t k, float* x, const float* gate, const float* shift,
+                              const float* scale, float eps, void* y, void* workspace,
+                              uint64_t workspace_bytes, void* stream);
+
+/* Workspace bytes pf_gemm can use for an [m, n, k] bf16 product (0: it never splits).
+ * Source: as pf_gemm.
+ * Errors: INVALID_ARG (bad sizes, NULL out), UNSUPPORTED (not gfx950). */
 pf_status pf_gemm_workspace_size(int64_t m, int64_t n, int64_t k, uint64_t* bytes);
 
 /* Full non-causal attention of `rows` query rows over the first seq_kv rows of kv:
@@ -343,16 +387,22 @@ pf_status pf_gemm_workspace_size(int64_t m, int64_t n, int64_t k, uint64_t* byte
  * key range across workgroups; pf_attention_workspace_size gives the bytes that allow every
  * split the kernel may choose.  A smaller (or NULL) workspace limits the split; the result
  * is the same function of the inputs either way, up to fp32 summation order.  The caller
- * owns the workspace and must not use it concurrently with this call. */
+ * owns the workspace and must not use it concurrently with this call.  Source: "Key
+ * contributions" of the PipeFusion summaries (the DiT keeps full attention: every query row
+ * attends over every buffer row, fresh or stale).  Errors: INVALID_ARG (pointers, strides,
+ * ranges, layouts), UNSUPPORTED (head_dim not 64 / 72 / 128, V not K8 for bf16), HIP. */
 pf_status pf_attention(const void* q, int64_t ldq, const pf_kv_view* kv, int64_t seq_kv,
                        int64_t rows, int32_t heads, int32_t head_dim, void* o, int64_t ldo,
                        void* workspace, uint64_t workspace_bytes, void* stream);
 
-/* Workspace bytes pf_attention can use for `rows` queries of `heads` x `head_dim`. */
+/* Workspace bytes pf_attention can use for `rows` queries of `heads` x `head_dim`.  Source:
+ * as pf_attention.  Errors:
+ * INVALID_ARG (bad sizes, NULL out). */
 pf_status pf_attention_workspace_size(int64_t rows, int32_t heads, int32_t head_dim, uint64_t* bytes);
 
 /* mod = SiLU(cond) . w_ada^T + b_ada: cond fp32 [hidden], w_ada [6*hidden, hidden] in
- * `dtype`, b_ada fp32 [6*hidden], mod fp32 [6*hidden]. */
+ * `dtype`, b_ada fp32 [6*hidden], mod fp32 [6*hidden].  Source: as stage_set_cond (a reading
+ * of the DiT block).  Errors: INVALID_ARG, UNSUPPORTED (hidden above 16384), HIP. */
 pf_status pf_adaln(const float* cond, const void* w_ada, const float* b_ada, int32_t hidden,
                    float* mod, int32_t dtype, void* stream);
 
@@ -364,7 +414,9 @@ pf_status pf_adaln(const float* cond, const void* w_ada, const float* b_ada, int
  * arithmetic, one bf16 rounding per value.  `flags` holds only those two bits (0: nothing
  * happens).  V and every other buffer row stay as they are.  q must not overlap the buffer.
  * Requirements: kv->dtype bf16, row_elems == heads * head_dim <= 6144, ldq and k_ld multiples
- * of 8; q, K, the gammas and the angles 16-byte aligned. */
+ * of 8; q, K, the gammas and the angles 16-byte aligned.  Source: as
+ * stage_load_text_weights (QK-RMSNorm and RoPE of the MM-DiT models, a reading).  Errors:
+ * INVALID_ARG, UNSUPPORTED, HIP. */
 pf_status pf_qk_norm_rope(void* q, int64_t ldq, const pf_kv_view* kv, int64_t row_offset, int64_t rows,
                           int32_t heads, int32_t head_dim, const float* q_gamma, const float* k_gamma,
                           const float* angles, uint32_t flags, void* stream);

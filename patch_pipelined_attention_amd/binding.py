@@ -91,6 +91,7 @@ _SIGNATURES = {
     "pf_gemm": [_P, _I64, _P, _P, _I64, _I64, _I64, _I32, _P, _I64, _P, _I32, _P, ctypes.c_uint64, _P],
     "pf_gemm_qkv_splice": [_P, _I64, _P, _P, _I64, _I64, _P, _I64, ctypes.POINTER(KVView), _I64, _P, ctypes.c_uint64,
                            _P],
+    "pf_gemm_residual_ln": [_P, _I64, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _F, _P, _P, ctypes.c_uint64, _P],
     "pf_gemm_workspace_size": [_I64, _I64, _I64, ctypes.POINTER(ctypes.c_uint64)],
     "pf_attention": [_P, _I64, ctypes.POINTER(KVView), _I64, _I64, _I32, _I32, _P, _I64, _P, ctypes.c_uint64, _P],
     "pf_qk_norm_rope": [_P, _I64, ctypes.POINTER(KVView), _I64, _I64, _I32, _I32, _P, _P, _P, _U32, _P],
@@ -233,6 +234,16 @@ def pf_gemm_qkv_splice(a, w, bias, q, kv: KVView, row_offset: int, m=None, lda=N
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().pf_gemm_qkv_splice(_ptr(a), lda, _ptr(w), _ptr(bias), m, hidden, _ptr(q), ldq, ctypes.byref(kv),
                                     row_offset, _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def pf_gemm_residual_ln(a, w, bias, x, gate, shift, scale, eps: float, y, lda=None, workspace=None,
+                        stream=None) -> None:
+    n, k = w.shape
+    m = x.shape[0]
+    lda = a.stride(0) if lda is None else lda
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().pf_gemm_residual_ln(_ptr(a), lda, _ptr(w), _ptr(bias), m, n, k, _ptr(x), _ptr(gate), _ptr(shift),
+                                     _ptr(scale), eps, _ptr(y), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def pf_gemm_workspace_size(m: int, n: int, k: int) -> int:

@@ -661,8 +661,12 @@ hipError_t launch_attention(const void* q, int64_t ldq, const void* k, int64_t l
                             int v_layout, int64_t hidden, int64_t seq_kv, int64_t rows, int heads, int head_dim,
                             void* o, int64_t ldo, int dtype, void* ws, size_t ws_bytes, hipStream_t s,
                             int64_t batch, int64_t kv_stride) {
-  (void)v_layout;
   if (rows <= 0 || batch <= 0) return hipSuccess;
+  // the bf16 kernel reads V in the K8 layout (8 keys of a column per 16 bytes) and whole
+  // heads of hidden columns; the fp32 kernel reads V row by row
+  if (v_layout != (dtype == kDtypeBF16 ? kLayoutK8 : kLayoutRows) || hidden != (int64_t)heads * head_dim ||
+      seq_kv < 1)
+    return hipErrorInvalidValue;
   switch (head_dim) {
     case 64:
       return launch_attn_d<64>(q, ldq, k, ldk, v, ldv, hidden, seq_kv, rows, heads, o, ldo, dtype, ws, ws_bytes, s,
@@ -670,9 +674,11 @@ hipError_t launch_attention(const void* q, int64_t ldq, const void* k, int64_t l
     case 72:
       return launch_attn_d<72>(q, ldq, k, ldk, v, ldv, hidden, seq_kv, rows, heads, o, ldo, dtype, ws, ws_bytes, s,
                                batch, kv_stride);
-    default:
+    case 128:
       return launch_attn_d<128>(q, ldq, k, ldk, v, ldv, hidden, seq_kv, rows, heads, o, ldo, dtype, ws, ws_bytes, s,
                                 batch, kv_stride);
+    default:
+      return hipErrorInvalidValue;
   }
 }
 

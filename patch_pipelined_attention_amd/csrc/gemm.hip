@@ -7,14 +7,12 @@
 // per lane, one token and 4 consecutive output features per 8-row group, so every
 // epilogue stores 4 contiguous values per access (8 B bf16 / 16 B fp32).
 //
-// Tiles: 128 x 128 with a 2-stage ring, two workgroups per CU.  A 128 x 64 variant and three
-// deep-ring variants (256 x 256 and 128 x 128 with one workgroup per CU, 256 x 128 with two)
-// can be forced for comparison.  Grids too small to fill the GPU split k: every slice writes its
-// fp32 partial tile and a reduce pass sums the slices in order (deterministic) and applies the
-// epilogue.  (A last-arriving-slice
-// merge inside the GEMM measured slower on MI355X: the partials cross XCDs, whose L2s are
-// not coherent, so they must be written through and read back from the device-coherent
-// level, a longer latency chain than one more launch.)
+// Tiles: 128 x 128 with a 2-stage ring, two workgroups per CU.  Grids too small to fill the
+// GPU split k: every slice writes its fp32 partial tile and a reduce pass sums the slices in
+// order (deterministic) and applies the epilogue.  (A last-arriving-slice merge inside the
+// GEMM measured slower on MI355X: the partials cross XCDs, whose L2s are not coherent, so
+// they must be written through and read back from the device-coherent level, a longer
+// latency chain than one more launch.)
 //
 // Workgroup ids map to tiles XCD by XCD (consecutive ids on one XCD), and within that in
 // groups of kGroupRows tile rows walked column by column, so the workgroups an XCD runs at
@@ -22,9 +20,6 @@
 //
 // fp32 path (tiny fp32 stages only): a plain 64x64 LDS-tiled FMA kernel.
 #include "pf_internal.h"
-
-#include <cstdlib>
-#include <cstring>
 
 namespace pf {
 
@@ -298,176 +293,6 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
   gemm_epilogue<BF, BT, FB, TB, EPI, SPLIT>(acc, m0, n0, M, N, bias, C, ldc, gate, sp, rg, split, part);
 }
 
-// vmcnt-only wait: at most N vector memory operations of this wavefront still outstanding.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// bf16 deep-ring kernel: BF features x BT tokens per workgroup, 4 wavefronts in a 2 x 2 grid,
-// each (BF/2) x (BT/2) = FB x TB blocks of 32 x 32.  k is staged 32 at a time (two MFMA
-// k-steps) in an NSTAGE ring filled NSTAGE - 1 tiles ahead by direct global -> LDS loads;
-// the loads are counted with explicit vmcnt waits so they stay in flight across barriers.
-// The first operands of tile kt+1 are read right after the barrier that publishes it, while
-// the MFMAs of tile kt's last k-step are still running.  One workgroup per CU.
-//   256 x 256, 4 stages: each wavefront 128 x 128 = 4 x 4 blocks (256 fp32 accumulators per
-//     lane, kept in the accumulation registers), 0.5 KB of LDS operand reads per MFMA: the
-//     highest per-k rate, for long reductions.
-//   128 x 128, 8 stages: seven tiles (224 k values) in flight hide the load latency that
-//     bounds a lone 2-stage workgroup, for grids with about one tile per CU.
-template <int BF, int BT, int NSTAGE, int OCC, int EPI, bool SPLIT>
-__global__ __launch_bounds__(256, OCC) void gemm_deep_kernel(const bf16* __restrict__ A, int64_t lda,
-                                                           const bf16* __restrict__ W, const float* __restrict__ bias,
-                                                           int64_t M, int64_t N, int64_t K, void* __restrict__ C,
-                                                           int64_t ldc, const float* __restrict__ gate, int tiles_n,
-                                                           int n_split, int ktiles_per_split,
-                                                           float* __restrict__ part, QkvSplice sp, RowGroups rg) {
-  constexpr int BK = 32;                 // k per stage: two MFMA k-steps
-  constexpr int KSTEPS = BK / 16;
-  constexpr int ROWS = BF + BT;          // stage rows: W rows, then X rows
-  constexpr int UPR = BK / 8;            // 16-byte units per row (4)
-  constexpr int UNITS = ROWS * UPR;      // 16-byte units per stage
-  constexpr int NINST = UNITS / 64;      // 64-lane direct loads per stage
-  constexpr int NPW = NINST / 4;         // per wavefront
-  constexpr int FB = BF / 64, TB = BT / 64;
-  constexpr int WJ = BF * UPR / 256;     // loads j < WJ of every wavefront fill W rows, the rest X rows
-  static_assert(BF * UPR % 256 == 0 && BT * UPR % 256 == 0, "W and X loads split evenly over the wavefronts");
-  static_assert(NSTAGE >= 3 && NSTAGE <= 9 && (NSTAGE - 2) * NPW < 64, "stage ring");
-  __shared__ __attribute__((aligned(16))) uint4 lds[NSTAGE][UNITS];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l32 = lane & 31, hi = lane >> 5;
-  const int wf = wave & 1, wt = wave >> 1;
-
-  const int lid = gemm_xcd_remap(blockIdx.x, gridDim.x);
-  const int split = lid % n_split;
-  const int rest = lid / n_split;
-  int64_t tile_m;
-  int tile_n;
-  gemm_tile_of(rest, (int)((M + BT - 1) / BT), tiles_n, tile_m, tile_n);
-  const int64_t n0 = (int64_t)tile_n * BF;
-  const int64_t m0 = tile_m * BT;
-  const int64_t nkt = K / BK;
-  const int64_t kt0 = (int64_t)split * ktiles_per_split;
-  const int64_t kt1 = kt0 + ktiles_per_split < nkt ? kt0 + ktiles_per_split : nkt;
-
-  // unit of (row r, chunk c in 0..3): the 8 rows of one 8-lane read phase land on distinct
-  // 16-byte bank groups (rows r, r+1 differ by 64 B; pairs of rows take the 4 chunk XORs)
-  auto unit = [](int r, int c) { return r * UPR + (c ^ ((r >> 1) & 3)); };
-
-  // Loads: wavefront w issues loads i = w + 4j; the first BF * UPR / 64 fill the W rows, the
-  // rest the X rows (j < WJ: W, else X, for every wavefront).  Per-lane byte offsets from the tile's
-  // row-0 base; rows past N or M read the last valid row (their results are never stored).
-  const bf16* Wt = W + n0 * K;
-  const bf16* Xt = A + m0 * lda;
-  uint32_t off[NPW];
-#pragma unroll
-  for (int j = 0; j < NPW; ++j) {
-    const int u = (wave + 4 * j) * 64 + lane;
-    const int r = u / UPR;
-    const int c = (u % UPR) ^ ((r >> 1) & 3);
-    if (r < BF) {
-      const int64_t rr = n0 + r < N ? r : N - 1 - n0;
-      off[j] = (uint32_t)((rr * K + c * 8) * 2);
-    } else {
-      const int64_t rr = m0 + (r - BF) < M ? r - BF : M - 1 - m0;
-      off[j] = (uint32_t)((rr * lda + c * 8) * 2);
-    }
-  }
-  auto issue = [&](int64_t kt, int st) {
-    const char* wb = reinterpret_cast<const char*>(Wt + kt * BK);
-    const char* xb = reinterpret_cast<const char*>(Xt + kt * BK);
-#pragma unroll
-    for (int j = 0; j < NPW; ++j)
-      dma_load16(j < WJ ? wb : xb, off[j], &lds[st][(wave + 4 * j) * 64]);
-  };
-  // this wavefront's loads of the tile before the `newer` most recently issued tiles are done
-  // (newer <= NSTAGE - 2: at most that many later tiles are ever in flight)
-  auto wait_tiles = [&](int newer) {
-    if constexpr (NSTAGE - 2 >= 7) { if (newer >= 7) { wait_vmcnt<(NSTAGE - 2 >= 7 ? 7 : 0) * NPW>(); return; } }
-    if constexpr (NSTAGE - 2 >= 6) { if (newer == 6) { wait_vmcnt<(NSTAGE - 2 >= 6 ? 6 : 0) * NPW>(); return; } }
-    if constexpr (NSTAGE - 2 >= 5) { if (newer == 5) { wait_vmcnt<(NSTAGE - 2 >= 5 ? 5 : 0) * NPW>(); return; } }
-    if constexpr (NSTAGE - 2 >= 4) { if (newer == 4) { wait_vmcnt<(NSTAGE - 2 >= 4 ? 4 : 0) * NPW>(); return; } }
-    if constexpr (NSTAGE - 2 >= 3) { if (newer == 3) { wait_vmcnt<(NSTAGE - 2 >= 3 ? 3 : 0) * NPW>(); return; } }
-    if (newer == 2) { wait_vmcnt<2 * NPW>(); return; }
-    if (newer == 1) { wait_vmcnt<NPW>(); return; }
-    wait_vmcnt<0>();
-  };
-
-  f32x16 acc[FB][TB];
-#pragma unroll
-  for (int i = 0; i < FB; ++i)
-#pragma unroll
-    for (int t = 0; t < TB; ++t)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][t][e] = 0.f;
-
-  auto read_frags = [&](const uint4* L, int ks, bf16x8 (&a)[FB], bf16x8 (&b)[TB]) {
-#pragma unroll
-    for (int i = 0; i < FB; ++i)
-      a[i] = *reinterpret_cast<const bf16x8*>(&L[unit(wf * (BF / 2) + i * 32 + l32, 2 * ks + hi)]);
-#pragma unroll
-    for (int t = 0; t < TB; ++t)
-      b[t] = *reinterpret_cast<const bf16x8*>(&L[unit(BF + wt * (BT / 2) + t * 32 + l32, 2 * ks + hi)]);
-  };
-
-  const int64_t nt = kt1 - kt0;
-  bf16x8 a[2][FB], b[2][TB];
-  // prologue: tiles kt0 .. kt0+NSTAGE-2 in flight, wait for kt0
-  for (int64_t u = 0; u < nt && u < NSTAGE - 1; ++u) issue(kt0 + u, (int)u);
-  {
-    const int64_t newer = (nt < NSTAGE - 1 ? nt : NSTAGE - 1) - 1;
-    wait_tiles((int)(newer < 0 ? 0 : newer));
-  }
-  lds_barrier();
-  if (nt > 0) read_frags(lds[0], 0, a[0], b[0]);
-  int st = 0;
-  // One k tile.  `steady`: tile kt + NSTAGE - 1 exists (so the loop body has no branch and
-  // the compiler can wait for exactly the operand reads each MFMA needs).
-  auto ktile = [&](int64_t kt, bool steady) {
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      const int cur = ks & 1, nxt = cur ^ 1;   // KSTEPS is even: k-step 0 of every tile uses buffer 0
-      if (ks + 1 < KSTEPS) {
-        read_frags(lds[st], ks + 1, a[nxt], b[nxt]);
-      } else if (steady || kt + 1 < kt1) {
-        // tile kt+1 landed for every wavefront; all are done with tile kt-1's stage
-        if (steady) {
-          wait_tiles(NSTAGE - 3);   // issued so far: tiles up to kt + NSTAGE - 2
-        } else {
-          const int64_t issued_after = (kt + NSTAGE - 2 < kt1 - 1 ? kt + NSTAGE - 2 : kt1 - 1) - (kt + 1);
-          wait_tiles((int)issued_after);
-        }
-        lds_barrier();
-        // operand reads first: the loads below are asm with a memory clobber, which nothing
-        // crosses, so reads placed after them could only start once all loads are issued
-        const int st1 = st + 1 == NSTAGE ? 0 : st + 1;
-        read_frags(lds[st1], 0, a[nxt], b[nxt]);
-        if (steady || kt + NSTAGE - 1 < kt1) issue(kt + NSTAGE - 1, st == 0 ? NSTAGE - 1 : st - 1);
-      }
-#pragma unroll
-      for (int i = 0; i < FB; ++i)
-#pragma unroll
-        for (int t = 0; t < TB; ++t)
-          acc[i][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cur][i], b[cur][t], acc[i][t], 0, 0, 0);
-      if (ks + 1 == KSTEPS && steady) {
-        // schedule: the next tile's operand reads, then this k-step's MFMAs
-        __builtin_amdgcn_sched_group_barrier(0x100, FB + TB, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, FB * TB, 0);
-      }
-    }
-    st = st + 1 == NSTAGE ? 0 : st + 1;
-  };
-  int64_t kt = kt0;
-  for (; kt + NSTAGE - 1 < kt1; ++kt) ktile(kt, true);
-  for (; kt < kt1; ++kt) ktile(kt, false);
-
-  gemm_epilogue<BF, BT, FB, TB, EPI, SPLIT>(acc, m0, n0, M, N, bias, C, ldc, gate, sp, rg, split, part);
-}
-
 // ---------------------------------------------------------------------------------
 // fp32 path: 64 tokens x 64 features per block, 256 threads with 4x4 outputs each,
 // k staged 16 at a time in LDS (k-major so the inner loop reads broadcast rows).
@@ -528,14 +353,6 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
   }
 }
 
-// Launch plan of a bf16 GEMM: kernel and k-split count.
-enum GemmKind { kGemm128 = 0, kGemmDeep256 = 1, kGemmDeep128 = 2, kGemm128x64 = 3, kGemm256x128 = 4 };
-struct GemmPlan {
-  int kind;     // GemmKind: 128 x 128 2-stage (2 per CU), 256 x 256 4-stage, 128 x 128 8-stage (1 per CU),
-                // 128 x 64 2-stage (2 per CU), 256 x 128 3-stage with k 32 deep (2 per CU)
-  int split;    // k slices (1 = no split)
-};
-
 static int gemm_cus() {
   static int cus = 0;
   if (cus == 0) {
@@ -550,127 +367,66 @@ static int gemm_cus() {
   return cus;
 }
 
-// The estimate only considers the 2-stage 128 x 128 kernel: with the grouped tile order it
-// measured faster than both deep-ring kernels at every DiT projection shape on MI355X (k from
-// 1152 to 12288, m from 1024 to 16384).  128 x 64 tiles beat it on narrow, short products
-// timed alone (the out-projections: PixArt patch 17.6 -> 12.1 us) but lost inside the stage,
-// where the weight tiles are no longer cache-resident and each is read by twice the
-// workgroups (C2 step 2.354 -> 2.377 ms).  The others stay selectable through PF_GEMM_TILE.
-// Smallest estimated time over tile size x k-split: rounds of resident workgroups x one
-// slice's time (a fixed cost plus its FLOPs at the tile's measured rate), plus writing and
-// re-reading the fp32 partials of a split.
-// The environment variable PF_GEMM_TILE=128, 128x64, 256 or 128d (the 8-stage 128 x 128 kernel)
-// forces the kernel (the k-split is still chosen by the estimate); any other value, or none,
-// leaves both to the plan.
-static int gemm_kind_override() {
-  const char* v = std::getenv("PF_GEMM_TILE");
-  if (!v) return -1;
-  if (std::strcmp(v, "128") == 0) return kGemm128;
-  if (std::strcmp(v, "256") == 0) return kGemmDeep256;
-  if (std::strcmp(v, "128d") == 0) return kGemmDeep128;
-  if (std::strcmp(v, "128x64") == 0) return kGemm128x64;
-  if (std::strcmp(v, "256x128") == 0) return kGemm256x128;
-  return -1;
-}
-
-// PF_GEMM_SPLIT=s forces s k slices where the workspace and k allow them (for measurements).
-// PF_FUSE_LN=0 turns the fused reduce + LayerNorm off (read on every call).
-static bool ln_fusion_enabled() {
-  const char* e = getenv("PF_FUSE_LN");
-  return !(e && e[0] == '0');
-}
-
-static int gemm_split_override() {
-  const char* v = std::getenv("PF_GEMM_SPLIT");
-  if (!v) return 0;
-  const int sp = std::atoi(v);
-  return sp >= 1 && sp <= kMaxGemmSplit ? sp : 0;
-}
-
-static GemmPlan gemm_plan(int64_t m, int64_t n, int64_t k, size_t ws_bytes) {
-  const int cus = gemm_cus();
-  const int force = gemm_kind_override();
-  const int force_sp = gemm_split_override();
-  GemmPlan best_plan{force >= 0 ? force : kGemm128, 1};
+// k-split count of a bf16 GEMM with 128 x 128 tiles (two resident workgroups per CU): the
+// smallest estimated time over the split s, rounds of resident workgroups x one slice's time
+// (a fixed cost plus its FLOPs at one workgroup's measured rate), plus writing and re-reading
+// the fp32 partials.  A split needs at least 4 k tiles per slice and fits the workspace.
+static int gemm_split_plan(int64_t m, int64_t n, int64_t k, size_t ws_bytes) {
+  constexpr int64_t kTile = 128, kBk = 64;
+  constexpr double kFixedS = 3e-6;       // per-tile fixed cost (prologue, epilogue)
+  constexpr double kRate = 1.65e12;      // FLOP/s of one resident workgroup
+  const int64_t slots = 2 * (int64_t)gemm_cus();
+  const int64_t tiles = ((m + kTile - 1) / kTile) * ((n + kTile - 1) / kTile);
+  int best_sp = 1;
   double best = 1e30;
-  for (int kind = 0; kind <= 4; ++kind) {
-    if (force >= 0 ? kind != force : kind != kGemm128) continue;
-    const int64_t bt = kind == kGemmDeep256 || kind == kGemm256x128 ? 256 : 128;   // features per tile
-    const int64_t bm = kind == kGemm128x64 ? 64 : kind == kGemm256x128 ? 128 : bt;  // tokens per tile
-    const int64_t bk = kind == kGemm128 || kind == kGemm128x64 ? 64 : 32;
-    const int64_t tiles = ((m + bm - 1) / bm) * ((n + bt - 1) / bt);
-    const int64_t slots = kind == kGemm128 || kind == kGemm128x64 || kind == kGemm256x128 ? 2 * (int64_t)cus
-                                                                                          : (int64_t)cus;
-    const double fixed_s = kind == kGemmDeep256 ? 30e-6 : 3e-6;
-    const double rate = kind == kGemmDeep256 ? 6.7e12 : 1.65e12;      // FLOP/s of one resident workgroup
-    for (int sp = 1; sp <= kMaxGemmSplit; ++sp) {
-      if (sp > 1 && k / bk < 4LL * sp) break;
-      if (sp > 1 && (size_t)sp * m * n * sizeof(float) > ws_bytes) break;
-      if (force_sp && sp != force_sp) continue;
-      const double t = (double)((tiles * sp + slots - 1) / slots) * (fixed_s + 2.0 * bt * bm * (double)k / sp / rate) +
-                       (sp > 1 ? 2.0 * sp * (double)m * (double)n * sizeof(float) / 5.0e12 : 0.0);
-      if (t < best * 0.98) {
-        best = t;
-        best_plan = {kind, sp};
-      }
+  for (int sp = 1; sp <= kMaxGemmSplit; ++sp) {
+    if (sp > 1 && k / kBk < 4LL * sp) break;
+    if (sp > 1 && (size_t)sp * m * n * sizeof(float) > ws_bytes) break;
+    const double t = (double)((tiles * sp + slots - 1) / slots) * (kFixedS + 2.0 * kTile * kTile * (double)k / sp / kRate) +
+                     (sp > 1 ? 2.0 * sp * (double)m * (double)n * sizeof(float) / 5.0e12 : 0.0);
+    if (t < best * 0.98) {
+      best = t;
+      best_sp = sp;
     }
   }
-  return best_plan;
+  return best_sp;
 }
 
 size_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k) {
-  const GemmPlan p = gemm_plan(m, n, k, (size_t)-1);
-  return p.split > 1 ? (size_t)p.split * m * n * sizeof(float) : 0;
+  const int sp = gemm_split_plan(m, n, k, (size_t)-1);
+  return sp > 1 ? (size_t)sp * m * n * sizeof(float) : 0;
 }
 
-template <int EPI, bool SPLIT>
-static constexpr auto gemm_small128 = gemm_bf16_kernel<128, 128, EPI, SPLIT>;
-template <int EPI, bool SPLIT>
-static constexpr auto gemm_small128x64 = gemm_bf16_kernel<128, 64, EPI, SPLIT>;
-template <int EPI, bool SPLIT>
-static constexpr auto gemm_deep256 = gemm_deep_kernel<256, 256, 4, 1, EPI, SPLIT>;
-template <int EPI, bool SPLIT>
-static constexpr auto gemm_deep128 = gemm_deep_kernel<128, 128, 8, 1, EPI, SPLIT>;
-template <int EPI, bool SPLIT>
-static constexpr auto gemm_wide = gemm_deep_kernel<256, 128, 3, 2, EPI, SPLIT>;
-
 template <int EPI>
-static void launch_gemm_epi(const void* a, int64_t lda, const void* w, const float* bias, int64_t m, int64_t n,
-                            int64_t k, void* c, int64_t ldc, const float* gate, int dtype, void* ws,
-                            size_t ws_bytes, hipStream_t s, const QkvSplice& sp, const RowGroups& rg,
-                            const LnAfter* ln, bool* ln_done) {
+static hipError_t launch_gemm_epi(const void* a, int64_t lda, const void* w, const float* bias, int64_t m, int64_t n,
+                                  int64_t k, void* c, int64_t ldc, const float* gate, int dtype, void* ws,
+                                  size_t ws_bytes, hipStream_t s, const QkvSplice& sp, const RowGroups& rg,
+                                  const LnAfter* ln, bool* ln_done) {
   if (dtype == kDtypeBF16) {
+    // the tile kernel reads whole 64-deep k tiles and 64-feature halves of its tiles
+    if (k % 64 != 0 || n % 64 != 0) return hipErrorInvalidValue;
     const bf16* A = static_cast<const bf16*>(a);
     const bf16* Wt = static_cast<const bf16*>(w);
-    const GemmPlan p = gemm_plan(m, n, k, ws ? ws_bytes : 0);
-    const int bt = p.kind == kGemmDeep256 || p.kind == kGemm256x128 ? 256 : 128;
-    const int bm = p.kind == kGemm128x64 ? 64 : p.kind == kGemm256x128 ? 128 : bt;
-    const int nkt = (int)(k / (p.kind == kGemm128 || p.kind == kGemm128x64 ? 64 : 32));
-    const int tiles_n = (int)((n + bt - 1) / bt);
-    const int64_t tiles = (int64_t)tiles_n * ((m + bm - 1) / bm);
-    const int kps = (nkt + p.split - 1) / p.split;
+    const int split = gemm_split_plan(m, n, k, ws ? ws_bytes : 0);
+    const int nkt = (int)(k / 64);
+    const int tiles_n = (int)((n + 127) / 128);
+    const int64_t tiles = (int64_t)tiles_n * ((m + 127) / 128);
+    const int kps = (nkt + split - 1) / split;
     const int used = (nkt + kps - 1) / kps;          // every slice gets at least one k tile
     float* part = static_cast<float*>(ws);
     const dim3 grid((unsigned)(tiles * used));
-#define PF_GEMM_LAUNCH(KERNEL)                                                                                       \
-  do {                                                                                                               \
-    if (used == 1)                                                                                                   \
-      hipLaunchKernelGGL((KERNEL<EPI, false>), grid, dim3(256), 0, s, A, lda, Wt, bias, m, n, k, c, ldc, gate, tiles_n, \
-                         1, nkt, nullptr, sp, rg);                                                                   \
-    else                                                                                                             \
-      hipLaunchKernelGGL((KERNEL<EPI, true>), grid, dim3(256), 0, s, A, lda, Wt, bias, m, n, k, c, ldc, gate, tiles_n, \
-                         used, kps, part, sp, rg);                                                                   \
-  } while (0)
-    if (p.kind == kGemmDeep256) PF_GEMM_LAUNCH(gemm_deep256);
-    else if (p.kind == kGemmDeep128) PF_GEMM_LAUNCH(gemm_deep128);
-    else if (p.kind == kGemm128x64) PF_GEMM_LAUNCH(gemm_small128x64);
-    else if (p.kind == kGemm256x128) PF_GEMM_LAUNCH(gemm_wide);
-    else PF_GEMM_LAUNCH(gemm_small128);
-#undef PF_GEMM_LAUNCH
+    if (used == 1)
+      hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, EPI, false>), grid, dim3(256), 0, s, A, lda, Wt, bias, m, n, k, c,
+                         ldc, gate, tiles_n, 1, nkt, nullptr, sp, rg);
+    else
+      hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, EPI, true>), grid, dim3(256), 0, s, A, lda, Wt, bias, m, n, k, c,
+                         ldc, gate, tiles_n, used, kps, part, sp, rg);
     if (used > 1) {
-      if (EPI == kEpiGatedResidual && ln && ln_fusion_enabled() && n <= kMaxHidden) {
+      if (EPI == kEpiGatedResidual && ln && n <= kMaxHidden) {
         // the reduce pass already holds whole updated rows: it applies the next LayerNorm too
-        (void)launch_reduce_residual_ln(part, used, m, (int)n, bias, static_cast<float*>(c), ldc, gate, rg, *ln, s);
+        const hipError_t e =
+            launch_reduce_residual_ln(part, used, m, (int)n, bias, static_cast<float*>(c), ldc, gate, rg, *ln, s);
+        if (e != hipSuccess) return e;
         if (ln_done) *ln_done = true;
       } else {
         const int64_t units = m * (n / 4);
@@ -684,6 +440,7 @@ static void launch_gemm_epi(const void* a, int64_t lda, const void* w, const flo
     hipLaunchKernelGGL(gemm_f32_kernel<EPI>, dim3((unsigned)tiles), dim3(256), 0, s, static_cast<const float*>(a), lda,
                        static_cast<const float*>(w), bias, m, n, k, static_cast<float*>(c), ldc, gate, tiles_n, rg);
   }
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm(const void* a, int64_t lda, const void* w, const float* bias, int64_t m, int64_t n, int64_t k,
@@ -697,28 +454,24 @@ hipError_t launch_gemm(const void* a, int64_t lda, const void* w, const float* b
   if (sp.grp_rows <= 0 || rg.rows <= 0) return hipErrorInvalidValue;
   switch (epi) {
     case kEpiStore:
-      launch_gemm_epi<kEpiStore>(a, lda, w, bias, m, n, k, c, ldc, gate, dtype, ws, ws_bytes, s, sp, rg, nullptr,
-                                 nullptr);
-      break;
+      return launch_gemm_epi<kEpiStore>(a, lda, w, bias, m, n, k, c, ldc, gate, dtype, ws, ws_bytes, s, sp, rg,
+                                        nullptr, nullptr);
     case kEpiGeluTanh:
-      launch_gemm_epi<kEpiGeluTanh>(a, lda, w, bias, m, n, k, c, ldc, gate, dtype, ws, ws_bytes, s, sp, rg, nullptr,
-                                    nullptr);
-      break;
+      return launch_gemm_epi<kEpiGeluTanh>(a, lda, w, bias, m, n, k, c, ldc, gate, dtype, ws, ws_bytes, s, sp, rg,
+                                           nullptr, nullptr);
     case kEpiGeluErf:
-      launch_gemm_epi<kEpiGeluErf>(a, lda, w, bias, m, n, k, c, ldc, gate, dtype, ws, ws_bytes, s, sp, rg, nullptr,
-                                   nullptr);
-      break;
+      return launch_gemm_epi<kEpiGeluErf>(a, lda, w, bias, m, n, k, c, ldc, gate, dtype, ws, ws_bytes, s, sp, rg,
+                                          nullptr, nullptr);
     case kEpiQkvSplice:
       if (dtype != kDtypeBF16 || !splice) return hipErrorInvalidValue;
-      launch_gemm_epi<kEpiQkvSplice>(a, lda, w, bias, m, n, k, c, ldc, gate, dtype, ws, ws_bytes, s, sp, rg, nullptr,
-                                     nullptr);
-      break;
+      return launch_gemm_epi<kEpiQkvSplice>(a, lda, w, bias, m, n, k, c, ldc, gate, dtype, ws, ws_bytes, s, sp, rg,
+                                            nullptr, nullptr);
+    case kEpiGatedResidual:
+      return launch_gemm_epi<kEpiGatedResidual>(a, lda, w, bias, m, n, k, c, ldc, gate, dtype, ws, ws_bytes, s, sp,
+                                                rg, ln, ln_done);
     default:
-      launch_gemm_epi<kEpiGatedResidual>(a, lda, w, bias, m, n, k, c, ldc, gate, dtype, ws, ws_bytes, s, sp, rg, ln,
-                                         ln_done);
-      break;
+      return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 }  // namespace pf

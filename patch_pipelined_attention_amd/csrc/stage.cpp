@@ -44,6 +44,10 @@ extern "C" const char* pf_last_error(void) { return g_last_error.c_str(); }
 void pf::pf_set_last_error(const char* msg) { g_last_error = msg; }
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+static bool ranges_overlap(const void* a, size_t an, const void* b, size_t bn) {
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + bn && b0 < a0 + an;
+}
 static size_t dtype_size(int dt) { return dt == PF_BF16 ? 2 : 4; }
 static bool dtype_ok(int dt) { return dt == PF_BF16 || dt == PF_FP32; }
 
@@ -205,6 +209,27 @@ extern "C" pf_status pf_gemm(const void* a, int64_t lda, const void* w, const fl
   hipError_t e = launch_gemm(a, lda, w, bias, m, n, k, epi, c, ldc, gate, dtype, workspace,
                              workspace ? (size_t)workspace_bytes : 0, (hipStream_t)stream);
   return e == hipSuccess ? PF_OK : hip_fail(e, "gemm launch");
+}
+
+extern "C" pf_status pf_gemm_residual_ln(const void* a, int64_t lda, const void* w, const float* bias, int64_t m,
+                                         int64_t n, int64_t k, float* x, const float* gate, const float* shift,
+                                         const float* scale, float eps, void* y, void* workspace,
+                                         uint64_t workspace_bytes, void* stream) {
+  pf_status st = validate_gemm(a, lda, w, bias, m, n, k, PF_EPI_GATED_RESIDUAL, x, n, gate, PF_BF16);
+  if (st != PF_OK) return st;
+  if ((st = validate_ln(x, m, (int32_t)n, shift, scale, y, PF_BF16)) != PF_OK) return st;
+  if (workspace && !aligned16(workspace))
+    return fail(PF_ERR_INVALID_ARG, "gemm_residual_ln: workspace must be 16-byte aligned");
+  if (ranges_overlap(y, (size_t)(m * n) * 2, x, (size_t)(m * n) * 4))
+    return fail(PF_ERR_INVALID_ARG, "gemm_residual_ln: y overlaps x");
+  if ((st = check_device()) != PF_OK) return st;
+  const hipStream_t s = (hipStream_t)stream;
+  const LnAfter ln{shift, scale, eps, y};
+  bool ln_done = false;
+  hipError_t e = launch_gemm(a, lda, w, bias, m, n, k, kEpiGatedResidual, x, n, gate, PF_BF16, workspace,
+                             workspace ? (size_t)workspace_bytes : 0, s, nullptr, nullptr, &ln, &ln_done);
+  if (e == hipSuccess && !ln_done) e = launch_ln_modulate(x, m, (int)n, shift, scale, eps, y, PF_BF16, s);
+  return e == hipSuccess ? PF_OK : hip_fail(e, "gemm_residual_ln launch");
 }
 
 extern "C" pf_status pf_gemm_qkv_splice(const void* a, int64_t lda, const void* w, const float* bias, int64_t m,
@@ -815,11 +840,6 @@ static pf_status run_patch_impl(pf_stage* st, int64_t off, int64_t n, const floa
     if (e != hipSuccess) return stage_hip_fail(st, e, "stage_run_patch: hipMemcpy2DAsync");
   }
   return run_rows(st, off, n, x_out, x_stride, s);
-}
-
-static bool ranges_overlap(const void* a, size_t an, const void* b, size_t bn) {
-  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
-  return a0 < b0 + bn && b0 < a0 + an;
 }
 
 extern "C" pf_status stage_run_patch(pf_stage* st, int64_t row_off, int64_t rows, const float* x_in, float* x_out,

@@ -70,38 +70,41 @@ def test_gemm_bf16(m, n, k, epi, split):
     assert_close(host(c), want, f"gemm bf16 {m}x{n}x{k} epi={epi}")
 
 
-@pytest.mark.parametrize("kernel", ["256", "128d", "128x64", "256x128"], ids=["deep256", "deep128", "t128x64", "t256x128"])
+@pytest.mark.parametrize("m,n,k", [(1024, 1152, 1152), (1024, 1152, 4608), (2048, 1536, 6144), (100, 3072, 3072),
+                                   (2048, 3072, 12288), (77, 192, 128)])
 @pytest.mark.parametrize("split", [False, True], ids=["whole", "ksplit"])
-@pytest.mark.parametrize("m,n,k", [(77, 192, 128), (300, 1344, 1152), (257, 640, 4608)])
-@pytest.mark.parametrize("epi", [B.PF_EPI_STORE, B.PF_EPI_GELU_TANH, B.PF_EPI_GATED_RESIDUAL])
-def test_gemm_bf16_deep_ring(m, n, k, epi, split, kernel, monkeypatch):
-    """The kernels other than the default, forced through PF_GEMM_TILE (deep rings: 256 x 256
-    with 4 stages, 128 x 128 with 8, 256 features x 128 tokens with 3 and two workgroups per CU;
-    and 128 features x 64 tokens with the 2-stage ring): ragged
-    m and n (partial tiles in both), k from fewer tiles than the ring holds to a long ring, with
-    and without the k split."""
+def test_gemm_residual_ln_is_bit_identical(m, n, k, split):
+    """The gated-residual projection followed by the modulated LayerNorm of its rows, as one call
+    (pf_gemm_residual_ln: with a workspace the k-split's reduce pass also computes the LayerNorm)
+    gives the same bits as pf_gemm with the same workspace followed by pf_ln_modulate, and both
+    match the oracle."""
     torch = torch_cuda()
-    monkeypatch.setenv("PF_GEMM_TILE", kernel)
-    ws = B.gemm_workspace(m, n, k) if split else None
-    seed = m * 5 + n * 3 + k + epi
+    seed = m + 3 * n + 7 * k
     a = synth.randn((m, k), seed, std=1.0, bf16=True)
-    w = synth.randn((n, k), seed + 1, std=1.0 / math.sqrt(k), bf16=True)
-    bias = synth.randn((n,), seed + 2, std=0.5)
-    y = ref.linear(a, w, bias)
-    if epi == B.PF_EPI_GATED_RESIDUAL:
-        x0 = synth.randn((m, n), seed + 3)
-        gate = synth.randn((n,), seed + 4)
-        c = dev(torch, x0)
-        B.pf_gemm(dev(torch, a, torch.bfloat16), dev(torch, w, torch.bfloat16), dev(torch, bias), epi, c,
-                  gate=dev(torch, gate), workspace=ws)
-        want = x0 + gate * y
-    else:
-        c = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
-        B.pf_gemm(dev(torch, a, torch.bfloat16), dev(torch, w, torch.bfloat16), dev(torch, bias), epi, c,
-                  workspace=ws)
-        act = {B.PF_EPI_STORE: lambda v: v, B.PF_EPI_GELU_TANH: ref.gelu_tanh}[epi]
-        want = ref.bf16_round(act(y))
-    assert_close(host(c), want, f"gemm bf16 deep ring {kernel} {m}x{n}x{k} epi={epi}")
+    w = synth.randn((n, k), seed + 1, std=0.02, bf16=True)
+    bias = synth.randn((n,), seed + 2, std=0.02)
+    x0 = synth.randn((m, n), seed + 3)
+    gate = synth.randn((n,), seed + 4, std=0.5)
+    shift = synth.randn((n,), seed + 5, std=0.4)
+    scale = synth.randn((n,), seed + 6, std=0.4)
+    ws = B.gemm_workspace(m, n, k) if split else None
+    ad, wd, bd, gd = dev(torch, a, torch.bfloat16), dev(torch, w, torch.bfloat16), dev(torch, bias), dev(torch, gate)
+    sd, scd = dev(torch, shift), dev(torch, scale)
+    x1, x2 = dev(torch, x0), dev(torch, x0)
+    y1 = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    y2 = torch.empty_like(y1)
+    print(f"[gemm+ln] {m}x{n}x{k} split={split}", flush=True)
+    B.pf_gemm_residual_ln(ad, wd, bd, x1, gd, sd, scd, 1e-6, y1, workspace=ws)
+    B.pf_gemm(ad, wd, bd, B.PF_EPI_GATED_RESIDUAL, x2, gate=gd, workspace=ws)
+    B.pf_ln_modulate(x2, sd, scd, 1e-6, y2)
+    torch.cuda.synchronize()
+    assert torch.equal(x1, x2), "residual differs from the unfused pair"
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16)), "LayerNorm output differs from the unfused pair"
+    rows = np.arange(m) if m <= 128 else np.random.default_rng(seed).choice(m, 48, replace=False)
+    xw = x0[rows] + gate * ref.linear(a[rows], w, bias)
+    assert_close(host(x1)[rows], xw, f"gemm+ln {m}x{n}x{k} residual", max_abs_tol=1e-3, rel_tol=1e-5)
+    assert_close(host(y1)[rows], ref.bf16_round(ref.modulate(ref.layer_norm(host(x1)[rows]), shift, scale)),
+                 f"gemm+ln {m}x{n}x{k} LayerNorm of the updated rows")
 
 
 def test_gemm_bf16_long_k_default_plan():

@@ -34,11 +34,14 @@ Three precision modes, all fp64 code:
   rounded to bf16 (round to nearest even): the modulated LayerNorm outputs,
   Q/K/V, the KV buffer after drift noise, the attention output and the GELU
   output.  Softmax probabilities are not rounded.
-* ``bf16p``: ``bf16`` plus the unnormalised softmax weights exp(s - rowmax)
-  rounded to bf16 before the product with V.  It is the same computation with
-  one more rounding point; comparing it with ``bf16`` measures how far bf16
-  probabilities alone move a stage's output (the noise floor any bf16
-  flash-attention path shares).
+* ``bf16p``: ``bf16`` plus bf16 softmax probabilities, the operand of the
+  probability-times-V contraction: the unnormalised weights 2^(s log2(e)) of
+  the scaled scores s are rounded to bf16 relative to a power-of-two reference
+  (the result does not depend on which power of two: rounding commutes with
+  scaling by 2^k), and each row is normalised by the sum of the same rounded
+  weights, so the normalised weights of a row sum to one.  It is the bf16-in /
+  fp32-accumulate computation with P among the bf16 inputs; comparing it with
+  ``bf16`` measures how far bf16 probabilities alone move a stage's output.
 
 Parity status: every function below is pinned in the CPU test-suite by closed
 forms, invariants, library special cases or brute force.  The choice of block
@@ -146,8 +149,10 @@ def attention(q, k, v, heads: int, head_dim: int, chunk: int = 256, round_p: boo
 
     Head j uses columns [j*d, (j+1)*d) of q, k and v.  O_j = softmax(Q_j K_j^T / sqrt(d)) V_j.
     Query rows are processed in chunks only to bound memory; each row's arithmetic is unchanged.
-    round_p: the unnormalised weights exp(s - rowmax) are rounded to bf16 before the product
-    with V and the row sum is taken unrounded (the plain definition of bf16 probabilities).
+    round_p: bf16 probabilities.  With t = s log2(e) the scores in base-2 units, the weights
+    w = bf16(2^(t - k)) for the integer k = ceil(max_row t) (any integer gives the same bits,
+    barring underflow, since scaling by a power of two commutes with rounding) multiply V, and
+    the row is normalised by sum(w), the sum of the same rounded weights.
     """
     q = np.asarray(q, F64)
     k = np.asarray(k, F64)
@@ -163,8 +168,9 @@ def attention(q, k, v, heads: int, head_dim: int, chunk: int = 256, round_p: boo
             r1 = min(n, r0 + chunk)
             s = (q[r0:r1, cs] @ kj.T) * scale
             if round_p:
-                e = np.exp(s - s.max(axis=-1, keepdims=True))
-                out[r0:r1, cs] = (bf16_round(e) @ vj) / e.sum(axis=-1, keepdims=True)
+                t = s / math.log(2.0)
+                w = bf16_round(np.exp2(t - np.ceil(t.max(axis=-1, keepdims=True))))
+                out[r0:r1, cs] = (w @ vj) / w.sum(axis=-1, keepdims=True)
             else:
                 out[r0:r1, cs] = softmax_rows(s) @ vj
     return out

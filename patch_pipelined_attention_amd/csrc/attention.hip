@@ -25,13 +25,17 @@
 //   * softmax in base 2: p = exp2(s * log2(e)/sqrt(D) - m), fp32 statistics, P rounded to
 //     bf16 for the P.V product and the row sum taken over the same rounded values (for
 //     D = 72 by the P.V MFMA itself, through a ones row in the padding of O^T).  The
-//     reference max m is raised (and O, l rescaled) only when a tile's max exceeds it by
-//     more than 8, so p <= 2^8 and the rescale is rare.
+//     reference m is an integer, raised (and O, l rescaled) only when a tile's max exceeds
+//     it by more than 8, so p <= 2^8 and the rescale is rare.  Because m is an integer, every
+//     rescale multiplies by an exact power of two, and the rounded weights are those of
+//     bf16(2^(s log2(e)/sqrt(D))) scaled by 2^-m: the same values whatever the order of the
+//     key tiles, the split of the key range or the running max at the time a tile is seen.
 //   * D = 72 pads the score contraction to 80 and the output rows to 96 with zero
 //     operands; nothing outside the real 72 columns is read or written.
 //   * when there are too few (query tile, head) pairs to fill the GPU, the key range is
-//     split across workgroups; each writes its slice's normalised result in bf16 with the
-//     slice's (m, l), and a combine kernel merges them (a convex combination).
+//     split across workgroups; each writes its slice's normalised result in fp32 with the
+//     slice's (m, l), and a combine kernel merges them (a convex combination with power-of-two
+//     weights times l, so the merge adds only fp32 rounding to the unsplit result).
 //   * the block index is remapped so each XCD (blocks are dealt round-robin to the 8
 //     XCDs) works on a contiguous run of query tiles that share K/V in its L2.
 //
@@ -67,7 +71,7 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const bf16* __restric
                                                          const bf16* __restrict__ Vb, int64_t hidden,
                                                          int64_t S, int64_t rows, int n_qtiles, int n_split,
                                                          int tiles_per_split, bf16* __restrict__ O,
-                                                         int64_t ldo, bf16* __restrict__ part_o,
+                                                         int64_t ldo, float* __restrict__ part_o,
                                                          float* __restrict__ part_ml, float scale_log2,
                                                          int64_t grp_rows, int qtiles_per_grp, int64_t kv_stride) {
   constexpr int BQ = kAttnWaves * 32 * QB;
@@ -336,7 +340,8 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const bf16* __restric
     if (__any(raise)) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        const float m_new = fmaxf(m_ref[qb], mt[qb]);
+        // integer reference: alpha is an exact power of two
+        const float m_new = fmaxf(m_ref[qb], __builtin_ceilf(mt[qb]));
         const float alpha = __builtin_amdgcn_exp2f(m_ref[qb] - m_new);
         m_ref[qb] = m_new;
         l_run[qb] *= alpha;
@@ -430,23 +435,36 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const bf16* __restric
 
 #pragma unroll
   // Whole key range: O = acc / l in bf16.  One slice of a split range: the slice's own
-  // normalised result acc_s / l_s, also in bf16, plus (m_s, l_s) for the merge.
+  // normalised result acc_s / l_s in fp32, plus (m_s, l_s) for the merge.
   for (int qb = 0; qb < QB; ++qb) {
     const float l_tot = l_run[qb] + __shfl_xor(l_run[qb], 32, 64);
     if (!q_ok[qb]) continue;
     const float inv = 1.0f / l_tot;
-    bf16* dst = n_split == 1 ? O + q_row[qb] * ldo + col0 : part_o + ((int64_t)split * rows + q_row[qb]) * hidden + col0;
+    if (n_split == 1) {
+      bf16* dst = O + q_row[qb] * ldo + col0;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d = db * 32 + 8 * g + 4 * hi;
-        if (d < D) {
-          bf16x4 ov = {(bf16)(o[qb][db][4 * g + 0] * inv), (bf16)(o[qb][db][4 * g + 1] * inv),
-                       (bf16)(o[qb][db][4 * g + 2] * inv), (bf16)(o[qb][db][4 * g + 3] * inv)};
-          *reinterpret_cast<bf16x4*>(dst + d) = ov;
+        for (int g = 0; g < 4; ++g) {
+          const int d = db * 32 + 8 * g + 4 * hi;
+          if (d < D) {
+            bf16x4 ov = {(bf16)(o[qb][db][4 * g + 0] * inv), (bf16)(o[qb][db][4 * g + 1] * inv),
+                         (bf16)(o[qb][db][4 * g + 2] * inv), (bf16)(o[qb][db][4 * g + 3] * inv)};
+            *reinterpret_cast<bf16x4*>(dst + d) = ov;
+          }
         }
-      }
+    } else {
+      float* dst = part_o + ((int64_t)split * rows + q_row[qb]) * hidden + col0;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d = db * 32 + 8 * g + 4 * hi;
+          if (d < D)
+            *reinterpret_cast<float4*>(dst + d) = make_float4(o[qb][db][4 * g + 0] * inv, o[qb][db][4 * g + 1] * inv,
+                                                              o[qb][db][4 * g + 2] * inv, o[qb][db][4 * g + 3] * inv);
+        }
+    }
     if (n_split > 1) {
       if (hi == 0) {
         const int64_t H = hidden / D;
@@ -457,14 +475,15 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const bf16* __restric
   }
 }
 
-// Merge the per-split partial results.  Slice s holds x_s = acc_s / l_s (bf16) with its
-// reference max m_s and weight sum l_s, so O = sum_s w_s x_s / sum_s w_s with
-// w_s = 2^(m_s - M) l_s (M = max_s m_s): a convex combination of the slices' results.
+// Merge the per-split partial results.  Slice s holds x_s = acc_s / l_s (fp32) with its
+// integer reference m_s and weight sum l_s, so O = sum_s w_s x_s / sum_s w_s with
+// w_s = 2^(m_s - M) l_s (M = max_s m_s, 2^(m_s - M) exact): a convex combination of the
+// slices' results.
 // One thread per (row, head, 8 columns).  The loop over slices is unrolled to the largest
 // split count (indices past n_split clamped, their terms skipped), so every load of a thread
 // is issued before the first is used.
 template <int D>
-__global__ __launch_bounds__(256) void attn_combine_kernel(const bf16* __restrict__ part_o,
+__global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ part_o,
                                                            const float* __restrict__ part_ml, int n_split,
                                                            int64_t rows, int H, bf16* __restrict__ O,
                                                            int64_t ldo) {
@@ -477,14 +496,16 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const bf16* __restric
   const int64_t row = rest / H;
   const int64_t hidden = (int64_t)H * D;
   float m[kMaxAttnSplit], l[kMaxAttnSplit];
-  bf16x8 x[kMaxAttnSplit];
+  float4 xa[kMaxAttnSplit], xb[kMaxAttnSplit];
 #pragma unroll
   for (int sp = 0; sp < kMaxAttnSplit; ++sp) {
     const int64_t sc = sp < n_split ? sp : n_split - 1;   // slices past n_split re-read the last (unused)
     const float2 ml = reinterpret_cast<const float2*>(part_ml)[(sc * H + head) * rows + row];
     m[sp] = ml.x;
     l[sp] = ml.y;
-    x[sp] = *reinterpret_cast<const bf16x8*>(part_o + (sc * rows + row) * hidden + (int64_t)head * D + chunk * 8);
+    const float4* src = reinterpret_cast<const float4*>(part_o + (sc * rows + row) * hidden + (int64_t)head * D + chunk * 8);
+    xa[sp] = src[0];
+    xb[sp] = src[1];
   }
   float M = m[0];
 #pragma unroll
@@ -497,8 +518,14 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const bf16* __restric
     if (sp < n_split) {
       const float w = __builtin_amdgcn_exp2f(m[sp] - M) * l[sp];
       wsum += w;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, (float)x[sp][e], acc[e]);
+      acc[0] = fmaf(w, xa[sp].x, acc[0]);
+      acc[1] = fmaf(w, xa[sp].y, acc[1]);
+      acc[2] = fmaf(w, xa[sp].z, acc[2]);
+      acc[3] = fmaf(w, xa[sp].w, acc[3]);
+      acc[4] = fmaf(w, xb[sp].x, acc[4]);
+      acc[5] = fmaf(w, xb[sp].y, acc[5]);
+      acc[6] = fmaf(w, xb[sp].z, acc[6]);
+      acc[7] = fmaf(w, xb[sp].w, acc[7]);
     }
   }
   const float inv = 1.0f / wsum;
@@ -629,9 +656,9 @@ static hipError_t launch_attn_d(const void* q, int64_t ldq, const void* k, int64
     const int tps = (int)((ntiles + n_split - 1) / n_split);
     const int n_used = (int)((ntiles + tps - 1) / tps);      // every split gets at least one tile
     const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
-    // workspace: bf16 slice results [n_used][all_rows][hidden], then fp32 (m, l) pairs [n_used][heads][all_rows]
-    bf16* part_o = static_cast<bf16*>(ws);
-    float* part_ml = part_o ? reinterpret_cast<float*>(part_o + (size_t)n_used * all_rows * hidden) : nullptr;
+    // workspace: fp32 slice results [n_used][all_rows][hidden], then fp32 (m, l) pairs [n_used][heads][all_rows]
+    float* part_o = static_cast<float*>(ws);
+    float* part_ml = part_o ? part_o + (size_t)n_used * all_rows * hidden : nullptr;
     hipLaunchKernelGGL((attn_bf16_kernel<D, QB>), dim3((unsigned)(wg * n_used)), dim3(64 * kAttnWaves), 0, s,
                        static_cast<const bf16*>(q), ldq, static_cast<const bf16*>(k), ldk,
                        static_cast<const bf16*>(v), hidden, seq_kv, all_rows, n_qtiles, n_used, tps,
@@ -654,7 +681,7 @@ static hipError_t launch_attn_d(const void* q, int64_t ldq, const void* k, int64
 
 size_t attention_workspace_bytes(int64_t rows, int64_t hidden, int heads, int n_split) {
   if (n_split <= 1) return 0;
-  return sizeof(bf16) * (size_t)n_split * rows * hidden + sizeof(float) * 2 * (size_t)n_split * rows * heads;
+  return sizeof(float) * (size_t)n_split * rows * hidden + sizeof(float) * 2 * (size_t)n_split * rows * heads;
 }
 
 hipError_t launch_attention(const void* q, int64_t ldq, const void* k, int64_t ldk, const void* v, int64_t ldv,

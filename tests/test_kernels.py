@@ -225,7 +225,8 @@ def test_attention_bf16(D, H, S, rows, split):
     print(f"[attn] D={D} H={H} S={S} rows={rows} split={split}", flush=True)
     B.pf_attention(dev(torch, q, torch.bfloat16), kv, S, rows, H, D, o, workspace=ws)
     want = ref.attention(q[:, :h], K, V, H, D)
-    assert_close(host(o), ref.bf16_round(want), f"attention bf16 D={D} S={S} rows={rows} vs bf16-in")
+    want_p = ref.attention(q[:, :h], K, V, H, D, round_p=True)
+    assert_close(host(o), ref.bf16_round(want_p), f"attention bf16 D={D} S={S} rows={rows} vs bf16p")
     assert_close(host(o), want, f"attention bf16 D={D} S={S} rows={rows} vs exact")
 
 
@@ -254,7 +255,8 @@ def test_attention_full_size_sampled(cfg):
     rows = np.unique(np.concatenate([[0, 1, 255, 256, 511, 512, P - 1], rng.choice(P, 41, replace=False)]))
     got = host(o)[rows]
     want = ref.attention(q[rows, :h], K, V, H, D)
-    assert_close(got, ref.bf16_round(want), f"attention {cfg} full size, sampled rows vs bf16-in")
+    want_p = ref.attention(q[rows, :h], K, V, H, D, round_p=True)
+    assert_close(got, ref.bf16_round(want_p), f"attention {cfg} full size, sampled rows vs bf16p")
     assert_close(got, want, f"attention {cfg} full size, sampled rows vs exact")
 
 
@@ -266,11 +268,12 @@ def test_attention_bf16_closed_forms(D):
     K = synth.randn((S, h), 51, bf16=True)
     V = synth.randn((S, h), 52, bf16=True)
     q = synth.randn((rows, h), 53, bf16=True)
-    # V = 1 -> every output is exactly 1 up to P rounding (softmax rows sum to one)
+    # V = 1 -> every output is 1: the rounded weights are normalised by their own sum, so only
+    # fp32 summation order separates l from the P.V row sums (far below one bf16 ulp of 1)
     kt, vt, kv = _kv_bf16(torch, K, np.ones_like(V))
     o = torch.empty((rows, h), dtype=torch.bfloat16, device="cuda")
     B.pf_attention(dev(torch, q, torch.bfloat16), kv, S, rows, H, D, o)
-    assert np.abs(host(o) - 1.0).max() <= 8e-3
+    assert np.abs(host(o) - 1.0).max() <= 2.0 ** -8
     # Q = 0 -> uniform weights -> column mean of V
     kt, vt, kv = _kv_bf16(torch, K, V)
     B.pf_attention(torch.zeros((rows, h), dtype=torch.bfloat16, device="cuda"), kv, S, rows, H, D, o)
@@ -288,6 +291,55 @@ def test_attention_bf16_closed_forms(D):
     for j in range(H):
         np.testing.assert_allclose(got[:, j * D:(j + 1) * D], np.broadcast_to(V[17 + j, j * D:(j + 1) * D], (rows, D)),
                                    atol=1e-6)
+
+
+@pytest.mark.parametrize("split", [False, True], ids=["whole", "split"])
+@pytest.mark.parametrize("D", [64, 72, 128])
+def test_attention_bf16_rescale_in_late_tiles(D, split):
+    """Row maxima that rise after the first key tile, so the kernel raises its reference and
+    rescales O and l in the middle of the key loop (and, with the split workspace, inside later
+    slices, whose references the merge then combines).  S = 2100 keys = 66 tiles, the last one
+    partial; 3 heads x 70 query rows fill 3 workgroups, so with the workspace the key range splits
+    into 8 slices of 9 tiles (slice 1 = keys 288..575, slice 5 = keys 1440..1727).
+      head 0: a ramp along one K column, 4 per key in base-2 score units over every 3 tiles for
+              the rows with a positive query component (the reference rises again and again)
+              and falling for the others (maximum in tile 0);
+      head 1: one key of logit +40 in slice 1 (key 300) and one of +60 in slice 5 (key 1500);
+      head 2: one key of logit +50 in the last, partial tile (key 2099).
+    Checked against the bf16p oracle at the contract's tolerances and the exact oracle."""
+    torch = torch_cuda()
+    H, S, rows = 3, 2100, 70
+    h = H * D
+    seed = 8100 + D
+    q = synth.randn((rows, h), seed, std=1.0)
+    K = synth.randn((S, h), seed + 1, std=1.0)
+    V = synth.randn((S, h), seed + 2, std=1.0, bf16=True)
+    sq = math.sqrt(D)
+    # head 0: ramp; logit slope q0 * a / sqrt(D) per key with q0 = +-4, a chosen for ~0.083 base-2 units per key
+    q[:, 0] = np.where(np.arange(rows) % 2 == 0, 4.0, -4.0)
+    K[:, 0] = np.arange(S) * (0.083 / math.log2(math.e)) * sq / 4.0
+    # head 1: q = 8 along its first column; dominant keys at 300 (+40) and 1500 (+60)
+    q[:, D] = 8.0
+    K[300, D] = 40.0 * sq / 8.0
+    K[1500, D] = 60.0 * sq / 8.0
+    # head 2: dominant key in the last, partial tile (+50)
+    q[:, 2 * D] = 8.0
+    K[S - 1, 2 * D] = 50.0 * sq / 8.0
+    q = synth.to_bf16_values(q).astype(np.float64)
+    K = synth.to_bf16_values(K).astype(np.float64)
+    kt, vt, kv = _kv_bf16(torch, K, V)
+    o = torch.empty((rows, h), dtype=torch.bfloat16, device="cuda")
+    ws = B.attention_workspace(rows, H, D) if split else None
+    print(f"[attn] rescale D={D} split={split}", flush=True)
+    B.pf_attention(dev(torch, q, torch.bfloat16), kv, S, rows, H, D, o, workspace=ws)
+    got = host(o)
+    want_p = ref.attention(q, K, V, H, D, round_p=True)
+    want = ref.attention(q, K, V, H, D)
+    assert_close(got, ref.bf16_round(want_p), f"attention rescale D={D} split={split} vs bf16p")
+    assert_close(got, want, f"attention rescale D={D} split={split} vs exact")
+    # the cases really exercise what they name: head 1 ends on key 1500, head 2 on key 2099
+    np.testing.assert_allclose(got[:, D:2 * D], np.broadcast_to(V[1500, D:2 * D], (rows, D)), atol=1e-2)
+    np.testing.assert_allclose(got[:, 2 * D:], np.broadcast_to(V[S - 1, 2 * D:], (rows, D)), atol=1e-2)
 
 
 @pytest.mark.parametrize("D,S,rows", [(64, 256, 64), (64, 100, 33), (128, 70, 5)])

@@ -392,7 +392,8 @@ def test_sampled_step_matches_full_step():
 
 
 def test_round_p_closed_forms():
-    """bf16 probabilities: exact when every exp(s - max) is a power of two; V = 1 stays within 2^-8 of 1."""
+    """bf16 probabilities: exact when every weight 2^t is a power of two; with V = 1 every output is
+    1 (the rounded weights are normalised by their own sum)."""
     H, d, S = 1, 4, 6
     q = np.zeros((1, 4))
     q[0, 0] = 2.0 * math.log(2.0)               # logits = k0 * ln2 (scale 1/2)
@@ -405,8 +406,43 @@ def test_round_p_closed_forms():
     q = rng.standard_normal((5, 8))
     k = rng.standard_normal((40, 8))
     o = ref.attention(q, k, np.ones((40, 8)), 2, 4, round_p=True)
-    assert np.abs(o - 1).max() <= 2.0 ** -8
-    assert np.abs(o - 1).max() > 0              # the rounding is really applied
+    np.testing.assert_allclose(o, 1.0, rtol=0, atol=1e-15)
+    v = rng.standard_normal((40, 8))
+    assert np.abs(ref.attention(q, k, v, 2, 4, round_p=True) - ref.attention(q, k, v, 2, 4)).max() > 1e-5
+
+
+def test_round_p_golden_two_keys():
+    rows = {r[0]: [float(v) for v in r[1:]] for r in _golden_rows("attention_bf16p_two_keys.txt")}
+    q = np.array([rows["q"]])
+    k = np.array([rows["k0"], rows["k1"]])
+    v = np.array([rows["v0"], rows["v1"]])
+    np.testing.assert_allclose(ref.attention(q, k, v, 1, 4, round_p=True)[0], rows["o"], rtol=0, atol=1e-14)
+
+
+def test_round_p_power_of_two_reference():
+    """The bf16 weights do not depend on the power-of-two reference: shifting every score of a row
+    by n ln2 (n an integer: the base-2 scores move by n) leaves the output unchanged, while a shift
+    by half of that moves the rounding points and changes it.  The shift is a fifth dimension with
+    q = a and k = b for every key: scores gain a b / sqrt(d)."""
+    rng = np.random.default_rng(23)
+    n_q, S, d = 6, 300, 5
+    q = np.zeros((n_q, d))
+    k = np.zeros((S, d))
+    q[:, :4] = rng.standard_normal((n_q, 4)) * 1.5
+    k[:, :4] = rng.standard_normal((S, 4))
+    v = rng.standard_normal((S, d))
+    base = ref.attention(q, k, v, 1, d, round_p=True)
+    for n, same in ((3.0, True), (-5.0, True), (0.5, False), (2.25, False)):
+        qs, ks = q.copy(), k.copy()
+        qs[:, 4] = 1.0
+        ks[:, 4] = n * math.log(2.0) * math.sqrt(d)
+        got = ref.attention(qs, ks, v, 1, d, round_p=True)
+        if same:
+            np.testing.assert_allclose(got, base, rtol=1e-13, atol=1e-13)
+        else:
+            assert np.abs(got - base).max() > 1e-6, n
+        np.testing.assert_allclose(ref.attention(qs, ks, v, 1, d), ref.attention(q, k, v, 1, d), rtol=1e-12,
+                                   atol=1e-12)
 
 
 # ---------------------------------------------------------------- MM-DiT block variants
@@ -584,3 +620,25 @@ def test_parallel_block_special_cases_reduce_to_the_dit_block(attn_only):
                           mlp_ratio=0 if attn_only else r, **kw)
     for warm in (True, False):
         np.testing.assert_allclose(par.step(x, c, warmup=warm), std.step(x, c, warmup=warm), rtol=1e-12, atol=1e-12)
+
+
+def test_round_p_pins_catch_planted_mistakes():
+    """Two plausible slips in the bf16-probability definition fail the pins above: rounding the
+    weights relative to the exact row maximum (a non-power-of-two reference) misses the golden
+    value, and normalising by the sum of the unrounded weights breaks the V = 1 identity."""
+    rows = {r[0]: [float(v) for v in r[1:]] for r in _golden_rows("attention_bf16p_two_keys.txt")}
+    q = np.array([rows["q"]])
+    k = np.array([rows["k0"], rows["k1"]])
+    v = np.array([rows["v0"], rows["v1"]])
+    s = q @ k.T / 2.0
+    e = np.exp(s - s.max(axis=-1, keepdims=True))
+    w = ref.bf16_round(e)
+    exact_max_ref = (w @ v) / w.sum(axis=-1, keepdims=True)
+    assert np.abs(exact_max_ref[0] - rows["o"]).max() > 1e-5
+    rng = np.random.default_rng(20)
+    q = rng.standard_normal((5, 4))
+    k = rng.standard_normal((40, 4))
+    t = (q @ k.T / 2.0) / math.log(2.0)
+    w = np.exp2(t - np.ceil(t.max(axis=-1, keepdims=True)))
+    unrounded_sum = (ref.bf16_round(w) @ np.ones((40, 4))) / w.sum(axis=-1, keepdims=True)
+    assert np.abs(unrounded_sum - 1.0).max() > 1e-6

@@ -32,12 +32,17 @@ SMALL = {
 }
 
 
-def stage_output_max_abs_tol(want_b, want_p):
-    """Max-abs gate for a stage output against the bf16-in oracle: the contract's 2e-2, or twice
-    the deviation that rounding the softmax weights to bf16 alone causes in the oracle (bf16p vs
-    bf16), whichever is larger.  Deep, wide stages amplify that rounding through later bf16
-    rounding points (rounding flips), so no bf16 flash-attention path can sit closer."""
-    return max(MAX_ABS, 2.0 * max_abs(want_p, want_b))
+def check_stage_output(got, want_p, what, want_b=None, want_e=None):
+    """A bf16 stage output against the oracle: the contract's max-abs 2e-2 and rel-L2 5e-3 against
+    the bf16-in oracle with bf16 probabilities (bf16p: the precision the kernels compute in), and
+    rel-L2 5e-3 against the exact fp64 oracle (its max-abs is reported: where wide stages have
+    adaLN gates near 2, an exact-arithmetic stage sits a bf16 rounding away from any bf16 path).
+    The bf16-in oracle without rounded probabilities is reported only."""
+    assert_close(got, want_p, f"{what} vs bf16p oracle")
+    if want_b is not None:
+        assert_close(got, want_b, f"{what} vs bf16-in oracle (reported)", max_abs_tol=None, rel_tol=None)
+    if want_e is not None:
+        assert_close(got, want_e, f"{what} vs exact oracle", max_abs_tol=None)
 
 
 def _run_chain(shape, steps, check_exact=True):
@@ -68,18 +73,11 @@ def _run_chain(shape, steps, check_exact=True):
             if bf16:
                 want_b = orc_b.step(inputs.x, inputs.c, warmup=warm)
                 want_p = orc_p.step(inputs.x, inputs.c, warmup=warm)
-                tol = stage_output_max_abs_tol(want_b, want_p)
-                assert_close(want_p, want_b, f"{shape.name} step {s} bf16p oracle vs bf16-in oracle (floor)",
-                             max_abs_tol=None, rel_tol=None)
-                assert_close(got, want_b, f"{shape.name} step {s} vs bf16-in oracle", max_abs_tol=tol)
-                if check_exact:
-                    assert_close(got, want_e, f"{shape.name} step {s} vs exact oracle", max_abs_tol=None)
+                check_stage_output(got, want_p, f"{shape.name} step {s}", want_b, want_e if check_exact else None)
                 for l in range(shape.num_layers):
                     k, v = st.kv_get(l)
-                    fk = 2.0 * max_abs(orc_p.K[l], orc_b.K[l])
-                    fv = 2.0 * max_abs(orc_p.V[l], orc_b.V[l])
-                    assert_bf16_close(k, orc_b.K[l], f"{shape.name} step {s} K[{l}]", floor=fk)
-                    assert_bf16_close(v, orc_b.V[l], f"{shape.name} step {s} V[{l}]", floor=fv)
+                    assert_bf16_close(k, orc_p.K[l], f"{shape.name} step {s} K[{l}]")
+                    assert_bf16_close(v, orc_p.V[l], f"{shape.name} step {s} V[{l}]")
             else:
                 assert_close(got, want_e, f"{shape.name} step {s} vs exact oracle", max_abs_tol=1e-3, rel_tol=1e-5)
                 for l in range(shape.num_layers):
@@ -106,8 +104,7 @@ def _run_pair_chain(shape, steps):
     inputs = synth.stage_inputs(shape)
     conds = list(synth.batch_conds(shape, inputs.c, 2))
     bf16 = shape.dtype == "bf16"
-    orc_b = [_oracle(shape, inputs, "bf16" if bf16 else "exact") for _ in range(2)]
-    orc_p = [_oracle(shape, inputs, "bf16p") for _ in range(2)] if bf16 else None
+    orc_b = [_oracle(shape, inputs, "bf16p" if bf16 else "exact") for _ in range(2)]
     S, h, L = shape.seq_kv, shape.hidden, shape.num_layers
     with Stage(shape, batch=2) as st:
         st.load(inputs.layers)
@@ -123,24 +120,17 @@ def _run_pair_chain(shape, steps):
                               synth.randn((S, h), seed + 2 * l + 1, std=shape.sigma_kv)) for l in range(L)]
                     st.add_noise(noise, sample=b)
                     orc_b[b].add_noise(noise)
-                    if bf16:
-                        orc_p[b].add_noise(noise)
             print(f"[stage pair] {shape.name} step {s} warmup={warm}", flush=True)
             st.run_step(x, c, warmup=warm, out=out)
             got = host(out)
             for b in range(2):
                 want = orc_b[b].step(inputs.x, conds[b], warmup=warm)
                 if bf16:
-                    want_p = orc_p[b].step(inputs.x, conds[b], warmup=warm)
-                    tol = stage_output_max_abs_tol(want, want_p)
-                    assert_close(got[b], want, f"{shape.name} pair step {s} sample {b} vs bf16-in oracle",
-                                 max_abs_tol=tol)
+                    check_stage_output(got[b], want, f"{shape.name} pair step {s} sample {b}")
                     for l in range(L):
                         k, v = st.kv_get(l, sample=b)
-                        assert_bf16_close(k, orc_b[b].K[l], f"pair step {s} sample {b} K[{l}]",
-                                          floor=2.0 * max_abs(orc_p[b].K[l], orc_b[b].K[l]))
-                        assert_bf16_close(v, orc_b[b].V[l], f"pair step {s} sample {b} V[{l}]",
-                                          floor=2.0 * max_abs(orc_p[b].V[l], orc_b[b].V[l]))
+                        assert_bf16_close(k, orc_b[b].K[l], f"pair step {s} sample {b} K[{l}]")
+                        assert_bf16_close(v, orc_b[b].V[l], f"pair step {s} sample {b} V[{l}]")
                 else:
                     assert_close(got[b], want, f"{shape.name} pair step {s} sample {b} vs exact oracle",
                                  max_abs_tol=1e-3, rel_tol=1e-5)
@@ -165,7 +155,9 @@ def test_cfg_pair_patch_matches_single_stages(name):
     """stage_run_patch on a pair equals the same micro-step on two single-sample stages, each
     with that sample's condition and buffer contents (up to the fp32 summation order of
     projections that see twice the rows, and of the key-range split: at full size the pair's
-    batched attention splits the keys in fewer slices than a single sample's)."""
+    batched attention splits the keys in fewer slices than a single sample's).  The attention's
+    bf16 probabilities do not depend on the split (power-of-two references), so only fp32
+    summation order differs."""
     torch = torch_cuda()
     shape = {"c2s": SMALL["c2s"], "c2-full-L1": dataclasses.replace(C2, num_layers=1),
              "c4-full-L1": dataclasses.replace(C4, num_layers=1)}[name]
@@ -188,9 +180,9 @@ def test_cfg_pair_patch_matches_single_stages(name):
         for b, st in enumerate(singles):
             st.set_cond(dev(torch, conds[b]))
             want = host(st.run_patch(off, P, dev(torch, x_patch)))
-            # rel-L2 is the contract tolerance; max-abs only bounds gross errors, because at
-            # h = 3072 the large adaLN gates turn one-ulp bf16 flips into ~0.1 single-element moves
-            assert_close(got[b], want, f"pair patch sample {b} vs single stage", max_abs_tol=0.25)
+            # the same arithmetic up to fp32 summation order (projections over twice the rows,
+            # a different key split): the contract's tolerances
+            assert_close(got[b], want, f"pair patch sample {b} vs single stage")
             for l in range(shape.num_layers):
                 kp, vp = pair.kv_get(l, sample=b)
                 ks, vs = st.kv_get(l)
@@ -222,10 +214,9 @@ def test_property_a_no_drift_full_size(shape):
     layer's K/V buffers see the same inputs; they agree to within one bf16 ulp per element
     (plus a tiny absolute floor for sums that cancel), since a patch-sized QKV projection may
     split its k range across workgroups (fp32 partial sums added in another order) while the
-    warm-up pass does not.  The outputs agree up to
-    fp32 summation order too: a patch's attention also splits the key range and merges the
-    partials, and later bf16 rounding points turn last-bit differences into occasional
-    one-ulp flips."""
+    warm-up pass does not.  The outputs agree up to fp32 summation order too (a patch's attention
+    also splits the key range and merges fp32 partials; its bf16 probabilities do not depend on
+    the split), within the contract's tolerances."""
     torch = torch_cuda()
     shape = dataclasses.replace(shape, num_layers=min(shape.num_layers, 2))
     inputs = synth.stage_inputs(shape)
@@ -251,23 +242,29 @@ def test_property_a_no_drift_full_size(shape):
                                          f"max |diff| {float(d.max()):.3g} at |value| "
                                          f"{float(a.flatten()[int(d.argmax())].abs()):.3g}")
         assert bool(torch.isfinite(out).all())
-        # rel-L2 is the contract tolerance; max-abs only bounds gross errors here, because at
-        # h = 3072 the large adaLN gates turn one-ulp bf16 flips into ~0.1 single-element moves
-        assert_close(host(out), host(warm), f"{shape.name} patched vs warm-up (no drift)", max_abs_tol=0.25)
+        # the contract's tolerances: the two passes differ only in fp32 summation order (a
+        # patch's projections and attention may split k or the key range; the warm-up's do not)
+        assert_close(host(out), host(warm), f"{shape.name} patched vs warm-up (no drift)")
 
 
-@pytest.mark.parametrize("shape", [C2, C3, C4], ids=lambda s: s.name)
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("shape", [C2, C3, C4, C5], ids=lambda s: s.name)
 def test_full_size_one_layer_sampled_parity(shape):
-    """Full sequence length and width, one layer: warm-up and one drifted patched step,
-    checked against the oracle on sampled rows of every patch."""
+    """Full sequence length and width, one layer, in the benchmark's launch configuration: the
+    warm-up step (one micro-step over every buffer row: projections of S_kv rows and the
+    unsplit attention) and one drifted patched step (every patch in turn), checked against the
+    bf16p oracle on sampled rows of every patch (first and last rows, patch starts, random rows)
+    and on the whole K/V buffer.  The oracle runs every projection and splice in full and
+    attention only for the sampled rows."""
     torch = torch_cuda()
     shape = dataclasses.replace(shape, num_layers=1, name=shape.name + "-L1")
     inputs = synth.stage_inputs(shape)
-    orc = _oracle(shape, inputs, "bf16")
-    orc_p = _oracle(shape, inputs, "bf16p")
+    orc = _oracle(shape, inputs, "bf16p")
     rng = np.random.default_rng(11)
-    rows = np.unique(np.concatenate([rng.choice(shape.seq_kv, 96, replace=False),
-                                     [0, shape.seq_kv - 1] + list(shape.patch_offsets())]))
+    n_rand = 96 if shape.seq_kv <= 20000 else 64
+    rows = np.unique(np.concatenate([rng.choice(shape.seq_kv, n_rand, replace=False),
+                                     [0, shape.seq_kv - 1] + list(shape.patch_offsets()) +
+                                     [o + shape.patch_rows - 1 for o in shape.patch_offsets()]]))
     with Stage(shape) as st:
         st.load(inputs.layers)
         x, c = dev(torch, inputs.x), dev(torch, inputs.c)
@@ -277,47 +274,41 @@ def test_full_size_one_layer_sampled_parity(shape):
                 noise = inputs.next_noise()
                 st.add_noise(noise)
                 orc.add_noise(noise)
-                orc_p.add_noise(noise)
-            print(f"[stage] {shape.name} sampled step {s}", flush=True)
+                del noise
+            print(f"[stage] {shape.name} sampled step {s}: GPU", flush=True)
             st.run_step(x, c, warmup=(s == 0), out=out)
-            got = host(out)[rows]
+            got = host(out[torch.from_numpy(rows).cuda()])
+            print(f"[stage] {shape.name} sampled step {s}: oracle", flush=True)
             want = orc.step_sampled(inputs.x, inputs.c, rows, warmup=(s == 0))
-            want_p = orc_p.step_sampled(inputs.x, inputs.c, rows, warmup=(s == 0))
-            assert_close(want_p, want, f"{shape.name} step {s} bf16p vs bf16-in oracle (floor)", max_abs_tol=None,
-                         rel_tol=None)
-            assert_close(got, want, f"{shape.name} step {s} sampled rows vs bf16-in oracle",
-                         max_abs_tol=stage_output_max_abs_tol(want, want_p))
+            check_stage_output(got, want, f"{shape.name} step {s} sampled rows")
+            print(f"[stage] {shape.name} sampled step {s}: K/V buffers", flush=True)
             k, v = st.kv_get(0)
             assert_bf16_close(k, orc.K[0], f"{shape.name} step {s} K buffer")
             assert_bf16_close(v, orc.V[0], f"{shape.name} step {s} V buffer")
+            del k, v
 
 
 def test_property_b_micro_steps_touch_only_their_rows():
     torch = torch_cuda()
     shape = SMALL["c4s"]
     inputs = synth.stage_inputs(shape)
-    orc = _oracle(shape, inputs, "bf16")
-    orc_p = _oracle(shape, inputs, "bf16p")
+    orc = _oracle(shape, inputs, "bf16p")
     with Stage(shape) as st:
         st.load(inputs.layers)
         x, c = dev(torch, inputs.x), dev(torch, inputs.c)
         st.run_step(x, c, warmup=True, out=torch.empty_like(x))
         orc.step(inputs.x, inputs.c, warmup=True)
-        orc_p.step(inputs.x, inputs.c, warmup=True)
         noise = inputs.next_noise()
         st.add_noise(noise)
         orc.add_noise(noise)
-        orc_p.add_noise(noise)
         st.set_cond(c)
         orc.set_cond(inputs.c)
-        orc_p.set_cond(inputs.c)
         xo = x.clone()
         h = shape.hidden
         for off, n in orc.micro_steps(False):
             before = [st.kv_get(l) for l in range(shape.num_layers)]
             st.run_patch(off, n, x[off:off + n], xo[off:off + n])
             orc.run_rows(off, n, inputs.x[off:off + n])
-            orc_p.run_rows(off, n, inputs.x[off:off + n])
             rs = slice(off, off + n)
             for l in range(shape.num_layers):
                 k, v = st.kv_get(l)
@@ -325,10 +316,8 @@ def test_property_b_micro_steps_touch_only_their_rows():
                 outside[rs] = False
                 np.testing.assert_array_equal(k[outside], before[l][0][outside])
                 np.testing.assert_array_equal(v[outside], before[l][1][outside])
-                fk = 2.0 * max_abs(orc_p.K[l][rs], orc.K[l][rs])
-                fv = 2.0 * max_abs(orc_p.V[l][rs], orc.V[l][rs])
-                assert_bf16_close(k[rs], orc.K[l][rs], f"fresh K rows [{off},{off + n}) layer {l}", floor=fk)
-                assert_bf16_close(v[rs], orc.V[l][rs], f"fresh V rows [{off},{off + n}) layer {l}", floor=fv)
+                assert_bf16_close(k[rs], orc.K[l][rs], f"fresh K rows [{off},{off + n}) layer {l}")
+                assert_bf16_close(v[rs], orc.V[l][rs], f"fresh V rows [{off},{off + n}) layer {l}")
         assert h == shape.hidden
 
 

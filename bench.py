@@ -1,14 +1,15 @@
 """Benchmark: one GPU's pipeline stage of patch-level (PipeFusion-style) DiT inference.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c2] [--breakdown] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c5] [--breakdown] [--no-cpu-baseline]
 
 A step is one patched diffusion step of the stage: every layer for every patch
 (QKV projection, in-place KV splice, attention of the patch over the full
 buffer, output projection, modulated MLP) over synthetic inputs already resident
 in HBM.  Prints one JSON line.  `value` is stage tokens/s (buffer rows per step
 divided by the median step time).  `roofline` describes the dominant kernel (the
-patch attention), timed with HIP events at the stage's launch shape.
-`cpu_baseline` times the fp64 oracle on a bounded sample of the same workload.
+patch attention): its launches inside the timed steps, each bracketed by HIP events on
+the stage's stream.  `cpu_baseline` times the fp64 oracle on a bounded sample of the same
+workload (one patch through one layer, extrapolated).
 """
 from __future__ import annotations
 
@@ -33,7 +34,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--config", default="c2")
+    ap.add_argument("--config", default="c5", help="c1..c5 (default c5: the long-sequence PixArt-shaped stage, "
+                                                   "262144 buffer rows, the largest single-GPU workload)")
     ap.add_argument("--batch", type=int, default=1,
                     help="samples per stage sharing the weights (2 = a classifier-free guidance pair)")
     ap.add_argument("--denoiser", type=int, default=0, metavar="STEPS",
@@ -44,7 +46,7 @@ def parse():
                          "block (parallel attention + MLP, QK-RMSNorm, RoPE)")
     ap.add_argument("--breakdown", action="store_true", help="also time every kernel of a patch-layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--probe", choices=PROBES,
                     help="only launch one kernel of a patch-layer at the stage's launch shape (or a plain 1 GiB "
                          "copy) --probe-iters times; a target for rocprofv3 counter runs")
@@ -54,10 +56,10 @@ def parse():
     return ap.parse_args()
 
 
-# Calibrated HBM traffic of the dominant kernel, recorded by a counter run (see the file for
-# its commands).  It describes the kernel sources whose hash it names; once they change, the
-# recorded traffic no longer applies and bench.py reports null.
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_c2_traffic.md")
+# Calibrated HBM traffic of the dominant kernel at a config's launch shape, recorded by a counter
+# run (see the file for its commands).  It describes the kernel sources whose hash it names;
+# once they change, the recorded traffic no longer applies and bench.py reports null.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_{config}_traffic.md")
 ATTENTION_SOURCES = ("patch_pipelined_attention_amd/csrc/attention.hip", "patch_pipelined_attention_amd/csrc/pf_internal.h")
 
 
@@ -75,7 +77,7 @@ def recorded_traffic(config: str):
     kernel sources, else None."""
     try:
         fields = {}
-        with open(TRAFFIC_FILE) as f:
+        with open(TRAFFIC_FILE.format(config=config)) as f:
             for line in f:
                 if line.startswith("- ") and ": " in line:
                     k, v = line[2:].split(": ", 1)
@@ -249,8 +251,12 @@ def time_denoiser(torch, B, synth, st, shape, nb, steps):
 
 
 def cpu_baseline(shape, inputs, budget_s, mm=None):
-    """Oracle (fp64 numpy) on a bounded sample: whole patches through all layers with a full
-    buffer, repeated until `budget_s` of CPU time; scaled to a step's rows."""
+    """The oracle (fp64 numpy, exact mode) on a bounded sample of the workload: one patch (the
+    last) through one layer over a full, filled S_kv-row buffer.  The patch's LayerNorm, QKV
+    projection and splice run for all its rows; attention and the MLP for an evenly spaced
+    sample of its query rows.  Two sample sizes give the fixed and the per-row cost, which are
+    extrapolated to the whole patch, then to a step (M patches and the text prefix, times L
+    layers).  tokens/s = S_kv rows / extrapolated step time."""
     import numpy as np
     from oracle import ref
     try:
@@ -258,32 +264,41 @@ def cpu_baseline(shape, inputs, budget_s, mm=None):
         threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     except Exception:
         threads = os.cpu_count() or 1
-    opts = {} if mm is None else dict(txt_layers=mm.txt_layers or None, qk_norm=True, rope_angles=mm.angles,
+    opts = {} if mm is None else dict(txt_layers=mm.txt_layers[:1] or None, qk_norm=True, rope_angles=mm.angles,
                                       parallel=not mm.txt_layers)
-    orc = ref.StageOracle(inputs.layers if mm is None else mm.layers, heads=shape.heads, head_dim=shape.head_dim,
-                          seq_txt=shape.seq_txt, seq_img=shape.seq_img, num_patches=shape.num_patches,
-                          mlp_ratio=shape.mlp_ratio, mode="exact", **opts)
+    layers = (inputs.layers if mm is None else mm.layers)[:1]
+    orc = ref.StageOracle(layers, heads=shape.heads, head_dim=shape.head_dim, seq_txt=shape.seq_txt,
+                          seq_img=shape.seq_img, num_patches=shape.num_patches, mlp_ratio=shape.mlp_ratio,
+                          mode="exact", **opts)
     rng = np.random.default_rng(0)
-    for l in range(shape.num_layers):           # a filled buffer (values do not change the work)
-        orc.K[l][:] = rng.standard_normal(orc.K[l].shape)
-        orc.V[l][:] = rng.standard_normal(orc.V[l].shape)
+    orc.K[0][:] = rng.standard_normal(orc.K[0].shape)     # a filled buffer (values do not change the work)
+    orc.V[0][:] = rng.standard_normal(orc.V[0].shape)
     orc.set_cond(inputs.c)
     P = shape.patch_rows
-    offs = shape.patch_offsets()
-    done_rows, t0 = 0, time.perf_counter()
-    i = 0
-    while True:
-        off = offs[i % len(offs)]
-        orc.run_rows(off, P, inputs.x[off:off + P])
-        done_rows += P
-        i += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or i >= 4 * len(offs):
-            break
-    rate = done_rows / el
-    return {"value": rate, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{i} patch(es) of {P} rows through all {shape.num_layers} layers over a full "
-                      f"{shape.seq_kv}-row buffer (fp64 numpy, exact mode), {el:.1f} s; tokens/s = rows / time",
+    off = shape.patch_offsets()[-1]
+    x = inputs.x[off:off + P]
+
+    def run(n):
+        sample = np.unique(np.linspace(0, P - 1, n).round().astype(np.int64))
+        t0 = time.perf_counter()
+        orc.run_rows(off, P, x, sample=sample)
+        return len(sample), time.perf_counter() - t0
+
+    n1, t1 = run(min(P, 32))
+    per_row = t1 / n1                                 # an upper bound: t1 includes the fixed cost
+    n2, t2 = run(min(P, max(4 * n1, int(0.6 * budget_s / per_row))))
+    if n2 >= P:
+        patch_s, how = t2, "measured"
+    else:
+        slope = max((t2 - t1) / (n2 - n1), 0.0)
+        patch_s, how = max(t1 - slope * n1, 0.0) + slope * P, "extrapolated"
+    step_s = shape.num_layers * patch_s * shape.seq_kv / P
+    return {"value": shape.seq_kv / step_s, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"one patch of {P} rows through one layer over a filled {shape.seq_kv}-row buffer (fp64 numpy, "
+                      f"exact mode): projections for all rows, attention + MLP for {n1} and {n2} sampled query rows "
+                      f"({t1:.1f} s, {t2:.1f} s); patch-layer time {how} to {P} rows = {patch_s:.1f} s, then x "
+                      f"{shape.seq_kv // P} patch-sized micro-steps x {shape.num_layers} layers (extrapolated); "
+                      f"tokens/s = {shape.seq_kv} rows / step time",
             "host_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0))}
 
 
@@ -397,6 +412,9 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] timing {args.steps} patched steps", file=sys.stderr, flush=True)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    # every attention launch of the timed steps is bracketed by HIP events on the stage's stream
+    per_step = shape.num_layers * (shape.num_patches + (1 if shape.seq_txt > 0 else 0))
+    B.stage_profile_begin(st.handle, args.steps * per_step)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s, e in evs:
@@ -405,9 +423,11 @@ def main():
         e.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    n_attn, attn_ms = B.stage_profile_end(st.handle)
     step_s = [s.elapsed_time(e) / 1e3 for s, e in evs]
     med = statistics.median(step_s)
     assert bool(torch.isfinite(out).all()), "non-finite stage output"
+    assert n_attn == args.steps * per_step, (n_attn, args.steps * per_step)
 
     # warm-up (M = 1) step time, same FLOPs: patching overhead on one GPU
     ws, we = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -421,8 +441,10 @@ def main():
     wdev = {k: torch.from_numpy(np.ascontiguousarray(a)).cuda().to(torch.bfloat16 if k.startswith("w") else torch.float32)
             for k, a in (inputs.layers if mm is None else mm.layers)[0].items()}
     probes = kernel_probes(torch, B, st, shape, wdev, nb, mm, parallel)
-    attn_fn, attn_flop, _ = probes["attention"]
-    attn_s = time_kernel(torch, attn_fn, iters=max(10, args.steps))
+    # a patched step's attention work, 4 S_kv^2 h per layer and sample, over its launches (one per
+    # layer and micro-step, all samples in one launch): 4 P S_kv h per launch without a text prefix
+    attn_flop = 4.0 * nb * shape.seq_kv * shape.seq_kv * shape.hidden * shape.num_layers / per_step
+    attn_s = attn_ms / 1e3 / n_attn
     attn_tflops = attn_flop / attn_s / 1e12
     breakdown = None
     if args.breakdown:
@@ -482,10 +504,12 @@ def main():
         "roofline": {"kernel": "attn_bf16_kernel", "bound": "mfma", "achieved": attn_tflops,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": attn_tflops / PEAK_BF16_TFLOPS,
                      "traffic": recorded_traffic(args.config), "avg_launch_us": attn_s * 1e6,
-                     "launch": "one pf_attention call: attn_bf16_kernel plus, when the key range is split, "
-                               "attn_combine_kernel; the duration covers both",
-                     "work": f"4*P*S_kv*h = {attn_flop:.4g} FLOP per launch (P={shape.patch_rows}, "
-                             f"S_kv={shape.seq_kv}, h={shape.hidden})"},
+                     "launches": n_attn,
+                     "launch": "the stage's attention launches inside the timed patched steps (one per layer and "
+                               "micro-step), each bracketed by HIP events on the stage's stream: attn_bf16_kernel "
+                               "plus, when the key range is split, attn_combine_kernel; the duration covers both",
+                     "work": f"4*rows*S_kv*h FLOP per launch = {attn_flop:.4g} (P={shape.patch_rows} query rows per "
+                             f"patch, S_kv={shape.seq_kv}, h={shape.hidden}, d={shape.head_dim} counted unpadded)"},
     }
     if breakdown:
         rec["breakdown"] = breakdown

@@ -243,6 +243,19 @@ pf_status stage_get_kvbuf_sample(pf_stage* st, int32_t layer, int32_t sample, pf
  * (a query a user of a stage object needs).  Errors: INVALID_ARG (NULL argument). */
 pf_status stage_get_config(const pf_stage* st, pf_stage_config* out);
 
+/* Live timing of the stage's patch attention (instrumentation for benchmarks).
+ * stage_profile_begin allocates 2 * max_launches HIP events (1 <= max_launches <= 2^20; it
+ * replaces any earlier profile); from then on every attention launch of a run call (one per
+ * layer, stream part and micro-step) is bracketed by a pair of events recorded on the run
+ * call's stream, until the pairs run out.  stage_profile_end waits for the recorded events
+ * (it synchronises the host with them), writes the number of timed launches and their summed
+ * device duration in milliseconds, frees the events and stops the timing.  Source: the
+ * pages' cost statement (attention grows quadratically with sequence length: "Problem
+ * statement" of the PipeFusion summaries), which makes the attention launch the one to time.
+ * Errors: INVALID_ARG, STATE (end without begin), OOM / HIP (event creation or reading). */
+pf_status stage_profile_begin(pf_stage* st, int32_t max_launches);
+pf_status stage_profile_end(pf_stage* st, int64_t* launches, double* attention_ms);
+
 /* ---------------------------------------------------------------------------------
  * The denoising loop around one stage (one GPU holding every layer).  The pages put the
  * stage inside a diffusion loop (PipeFusion "Core mechanisms" 2: consecutive steps see

@@ -82,6 +82,8 @@ _SIGNATURES = {
     "stage_get_kvbuf": [_P, _I32, ctypes.POINTER(KVView)],
     "stage_get_kvbuf_sample": [_P, _I32, _I32, ctypes.POINTER(KVView)],
     "stage_get_config": [_P, ctypes.POINTER(StageConfig)],
+    "stage_profile_begin": [_P, _I32],
+    "stage_profile_end": [_P, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double)],
     "denoiser_create": [_P, ctypes.POINTER(DenoiserConfig), ctypes.POINTER(_P)],
     "denoiser_destroy": [_P],
     "denoiser_load_weights": [_P, ctypes.POINTER(DenoiserWeights), _P],
@@ -302,6 +304,17 @@ def kv_view(k, v, rows: int, row_elems: int, v_layout: int, k_ld=None, v_ld=None
     return KVView(k=_ptr(k), v=_ptr(v), rows=rows, row_elems=row_elems,
                   k_ld=row_elems if k_ld is None else k_ld, v_ld=row_elems if v_ld is None else v_ld,
                   dtype=_dtype_code(k), v_layout=v_layout)
+
+
+def stage_profile_begin(handle, max_launches: int) -> None:
+    _check(lib().stage_profile_begin(handle, max_launches))
+
+
+def stage_profile_end(handle):
+    """(timed attention launches, their summed duration in ms) since stage_profile_begin."""
+    n, ms = ctypes.c_int64(), ctypes.c_double()
+    _check(lib().stage_profile_end(handle, ctypes.byref(n), ctypes.byref(ms)))
+    return n.value, ms.value
 
 
 def stage_get_config(handle) -> StageConfig:

@@ -25,11 +25,13 @@
 //   * softmax in base 2: p = exp2(s * log2(e)/sqrt(D) - m), fp32 statistics, P rounded to
 //     bf16 for the P.V product and the row sum taken over the same rounded values (for
 //     D = 72 by the P.V MFMA itself, through a ones row in the padding of O^T).  The
-//     reference m is an integer, raised (and O, l rescaled) only when a tile's max exceeds
-//     it by more than 8, so p <= 2^8 and the rescale is rare.  Because m is an integer, every
-//     rescale multiplies by an exact power of two, and the rounded weights are those of
-//     bf16(2^(s log2(e)/sqrt(D))) scaled by 2^-m: the same values whatever the order of the
-//     key tiles, the split of the key range or the running max at the time a tile is seen.
+//     reference m is an integer, raised (and O, l rescaled) only when a tile holds a score
+//     more than 64 above it, so p < 2^64, far from fp32 overflow, and the rescale is rare;
+//     the common path takes no row max (a lane-local sum or max test instead).  Because m is
+//     an integer, every rescale multiplies by an exact power of two, and the rounded weights
+//     are those of bf16(2^(s log2(e)/sqrt(D))) scaled by 2^-m: the same values whatever the
+//     order of the key tiles, the split of the key range or the running max at the time a
+//     tile is seen.
 //   * D = 72 pads the score contraction to 80 and the output rows to 96 with zero
 //     operands; nothing outside the real 72 columns is read or written.
 //   * when there are too few (query tile, head) pairs to fill the GPU, the key range is
@@ -222,6 +224,22 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const bf16* __restric
       }
     }
   };
+  auto issue_tile_full = [&](int64_t t, int st) {
+    const char* kbase = reinterpret_cast<const char*>(Kb + (t * TK) * ldk + col0);
+    const char* vbase = reinterpret_cast<const char*>(Vb + (t * (TK / 8) * hidden + col0) * 8);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int i = wl + 4 * j;
+      if (i >= NINST) continue;                   // wavefront-uniform
+      const bool kpart = i < NI;
+      dma_load16(kpart ? kbase : vbase, ld_off[j], &lds[st][(kpart ? i : KUP / 64 + i - NI) * 64]);
+    }
+  };
+  // NSTAGE - 3 newer tiles in flight (the steady state)
+  auto wait_loads_const = [&] {
+    constexpr int n = (NSTAGE - 3) * NMIN;
+    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+  };
   auto wait_loads = [&](int newer_tiles) {
     if (newer_tiles >= 3) __builtin_amdgcn_s_waitcnt(((3 * NMIN) & 15) | (((3 * NMIN) >> 4) << 14) | (7 << 4) | (15 << 8));
     else if (newer_tiles == 2) __builtin_amdgcn_s_waitcnt(((2 * NMIN) & 15) | (((2 * NMIN) >> 4) << 14) | (7 << 4) | (15 << 8));
@@ -315,33 +333,70 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const bf16* __restric
           o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[h2][db], pb[qb][h2], o[qb][db], 0, 0, 0);
   };
   const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
-  // tile max (3-input maximum tree; the two 32-lane halves hold the same queries' other keys),
-  // lazy rescale, p = 2^(s*c - m) packed to bf16
-  auto softmax = [&](f32x16 (&sc)[QB], bf16x8 (&pc)[QB][2]) {
-    float mt[QB];
-    bool raise = false;
+  // p = 2^(s c - m) packed to bf16 for every score of the tile; the reference m of a query is an
+  // integer, raised only when the tile holds a score more than kRaise above it (so p < 2^kRaise
+  // and sums stay far from fp32 overflow).  Common path without a row max: for D = 64 / 128 the
+  // lane's partial sum of the tile's rounded weights (needed for l anyway) exceeds 2^kRaise
+  // whenever a weight does (the first tile, where m = -inf, gives inf); for D = 72 (the row sum
+  // comes from the P.V MFMA) a lane-local maximum of the raw scores is compared with the
+  // threshold.  Only then (rare after the first tile) does the wave take the row max across
+  // both halves of the query's keys, raise m to its ceiling and rescale O and l by the exact
+  // power of two 2^(m_old - m_new), and recompute the tile's weights.
+  constexpr float kRaise = 64.0f;
+  auto exp_pack = [&](f32x16 (&sc)[QB], bf16x8 (&pc)[QB][2], float (&lt)[QB]) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      auto mx3 = [](float a, float b, float c) {
-        return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
-      };
-      const float m0 = mx3(sc[qb][0], sc[qb][1], sc[qb][2]);
-      const float m1 = mx3(sc[qb][3], sc[qb][4], sc[qb][5]);
-      const float m2 = mx3(sc[qb][6], sc[qb][7], sc[qb][8]);
-      const float m3 = mx3(sc[qb][9], sc[qb][10], sc[qb][11]);
-      const float m4 = mx3(sc[qb][12], sc[qb][13], sc[qb][14]);
-      const float m5 = mx3(m0, m1, sc[qb][15]);
-      const float mh = mx3(m2, m3, mx3(m4, m5, m5));
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mh), __float_as_uint(mh), false, false);
-      const float mx = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-      mt[qb] = mx * scale_log2;
-      raise |= mt[qb] > m_ref[qb] + 8.0f;
+      uint32_t pk[8];
+      lt[qb] = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const f32x2 pp = {__builtin_amdgcn_exp2f(fmaf(sc[qb][2 * e], scale_log2, -m_ref[qb])),
+                          __builtin_amdgcn_exp2f(fmaf(sc[qb][2 * e + 1], scale_log2, -m_ref[qb]))};
+        const bf16x2 pb2 = __builtin_convertvector(pp, bf16x2);
+        if constexpr (!kSumRow) lt[qb] = __builtin_amdgcn_fdot2_f32_bf16(pb2, ones, lt[qb], false);
+        pk[e] = __builtin_bit_cast(uint32_t, pb2);
+      }
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const u32x4 w = {pk[4 * h2], pk[4 * h2 + 1], pk[4 * h2 + 2], pk[4 * h2 + 3]};
+        pc[qb][h2] = __builtin_bit_cast(bf16x8, w);
+      }
+    }
+  };
+  auto mx3 = [](float a, float b, float c) {
+    return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+  };
+  auto lane_max = [&](const f32x16& v) {
+    const float m0 = mx3(v[0], v[1], v[2]);
+    const float m1 = mx3(v[3], v[4], v[5]);
+    const float m2 = mx3(v[6], v[7], v[8]);
+    const float m3 = mx3(v[9], v[10], v[11]);
+    const float m4 = mx3(v[12], v[13], v[14]);
+    const float m5 = mx3(m0, m1, v[15]);
+    return mx3(m2, m3, mx3(m4, m5, m5));
+  };
+  auto softmax = [&](f32x16 (&sc)[QB], bf16x8 (&pc)[QB][2]) {
+    float lt[QB];
+    bool raise = false;
+    if constexpr (kSumRow) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) raise |= lane_max(sc[qb]) * scale_log2 > m_ref[qb] + kRaise;
+    }
+    if (!kSumRow || !__any(raise)) {
+      exp_pack(sc, pc, lt);
+      if constexpr (!kSumRow) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) raise |= !(lt[qb] <= 0x1p64f);   // also true for inf / nan
+      }
     }
     if (__any(raise)) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        // integer reference: alpha is an exact power of two
-        const float m_new = fmaxf(m_ref[qb], __builtin_ceilf(mt[qb]));
+        const float mh = lane_max(sc[qb]);
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mh), __float_as_uint(mh), false, false);
+        const float mt = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale_log2;
+        // integer reference: alpha is an exact power of two (0 on the first tile)
+        const float m_new = fmaxf(m_ref[qb], __builtin_ceilf(mt));
         const float alpha = __builtin_amdgcn_exp2f(m_ref[qb] - m_new);
         m_ref[qb] = m_new;
         l_run[qb] *= alpha;
@@ -350,23 +405,11 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const bf16* __restric
 #pragma unroll
           for (int e = 0; e < 16; ++e) o[qb][db][e] *= alpha;
       }
+      exp_pack(sc, pc, lt);
     }
+    if constexpr (!kSumRow) {
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      uint32_t pk[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const f32x2 pp = {__builtin_amdgcn_exp2f(fmaf(sc[qb][2 * e], scale_log2, -m_ref[qb])),
-                          __builtin_amdgcn_exp2f(fmaf(sc[qb][2 * e + 1], scale_log2, -m_ref[qb]))};
-        const bf16x2 pb2 = __builtin_convertvector(pp, bf16x2);
-        if constexpr (!kSumRow) l_run[qb] = __builtin_amdgcn_fdot2_f32_bf16(pb2, ones, l_run[qb], false);
-        pk[e] = __builtin_bit_cast(uint32_t, pb2);
-      }
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        const u32x4 w = {pk[4 * h2], pk[4 * h2 + 1], pk[4 * h2 + 2], pk[4 * h2 + 3]};
-        pc[qb][h2] = __builtin_bit_cast(bf16x8, w);
-      }
+      for (int qb = 0; qb < QB; ++qb) l_run[qb] += lt[qb];
     }
   };
 
@@ -419,8 +462,35 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const bf16* __restric
     st = st + 1 == NSTAGE ? 0 : st + 1;
     st_issue = st_issue + 1 == NSTAGE ? 0 : st_issue + 1;
   };
+  // steady state: the tile NSTAGE - 2 ahead exists and is full, so every wait is the same.  For
+  // D = 72 and 128 the wavefront in its MFMA phase runs at a raised priority, so the SIMD's
+  // arbiter issues its MFMAs as soon as the matrix core frees up and fills the gaps with the
+  // other wavefront's softmax (measured: +5% at 262144 keys, d = 72; at d = 64, where the
+  // softmax phase is the longer one, it costs 3%)
+  constexpr bool kPingPongPrio = D != 64;
+  auto iter_steady = [&](int64_t t) {
+    bf16x8 kf[KS];
+    if constexpr (kPingPongPrio) __builtin_amdgcn_s_setprio(1);
+    read_k(st, kf);
+    f32x16 sc[QB];
+    pv(vf, pb);
+    if (grp == 0) issue_tile_full(t + NSTAGE - 2, st_issue);
+    scores(kf, sc);
+    barrier();
+    if constexpr (kPingPongPrio) __builtin_amdgcn_s_setprio(0);
+    softmax(sc, pb);
+    read_v(t, st, vf, false);
+    if (grp == 0) wait_loads_const();
+    barrier();
+    st = st + 1 == NSTAGE ? 0 : st + 1;
+    st_issue = st_issue + 1 == NSTAGE ? 0 : st_issue + 1;
+  };
   const int64_t t_full = t_end * TK > S ? t_end - 1 : t_end;
-  for (int64_t t = t_begin; t < t_full; ++t) iter(t, false);
+  // the last full tile t can run steady if t + NSTAGE - 2 is a full tile below t_end
+  const int64_t t_steady_end = t_full - (NSTAGE - 2) > t_begin ? t_full - (NSTAGE - 2) : t_begin;
+  int64_t t = t_begin;
+  for (; t < t_steady_end; ++t) iter_steady(t);
+  for (; t < t_full; ++t) iter(t, false);
   if (t_full < t_end) iter(t_full, true);
   if (nt > 0) pv(vf, pb);
   if (grp == 0) barrier();
@@ -677,6 +747,28 @@ static hipError_t launch_attn_d(const void* q, int64_t ldq, const void* k, int64
                          static_cast<float*>(o) + b * rows * ldo, ldo, 1.0f / sqrtf((float)D));
   }
   return hipGetLastError();
+}
+
+template <int D>
+static size_t split_bytes_d(int64_t rows, int64_t seq_kv, int64_t hidden, int heads, int64_t batch) {
+  constexpr int BQ = kAttnWaves * 32 * AttnCfg<D>::QB;
+  const int64_t n_qtiles = batch * ((rows + BQ - 1) / BQ);
+  const int64_t ntiles = (seq_kv + kTileKeys - 1) / kTileKeys;
+  const int n_split = choose_split(n_qtiles * heads, attn_slots<D>(), ntiles, batch * rows, hidden, heads, (size_t)-1);
+  const int tps = (int)((ntiles + n_split - 1) / n_split);
+  const int n_used = (int)((ntiles + tps - 1) / tps);
+  return attention_workspace_bytes(batch * rows, hidden, heads, n_used);
+}
+
+size_t attention_split_workspace_bytes(int64_t rows, int64_t seq_kv, int64_t hidden, int heads, int head_dim,
+                                       int dtype, int64_t batch) {
+  if (dtype != kDtypeBF16 || rows <= 0 || batch <= 0) return 0;
+  switch (head_dim) {
+    case 64: return split_bytes_d<64>(rows, seq_kv, hidden, heads, batch);
+    case 72: return split_bytes_d<72>(rows, seq_kv, hidden, heads, batch);
+    case 128: return split_bytes_d<128>(rows, seq_kv, hidden, heads, batch);
+    default: return 0;
+  }
 }
 
 size_t attention_workspace_bytes(int64_t rows, int64_t hidden, int heads, int n_split) {

@@ -177,6 +177,11 @@ size_t attention_workspace_bytes(int64_t rows, int64_t hidden, int heads, int n_
 // Upper bound of the split count launch_attention uses.
 constexpr int kMaxAttnSplit = 8;
 
+// Workspace bytes of the key-range split launch_attention chooses for this launch when the
+// workspace does not limit it (0: no split; always 0 for fp32).
+size_t attention_split_workspace_bytes(int64_t rows, int64_t seq_kv, int64_t hidden, int heads, int head_dim,
+                                       int dtype, int64_t batch = 1);
+
 // Q rows (q, row stride ldq) and K buffer rows [off, off + n) (row stride ldk; sample g's
 // buffer kv_stride elements after sample 0's) of nb samples, bf16 in place: per-head RMSNorm
 // times gq / gk (norm), then rotary pairs by angles[buffer row] (rope).

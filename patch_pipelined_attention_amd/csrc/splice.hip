@@ -7,10 +7,11 @@
 //
 // Paths (chosen per matrix on the host):
 //   rows -> rows : one thread per 16-byte chunk of a row.
-//   rows -> K8   : one thread per (8-row group of the destination, 8 columns): 8 row
-//                  loads of 16 B, an 8x8 transpose of 16-bit values in registers, 8
-//                  stores of 16 B.  Groups cut by the ends of the range merge with the
-//                  destination's existing bytes (read-modify-write of that group only).
+//   rows -> K8   : one workgroup per (8-row group of the destination, 512 columns): the
+//                  rows are read in 16-byte units into LDS, and each thread assembles one
+//                  column's 8 rows into a 16-byte K8 unit, so loads and stores both run
+//                  along contiguous memory.  Groups cut by the ends of the range merge with
+//                  the destination's existing bytes (read-modify-write of that group only).
 //   generic      : one thread per element (any other layout pair, e.g. K8 -> rows).
 #include "pf_internal.h"
 
@@ -39,42 +40,39 @@ __global__ __launch_bounds__(256) void splice_rows_kernel(SpliceMat m0, SpliceMa
   *reinterpret_cast<uint4*>(m.dst + (offset + i) * m.dst_ld * esize + ch * 16) = v;
 }
 
-// 16-bit elements only.  Thread = (destination group g, column chunk cc of 8 columns).
+// 16-bit elements only.  Workgroup = one destination group g of 8 rows x kK8Cols columns: the
+// group's source rows are read in 16-byte units (a wavefront covers 1 KB of one row) into an
+// LDS tile, then thread j assembles column c's 8 rows (one 16-byte K8 unit) and stores it, so
+// consecutive threads write consecutive 16-byte units.  Groups cut by the ends of the range
+// merge with the destination's existing bytes (read-modify-write of those units only).
+constexpr int kK8Cols = 512;
 __global__ __launch_bounds__(256) void splice_rows_to_k8_kernel(SpliceMat m0, SpliceMat m1,
                                                                 int64_t row_elems, int64_t len,
                                                                 int64_t offset) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[8][kK8Cols];
   const SpliceMat m = blockIdx.y == 0 ? m0 : m1;
-  const int64_t ncc = row_elems >> 3;
-  const int64_t g0 = offset >> 3;
-  const int64_t ngroups = ((offset + len - 1) >> 3) - g0 + 1;
-  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (id >= ngroups * ncc) return;
-  const int64_t g = g0 + id / ncc;
-  const int64_t cc = id - (id / ncc) * ncc;
+  const int64_t ncb = (row_elems + kK8Cols - 1) / kK8Cols;
+  const int64_t g = (offset >> 3) + (int64_t)blockIdx.x / ncb;
+  const int64_t c0 = ((int64_t)blockIdx.x % ncb) * kK8Cols;
+  const int ncols = (int)(row_elems - c0 < kK8Cols ? row_elems - c0 : kK8Cols);   // a multiple of 8
   const uint16_t* src = reinterpret_cast<const uint16_t*>(m.src);
   uint16_t* dst = reinterpret_cast<uint16_t*>(m.dst);
-  uint16_t in[8][8];
   unsigned valid = 0;
 #pragma unroll
   for (int rr = 0; rr < 8; ++rr) {
     const int64_t r = g * 8 + rr;
-    if (r >= offset && r < offset + len) {
-      valid |= 1u << rr;
-      const uint4 v = *reinterpret_cast<const uint4*>(src + (r - offset) * m.src_ld + cc * 8);
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        in[rr][2 * e] = (uint16_t)(w[e] & 0xFFFFu);
-        in[rr][2 * e + 1] = (uint16_t)(w[e] >> 16);
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) in[rr][e] = 0;
-    }
+    if (r >= offset && r < offset + len) valid |= 1u << rr;
   }
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    uint16_t* p = dst + (g * row_elems + cc * 8 + c) * 8;
+  // load: 8 rows x ncols / 8 units of 16 bytes
+  for (int idx = threadIdx.x; idx < 8 * (kK8Cols / 8); idx += 256) {
+    const int rr = idx / (kK8Cols / 8), ch = idx % (kK8Cols / 8);
+    if (ch * 8 >= ncols || !(valid & (1u << rr))) continue;
+    const int64_t i = g * 8 + rr - offset;
+    *reinterpret_cast<uint4*>(&tile[rr][ch * 8]) = *reinterpret_cast<const uint4*>(src + i * m.src_ld + c0 + ch * 8);
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < ncols; c += 256) {
+    uint16_t* p = dst + (g * row_elems + c0 + c) * 8;
     uint16_t out[8];
     if (valid != 0xFFu) {
       const uint4 old = *reinterpret_cast<const uint4*>(p);
@@ -87,7 +85,7 @@ __global__ __launch_bounds__(256) void splice_rows_to_k8_kernel(SpliceMat m0, Sp
     }
 #pragma unroll
     for (int rr = 0; rr < 8; ++rr)
-      if (valid & (1u << rr)) out[rr] = in[rr][c];
+      if (valid & (1u << rr)) out[rr] = tile[rr][c];
     uint4 v;
     v.x = (uint32_t)out[0] | ((uint32_t)out[1] << 16);
     v.y = (uint32_t)out[2] | ((uint32_t)out[3] << 16);
@@ -151,9 +149,9 @@ hipError_t launch_splice(const KVDesc dst[2], const KVDesc src[2], int64_t row_e
                          b, row_elems * esize, len, offset, esize);
     } else if (p == 1) {
       const int64_t ngroups = ((offset + len - 1) >> 3) - (offset >> 3) + 1;
-      const int64_t units = ngroups * (row_elems >> 3);
-      hipLaunchKernelGGL(splice_rows_to_k8_kernel, dim3((unsigned)((units + 255) / 256), ny), dim3(256), 0,
-                         s, a, b, row_elems, len, offset);
+      const int64_t blocks = ngroups * ((row_elems + kK8Cols - 1) / kK8Cols);
+      hipLaunchKernelGGL(splice_rows_to_k8_kernel, dim3((unsigned)blocks, ny), dim3(256), 0, s, a, b, row_elems,
+                         len, offset);
     } else {
       const int64_t units = row_elems * len;
       hipLaunchKernelGGL(splice_generic_kernel, dim3((unsigned)((units + 255) / 256), ny), dim3(256), 0, s,

@@ -395,6 +395,10 @@ struct pf_stage {
   std::vector<LayerMem> layers;
   bool cond_set = false;
   bool broken = false;   // a HIP call failed: every later call returns PF_ERR_HIP
+  // stage_profile_begin / _end: event pairs recorded around attention launches
+  std::vector<hipEvent_t> prof_ev;
+  size_t prof_used = 0;
+  bool prof_on = false;
 };
 
 static size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -573,8 +577,16 @@ extern "C" pf_status stage_create(const pf_stage_config* cfg, pf_stage** out) {
   return PF_OK;
 }
 
+static void free_profile_events(pf_stage* st) {
+  for (hipEvent_t ev : st->prof_ev) (void)hipEventDestroy(ev);
+  st->prof_ev.clear();
+  st->prof_used = 0;
+  st->prof_on = false;
+}
+
 extern "C" pf_status stage_destroy(pf_stage* st) {
   if (!st) return PF_OK;
+  free_profile_events(st);
   free_stage_mem(st);
   delete st;
   return PF_OK;
@@ -781,10 +793,18 @@ static pf_status run_rows(pf_stage* st, int64_t off, int64_t n, float* x, int64_
     // one launch per part for every sample; each sample's queries attend over its own buffer
     for (int pi = 0; pi < n_parts; ++pi) {
       const Part& p = parts[pi];
+      const bool timed = st->prof_on && st->prof_used + 2 <= st->prof_ev.size();
+      if (timed && (e = hipEventRecord(st->prof_ev[st->prof_used], s)) != hipSuccess)
+        return stage_hip_fail(st, e, "attention timing event");
       if ((e = launch_attention(qkv + (size_t)(p.srow * 3 * h) * es, 3 * h, lm.k, h, lm.v, h, v_layout, h, st->s_kv,
                                 p.n, st->cfg.heads, st->cfg.head_dim, o + (size_t)(p.srow * ld_o) * es, ld_o, dt,
                                 st->attn_ws, st->attn_ws_bytes, s, nb, kv_stride)) != hipSuccess)
         return stage_hip_fail(st, e, "attention");
+      if (timed) {
+        if ((e = hipEventRecord(st->prof_ev[st->prof_used + 1], s)) != hipSuccess)
+          return stage_hip_fail(st, e, "attention timing event");
+        st->prof_used += 2;
+      }
     }
     for (int pi = 0; pi < n_parts; ++pi) {
       const Part& p = parts[pi];
@@ -884,6 +904,49 @@ extern "C" pf_status stage_run_step(pf_stage* st, const float* x_in, float* x_ou
     const int64_t off = st->cfg.seq_txt + (int64_t)m * st->patch_rows;
     if ((s = run_rows(st, off, st->patch_rows, x_out + off * h, xs, hs)) != PF_OK) return s;
   }
+  return PF_OK;
+}
+
+extern "C" pf_status stage_profile_begin(pf_stage* st, int32_t max_launches) {
+  pf_status s = check_stage(st, "stage_profile_begin");
+  if (s != PF_OK) return s;
+  if (max_launches < 1 || max_launches > (1 << 20))
+    return fail(PF_ERR_INVALID_ARG, "stage_profile_begin: max_launches %d outside [1, 2^20]", max_launches);
+  free_profile_events(st);
+  st->prof_ev.reserve(2 * (size_t)max_launches);
+  for (int32_t i = 0; i < 2 * max_launches; ++i) {
+    hipEvent_t ev;
+    hipError_t e = hipEventCreate(&ev);
+    if (e != hipSuccess) {
+      free_profile_events(st);
+      return hip_fail(e, "stage_profile_begin: hipEventCreate");
+    }
+    st->prof_ev.push_back(ev);
+  }
+  st->prof_on = true;
+  return PF_OK;
+}
+
+extern "C" pf_status stage_profile_end(pf_stage* st, int64_t* launches, double* attention_ms) {
+  pf_status s = check_stage(st, "stage_profile_end");
+  if (s != PF_OK) return s;
+  if (!launches || !attention_ms) return fail(PF_ERR_INVALID_ARG, "stage_profile_end: null out");
+  if (!st->prof_on) return fail(PF_ERR_STATE, "stage_profile_end: stage_profile_begin not called");
+  st->prof_on = false;
+  double total = 0.0;
+  for (size_t i = 0; i + 1 < st->prof_used; i += 2) {
+    hipError_t e = hipEventSynchronize(st->prof_ev[i + 1]);
+    float ms = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, st->prof_ev[i], st->prof_ev[i + 1]);
+    if (e != hipSuccess) {
+      free_profile_events(st);
+      return stage_hip_fail(st, e, "stage_profile_end: reading events");
+    }
+    total += ms;
+  }
+  *launches = (int64_t)(st->prof_used / 2);
+  *attention_ms = total;
+  free_profile_events(st);
   return PF_OK;
 }
 

@@ -52,7 +52,15 @@ def bf16_ulp(v):
     return np.ldexp(1.0, np.maximum(e, -125) - 8)
 
 
-def assert_bf16_close(got, want, what: str, floor: float = 0.0, ulps: int = 1, scale=None):
+def chain_elementwise(layer: int, hidden: int) -> bool:
+    """Whether a stored bf16 tensor of a chained stage (a K/V buffer) is gated element by element:
+    always for layer 0 (its inputs are the stage's own fp32 rows), and for later layers below the
+    Flux-shaped width; there the rounding flips of earlier layers fan out (see WIDE_HIDDEN), so
+    deeper buffers are gated on rel-L2 with the element bound reported."""
+    return layer == 0 or hidden < WIDE_HIDDEN
+
+
+def assert_bf16_close(got, want, what: str, floor: float = 0.0, ulps: int = 1, scale=None, elementwise: bool = True):
     """Stored bf16 tensors: each element within max(2e-2, `ulps` bf16 ulps of `scale` (default:
     the oracle value), floor) (a rounding flip at |v| >= 4 is 2^-5 > 2e-2), and rel-L2 within the
     contract tolerance.  `floor` is the bf16-probability noise floor of a chained comparison (0
@@ -71,7 +79,8 @@ def assert_bf16_close(got, want, what: str, floor: float = 0.0, ulps: int = 1, s
     worst = float((err / lim).max())
     print(f"[parity] {what}: max_abs={err.max():.3e} worst/limit={worst:.2f} rel_l2={rl:.3e}", flush=True)
     assert np.all(np.isfinite(got)), f"{what}: non-finite"
-    assert worst <= 1.0, f"{what}: an element is off by more than max(2e-2, {ulps} bf16 ulp)"
+    if elementwise:
+        assert worst <= 1.0, f"{what}: an element is off by more than max(2e-2, {ulps} bf16 ulp)"
     assert rl <= REL_L2, f"{what}: rel_l2 {rl:.3e} > {REL_L2}"
 
 

@@ -14,8 +14,8 @@ from patch_pipelined_attention_amd import synth
 from patch_pipelined_attention_amd.configs import C2, C3, C4
 from patch_pipelined_attention_amd.stage import Stage
 
-from _util import (assert_bf16_close, assert_close, bf16_ulp, chain_max_abs_tol, dev, host, max_abs, pair_norms,
-                   torch_cuda)
+from _util import (assert_bf16_close, assert_close, bf16_ulp, chain_elementwise, chain_max_abs_tol, dev, host, max_abs,
+                   pair_norms, torch_cuda)
 from test_stage import check_stage_output
 
 pytestmark = pytest.mark.gpu
@@ -91,8 +91,10 @@ def test_mmdit_stage_chain(case):
             check_stage_output(got, want_p, f"{case} step {s}", want, want_e, hidden=shape.hidden)
             for l in range(shape.num_layers):
                 k, v = st.kv_get(l)
-                assert_bf16_close(k, orc_p.K[l], f"{case} step {s} K[{l}]", **k_bound(orc_p.K[l], qk_norm, rope))
-                assert_bf16_close(v, orc_p.V[l], f"{case} step {s} V[{l}]")
+                ew = chain_elementwise(l, shape.hidden)
+                assert_bf16_close(k, orc_p.K[l], f"{case} step {s} K[{l}]", elementwise=ew,
+                                  **k_bound(orc_p.K[l], qk_norm, rope))
+                assert_bf16_close(v, orc_p.V[l], f"{case} step {s} V[{l}]", elementwise=ew)
 
 
 def test_mmdit_options_change_the_output():
@@ -148,7 +150,7 @@ def test_mmdit_guidance_pair_all_options():
                 for l in range(L):
                     k, _ = st.kv_get(l, sample=b)
                     assert_bf16_close(k, orc_p[b].K[l], f"pair step {s} sample {b} K[{l}]",
-                                      **k_bound(orc_p[b].K[l], True, True))
+                                      elementwise=chain_elementwise(l, shape.hidden), **k_bound(orc_p[b].K[l], True, True))
             assert max_abs(got[0], got[1]) > 1e-3
 
 
@@ -173,7 +175,8 @@ def test_mmdit_patch_across_the_text_boundary():
         check_stage_output(got, want, "straddling micro-step", hidden=shape.hidden)
         for l in range(shape.num_layers):
             k, _ = st.kv_get(l)
-            assert_bf16_close(k, orc.K[l], f"straddling micro-step K[{l}]", **k_bound(orc.K[l], True, True))
+            assert_bf16_close(k, orc.K[l], f"straddling micro-step K[{l}]", elementwise=chain_elementwise(l, shape.hidden),
+                              **k_bound(orc.K[l], True, True))
 
 
 # parallel (Flux.1 single-stream) block: (shape, qk_norm, rope, mlp_ratio)
@@ -218,9 +221,10 @@ def _parallel_chain(shape, par, qk_norm, rope, batch):
                 check_stage_output(got[b], want_p, f"parallel step {s} sample {b}", hidden=shape.hidden)
                 for l in range(L):
                     k, v = st.kv_get(l, sample=b)
-                    assert_bf16_close(k, orc_p[b].K[l], f"parallel step {s} sample {b} K[{l}]",
+                    ew = chain_elementwise(l, shape.hidden)
+                    assert_bf16_close(k, orc_p[b].K[l], f"parallel step {s} sample {b} K[{l}]", elementwise=ew,
                                       **k_bound(orc_p[b].K[l], qk_norm, rope))
-                    assert_bf16_close(v, orc_p[b].V[l], f"parallel step {s} sample {b} V[{l}]")
+                    assert_bf16_close(v, orc_p[b].V[l], f"parallel step {s} sample {b} V[{l}]", elementwise=ew)
         if batch > 1:
             assert max_abs(got[0], got[1]) > 1e-3
 
@@ -404,9 +408,11 @@ def test_flux_blocks_property_b_micro_steps_touch_only_their_rows(block):
                 k, v = st.kv_get(l)
                 np.testing.assert_array_equal(k[outside], before[l][0][outside])
                 np.testing.assert_array_equal(v[outside], before[l][1][outside])
+                ew = chain_elementwise(l, shape.hidden)
                 assert_bf16_close(k[rs], orc.K[l][rs], f"{block} fresh K rows [{off},{off + n}) layer {l}",
-                                  **k_bound(orc.K[l][rs], True, True))
-                assert_bf16_close(v[rs], orc.V[l][rs], f"{block} fresh V rows [{off},{off + n}) layer {l}")
+                                  elementwise=ew, **k_bound(orc.K[l][rs], True, True))
+                assert_bf16_close(v[rs], orc.V[l][rs], f"{block} fresh V rows [{off},{off + n}) layer {l}",
+                                  elementwise=ew)
 
 
 @pytest.mark.parametrize("block", ["mmdit", "flux-single"])

@@ -13,8 +13,8 @@ from patch_pipelined_attention_amd import synth
 from patch_pipelined_attention_amd.configs import C1, C2, C3, C4, C5
 from patch_pipelined_attention_amd.stage import Stage
 
-from _util import (MAX_ABS, REL_L2, assert_bf16_close, assert_close, chain_max_abs_tol, dev, host, max_abs,
-                   torch_cuda)
+from _util import (MAX_ABS, REL_L2, assert_bf16_close, assert_close, chain_elementwise, chain_max_abs_tol, dev, host,
+                   max_abs, torch_cuda)
 
 pytestmark = pytest.mark.gpu
 
@@ -78,8 +78,9 @@ def _run_chain(shape, steps, check_exact=True):
                                    hidden=shape.hidden)
                 for l in range(shape.num_layers):
                     k, v = st.kv_get(l)
-                    assert_bf16_close(k, orc_p.K[l], f"{shape.name} step {s} K[{l}]")
-                    assert_bf16_close(v, orc_p.V[l], f"{shape.name} step {s} V[{l}]")
+                    ew = chain_elementwise(l, shape.hidden)
+                    assert_bf16_close(k, orc_p.K[l], f"{shape.name} step {s} K[{l}]", elementwise=ew)
+                    assert_bf16_close(v, orc_p.V[l], f"{shape.name} step {s} V[{l}]", elementwise=ew)
             else:
                 assert_close(got, want_e, f"{shape.name} step {s} vs exact oracle", max_abs_tol=1e-3, rel_tol=1e-5)
                 for l in range(shape.num_layers):
@@ -131,8 +132,9 @@ def _run_pair_chain(shape, steps):
                     check_stage_output(got[b], want, f"{shape.name} pair step {s} sample {b}", hidden=shape.hidden)
                     for l in range(L):
                         k, v = st.kv_get(l, sample=b)
-                        assert_bf16_close(k, orc_b[b].K[l], f"pair step {s} sample {b} K[{l}]")
-                        assert_bf16_close(v, orc_b[b].V[l], f"pair step {s} sample {b} V[{l}]")
+                        ew = chain_elementwise(l, shape.hidden)
+                        assert_bf16_close(k, orc_b[b].K[l], f"pair step {s} sample {b} K[{l}]", elementwise=ew)
+                        assert_bf16_close(v, orc_b[b].V[l], f"pair step {s} sample {b} V[{l}]", elementwise=ew)
                 else:
                     assert_close(got[b], want, f"{shape.name} pair step {s} sample {b} vs exact oracle",
                                  max_abs_tol=1e-3, rel_tol=1e-5)
@@ -320,8 +322,9 @@ def test_property_b_micro_steps_touch_only_their_rows():
                 outside[rs] = False
                 np.testing.assert_array_equal(k[outside], before[l][0][outside])
                 np.testing.assert_array_equal(v[outside], before[l][1][outside])
-                assert_bf16_close(k[rs], orc.K[l][rs], f"fresh K rows [{off},{off + n}) layer {l}")
-                assert_bf16_close(v[rs], orc.V[l][rs], f"fresh V rows [{off},{off + n}) layer {l}")
+                ew = chain_elementwise(l, shape.hidden)
+                assert_bf16_close(k[rs], orc.K[l][rs], f"fresh K rows [{off},{off + n}) layer {l}", elementwise=ew)
+                assert_bf16_close(v[rs], orc.V[l][rs], f"fresh V rows [{off},{off + n}) layer {l}", elementwise=ew)
         assert h == shape.hidden
 
 

@@ -46,7 +46,7 @@ def parse():
                          "block (parallel attention + MLP, QK-RMSNorm, RoPE)")
     ap.add_argument("--breakdown", action="store_true", help="also time every kernel of a patch-layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=25.0, help="target CPU time of the oracle sample")
     ap.add_argument("--probe", choices=PROBES,
                     help="only launch one kernel of a patch-layer at the stage's launch shape (or a plain 1 GiB "
                          "copy) --probe-iters times; a target for rocprofv3 counter runs")

@@ -408,6 +408,18 @@ pf_status pf_attention(const void* q, int64_t ldq, const pf_kv_view* kv, int64_t
                        int64_t rows, int32_t heads, int32_t head_dim, void* o, int64_t ldo,
                        void* workspace, uint64_t workspace_bytes, void* stream);
 
+/* pf_attention without a workspace argument and without any allocation, for callers that
+ * cannot allocate (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments and result as pf_attention given a workspace of
+ * pf_attention_workspace_size bytes (the same key-range split, the same bits); the split
+ * partials go to the library's static device scratch of 128 MiB (134217728 bytes), which each
+ * GPU the library runs on holds until the process ends.  A launch whose split needs more than
+ * that (for example 4 splits of 6144 rows x 3072 columns) returns PF_ERR_UNSUPPORTED and
+ * enqueues nothing.  Every call on one GPU shares the scratch: calls that overlap in time on
+ * one GPU (different streams without ordering) race.  Errors: as pf_attention. */
+pf_status pf_attention_noalloc(const void* q, int64_t ldq, const pf_kv_view* kv, int64_t seq_kv, int64_t rows,
+                               int32_t heads, int32_t head_dim, void* o, int64_t ldo, void* stream);
+
 /* Workspace bytes pf_attention can use for `rows` queries of `heads` x `head_dim`.  Source:
  * as pf_attention.  Errors:
  * INVALID_ARG (bad sizes, NULL out). */

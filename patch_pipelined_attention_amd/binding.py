@@ -98,6 +98,7 @@ _SIGNATURES = {
     "pf_attention": [_P, _I64, ctypes.POINTER(KVView), _I64, _I64, _I32, _I32, _P, _I64, _P, ctypes.c_uint64, _P],
     "pf_qk_norm_rope": [_P, _I64, ctypes.POINTER(KVView), _I64, _I64, _I32, _I32, _P, _P, _P, _U32, _P],
     "pf_attention_workspace_size": [_I64, _I32, _I32, ctypes.POINTER(ctypes.c_uint64)],
+    "pf_attention_noalloc": [_P, _I64, ctypes.POINTER(KVView), _I64, _I64, _I32, _I32, _P, _I64, _P],
     "pf_adaln": [_P, _P, _P, _I32, _P, _I32, _P],
 }
 
@@ -268,6 +269,14 @@ def pf_attention(q, kv: KVView, seq_kv: int, rows: int, heads: int, head_dim: in
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().pf_attention(_ptr(q), ldq, ctypes.byref(kv), seq_kv, rows, heads, head_dim, _ptr(o), ldo,
                               _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def pf_attention_noalloc(q, kv: KVView, seq_kv: int, rows: int, heads: int, head_dim: int, o, ldq=None, ldo=None,
+                         stream=None) -> None:
+    ldq = q.stride(0) if ldq is None else ldq
+    ldo = o.stride(0) if ldo is None else ldo
+    _check(lib().pf_attention_noalloc(_ptr(q), ldq, ctypes.byref(kv), seq_kv, rows, heads, head_dim, _ptr(o), ldo,
+                                      _stream(stream)))
 
 
 def pf_qk_norm_rope(q, kv: KVView, row_offset: int, rows: int, heads: int, head_dim: int, q_gamma=None,

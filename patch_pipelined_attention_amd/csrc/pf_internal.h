@@ -182,6 +182,11 @@ constexpr int kMaxAttnSplit = 8;
 size_t attention_split_workspace_bytes(int64_t rows, int64_t seq_kv, int64_t hidden, int heads, int head_dim,
                                        int dtype, int64_t batch = 1);
 
+// The library's static device scratch (allocation-free entry points): its address on the
+// current device (looked up once per device) and its size.
+constexpr size_t kStaticScratchBytes = (size_t)128 << 20;
+hipError_t static_scratch(void** ptr);
+
 // Q rows (q, row stride ldq) and K buffer rows [off, off + n) (row stride ldk; sample g's
 // buffer kv_stride elements after sample 0's) of nb samples, bf16 in place: per-head RMSNorm
 // times gq / gk (norm), then rotary pairs by angles[buffer row] (rope).

@@ -316,6 +316,29 @@ extern "C" pf_status pf_attention(const void* q, int64_t ldq, const pf_kv_view* 
   return e == hipSuccess ? PF_OK : hip_fail(e, "attention launch");
 }
 
+extern "C" pf_status pf_attention_noalloc(const void* q, int64_t ldq, const pf_kv_view* kv, int64_t seq_kv,
+                                          int64_t rows, int32_t heads, int32_t head_dim, void* o, int64_t ldo,
+                                          void* stream) {
+  pf_status st = validate_attention(q, ldq, kv, seq_kv, rows, heads, head_dim, o, ldo);
+  if (st != PF_OK) return st;
+  if ((st = check_device()) != PF_OK) return st;
+  // the split pf_attention would choose with a workspace of pf_attention_workspace_size bytes
+  const size_t need = attention_split_workspace_bytes(rows, seq_kv, kv->row_elems, heads, head_dim, kv->dtype);
+  if (need > kStaticScratchBytes)
+    return fail(PF_ERR_UNSUPPORTED,
+                "attention_noalloc: this launch's key-range split needs %zu bytes of scratch, more than the "
+                "library's static %zu bytes (use pf_attention with a workspace)",
+                need, kStaticScratchBytes);
+  void* ws = nullptr;
+  if (need > 0) {
+    const hipError_t e = static_scratch(&ws);
+    if (e != hipSuccess) return hip_fail(e, "attention_noalloc: static scratch address");
+  }
+  const hipError_t e = launch_attention(q, ldq, kv->k, kv->k_ld, kv->v, kv->v_ld, kv->v_layout, kv->row_elems, seq_kv,
+                                        rows, heads, head_dim, o, ldo, kv->dtype, ws, need, (hipStream_t)stream);
+  return e == hipSuccess ? PF_OK : hip_fail(e, "attention_noalloc launch");
+}
+
 extern "C" pf_status pf_attention_workspace_size(int64_t rows, int32_t heads, int32_t head_dim, uint64_t* bytes) {
   if (!bytes) return fail(PF_ERR_INVALID_ARG, "attention_workspace_size: null out");
   if (rows < 0 || heads <= 0 || head_dim <= 0) return fail(PF_ERR_INVALID_ARG, "attention_workspace_size: bad sizes");

@@ -35,9 +35,13 @@
 //   * D = 72 pads the score contraction to 80 and the output rows to 96 with zero
 //     operands; nothing outside the real 72 columns is read or written.
 //   * when there are too few (query tile, head) pairs to fill the GPU, the key range is
-//     split across workgroups; each writes its slice's normalised result in fp32 with the
-//     slice's (m, l), and a combine kernel merges them (a convex combination with power-of-two
-//     weights times l, so the merge adds only fp32 rounding to the unsplit result).
+//     cut into pieces run by different workgroups: either a fixed split of every head's key
+//     range, or (one patch of a large stage: a few query tiles, many heads) a grouped stream-K
+//     schedule, where one group of workgroups per query-tile set takes an equal stretch of the
+//     (head, key tile) line, so every CU gets the same number of key tiles in one round.  A
+//     piece short of a whole key range writes its normalised result in fp32 with its (m, l),
+//     and a combine kernel merges them (a convex combination with power-of-two weights times
+//     l, so the merge adds only fp32 rounding to the unsplit result).
 //   * the block index is remapped so each XCD (blocks are dealt round-robin to the 8
 //     XCDs) works on a contiguous run of query tiles that share K/V in its L2.
 //
@@ -72,7 +76,8 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const bf16* __restric
                                                          const bf16* __restrict__ Kb, int64_t ldk,
                                                          const bf16* __restrict__ Vb, int64_t hidden,
                                                          int64_t S, int64_t rows, int n_qtiles, int n_split,
-                                                         int tiles_per_split, bf16* __restrict__ O,
+                                                         int tiles_per_split, int64_t group_tiles,
+                                                         bf16* __restrict__ O,
                                                          int64_t ldo, float* __restrict__ part_o,
                                                          float* __restrict__ part_ml, float scale_log2,
                                                          int64_t grp_rows, int qtiles_per_grp, int64_t kv_stride) {
@@ -100,20 +105,36 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const bf16* __restric
   // Samples of a batch: query rows [g * grp_rows, (g+1) * grp_rows) of Q / O and the partials
   // belong to sample g, whose K / V buffers start g * kv_stride elements on; each sample has
   // qtiles_per_grp query tiles (n_qtiles in all).
+  // Work of the launch: for every query tile, the key tiles of every head in the order
+  // (head, key tile), a line of H * ntiles tiles.  Workgroup (query tile qt_all, index gi) takes
+  // one stretch of that line:
+  //   * fixed split (group_tiles == 0): gi = split + n_split * head, key tiles
+  //     [split * tiles_per_split, +tiles_per_split) of that head;
+  //   * grouped stream-K (group_tiles > 0): gi is a group of n_qtiles workgroups, one per
+  //     query tile, that all take line positions [gi * group_tiles, +group_tiles): the same
+  //     key tiles at the same time (shared in L2), and a stretch may run over several heads.
+  // Each head met by a stretch is one piece.  A piece covering all of a head's key tiles writes
+  // O directly; any other piece writes its normalised fp32 result and (m, l) into partial slot
+  // split * H + head (fixed split) or head + gi (stream-K), merged by attn_combine_kernel.
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
   const int qt_all = lid % n_qtiles;
-  const int rest = lid / n_qtiles;
-  const int split = rest % n_split;
-  const int head = rest / n_split;
+  const int gi = lid / n_qtiles;
   const int grp_id = qt_all / qtiles_per_grp;
   const int qt = qt_all - grp_id * qtiles_per_grp;
   Kb += grp_id * kv_stride;
   Vb += grp_id * kv_stride;
   const int64_t row_base = (int64_t)grp_id * grp_rows;
-  const int64_t col0 = (int64_t)head * D;
   const int64_t ntiles = (S + TK - 1) / TK;
-  const int64_t t_begin = (int64_t)split * tiles_per_split;
-  const int64_t t_end = t_begin + tiles_per_split < ntiles ? t_begin + tiles_per_split : ntiles;
+  const int64_t H = hidden / D;
+  int64_t pos, pos_end;
+  if (group_tiles > 0) {
+    pos = (int64_t)gi * group_tiles;
+    pos_end = pos + group_tiles < H * ntiles ? pos + group_tiles : H * ntiles;
+  } else {
+    const int split = gi % n_split, head0 = gi / n_split;
+    pos = head0 * ntiles + (int64_t)split * tiles_per_split;
+    pos_end = pos + tiles_per_split < (head0 + 1) * ntiles ? pos + tiles_per_split : (head0 + 1) * ntiles;
+  }
 
   int64_t q_row[QB];   // row of Q / O / the partials
   bool q_ok[QB];       // inside this sample's rows
@@ -124,81 +145,125 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const bf16* __restric
     q_row[qb] = row_base + local;
   }
 
-  bf16x8 qf[QB][KS];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int d0 = ks * 16 + hi * 8;
-      if (q_ok[qb] && d0 < D) {
-        qf[qb][ks] = *reinterpret_cast<const bf16x8*>(Q + q_row[qb] * ldq + col0 + d0);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qf[qb][ks][e] = (bf16)0.f;
-      }
-    }
-  // Q has landed before the first direct load is issued: from here on every outstanding
-  // global load is a tile load, counted by the explicit waits below.
-  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
-
-  f32x16 o[QB][DB];
-  float m_ref[QB], l_run[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    l_run[qb] = 0.f;
-    m_ref[qb] = -INFINITY;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) o[qb][db][e] = 0.f;
-  }
-
-  const int64_t ngroups = (S + 7) >> 3;
-  auto k_unit = [](int p, int c) -> int {
-    if constexpr (W % 2 == 1) return p * W + c;
-    else if constexpr (W == 8) return p * 8 + (c ^ (p & 7));
-    else return p * 16 + (c ^ (p & 15));
+  auto barrier_all = [] {
+    __builtin_amdgcn_sched_barrier(0);
+    lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);
   };
+  for (bool first = true; pos < pos_end; first = false) {
+    const int64_t head = pos / ntiles;
+    const int64_t t_begin = pos - head * ntiles;
+    const int64_t t_end = t_begin + (pos_end - pos) < ntiles ? t_begin + (pos_end - pos) : ntiles;
+    pos += t_end - t_begin;
+    const bool whole = t_begin == 0 && t_end == ntiles;
+    const int64_t slot = group_tiles > 0 ? head + gi : (int64_t)(gi % n_split) * H + head;
+    const int64_t col0 = head * D;
+    // a later piece reuses the LDS ring: every wavefront is past its last read of the previous one
+    if (!first) barrier_all();
 
-  // Lane l of load i (i = wl + 4j, this wavefront's j-th) fills unit 64(i mod NI) + l of the
-  // K part (i < NI) or the V part.  Lanes past the part's KU real units fill padding units
-  // that nothing reads, from the part's unit 0 (a valid address), so no lane is masked off.
-  uint32_t ld_off[NJ];
-  int ld_row[NJ];
+    bf16x8 qf[QB][KS];
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const int i = wl + 4 * j;
-    const bool kpart = i < NI;
-    int u = (kpart ? i : i - NI) * 64 + lane;
-    if (u >= KU) u = 0;
-    if (kpart) {
-      int p, c;
-      if constexpr (W % 2 == 1) {
-        p = u / W;
-        c = u - p * W;
-      } else if constexpr (W == 8) {
-        p = u >> 3;
-        c = (u & 7) ^ (p & 7);
-      } else {
-        p = u >> 4;
-        c = (u & 15) ^ (p & 15);
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int d0 = ks * 16 + hi * 8;
+        if (q_ok[qb] && d0 < D) {
+          qf[qb][ks] = *reinterpret_cast<const bf16x8*>(Q + q_row[qb] * ldq + col0 + d0);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) qf[qb][ks][e] = (bf16)0.f;
+        }
       }
-      const int row = swap_bits23(p);
-      ld_row[j] = row;
-      ld_off[j] = (uint32_t)(row * ldk * 2 + c * 16);
-    } else {
-      const int g = u / D, d = u - g * D;
-      ld_row[j] = g;
-      ld_off[j] = (uint32_t)((g * hidden + d) * 16);
+    // Q has landed before the first direct load is issued: from here on every outstanding
+    // global load is a tile load, counted by the explicit waits below.
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+
+    f32x16 o[QB][DB];
+    float m_ref[QB], l_run[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      l_run[qb] = 0.f;
+      m_ref[qb] = -INFINITY;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[qb][db][e] = 0.f;
     }
-  }
-  // Tile t into stage st (group 0 only).  Only the buffer's last tile can run past S: its rows
-  // (K8 groups) past the end read the last valid row (group) instead; their scores are masked
-  // and their V entries zeroed before use.
-  auto issue_tile = [&](int64_t t, int st) {
-    const char* kbase = reinterpret_cast<const char*>(Kb + (t * TK) * ldk + col0);
-    const char* vbase = reinterpret_cast<const char*>(Vb + (t * (TK / 8) * hidden + col0) * 8);
-    if ((t + 1) * TK <= S) {
+
+    const int64_t ngroups = (S + 7) >> 3;
+    auto k_unit = [](int p, int c) -> int {
+      if constexpr (W % 2 == 1) return p * W + c;
+      else if constexpr (W == 8) return p * 8 + (c ^ (p & 7));
+      else return p * 16 + (c ^ (p & 15));
+    };
+
+    // Lane l of load i (i = wl + 4j, this wavefront's j-th) fills unit 64(i mod NI) + l of the
+    // K part (i < NI) or the V part.  Lanes past the part's KU real units fill padding units
+    // that nothing reads, from the part's unit 0 (a valid address), so no lane is masked off.
+    uint32_t ld_off[NJ];
+    int ld_row[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int i = wl + 4 * j;
+      const bool kpart = i < NI;
+      int u = (kpart ? i : i - NI) * 64 + lane;
+      if (u >= KU) u = 0;
+      if (kpart) {
+        int p, c;
+        if constexpr (W % 2 == 1) {
+          p = u / W;
+          c = u - p * W;
+        } else if constexpr (W == 8) {
+          p = u >> 3;
+          c = (u & 7) ^ (p & 7);
+        } else {
+          p = u >> 4;
+          c = (u & 15) ^ (p & 15);
+        }
+        const int row = swap_bits23(p);
+        ld_row[j] = row;
+        ld_off[j] = (uint32_t)(row * ldk * 2 + c * 16);
+      } else {
+        const int g = u / D, d = u - g * D;
+        ld_row[j] = g;
+        ld_off[j] = (uint32_t)((g * hidden + d) * 16);
+      }
+    }
+    // Tile t into stage st (group 0 only).  Only the buffer's last tile can run past S: its rows
+    // (K8 groups) past the end read the last valid row (group) instead; their scores are masked
+    // and their V entries zeroed before use.
+    auto issue_tile = [&](int64_t t, int st) {
+      const char* kbase = reinterpret_cast<const char*>(Kb + (t * TK) * ldk + col0);
+      const char* vbase = reinterpret_cast<const char*>(Vb + (t * (TK / 8) * hidden + col0) * 8);
+      if ((t + 1) * TK <= S) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const int i = wl + 4 * j;
+          if (i >= NINST) continue;                   // wavefront-uniform
+          const bool kpart = i < NI;
+          dma_load16(kpart ? kbase : vbase, ld_off[j], &lds[st][(kpart ? i : KUP / 64 + i - NI) * 64]);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const int i = wl + 4 * j;
+          if (i >= NINST) continue;
+          const bool kpart = i < NI;
+          uint32_t off = ld_off[j];
+          if (kpart) {
+            const int64_t over = t * TK + ld_row[j] - (S - 1);
+            if (over > 0) off -= (uint32_t)(over * ldk * 2);
+          } else {
+            const int64_t over = t * (TK / 8) + ld_row[j] - (ngroups - 1);
+            if (over > 0) off -= (uint32_t)(over * hidden * 16);
+          }
+          dma_load16(kpart ? kbase : vbase, off, &lds[st][(kpart ? i : KUP / 64 + i - NI) * 64]);
+        }
+      }
+    };
+    auto issue_tile_full = [&](int64_t t, int st) {
+      const char* kbase = reinterpret_cast<const char*>(Kb + (t * TK) * ldk + col0);
+      const char* vbase = reinterpret_cast<const char*>(Vb + (t * (TK / 8) * hidden + col0) * 8);
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         const int i = wl + 4 * j;
@@ -206,357 +271,332 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const bf16* __restric
         const bool kpart = i < NI;
         dma_load16(kpart ? kbase : vbase, ld_off[j], &lds[st][(kpart ? i : KUP / 64 + i - NI) * 64]);
       }
-    } else {
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const int i = wl + 4 * j;
-        if (i >= NINST) continue;
-        const bool kpart = i < NI;
-        uint32_t off = ld_off[j];
-        if (kpart) {
-          const int64_t over = t * TK + ld_row[j] - (S - 1);
-          if (over > 0) off -= (uint32_t)(over * ldk * 2);
-        } else {
-          const int64_t over = t * (TK / 8) + ld_row[j] - (ngroups - 1);
-          if (over > 0) off -= (uint32_t)(over * hidden * 16);
-        }
-        dma_load16(kpart ? kbase : vbase, off, &lds[st][(kpart ? i : KUP / 64 + i - NI) * 64]);
-      }
-    }
-  };
-  auto issue_tile_full = [&](int64_t t, int st) {
-    const char* kbase = reinterpret_cast<const char*>(Kb + (t * TK) * ldk + col0);
-    const char* vbase = reinterpret_cast<const char*>(Vb + (t * (TK / 8) * hidden + col0) * 8);
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int i = wl + 4 * j;
-      if (i >= NINST) continue;                   // wavefront-uniform
-      const bool kpart = i < NI;
-      dma_load16(kpart ? kbase : vbase, ld_off[j], &lds[st][(kpart ? i : KUP / 64 + i - NI) * 64]);
-    }
-  };
-  // NSTAGE - 3 newer tiles in flight (the steady state)
-  auto wait_loads_const = [&] {
-    constexpr int n = (NSTAGE - 3) * NMIN;
-    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
-  };
-  auto wait_loads = [&](int newer_tiles) {
-    if (newer_tiles >= 3) __builtin_amdgcn_s_waitcnt(((3 * NMIN) & 15) | (((3 * NMIN) >> 4) << 14) | (7 << 4) | (15 << 8));
-    else if (newer_tiles == 2) __builtin_amdgcn_s_waitcnt(((2 * NMIN) & 15) | (((2 * NMIN) >> 4) << 14) | (7 << 4) | (15 << 8));
-    else if (newer_tiles == 1) __builtin_amdgcn_s_waitcnt((NMIN & 15) | ((NMIN >> 4) << 14) | (7 << 4) | (15 << 8));
-    else __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
-  };
-  auto barrier = [] {
-    __builtin_amdgcn_sched_barrier(0);
-    lds_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-  };
+    };
+    // NSTAGE - 3 newer tiles in flight (the steady state)
+    auto wait_loads_const = [&] {
+      constexpr int n = (NSTAGE - 3) * NMIN;
+      __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+    };
+    auto wait_loads = [&](int newer_tiles) {
+      if (newer_tiles >= 3) __builtin_amdgcn_s_waitcnt(((3 * NMIN) & 15) | (((3 * NMIN) >> 4) << 14) | (7 << 4) | (15 << 8));
+      else if (newer_tiles == 2) __builtin_amdgcn_s_waitcnt(((2 * NMIN) & 15) | (((2 * NMIN) >> 4) << 14) | (7 << 4) | (15 << 8));
+      else if (newer_tiles == 1) __builtin_amdgcn_s_waitcnt((NMIN & 15) | ((NMIN >> 4) << 14) | (7 << 4) | (15 << 8));
+      else __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+    };
+    auto barrier = [] {
+      __builtin_amdgcn_sched_barrier(0);
+      lds_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    };
 
-  // K_t operands of S^T = K_t . Q^T (lane: key row l32, 8 consecutive d).  Rows of the
-  // padded k-step past D read a valid LDS unit and are zeroed by a select (no branch).
-  auto read_k = [&](int st, bf16x8 (&kf)[KS]) {
-    const uint4* base = lds[st];
+    // K_t operands of S^T = K_t . Q^T (lane: key row l32, 8 consecutive d).  Rows of the
+    // padded k-step past D read a valid LDS unit and are zeroed by a select (no branch).
+    auto read_k = [&](int st, bf16x8 (&kf)[KS]) {
+      const uint4* base = lds[st];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int d0 = ks * 16 + hi * 8;
-      if constexpr (KS * 16 > D) {
-        if (ks == KS - 1) {
-          const int c = d0 < D ? 2 * ks + hi : 2 * ks;
-          const u32x4 w = *reinterpret_cast<const u32x4*>(&base[k_unit(l32, c)]);
-          const u32x4 z = {0u, 0u, 0u, 0u};
-          kf[ks] = __builtin_bit_cast(bf16x8, d0 < D ? w : z);
-          continue;
+      for (int ks = 0; ks < KS; ++ks) {
+        const int d0 = ks * 16 + hi * 8;
+        if constexpr (KS * 16 > D) {
+          if (ks == KS - 1) {
+            const int c = d0 < D ? 2 * ks + hi : 2 * ks;
+            const u32x4 w = *reinterpret_cast<const u32x4*>(&base[k_unit(l32, c)]);
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            kf[ks] = __builtin_bit_cast(bf16x8, d0 < D ? w : z);
+            continue;
+          }
         }
+        kf[ks] = *reinterpret_cast<const bf16x8*>(&base[k_unit(l32, 2 * ks + hi)]);
       }
-      kf[ks] = *reinterpret_cast<const bf16x8*>(&base[k_unit(l32, 2 * ks + hi)]);
-    }
-  };
-  auto scores = [&](const bf16x8 (&kf)[KS], f32x16 (&sc)[QB]) {
+    };
+    auto scores = [&](const bf16x8 (&kf)[KS], f32x16 (&sc)[QB]) {
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
+      for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) sc[qb][e] = 0.f;
+        for (int e = 0; e < 16; ++e) sc[qb][e] = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
+      for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) sc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[qb][ks], sc[qb], 0, 0, 0);
-  };
-  auto mask_scores = [&](int64_t t, f32x16 (&sc)[QB]) {
-    const int lim = (int)(S - t * TK);
+        for (int qb = 0; qb < QB; ++qb) sc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[qb][ks], sc[qb], 0, 0, 0);
+    };
+    auto mask_scores = [&](int64_t t, f32x16 (&sc)[QB]) {
+      const int lim = (int)(S - t * TK);
 #pragma unroll
-    for (int g = 0; g < 4; ++g)
+      for (int g = 0; g < 4; ++g)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (16 * (g >> 1) + 8 * hi + 4 * (g & 1) + j >= lim) {
+        for (int j = 0; j < 4; ++j) {
+          if (16 * (g >> 1) + 8 * hi + 4 * (g & 1) + j >= lim) {
 #pragma unroll
-          for (int qb = 0; qb < QB; ++qb) sc[qb][4 * g + j] = -INFINITY;
+            for (int qb = 0; qb < QB; ++qb) sc[qb][4 * g + j] = -INFINITY;
+          }
         }
-      }
-  };
-  constexpr bool kSumRow = D % 32 != 0;
-  constexpr int kSumIdx = 4 * ((D % 32) / 8) + 0;
-  // V_t^T operands of O^T += V_t^T . P^T (lane: row d = db*32 + l32, 8 keys of group 2*h2 + hi);
-  // rows past D are zero, or ones in row D for the MFMA row sum; `zero_tail` zeroes keys past S
-  auto read_v = [&](int64_t t, int st, bf16x8 (&vf)[2][DB], bool zero_tail) {
-    const uint4* base = lds[st] + KUP;
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      const int grp8 = 2 * h2 + hi;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const int d = db * 32 + l32;
-        if (db * 32 + 32 <= D) {
-          vf[h2][db] = *reinterpret_cast<const bf16x8*>(&base[grp8 * D + d]);
-        } else {
-          // rows past D: zero, or ones in row D (MFMA row sum); selected without a branch
-          const u32x4 w = *reinterpret_cast<const u32x4*>(&base[grp8 * D + (d < D ? d : D - 1)]);
-          const uint32_t f = (kSumRow && d == D) ? 0x3f803f80u : 0u;   // bf16 pair (1, 1) or (0, 0)
-          const u32x4 fv = {f, f, f, f};
-          vf[h2][db] = __builtin_bit_cast(bf16x8, d < D ? w : fv);
-        }
-        if (zero_tail) {
-          const int lim = (int)(S - t * TK) - grp8 * 8;
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (e >= lim && db * 32 + l32 < D) vf[h2][db][e] = (bf16)0.f;
-        }
-      }
-    }
-  };
-  auto pv = [&](const bf16x8 (&vf)[2][DB], const bf16x8 (&pb)[QB][2]) {
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[h2][db], pb[qb][h2], o[qb][db], 0, 0, 0);
-  };
-  const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
-  // p = 2^(s c - m) packed to bf16 for every score of the tile; the reference m of a query is an
-  // integer, raised only when the tile holds a score more than kRaise above it (so p < 2^kRaise
-  // and sums stay far from fp32 overflow).  Common path without a row max: for D = 64 / 128 the
-  // lane's partial sum of the tile's rounded weights (needed for l anyway) exceeds 2^kRaise
-  // whenever a weight does (the first tile, where m = -inf, gives inf); for D = 72 (the row sum
-  // comes from the P.V MFMA) a lane-local maximum of the raw scores is compared with the
-  // threshold.  Only then (rare after the first tile) does the wave take the row max across
-  // both halves of the query's keys, raise m to its ceiling and rescale O and l by the exact
-  // power of two 2^(m_old - m_new), and recompute the tile's weights.
-  constexpr float kRaise = 64.0f;
-  auto exp_pack = [&](f32x16 (&sc)[QB], bf16x8 (&pc)[QB][2], float (&lt)[QB]) {
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      uint32_t pk[8];
-      lt[qb] = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const f32x2 pp = {__builtin_amdgcn_exp2f(fmaf(sc[qb][2 * e], scale_log2, -m_ref[qb])),
-                          __builtin_amdgcn_exp2f(fmaf(sc[qb][2 * e + 1], scale_log2, -m_ref[qb]))};
-        const bf16x2 pb2 = __builtin_convertvector(pp, bf16x2);
-        if constexpr (!kSumRow) lt[qb] = __builtin_amdgcn_fdot2_f32_bf16(pb2, ones, lt[qb], false);
-        pk[e] = __builtin_bit_cast(uint32_t, pb2);
-      }
+    };
+    constexpr bool kSumRow = D % 32 != 0;
+    constexpr int kSumIdx = 4 * ((D % 32) / 8) + 0;
+    // V_t^T operands of O^T += V_t^T . P^T (lane: row d = db*32 + l32, 8 keys of group 2*h2 + hi);
+    // rows past D are zero, or ones in row D for the MFMA row sum; `zero_tail` zeroes keys past S
+    auto read_v = [&](int64_t t, int st, bf16x8 (&vf)[2][DB], bool zero_tail) {
+      const uint4* base = lds[st] + KUP;
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
-        const u32x4 w = {pk[4 * h2], pk[4 * h2 + 1], pk[4 * h2 + 2], pk[4 * h2 + 3]};
-        pc[qb][h2] = __builtin_bit_cast(bf16x8, w);
+        const int grp8 = 2 * h2 + hi;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const int d = db * 32 + l32;
+          if (db * 32 + 32 <= D) {
+            vf[h2][db] = *reinterpret_cast<const bf16x8*>(&base[grp8 * D + d]);
+          } else {
+            // rows past D: zero, or ones in row D (MFMA row sum); selected without a branch
+            const u32x4 w = *reinterpret_cast<const u32x4*>(&base[grp8 * D + (d < D ? d : D - 1)]);
+            const uint32_t f = (kSumRow && d == D) ? 0x3f803f80u : 0u;   // bf16 pair (1, 1) or (0, 0)
+            const u32x4 fv = {f, f, f, f};
+            vf[h2][db] = __builtin_bit_cast(bf16x8, d < D ? w : fv);
+          }
+          if (zero_tail) {
+            const int lim = (int)(S - t * TK) - grp8 * 8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (e >= lim && db * 32 + l32 < D) vf[h2][db][e] = (bf16)0.f;
+          }
+        }
       }
-    }
-  };
-  auto mx3 = [](float a, float b, float c) {
-    return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
-  };
-  auto lane_max = [&](const f32x16& v) {
-    const float m0 = mx3(v[0], v[1], v[2]);
-    const float m1 = mx3(v[3], v[4], v[5]);
-    const float m2 = mx3(v[6], v[7], v[8]);
-    const float m3 = mx3(v[9], v[10], v[11]);
-    const float m4 = mx3(v[12], v[13], v[14]);
-    const float m5 = mx3(m0, m1, v[15]);
-    return mx3(m2, m3, mx3(m4, m5, m5));
-  };
-  auto softmax = [&](f32x16 (&sc)[QB], bf16x8 (&pc)[QB][2]) {
-    float lt[QB];
-    bool raise = false;
-    if constexpr (kSumRow) {
+    };
+    auto pv = [&](const bf16x8 (&vf)[2][DB], const bf16x8 (&pb)[QB][2]) {
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) raise |= lane_max(sc[qb]) * scale_log2 > m_ref[qb] + kRaise;
-    }
-    if (!kSumRow || !__any(raise)) {
-      exp_pack(sc, pc, lt);
-      if constexpr (!kSumRow) {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) raise |= !(lt[qb] <= 0x1p64f);   // also true for inf / nan
-      }
-    }
-    if (__any(raise)) {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const float mh = lane_max(sc[qb]);
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mh), __float_as_uint(mh), false, false);
-        const float mt = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale_log2;
-        // integer reference: alpha is an exact power of two (0 on the first tile)
-        const float m_new = fmaxf(m_ref[qb], __builtin_ceilf(mt));
-        const float alpha = __builtin_amdgcn_exp2f(m_ref[qb] - m_new);
-        m_ref[qb] = m_new;
-        l_run[qb] *= alpha;
+      for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) o[qb][db][e] *= alpha;
+          for (int qb = 0; qb < QB; ++qb)
+            o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[h2][db], pb[qb][h2], o[qb][db], 0, 0, 0);
+    };
+    const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+    // p = 2^(s c - m) packed to bf16 for every score of the tile; the reference m of a query is an
+    // integer, raised only when the tile holds a score more than kRaise above it (so p < 2^kRaise
+    // and sums stay far from fp32 overflow).  Common path without a row max: for D = 64 / 128 the
+    // lane's partial sum of the tile's rounded weights (needed for l anyway) exceeds 2^kRaise
+    // whenever a weight does (the first tile, where m = -inf, gives inf); for D = 72 (the row sum
+    // comes from the P.V MFMA) a lane-local maximum of the raw scores is compared with the
+    // threshold.  Only then (rare after the first tile) does the wave take the row max across
+    // both halves of the query's keys, raise m to its ceiling and rescale O and l by the exact
+    // power of two 2^(m_old - m_new), and recompute the tile's weights.
+    constexpr float kRaise = 64.0f;
+    auto exp_pack = [&](f32x16 (&sc)[QB], bf16x8 (&pc)[QB][2], float (&lt)[QB]) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        uint32_t pk[8];
+        lt[qb] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const f32x2 pp = {__builtin_amdgcn_exp2f(fmaf(sc[qb][2 * e], scale_log2, -m_ref[qb])),
+                            __builtin_amdgcn_exp2f(fmaf(sc[qb][2 * e + 1], scale_log2, -m_ref[qb]))};
+          const bf16x2 pb2 = __builtin_convertvector(pp, bf16x2);
+          if constexpr (!kSumRow) lt[qb] = __builtin_amdgcn_fdot2_f32_bf16(pb2, ones, lt[qb], false);
+          pk[e] = __builtin_bit_cast(uint32_t, pb2);
+        }
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const u32x4 w = {pk[4 * h2], pk[4 * h2 + 1], pk[4 * h2 + 2], pk[4 * h2 + 3]};
+          pc[qb][h2] = __builtin_bit_cast(bf16x8, w);
+        }
       }
-      exp_pack(sc, pc, lt);
-    }
-    if constexpr (!kSumRow) {
+    };
+    auto mx3 = [](float a, float b, float c) {
+      return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+    };
+    auto lane_max = [&](const f32x16& v) {
+      const float m0 = mx3(v[0], v[1], v[2]);
+      const float m1 = mx3(v[3], v[4], v[5]);
+      const float m2 = mx3(v[6], v[7], v[8]);
+      const float m3 = mx3(v[9], v[10], v[11]);
+      const float m4 = mx3(v[12], v[13], v[14]);
+      const float m5 = mx3(m0, m1, v[15]);
+      return mx3(m2, m3, mx3(m4, m5, m5));
+    };
+    auto softmax = [&](f32x16 (&sc)[QB], bf16x8 (&pc)[QB][2]) {
+      float lt[QB];
+      bool raise = false;
+      if constexpr (kSumRow) {
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) l_run[qb] += lt[qb];
-    }
-  };
+        for (int qb = 0; qb < QB; ++qb) raise |= lane_max(sc[qb]) * scale_log2 > m_ref[qb] + kRaise;
+      }
+      if (!kSumRow || !__any(raise)) {
+        exp_pack(sc, pc, lt);
+        if constexpr (!kSumRow) {
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) raise |= !(lt[qb] <= 0x1p64f);   // also true for inf / nan
+        }
+      }
+      if (__any(raise)) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const float mh = lane_max(sc[qb]);
+          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mh), __float_as_uint(mh), false, false);
+          const float mt = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale_log2;
+          // integer reference: alpha is an exact power of two (0 on the first tile)
+          const float m_new = fmaxf(m_ref[qb], __builtin_ceilf(mt));
+          const float alpha = __builtin_amdgcn_exp2f(m_ref[qb] - m_new);
+          m_ref[qb] = m_new;
+          l_run[qb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) o[qb][db][e] *= alpha;
+        }
+        exp_pack(sc, pc, lt);
+      }
+      if constexpr (!kSumRow) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) l_run[qb] += lt[qb];
+      }
+    };
 
-  // Slots between barriers: group 0 runs the MFMA phase of tile t in slot 2(t - t_begin) and
-  // its softmax in the next slot; group 1 runs the same one slot later.  MFMA phase of t:
-  // P.V of tile t-1 (V operands already in registers) and the scores of tile t.  Softmax
-  // phase of t: P_t, then the V_t operands are read for the next MFMA phase.  Tile t sits in
-  // stage (t - t_begin) mod NSTAGE and is last read by group 1 in slot 2(t - t_begin) + 2,
-  // so group 0 issues tile t + NSTAGE - 2 at the start of its slot 2(t - t_begin), into
-  // the stage tile t - 2 used.
-  const int64_t nt = t_end - t_begin;
-  if (grp == 0) {
-    for (int64_t u = 0; u < nt && u < NSTAGE - 2; ++u) issue_tile(t_begin + u, (int)u);
-    const int64_t newer = (nt < NSTAGE - 2 ? nt : NSTAGE - 2) - 1;
-    wait_loads((int)newer);
-  }
-  barrier();
-  if (grp == 1) barrier();
-
-  // P.V of "tile t_begin - 1" multiplies zero weights, so every MFMA phase has the same shape
-  bf16x8 pb[QB][2];
-  bf16x8 vf[2][DB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) pb[qb][0][e] = pb[qb][1][e] = (bf16)0.f;
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) vf[0][db][e] = vf[1][db][e] = (bf16)0.f;
-  int st = 0;                         // stage of tile t
-  int st_issue = NSTAGE - 2;          // stage of tile t + NSTAGE - 2
-  auto iter = [&](int64_t t, bool partial) {
-    bf16x8 kf[KS];
-    read_k(st, kf);
-    f32x16 sc[QB];
-    pv(vf, pb);
-    if (grp == 0 && t + NSTAGE - 2 < t_end) issue_tile(t + NSTAGE - 2, st_issue);
-    scores(kf, sc);
-    barrier();
-    if (partial) mask_scores(t, sc);
-    softmax(sc, pb);
-    read_v(t, st, vf, partial);
+    // Slots between barriers: group 0 runs the MFMA phase of tile t in slot 2(t - t_begin) and
+    // its softmax in the next slot; group 1 runs the same one slot later.  MFMA phase of t:
+    // P.V of tile t-1 (V operands already in registers) and the scores of tile t.  Softmax
+    // phase of t: P_t, then the V_t operands are read for the next MFMA phase.  Tile t sits in
+    // stage (t - t_begin) mod NSTAGE and is last read by group 1 in slot 2(t - t_begin) + 2,
+    // so group 0 issues tile t + NSTAGE - 2 at the start of its slot 2(t - t_begin), into
+    // the stage tile t - 2 used.
+    const int64_t nt = t_end - t_begin;
     if (grp == 0) {
-      const int64_t last_issued = t + NSTAGE - 2 < t_end - 1 ? t + NSTAGE - 2 : t_end - 1;
-      const int64_t newer = last_issued - (t + 1);
-      wait_loads((int)(newer < 0 ? 0 : newer));
+      for (int64_t u = 0; u < nt && u < NSTAGE - 2; ++u) issue_tile(t_begin + u, (int)u);
+      const int64_t newer = (nt < NSTAGE - 2 ? nt : NSTAGE - 2) - 1;
+      wait_loads((int)newer);
     }
     barrier();
-    st = st + 1 == NSTAGE ? 0 : st + 1;
-    st_issue = st_issue + 1 == NSTAGE ? 0 : st_issue + 1;
-  };
-  // steady state: the tile NSTAGE - 2 ahead exists and is full, so every wait is the same.  For
-  // D = 72 and 128 the wavefront in its MFMA phase runs at a raised priority, so the SIMD's
-  // arbiter issues its MFMAs as soon as the matrix core frees up and fills the gaps with the
-  // other wavefront's softmax (measured: +5% at 262144 keys, d = 72; at d = 64, where the
-  // softmax phase is the longer one, it costs 3%)
-  constexpr bool kPingPongPrio = D != 64;
-  auto iter_steady = [&](int64_t t) {
-    bf16x8 kf[KS];
-    if constexpr (kPingPongPrio) __builtin_amdgcn_s_setprio(1);
-    read_k(st, kf);
-    f32x16 sc[QB];
-    pv(vf, pb);
-    if (grp == 0) issue_tile_full(t + NSTAGE - 2, st_issue);
-    scores(kf, sc);
-    barrier();
-    if constexpr (kPingPongPrio) __builtin_amdgcn_s_setprio(0);
-    softmax(sc, pb);
-    read_v(t, st, vf, false);
-    if (grp == 0) wait_loads_const();
-    barrier();
-    st = st + 1 == NSTAGE ? 0 : st + 1;
-    st_issue = st_issue + 1 == NSTAGE ? 0 : st_issue + 1;
-  };
-  const int64_t t_full = t_end * TK > S ? t_end - 1 : t_end;
-  // the last full tile t can run steady if t + NSTAGE - 2 is a full tile below t_end
-  const int64_t t_steady_end = t_full - (NSTAGE - 2) > t_begin ? t_full - (NSTAGE - 2) : t_begin;
-  int64_t t = t_begin;
-  for (; t < t_steady_end; ++t) iter_steady(t);
-  for (; t < t_full; ++t) iter(t, false);
-  if (t_full < t_end) iter(t_full, true);
-  if (nt > 0) pv(vf, pb);
-  if (grp == 0) barrier();
+    if (grp == 1) barrier();
 
-  if constexpr (kSumRow) {
+    // P.V of "tile t_begin - 1" multiplies zero weights, so every MFMA phase has the same shape
+    bf16x8 pb[QB][2];
+    bf16x8 vf[2][DB];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const float sum_row = o[qb][DB - 1][kSumIdx];
-      l_run[qb] = hi == 0 ? sum_row : 0.f;
-    }
-  }
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pb[qb][0][e] = pb[qb][1][e] = (bf16)0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vf[0][db][e] = vf[1][db][e] = (bf16)0.f;
+    int st = 0;                         // stage of tile t
+    int st_issue = NSTAGE - 2;          // stage of tile t + NSTAGE - 2
+    auto iter = [&](int64_t t, bool partial) {
+      bf16x8 kf[KS];
+      read_k(st, kf);
+      f32x16 sc[QB];
+      pv(vf, pb);
+      if (grp == 0 && t + NSTAGE - 2 < t_end) issue_tile(t + NSTAGE - 2, st_issue);
+      scores(kf, sc);
+      barrier();
+      if (partial) mask_scores(t, sc);
+      softmax(sc, pb);
+      read_v(t, st, vf, partial);
+      if (grp == 0) {
+        const int64_t last_issued = t + NSTAGE - 2 < t_end - 1 ? t + NSTAGE - 2 : t_end - 1;
+        const int64_t newer = last_issued - (t + 1);
+        wait_loads((int)(newer < 0 ? 0 : newer));
+      }
+      barrier();
+      st = st + 1 == NSTAGE ? 0 : st + 1;
+      st_issue = st_issue + 1 == NSTAGE ? 0 : st_issue + 1;
+    };
+    // steady state: the tile NSTAGE - 2 ahead exists and is full, so every wait is the same.  For
+    // D = 72 and 128 the wavefront in its MFMA phase runs at a raised priority, so the SIMD's
+    // arbiter issues its MFMAs as soon as the matrix core frees up and fills the gaps with the
+    // other wavefront's softmax (measured: +5% at 262144 keys, d = 72; at d = 64, where the
+    // softmax phase is the longer one, it costs 3%)
+    constexpr bool kPingPongPrio = D != 64;
+    // at D = 128 the V operand reads go out before the softmax, so their LDS latency hides behind
+    // its exponentials (measured: -7% time at 2048 x 16896 keys, 24 heads; at D = 72 and 64 the
+    // extra live registers cost 1-2%)
+    constexpr bool kEarlyV = D == 128;
+    auto iter_steady = [&](int64_t t) {
+      bf16x8 kf[KS];
+      if constexpr (kPingPongPrio) __builtin_amdgcn_s_setprio(1);
+      read_k(st, kf);
+      f32x16 sc[QB];
+      pv(vf, pb);
+      if (grp == 0) issue_tile_full(t + NSTAGE - 2, st_issue);
+      scores(kf, sc);
+      barrier();
+      if constexpr (kPingPongPrio) __builtin_amdgcn_s_setprio(0);
+      if constexpr (kEarlyV) read_v(t, st, vf, false);
+      softmax(sc, pb);
+      if constexpr (!kEarlyV) read_v(t, st, vf, false);
+      if (grp == 0) wait_loads_const();
+      barrier();
+      st = st + 1 == NSTAGE ? 0 : st + 1;
+      st_issue = st_issue + 1 == NSTAGE ? 0 : st_issue + 1;
+    };
+    const int64_t t_full = t_end * TK > S ? t_end - 1 : t_end;
+    // the last full tile t can run steady if t + NSTAGE - 2 is a full tile below t_end
+    const int64_t t_steady_end = t_full - (NSTAGE - 2) > t_begin ? t_full - (NSTAGE - 2) : t_begin;
+    int64_t t = t_begin;
+    for (; t < t_steady_end; ++t) iter_steady(t);
+    for (; t < t_full; ++t) iter(t, false);
+    if (t_full < t_end) iter(t_full, true);
+    if (nt > 0) pv(vf, pb);
+    if (grp == 0) barrier();
 
+    if constexpr (kSumRow) {
 #pragma unroll
-  // Whole key range: O = acc / l in bf16.  One slice of a split range: the slice's own
-  // normalised result acc_s / l_s in fp32, plus (m_s, l_s) for the merge.
-  for (int qb = 0; qb < QB; ++qb) {
-    const float l_tot = l_run[qb] + __shfl_xor(l_run[qb], 32, 64);
-    if (!q_ok[qb]) continue;
-    const float inv = 1.0f / l_tot;
-    if (n_split == 1) {
-      bf16* dst = O + q_row[qb] * ldo + col0;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int d = db * 32 + 8 * g + 4 * hi;
-          if (d < D) {
-            bf16x4 ov = {(bf16)(o[qb][db][4 * g + 0] * inv), (bf16)(o[qb][db][4 * g + 1] * inv),
-                         (bf16)(o[qb][db][4 * g + 2] * inv), (bf16)(o[qb][db][4 * g + 3] * inv)};
-            *reinterpret_cast<bf16x4*>(dst + d) = ov;
-          }
-        }
-    } else {
-      float* dst = part_o + ((int64_t)split * rows + q_row[qb]) * hidden + col0;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int d = db * 32 + 8 * g + 4 * hi;
-          if (d < D)
-            *reinterpret_cast<float4*>(dst + d) = make_float4(o[qb][db][4 * g + 0] * inv, o[qb][db][4 * g + 1] * inv,
-                                                              o[qb][db][4 * g + 2] * inv, o[qb][db][4 * g + 3] * inv);
-        }
-    }
-    if (n_split > 1) {
-      if (hi == 0) {
-        const int64_t H = hidden / D;
-        reinterpret_cast<float2*>(part_ml)[((int64_t)split * H + head) * rows + q_row[qb]] =
-            make_float2(m_ref[qb], l_tot);
+      for (int qb = 0; qb < QB; ++qb) {
+        const float sum_row = o[qb][DB - 1][kSumIdx];
+        l_run[qb] = hi == 0 ? sum_row : 0.f;
       }
     }
-  }
+
+#pragma unroll
+    // Whole key range: O = acc / l in bf16.  One slice of a split range: the slice's own
+    // normalised result acc_s / l_s in fp32, plus (m_s, l_s) for the merge.
+    for (int qb = 0; qb < QB; ++qb) {
+      const float l_tot = l_run[qb] + __shfl_xor(l_run[qb], 32, 64);
+      if (!q_ok[qb]) continue;
+      const float inv = 1.0f / l_tot;
+      if (whole) {
+        bf16* dst = O + q_row[qb] * ldo + col0;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int d = db * 32 + 8 * g + 4 * hi;
+            if (d < D) {
+              bf16x4 ov = {(bf16)(o[qb][db][4 * g + 0] * inv), (bf16)(o[qb][db][4 * g + 1] * inv),
+                           (bf16)(o[qb][db][4 * g + 2] * inv), (bf16)(o[qb][db][4 * g + 3] * inv)};
+              *reinterpret_cast<bf16x4*>(dst + d) = ov;
+            }
+          }
+      } else {
+        float* dst = part_o + (slot * rows + q_row[qb]) * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int d = db * 32 + 8 * g + 4 * hi;
+            if (d < D)
+              *reinterpret_cast<float4*>(dst + d) = make_float4(o[qb][db][4 * g + 0] * inv, o[qb][db][4 * g + 1] * inv,
+                                                                o[qb][db][4 * g + 2] * inv, o[qb][db][4 * g + 3] * inv);
+          }
+      }
+      if (!whole && hi == 0)
+        reinterpret_cast<float2*>(part_ml)[slot * rows + q_row[qb]] = make_float2(m_ref[qb], l_tot);
+    }
+  }   // pieces
 }
 
-// Merge the per-split partial results.  Slice s holds x_s = acc_s / l_s (fp32) with its
-// integer reference m_s and weight sum l_s, so O = sum_s w_s x_s / sum_s w_s with
-// w_s = 2^(m_s - M) l_s (M = max_s m_s, 2^(m_s - M) exact): a convex combination of the
-// slices' results.
-// One thread per (row, head, 8 columns).  The loop over slices is unrolled to the largest
-// split count (indices past n_split clamped, their terms skipped), so every load of a thread
-// is issued before the first is used.
+// Merge the partial results of the pieces of each (query row, head).  Piece k holds
+// x_k = acc_k / l_k (fp32) with its integer reference m_k and weight sum l_k, so
+// O = sum_k w_k x_k / sum_k w_k with w_k = 2^(m_k - M) l_k (M = max_k m_k, 2^(m_k - M) exact):
+// a convex combination of the pieces' results.  The pieces of head h sit in slots
+// h + k * H, k < n_split (fixed split), or h + g for the groups g whose stretches of the
+// (head, key tile) line meet head h (stream-K; a head inside one stretch was written whole).
+// One thread per (row, head, 8 columns).  The loop over pieces is unrolled to the largest
+// piece count (indices past the count clamped, their terms skipped), so every load of a
+// thread is issued before the first is used.
 template <int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ part_o,
                                                            const float* __restrict__ part_ml, int n_split,
-                                                           int64_t rows, int H, bf16* __restrict__ O,
-                                                           int64_t ldo) {
+                                                           int64_t group_tiles, int64_t ntiles, int64_t rows,
+                                                           int H, bf16* __restrict__ O, int64_t ldo) {
   constexpr int NC = D / 8;
   const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (id >= rows * H * NC) return;
@@ -564,28 +604,41 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
   const int64_t rest = id / NC;
   const int head = (int)(rest % H);
   const int64_t row = rest / H;
-  const int64_t hidden = (int64_t)H * D;
+  int count;
+  int64_t base, stride;
+  if (group_tiles > 0) {
+    const int64_t g0 = (int64_t)head * ntiles / group_tiles;
+    const int64_t g1 = ((int64_t)head * ntiles + ntiles - 1) / group_tiles;
+    if (g0 == g1) return;
+    count = (int)(g1 - g0 + 1);
+    base = head + g0;
+    stride = 1;
+  } else {
+    count = n_split;
+    base = head;
+    stride = H;
+  }
   float m[kMaxAttnSplit], l[kMaxAttnSplit];
   float4 xa[kMaxAttnSplit], xb[kMaxAttnSplit];
 #pragma unroll
   for (int sp = 0; sp < kMaxAttnSplit; ++sp) {
-    const int64_t sc = sp < n_split ? sp : n_split - 1;   // slices past n_split re-read the last (unused)
-    const float2 ml = reinterpret_cast<const float2*>(part_ml)[(sc * H + head) * rows + row];
+    const int64_t sc = base + (sp < count ? sp : count - 1) * stride;   // past the count: re-read the last (unused)
+    const float2 ml = reinterpret_cast<const float2*>(part_ml)[sc * rows + row];
     m[sp] = ml.x;
     l[sp] = ml.y;
-    const float4* src = reinterpret_cast<const float4*>(part_o + (sc * rows + row) * hidden + (int64_t)head * D + chunk * 8);
+    const float4* src = reinterpret_cast<const float4*>(part_o + (sc * rows + row) * D + chunk * 8);
     xa[sp] = src[0];
     xb[sp] = src[1];
   }
   float M = m[0];
 #pragma unroll
   for (int sp = 1; sp < kMaxAttnSplit; ++sp)
-    if (sp < n_split) M = fmaxf(M, m[sp]);
+    if (sp < count) M = fmaxf(M, m[sp]);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
 #pragma unroll
   for (int sp = 0; sp < kMaxAttnSplit; ++sp) {
-    if (sp < n_split) {
+    if (sp < count) {
       const float w = __builtin_amdgcn_exp2f(m[sp] - M) * l[sp];
       wsum += w;
       acc[0] = fmaf(w, xa[sp].x, acc[0]);
@@ -688,20 +741,66 @@ static int attn_slots() {
   return cached[dev];
 }
 
-// Number of key-range splits: the smallest that minimises the estimated time
-// ceil(wg * s / slots) / s, limited so every split keeps at least 8 key tiles and the
-// partial results fit in the workspace.
-static int choose_split(int64_t wg, int slots, int64_t ntiles, int64_t rows, int64_t hidden, int heads,
-                        size_t ws_bytes) {
-  int best = 1;
-  double best_cost = (double)((wg + slots - 1) / slots);
+// How one bf16 launch divides its work (see attn_bf16_kernel): the fixed split of every
+// (query tile, head) pair's key range into n_split equal parts, or the grouped stream-K
+// schedule with group_tiles key tiles per group.  The choice minimises an estimate of the
+// busiest workgroup slot's time in key tiles: the tiles it runs plus kPieceTiles for each
+// piece (Q load, ring fill, result write), plus 3% for the merge pass when there are
+// partials, among the schedules whose partials fit in ws_bytes.
+struct AttnPlan {
+  int n_split = 1;            // fixed split: parts of each key range (1: no partials)
+  int tps = 0;                // fixed split: key tiles per part
+  int64_t group_tiles = 0;    // > 0: grouped stream-K, key tiles per group
+  int64_t grid = 0;           // workgroups
+  int64_t slots = 0;          // partial slots (0: none)
+};
+constexpr double kPieceTiles = 16.0;
+
+static size_t partial_bytes(int64_t slots, int64_t rows, int head_dim) {
+  return (size_t)slots * rows * ((size_t)head_dim * sizeof(float) + 2 * sizeof(float));
+}
+
+static AttnPlan plan_attention(int64_t n_qtiles, int heads, int64_t ntiles, int64_t all_rows, int head_dim,
+                               int slots, size_t ws_bytes) {
+  AttnPlan best;
+  const int64_t wg = n_qtiles * heads;
+  best.tps = (int)ntiles;
+  best.grid = wg;
+  double best_cost = (double)((wg + slots - 1) / slots) * ((double)ntiles + kPieceTiles);
+  // fixed split: every part keeps at least 8 key tiles
   for (int sp = 2; sp <= kMaxAttnSplit; ++sp) {
     if (ntiles < 8LL * sp) break;
-    if (attention_workspace_bytes(rows, hidden, heads, sp) > ws_bytes) break;
-    const double cost = (double)((wg * sp + slots - 1) / slots) / sp * 1.03;   // 3% for the merge pass
+    const int tps = (int)((ntiles + sp - 1) / sp);
+    const int used = (int)((ntiles + tps - 1) / tps);
+    if (partial_bytes((int64_t)used * heads, all_rows, head_dim) > ws_bytes) break;
+    const double cost = (double)((wg * used + slots - 1) / slots) * (tps + kPieceTiles) * 1.03;
     if (cost < best_cost - 1e-9) {
       best_cost = cost;
-      best = sp;
+      best.n_split = used;
+      best.tps = tps;
+      best.grid = wg * used;
+      best.slots = (int64_t)used * heads;
+    }
+  }
+  // grouped stream-K: one group of n_qtiles workgroups per slot group, one round
+  const int64_t groups = slots / n_qtiles;
+  if (groups >= 2) {
+    const int64_t line = (int64_t)heads * ntiles;
+    const int64_t gt = (line + groups - 1) / groups;
+    const int64_t used = (line + gt - 1) / gt;
+    const int64_t pieces = (gt + ntiles - 1) / ntiles + 1;        // heads one stretch can meet
+    const int64_t per_head = (ntiles + gt - 1) / gt + 1;          // stretches one head can meet
+    const int64_t nslots = heads + used - 1;
+    if (gt >= 8 && per_head <= kMaxAttnSplit && partial_bytes(nslots, all_rows, head_dim) <= ws_bytes) {
+      const double cost = ((double)gt + kPieceTiles * (double)pieces) * 1.03;
+      if (cost < best_cost - 1e-9) {
+        best_cost = cost;
+        best.n_split = 1;
+        best.tps = 0;
+        best.group_tiles = gt;
+        best.grid = used * n_qtiles;
+        best.slots = nslots;
+      }
     }
   }
   return best;
@@ -709,6 +808,14 @@ static int choose_split(int64_t wg, int slots, int64_t ntiles, int64_t rows, int
 
 // `rows` query rows per sample, `batch` samples: sample b's query rows are rows b*rows ..
 // of Q and O, its K / V buffers start b * kv_stride elements after sample 0's.
+template <int D>
+static AttnPlan plan_attn_d(int64_t rows, int64_t seq_kv, int heads, int64_t batch, size_t ws_bytes) {
+  constexpr int BQ = kAttnWaves * 32 * AttnCfg<D>::QB;
+  const int64_t n_qtiles = batch * ((rows + BQ - 1) / BQ);
+  const int64_t ntiles = (seq_kv + kTileKeys - 1) / kTileKeys;
+  return plan_attention(n_qtiles, heads, ntiles, batch * rows, D, attn_slots<D>(), ws_bytes);
+}
+
 template <int D>
 static hipError_t launch_attn_d(const void* q, int64_t ldq, const void* k, int64_t ldk, const void* v, int64_t ldv,
                                 int64_t hidden, int64_t seq_kv, int64_t rows, int heads, void* o, int64_t ldo,
@@ -721,22 +828,22 @@ static hipError_t launch_attn_d(const void* q, int64_t ldq, const void* k, int64
     const int per_grp = (int)((rows + BQ - 1) / BQ);
     const int n_qtiles = (int)(batch * per_grp);
     const int64_t ntiles = (seq_kv + kTileKeys - 1) / kTileKeys;
-    const int64_t wg = (int64_t)n_qtiles * heads;
-    const int n_split = ws ? choose_split(wg, attn_slots<D>(), ntiles, all_rows, hidden, heads, ws_bytes) : 1;
-    const int tps = (int)((ntiles + n_split - 1) / n_split);
-    const int n_used = (int)((ntiles + tps - 1) / tps);      // every split gets at least one tile
+    const AttnPlan plan = plan_attn_d<D>(rows, seq_kv, heads, batch, ws ? ws_bytes : 0);
+    if (plan.slots && partial_bytes(plan.slots, all_rows, D) > ws_bytes) return hipErrorInvalidValue;
     const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
-    // workspace: fp32 slice results [n_used][all_rows][hidden], then fp32 (m, l) pairs [n_used][heads][all_rows]
-    float* part_o = static_cast<float*>(ws);
-    float* part_ml = part_o ? part_o + (size_t)n_used * all_rows * hidden : nullptr;
-    hipLaunchKernelGGL((attn_bf16_kernel<D, QB>), dim3((unsigned)(wg * n_used)), dim3(64 * kAttnWaves), 0, s,
+    // workspace: fp32 piece results [slots][all_rows][D], then fp32 (m, l) pairs [slots][all_rows]
+    float* part_o = plan.slots ? static_cast<float*>(ws) : nullptr;
+    float* part_ml = part_o ? part_o + (size_t)plan.slots * all_rows * D : nullptr;
+    hipLaunchKernelGGL((attn_bf16_kernel<D, QB>), dim3((unsigned)plan.grid), dim3(64 * kAttnWaves), 0, s,
                        static_cast<const bf16*>(q), ldq, static_cast<const bf16*>(k), ldk,
-                       static_cast<const bf16*>(v), hidden, seq_kv, all_rows, n_qtiles, n_used, tps,
-                       static_cast<bf16*>(o), ldo, part_o, part_ml, scale_log2, rows, per_grp, kv_stride);
-    if (n_used > 1) {
+                       static_cast<const bf16*>(v), hidden, seq_kv, all_rows, n_qtiles, plan.n_split, plan.tps,
+                       plan.group_tiles, static_cast<bf16*>(o), ldo, part_o, part_ml, scale_log2, rows, per_grp,
+                       kv_stride);
+    if (plan.slots) {
       const int64_t units = all_rows * heads * (D / 8);
       hipLaunchKernelGGL(attn_combine_kernel<D>, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, s, part_o,
-                         part_ml, n_used, all_rows, heads, static_cast<bf16*>(o), ldo);
+                         part_ml, plan.n_split, plan.group_tiles, ntiles, all_rows, heads,
+                         static_cast<bf16*>(o), ldo);
     }
   } else {
     const int n_qtiles = (int)((rows + 63) / 64);
@@ -750,23 +857,18 @@ static hipError_t launch_attn_d(const void* q, int64_t ldq, const void* k, int64
 }
 
 template <int D>
-static size_t split_bytes_d(int64_t rows, int64_t seq_kv, int64_t hidden, int heads, int64_t batch) {
-  constexpr int BQ = kAttnWaves * 32 * AttnCfg<D>::QB;
-  const int64_t n_qtiles = batch * ((rows + BQ - 1) / BQ);
-  const int64_t ntiles = (seq_kv + kTileKeys - 1) / kTileKeys;
-  const int n_split = choose_split(n_qtiles * heads, attn_slots<D>(), ntiles, batch * rows, hidden, heads, (size_t)-1);
-  const int tps = (int)((ntiles + n_split - 1) / n_split);
-  const int n_used = (int)((ntiles + tps - 1) / tps);
-  return attention_workspace_bytes(batch * rows, hidden, heads, n_used);
+static size_t split_bytes_d(int64_t rows, int64_t seq_kv, int heads, int64_t batch) {
+  const AttnPlan plan = plan_attn_d<D>(rows, seq_kv, heads, batch, attention_workspace_bytes(batch * rows, (int64_t)heads * D, heads, kMaxAttnSplit));
+  return partial_bytes(plan.slots, batch * rows, D);
 }
 
 size_t attention_split_workspace_bytes(int64_t rows, int64_t seq_kv, int64_t hidden, int heads, int head_dim,
                                        int dtype, int64_t batch) {
   if (dtype != kDtypeBF16 || rows <= 0 || batch <= 0) return 0;
   switch (head_dim) {
-    case 64: return split_bytes_d<64>(rows, seq_kv, hidden, heads, batch);
-    case 72: return split_bytes_d<72>(rows, seq_kv, hidden, heads, batch);
-    case 128: return split_bytes_d<128>(rows, seq_kv, hidden, heads, batch);
+    case 64: return split_bytes_d<64>(rows, seq_kv, heads, batch);
+    case 72: return split_bytes_d<72>(rows, seq_kv, heads, batch);
+    case 128: return split_bytes_d<128>(rows, seq_kv, heads, batch);
     default: return 0;
   }
 }

@@ -342,6 +342,50 @@ def test_attention_bf16_rescale_in_late_tiles(D, split):
     np.testing.assert_allclose(got[:, 2 * D:], np.broadcast_to(V[S - 1, 2 * D:], (rows, D)), atol=1e-2)
 
 
+# Shapes whose work a 256-CU MI355X runs on the grouped stream-K schedule (each group of
+# workgroups, one per query tile, takes an equal stretch of the (head, key tile) line, so
+# stretches start and end inside heads and run over head boundaries): the key tiles per
+# stretch are 59 (d = 64, 157 tiles per head), 54 (d = 72, 94 tiles) and 45 (d = 128, 129
+# tiles), never a multiple of the tiles per head; every S ends in a partial tile.
+SK_CASES = [(64, 24, 5000, 1664), (72, 24, 3000, 2688), (128, 8, 4100, 2688)]
+
+
+@pytest.mark.parametrize("D,H,S,rows", SK_CASES)
+def test_attention_bf16_stream_k(D, H, S, rows):
+    """Key ranges cut into pieces that the merge pass recombines, with row maxima that move
+    between pieces: head 0 has a key of logit +50 in the last, partial tile, head 1 one of +40
+    a third of the way in and one of +60 two thirds of the way in (different pieces for the
+    queries of every query tile), the other heads random logits.  Checked on 64 sampled query
+    rows against the bf16p and the exact oracle."""
+    torch = torch_cuda()
+    h = H * D
+    seed = 9100 + D
+    q = synth.randn((rows, h), seed, std=1.0)
+    K = synth.randn((S, h), seed + 1, std=1.0)
+    V = synth.randn((S, h), seed + 2, std=1.0, bf16=True)
+    sq = math.sqrt(D)
+    q[:, 0] = 8.0
+    K[S - 1, 0] = 50.0 * sq / 8.0
+    q[:, D] = 8.0
+    K[S // 3, D] = 40.0 * sq / 8.0
+    K[2 * S // 3, D] = 60.0 * sq / 8.0
+    q = synth.to_bf16_values(q).astype(np.float64)
+    K = synth.to_bf16_values(K).astype(np.float64)
+    kt, vt, kv = _kv_bf16(torch, K, V)
+    o = torch.empty((rows, h), dtype=torch.bfloat16, device="cuda")
+    print(f"[attn] stream-K D={D} H={H} S={S} rows={rows}", flush=True)
+    B.pf_attention(dev(torch, q, torch.bfloat16), kv, S, rows, H, D, o, workspace=B.attention_workspace(rows, H, D))
+    rng = np.random.default_rng(seed)
+    sel = np.unique(np.concatenate([[0, 1, 511, 512, rows - 1], rng.choice(rows, 59, replace=False)]))
+    got = host(o)[sel]
+    want_p = ref.attention(q[sel], K, V, H, D, round_p=True)
+    want = ref.attention(q[sel], K, V, H, D)
+    assert_close(got, ref.bf16_round(want_p), f"attention stream-K D={D} vs bf16p")
+    assert_close(got, want, f"attention stream-K D={D} vs exact")
+    np.testing.assert_allclose(got[:, :D], np.broadcast_to(V[S - 1, :D], (len(sel), D)), atol=1e-2)
+    np.testing.assert_allclose(got[:, D:2 * D], np.broadcast_to(V[2 * S // 3, D:2 * D], (len(sel), D)), atol=1e-2)
+
+
 @pytest.mark.parametrize("D,S,rows", [(64, 256, 64), (64, 100, 33), (128, 70, 5)])
 def test_attention_fp32(D, S, rows):
     torch = torch_cuda()

@@ -38,10 +38,10 @@ def test_attention_noalloc_matches_workspace_entry_point(first, second):
 
 
 def test_attention_noalloc_rejects_splits_beyond_the_scratch():
-    """6144 query rows x 24 heads x 128 split 4 ways need 302 MB of partials: rejected before any
-    launch (the output keeps its contents)."""
+    """6144 query rows x 24 heads x 128 over 32768 keys, split 4 ways, need 307 MB of partials:
+    rejected before any launch (the output keeps its contents)."""
     torch = torch_cuda()
-    rows, S, H, D = 6144, 8192, 24, 128
+    rows, S, H, D = 6144, 32768, 24, 128
     h = H * D
     q = torch.zeros((rows, h), dtype=torch.bfloat16, device="cuda")
     k = torch.zeros((S, h), dtype=torch.bfloat16, device="cuda")

@@ -71,7 +71,9 @@ template <> struct AttnCfg<128> { static constexpr int QB = 1; };
 constexpr int kAttnWaves = 8;
 constexpr int kAttnStages = 5;
 
-template <int D, int QB>
+// SK: the grouped stream-K schedule (a workgroup may run several pieces); otherwise every
+// workgroup runs exactly one piece and the kernel has no piece loop.
+template <int D, int QB, bool SK>
 __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const bf16* __restrict__ Q, int64_t ldq,
                                                          const bf16* __restrict__ Kb, int64_t ldk,
                                                          const bf16* __restrict__ Vb, int64_t hidden,
@@ -96,11 +98,8 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const bf16* __restric
   static_assert(NSTAGE >= 3 && NSTAGE <= 8, "stage ring");
   __shared__ __attribute__((aligned(16))) uint4 lds[NSTAGE][2 * KUP];
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wavefront-uniform (scalar)
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);   // wavefront-uniform (scalar)
   const int grp = wave >> 2, wl = wave & 3;
-  const int l32 = lane & 31, hi = lane >> 5;
 
   // Samples of a batch: query rows [g * grp_rows, (g+1) * grp_rows) of Q / O and the partials
   // belong to sample g, whose K / V buffers start g * kv_stride elements on; each sample has
@@ -115,7 +114,9 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const bf16* __restric
   //     key tiles at the same time (shared in L2), and a stretch may run over several heads.
   // Each head met by a stretch is one piece.  A piece covering all of a head's key tiles writes
   // O directly; any other piece writes its normalised fp32 result and (m, l) into partial slot
-  // split * H + head (fixed split) or head + gi (stream-K), merged by attn_combine_kernel.
+  // split * H + head (fixed split) or head + gi (stream-K), merged by attn_combine_kernel.  The
+  // fp32 results of the fixed split lie as [split][row][hidden] (a row's heads side by side, as
+  // the merge reads them), those of stream-K as [slot][row][D].
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
   const int qt_all = lid % n_qtiles;
   const int gi = lid / n_qtiles;
@@ -136,15 +137,6 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const bf16* __restric
     pos_end = pos + tiles_per_split < (head0 + 1) * ntiles ? pos + tiles_per_split : (head0 + 1) * ntiles;
   }
 
-  int64_t q_row[QB];   // row of Q / O / the partials
-  bool q_ok[QB];       // inside this sample's rows
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int64_t local = (int64_t)qt * BQ + (wave * QB + qb) * 32 + l32;
-    q_ok[qb] = local < grp_rows;
-    q_row[qb] = row_base + local;
-  }
-
   auto barrier_all = [] {
     __builtin_amdgcn_sched_barrier(0);
     lds_barrier();
@@ -160,6 +152,22 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const bf16* __restric
     const int64_t col0 = head * D;
     // a later piece reuses the LDS ring: every wavefront is past its last read of the previous one
     if (!first) barrier_all();
+    // With several pieces at head_dim 72, lane-dependent values are derived anew in every piece
+    // from a copy of the thread id the compiler cannot see through, so none of them is hoisted
+    // out of the piece loop and kept live across the key loop: hoisted, they push that kernel
+    // past 256 registers (spills).  At 64 and 128 the hoisted form fits and measured faster.
+    int tid = (int)threadIdx.x;
+    if constexpr (SK && D == 72) asm volatile("" : "+v"(tid));
+    const int lane = tid & 63;
+    const int l32 = lane & 31, hi = lane >> 5;
+    int64_t q_row[QB];   // row of Q / O / the partials
+    bool q_ok[QB];       // inside this sample's rows
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int64_t local = (int64_t)qt * BQ + (wave * QB + qb) * 32 + l32;
+      q_ok[qb] = local < grp_rows;
+      q_row[qb] = row_base + local;
+    }
 
     bf16x8 qf[QB][KS];
 #pragma unroll
@@ -566,7 +574,8 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const bf16* __restric
             }
           }
       } else {
-        float* dst = part_o + (slot * rows + q_row[qb]) * D;
+        float* dst = part_o + (group_tiles > 0 ? (slot * rows + q_row[qb]) * D
+                                               : ((int64_t)(gi % n_split) * rows + q_row[qb]) * hidden + col0);
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -580,6 +589,7 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const bf16* __restric
       if (!whole && hi == 0)
         reinterpret_cast<float2*>(part_ml)[slot * rows + q_row[qb]] = make_float2(m_ref[qb], l_tot);
     }
+    if constexpr (!SK) break;   // one piece
   }   // pieces
 }
 
@@ -587,8 +597,9 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const bf16* __restric
 // x_k = acc_k / l_k (fp32) with its integer reference m_k and weight sum l_k, so
 // O = sum_k w_k x_k / sum_k w_k with w_k = 2^(m_k - M) l_k (M = max_k m_k, 2^(m_k - M) exact):
 // a convex combination of the pieces' results.  The pieces of head h sit in slots
-// h + k * H, k < n_split (fixed split), or h + g for the groups g whose stretches of the
-// (head, key tile) line meet head h (stream-K; a head inside one stretch was written whole).
+// h + k * H, k < n_split (fixed split: results [k][row][hidden]), or h + g for the groups g
+// whose stretches of the (head, key tile) line meet head h (stream-K: results [slot][row][D];
+// a head inside one stretch was written whole).
 // One thread per (row, head, 8 columns).  The loop over pieces is unrolled to the largest
 // piece count (indices past the count clamped, their terms skipped), so every load of a
 // thread is issued before the first is used.
@@ -626,7 +637,10 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
     const float2 ml = reinterpret_cast<const float2*>(part_ml)[sc * rows + row];
     m[sp] = ml.x;
     l[sp] = ml.y;
-    const float4* src = reinterpret_cast<const float4*>(part_o + (sc * rows + row) * D + chunk * 8);
+    const int64_t k = sp < count ? sp : count - 1;
+    const float4* src = reinterpret_cast<const float4*>(
+        part_o + (group_tiles > 0 ? (sc * rows + row) * D : (k * rows + row) * (int64_t)H * D + (int64_t)head * D) +
+        chunk * 8);
     xa[sp] = src[0];
     xb[sp] = src[1];
   }
@@ -732,7 +746,7 @@ static int attn_slots() {
   if (cached[dev] == 0) {
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_bf16_kernel<D, AttnCfg<D>::QB>, 64 * kAttnWaves,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_bf16_kernel<D, AttnCfg<D>::QB, false>, 64 * kAttnWaves,
                                                      0) != hipSuccess || per_cu <= 0)
       per_cu = 1;
     (void)hipGetLastError();
@@ -831,10 +845,11 @@ static hipError_t launch_attn_d(const void* q, int64_t ldq, const void* k, int64
     const AttnPlan plan = plan_attn_d<D>(rows, seq_kv, heads, batch, ws ? ws_bytes : 0);
     if (plan.slots && partial_bytes(plan.slots, all_rows, D) > ws_bytes) return hipErrorInvalidValue;
     const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
-    // workspace: fp32 piece results [slots][all_rows][D], then fp32 (m, l) pairs [slots][all_rows]
+    // workspace: fp32 piece results (slots x all_rows x D floats), then fp32 (m, l) pairs [slots][all_rows]
     float* part_o = plan.slots ? static_cast<float*>(ws) : nullptr;
     float* part_ml = part_o ? part_o + (size_t)plan.slots * all_rows * D : nullptr;
-    hipLaunchKernelGGL((attn_bf16_kernel<D, QB>), dim3((unsigned)plan.grid), dim3(64 * kAttnWaves), 0, s,
+    auto kernel = plan.group_tiles > 0 ? attn_bf16_kernel<D, QB, true> : attn_bf16_kernel<D, QB, false>;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)plan.grid), dim3(64 * kAttnWaves), 0, s,
                        static_cast<const bf16*>(q), ldq, static_cast<const bf16*>(k), ldk,
                        static_cast<const bf16*>(v), hidden, seq_kv, all_rows, n_qtiles, plan.n_split, plan.tps,
                        plan.group_tiles, static_cast<bf16*>(o), ldo, part_o, part_ml, scale_log2, rows, per_grp,

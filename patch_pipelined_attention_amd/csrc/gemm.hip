@@ -9,7 +9,10 @@
 //
 // Tiles: 128 x 128 with a 2-stage ring, two workgroups per CU.  Grids too small to fill the
 // GPU split k: every slice writes its fp32 partial tile and a reduce pass sums the slices in
-// order (deterministic) and applies the epilogue.  (A last-arriving-slice merge inside the
+// order (deterministic) and applies the epilogue.  A grid whose last round would run part
+// full splits only the tiles of that round ("remainder split"): the full rounds run whole
+// tiles, the remaining tiles run as k slices that fill one round, and a reduce pass over
+// those tiles alone finishes them.  (A last-arriving-slice merge inside the
 // GEMM measured slower on MI355X: the partials cross XCDs, whose L2s are not coherent, so
 // they must be written through and read back from the device-coherent level, a longer
 // latency chain than one more launch.)
@@ -165,9 +168,41 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(const float* __restric
   gemm_store4<EPI>(s.x, s.y, s.z, s.w, m, f, bias, C, ldc, gate, sp, rg);
 }
 
+// Reduce pass of a remainder split: the k slices of tiles n_whole.. (tile order of
+// gemm_tile_of), one thread per 4 consecutive outputs of a tile row; slices summed in order.
+template <int EPI>
+__global__ __launch_bounds__(256) void gemm_reduce_tiles_kernel(const float* __restrict__ part, int n_split,
+                                                                int64_t n_whole, int64_t n_tiles, int tiles_n,
+                                                                int64_t M, int64_t N, const float* __restrict__ bias,
+                                                                void* __restrict__ C, int64_t ldc,
+                                                                const float* __restrict__ gate, QkvSplice sp,
+                                                                RowGroups rg) {
+  constexpr int T = 128;
+  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (id >= (n_tiles - n_whole) * T * (T / 4)) return;
+  const int64_t tile = n_whole + id / (T * (T / 4));
+  const int within = (int)(id % (T * (T / 4)));
+  int64_t tm;
+  int tn;
+  gemm_tile_of((int)tile, (int)((M + T - 1) / T), tiles_n, tm, tn);
+  const int64_t m = tm * T + within / (T / 4);
+  const int64_t f = (int64_t)tn * T + (within % (T / 4)) * 4;
+  if (m >= M || f >= N) return;
+  float4 s = *reinterpret_cast<const float4*>(part + m * N + f);
+  for (int s2 = 1; s2 < n_split; ++s2) {
+    const float4 v = *reinterpret_cast<const float4*>(part + ((int64_t)s2 * M + m) * N + f);
+    s.x += v.x;
+    s.y += v.y;
+    s.z += v.z;
+    s.w += v.w;
+  }
+  gemm_store4<EPI>(s.x, s.y, s.z, s.w, m, f, bias, C, ldc, gate, sp, rg);
+}
+
 // bf16 tile kernel: BF features x BT tokens per workgroup (4 wavefronts in a 2 x 2 grid, each
 // (BF/2) x (BT/2) = FB x TB blocks of 32 x 32), k staged 64 at a time (4 MFMA k-steps per
-// barrier), two workgroups per CU.  The W rows and X rows of a k tile are copied global ->
+// barrier), two workgroups per CU.  Tiles [0, n_whole) run whole; with SPLIT, tiles n_whole..
+// run as n_split k slices each (n_whole = 0: every tile split).  The W rows and X rows of a k tile are copied global ->
 // LDS with direct 16-byte loads into a 2-stage ring (one tile ahead; the other resident
 // workgroup covers the rest of the latency); LDS units are swizzled so every 8-lane operand
 // read phase hits distinct bank groups, and the operands of k-step s+1 are read while the
@@ -177,7 +212,7 @@ template <int BF, int BT, int EPI, bool SPLIT>
 __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
     const bf16* __restrict__ A, int64_t lda, const bf16* __restrict__ W, const float* __restrict__ bias, int64_t M,
     int64_t N, int64_t K, void* __restrict__ C, int64_t ldc, const float* __restrict__ gate, int tiles_n,
-    int n_split, int ktiles_per_split, float* __restrict__ part, QkvSplice sp, RowGroups rg) {
+    int n_split, int ktiles_per_split, int64_t n_whole, float* __restrict__ part, QkvSplice sp, RowGroups rg) {
   constexpr int BK = 64;                 // k per stage: four MFMA k-steps
   constexpr int KSTEPS = BK / 16;
   constexpr int ROWS = BF + BT;          // stage rows: W rows, then X rows
@@ -196,17 +231,35 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
   const int l32 = lane & 31, hi = lane >> 5;
   const int wf = wave & 1, wt = wave >> 1;
 
-  const int lid = gemm_xcd_remap(blockIdx.x, gridDim.x);
-  const int split = lid % n_split;
-  const int rest = lid / n_split;
+  bool sliced = SPLIT;
+  int split = 0, rest;
+  if (SPLIT && n_whole > 0) {
+    // remainder split: on every XCD (blocks are dealt to the 8 XCDs round-robin, and each XCD
+    // starts its blocks in order) the first n_whole / 8 blocks run a contiguous run of whole
+    // tiles, the later ones the k slices, so the slices fill the last round of every XCD
+    const int x = (int)(blockIdx.x % 8), j = (int)(blockIdx.x / 8);
+    const int wpx = (int)(n_whole / 8);
+    sliced = j >= wpx;
+    if (sliced) {
+      const int64_t si = (int64_t)(j - wpx) * 8 + x;
+      split = (int)(si % n_split);
+      rest = (int)(n_whole + si / n_split);
+    } else {
+      rest = x * wpx + j;
+    }
+  } else {
+    const int lid = gemm_xcd_remap(blockIdx.x, gridDim.x);
+    split = SPLIT ? lid % n_split : 0;
+    rest = SPLIT ? lid / n_split : lid;
+  }
   int64_t tile_m;
   int tile_n;
   gemm_tile_of(rest, (int)((M + BT - 1) / BT), tiles_n, tile_m, tile_n);
   const int64_t n0 = (int64_t)tile_n * BF;
   const int64_t m0 = tile_m * BT;
   const int64_t nkt = K / BK;
-  const int64_t kt0 = (int64_t)split * ktiles_per_split;
-  const int64_t kt1 = kt0 + ktiles_per_split < nkt ? kt0 + ktiles_per_split : nkt;
+  const int64_t kt0 = sliced ? (int64_t)split * ktiles_per_split : 0;
+  const int64_t kt1 = sliced && kt0 + ktiles_per_split < nkt ? kt0 + ktiles_per_split : nkt;
 
   // unit of (row, chunk c in 0..7): rows r..r+7 at one chunk land in 8 distinct bank groups
   auto unit = [](int r, int c) { return r * 8 + (c ^ (r & 7)); };
@@ -290,7 +343,10 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
   for (; kt + 1 < kt1; ++kt) ktile(kt, true);
   if (kt < kt1) ktile(kt, false);
 
-  gemm_epilogue<BF, BT, FB, TB, EPI, SPLIT>(acc, m0, n0, M, N, bias, C, ldc, gate, sp, rg, split, part);
+  if (sliced)
+    gemm_epilogue<BF, BT, FB, TB, EPI, true>(acc, m0, n0, M, N, bias, C, ldc, gate, sp, rg, split, part);
+  else
+    gemm_epilogue<BF, BT, FB, TB, EPI, false>(acc, m0, n0, M, N, bias, C, ldc, gate, sp, rg, split, part);
 }
 
 // ---------------------------------------------------------------------------------
@@ -367,34 +423,70 @@ static int gemm_cus() {
   return cus;
 }
 
-// k-split count of a bf16 GEMM with 128 x 128 tiles (two resident workgroups per CU): the
-// smallest estimated time over the split s, rounds of resident workgroups x one slice's time
-// (a fixed cost plus its FLOPs at one workgroup's measured rate), plus writing and re-reading
-// the fp32 partials.  A split needs at least 4 k tiles per slice and fits the workspace.
-static int gemm_split_plan(int64_t m, int64_t n, int64_t k, size_t ws_bytes) {
+// Work division of a bf16 GEMM with 128 x 128 tiles (two resident workgroups per CU): the
+// smallest estimated time over
+//   * a uniform k split s (s = 1: none): rounds of resident workgroups x one slice's time (a
+//     fixed cost plus its FLOPs at one workgroup's measured rate), plus writing and re-reading
+//     the fp32 partials;
+//   * a remainder split s: the full rounds of whole tiles, then the last round's few tiles in
+//     s slices each (at most one round of slices), plus their partials and the reduce launch.
+// A split needs at least 4 k tiles per slice and fits the workspace ([s][m][n] fp32).
+struct GemmPlan {
+  int split = 1;          // k slices per split tile
+  int64_t whole = 0;      // tiles run whole (the first in tile order); the rest are split
+  int64_t tiles = 0;
+};
+
+static GemmPlan gemm_split_plan(int64_t m, int64_t n, int64_t k, size_t ws_bytes) {
   constexpr int64_t kTile = 128, kBk = 64;
   constexpr double kFixedS = 3e-6;       // per-tile fixed cost (prologue, epilogue)
   constexpr double kRate = 1.65e12;      // FLOP/s of one resident workgroup
+  constexpr double kHbm = 5.0e12;        // B/s for partial traffic
+  constexpr double kLaunchS = 2e-6;      // the extra reduce launch
   const int64_t slots = 2 * (int64_t)gemm_cus();
   const int64_t tiles = ((m + kTile - 1) / kTile) * ((n + kTile - 1) / kTile);
-  int best_sp = 1;
-  double best = 1e30;
+  const double tile_s = 2.0 * kTile * kTile * (double)k / kRate;
+  GemmPlan best;
+  best.tiles = tiles;
+  best.whole = tiles;
+  double best_t = 1e30;
   for (int sp = 1; sp <= kMaxGemmSplit; ++sp) {
     if (sp > 1 && k / kBk < 4LL * sp) break;
     if (sp > 1 && (size_t)sp * m * n * sizeof(float) > ws_bytes) break;
-    const double t = (double)((tiles * sp + slots - 1) / slots) * (kFixedS + 2.0 * kTile * kTile * (double)k / sp / kRate) +
-                     (sp > 1 ? 2.0 * sp * (double)m * (double)n * sizeof(float) / 5.0e12 : 0.0);
-    if (t < best * 0.98) {
-      best = t;
-      best_sp = sp;
+    const double t = (double)((tiles * sp + slots - 1) / slots) * (kFixedS + tile_s / sp) +
+                     (sp > 1 ? 2.0 * sp * (double)m * (double)n * sizeof(float) / kHbm + kLaunchS : 0.0);
+    if (t < best_t * 0.98) {
+      best_t = t;
+      best.split = sp;
+      best.whole = sp > 1 ? 0 : tiles;
     }
   }
-  return best_sp;
+  // Only a small remainder (at most one workgroup for every fourth CU) is worth it: a last round
+  // that runs part full runs its lone workgroups faster than a full round's, so the measured
+  // gain shrinks with the remainder (2048 x 4608 x 1536, 64 of 576 tiles left: 49.0 -> 45.6 us;
+  // 2048 x 9216 x 3072, 128 of 1152: 135.9 -> 133.2; 16384 x 1152 x 4608, 128 of 1152:
+  // 198.9 -> 207.7).  The full rounds must divide evenly over the 8 XCDs.
+  const int64_t rem = tiles % slots;
+  if (tiles > slots && rem > 0 && rem * 8 <= slots && (tiles - rem) % 8 == 0) {
+    const int64_t full = tiles - rem;
+    for (int sp = 2; sp <= kMaxGemmSplit; ++sp) {
+      if (k / kBk < 4LL * sp || rem * sp > slots) break;
+      if ((size_t)sp * m * n * sizeof(float) > ws_bytes) break;
+      const double t = (double)(full / slots) * (kFixedS + tile_s) + kFixedS + tile_s / sp +
+                       2.0 * sp * (double)rem * kTile * kTile * sizeof(float) / kHbm + kLaunchS;
+      if (t < best_t * 0.98) {
+        best_t = t;
+        best.split = sp;
+        best.whole = full;
+      }
+    }
+  }
+  return best;
 }
 
 size_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k) {
-  const int sp = gemm_split_plan(m, n, k, (size_t)-1);
-  return sp > 1 ? (size_t)sp * m * n * sizeof(float) : 0;
+  const GemmPlan plan = gemm_split_plan(m, n, k, (size_t)-1);
+  return plan.split > 1 ? (size_t)plan.split * m * n * sizeof(float) : 0;
 }
 
 template <int EPI>
@@ -407,21 +499,26 @@ static hipError_t launch_gemm_epi(const void* a, int64_t lda, const void* w, con
     if (k % 64 != 0 || n % 64 != 0) return hipErrorInvalidValue;
     const bf16* A = static_cast<const bf16*>(a);
     const bf16* Wt = static_cast<const bf16*>(w);
-    const int split = gemm_split_plan(m, n, k, ws ? ws_bytes : 0);
+    const GemmPlan plan = gemm_split_plan(m, n, k, ws ? ws_bytes : 0);
     const int nkt = (int)(k / 64);
     const int tiles_n = (int)((n + 127) / 128);
-    const int64_t tiles = (int64_t)tiles_n * ((m + 127) / 128);
-    const int kps = (nkt + split - 1) / split;
+    const int64_t tiles = plan.tiles;
+    const int kps = (nkt + plan.split - 1) / plan.split;
     const int used = (nkt + kps - 1) / kps;          // every slice gets at least one k tile
+    if (used > 1 && (size_t)used * m * n * sizeof(float) > ws_bytes) return hipErrorInvalidValue;
     float* part = static_cast<float*>(ws);
-    const dim3 grid((unsigned)(tiles * used));
+    const dim3 grid((unsigned)(plan.whole + (tiles - plan.whole) * used));
     if (used == 1)
       hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, EPI, false>), grid, dim3(256), 0, s, A, lda, Wt, bias, m, n, k, c,
-                         ldc, gate, tiles_n, 1, nkt, nullptr, sp, rg);
+                         ldc, gate, tiles_n, 1, nkt, tiles, nullptr, sp, rg);
     else
       hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, EPI, true>), grid, dim3(256), 0, s, A, lda, Wt, bias, m, n, k, c,
-                         ldc, gate, tiles_n, used, kps, part, sp, rg);
-    if (used > 1) {
+                         ldc, gate, tiles_n, used, kps, plan.whole, part, sp, rg);
+    if (used > 1 && plan.whole > 0) {
+      const int64_t units = (tiles - plan.whole) * 128 * 32;
+      hipLaunchKernelGGL(gemm_reduce_tiles_kernel<EPI>, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, s, part,
+                         used, plan.whole, tiles, tiles_n, m, n, bias, c, ldc, gate, sp, rg);
+    } else if (used > 1) {
       if (EPI == kEpiGatedResidual && ln && n <= kMaxHidden) {
         // the reduce pass already holds whole updated rows: it applies the next LayerNorm too
         const hipError_t e =

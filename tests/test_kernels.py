@@ -128,6 +128,41 @@ def test_gemm_bf16_long_k_default_plan():
     assert_close(host(c)[rows], want, "gemm bf16 2048x3072x12288 gated residual, sampled rows")
 
 
+@pytest.mark.parametrize("epi", [B.PF_EPI_STORE, B.PF_EPI_GELU_TANH, B.PF_EPI_GATED_RESIDUAL])
+@pytest.mark.parametrize("m,n,k,tail", [(2048, 4608, 1536, 1536), (2432, 3456, 1152, 2304)])
+def test_gemm_bf16_remainder_split(m, n, k, tail, epi):
+    """Shapes whose last round of 128 x 128 tiles would hold only a few tiles on 512 workgroup
+    slots (576 tiles: one round + 64; 513 tiles: one round + 1), so the plan runs the full round
+    as whole tiles and splits k for the remaining tiles only, which a reduce pass over those
+    tiles finishes.  Checked against the oracle on sampled rows from both parts: the split tiles
+    are the last in the grouped tile order, so token rows from `tail` on lie in split tiles for
+    part of their columns."""
+    torch = torch_cuda()
+    ws = B.gemm_workspace(m, n, k)
+    seed = 6100 + m + n + k + epi
+    a = synth.randn((m, k), seed, std=1.0, bf16=True)
+    w = synth.randn((n, k), seed + 1, std=1.0 / math.sqrt(k), bf16=True)
+    bias = synth.randn((n,), seed + 2, std=0.5)
+    rng = np.random.default_rng(seed)
+    rows = np.unique(np.concatenate([[0, tail - 1, tail, m - 1], rng.choice(tail, 20, replace=False),
+                                     tail + rng.choice(m - tail, 24, replace=False)]))
+    y = ref.linear(a[rows], w, bias)
+    print(f"[gemm] remainder split {m}x{n}x{k} epi={epi}", flush=True)
+    if epi == B.PF_EPI_GATED_RESIDUAL:
+        x0 = synth.randn((m, n), seed + 3)
+        gate = synth.randn((n,), seed + 4)
+        c = dev(torch, x0)
+        B.pf_gemm(dev(torch, a, torch.bfloat16), dev(torch, w, torch.bfloat16), dev(torch, bias), epi, c,
+                  gate=dev(torch, gate), workspace=ws)
+        want = x0[rows] + gate * y
+    else:
+        c = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+        B.pf_gemm(dev(torch, a, torch.bfloat16), dev(torch, w, torch.bfloat16), dev(torch, bias), epi, c,
+                  workspace=ws)
+        want = ref.bf16_round(ref.gelu_tanh(y) if epi == B.PF_EPI_GELU_TANH else y)
+    assert_close(host(c)[rows], want, f"gemm bf16 {m}x{n}x{k} epi={epi} remainder split, sampled rows")
+
+
 def test_gemm_bf16_split_workspace_reuse():
     """One workspace serves k-split GEMMs of different shapes in turn (the stage's pattern:
     QKV, out-projection, QKV again): results match the oracle, and a repeated call reproduces

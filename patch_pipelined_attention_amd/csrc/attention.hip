@@ -13,8 +13,9 @@
 //     register staging) into a 5-stage ring, three tiles ahead; the loads are counted with
 //     explicit vmcnt waits, so they stay in flight across barriers.  K keeps its rows in a
 //     permuted, swizzled unit order (conflict-free operand reads), V the K8 layout of the
-//     buffer (see pf.h).  The V operands of a tile are read into registers at the end of
-//     its softmax phase, so the next MFMA phase starts without waiting on LDS.
+//     buffer (see pf.h).  The V operands of a tile are read into registers one phase before
+//     the P.V MFMAs that use them (in the MFMA phase at D = 72, in the softmax phase
+//     otherwise), so no MFMA phase starts by waiting on LDS.
 //   * scores are computed transposed, S^T = K . Q^T, so each lane owns one query and 16
 //     keys per block: the row max is a lane-local max chain plus one exchange with the
 //     lane 32 away, and the row sum stays lane-local until the end.
@@ -353,11 +354,12 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const bf16* __restric
           if (db * 32 + 32 <= D) {
             vf[h2][db] = *reinterpret_cast<const bf16x8*>(&base[grp8 * D + d]);
           } else {
-            // rows past D: zero, or ones in row D (MFMA row sum); selected without a branch
-            const u32x4 w = *reinterpret_cast<const u32x4*>(&base[grp8 * D + (d < D ? d : D - 1)]);
+            // rows past D: zero, or ones in row D (MFMA row sum); only lanes of real rows read LDS
+            // (reading a valid unit in every lane and selecting measured 3% slower at D = 72)
             const uint32_t f = (kSumRow && d == D) ? 0x3f803f80u : 0u;   // bf16 pair (1, 1) or (0, 0)
-            const u32x4 fv = {f, f, f, f};
-            vf[h2][db] = __builtin_bit_cast(bf16x8, d < D ? w : fv);
+            u32x4 w = {f, f, f, f};
+            if (d < D) w = *reinterpret_cast<const u32x4*>(&base[grp8 * D + d]);
+            vf[h2][db] = __builtin_bit_cast(bf16x8, w);
           }
           if (zero_tail) {
             const int lim = (int)(S - t * TK) - grp8 * 8;
@@ -513,9 +515,13 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const bf16* __restric
     // other wavefront's softmax (measured: +5% at 262144 keys, d = 72; at d = 64, where the
     // softmax phase is the longer one, it costs 3%)
     constexpr bool kPingPongPrio = D != 64;
-    // at D = 128 the V operand reads go out before the softmax, so their LDS latency hides behind
-    // its exponentials (measured: -7% time at 2048 x 16896 keys, 24 heads; at D = 72 and 64 the
-    // extra live registers cost 1-2%)
+    // Where the V operands of tile t are read.  At D = 72 (single-piece kernel) the wavefront in
+    // its MFMA phase reads them right after its P.V MFMAs have consumed the previous tile's: a
+    // wavefront then issues its LDS reads next to its MFMAs, not next to its softmax VALU work
+    // (measured: -5% time at 16384 x 262144 keys, 16 heads; in the stream-K kernel the extra
+    // live registers spill).  At D = 128 they go out before the softmax, so their latency hides
+    // behind its exponentials (-7% at 2048 x 16896 keys, 24 heads).  At D = 64 both cost 1-3%.
+    constexpr bool kVInMfmaPhase = D == 72 && !SK;
     constexpr bool kEarlyV = D == 128;
     auto iter_steady = [&](int64_t t) {
       bf16x8 kf[KS];
@@ -523,13 +529,14 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const bf16* __restric
       read_k(st, kf);
       f32x16 sc[QB];
       pv(vf, pb);
+      if constexpr (kVInMfmaPhase) read_v(t, st, vf, false);
       if (grp == 0) issue_tile_full(t + NSTAGE - 2, st_issue);
       scores(kf, sc);
       barrier();
       if constexpr (kPingPongPrio) __builtin_amdgcn_s_setprio(0);
       if constexpr (kEarlyV) read_v(t, st, vf, false);
       softmax(sc, pb);
-      if constexpr (!kEarlyV) read_v(t, st, vf, false);
+      if constexpr (!kEarlyV && !kVInMfmaPhase) read_v(t, st, vf, false);
       if (grp == 0) wait_loads_const();
       barrier();
       st = st + 1 == NSTAGE ? 0 : st + 1;

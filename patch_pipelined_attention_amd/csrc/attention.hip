@@ -14,8 +14,8 @@
 //     explicit vmcnt waits, so they stay in flight across barriers.  K keeps its rows in a
 //     permuted, swizzled unit order (conflict-free operand reads), V the K8 layout of the
 //     buffer (see pf.h).  The V operands of a tile are read into registers one phase before
-//     the P.V MFMAs that use them (in the MFMA phase at D = 72, in the softmax phase
-//     otherwise), so no MFMA phase starts by waiting on LDS.
+//     the P.V MFMAs that use them (in the MFMA phase at D = 64 and 72, in the softmax phase
+//     at D = 128), so no MFMA phase starts by waiting on LDS.
 //   * scores are computed transposed, S^T = K . Q^T, so each lane owns one query and 16
 //     keys per block: the row max is a lane-local max chain plus one exchange with the
 //     lane 32 away, and the row sum stays lane-local until the end.
@@ -515,13 +515,14 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const bf16* __restric
     // other wavefront's softmax (measured: +5% at 262144 keys, d = 72; at d = 64, where the
     // softmax phase is the longer one, it costs 3%)
     constexpr bool kPingPongPrio = D != 64;
-    // Where the V operands of tile t are read.  At D = 72 (single-piece kernel) the wavefront in
-    // its MFMA phase reads them right after its P.V MFMAs have consumed the previous tile's: a
-    // wavefront then issues its LDS reads next to its MFMAs, not next to its softmax VALU work
-    // (measured: -5% time at 16384 x 262144 keys, 16 heads; in the stream-K kernel the extra
-    // live registers spill).  At D = 128 they go out before the softmax, so their latency hides
-    // behind its exponentials (-7% at 2048 x 16896 keys, 24 heads).  At D = 64 both cost 1-3%.
-    constexpr bool kVInMfmaPhase = D == 72 && !SK;
+    // Where the V operands of tile t are read.  At D = 64 and 72 the wavefront in its MFMA phase
+    // reads them right after its P.V MFMAs have consumed the previous tile's: a wavefront then
+    // issues its LDS reads next to its MFMAs, not next to its softmax VALU work (measured: -5%
+    // time at 16384 x 262144 keys, 16 heads, d = 72; -5% at 16384 x 16384 keys, 24 heads, d = 64;
+    // neutral for d = 64 stream-K; in the d = 72 stream-K kernel the extra live registers spill).
+    // At D = 128 they go out before the softmax, so their latency hides behind its exponentials
+    // (-7% at 2048 x 16896 keys, 24 heads).
+    constexpr bool kVInMfmaPhase = (D == 72 && !SK) || D == 64;
     constexpr bool kEarlyV = D == 128;
     auto iter_steady = [&](int64_t t) {
       bf16x8 kf[KS];

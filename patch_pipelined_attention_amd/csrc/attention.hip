@@ -5,10 +5,12 @@
 // bf16 kernel (head_dim D in {64, 72, 128}), gfx950 MFMA v_mfma_f32_32x32x16_bf16:
 //   * workgroup = 8 wavefronts in two groups of four; wavefronts w and w + 4 share a SIMD.
 //     Each wavefront owns QB blocks of 32 queries of one head, so every K/V operand read
-//     from LDS feeds QB MFMAs.  The groups run one phase apart between workgroup barriers
-//     ("ping-pong"): while one wavefront of a SIMD issues its MFMAs (P.V of the previous
-//     key tile and the scores of the current one) the other runs its softmax on the VALU,
-//     so the matrix cores and the vector ALUs of every SIMD work at the same time.
+//     from LDS feeds QB MFMAs.  The groups run one phase apart ("ping-pong"): while one
+//     wavefront of a SIMD issues its MFMAs (P.V of the previous key tile and the scores of
+//     the current one) the other runs its softmax on the VALU, so the matrix cores and the
+//     vector ALUs of every SIMD work at the same time.  The phases are held apart by a
+//     workgroup barrier after every phase, or (stream-K and D = 72) by one barrier per key
+//     tile that falls after the MFMA phase in group 1 and after the softmax in group 0.
 //   * key tiles of 32 rows are copied global -> LDS by the gfx950 direct 16-byte loads (no
 //     register staging) into a 5-stage ring, three tiles ahead; the loads are counted with
 //     explicit vmcnt waits, so they stay in flight across barriers.  K keeps its rows in a
@@ -465,21 +467,34 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const bf16* __restric
       }
     };
 
-    // Slots between barriers: group 0 runs the MFMA phase of tile t in slot 2(t - t_begin) and
-    // its softmax in the next slot; group 1 runs the same one slot later.  MFMA phase of t:
-    // P.V of tile t-1 (V operands already in registers) and the scores of tile t.  Softmax
-    // phase of t: P_t, then the V_t operands are read for the next MFMA phase.  Tile t sits in
-    // stage (t - t_begin) mod NSTAGE and is last read by group 1 in slot 2(t - t_begin) + 2,
-    // so group 0 issues tile t + NSTAGE - 2 at the start of its slot 2(t - t_begin), into
-    // the stage tile t - 2 used.
+    // MFMA phase of tile t: P.V of tile t-1 (V operands already in registers) and the scores
+    // of tile t.  Softmax phase of t: P_t (and, where the V operands are not read in the MFMA
+    // phase, the V_t operands for the next one).  Tile t sits in stage (t - t_begin) mod NSTAGE.
+    //   * Two barriers per tile: group 0 runs the MFMA phase of t in slot 2(t - t_begin) and its
+    //     softmax in the next slot; group 1 runs the same one slot later (one extra barrier at
+    //     the start, matched by group 0 at the end).  Tile t is last read by group 1 in slot
+    //     2(t - t_begin) + 2, so group 0 issues tile t + NSTAGE - 2 at the start of its slot
+    //     2(t - t_begin), into the stage tile t - 2 used.
+    //   * One barrier per tile (kOneBarrier): between barriers t-1 and t group 0 runs the MFMA
+    //     phase of t, then its softmax; group 1 the softmax of t-1, then the MFMA phase of t.
+    //     Tile t is last read by group 1 before barrier t+1 (its V operands, where they are read
+    //     in the softmax phase).  Group 0 issues tile t + NSTAGE - 2 between barriers t-1 and t,
+    //     into the stage of tile t - 2, so tile t's stage is written again only after barrier
+    //     t+1.  Tile t+1 has landed (group 0 waits for it before barrier t) and barrier t
+    //     publishes it before either group reads it.  Measured against two barriers:
+    //     -2% for the stream-K launches of 2048 x 16384 keys (24 heads, d = 64) and 2048 x
+    //     16896 (d = 128), -1.5% for the split launch of 1024 x 4096 (d = 72), the same at
+    //     16384 x 262144 (d = 72); 2% slower for whole-head launches at d = 64 and no faster at
+    //     d = 128, hence not for those.
     const int64_t nt = t_end - t_begin;
+    constexpr bool kOneBarrier = SK || D == 72;
     if (grp == 0) {
       for (int64_t u = 0; u < nt && u < NSTAGE - 2; ++u) issue_tile(t_begin + u, (int)u);
       const int64_t newer = (nt < NSTAGE - 2 ? nt : NSTAGE - 2) - 1;
       wait_loads((int)newer);
     }
     barrier();
-    if (grp == 1) barrier();
+    if (!kOneBarrier && grp == 1) barrier();
 
     // P.V of "tile t_begin - 1" multiplies zero weights, so every MFMA phase has the same shape
     bf16x8 pb[QB][2];
@@ -501,7 +516,7 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const bf16* __restric
       pv(vf, pb);
       if (grp == 0 && t + NSTAGE - 2 < t_end) issue_tile(t + NSTAGE - 2, st_issue);
       scores(kf, sc);
-      barrier();
+      if (!kOneBarrier || grp == 1) barrier();
       if (partial) mask_scores(t, sc);
       softmax(sc, pb);
       read_v(t, st, vf, partial);
@@ -510,7 +525,7 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const bf16* __restric
         const int64_t newer = last_issued - (t + 1);
         wait_loads((int)(newer < 0 ? 0 : newer));
       }
-      barrier();
+      if (!kOneBarrier || grp == 0) barrier();
       st = st + 1 == NSTAGE ? 0 : st + 1;
       st_issue = st_issue + 1 == NSTAGE ? 0 : st_issue + 1;
     };
@@ -538,13 +553,13 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const bf16* __restric
       if constexpr (kVInMfmaPhase) read_v(t, st, vf, false);
       if (grp == 0) issue_tile_full(t + NSTAGE - 2, st_issue);
       scores(kf, sc);
-      barrier();
+      if (!kOneBarrier || grp == 1) barrier();
       if constexpr (kPingPongPrio) __builtin_amdgcn_s_setprio(0);
       if constexpr (kEarlyV) read_v(t, st, vf, false);
       softmax(sc, pb);
       if constexpr (!kEarlyV && !kVInMfmaPhase) read_v(t, st, vf, false);
       if (grp == 0) wait_loads_const();
-      barrier();
+      if (!kOneBarrier || grp == 0) barrier();
       st = st + 1 == NSTAGE ? 0 : st + 1;
       st_issue = st_issue + 1 == NSTAGE ? 0 : st_issue + 1;
     };
@@ -556,7 +571,7 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const bf16* __restric
     for (; t < t_full; ++t) iter(t, false);
     if (t_full < t_end) iter(t_full, true);
     if (nt > 0) pv(vf, pb);
-    if (grp == 0) barrier();
+    if (!kOneBarrier && grp == 0) barrier();
 
     if constexpr (kSumRow) {
 #pragma unroll

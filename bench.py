@@ -73,9 +73,12 @@ def attention_source_hash() -> str:
     return h.hexdigest()
 
 
-def recorded_traffic(config: str):
+def recorded_traffic(config: str, batch: int = 1):
     """Bytes per attention call from TRAFFIC_FILE if it matches this config and the current
-    kernel sources, else None."""
+    kernel sources, else None.  The files record one sample's launch; a batched stage (a CFG
+    pair) launches over all samples' rows, so its traffic is not the recorded figure."""
+    if batch != 1:
+        return None
     try:
         fields = {}
         with open(TRAFFIC_FILE.format(config=config)) as f:
@@ -514,7 +517,7 @@ def main():
         "wall_s_timed": wall,
         "roofline": {"kernel": "attn_bf16_kernel", "bound": "mfma", "achieved": attn_tflops,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": attn_tflops / PEAK_BF16_TFLOPS,
-                     "traffic": recorded_traffic(args.config), "avg_launch_us": attn_s * 1e6,
+                     "traffic": recorded_traffic(args.config, args.batch), "avg_launch_us": attn_s * 1e6,
                      "launches": n_attn,
                      "launch": "the stage's attention launches inside a second timed pass of the same patched "
                                "steps (one per layer and micro-step), each bracketed by HIP events on the stage's "

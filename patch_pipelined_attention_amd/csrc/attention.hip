@@ -305,8 +305,14 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const bf16* __restric
       __builtin_amdgcn_sched_barrier(0);
     };
 
-    // K_t operands of S^T = K_t . Q^T (lane: key row l32, 8 consecutive d).  Rows of the
-    // padded k-step past D read a valid LDS unit and are zeroed by a select (no branch).
+    // K_t operands of S^T = K_t . Q^T (lane: key row l32, 8 consecutive d).  In the padded
+    // k-step (D = 72: d 64..79) only the lanes of real columns read LDS, into a register that
+    // lives across the key loop; the other lanes never write it and keep its zeros (an
+    // exec-masked read of half the lanes; reading a valid unit in every lane and selecting
+    // zero measured 2.5% slower at 16384 x 262144 keys, 16 heads).
+    bf16x8 kpad;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) kpad[e] = (bf16)0.f;
     auto read_k = [&](int st, bf16x8 (&kf)[KS]) {
       const uint4* base = lds[st];
 #pragma unroll
@@ -314,10 +320,8 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const bf16* __restric
         const int d0 = ks * 16 + hi * 8;
         if constexpr (KS * 16 > D) {
           if (ks == KS - 1) {
-            const int c = d0 < D ? 2 * ks + hi : 2 * ks;
-            const u32x4 w = *reinterpret_cast<const u32x4*>(&base[k_unit(l32, c)]);
-            const u32x4 z = {0u, 0u, 0u, 0u};
-            kf[ks] = __builtin_bit_cast(bf16x8, d0 < D ? w : z);
+            if (d0 < D) kpad = *reinterpret_cast<const bf16x8*>(&base[k_unit(l32, 2 * ks + hi)]);
+            kf[ks] = kpad;
             continue;
           }
         }
@@ -361,12 +365,10 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const bf16* __restric
           if (db * 32 + 32 <= D) {
             vf[h2][db] = *reinterpret_cast<const bf16x8*>(&base[grp8 * D + d]);
           } else {
-            // rows past D: zero, or ones in row D (MFMA row sum); only lanes of real rows read LDS
-            // (reading a valid unit in every lane and selecting measured 3% slower at D = 72)
-            const uint32_t f = (kSumRow && d == D) ? 0x3f803f80u : 0u;   // bf16 pair (1, 1) or (0, 0)
-            u32x4 w = {f, f, f, f};
-            if (d < D) w = *reinterpret_cast<const u32x4*>(&base[grp8 * D + d]);
-            vf[h2][db] = __builtin_bit_cast(bf16x8, w);
+            // rows past D: only lanes of real rows read LDS (reading a valid unit in every lane and
+            // selecting measured 3% slower at D = 72); the others keep the zeros, or the ones of row
+            // D (MFMA row sum), they were given before the key loop
+            if (d < D) vf[h2][db] = *reinterpret_cast<const bf16x8*>(&base[grp8 * D + d]);
           }
           if (zero_tail) {
             const int lim = (int)(S - t * TK) - grp8 * 8;
@@ -507,6 +509,13 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const bf16* __restric
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int e = 0; e < 8; ++e) vf[0][db][e] = vf[1][db][e] = (bf16)0.f;
+    if constexpr (DB * 32 > D) {
+      // rows past D of the padded V^T block keep their values: zero, or ones in row D (MFMA row sum)
+      const int d = (DB - 1) * 32 + l32;
+      const uint32_t f = (kSumRow && d == D) ? 0x3f803f80u : 0u;
+      const u32x4 w = {f, f, f, f};
+      vf[0][DB - 1] = vf[1][DB - 1] = __builtin_bit_cast(bf16x8, w);
+    }
     int st = 0;                         // stage of tile t
     int st_issue = NSTAGE - 2;          // stage of tile t + NSTAGE - 2
     auto iter = [&](int64_t t, bool partial) {

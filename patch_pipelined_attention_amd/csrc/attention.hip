@@ -16,8 +16,8 @@
 //     explicit vmcnt waits, so they stay in flight across barriers.  K keeps its rows in a
 //     permuted, swizzled unit order (conflict-free operand reads), V the K8 layout of the
 //     buffer (see pf.h).  The V operands of a tile are read into registers one phase before
-//     the P.V MFMAs that use them (in the MFMA phase at D = 64 and 72, in the softmax phase
-//     at D = 128), so no MFMA phase starts by waiting on LDS.
+//     the P.V MFMAs that use them (in the MFMA phase at D = 64 and in the single-piece D = 72
+//     kernel, in the softmax phase otherwise), so no MFMA phase starts by waiting on LDS.
 //   * scores are computed transposed, S^T = K . Q^T, so each lane owns one query and 16
 //     keys per block: the row max is a lane-local max chain plus one exchange with the
 //     lane 32 away, and the row sum stays lane-local until the end.

@@ -164,6 +164,20 @@ def test_gemm_bf16_remainder_split(m, n, k, tail, epi):
     assert_close(host(c)[rows], want, f"gemm bf16 {m}x{n}x{k} epi={epi} remainder split, sampled rows")
 
 
+def test_gemm_split_plan_rules():
+    """The k-split plan on a 256-CU MI355X: grids with fewer 128 x 128 tiles than CUs split k
+    (the workspace size is that of the split), grids with a tile for every CU run whole unless a
+    small last round is left (then only its tiles split), and grids of full rounds run whole."""
+    torch_cuda()
+    mnk = lambda m, n, k: B.pf_gemm_workspace_size(m, n, k)
+    assert mnk(2048, 1536, 1536) > 0          # 192 tiles: split
+    assert mnk(1024, 1152, 4608) > 0          # 72 tiles: split
+    assert mnk(2048, 3072, 12288) == 0        # 384 tiles: every CU has one, whole
+    assert mnk(2048, 3072, 3072) == 0         # 384 tiles
+    assert mnk(2048, 12288, 3072) == 0        # 1536 tiles: three full rounds
+    assert mnk(2048, 4608, 1536) > 0          # 576 tiles: 64 left after a full round, those split
+
+
 def test_gemm_bf16_split_workspace_reuse():
     """One workspace serves k-split GEMMs of different shapes in turn (the stage's pattern:
     QKV, out-projection, QKV again): results match the oracle, and a repeated call reproduces

@@ -352,7 +352,9 @@ pf_status pf_ln_modulate(const float* x, int64_t rows, int32_t hidden, const flo
  * (in a fixed order: deterministic);
  * calls sharing a workspace must not overlap in time (one stream, or ordered streams).
  * pf_gemm_workspace_size gives the bytes that allow the split the library would choose.
- * Tiles are 128 x 128 (a 2-stage ring, two workgroups per CU).  Source: the projections of the
+ * Tiles are 128 x 128, or 192 features x 128 tokens for a grid of whole tiles with n % 192 == 0
+ * and at least 1.5 tiles per CU (either with a 2-stage ring, two workgroups per CU); the tile
+ * does not change the result, which is the same sum in the same k order.  Source: the projections of the
  * transformer layers (mechanism 1; the block is a reading).  Errors: INVALID_ARG for a bad
  * pointer, size, stride or epilogue; UNSUPPORTED for bf16 shapes with n or k not a multiple
  * of 64; HIP if the launch fails. */

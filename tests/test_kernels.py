@@ -46,7 +46,8 @@ GEMM_SHAPES = [(1, 64, 64), (77, 192, 128), (128, 128, 1152), (300, 1152, 1152),
 @pytest.mark.parametrize("m,n,k", GEMM_SHAPES)
 @pytest.mark.parametrize("epi", [B.PF_EPI_STORE, B.PF_EPI_GELU_TANH, B.PF_EPI_GELU_ERF, B.PF_EPI_GATED_RESIDUAL])
 def test_gemm_bf16(m, n, k, epi, split):
-    """Small grids split k when given a workspace (default tile choice: 128 x 128 here)."""
+    """Small grids split k when given a workspace.  Tiles: 128 x 128, except 4100 x 4608 x 1152
+    (33 x 24 tiles of 192 features x 128 tokens, more than 1.5 per CU: whole, ragged last tile row)."""
     torch = torch_cuda()
     ws = B.gemm_workspace(m, n, k) if split else None
     seed = m * 7 + n * 11 + k * 13 + epi
@@ -71,14 +72,15 @@ def test_gemm_bf16(m, n, k, epi, split):
 
 
 @pytest.mark.parametrize("m,n,k", [(1024, 1152, 1152), (1024, 1152, 4608), (2048, 1536, 6144), (100, 3072, 3072),
-                                   (2048, 3072, 12288), (77, 192, 128), (2432, 3456, 1152)])
+                                   (2048, 3072, 12288), (77, 192, 128), (2432, 3456, 1152), (8192, 1152, 1152)])
 @pytest.mark.parametrize("split", [False, True], ids=["whole", "ksplit"])
 def test_gemm_residual_ln_is_bit_identical(m, n, k, split):
     """The gated-residual projection followed by the modulated LayerNorm of its rows, as one call
     (pf_gemm_residual_ln: with a workspace the k-split's reduce pass also computes the LayerNorm)
     gives the same bits as pf_gemm with the same workspace followed by pf_ln_modulate, and both
     match the oracle.  2432 x 3456 x 1152 (513 tiles) takes the remainder split, whose reduce pass
-    covers only the split tiles, so the LayerNorm runs as its own launch."""
+    covers only the split tiles, and 8192 x 1152 x 1152 runs whole with 192 x 128 tiles; in both
+    the LayerNorm runs as its own launch."""
     torch = torch_cuda()
     seed = m + 3 * n + 7 * k
     a = synth.randn((m, k), seed, std=1.0, bf16=True)
@@ -108,6 +110,42 @@ def test_gemm_residual_ln_is_bit_identical(m, n, k, split):
                  f"gemm+ln {m}x{n}x{k} LayerNorm of the updated rows")
 
 
+@pytest.mark.parametrize("epi", [B.PF_EPI_STORE, B.PF_EPI_GELU_TANH, B.PF_EPI_GELU_ERF, B.PF_EPI_GATED_RESIDUAL])
+@pytest.mark.parametrize("m,n,k", [(2689, 4608, 1536), (16384, 1152, 4608)])
+def test_gemm_bf16_wide_tiles(m, n, k, epi):
+    """Grids the plan runs whole with 192-feature x 128-token tiles (n % 192 == 0, at least 1.5
+    tiles per CU): 2689 rows end in a tile row of one token (rows past m clamped on load, never
+    stored), and 16384 x 1152 x 4608 is the long-sequence PixArt-shaped MLP down projection.
+    Checked against the oracle on sampled rows, the first and last rows included."""
+    torch = torch_cuda()
+    assert B.pf_gemm_workspace_size(m, n, k) == 0, "wide-tile grids run whole"
+    seed = 5300 + m + n + k + epi
+    a = synth.randn((m, k), seed, std=1.0, bf16=True)
+    w = synth.randn((n, k), seed + 1, std=1.0 / math.sqrt(k), bf16=True)
+    bias = synth.randn((n,), seed + 2, std=0.5)
+    rng = np.random.default_rng(seed)
+    rows = np.unique(np.concatenate([[0, 127, 128, m - 2, m - 1], rng.choice(m, 40, replace=False)]))
+    y = ref.linear(a[rows], w, bias)
+    ws = B.gemm_workspace(m, n, k)
+    print(f"[gemm] wide tiles {m}x{n}x{k} epi={epi}", flush=True)
+    if epi == B.PF_EPI_GATED_RESIDUAL:
+        x0 = synth.randn((m, n), seed + 3)
+        gate = synth.randn((n,), seed + 4)
+        c = dev(torch, x0)
+        B.pf_gemm(dev(torch, a, torch.bfloat16), dev(torch, w, torch.bfloat16), dev(torch, bias), epi, c,
+                  gate=dev(torch, gate), workspace=ws)
+        got = host(c)[rows]
+        want = x0[rows] + gate * y
+    else:
+        c = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+        B.pf_gemm(dev(torch, a, torch.bfloat16), dev(torch, w, torch.bfloat16), dev(torch, bias), epi, c,
+                  workspace=ws)
+        act = {B.PF_EPI_STORE: lambda v: v, B.PF_EPI_GELU_TANH: ref.gelu_tanh, B.PF_EPI_GELU_ERF: ref.gelu_erf}[epi]
+        want = ref.bf16_round(act(y))
+        got = host(c)[rows]
+    assert_close(got, want, f"gemm bf16 {m}x{n}x{k} epi={epi} wide tiles, sampled rows")
+
+
 def test_gemm_bf16_long_k_default_plan():
     """The Flux-shaped MLP down projection (2048 x 3072 x 12288, gated residual) with the
     workspace the stage gives it (the default plan: 128 x 128 tiles, a 192-step k loop).
@@ -130,10 +168,11 @@ def test_gemm_bf16_long_k_default_plan():
 
 
 @pytest.mark.parametrize("epi", [B.PF_EPI_STORE, B.PF_EPI_GELU_TANH, B.PF_EPI_GATED_RESIDUAL])
-@pytest.mark.parametrize("m,n,k,tail", [(2048, 4608, 1536, 1536), (2432, 3456, 1152, 2304)])
+@pytest.mark.parametrize("m,n,k,tail", [(2304, 4096, 1536, 2048), (2432, 3456, 1152, 2304)])
 def test_gemm_bf16_remainder_split(m, n, k, tail, epi):
     """Shapes whose last round of 128 x 128 tiles would hold only a few tiles on 512 workgroup
-    slots (576 tiles: one round + 64; 513 tiles: one round + 1), so the plan runs the full round
+    slots (576 tiles: one round + 64; 513 tiles: one round + 1; neither has enough 192 x 128
+    tiles for the wide tile: n = 4096 is no multiple of 192, 342 tiles), so the plan runs the full round
     as whole tiles and splits k for the remaining tiles only, which a reduce pass over those
     tiles finishes.  Checked against the oracle on sampled rows from both parts: the split tiles
     are the last in the grouped tile order, so token rows from `tail` on lie in split tiles for
@@ -165,8 +204,9 @@ def test_gemm_bf16_remainder_split(m, n, k, tail, epi):
 
 
 def test_gemm_split_plan_rules():
-    """The k-split plan on a 256-CU MI355X: grids with fewer 128 x 128 tiles than CUs split k
-    (the workspace size is that of the split), grids with a tile for every CU run whole unless a
+    """The k-split plan on a 256-CU MI355X: grids of at least 384 tiles of 192 x 128 (n % 192 == 0)
+    run whole with that tile; otherwise, with 128 x 128 tiles, grids with fewer tiles than CUs split
+    k (the workspace size is that of the split), grids with a tile for every CU run whole unless a
     small last round is left (then only its tiles split), and grids of full rounds run whole."""
     torch_cuda()
     mnk = lambda m, n, k: B.pf_gemm_workspace_size(m, n, k)
@@ -175,7 +215,10 @@ def test_gemm_split_plan_rules():
     assert mnk(2048, 3072, 12288) == 0        # 384 tiles: every CU has one, whole
     assert mnk(2048, 3072, 3072) == 0         # 384 tiles
     assert mnk(2048, 12288, 3072) == 0        # 1536 tiles: three full rounds
-    assert mnk(2048, 4608, 1536) > 0          # 576 tiles: 64 left after a full round, those split
+    assert mnk(2304, 4096, 1536) > 0          # 576 tiles: 64 left after a full round, those split
+    assert mnk(2048, 4608, 1536) == 0         # 384 tiles of 192 x 128 (1.5 per CU): whole
+    assert mnk(16384, 1152, 4608) == 0        # 768 tiles of 192 x 128
+    assert mnk(2432, 3456, 1152) > 0          # 342 tiles of 192 x 128 (too few): 513 of 128, remainder split
 
 
 def test_gemm_bf16_split_workspace_reuse():

@@ -46,11 +46,11 @@ def check_stage_output(got, want_p, what, want_b=None, want_e=None, hidden=0):
         assert_close(got, want_e, f"{what} vs exact oracle", max_abs_tol=None)
 
 
-def _run_chain(shape, steps, check_exact=True):
+def _run_chain(shape, steps, check_exact=True, report_bf16=True):
     torch = torch_cuda()
     inputs = synth.stage_inputs(shape)
     bf16 = shape.dtype == "bf16"
-    orc_b = _oracle(shape, inputs, "bf16") if bf16 else None
+    orc_b = _oracle(shape, inputs, "bf16") if bf16 and report_bf16 else None
     orc_p = _oracle(shape, inputs, "bf16p") if bf16 else None
     orc_e = _oracle(shape, inputs, "exact")
     with Stage(shape) as st:
@@ -66,13 +66,14 @@ def _run_chain(shape, steps, check_exact=True):
                 orc_e.add_noise(noise)
                 if orc_b:
                     orc_b.add_noise(noise)
+                if orc_p:
                     orc_p.add_noise(noise)
             print(f"[stage] {shape.name} step {s} warmup={warm}", flush=True)
             st.run_step(x, c, warmup=warm, out=out)
             got = host(out)
             want_e = orc_e.step(inputs.x, inputs.c, warmup=warm)
             if bf16:
-                want_b = orc_b.step(inputs.x, inputs.c, warmup=warm)
+                want_b = orc_b.step(inputs.x, inputs.c, warmup=warm) if orc_b else None
                 want_p = orc_p.step(inputs.x, inputs.c, warmup=warm)
                 check_stage_output(got, want_p, f"{shape.name} step {s}", want_b, want_e if check_exact else None,
                                    hidden=shape.hidden)
@@ -96,6 +97,24 @@ def test_c1_tiny_fp32_all_steps():
 @pytest.mark.parametrize("name", sorted(SMALL))
 def test_small_bf16_stage_chain(name):
     _run_chain(SMALL[name], 3)
+
+
+# Every bf16 config at its full depth (4 blocks, 8 for the Flux-shaped stage) at the config's
+# width, heads and patch count, on a shortened sequence: the warm-up step and one patched step
+# with drifted stale K/V, every output row and every layer's K/V buffers.
+DEEP = {
+    "c2d": C2.small(seq_img=400),                                      # 4 layers, D=72, P=100
+    "c3d": C3.small(seq_img=512),                                      # 4 layers, D=64, M=8
+    "c4d": C4.small(seq_img=128, seq_txt=40),                          # 8 layers, D=128, text prefix
+    "c5d": C5.small(seq_img=1024, num_patches=16),                     # 4 layers, D=72, M=16
+}
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", sorted(DEEP))
+def test_full_depth_bf16_stage_chain(name):
+    assert DEEP[name].num_layers in (4, 8)
+    _run_chain(DEEP[name], 2, report_bf16=False)
 
 
 def _run_pair_chain(shape, steps):

@@ -146,8 +146,9 @@ def test_invalid_splice_writes_nothing():
 
 
 @pytest.mark.parametrize("m,off,split", [(1024, 1024, False), (77, 1003, False), (300, 8, True), (1, 4095, True),
-                                         (2432, 1003, True), (3000, 1001, False)],
-                         ids=["patch", "ragged", "ksplit", "one-row-ksplit", "remainder-split", "wide-tiles"])
+                                         (2432, 1003, True), (3000, 1001, False), (3002, 1000, False)],
+                         ids=["patch", "ragged", "ksplit", "one-row-ksplit", "remainder-split", "wide-tiles",
+                              "wide-tiles-aligned"])
 def test_fused_qkv_splice_matches_gemm_then_splice(m, off, split):
     """The stage's QKV projection writes K and V straight into the buffer (pf_gemm_qkv_splice).
     Its Q and every byte of the buffer must equal the unfused path, pf_gemm(PF_EPI_STORE) then
@@ -155,9 +156,8 @@ def test_fused_qkv_splice_matches_gemm_then_splice(m, off, split):
     assignment above): same rows replaced, including partial 8-row groups of the K8 layout,
     and nothing else touched.  2432 rows make 513 tiles of 128 x 128: one full round of 512
     slots plus one tile, which the plan runs as k slices finished by a reduce pass.  3000 rows
-    make 24 x 18 tiles of 192 features x 128 tokens, which run whole with that tile (a tile's
-    192 features straddle no Q / K / V boundary here, as 3 x 1152 is a multiple of 192; each
-    4-feature store picks its destination on its own either way)."""
+    make 24 x 18 tiles of 192 features x 128 tokens, which run whole with that tile (offsets 1000
+    and 1001: whole and partial 8-row groups of the K8 layout at both ends of the range)."""
     import math
     from _util import dev
     torch = torch_cuda()

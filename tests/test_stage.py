@@ -167,9 +167,15 @@ def _run_pair_chain(shape, steps):
             assert max_abs(got[0], got[1]) > 1e-3
 
 
-@pytest.mark.parametrize("name", ["c1", "c2s", "c4s"])
+# A pair whose patches of 1351 rows (odd) make 2702-row projections: 22 x 18 tiles of 192 x 128,
+# so the QKV splice takes the wide tile, and its tiles straddle the boundary between the samples
+# (whose rows go to different buffers) at an odd row.
+PAIR_WIDE = C2.small(seq_img=2702, num_layers=1, num_patches=2)
+
+
+@pytest.mark.parametrize("name", ["c1", "c2s", "c4s", "c2-wide-odd"])
 def test_cfg_pair_stage_chain(name):
-    shape = C1 if name == "c1" else SMALL[name]
+    shape = C1 if name == "c1" else PAIR_WIDE if name == "c2-wide-odd" else SMALL[name]
     _run_pair_chain(shape, 3)
 
 

@@ -146,8 +146,10 @@ typedef struct pf_stage pf_stage;
  * full-spatial K/V for its own layers only, PipeFusion mechanism 4), and scratch for
  * seq_txt + seq_img rows of every sample.  bf16 stages keep V in PF_LAYOUT_K8, fp32 stages in PF_LAYOUT_ROWS.  Buffers
  * start zeroed.  Requires h = H * d, d in {64,72,128}, h % 64 == 0 for bf16,
- * seq_img % num_patches == 0.  Errors: INVALID_ARG, UNSUPPORTED, OOM, HIP; nothing is
- * allocated on failure.  *out receives the stage. */
+ * seq_img % num_patches == 0.  Source: "Core mechanisms" 1 and 4 of the PipeFusion summaries
+ * (a stage of contiguous layers over M patches; each device keeps the full-spatial K/V of its
+ * own layers only).  Errors: INVALID_ARG, UNSUPPORTED, OOM, HIP; nothing is allocated on
+ * failure.  *out receives the stage. */
 pf_status stage_create(const pf_stage_config* cfg, pf_stage** out);
 
 /* Free everything the stage owns.  The caller synchronises its stream first.  NULL is a
@@ -198,7 +200,9 @@ pf_status stage_set_cond(pf_stage* st, const float* cond, void* stream);
  * batch * rows rows, each sample's own modulation and gates, its fresh K/V spliced into its
  * own buffers and its queries attending over its own buffer.  Requires 0 <= row_off,
  * rows >= 1, row_off + rows <= seq_txt + seq_img, weights loaded and stage_set_cond
- * called. */
+ * called.  Source: "Core mechanisms" 1 and 2 of the PipeFusion summaries.  Errors:
+ * INVALID_ARG (rows outside the buffer, NULL or misaligned x, partially overlapping x_in /
+ * x_out), STATE (weights not loaded, stage_set_cond not called), HIP. */
 pf_status stage_run_patch(pf_stage* st, int64_t row_off, int64_t rows, const float* x_in,
                           float* x_out, void* stream);
 
@@ -222,7 +226,10 @@ pf_status stage_run_step(pf_stage* st, const float* x_in, float* x_out, const fl
  * is a no-op.  Requires equal dtype and row_elems, 0 <= offset, offset + len <= dst.rows,
  * len <= src.rows, and src/dst not overlapping.  Needs no stage.  This is the update that
  * makes a layer's buffer hold fresh rows for the current patch and the previous step's
- * values elsewhere (PipeFusion mechanism 2). */
+ * values elsewhere.  Source: "Core mechanisms" 2 of the PipeFusion summaries (stale step-(T+1)
+ * context, refreshed row block by row block).  Errors: INVALID_ARG (NULL view or pointer, bad
+ * dtype, layout or strides, dtype or row_elems mismatch, rows out of range, misaligned or
+ * overlapping src / dst), HIP. */
 pf_status kvbuf_splice(const pf_kv_view* dst, const pf_kv_view* src, int64_t offset, int64_t len,
                        void* stream);
 
@@ -370,8 +377,11 @@ pf_status pf_gemm(const void* a, int64_t lda, const void* w, const float* bias, 
  * of the buffer changes.  Each value is the bf16 rounding of its fp32 sum, identical to
  * pf_gemm(PF_EPI_STORE) followed by kvbuf_splice of the K and V columns.  This is the
  * in-place update of a layer's full-spatial buffer with the current patch's fresh K/V
- * (PipeFusion mechanism 2), done where the values are produced.  q, a and the buffer must not
- * overlap.  The workspace is as for pf_gemm with n = 3 hidden, k = hidden. */
+ * done where the values are produced.  q, a and the buffer must not overlap.  The workspace is
+ * as for pf_gemm with n = 3 hidden, k = hidden.  Source: "Core mechanisms" 2 of the PipeFusion
+ * summaries, with the layer's QKV projection (mechanism 1).  Errors: UNSUPPORTED (not bf16, V not
+ * K8, hidden % 64 != 0), INVALID_ARG (buffer row_elems or k_ld != hidden, rows outside the
+ * buffer, NULL or misaligned pointers, bad strides), HIP. */
 pf_status pf_gemm_qkv_splice(const void* a, int64_t lda, const void* w, const float* bias, int64_t m,
                              int64_t hidden, void* q, int64_t ldq, const pf_kv_view* kv, int64_t row_offset,
                              void* workspace, uint64_t workspace_bytes, void* stream);

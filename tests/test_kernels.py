@@ -353,6 +353,54 @@ def test_attention_full_size_sampled(cfg):
     assert_close(got, want, f"attention {cfg} full size, sampled rows vs exact")
 
 
+@pytest.mark.parametrize("split", [False, True], ids=["whole", "split"])
+@pytest.mark.parametrize("D", [64, 72, 128])
+def test_attention_bf16_single_key(D, split):
+    """One key: every softmax row is the single weight 1, so each query's output is that key's V
+    row.  The weight is bf16(2^(t - ceil t)) and the row sum the same value, so acc / l = v up to
+    fp32 rounding, which bf16 rounds back to v: the output equals V[0] bit for bit, whatever Q."""
+    torch = torch_cuda()
+    H, rows = 3, 70
+    h = H * D
+    q = synth.randn((rows, h), 910 + D, std=3.0, bf16=True)
+    K = synth.randn((1, h), 911 + D, bf16=True)
+    V = synth.randn((1, h), 912 + D, bf16=True)
+    kt, vt, kv = _kv_bf16(torch, K, V)
+    ws = torch.empty((B.pf_attention_workspace_size(rows, H, D) or 1,), dtype=torch.uint8, device="cuda") \
+        if split else None
+    o = torch.empty((rows, h), dtype=torch.bfloat16, device="cuda")
+    print(f"[attention] single key D={D} split={split}", flush=True)
+    B.pf_attention(dev(torch, q, torch.bfloat16), kv, 1, rows, H, D, o, workspace=ws)
+    got = host(o)
+    assert np.array_equal(got, np.broadcast_to(V[0], got.shape)), "output differs from the single key's V row"
+
+
+def test_degenerate_sizes_are_no_ops_or_errors():
+    """Zero query rows (attention) and zero token rows (GEMM) launch nothing and leave the
+    output untouched; an empty key range has no softmax and is rejected."""
+    torch = torch_cuda()
+    D, H = 64, 2
+    h = H * D
+    K = synth.randn((40, h), 920, bf16=True)
+    V = synth.randn((40, h), 921, bf16=True)
+    kt, vt, kv = _kv_bf16(torch, K, V)
+    q = torch.zeros((4, h), dtype=torch.bfloat16, device="cuda")
+    o = torch.full((4, h), 7.0, dtype=torch.bfloat16, device="cuda")
+    B.pf_attention(q, kv, 40, 0, H, D, o)
+    torch.cuda.synchronize()
+    assert bool((o == 7.0).all()), "rows = 0 wrote the output"
+    with pytest.raises(B.PFError) as ei:
+        B.pf_attention(q, kv, 0, 4, H, D, o)
+    assert ei.value.status == B.PF_ERR_INVALID_ARG
+    a = torch.zeros((4, 64), dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros((128, 64), dtype=torch.bfloat16, device="cuda")
+    bias = torch.zeros((128,), dtype=torch.float32, device="cuda")
+    c = torch.full((4, 128), 5.0, dtype=torch.bfloat16, device="cuda")
+    B.pf_gemm(a, w, bias, B.PF_EPI_STORE, c, m=0)
+    torch.cuda.synchronize()
+    assert bool((c == 5.0).all()), "m = 0 wrote the output"
+
+
 @pytest.mark.parametrize("D", [64, 72, 128])
 def test_attention_bf16_closed_forms(D):
     torch = torch_cuda()

@@ -542,8 +542,14 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const bf16* __restric
     // D = 72 and 128 the wavefront in its MFMA phase runs at a raised priority, so the SIMD's
     // arbiter issues its MFMAs as soon as the matrix core frees up and fills the gaps with the
     // other wavefront's softmax (measured: +5% at 262144 keys, d = 72; at d = 64, where the
-    // softmax phase is the longer one, it costs 3%)
+    // softmax phase is the longer one, it costs 3%).  In the D = 128 stream-K kernel group 0's
+    // MFMA phase runs one level above group 1's: with one barrier per key tile group 1 can enter
+    // its MFMA phase while group 0 is still in its own, and equal priorities then share the
+    // matrix core between them, which stretches group 0's MFMA phase and pushes its softmax
+    // towards the barrier (measured: -1.8% for the 2048 x 16896-key, 24-head stream-K launch; at
+    // D = 72 it cost 0.8%)
     constexpr bool kPingPongPrio = D != 64;
+    constexpr bool kGroupPrio = D == 128 && kOneBarrier;
     // Where the V operands of tile t are read.  At D = 64 and 72 the wavefront in its MFMA phase
     // reads them right after its P.V MFMAs have consumed the previous tile's: a wavefront then
     // issues its LDS reads next to its MFMAs, not next to its softmax VALU work (measured: -5%
@@ -555,7 +561,12 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const bf16* __restric
     constexpr bool kEarlyV = D == 128;
     auto iter_steady = [&](int64_t t) {
       bf16x8 kf[KS];
-      if constexpr (kPingPongPrio) __builtin_amdgcn_s_setprio(1);
+      if constexpr (kGroupPrio) {
+        if (grp == 0) __builtin_amdgcn_s_setprio(2);
+        else __builtin_amdgcn_s_setprio(1);
+      } else if constexpr (kPingPongPrio) {
+        __builtin_amdgcn_s_setprio(1);
+      }
       read_k(st, kf);
       f32x16 sc[QB];
       pv(vf, pb);

@@ -254,6 +254,18 @@ def time_denoiser(torch, B, synth, st, shape, nb, steps):
             "note": "whole denoising loop: condition, patch embedding, stage step, final layer, DDIM update"}
 
 
+def host_cpu_model() -> str:
+    """The host CPU's model name (Linux /proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name") and ":" in line:
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(shape, inputs, budget_s, mm=None):
     """The oracle (fp64 numpy, exact mode) on a bounded sample of the workload: one patch (the
     last) through one layer over a full, filled S_kv-row buffer.  The patch's LayerNorm, QKV
@@ -303,7 +315,8 @@ def cpu_baseline(shape, inputs, budget_s, mm=None):
                       f"({t1:.1f} s, {t2:.1f} s); patch-layer time {how} to {P} rows = {patch_s:.1f} s, then x "
                       f"{shape.seq_kv // P} patch-sized micro-steps x {shape.num_layers} layers (extrapolated); "
                       f"tokens/s = {shape.seq_kv} rows / step time",
-            "host_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0))}
+            "host_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)), "blas_threads": int(threads),
+            "cpu_model": host_cpu_model()}
 
 
 PROBES = ["attention", "copy", "ln_modulate", "gemm_qkv_splice", "kv_splice_entry", "gemm_out", "gemm_up_gelu",

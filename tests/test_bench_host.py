@@ -24,3 +24,8 @@ def test_recorded_traffic_null_after_a_source_change(monkeypatch):
     monkeypatch.setattr(bench, "attention_source_hash", lambda: "0" * 64)
     assert bench.recorded_traffic("c5") is None
     assert bench.recorded_traffic("c2") is None
+
+
+def test_host_cpu_model_is_named():
+    m = bench.host_cpu_model()
+    assert isinstance(m, str) and m

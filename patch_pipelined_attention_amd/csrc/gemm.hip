@@ -12,8 +12,8 @@
 // fewer LDS and L2 bytes per FLOP and gives each k tile 1.5x the MFMA work to hide the next
 // tile's load behind; it is taken for grids of whole tiles that still give every CU at least
 // 1.5 of them (fewer leave CUs with a lone workgroup, which runs slower).  Grids too small to
-// fill the GPU split k: every slice writes its fp32 partial tile and a reduce pass sums the slices in
-// order (deterministic) and applies the epilogue.  A grid whose last round would run part
+// fill the GPU split k: every slice writes its fp32 partial tile and a reduce pass sums the
+// slices in order (deterministic) and applies the epilogue.  A grid whose last round would run part
 // full splits only the tiles of that round ("remainder split"): the full rounds run whole
 // tiles, the remaining tiles run as k slices that fill one round, and a reduce pass over
 // those tiles alone finishes them.  (A last-arriving-slice merge inside the

@@ -117,54 +117,56 @@ def test_full_depth_bf16_stage_chain(name):
     _run_chain(DEEP[name], 2, report_bf16=False)
 
 
-def _run_pair_chain(shape, steps):
-    """A classifier-free guidance pair through one batched stage: both samples share the
-    latent rows and the weights, each has its own condition (the second stands in for the
-    unconditional embedding), its own drift between steps and its own K/V buffers.  Each
-    sample must match its own oracle stage, which never sees the other sample."""
+def _run_pair_chain(shape, steps, nb=2):
+    """A classifier-free guidance pair (nb = 2), or a batch of nb samples, through one batched
+    stage: the samples share the latent rows and the weights, each has its own condition (the
+    second stands in for the unconditional embedding), its own drift between steps and its own
+    K/V buffers.  Each sample must match its own oracle stage, which never sees the others."""
     torch = torch_cuda()
     inputs = synth.stage_inputs(shape)
-    conds = list(synth.batch_conds(shape, inputs.c, 2))
+    conds = list(synth.batch_conds(shape, inputs.c, nb))
     bf16 = shape.dtype == "bf16"
-    orc_b = [_oracle(shape, inputs, "bf16p" if bf16 else "exact") for _ in range(2)]
+    orc_b = [_oracle(shape, inputs, "bf16p" if bf16 else "exact") for _ in range(nb)]
     S, h, L = shape.seq_kv, shape.hidden, shape.num_layers
-    with Stage(shape, batch=2) as st:
+    what = "pair" if nb == 2 else f"batch {nb}"
+    with Stage(shape, batch=nb) as st:
         st.load(inputs.layers)
-        x = dev(torch, np.stack([inputs.x, inputs.x]))
+        x = dev(torch, np.stack([inputs.x] * nb))
         c = dev(torch, np.stack(conds))
         out = torch.empty_like(x)
         for s in range(steps):
             warm = s == 0
             if s > 0:
-                for b in range(2):
+                for b in range(nb):
                     seed = shape.seed + 100 * s + 10 * b
                     noise = [(synth.randn((S, h), seed + 2 * l, std=shape.sigma_kv),
                               synth.randn((S, h), seed + 2 * l + 1, std=shape.sigma_kv)) for l in range(L)]
                     st.add_noise(noise, sample=b)
                     orc_b[b].add_noise(noise)
-            print(f"[stage pair] {shape.name} step {s} warmup={warm}", flush=True)
+            print(f"[stage {what}] {shape.name} step {s} warmup={warm}", flush=True)
             st.run_step(x, c, warmup=warm, out=out)
             got = host(out)
-            for b in range(2):
+            for b in range(nb):
                 want = orc_b[b].step(inputs.x, conds[b], warmup=warm)
                 if bf16:
-                    check_stage_output(got[b], want, f"{shape.name} pair step {s} sample {b}", hidden=shape.hidden)
+                    check_stage_output(got[b], want, f"{shape.name} {what} step {s} sample {b}", hidden=shape.hidden)
                     for l in range(L):
                         k, v = st.kv_get(l, sample=b)
                         ew = chain_elementwise(l, shape.hidden)
-                        assert_bf16_close(k, orc_b[b].K[l], f"pair step {s} sample {b} K[{l}]", elementwise=ew)
-                        assert_bf16_close(v, orc_b[b].V[l], f"pair step {s} sample {b} V[{l}]", elementwise=ew)
+                        assert_bf16_close(k, orc_b[b].K[l], f"{what} step {s} sample {b} K[{l}]", elementwise=ew)
+                        assert_bf16_close(v, orc_b[b].V[l], f"{what} step {s} sample {b} V[{l}]", elementwise=ew)
                 else:
-                    assert_close(got[b], want, f"{shape.name} pair step {s} sample {b} vs exact oracle",
+                    assert_close(got[b], want, f"{shape.name} {what} step {s} sample {b} vs exact oracle",
                                  max_abs_tol=1e-3, rel_tol=1e-5)
                     for l in range(L):
                         k, v = st.kv_get(l, sample=b)
-                        assert_close(k, orc_b[b].K[l], f"pair step {s} sample {b} K[{l}]", max_abs_tol=1e-4,
+                        assert_close(k, orc_b[b].K[l], f"{what} step {s} sample {b} K[{l}]", max_abs_tol=1e-4,
                                      rel_tol=1e-5)
-                        assert_close(v, orc_b[b].V[l], f"pair step {s} sample {b} V[{l}]", max_abs_tol=1e-4,
+                        assert_close(v, orc_b[b].V[l], f"{what} step {s} sample {b} V[{l}]", max_abs_tol=1e-4,
                                      rel_tol=1e-5)
-            # the two samples really differ (different conditions reach every row)
-            assert max_abs(got[0], got[1]) > 1e-3
+            # the samples really differ (different conditions reach every row)
+            for b in range(1, nb):
+                assert max_abs(got[0], got[b]) > 1e-3
 
 
 # A pair whose patches of 1351 rows (odd) make 2702-row projections: 22 x 18 tiles of 192 x 128,
@@ -177,6 +179,16 @@ PAIR_WIDE = C2.small(seq_img=2702, num_layers=1, num_patches=2)
 def test_cfg_pair_stage_chain(name):
     shape = C1 if name == "c1" else PAIR_WIDE if name == "c2-wide-odd" else SMALL[name]
     _run_pair_chain(shape, 3)
+
+
+@pytest.mark.parametrize("name", ["c1", "c3-width"])
+def test_max_batch_stage_chain(name):
+    """The largest batch a stage takes (PF_MAX_STAGE_BATCH = 8 samples sharing the weights): every
+    sample against its own oracle over a warm-up and a drifted patched step, at the tiny fp32
+    config and at the SD3-shaped width (8 x 256 rows: one projection over 2048 rows, one
+    attention launch over all samples' query tiles, each sample's own buffers)."""
+    shape = C1 if name == "c1" else C3.small(seq_img=256, num_layers=1, num_patches=4)
+    _run_pair_chain(shape, 2, nb=8)
 
 
 @pytest.mark.parametrize("name", ["c2s", "c2-full-L1", "c4-full-L1"])

@@ -111,11 +111,12 @@ def test_gemm_residual_ln_is_bit_identical(m, n, k, split):
 
 
 @pytest.mark.parametrize("epi", [B.PF_EPI_STORE, B.PF_EPI_GELU_TANH, B.PF_EPI_GELU_ERF, B.PF_EPI_GATED_RESIDUAL])
-@pytest.mark.parametrize("m,n,k", [(2689, 4608, 1536), (16384, 1152, 4608)])
+@pytest.mark.parametrize("m,n,k", [(2689, 4608, 1536), (16384, 1152, 4608), (10000, 960, 128)])
 def test_gemm_bf16_wide_tiles(m, n, k, epi):
     """Grids the plan runs whole with 192-feature x 128-token tiles (n % 192 == 0, at least 1.5
     tiles per CU): 2689 rows end in a tile row of one token (rows past m clamped on load, never
-    stored), and 16384 x 1152 x 4608 is the long-sequence PixArt-shaped MLP down projection.
+    stored), 16384 x 1152 x 4608 is the long-sequence PixArt-shaped MLP down projection, and
+    n = 960 is a multiple of 192 but not of 128 (79 x 5 tiles, a two-step k loop).
     Checked against the oracle on sampled rows, the first and last rows included."""
     torch = torch_cuda()
     assert B.pf_gemm_workspace_size(m, n, k) == 0, "wide-tile grids run whole"
